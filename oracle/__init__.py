@@ -1,0 +1,190 @@
+"""CPU oracle for SageAttention-style quantized attention (test infrastructure).
+
+Only the tests, the package smoke check and the benchmark's CPU-baseline leg
+use this package; the library's product path never imports it.  The numeric
+work is plain C in ``sage_oracle.c`` (fp64 unless the format fixes fp32),
+loaded here through ctypes; this file only marshals numpy arrays.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sage_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build():
+    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+           "-std=c11", "-Wall", "-o", _LIB + ".tmp", _SRC, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(_LIB + ".tmp", _LIB)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        L.or_e4m3_decode.restype = ctypes.c_double
+        L.or_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.or_e4m3_encode.restype = ctypes.c_uint8
+        L.or_e4m3_encode.argtypes = [ctypes.c_double]
+        L.or_e2m1_decode.restype = ctypes.c_double
+        L.or_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.or_e2m1_encode.restype = ctypes.c_uint8
+        L.or_e2m1_encode.argtypes = [ctypes.c_double]
+        L.or_mx_scale_byte.restype = ctypes.c_uint8
+        L.or_mx_scale_byte.argtypes = [ctypes.c_double, ctypes.c_int]
+        L.or_int8_encode.restype = ctypes.c_int8
+        L.or_int8_encode.argtypes = [ctypes.c_float, ctypes.c_float]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(x):
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def widen(u16, dtype):
+    """bf16 ('bf16') or fp16 ('f16') bit patterns -> float32, exactly."""
+    u16 = np.ascontiguousarray(u16, dtype=np.uint16)
+    out = np.empty(u16.shape, np.float32)
+    lib().or_widen(_p(u16), ctypes.c_int(0 if dtype == "bf16" else 1), _p(out), ctypes.c_int64(u16.size))
+    return out
+
+
+def e4m3_encode(x):
+    f = lib().or_e4m3_encode
+    return np.array([f(float(v)) for v in np.ravel(x)], np.uint8).reshape(np.shape(x))
+
+
+def e4m3_decode(c):
+    f = lib().or_e4m3_decode
+    return np.array([f(int(v)) for v in np.ravel(c)], np.float64).reshape(np.shape(c))
+
+
+def e2m1_encode(x):
+    f = lib().or_e2m1_encode
+    return np.array([f(float(v)) for v in np.ravel(x)], np.uint8).reshape(np.shape(x))
+
+
+def e2m1_decode(c):
+    f = lib().or_e2m1_decode
+    return np.array([f(int(v)) for v in np.ravel(c)], np.float64).reshape(np.shape(c))
+
+
+def mx_scale_byte(amax, emax):
+    return int(lib().or_mx_scale_byte(float(amax), int(emax)))
+
+
+def int8_encode(x, delta):
+    return int(lib().or_int8_encode(float(x), float(delta)))
+
+
+def quant_int8_fp8(q, k, v, sm, blk=64):
+    """Prologue of the INT8/FP8 path on [BH,N,d] float32 arrays."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    BH, N, d = q.shape
+    nb = (N + blk - 1) // blk
+    r = dict(mu_k=np.empty((BH, d), np.float32), qc=np.empty((BH, N, d), np.int8),
+             qs=np.empty((BH, nb), np.float32), kc=np.empty((BH, N, d), np.int8),
+             ks=np.empty((BH, nb), np.float32), vc=np.empty((BH, N, d), np.uint8),
+             vs=np.empty((BH, d), np.float32), corr=np.empty((BH, N), np.float64))
+    lib().or_quant_int8_fp8(_p(q), _p(k), _p(v), BH, N, d, blk, ctypes.c_double(sm),
+                            _p(r["mu_k"]), _p(r["qc"]), _p(r["qs"]), _p(r["kc"]), _p(r["ks"]),
+                            _p(r["vc"]), _p(r["vs"]), _p(r["corr"]))
+    return r
+
+
+def quant_mxfp4(q, k, v, sm, pv_fmt="mxfp4"):
+    """Prologue of the MXFP4 path on [BH,N,d] float32 arrays (codes one per byte)."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    BH, N, d = q.shape
+    ng, nvg = d // 32, (N + 31) // 32
+    pv = 3 if pv_fmt == "mxfp4" else 2
+    r = dict(mu_q=np.empty((BH, d), np.float32), mu_k=np.empty((BH, d), np.float32),
+             qc=np.empty((BH, N, d), np.uint8), qe=np.empty((BH, N, ng), np.uint8),
+             kc=np.empty((BH, N, d), np.uint8), ke=np.empty((BH, N, ng), np.uint8),
+             dS=np.empty((BH, N), np.float32), corr=np.empty((BH, N), np.float64),
+             vc=np.empty((BH, N, d), np.uint8), ve=np.zeros((BH, nvg, d), np.uint8),
+             vs=np.zeros((BH, d), np.float32))
+    lib().or_quant_mxfp4(_p(q), _p(k), _p(v), BH, N, d, pv, ctypes.c_double(sm),
+                         _p(r["mu_q"]), _p(r["mu_k"]), _p(r["qc"]), _p(r["qe"]), _p(r["kc"]), _p(r["ke"]),
+                         _p(r["dS"]), _p(r["corr"]), _p(r["vc"]), _p(r["ve"]), _p(r["vs"]))
+    r["pv_fmt"] = pv_fmt
+    return r
+
+
+def _rows(rows, N):
+    rows = np.arange(N, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    assert rows.min() >= 0 and rows.max() < N
+    return rows
+
+
+def attn_int8_fp8(qz, N, d, causal, sm, tile, rows=None, blk=64):
+    """Tiled quantized forward (INT8 QK, FP8 P~V) on a quant_int8_fp8 result."""
+    BH = qz["qc"].shape[0]
+    rows = _rows(rows, N)
+    out = np.empty((BH, len(rows), d), np.float64)
+    lse = np.empty((BH, len(rows)), np.float64)
+    lib().or_attn_int8_fp8(_p(qz["qc"]), _p(qz["qs"]), _p(qz["kc"]), _p(qz["ks"]), _p(qz["vc"]),
+                           _p(qz["vs"]), _p(qz["corr"]), BH, N, d, blk, tile, int(causal),
+                           ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
+    return out, lse
+
+
+def attn_mxfp4(qz, N, d, causal, sm, tile, rows=None):
+    """Tiled quantized forward (MXFP4 QK, MXFP4 or FP8 P~V) on a quant_mxfp4 result."""
+    BH = qz["qc"].shape[0]
+    rows = _rows(rows, N)
+    out = np.empty((BH, len(rows), d), np.float64)
+    lse = np.empty((BH, len(rows)), np.float64)
+    pv = 3 if qz["pv_fmt"] == "mxfp4" else 2
+    lib().or_attn_mxfp4(_p(qz["qc"]), _p(qz["qe"]), _p(qz["kc"]), _p(qz["ke"]), _p(qz["dS"]), _p(qz["corr"]),
+                        _p(qz["vc"]), _p(qz["ve"]), _p(qz["vs"]), pv, BH, N, d, tile, int(causal),
+                        ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
+    return out, lse
+
+
+def attn_tiled_exact(q, k, v, causal, sm, tile, smooth_q=False, rows=None):
+    """The tiled forward with identity codecs (smoothing and its corrections kept, in fp64)."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    BH, N, d = q.shape
+    rows = _rows(rows, N)
+    out = np.empty((BH, len(rows), d), np.float64)
+    lse = np.empty((BH, len(rows)), np.float64)
+    lib().or_attn_tiled_exact(_p(q), _p(k), _p(v), BH, N, d, tile, int(causal), ctypes.c_double(sm),
+                              int(smooth_q), _p(rows), len(rows), _p(out), _p(lse))
+    return out, lse
+
+
+def attn_ref(q, k, v, causal, sm, rows=None):
+    """Exact fp64 two-pass attention and LSE for the listed rows."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    BH, N, d = q.shape
+    rows = _rows(rows, N)
+    out = np.empty((BH, len(rows), d), np.float64)
+    lse = np.empty((BH, len(rows)), np.float64)
+    lib().or_attn_ref(_p(q), _p(k), _p(v), BH, N, d, int(causal), ctypes.c_double(sm),
+                      _p(rows), len(rows), _p(out), _p(lse))
+    return out, lse
+
+
+def attn_bwd_ref(q, k, v, do, causal, sm):
+    """Exact fp64 gradients dQ, dK, dV of softmax attention."""
+    q, k, v, do = _f32(q), _f32(k), _f32(v), _f32(do)
+    BH, N, d = q.shape
+    dq, dk, dv = (np.empty((BH, N, d), np.float64) for _ in range(3))
+    lib().or_attn_bwd_ref(_p(q), _p(k), _p(v), _p(do), BH, N, d, int(causal), ctypes.c_double(sm),
+                          _p(dq), _p(dk), _p(dv))
+    return dq, dk, dv

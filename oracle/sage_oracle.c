@@ -1,0 +1,723 @@
+/*
+ * sage_oracle.c -- plain, slow CPU oracle for SageAttention-style quantized
+ * attention.  TEST INFRASTRUCTURE ONLY: it is loaded by the tests, by the
+ * package's smoke check and by the benchmark's CPU-baseline leg, never by the
+ * library's product path.  It shares no code with the HIP kernels.
+ *
+ * Built with gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp, so every
+ * float expression below rounds exactly once, in the written order.
+ *
+ * What it computes, and the passages it follows:
+ *   - Online softmax: m_0 = -inf, d_0 = 0, m_i = max(m_{i-1}, a_i),
+ *     d_i = d_{i-1} exp(m_{i-1}-m_i) + exp(a_i - m_i); result exp(a-m_n)/d_n
+ *     (SageAttention review thread, reply to reviewer xY6z Q3).
+ *   - FlashAttention tiling: rows of the score tile S_i^j are the queries of a
+ *     Q tile, columns the keys of a K tile; one pass over K tiles per query
+ *     (same reply).  Normalisation by diag(l)^-1 once, after the last K tile,
+ *     with l^0 = 0 (reply to xY6z Q2).
+ *   - Smoothing K, INT8 QK^T, per-block quantization granularity
+ *     (SageAttention contributions, reply to reviewer wwcu W1; SageAttn-B, reply
+ *     to xY6z W1-(2) and Q1).
+ *   - P~ and V in FP8, smoothing Q for the 4-bit QK^T, two-level accumulation
+ *     of P~V (SageAttention2 abstract, Jianfei Chen author page).
+ *   - Microscaling FP4 attention (SageAttention3 abstract); the MX format is a
+ *     fine-grained per-group quantization (TetraJet abstract, same author page).
+ *   - 8-bit forward + backward for training (SageAttention3 abstract): the
+ *     oracle gives the exact fp64 backward the GPU gradients are held to.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *   mean over all N tokens per (b,h,channel) for smoothing; INT8 symmetric
+ *   +-127 with delta = amax/127 and code = rne(x/delta) in fp32; FP8 = OCP
+ *   E4M3FN (RNE, saturating at 448); P~ = E4M3(448 p); V per-channel FP8 scale;
+ *   MXFP4 = OCP MX: E2M1 elements, 32-element blocks, E8M0 scale with
+ *   e = floor(log2 amax) - 2; P~ in the 4-bit path gets a per-row per-K-tile
+ *   fp32 scale sigma = 6 / max_tile(p) before MX quantization over 32-key groups;
+ *   the row sum l accumulates the unquantized p; LSE is natural-log over the
+ *   true (unsmoothed) scores.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_API __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------ */
+/* Widening of the 16-bit input formats (exact).                       */
+/* ------------------------------------------------------------------ */
+static float bf16_to_float(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static float f16_to_float(uint16_t h)
+{
+    int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                 /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);     /* (1 + m/1024) * 2^(e-15) */
+    return (float)(s ? -v : v);
+}
+
+/* dtype: 0 = bf16, 1 = fp16 */
+OR_API void or_widen(const uint16_t *src, int dtype, float *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        dst[i] = dtype == 0 ? bf16_to_float(src[i]) : f16_to_float(src[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Element codecs (OCP 8-bit FP and MX formats, INT8).                 */
+/* ------------------------------------------------------------------ */
+
+/* floor(log2 a) for finite a > 0, exact. */
+static int floor_log2(double a)
+{
+    int e;
+    frexp(a, &e);          /* a = f * 2^e, f in [0.5, 1) */
+    return e - 1;
+}
+
+/* E4M3FN decode: bias 7, 3 mantissa bits, subnormals, 0x7F/0xFF = NaN. */
+OR_API double or_e4m3_decode(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);                  /* m/8 * 2^-6 */
+    else
+        v = ldexp((double)(8 + m), e - 10);        /* (1 + m/8) * 2^(e-7) */
+    return s ? -v : v;
+}
+
+/* E4M3FN encode: round to nearest, ties to even, saturate to +-448. */
+OR_API uint8_t or_e4m3_encode(double x)
+{
+    uint8_t s = signbit(x) ? 0x80 : 0x00;
+    if (isnan(x))
+        return s | 0x7F;
+    double a = fabs(x);
+    if (a >= 448.0)
+        return s | 0x7E;
+    if (a == 0.0)
+        return s;
+    int E = floor_log2(a);
+    if (E < -6)
+        E = -6;                                    /* subnormal range shares 2^-6's quantum */
+    double quantum = ldexp(1.0, E - 3);
+    double n = rint(a / quantum);                  /* integer in [0, 16]; rint = RNE */
+    double v = n * quantum;                        /* the rounded magnitude, <= 448 */
+    if (v == 0.0)
+        return s;
+    int Ev = floor_log2(v);
+    if (Ev < -6)
+        return s | (uint8_t)(v / ldexp(1.0, -9));  /* subnormal: exponent field 0 */
+    int mant = (int)(v / ldexp(1.0, Ev - 3)) - 8;
+    return s | (uint8_t)(((Ev + 7) << 3) | mant);
+}
+
+/* E2M1 decode: magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}. */
+OR_API double or_e2m1_decode(uint8_t c)
+{
+    int e = (c >> 1) & 3, m = c & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return (c & 8) ? -v : v;
+}
+
+/* E2M1 encode: round to nearest, ties to even, saturate to +-6. */
+OR_API uint8_t or_e2m1_encode(double x)
+{
+    uint8_t s = signbit(x) ? 0x8 : 0x0;
+    double a = fabs(x);
+    if (isnan(x))
+        return s | 0x7;                            /* no NaN in E2M1: saturate */
+    if (a >= 6.0)
+        return s | 0x7;
+    int E = (a < 1.0) ? 0 : floor_log2(a);
+    double quantum = ldexp(1.0, E - 1);
+    double v = rint(a / quantum) * quantum;
+    for (uint8_t c = 0; c < 8; c++)
+        if (or_e2m1_decode(c) == v)
+            return s | c;
+    return s | 0x7;                                /* unreachable */
+}
+
+/* MX shared exponent of a block with amax a, for an element format whose
+ * largest power of two is 2^emax: e = floor(log2 a) - emax, clamped to the
+ * E8M0 range; a == 0 gives the byte 0.  Returns the E8M0 byte (e + 127). */
+OR_API uint8_t or_mx_scale_byte(double amax, int emax)
+{
+    if (amax == 0.0)
+        return 0;
+    if (isnan(amax) || isinf(amax))
+        return 0xFF;
+    int e = floor_log2(amax) - emax;
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    return (uint8_t)(e + 127);
+}
+
+/* INT8 symmetric code with step delta (fp32): clamp(rne(fl32(x / delta)), -127, 127). */
+OR_API int8_t or_int8_encode(float x, float delta)
+{
+    if (delta == 0.0f)
+        return 0;
+    float r = x / delta;                           /* one correctly rounded fp32 division */
+    float n = rintf(r);
+    if (n > 127.0f)
+        n = 127.0f;
+    if (n < -127.0f)
+        n = -127.0f;
+    return (int8_t)n;
+}
+
+/* ------------------------------------------------------------------ */
+/* Prologue: statistics and codes for one (b,h) head.                  */
+/* ------------------------------------------------------------------ */
+
+/* mu[c] = fl32( (sum_t x[t,c]) / N ), the sum in fp64 in token order. */
+static void channel_mean(const float *x, int N, int d, float *mu)
+{
+    for (int c = 0; c < d; c++) {
+        double s = 0.0;
+        for (int t = 0; t < N; t++)
+            s += (double)x[(int64_t)t * d + c];
+        mu[c] = (float)(s / (double)N);
+    }
+}
+
+static float absmax(const float *x, int64_t n, int64_t stride)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < n; i++) {
+        float v = fabsf(x[i * stride]);
+        if (v > a || isnan(v))
+            a = v;
+    }
+    return a;
+}
+
+/* INT8 codes per blk-token block over all d channels. */
+static void quant_int8_blocks(const float *x, int N, int d, int blk, int8_t *codes, float *scales)
+{
+    int nb = (N + blk - 1) / blk;
+    for (int b = 0; b < nb; b++) {
+        int t0 = b * blk, t1 = t0 + blk < N ? t0 + blk : N;
+        float a = absmax(x + (int64_t)t0 * d, (int64_t)(t1 - t0) * d, 1);
+        float delta = a / 127.0f;
+        scales[b] = delta;
+        for (int64_t i = (int64_t)t0 * d; i < (int64_t)t1 * d; i++)
+            codes[i] = or_int8_encode(x[i], delta);
+    }
+}
+
+/* MX quantization of a group of n elements at stride `stride`, element format
+ * E2M1 (emax 2) or E4M3 (emax 8).  Codes are stored one per byte. */
+static void quant_mx_group(const float *x, int n, int64_t stride, int elem_fmt,
+                           uint8_t *codes, int64_t cstride, uint8_t *scale_byte)
+{
+    int emax = elem_fmt == 4 ? 2 : 8;
+    float a = absmax(x, n, stride);
+    uint8_t sb = or_mx_scale_byte(a, emax);
+    *scale_byte = sb;
+    double inv = ldexp(1.0, -((int)sb - 127));     /* 2^-e, exact */
+    for (int i = 0; i < n; i++) {
+        double y = (sb == 0 && a == 0.0f) ? 0.0 * x[i * stride] : (double)x[i * stride] * inv;
+        codes[i * cstride] = elem_fmt == 4 ? or_e2m1_encode(y) : or_e4m3_encode(y);
+    }
+}
+
+/*
+ * INT8-QK / FP8-PV prologue for BH heads of [N, d] fp32 inputs.
+ *   mu_k [BH,d]; qc, kc [BH,N,d] int8; qs, ks [BH,nb] fp32 (nb = ceil(N/blk));
+ *   vc [BH,N,d] E4M3 codes (token-major); vs [BH,d] fp32; corr [BH,N] fp64 =
+ *   sm * q_i . mu_k (the per-row score shift removed by smoothing K).
+ */
+OR_API void or_quant_int8_fp8(const float *q, const float *k, const float *v,
+                              int BH, int N, int d, int blk, double sm,
+                              float *mu_k, int8_t *qc, float *qs, int8_t *kc, float *ks,
+                              uint8_t *vc, float *vs, double *corr)
+{
+    int nb = (N + blk - 1) / blk;
+#pragma omp parallel for schedule(dynamic)
+    for (int h = 0; h < BH; h++) {
+        int64_t off = (int64_t)h * N * d;
+        const float *Q = q + off, *K = k + off, *V = v + off;
+        float *mu = mu_k + (int64_t)h * d;
+        channel_mean(K, N, d, mu);
+        float *Ks = malloc(sizeof(float) * (size_t)N * d);
+        for (int t = 0; t < N; t++)
+            for (int c = 0; c < d; c++)
+                Ks[(int64_t)t * d + c] = K[(int64_t)t * d + c] - mu[c];
+        quant_int8_blocks(Q, N, d, blk, qc + off, qs + (int64_t)h * nb);
+        quant_int8_blocks(Ks, N, d, blk, kc + off, ks + (int64_t)h * nb);
+        for (int c = 0; c < d; c++) {
+            float a = absmax(V + c, N, d);
+            float delta = a / 448.0f;
+            vs[(int64_t)h * d + c] = delta;
+            for (int t = 0; t < N; t++) {
+                float y = delta == 0.0f ? 0.0f : V[(int64_t)t * d + c] / delta;
+                vc[off + (int64_t)t * d + c] = or_e4m3_encode(y);
+            }
+        }
+        for (int t = 0; t < N; t++) {
+            double s = 0.0;
+            for (int c = 0; c < d; c++)
+                s += (double)Q[(int64_t)t * d + c] * (double)mu[c];
+            corr[(int64_t)h * N + t] = sm * s;
+        }
+        free(Ks);
+    }
+}
+
+/*
+ * MXFP4-QK prologue.  Q and K are both smoothed by their channel means; the
+ * smoothed rows are MX-quantized in 32-channel groups (E2M1 codes one per
+ * byte, [BH,N,d]; E8M0 bytes [BH,N,d/32]).
+ *   dS [BH,N] = fl32(sum_c mu_q[c] * Ks[t,c]) (fp64 sum in channel order):
+ *       Q.Ks^T = Qs.Ks^T + 1 dS^T exactly, so dS is added back to every score.
+ *   corr [BH,N] = sm * q_t . mu_k (fp64), added back to the LSE only.
+ *   pv_fmt 3 (MXFP4): V codes [BH,N,d] E2M1 in 32-token groups per channel,
+ *       E8M0 bytes ve [BH, ceil(N/32), d].
+ *   pv_fmt 2 (FP8): V codes E4M3 with per-channel fp32 scale vs [BH,d].
+ */
+OR_API void or_quant_mxfp4(const float *q, const float *k, const float *v,
+                           int BH, int N, int d, int pv_fmt, double sm,
+                           float *mu_q, float *mu_k,
+                           uint8_t *qc, uint8_t *qe, uint8_t *kc, uint8_t *ke,
+                           float *dS, double *corr,
+                           uint8_t *vc, uint8_t *ve, float *vs)
+{
+    int ng = d / 32, nvg = (N + 31) / 32;
+#pragma omp parallel for schedule(dynamic)
+    for (int h = 0; h < BH; h++) {
+        int64_t off = (int64_t)h * N * d;
+        const float *Q = q + off, *K = k + off, *V = v + off;
+        float *muq = mu_q + (int64_t)h * d, *muk = mu_k + (int64_t)h * d;
+        channel_mean(Q, N, d, muq);
+        channel_mean(K, N, d, muk);
+        float *Qs = malloc(sizeof(float) * (size_t)N * d);
+        float *Ks = malloc(sizeof(float) * (size_t)N * d);
+        for (int t = 0; t < N; t++)
+            for (int c = 0; c < d; c++) {
+                Qs[(int64_t)t * d + c] = Q[(int64_t)t * d + c] - muq[c];
+                Ks[(int64_t)t * d + c] = K[(int64_t)t * d + c] - muk[c];
+            }
+        for (int t = 0; t < N; t++)
+            for (int g = 0; g < ng; g++) {
+                int64_t e0 = (int64_t)t * d + 32 * g;
+                quant_mx_group(Qs + e0, 32, 1, 4, qc + off + e0, 1, qe + ((int64_t)h * N + t) * ng + g);
+                quant_mx_group(Ks + e0, 32, 1, 4, kc + off + e0, 1, ke + ((int64_t)h * N + t) * ng + g);
+            }
+        for (int t = 0; t < N; t++) {
+            double s = 0.0, cq = 0.0;
+            for (int c = 0; c < d; c++) {
+                s += (double)muq[c] * (double)Ks[(int64_t)t * d + c];
+                cq += (double)Q[(int64_t)t * d + c] * (double)muk[c];
+            }
+            dS[(int64_t)h * N + t] = (float)s;
+            corr[(int64_t)h * N + t] = sm * cq;
+        }
+        if (pv_fmt == 3) {
+            for (int c = 0; c < d; c++)
+                for (int g = 0; g < nvg; g++) {
+                    int t0 = 32 * g, n = N - t0 < 32 ? N - t0 : 32;
+                    quant_mx_group(V + (int64_t)t0 * d + c, n, d, 4, vc + off + (int64_t)t0 * d + c, d,
+                                   ve + ((int64_t)h * nvg + g) * d + c);
+                }
+        } else {
+            for (int c = 0; c < d; c++) {
+                float a = absmax(V + c, N, d);
+                float delta = a / 448.0f;
+                vs[(int64_t)h * d + c] = delta;
+                for (int t = 0; t < N; t++) {
+                    float y = delta == 0.0f ? 0.0f : V[(int64_t)t * d + c] / delta;
+                    vc[off + (int64_t)t * d + c] = or_e4m3_encode(y);
+                }
+            }
+        }
+        free(Qs);
+        free(Ks);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* The tiled forward (one query row at a time).                        */
+/* ------------------------------------------------------------------ */
+
+enum { QK_EXACT = 0, QK_INT8 = 1, QK_MXFP4 = 3 };
+enum { PV_EXACT = 0, PV_FP8 = 2, PV_MXFP4 = 3 };
+
+typedef struct {
+    int N, d, causal, tile, blk;
+    double sm;
+    int qk, pv;
+    /* QK_EXACT: fp64 (smoothed) rows and an optional additive key term */
+    const double *qx, *kx;
+    /* QK_INT8 */
+    const int8_t *qc, *kc;
+    const float *qs, *ks;
+    /* QK_MXFP4 */
+    const uint8_t *q4, *qe, *k4, *ke;
+    const float *dS;           /* per-key additive score term (may be NULL) */
+    const double *dSx;         /* same, fp64, exact mode */
+    /* PV */
+    const double *vx;          /* PV_EXACT */
+    const uint8_t *vc;         /* PV_FP8 codes or PV_MXFP4 codes */
+    const float *vs;           /* PV_FP8 per-channel scale */
+    const uint8_t *ve;         /* PV_MXFP4 E8M0 bytes [ceil(N/32), d] */
+    const double *corr;        /* per-row LSE correction (may be NULL) */
+} head_t;
+
+/* Unscaled score s_ij (sm not applied). */
+static double score(const head_t *H, int i, int j)
+{
+    int d = H->d;
+    double s = 0.0;
+    if (H->qk == QK_EXACT) {
+        for (int c = 0; c < d; c++)
+            s += H->qx[(int64_t)i * d + c] * H->kx[(int64_t)j * d + c];
+        if (H->dSx)
+            s += H->dSx[j];
+    } else if (H->qk == QK_INT8) {
+        int64_t acc = 0;
+        for (int c = 0; c < d; c++)
+            acc += (int64_t)H->qc[(int64_t)i * d + c] * (int64_t)H->kc[(int64_t)j * d + c];
+        s = (double)H->qs[i / H->blk] * (double)H->ks[j / H->blk] * (double)acc;
+    } else {
+        int ng = d / 32;
+        for (int g = 0; g < ng; g++) {
+            double part = 0.0;
+            for (int c = 32 * g; c < 32 * g + 32; c++)
+                part += or_e2m1_decode(H->q4[(int64_t)i * d + c]) * or_e2m1_decode(H->k4[(int64_t)j * d + c]);
+            s += part * ldexp(1.0, (int)H->qe[(int64_t)i * ng + g] - 127)
+                      * ldexp(1.0, (int)H->ke[(int64_t)j * ng + g] - 127);
+        }
+        if (H->dS)
+            s += (double)H->dS[j];
+    }
+    return s;
+}
+
+/* Decoded V element (without the per-channel FP8 scale, which the epilogue applies). */
+static double vval(const head_t *H, int j, int c)
+{
+    int64_t idx = (int64_t)j * H->d + c;
+    if (H->pv == PV_EXACT)
+        return H->vx[idx];
+    if (H->pv == PV_FP8)
+        return or_e4m3_decode(H->vc[idx]);
+    return or_e2m1_decode(H->vc[idx]) * ldexp(1.0, (int)H->ve[(int64_t)(j / 32) * H->d + c] - 127);
+}
+
+static void forward_row(const head_t *H, int i, double *o, double *lse)
+{
+    int N = H->N, d = H->d, T = H->tile;
+    double *O = calloc((size_t)d, sizeof(double));
+    double *acc = malloc(sizeof(double) * (size_t)d);
+    double *x = malloc(sizeof(double) * (size_t)T);
+    double *p = malloc(sizeof(double) * (size_t)T);
+    double *pq = malloc(sizeof(double) * (size_t)T);
+    double m = -INFINITY, l = 0.0;
+    for (int j0 = 0; j0 < N; j0 += T) {
+        if (H->causal && j0 > i)
+            break;
+        int n = N - j0 < T ? N - j0 : T;
+        /* score tile row, masked entries -inf */
+        double mt = -INFINITY;
+        for (int jj = 0; jj < n; jj++) {
+            int j = j0 + jj;
+            x[jj] = (H->causal && j > i) ? -INFINITY : H->sm * score(H, i, j);
+            if (x[jj] > mt)
+                mt = x[jj];
+        }
+        double mn = m > mt ? m : mt;
+        if (mn == -INFINITY)
+            continue;
+        double alpha = (m == -INFINITY) ? 0.0 : exp(m - mn);
+        double psum = 0.0, pmax = 0.0;
+        for (int jj = 0; jj < n; jj++) {
+            p[jj] = (x[jj] == -INFINITY) ? 0.0 : exp(x[jj] - mn);
+            psum += p[jj];
+            if (p[jj] > pmax)
+                pmax = p[jj];
+        }
+        l = alpha * l + psum;
+        /* P~: quantize the tile row */
+        double post = 1.0;
+        if (H->pv == PV_EXACT) {
+            for (int jj = 0; jj < n; jj++)
+                pq[jj] = p[jj];
+        } else if (H->pv == PV_FP8) {
+            for (int jj = 0; jj < n; jj++)
+                pq[jj] = or_e4m3_decode(or_e4m3_encode(448.0 * p[jj]));
+        } else if (pmax == 0.0) {
+            for (int jj = 0; jj < n; jj++)
+                pq[jj] = 0.0;
+        } else {
+            /* second-level fp32 scale sigma, then MX E2M1 over 32-key groups */
+            float sigma = (float)(6.0 / pmax);
+            float *pf = malloc(sizeof(float) * (size_t)n);
+            uint8_t *codes = malloc((size_t)n);
+            for (int jj = 0; jj < n; jj++)
+                pf[jj] = (float)((double)sigma * p[jj]);
+            for (int g0 = 0; g0 < n; g0 += 32) {
+                int gn = n - g0 < 32 ? n - g0 : 32;
+                uint8_t sb;
+                quant_mx_group(pf + g0, gn, 1, 4, codes + g0, 1, &sb);
+                for (int jj = g0; jj < g0 + gn; jj++)
+                    pq[jj] = or_e2m1_decode(codes[jj]) * ldexp(1.0, (int)sb - 127);
+            }
+            post = 1.0 / (double)sigma;
+            free(pf);
+            free(codes);
+        }
+        /* first level: this tile's product; second level: the running O */
+        for (int c = 0; c < d; c++)
+            acc[c] = 0.0;
+        for (int jj = 0; jj < n; jj++) {
+            if (pq[jj] == 0.0)
+                continue;
+            for (int c = 0; c < d; c++)
+                acc[c] += pq[jj] * vval(H, j0 + jj, c);
+        }
+        for (int c = 0; c < d; c++)
+            O[c] = alpha * O[c] + acc[c] * post;
+        m = mn;
+    }
+    for (int c = 0; c < d; c++) {
+        if (H->pv == PV_FP8)
+            o[c] = O[c] * (double)H->vs[c] / (448.0 * l);
+        else
+            o[c] = O[c] / l;
+    }
+    *lse = m + log(l) + (H->corr ? H->corr[i] : 0.0);
+    free(O);
+    free(acc);
+    free(x);
+    free(p);
+    free(pq);
+}
+
+/* rows: the query rows to compute (shared by every head); out [BH,nrows,d], lse [BH,nrows]. */
+static void run_rows(const head_t *heads, int BH, const int *rows, int nrows, double *out, double *lse)
+{
+    int d = heads[0].d;
+#pragma omp parallel for schedule(dynamic) collapse(2)
+    for (int h = 0; h < BH; h++)
+        for (int r = 0; r < nrows; r++)
+            forward_row(&heads[h], rows[r], out + ((int64_t)h * nrows + r) * d, lse + (int64_t)h * nrows + r);
+}
+
+/* Simulation of the INT8-QK / FP8-PV forward on codes from or_quant_int8_fp8. */
+OR_API void or_attn_int8_fp8(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks,
+                             const uint8_t *vc, const float *vs, const double *corr,
+                             int BH, int N, int d, int blk, int tile, int causal, double sm,
+                             const int *rows, int nrows, double *out, double *lse)
+{
+    int nb = (N + blk - 1) / blk;
+    head_t *H = calloc((size_t)BH, sizeof(head_t));
+    for (int h = 0; h < BH; h++) {
+        int64_t off = (int64_t)h * N * d;
+        H[h] = (head_t){.N = N, .d = d, .causal = causal, .tile = tile, .blk = blk, .sm = sm,
+                        .qk = QK_INT8, .pv = PV_FP8,
+                        .qc = qc + off, .kc = kc + off, .qs = qs + (int64_t)h * nb, .ks = ks + (int64_t)h * nb,
+                        .vc = vc + off, .vs = vs + (int64_t)h * d, .corr = corr + (int64_t)h * N};
+    }
+    run_rows(H, BH, rows, nrows, out, lse);
+    free(H);
+}
+
+/* Simulation of the MXFP4-QK forward; pv_fmt 3 = MXFP4 P~ and V, 2 = FP8 P~ and V. */
+OR_API void or_attn_mxfp4(const uint8_t *qc, const uint8_t *qe, const uint8_t *kc, const uint8_t *ke,
+                          const float *dS, const double *corr,
+                          const uint8_t *vc, const uint8_t *ve, const float *vs, int pv_fmt,
+                          int BH, int N, int d, int tile, int causal, double sm,
+                          const int *rows, int nrows, double *out, double *lse)
+{
+    int ng = d / 32, nvg = (N + 31) / 32;
+    head_t *H = calloc((size_t)BH, sizeof(head_t));
+    for (int h = 0; h < BH; h++) {
+        int64_t off = (int64_t)h * N * d;
+        H[h] = (head_t){.N = N, .d = d, .causal = causal, .tile = tile, .sm = sm,
+                        .qk = QK_MXFP4, .pv = pv_fmt == 3 ? PV_MXFP4 : PV_FP8,
+                        .q4 = qc + off, .qe = qe + (int64_t)h * N * ng, .k4 = kc + off, .ke = ke + (int64_t)h * N * ng,
+                        .dS = dS + (int64_t)h * N, .corr = corr + (int64_t)h * N, .vc = vc + off};
+        if (pv_fmt == 3)
+            H[h].ve = ve + (int64_t)h * nvg * d;
+        else
+            H[h].vs = vs + (int64_t)h * d;
+    }
+    run_rows(H, BH, rows, nrows, out, lse);
+    free(H);
+}
+
+/*
+ * The same tiled forward with every codec replaced by the identity: smoothing
+ * of K (and of Q when smooth_q) in fp64, the dS term and the LSE correction
+ * kept.  In exact arithmetic it equals the two-pass softmax attention, which
+ * is what pins the tile recurrence, the masking, the deferred normalisation
+ * and the smoothing decomposition.
+ */
+OR_API void or_attn_tiled_exact(const float *q, const float *k, const float *v,
+                                int BH, int N, int d, int tile, int causal, double sm, int smooth_q,
+                                const int *rows, int nrows, double *out, double *lse)
+{
+    head_t *H = calloc((size_t)BH, sizeof(head_t));
+    double **bufs = calloc((size_t)BH * 5, sizeof(double *));
+    for (int h = 0; h < BH; h++) {
+        int64_t off = (int64_t)h * N * d;
+        double *qx = malloc(sizeof(double) * (size_t)N * d), *kx = malloc(sizeof(double) * (size_t)N * d);
+        double *vx = malloc(sizeof(double) * (size_t)N * d), *dSx = calloc((size_t)N, sizeof(double));
+        double *corr = calloc((size_t)N, sizeof(double));
+        double *muq = calloc((size_t)d, sizeof(double)), *muk = calloc((size_t)d, sizeof(double));
+        for (int t = 0; t < N; t++)
+            for (int c = 0; c < d; c++) {
+                muq[c] += q[off + (int64_t)t * d + c];
+                muk[c] += k[off + (int64_t)t * d + c];
+            }
+        for (int c = 0; c < d; c++) {
+            muq[c] = smooth_q ? muq[c] / N : 0.0;
+            muk[c] /= N;
+        }
+        for (int t = 0; t < N; t++) {
+            double cs = 0.0, ds = 0.0;
+            for (int c = 0; c < d; c++) {
+                int64_t i = (int64_t)t * d + c;
+                qx[i] = q[off + i] - muq[c];
+                kx[i] = k[off + i] - muk[c];
+                vx[i] = v[off + i];
+                cs += (double)q[off + i] * muk[c];
+            }
+            for (int c = 0; c < d; c++)
+                ds += muq[c] * kx[(int64_t)t * d + c];
+            corr[t] = sm * cs;
+            dSx[t] = ds;
+        }
+        free(muq);
+        free(muk);
+        H[h] = (head_t){.N = N, .d = d, .causal = causal, .tile = tile, .sm = sm, .qk = QK_EXACT, .pv = PV_EXACT,
+                        .qx = qx, .kx = kx, .vx = vx, .dSx = dSx, .corr = corr};
+        bufs[h * 5 + 0] = qx;
+        bufs[h * 5 + 1] = kx;
+        bufs[h * 5 + 2] = vx;
+        bufs[h * 5 + 3] = dSx;
+        bufs[h * 5 + 4] = corr;
+    }
+    run_rows(H, BH, rows, nrows, out, lse);
+    for (int i = 0; i < BH * 5; i++)
+        free(bufs[i]);
+    free(bufs);
+    free(H);
+}
+
+/* ------------------------------------------------------------------ */
+/* Exact fp64 attention (two-pass softmax) and its backward.           */
+/* ------------------------------------------------------------------ */
+
+static void ref_row(const float *Q, const float *K, const float *V, int N, int d, int causal, double sm,
+                    int i, double *x, double *o, double *lse)
+{
+    int n = causal ? i + 1 : N;
+    double mx = -INFINITY;
+    for (int j = 0; j < n; j++) {
+        double s = 0.0;
+        for (int c = 0; c < d; c++)
+            s += (double)Q[(int64_t)i * d + c] * (double)K[(int64_t)j * d + c];
+        x[j] = sm * s;
+        if (x[j] > mx)
+            mx = x[j];
+    }
+    double l = 0.0;
+    for (int j = 0; j < n; j++) {
+        x[j] = exp(x[j] - mx);
+        l += x[j];
+    }
+    for (int c = 0; c < d; c++) {
+        double s = 0.0;
+        for (int j = 0; j < n; j++)
+            s += x[j] * (double)V[(int64_t)j * d + c];
+        o[c] = s / l;
+    }
+    *lse = mx + log(l);
+}
+
+/* O = softmax(sm Q K^T + mask) V and LSE, exact in fp64, for the listed rows. */
+OR_API void or_attn_ref(const float *q, const float *k, const float *v, int BH, int N, int d,
+                        int causal, double sm, const int *rows, int nrows, double *out, double *lse)
+{
+#pragma omp parallel for schedule(dynamic) collapse(2)
+    for (int h = 0; h < BH; h++)
+        for (int r = 0; r < nrows; r++) {
+            int64_t off = (int64_t)h * N * d;
+            double *x = malloc(sizeof(double) * (size_t)N);
+            ref_row(q + off, k + off, v + off, N, d, causal, sm, rows[r],
+                    x, out + ((int64_t)h * nrows + r) * d, lse + (int64_t)h * nrows + r);
+            free(x);
+        }
+}
+
+/*
+ * Exact fp64 backward of O = softmax(sm Q K^T + mask) V for BH heads:
+ *   P = softmax rows, D_i = sum_c dO_ic O_ic, dV = P^T dO, dP = dO V^T,
+ *   dS = P o (dP - D), dQ = sm dS K, dK = sm dS^T Q.
+ */
+OR_API void or_attn_bwd_ref(const float *q, const float *k, const float *v, const float *dout,
+                            int BH, int N, int d, int causal, double sm,
+                            double *dq, double *dk, double *dv)
+{
+#pragma omp parallel for schedule(dynamic)
+    for (int h = 0; h < BH; h++) {
+        int64_t off = (int64_t)h * N * d;
+        const float *Q = q + off, *K = k + off, *V = v + off, *dO = dout + off;
+        double *dQ = dq + off, *dK = dk + off, *dV = dv + off;
+        double *P = malloc(sizeof(double) * (size_t)N);
+        double *dP = malloc(sizeof(double) * (size_t)N);
+        double *o = malloc(sizeof(double) * (size_t)d);
+        memset(dQ, 0, sizeof(double) * (size_t)N * d);
+        memset(dK, 0, sizeof(double) * (size_t)N * d);
+        memset(dV, 0, sizeof(double) * (size_t)N * d);
+        for (int i = 0; i < N; i++) {
+            int n = causal ? i + 1 : N;
+            double lse;
+            ref_row(Q, K, V, N, d, causal, sm, i, P, o, &lse);
+            for (int j = 0; j < n; j++) {
+                double s = 0.0;
+                for (int c = 0; c < d; c++)
+                    s += (double)Q[(int64_t)i * d + c] * (double)K[(int64_t)j * d + c];
+                P[j] = exp(sm * s - lse);
+            }
+            double D = 0.0;
+            for (int c = 0; c < d; c++)
+                D += (double)dO[(int64_t)i * d + c] * o[c];
+            for (int j = 0; j < n; j++) {
+                double s = 0.0;
+                for (int c = 0; c < d; c++)
+                    s += (double)dO[(int64_t)i * d + c] * (double)V[(int64_t)j * d + c];
+                dP[j] = s;
+            }
+            for (int j = 0; j < n; j++) {
+                double dS = P[j] * (dP[j] - D);
+                for (int c = 0; c < d; c++) {
+                    dV[(int64_t)j * d + c] += P[j] * (double)dO[(int64_t)i * d + c];
+                    dQ[(int64_t)i * d + c] += sm * dS * (double)K[(int64_t)j * d + c];
+                    dK[(int64_t)j * d + c] += sm * dS * (double)Q[(int64_t)i * d + c];
+                }
+            }
+        }
+        free(P);
+        free(dP);
+        free(o);
+    }
+}

@@ -1,0 +1,456 @@
+"""Pins of the oracle's attention functions against things other than itself:
+40-digit decimal brute force, torch fp64 SDPA / autograd, closed forms,
+invariants, finite differences, and inputs built on the codec grids so that
+every quantization step is exact and the simulated quantized forward must
+equal exact attention to rounding."""
+import math
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+import torch
+
+LN2 = math.log(2.0)
+
+
+def _rand(shape, seed, scale=1.0):
+    return (np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32)
+
+
+# ---------------------------------------------------------------- exact reference
+
+def _decimal_attention(q, k, v, causal, sm):
+    getcontext().prec = 40
+    N, d = q.shape
+    smd = Decimal(float(sm))
+    out = np.zeros((N, d))
+    lse = np.zeros(N)
+    for i in range(N):
+        n = i + 1 if causal else N
+        xs = [smd * sum(Decimal(float(q[i, c])) * Decimal(float(k[j, c])) for c in range(d)) for j in range(n)]
+        m = max(xs)
+        e = [(x - m).exp() for x in xs]
+        l = sum(e)
+        for c in range(d):
+            out[i, c] = float(sum(e[j] * Decimal(float(v[j, c])) for j in range(n)) / l)
+        lse[i] = float(m + l.ln())
+    return out, lse
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ref_matches_decimal_bruteforce(orc, causal):
+    for seed, (N, d) in enumerate([(1, 1), (3, 2), (5, 4), (6, 3)]):
+        q, k, v = _rand((1, N, d), seed), _rand((1, N, d), seed + 10, 2.0), _rand((1, N, d), seed + 20)
+        sm = 0.7
+        o, lse = orc.attn_ref(q, k, v, causal, sm)
+        od, lsed = _decimal_attention(q[0], k[0], v[0], causal, sm)
+        assert np.allclose(o[0], od, rtol=0, atol=1e-13)
+        assert np.allclose(lse[0], lsed, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ref_matches_torch_sdpa_fp64(orc, causal):
+    q, k, v = _rand((3, 37, 16), 1), _rand((3, 37, 16), 2, 3.0), _rand((3, 37, 16), 3)
+    sm = 0.25
+    o, lse = orc.attn_ref(q, k, v, causal, sm)
+    t = [torch.from_numpy(x).double() for x in (q, k, v)]
+    ot = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=causal, scale=sm).numpy()
+    s = (t[0] @ t[1].transpose(-1, -2)) * sm
+    if causal:
+        s = s.masked_fill(torch.ones(37, 37, dtype=torch.bool).triu(1), float("-inf"))
+    assert np.allclose(o, ot, rtol=0, atol=1e-12)
+    assert np.allclose(lse, torch.logsumexp(s, -1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_ref_closed_forms(orc):
+    q, k, v = _rand((2, 9, 8), 4), _rand((2, 9, 8), 5), _rand((2, 9, 8), 6)
+    # softmax rows sum to one: V = 1 gives O = 1
+    o, _ = orc.attn_ref(q, k, np.ones_like(v), False, 0.5)
+    assert np.allclose(o, 1.0, rtol=0, atol=1e-14)
+    # one token: O = V
+    o, lse = orc.attn_ref(q[:, :1], k[:, :1], v[:, :1], False, 0.5)
+    assert np.array_equal(o[:, 0], v[:, 0].astype(np.float64))
+    # constant keys: uniform weights, O_i = mean of the allowed V_j
+    kc = np.repeat(k[:, :1], 9, axis=1)
+    o, _ = orc.attn_ref(q, kc, v, False, 0.5)
+    assert np.allclose(o, v.astype(np.float64).mean(axis=1, keepdims=True), rtol=0, atol=1e-14)
+    o, _ = orc.attn_ref(q, kc, v, True, 0.5)
+    pref = np.cumsum(v.astype(np.float64), axis=1) / np.arange(1, 10)[None, :, None]
+    assert np.allclose(o, pref, rtol=0, atol=1e-14)
+    # causal row 0 sees only key 0
+    o, _ = orc.attn_ref(q, k, v, True, 0.5)
+    assert np.array_equal(o[:, 0], v[:, 0].astype(np.float64))
+
+
+def test_ref_key_shift_invariance(orc):
+    """Adding the same vector to every key shifts each score row by a constant."""
+    rng = np.random.default_rng(7)
+    q = (rng.integers(-16, 16, (2, 11, 8)) / 8).astype(np.float32)
+    k = (rng.integers(-16, 16, (2, 11, 8)) / 8).astype(np.float32)
+    v = _rand((2, 11, 8), 8)
+    shift = (rng.integers(-40, 40, (2, 1, 8)) / 4).astype(np.float32)
+    for causal in (False, True):
+        o1, _ = orc.attn_ref(q, k, v, causal, 0.3)
+        o2, _ = orc.attn_ref(q, k + shift, v, causal, 0.3)
+        assert np.allclose(o1, o2, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------- tiled recurrence machinery
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("smooth_q", [False, True])
+def test_tiled_online_softmax_equals_two_pass_every_tile(orc, causal, smooth_q):
+    N, d = 13, 8
+    q, k, v = _rand((2, N, d), 11), _rand((2, N, d), 12, 2.0), _rand((2, N, d), 13)
+    k += np.float32(3.0) * _rand((2, 1, d), 14)          # a large key offset: smoothing does real work
+    q += _rand((2, 1, d), 15)
+    o_ref, lse_ref = orc.attn_ref(q, k, v, causal, 0.6)
+    for tile in list(range(1, N + 2)) + [64]:
+        o, lse = orc.attn_tiled_exact(q, k, v, causal, 0.6, tile, smooth_q=smooth_q)
+        assert np.allclose(o, o_ref, rtol=0, atol=1e-12), tile
+        assert np.allclose(lse, lse_ref, rtol=0, atol=1e-12), tile
+
+
+def test_tiled_row_subset_matches_full(orc):
+    q, k, v = _rand((2, 50, 8), 16), _rand((2, 50, 8), 17), _rand((2, 50, 8), 18)
+    o_all, l_all = orc.attn_tiled_exact(q, k, v, True, 0.4, 16)
+    rows = np.array([0, 7, 16, 49], np.int32)
+    o, l = orc.attn_tiled_exact(q, k, v, True, 0.4, 16, rows=rows)
+    assert np.array_equal(o, o_all[:, rows]) and np.array_equal(l, l_all[:, rows])
+
+
+# ------------------------------------------------------------- statistics exactness
+
+def test_channel_mean_sum_is_exact(orc):
+    """The fp64 token sum of bf16 data equals the exactly rounded sum, so the mean
+    does not depend on summation order."""
+    from bit_quantized_attention_smooth_amd.workloads import make_inputs, as_u16
+    x = make_inputs(1, 2, 4096, 128, dtype="bf16", seed=1, k_off_std=5.0, outlier_frac=0.01)
+    k = orc.widen(as_u16(x["k"]), "bf16").reshape(2, 4096, 128)
+    qz = orc.quant_int8_fp8(k, k, k, 0.1)
+    for h in range(2):
+        for c in range(0, 128, 7):
+            col = k[h, :, c].astype(np.float64)
+            s = 0.0
+            for t in col:
+                s += t
+            assert s == math.fsum(col)
+            assert qz["mu_k"][h, c] == np.float32(math.fsum(col) / 4096)
+
+
+# --------------------------------------------- quantized forward: lossless constructions
+
+def _e4m3_grid():
+    vals = []
+    for e in range(1, 16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue
+            vals.append((1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+def _lossless_fp8_v(rng, BH, N, d):
+    """V whose per-channel FP8 step is a power of two and whose entries sit on the grid."""
+    grid = _e4m3_grid()
+    v = rng.choice(grid, size=(BH, N, d)) * rng.choice([-1.0, 1.0], size=(BH, N, d))
+    v[:, 0, :] = 448.0 * rng.choice([-1.0, 1.0], size=(BH, d))
+    v *= 2.0 ** -rng.integers(4, 10, size=(BH, 1, d))
+    return v.astype(np.float32)
+
+
+def _lossless_mx_v(rng, BH, N, d):
+    """V on the E2M1 grid per 32-token group, each group's max magnitude 4 or 6."""
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    v = rng.choice(mags, size=(BH, N, d)) * rng.choice([-1.0, 1.0], size=(BH, N, d))
+    for g0 in range(0, N, 32):
+        v[:, g0, :] = rng.choice([4.0, 6.0, -4.0, -6.0], size=(BH, d))
+        v[:, g0:g0 + 32, :] *= 2.0 ** rng.integers(-3, 3, size=(BH, 1, d))
+    return v.astype(np.float32)
+
+
+def _int8_score_design(rng, BH, N, d, blk=64):
+    """Q raw and K = Ks + mu with exact INT8 codes for Q and Ks (power-of-two block steps),
+    Ks with zero channel means; the scores q.k are 0 or q_i2 in {1, 2}."""
+    nb = (N + blk - 1) // blk
+    q = np.zeros((BH, N, d))
+    ks = np.zeros((BH, N, d))
+    for h in range(BH):
+        for b in range(nb):
+            t0, t1 = b * blk, min(N, b * blk + blk)
+            a, c = rng.integers(0, 6), rng.integers(1, 8)
+            q[h, t0, 0] = 127 * 2.0 ** -a                      # Q block max, channel 0 (K there is 0)
+            if t1 - t0 >= 2:
+                ks[h, t0, 1] = 127 * 2.0 ** -c                 # Ks block max in channel 1 (Q there is 0),
+                ks[h, t0 + 1, 1] = -127 * 2.0 ** -c            # paired so the channel mean stays 0
+    q[:, :, 2] = rng.integers(1, 3, size=(BH, N))
+    kk = np.zeros((BH, N, d))
+    kk[:, :, 2] = rng.permutation(np.arange(N) % 2)             # half ones, half zeros: mean 0.5 when N even
+    k = ks + kk
+    return q.astype(np.float32), k.astype(np.float32)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("tile", [32, 64, 128])
+def test_int8_fp8_sim_is_exact_on_lossless_grid(orc, causal, tile):
+    rng = np.random.default_rng(21)
+    BH, N, d = 2, 160, 64
+    q, k = _int8_score_design(rng, BH, N, d)
+    v = _lossless_fp8_v(rng, BH, N, d)
+    sm = LN2                                               # p takes the values 2^0, 2^-1, 2^-2
+    qz = orc.quant_int8_fp8(q, k, v, sm)
+    o, lse = orc.attn_int8_fp8(qz, N, d, causal, sm, tile)
+    o_ref, lse_ref = orc.attn_ref(q, k, v, causal, sm)
+    assert np.allclose(lse, lse_ref, rtol=0, atol=1e-12)
+    assert np.allclose(o, o_ref, rtol=1e-12, atol=1e-12 * np.abs(v).max())
+
+
+def test_int8_scores_exact_on_random_lossless_codes(orc):
+    """Random INT8 codes with per-block power-of-two steps and a smoothed K: the LSE
+    (which does not depend on the P~ codec) must equal exact attention's."""
+    rng = np.random.default_rng(22)
+    BH, N, d, blk = 2, 200, 64, 64
+    nb = (N + blk - 1) // blk
+    q = np.zeros((BH, N, d))
+    ks = np.zeros((BH, N, d))
+    for h in range(BH):
+        for b in range(nb):
+            t0, t1 = b * blk, min(N, b * blk + blk)
+            n = t1 - t0
+            qc = rng.integers(-127, 128, size=(n, d)).astype(np.float64)
+            qc[0, 0] = 127
+            q[h, t0:t1] = qc * 2.0 ** -rng.integers(0, 8)
+            half = n // 2
+            kc = rng.integers(-127, 128, size=(half, d)).astype(np.float64)
+            kc[0, 0] = -127
+            blockk = np.zeros((n, d))
+            blockk[:half] = kc
+            blockk[half:2 * half] = -kc                       # paired rows: zero channel sums
+            ks[h, t0:t1] = blockk * 2.0 ** -rng.integers(2, 9)
+    mu = (rng.integers(-24, 24, size=(BH, 1, d)) / 8.0)
+    k = (ks + mu).astype(np.float32)
+    assert np.array_equal(k - mu.astype(np.float32), ks.astype(np.float32))
+    v = _rand((BH, N, d), 23)
+    for causal in (False, True):
+        sm = 0.01
+        qz = orc.quant_int8_fp8(q.astype(np.float32), k, v, sm)
+        assert np.array_equal(qz["mu_k"], np.broadcast_to(mu[:, 0, :], (BH, d)).astype(np.float32))
+        _, lse = orc.attn_int8_fp8(qz, N, d, causal, sm, 64)
+        _, lse_ref = orc.attn_ref(q.astype(np.float32), k, v, causal, sm)
+        assert np.allclose(lse, lse_ref, rtol=0, atol=1e-11)
+
+
+def _mx_score_design(rng, BH, N, d):
+    """Q = Qs + mu_q, K = Ks + mu_k with Qs, Ks exactly on the MX grid and zero channel
+    means; channel 2 carries scores q.k in {0, q_i2}, q_i2 in {1, 2}."""
+    q = np.zeros((BH, N, d))
+    k = np.zeros((BH, N, d))
+    for h in range(BH):
+        q[h, :, 2] = 1.0 + rng.permutation(np.arange(N) % 2)  # {1, 2}: mean 1.5, Qs = -+0.5
+        k[h, :, 2] = rng.permutation(np.arange(N) % 2)        # {0, 1}: mean 0.5, Ks = -+0.5
+    return q.astype(np.float32), k.astype(np.float32)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("pv_fmt", ["mxfp4", "fp8"])
+def test_mxfp4_sim_is_exact_on_lossless_grid(orc, causal, pv_fmt):
+    rng = np.random.default_rng(31)
+    BH, N, d = 2, 160, 64
+    q, k = _mx_score_design(rng, BH, N, d)
+    v = _lossless_mx_v(rng, BH, N, d) if pv_fmt == "mxfp4" else _lossless_fp8_v(rng, BH, N, d)
+    sm = LN2
+    qz = orc.quant_mxfp4(q, k, v, sm, pv_fmt=pv_fmt)
+    assert np.array_equal(qz["mu_q"][:, 2], np.full(BH, 1.5, np.float32))
+    assert np.array_equal(qz["dS"], np.float32(1.5) * (k[:, :, 2] - np.float32(0.5)))
+    for tile in (64, 128):
+        o, lse = orc.attn_mxfp4(qz, N, d, causal, sm, tile)
+        o_ref, lse_ref = orc.attn_ref(q, k, v, causal, sm)
+        assert np.allclose(lse, lse_ref, rtol=0, atol=1e-12)
+        assert np.allclose(o, o_ref, rtol=1e-12, atol=1e-12 * np.abs(v).max())
+
+
+def test_mxfp4_scores_exact_on_random_lossless_codes(orc):
+    """Random MX codes for Qs and Ks with smoothing of both: LSE equals exact attention's,
+    which pins the dS = mu_q . Ks term and the LSE correction."""
+    rng = np.random.default_rng(32)
+    BH, N, d = 2, 96, 64
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+
+    def grid_rows(n):
+        x = rng.choice(mags, size=(BH, n, d)) * rng.choice([-1.0, 1.0], size=(BH, n, d))
+        x[:, :, 0::32] = rng.choice([4.0, -6.0], size=(BH, n, d // 32))
+        x *= 2.0 ** rng.integers(-3, 1, size=(BH, n, 1))
+        return x
+
+    qh, kh = grid_rows(N // 2), grid_rows(N // 2)
+    qs = np.concatenate([qh, -qh], axis=1)
+    ks = np.concatenate([kh, -kh], axis=1)
+    mu_q = rng.integers(-8, 8, size=(BH, 1, d)) / 4.0
+    mu_k = rng.integers(-8, 8, size=(BH, 1, d)) / 4.0
+    q = (qs + mu_q).astype(np.float32)
+    k = (ks + mu_k).astype(np.float32)
+    v = _rand((BH, N, d), 33)
+    for causal in (False, True):
+        sm = 0.02
+        qz = orc.quant_mxfp4(q, k, v, sm)
+        _, lse = orc.attn_mxfp4(qz, N, d, causal, sm, 64)
+        _, lse_ref = orc.attn_ref(q, k, v, causal, sm)
+        assert np.allclose(lse, lse_ref, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("path", ["int8_fp8", "mxfp4_mxfp4", "mxfp4_fp8"])
+def test_constant_keys_give_mean_of_values(orc, path):
+    """K constant along tokens: smoothing zeroes it, every score is 0, p = 1, and O is
+    the (prefix) mean of the dequantized V, exact on grid V."""
+    rng = np.random.default_rng(41)
+    BH, N, d = 2, 100, 64
+    q = _rand((BH, N, d), 42)
+    k = np.repeat(_rand((BH, 1, d), 43, 3.0), N, axis=1)
+    v = _lossless_mx_v(rng, BH, N, d) if path == "mxfp4_mxfp4" else _lossless_fp8_v(rng, BH, N, d)
+    for causal in (False, True):
+        if path == "int8_fp8":
+            qz = orc.quant_int8_fp8(q, k, v, 0.1)
+            assert not qz["kc"].any()
+            o, _ = orc.attn_int8_fp8(qz, N, d, causal, 0.1, 64)
+        else:
+            qz = orc.quant_mxfp4(q, k, v, 0.1, pv_fmt=path.split("_")[1])
+            assert not (qz["kc"] & 7).any()
+            o, _ = orc.attn_mxfp4(qz, N, d, causal, 0.1, 64)
+        v64 = v.astype(np.float64)
+        want = (np.cumsum(v64, axis=1) / np.arange(1, N + 1)[None, :, None]) if causal else \
+            np.broadcast_to(v64.mean(axis=1, keepdims=True), v64.shape)
+        assert np.allclose(o, want, rtol=1e-14, atol=1e-14 * np.abs(v64).max())
+
+
+def test_int8_fp8_key_shift_gives_identical_codes_and_output(orc):
+    """Smoothing K removes a per-channel shift shared by all tokens: shifted inputs give the
+    same codes and the same output (inputs chosen so the shift is exact in fp32)."""
+    rng = np.random.default_rng(51)
+    BH, N, d = 2, 128, 64
+    q = (rng.integers(-64, 64, (BH, N, d)) / 16).astype(np.float32)
+    k = (rng.integers(-64, 64, (BH, N, d)) / 16).astype(np.float32)
+    v = _rand((BH, N, d), 52)
+    shift = (rng.integers(-80, 80, (BH, 1, d)) / 4).astype(np.float32)
+    for causal in (False, True):
+        a = orc.quant_int8_fp8(q, k, v, 0.125)
+        b = orc.quant_int8_fp8(q, k + shift, v, 0.125)
+        assert np.array_equal(a["kc"], b["kc"]) and np.array_equal(a["ks"], b["ks"])
+        oa, la = orc.attn_int8_fp8(a, N, d, causal, 0.125, 64)
+        ob, lb = orc.attn_int8_fp8(b, N, d, causal, 0.125, 64)
+        assert np.array_equal(oa, ob)
+        # the LSE moves by exactly the per-row constant sm * q.shift
+        assert np.allclose(lb - la, 0.125 * np.einsum("hnd,hd->hn", q.astype(np.float64),
+                                                       shift[:, 0].astype(np.float64)), rtol=0, atol=1e-10)
+
+
+# ---------------------------------------------------------- accuracy on seeded data
+
+def _cos(a, b):
+    a, b = a.ravel().astype(np.float64), b.ravel().astype(np.float64)
+    return float(a @ b / math.sqrt((a @ a) * (b @ b)))
+
+
+def test_int8_fp8_sim_accuracy_vs_exact(orc):
+    from bit_quantized_attention_smooth_amd.workloads import make_inputs, as_u16
+    x = make_inputs(1, 2, 256, 64, dtype="f16", seed=0, k_off_std=4.0)
+    q, k, v = (orc.widen(as_u16(x[n]), "f16").reshape(2, 256, 64) for n in "qkv")
+    for causal in (False, True):
+        qz = orc.quant_int8_fp8(q, k, v, 0.125)
+        o, lse = orc.attn_int8_fp8(qz, 256, 64, causal, 0.125, 64)
+        o_ref, lse_ref = orc.attn_ref(q, k, v, causal, 0.125)
+        assert _cos(o, o_ref) > 0.999
+        assert np.abs(lse - lse_ref).max() < 0.05
+
+
+def test_mxfp4_sim_accuracy_vs_exact(orc):
+    from bit_quantized_attention_smooth_amd.workloads import make_inputs, as_u16
+    x = make_inputs(1, 2, 512, 128, dtype="bf16", seed=3, k_off_std=5.0)
+    q, k, v = (orc.widen(as_u16(x[n]), "bf16").reshape(2, 512, 128) for n in "qkv")
+    sm = 1 / math.sqrt(128)
+    o_ref, _ = orc.attn_ref(q, k, v, False, sm)
+    # MXFP4 QK with FP8 P~V meets the 0.98 bar; with P~ and V also in MXFP4 the
+    # single E2M1 mantissa bit on the probabilities costs about 1 % more (measured
+    # 0.972 here), so that variant is held to a lower band.
+    for pv, bar in (("fp8", 0.98), ("mxfp4", 0.965)):
+        qz = orc.quant_mxfp4(q, k, v, sm, pv_fmt=pv)
+        o, _ = orc.attn_mxfp4(qz, 512, 128, False, sm, 64)
+        assert _cos(o, o_ref) > bar, pv
+
+
+def test_sim_accuracy_on_the_pages_stress_distribution(orc):
+    """The pages' kernel-accuracy protocol (N(0,1), 1 % of entries from N(1,10)); a soft,
+    one-sided check against the printed numbers (tests/golden/kernel_accuracy_table.txt)."""
+    import os
+    from bit_quantized_attention_smooth_amd.workloads import make_inputs, as_u16
+    table = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", "kernel_accuracy_table.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                name, cs, l1, rmse = line.split()
+                table[name] = (float(cs), float(l1), float(rmse))
+    x = make_inputs(1, 2, 1024, 64, dtype="bf16", seed=9, stress=True)
+    q, k, v = (orc.widen(as_u16(x[n]), "bf16").reshape(2, 1024, 64) for n in "qkv")
+    rows = np.arange(0, 1024, 4, dtype=np.int32)
+    qz = orc.quant_int8_fp8(q, k, v, 0.125)
+    o, _ = orc.attn_int8_fp8(qz, 1024, 64, False, 0.125, 64, rows=rows)
+    o_ref, _ = orc.attn_ref(q, k, v, False, 0.125, rows=rows)
+    rel_l1 = np.abs(o - o_ref).sum() / np.abs(o_ref).sum()
+    assert _cos(o, o_ref) >= table["FlashAttention3-fp8"][0]
+    assert rel_l1 <= table["FlashAttention3-fp8"][1]
+
+
+# ---------------------------------------------------------------- exact backward
+
+def _torch_grads(q, k, v, do, causal, sm):
+    t = [torch.from_numpy(x.astype(np.float64)).requires_grad_(True) for x in (q, k, v)]
+    s = (t[0] @ t[1].transpose(-1, -2)) * sm
+    if causal:
+        N = q.shape[1]
+        s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    o = torch.softmax(s, -1) @ t[2]
+    o.backward(torch.from_numpy(do.astype(np.float64)))
+    return [x.grad.numpy() for x in t]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_ref_matches_torch_autograd(orc, causal):
+    q, k, v, do = (_rand((2, 21, 8), s) for s in (60, 61, 62, 63))
+    dq, dk, dv = orc.attn_bwd_ref(q, k, v, do, causal, 0.35)
+    tq, tk, tv = _torch_grads(q, k, v, do, causal, 0.35)
+    assert np.allclose(dq, tq, rtol=0, atol=1e-12)
+    assert np.allclose(dk, tk, rtol=0, atol=1e-12)
+    assert np.allclose(dv, tv, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_ref_matches_finite_differences(orc, causal):
+    rng = np.random.default_rng(70)
+    BH, N, d = 1, 5, 3
+    q, k, v, do = ((rng.integers(-24, 24, (BH, N, d)) / 16).astype(np.float32) for _ in range(4))
+    sm = 0.5
+    grads = orc.attn_bwd_ref(q, k, v, do, causal, sm)
+    h = 2.0 ** -10                                      # exact in fp32 on these inputs
+
+    def loss(qq, kk, vv):
+        o, _ = orc.attn_ref(qq, kk, vv, causal, sm)
+        return float((o * do.astype(np.float64)).sum())
+
+    for which, g in zip(range(3), grads):
+        for idx in np.ndindex(BH, N, d):
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][idx] += np.float32(h)
+            lp = loss(*args)
+            args[which][idx] -= np.float32(2 * h)
+            lm = loss(*args)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - g[idx]) < 1e-5, (which, idx, fd, g[idx])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_ref_invariants(orc, causal):
+    q, k, v, do = (_rand((2, 33, 16), s) for s in (80, 81, 82, 83))
+    dq, dk, dv = orc.attn_bwd_ref(q, k, v, do, causal, 0.25)
+    # rows of P sum to one: sum_j dV_j = sum_i dO_i
+    assert np.allclose(dv.sum(axis=1), do.astype(np.float64).sum(axis=1), rtol=0, atol=1e-11)
+    # rows of dS sum to zero: sum_j dK_j = 0
+    assert np.abs(dk.sum(axis=1)).max() < 1e-11
