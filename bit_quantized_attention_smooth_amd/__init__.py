@@ -1,0 +1,200 @@
+"""MI355X-native SageAttention-style quantized attention.
+
+A thin ctypes binding over ``libsage_attn.so`` (C ABI in ``include/sage_attn.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensor shapes, allocates outputs / workspaces with torch and
+passes raw device pointers and the current HIP stream.  If the library is not
+built, every entry point raises; there is no CPU fallback.
+
+Entry points follow the pages' names: ``sageattn`` (alias ``attn``) computes
+softmax(sm_scale Q K^T) V with INT8 or MXFP4 QK^T and FP8 P~V; ``quantize``
+and ``attn_fwd_quantized`` expose the two stages; ``attn_bwd`` and
+``SageAttnFn`` give the 8-bit backward.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsage_attn.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_OUT_OF_MEMORY, ERR_HIP = range(6)
+FMT = {"int8": 1, "fp8": 2, "mxfp4": 3}
+DT = {torch.bfloat16: 0, torch.float16: 1}
+
+# Every symbol the header declares (kept in sync by a CPU test that parses the header).
+EXPORTS = ["sage_attn_fwd", "sage_quant_size", "sage_quantize", "sage_attn_fwd_quantized",
+           "sage_attn_fwd_ws_size", "sage_attn_fwd_ex", "sage_attn_bwd_ws_size", "sage_attn_bwd",
+           "sage_status_string", "sage_last_error", "sage_abi_version"]
+
+
+class SageError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"sage status {status}: {msg}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int), ("d", ctypes.c_int),
+                ("causal", ctypes.c_int), ("sm_scale", ctypes.c_float), ("io_dtype", ctypes.c_int),
+                ("qk_fmt", ctypes.c_int), ("pv_fmt", ctypes.c_int)]
+
+
+class QuantLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("mu_k", "mu_q", "q_codes", "q_scales", "k_codes", "k_scales", "v_codes", "v_scales",
+                 "delta_s", "lse_corr", "stats", "total")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run bit_quantized_attention_smooth_amd/build.py "
+                               "(or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i, f = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
+        P = ctypes.POINTER(Problem)
+        sigs = {
+            "sage_attn_fwd": [vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp],
+            "sage_quant_size": [P, ctypes.POINTER(sz), ctypes.POINTER(QuantLayout)],
+            "sage_quantize": [vp, vp, vp, P, vp, sz, vp],
+            "sage_attn_fwd_quantized": [vp, sz, P, vp, vp, vp],
+            "sage_attn_fwd_ws_size": [P, ctypes.POINTER(sz)],
+            "sage_attn_fwd_ex": [P, vp, vp, vp, vp, vp, vp, sz, vp],
+            "sage_attn_bwd_ws_size": [P, ctypes.POINTER(sz)],
+            "sage_attn_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.sage_status_string.argtypes = [ctypes.c_int]
+        L.sage_status_string.restype = ctypes.c_char_p
+        L.sage_last_error.restype = ctypes.c_char_p
+        L.sage_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != OK:
+        raise SageError(status, lib().sage_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(None)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def problem(B, H, N, d, *, causal=False, sm_scale=None, dtype=torch.bfloat16, qk_fmt="int8", pv_fmt="fp8"):
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    return Problem(B, H, N, d, int(bool(causal)), sm, DT[dtype], FMT[qk_fmt], FMT[pv_fmt])
+
+
+def quant_size(p):
+    """(bytes, {part: byte offset}) of the quantized buffer for problem ``p``."""
+    n = ctypes.c_size_t()
+    lay = QuantLayout()
+    _check(lib().sage_quant_size(ctypes.byref(p), ctypes.byref(n), ctypes.byref(lay)))
+    return n.value, {name: getattr(lay, name) for name, _ in QuantLayout._fields_}
+
+
+def _qkv(q, k, v):
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q, k, v must share a [B,H,N,d] shape, got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if q.dtype not in DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be bfloat16 or all float16")
+    return q.contiguous(), k.contiguous(), v.contiguous()
+
+
+def quantize(q, k, v, *, causal=False, sm_scale=None, qk_fmt="int8", pv_fmt="fp8"):
+    """Smoothing + quantization prologue; returns (buffer uint8 tensor, problem, layout)."""
+    q, k, v = _qkv(q, k, v)
+    B, H, N, d = q.shape
+    p = problem(B, H, N, d, causal=causal, sm_scale=sm_scale, dtype=q.dtype, qk_fmt=qk_fmt, pv_fmt=pv_fmt)
+    nbytes, lay = quant_size(p)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check(lib().sage_quantize(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(p), _ptr(buf), nbytes, _stream()))
+    return buf, p, lay
+
+
+def attn_fwd_quantized(buf, p, *, dtype=torch.bfloat16, return_lse=False):
+    """Fused attention on a quantized buffer; returns O (and the fp32 LSE)."""
+    o = torch.empty((p.B, p.H, p.N, p.d), dtype=dtype, device=buf.device)
+    lse = torch.empty((p.B, p.H, p.N), dtype=torch.float32, device=buf.device) if return_lse else None
+    _check(lib().sage_attn_fwd_quantized(_ptr(buf), buf.numel(), ctypes.byref(p), _ptr(o), _ptr(lse), _stream()))
+    return (o, lse) if return_lse else o
+
+
+def sageattn(q, k, v, *, causal=False, sm_scale=None, qk_fmt="int8", pv_fmt="fp8", return_lse=False, workspace=None):
+    """Quantized attention forward on [B,H,N,d] bf16/fp16 device tensors."""
+    q, k, v = _qkv(q, k, v)
+    B, H, N, d = q.shape
+    p = problem(B, H, N, d, causal=causal, sm_scale=sm_scale, dtype=q.dtype, qk_fmt=qk_fmt, pv_fmt=pv_fmt)
+    nbytes = ctypes.c_size_t()
+    _check(lib().sage_attn_fwd_ws_size(ctypes.byref(p), ctypes.byref(nbytes)))
+    ws = workspace if workspace is not None and workspace.numel() >= nbytes.value else \
+        torch.empty(nbytes.value, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib().sage_attn_fwd_ex(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws),
+                                  ws.numel(), _stream()))
+    return (o, lse) if return_lse else o
+
+
+attn = sageattn
+
+
+def attn_fwd_oneshot(q, k, v, *, causal=False, sm_scale=None, qk_fmt="int8", pv_fmt="fp8"):
+    """The one-call C entry (bf16 only; the library allocates its scratch stream-ordered)."""
+    q, k, v = _qkv(q, k, v)
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    _check(lib().sage_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, int(bool(causal)), sm,
+                               FMT[qk_fmt], FMT[pv_fmt], _stream()))
+    return o
+
+
+def attn_bwd(q, k, v, o, do, lse, *, causal=False, sm_scale=None):
+    """8-bit backward: returns dQ, dK, dV in the input dtype."""
+    q, k, v = _qkv(q, k, v)
+    B, H, N, d = q.shape
+    p = problem(B, H, N, d, causal=causal, sm_scale=sm_scale, dtype=q.dtype)
+    nbytes = ctypes.c_size_t()
+    _check(lib().sage_attn_bwd_ws_size(ctypes.byref(p), ctypes.byref(nbytes)))
+    ws = torch.empty(max(nbytes.value, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    o, do, lse = o.contiguous(), do.contiguous(), lse.contiguous()
+    _check(lib().sage_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()))
+    return dq, dk, dv
+
+
+class SageAttnFn(torch.autograd.Function):
+    """Training attention: 8-bit forward (INT8 QK, FP8 P~V) and 8-bit backward."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal=False, sm_scale=None):
+        o, lse = sageattn(q, k, v, causal=causal, sm_scale=sm_scale, return_lse=True)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.sm_scale = causal, sm_scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = attn_bwd(q, k, v, o, do, lse, causal=ctx.causal, sm_scale=ctx.sm_scale)
+        return dq, dk, dv, None, None

@@ -1,0 +1,357 @@
+// prologue.hip -- the smoothing + quantization prologue (HBM-bound).
+//
+// Smoothing K: subtract the per-channel token mean of K before quantizing; it
+// shifts every score of a query row by the same constant, so softmax is
+// unchanged (SageAttention contributions, reply to reviewer wwcu W1).  Smooth
+// Q for the 4-bit QK^T: Q - mean(Q), with the removed part mean(Q).K_s added
+// back to every score (SageAttention2 abstract).  Per-block INT8 codes for Q
+// and K (SageAttn-B, reply to reviewer xY6z W1-(2)); FP8 V (SageAttention2
+// abstract); microscaling FP4 (SageAttention3 abstract) in the OCP MX layout.
+//
+// Two passes over the inputs:
+//   stats:  exact fp64 per-channel token sums of K (and Q), and max |V| per
+//           channel.  Every partial sum of bf16/fp16 values at these sizes is
+//           exactly representable in fp64, so the atomics make the result
+//           independent of order.
+//   codes:  one workgroup per 64-token block: smoothed values, block scales,
+//           codes, the dS / LSE correction terms, V transposed into tiles.
+#include "sage_device.hpp"
+#include "sage_launch.hpp"
+
+namespace sage {
+
+constexpr int kStatRows = 256;   // tokens per stats workgroup
+
+__global__ void zero_stats_kernel(double* sums, int nsum, uint32_t* amax, int namax) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nsum) sums[i] = 0.0;
+  if (i < namax) amax[i] = 0u;
+}
+
+// 16 bytes = 8 contiguous 16-bit inputs.
+template <int DT>
+__device__ __forceinline__ void load8(const uint16_t* p, float* x) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    x[2 * i] = DT == 0 ? bf16_to_f32(w[i] & 0xffff) : f16_to_f32(w[i] & 0xffff);
+    x[2 * i + 1] = DT == 0 ? bf16_to_f32(w[i] >> 16) : f16_to_f32(w[i] >> 16);
+  }
+}
+
+// grid (ceil(N/kStatRows), BH), 256 threads.  Sums K (and Q when SUMQ), max |V| when AMAXV.
+template <int DT, int D, bool SUMQ, bool AMAXV>
+__global__ __launch_bounds__(256) void stats_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                    const uint16_t* __restrict__ v, int N, int BH,
+                                                    double* __restrict__ sums, uint32_t* __restrict__ amax_v) {
+  constexpr int C8 = D / 8, RP = 256 / C8;
+  const int bh = blockIdx.y, t0 = blockIdx.x * kStatRows;
+  const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
+  const size_t base = (size_t)bh * N * D;
+  double sk[8] = {}, sq[8] = {};
+  uint32_t av[8] = {};
+  for (int r = t0 + r0; r < t0 + kStatRows && r < N; r += RP) {
+    float x[8];
+    load8<DT>(reinterpret_cast<const uint16_t*>(k) + base + (size_t)r * D + c0, x);
+#pragma unroll
+    for (int i = 0; i < 8; i++) sk[i] += (double)x[i];
+    if (SUMQ) {
+      load8<DT>(q + base + (size_t)r * D + c0, x);
+#pragma unroll
+      for (int i = 0; i < 8; i++) sq[i] += (double)x[i];
+    }
+    if (AMAXV) {
+      load8<DT>(v + base + (size_t)r * D + c0, x);
+#pragma unroll
+      for (int i = 0; i < 8; i++) av[i] = max(av[i], __float_as_uint(fabsf(x[i])));  // NaN-propagating
+    }
+  }
+  __shared__ double s_k[RP][D];
+  __shared__ double s_q[SUMQ ? RP : 1][D];
+  __shared__ uint32_t s_v[AMAXV ? RP : 1][D];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    s_k[r0][c0 + i] = sk[i];
+    if (SUMQ) s_q[r0][c0 + i] = sq[i];
+    if (AMAXV) s_v[r0][c0 + i] = av[i];
+  }
+  __syncthreads();
+  if (tid < D) {
+    double a = 0.0, b = 0.0;
+    uint32_t m = 0;
+    for (int r = 0; r < RP; r++) {
+      a += s_k[r][tid];
+      if (SUMQ) b += s_q[r][tid];
+      if (AMAXV) m = max(m, s_v[r][tid]);
+    }
+    atomicAdd(&sums[(size_t)bh * D + tid], a);
+    if (SUMQ) atomicAdd(&sums[(size_t)(BH + bh) * D + tid], b);
+    if (AMAXV) atomicMax(&amax_v[(size_t)bh * D + tid], m);
+  }
+}
+
+// Block-wide max of non-negative float bit patterns (NaN-propagating), 256 threads.
+__device__ __forceinline__ uint32_t block_umax(uint32_t x, uint32_t* red) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  x = max(max(red[0], red[1]), max(red[2], red[3]));
+  __syncthreads();
+  return x;
+}
+
+__device__ __forceinline__ int8_t int8_code(float x, float delta) {
+  if (delta == 0.0f) return 0;
+  float n = rintf(x / delta);             // correctly rounded fp32 division, then RNE
+  n = fminf(fmaxf(n, -127.0f), 127.0f);
+  return (int8_t)n;
+}
+
+// Writes this thread's 8 FP8 V codes of token row `rl` into the [D][64] LDS transpose tile.
+__device__ __forceinline__ void put_v_fp8(uint8_t* s_vt, int rl, int c0, const float* x, const float* dv) {
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    float a = dv[i] == 0.0f ? 0.0f : x[i] / dv[i];
+    float b = dv[i + 1] == 0.0f ? 0.0f : x[i + 1] / dv[i + 1];
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    s_vt[(c0 + i) * 64 + rl] = (uint8_t)(w & 0xff);
+    s_vt[(c0 + i + 1) * 64 + rl] = (uint8_t)((w >> 8) & 0xff);
+  }
+}
+
+// INT8 Q / K codes and FP8 V.  grid (Np/64, BH), 256 threads.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v, int N, int Np, float sm,
+                                                             QuantPtrs qp) {
+  constexpr int C8 = D / 8, RP = 256 / C8, NP = 64 / RP;
+  const int bh = blockIdx.y, blk = blockIdx.x, t0 = blk * 64;
+  const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
+  const size_t base = (size_t)bh * N * D;
+  __shared__ float s_mu[D];
+  __shared__ uint32_t s_red[4];
+  __shared__ __align__(16) uint8_t s_vt[D * 64];
+  if (tid < D) {
+    float mu = (float)(qp.sums[(size_t)bh * D + tid] / (double)N);
+    s_mu[tid] = mu;
+    if (blk == 0) qp.mu_k[(size_t)bh * D + tid] = mu;
+  }
+  __syncthreads();
+  float dv[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) dv[i] = __uint_as_float(qp.amax_v[(size_t)bh * D + c0 + i]) / 448.0f;
+  float xq[NP][8], xk[NP][8];
+  uint32_t aq = 0, ak = 0;
+#pragma unroll
+  for (int p = 0; p < NP; p++) {
+    const int rl = r0 + p * RP, row = t0 + rl;
+    if (row < N) {
+      float xv[8];
+      load8<DT>(q + base + (size_t)row * D + c0, xq[p]);
+      load8<DT>(k + base + (size_t)row * D + c0, xk[p]);
+      load8<DT>(v + base + (size_t)row * D + c0, xv);
+      put_v_fp8(s_vt, rl, c0, xv, dv);
+      float cs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        xk[p][i] = xk[p][i] - s_mu[c0 + i];
+        aq = max(aq, __float_as_uint(fabsf(xq[p][i])));
+        ak = max(ak, __float_as_uint(fabsf(xk[p][i])));
+        cs += xq[p][i] * s_mu[c0 + i];
+      }
+      // LSE correction: sm * q_t . mu_k (reduced over the C8 threads of this row)
+#pragma unroll
+      for (int o = 1; o < C8; o <<= 1) cs += __shfl_xor(cs, o);
+      if ((tid % C8) == 0) qp.lse_corr[(size_t)bh * N + row] = sm * cs;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        xq[p][i] = 0.0f;
+        xk[p][i] = 0.0f;
+        s_vt[(c0 + i) * 64 + rl] = 0;
+      }
+    }
+  }
+  const float dq = __uint_as_float(block_umax(aq, s_red)) / 127.0f;
+  const float dk = __uint_as_float(block_umax(ak, s_red)) / 127.0f;
+  if (tid == 0) {
+    reinterpret_cast<float*>(qp.q_scales)[(size_t)bh * (Np / 64) + blk] = dq;
+    reinterpret_cast<float*>(qp.k_scales)[(size_t)bh * (Np / 64) + blk] = dk;
+  }
+#pragma unroll
+  for (int p = 0; p < NP; p++) {
+    const int row = t0 + r0 + p * RP;
+    uint32_t wq[2] = {0, 0}, wk[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      wq[i / 4] |= (uint32_t)(uint8_t)int8_code(xq[p][i], dq) << (8 * (i % 4));
+      wk[i / 4] |= (uint32_t)(uint8_t)int8_code(xk[p][i], dk) << (8 * (i % 4));
+    }
+    const size_t off = ((size_t)bh * Np + row) * D + c0;
+    *reinterpret_cast<uint2*>(qp.q_codes + off) = make_uint2(wq[0], wq[1]);
+    *reinterpret_cast<uint2*>(qp.k_codes + off) = make_uint2(wk[0], wk[1]);
+  }
+  __syncthreads();
+  // V tile [D][64] -> v_codes[bh][blk][D][64], coalesced 16-byte stores
+  uint8_t* dst = qp.v_codes + ((size_t)bh * (Np / 64) + blk) * D * 64;
+  for (int c = tid; c < D * 4; c += 256)
+    *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(s_vt + c * 16);
+  if (blk == 0 && tid < D) reinterpret_cast<float*>(qp.v_scales)[(size_t)bh * D + tid] = __uint_as_float(qp.amax_v[(size_t)bh * D + tid]) / 448.0f;
+}
+
+// MXFP4 Q_s and K_s codes (32-channel blocks), dS and LSE correction; V in FP8
+// (PV == PV_FP8) or MXFP4 (32-token blocks per channel).  grid (Np/64, BH), 256 threads.
+template <int DT, int D, int PV>
+__global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v, int N, int Np, int BH, float sm,
+                                                          QuantPtrs qp) {
+  constexpr int C8 = D / 8, RP = 256 / C8, NP = 64 / RP;
+  const int bh = blockIdx.y, blk = blockIdx.x, t0 = blk * 64;
+  const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
+  const size_t base = (size_t)bh * N * D;
+  __shared__ float s_mk[D], s_mq[D];
+  __shared__ __align__(16) uint8_t s_vt[PV == PV_FP8 ? D * 64 : 1];
+  __shared__ float s_vf[PV == PV_MXFP4 ? 64 : 1][PV == PV_MXFP4 ? D + 1 : 1];
+  if (tid < D) {
+    float mk = (float)(qp.sums[(size_t)bh * D + tid] / (double)N);
+    float mq = (float)(qp.sums[(size_t)(BH + bh) * D + tid] / (double)N);
+    s_mk[tid] = mk;
+    s_mq[tid] = mq;
+    if (blk == 0) {
+      qp.mu_k[(size_t)bh * D + tid] = mk;
+      qp.mu_q[(size_t)bh * D + tid] = mq;
+    }
+  }
+  __syncthreads();
+  float dv[8];
+  if (PV == PV_FP8) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) dv[i] = __uint_as_float(qp.amax_v[(size_t)bh * D + c0 + i]) / 448.0f;
+  }
+  uint8_t* qe = reinterpret_cast<uint8_t*>(qp.q_scales);
+  uint8_t* ke = reinterpret_cast<uint8_t*>(qp.k_scales);
+#pragma unroll
+  for (int p = 0; p < NP; p++) {
+    const int rl = r0 + p * RP, row = t0 + rl;
+    float xq[8], xk[8], xv[8];
+    double ds = 0.0, cs = 0.0;
+    if (row < N) {
+      load8<DT>(q + base + (size_t)row * D + c0, xq);
+      load8<DT>(k + base + (size_t)row * D + c0, xk);
+      load8<DT>(v + base + (size_t)row * D + c0, xv);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        cs += (double)xq[i] * (double)s_mk[c0 + i];
+        xq[i] = xq[i] - s_mq[c0 + i];
+        xk[i] = xk[i] - s_mk[c0 + i];
+        ds += (double)s_mq[c0 + i] * (double)xk[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) xq[i] = xk[i] = xv[i] = 0.0f;
+    }
+    // one MX block = 32 channels = 4 neighbouring threads
+    uint32_t aq = 0, ak = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      aq = max(aq, __float_as_uint(fabsf(xq[i])));
+      ak = max(ak, __float_as_uint(fabsf(xk[i])));
+    }
+#pragma unroll
+    for (int o = 1; o < 4; o <<= 1) {
+      aq = max(aq, (uint32_t)__shfl_xor((int)aq, o));
+      ak = max(ak, (uint32_t)__shfl_xor((int)ak, o));
+    }
+    const unsigned bq = mx_fp4_scale_byte(__uint_as_float(aq)), bk = mx_fp4_scale_byte(__uint_as_float(ak));
+    const float sq = bq == 0 ? 1.0f : e8m0_to_float(bq), sk = bk == 0 ? 1.0f : e8m0_to_float(bk);
+    const size_t off = ((size_t)bh * Np + row) * (D / 2) + c0 / 2;
+    *reinterpret_cast<uint32_t*>(qp.q_codes + off) = pack_fp4x8(xq, sq);
+    *reinterpret_cast<uint32_t*>(qp.k_codes + off) = pack_fp4x8(xk, sk);
+    if ((c0 % 32) == 0) {
+      qe[((size_t)bh * Np + row) * (D / 32) + c0 / 32] = (uint8_t)bq;
+      ke[((size_t)bh * Np + row) * (D / 32) + c0 / 32] = (uint8_t)bk;
+    }
+#pragma unroll
+    for (int o = 1; o < C8; o <<= 1) {
+      ds += __shfl_xor(ds, o);
+      cs += __shfl_xor(cs, o);
+    }
+    if ((tid % C8) == 0) {
+      qp.delta_s[(size_t)bh * Np + row] = row < N ? (float)ds : 0.0f;
+      if (row < N) qp.lse_corr[(size_t)bh * N + row] = (float)(sm * cs);
+    }
+    if (PV == PV_FP8) {
+      if (row < N) {
+        put_v_fp8(s_vt, rl, c0, xv, dv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) s_vt[(c0 + i) * 64 + rl] = 0;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) s_vf[rl][c0 + i] = xv[i];
+    }
+  }
+  __syncthreads();
+  if (PV == PV_FP8) {
+    uint8_t* dst = qp.v_codes + ((size_t)bh * (Np / 64) + blk) * D * 64;
+    for (int c = tid; c < D * 4; c += 256)
+      *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(s_vt + c * 16);
+    if (blk == 0 && tid < D)
+      reinterpret_cast<float*>(qp.v_scales)[(size_t)bh * D + tid] = __uint_as_float(qp.amax_v[(size_t)bh * D + tid]) / 448.0f;
+  } else {
+    // one thread per (channel, 32-token group)
+    for (int w = tid; w < D * 2; w += 256) {
+      const int ch = w % D, g = w / D;
+      float x[32];
+      uint32_t a = 0;
+#pragma unroll
+      for (int i = 0; i < 32; i++) {
+        x[i] = s_vf[32 * g + i][ch];
+        a = max(a, __float_as_uint(fabsf(x[i])));
+      }
+      const unsigned b = mx_fp4_scale_byte(__uint_as_float(a));
+      const float sc = b == 0 ? 1.0f : e8m0_to_float(b);
+      uint4 pk;
+      pk.x = pack_fp4x8(x, sc);
+      pk.y = pack_fp4x8(x + 8, sc);
+      pk.z = pack_fp4x8(x + 16, sc);
+      pk.w = pack_fp4x8(x + 24, sc);
+      *reinterpret_cast<uint4*>(qp.v_codes + (((size_t)bh * (Np / 64) + blk) * D + ch) * 32 + 16 * g) = pk;
+      reinterpret_cast<uint8_t*>(qp.v_scales)[((size_t)bh * (Np / 32) + 2 * blk + g) * D + ch] = (uint8_t)b;
+    }
+  }
+}
+
+template <int DT, int D>
+static hipError_t prologue_dispatch(const void* q, const void* k, const void* v, const Shape& s, const QuantPtrs& qp,
+                                    hipStream_t st) {
+  const int BH = s.B * s.H;
+  const uint16_t *Q = (const uint16_t*)q, *K = (const uint16_t*)k, *V = (const uint16_t*)v;
+  const int nsum = 2 * BH * D, namax = BH * D;
+  zero_stats_kernel<<<(nsum + 255) / 256, 256, 0, st>>>(qp.sums, nsum, qp.amax_v, namax);
+  dim3 sg((s.N + kStatRows - 1) / kStatRows, BH), qg(s.Np / 64, BH);
+  const bool mx = s.qk_fmt == QK_MXFP4, fp8v = s.pv_fmt == PV_FP8;
+  if (!mx) {
+    stats_kernel<DT, D, false, true><<<sg, 256, 0, st>>>(Q, K, V, s.N, BH, qp.sums, qp.amax_v);
+    quant_int8_fp8_kernel<DT, D><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, s.sm_scale, qp);
+  } else if (fp8v) {
+    stats_kernel<DT, D, true, true><<<sg, 256, 0, st>>>(Q, K, V, s.N, BH, qp.sums, qp.amax_v);
+    quant_mxfp4_kernel<DT, D, PV_FP8><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BH, s.sm_scale, qp);
+  } else {
+    stats_kernel<DT, D, true, false><<<sg, 256, 0, st>>>(Q, K, V, s.N, BH, qp.sums, qp.amax_v);
+    quant_mxfp4_kernel<DT, D, PV_MXFP4><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BH, s.sm_scale, qp);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prologue(const void* q, const void* k, const void* v, const Shape& s, const QuantPtrs& qp,
+                           hipStream_t st) {
+  if (s.io_dtype == 0)
+    return s.d == 64 ? prologue_dispatch<0, 64>(q, k, v, s, qp, st) : prologue_dispatch<0, 128>(q, k, v, s, qp, st);
+  return s.d == 64 ? prologue_dispatch<1, 64>(q, k, v, s, qp, st) : prologue_dispatch<1, 128>(q, k, v, s, qp, st);
+}
+
+}  // namespace sage

@@ -1,0 +1,271 @@
+// sage_abi.cpp -- the C ABI (include/sage_attn.h): argument checks on the host,
+// quantized-buffer layout, dispatch to the HIP launchers, status and error text.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/sage_attn.h"
+#include "sage_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sage_status fail(sage_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+sage_status hip_fail(hipError_t e, const char* where) {
+  return fail(SAGE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Fault injection for host tests of the error paths (SAGE_FAULT_INJECT=alloc).
+bool inject_alloc_failure() {
+  const char* e = getenv("SAGE_FAULT_INJECT");
+  return e && strcmp(e, "alloc") == 0;
+}
+
+sage_status check_problem(const sage_problem* p) {
+  if (!p) return fail(SAGE_ERR_INVALID_ARG, "problem descriptor is NULL");
+  if (p->B < 1 || p->H < 1 || p->N < 1)
+    return fail(SAGE_ERR_INVALID_ARG, "B, H and N must be >= 1 (got B=%d H=%d N=%d)", p->B, p->H, p->N);
+  if ((long long)p->B * p->H * ((long long)p->N + sage::kTokenPad) * p->d > (1LL << 40))
+    return fail(SAGE_ERR_INVALID_ARG, "problem too large");
+  if (p->d != 64 && p->d != 128)
+    return fail(SAGE_ERR_UNSUPPORTED, "head dim d=%d is not supported (64 or 128)", p->d);
+  if (p->causal != 0 && p->causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!std::isfinite(p->sm_scale) || !(p->sm_scale > 0.0f))
+    return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  if (p->io_dtype != SAGE_DT_BF16 && p->io_dtype != SAGE_DT_F16)
+    return fail(SAGE_ERR_INVALID_ARG, "io_dtype %d is not a SAGE_DT_* value", p->io_dtype);
+  const bool fmts_known = (p->qk_fmt == SAGE_FMT_INT8 || p->qk_fmt == SAGE_FMT_FP8 || p->qk_fmt == SAGE_FMT_MXFP4) &&
+                          (p->pv_fmt == SAGE_FMT_INT8 || p->pv_fmt == SAGE_FMT_FP8 || p->pv_fmt == SAGE_FMT_MXFP4);
+  if (!fmts_known) return fail(SAGE_ERR_INVALID_ARG, "qk_fmt/pv_fmt must be SAGE_FMT_* values");
+  const bool pair_ok = (p->qk_fmt == SAGE_FMT_INT8 && p->pv_fmt == SAGE_FMT_FP8) ||
+                       (p->qk_fmt == SAGE_FMT_MXFP4 && p->pv_fmt == SAGE_FMT_FP8) ||
+                       (p->qk_fmt == SAGE_FMT_MXFP4 && p->pv_fmt == SAGE_FMT_MXFP4);
+  if (!pair_ok)
+    return fail(SAGE_ERR_UNSUPPORTED, "format pair (qk=%d, pv=%d) is not supported", p->qk_fmt, p->pv_fmt);
+  return SAGE_OK;
+}
+
+sage::Shape to_shape(const sage_problem* p) {
+  sage::Shape s;
+  s.B = p->B;
+  s.H = p->H;
+  s.N = p->N;
+  s.d = p->d;
+  s.Np = (int)round_up((size_t)p->N, sage::kTokenPad);
+  s.causal = p->causal;
+  s.io_dtype = p->io_dtype;
+  s.qk_fmt = p->qk_fmt;
+  s.pv_fmt = p->pv_fmt;
+  s.sm_scale = p->sm_scale;
+  return s;
+}
+
+void compute_layout(const sage_problem* p, sage_quant_layout* L) {
+  const size_t BH = (size_t)p->B * p->H, d = p->d, N = p->N;
+  const size_t Np = round_up(N, sage::kTokenPad), nb = Np / 64;
+  const bool mx = p->qk_fmt == SAGE_FMT_MXFP4, mxv = p->pv_fmt == SAGE_FMT_MXFP4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  L->mu_k = take(BH * d * 4);
+  L->mu_q = take(BH * d * 4);
+  L->q_codes = take(mx ? BH * Np * d / 2 : BH * Np * d);
+  L->q_scales = take(mx ? BH * Np * (d / 32) : BH * nb * 4);
+  L->k_codes = take(mx ? BH * Np * d / 2 : BH * Np * d);
+  L->k_scales = take(mx ? BH * Np * (d / 32) : BH * nb * 4);
+  L->v_codes = take(mxv ? BH * Np * d / 2 : BH * Np * d);
+  L->v_scales = take(mxv ? BH * (Np / 32) * d : BH * d * 4);
+  L->delta_s = take(BH * Np * 4);
+  L->lse_corr = take(BH * N * 4);
+  L->stats = take(BH * d * 8 * 2 + BH * d * 4);
+  L->total = off;
+}
+
+sage::QuantPtrs resolve(void* buf, const sage_problem* p, const sage_quant_layout& L) {
+  uint8_t* b = static_cast<uint8_t*>(buf);
+  const size_t BH = (size_t)p->B * p->H;
+  sage::QuantPtrs q;
+  q.mu_k = reinterpret_cast<float*>(b + L.mu_k);
+  q.mu_q = reinterpret_cast<float*>(b + L.mu_q);
+  q.q_codes = b + L.q_codes;
+  q.q_scales = b + L.q_scales;
+  q.k_codes = b + L.k_codes;
+  q.k_scales = b + L.k_scales;
+  q.v_codes = b + L.v_codes;
+  q.v_scales = b + L.v_scales;
+  q.delta_s = reinterpret_cast<float*>(b + L.delta_s);
+  q.lse_corr = reinterpret_cast<float*>(b + L.lse_corr);
+  q.sums = reinterpret_cast<double*>(b + L.stats);
+  q.amax_v = reinterpret_cast<uint32_t*>(b + L.stats + BH * p->d * 8 * 2);
+  return q;
+}
+
+sage_problem make_problem(int B, int H, int N, int d, int causal, float sm, int io, int qk, int pv) {
+  sage_problem p;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.d = d;
+  p.causal = causal;
+  p.sm_scale = sm;
+  p.io_dtype = io;
+  p.qk_fmt = qk;
+  p.pv_fmt = pv;
+  return p;
+}
+
+sage_status check_tensors(std::initializer_list<const void*> ptrs) {
+  for (const void* x : ptrs) {
+    if (!x) return fail(SAGE_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+    if (!aligned16(x)) return fail(SAGE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  }
+  return SAGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sage_abi_version(void) { return SAGE_ABI_VERSION; }
+
+const char* sage_last_error(void) { return g_err; }
+
+const char* sage_status_string(sage_status s) {
+  switch (s) {
+    case SAGE_OK: return "ok";
+    case SAGE_ERR_INVALID_ARG: return "invalid argument";
+    case SAGE_ERR_UNSUPPORTED: return "unsupported";
+    case SAGE_ERR_WORKSPACE: return "workspace too small";
+    case SAGE_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case SAGE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+sage_status sage_quant_size(const sage_problem* p, size_t* bytes, sage_quant_layout* layout) {
+  sage_status s = check_problem(p);
+  if (s != SAGE_OK) return s;
+  if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
+  sage_quant_layout L;
+  compute_layout(p, &L);
+  *bytes = L.total;
+  if (layout) *layout = L;
+  return SAGE_OK;
+}
+
+sage_status sage_quantize(const void* q, const void* k, const void* v, const sage_problem* p, void* quant_buf,
+                          size_t quant_bytes, void* stream) {
+  sage_status s = check_problem(p);
+  if (s != SAGE_OK) return s;
+  if ((s = check_tensors({q, k, v, quant_buf})) != SAGE_OK) return s;
+  sage_quant_layout L;
+  compute_layout(p, &L);
+  if (quant_bytes < L.total)
+    return fail(SAGE_ERR_WORKSPACE, "quant buffer has %zu bytes, needs %zu", quant_bytes, L.total);
+  hipError_t e = sage::launch_prologue(q, k, v, to_shape(p), resolve(quant_buf, p, L), (hipStream_t)stream);
+  return e == hipSuccess ? SAGE_OK : hip_fail(e, "quantize launch");
+}
+
+sage_status sage_attn_fwd_quantized(const void* quant_buf, size_t quant_bytes, const sage_problem* p, void* o,
+                                    float* lse, void* stream) {
+  sage_status s = check_problem(p);
+  if (s != SAGE_OK) return s;
+  if ((s = check_tensors({quant_buf, o})) != SAGE_OK) return s;
+  if (lse && !aligned16(lse)) return fail(SAGE_ERR_INVALID_ARG, "lse must be 16-byte aligned");
+  if (p->pv_fmt == SAGE_FMT_MXFP4)
+    return fail(SAGE_ERR_UNSUPPORTED, "MXFP4 P~V is not implemented by the fused kernel in this build");
+  sage_quant_layout L;
+  compute_layout(p, &L);
+  if (quant_bytes < L.total)
+    return fail(SAGE_ERR_WORKSPACE, "quant buffer has %zu bytes, needs %zu", quant_bytes, L.total);
+  hipError_t e = sage::launch_attn_fwd(to_shape(p), resolve(const_cast<void*>(quant_buf), p, L), o, lse,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? SAGE_OK : hip_fail(e, "attention launch");
+}
+
+sage_status sage_attn_fwd_ws_size(const sage_problem* p, size_t* bytes) { return sage_quant_size(p, bytes, nullptr); }
+
+sage_status sage_attn_fwd_ex(const sage_problem* p, const void* q, const void* k, const void* v, void* o, float* lse,
+                             void* ws, size_t ws_bytes, void* stream) {
+  sage_status s = check_problem(p);
+  if (s != SAGE_OK) return s;
+  if ((s = check_tensors({q, k, v, o, ws})) != SAGE_OK) return s;
+  if (lse && !aligned16(lse)) return fail(SAGE_ERR_INVALID_ARG, "lse must be 16-byte aligned");
+  if (p->pv_fmt == SAGE_FMT_MXFP4)
+    return fail(SAGE_ERR_UNSUPPORTED, "MXFP4 P~V is not implemented by the fused kernel in this build");
+  sage_quant_layout L;
+  compute_layout(p, &L);
+  if (ws_bytes < L.total) return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  const sage::Shape sh = to_shape(p);
+  const sage::QuantPtrs qp = resolve(ws, p, L);
+  hipError_t e = sage::launch_prologue(q, k, v, sh, qp, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  e = sage::launch_attn_fwd(sh, qp, o, lse, (hipStream_t)stream);
+  return e == hipSuccess ? SAGE_OK : hip_fail(e, "attention launch");
+}
+
+sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int causal,
+                          float sm_scale, int qk_fmt, int pv_fmt, void* stream) {
+  sage_problem p = make_problem(B, H, N, d, causal, sm_scale, SAGE_DT_BF16, qk_fmt, pv_fmt);
+  sage_status s = check_problem(&p);
+  if (s != SAGE_OK) return s;
+  if ((s = check_tensors({q, k, v, o})) != SAGE_OK) return s;
+  if (p.pv_fmt == SAGE_FMT_MXFP4)
+    return fail(SAGE_ERR_UNSUPPORTED, "MXFP4 P~V is not implemented by the fused kernel in this build");
+  size_t bytes = 0;
+  sage_quant_size(&p, &bytes, nullptr);
+  void* ws = nullptr;
+  if (inject_alloc_failure()) return fail(SAGE_ERR_OUT_OF_MEMORY, "injected allocation failure");
+  hipError_t e = hipMallocAsync(&ws, bytes, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SAGE_ERR_OUT_OF_MEMORY, "hipMallocAsync(%zu): %s", bytes, hipGetErrorString(e));
+  }
+  s = sage_attn_fwd_ex(&p, q, k, v, o, nullptr, ws, bytes, stream);
+  hipError_t f = hipFreeAsync(ws, (hipStream_t)stream);
+  if (s == SAGE_OK && f != hipSuccess) return hip_fail(f, "hipFreeAsync");
+  return s;
+}
+
+sage_status sage_attn_bwd_ws_size(const sage_problem* p, size_t* bytes) {
+  sage_status s = check_problem(p);
+  if (s != SAGE_OK) return s;
+  if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
+  if (p->qk_fmt != SAGE_FMT_INT8 || p->pv_fmt != SAGE_FMT_FP8)
+    return fail(SAGE_ERR_UNSUPPORTED, "the backward supports qk_fmt=INT8, pv_fmt=FP8 only");
+  *bytes = sage::attn_bwd_ws_bytes(to_shape(p));
+  return SAGE_OK;
+}
+
+sage_status sage_attn_bwd(const sage_problem* p, const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                          void* stream) {
+  size_t need = 0;
+  sage_status s = sage_attn_bwd_ws_size(p, &need);
+  if (s != SAGE_OK) return s;
+  if ((s = check_tensors({q, k, v, o, dout, lse, dq, dk, dv, ws})) != SAGE_OK) return s;
+  if (ws_bytes < need) return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  hipError_t e = sage::launch_attn_bwd(to_shape(p), q, k, v, o, dout, lse, dq, dk, dv, ws, (hipStream_t)stream);
+  return e == hipSuccess ? SAGE_OK : hip_fail(e, "backward launch");
+}
+
+}  // extern "C"

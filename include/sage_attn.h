@@ -1,0 +1,154 @@
+/*
+ * sage_attn.h -- C ABI of an MI355X (gfx950) library for SageAttention-style
+ * quantized attention: O = softmax(sm_scale * Q K^T + mask) V computed tile by
+ * tile with online softmax, after mean-smoothing of K (and of Q on the 4-bit
+ * path) and per-block low-bit quantization of Q and K; P and V are quantized
+ * for the PV product; an 8-bit backward produces dQ, dK, dV.
+ *
+ * Sources of the operation (web pages on SageAttention):
+ *   - the problem is plug-and-play attention on q, k, v with a causal flag
+ *     (SageAttention3 abstract; "compatible with FlashAttention" in the
+ *     SageAttention contributions, reply to reviewer wwcu W1);
+ *   - online softmax and FlashAttention tiling (SageAttention review thread,
+ *     reply to reviewer xY6z Q3; deferred normalisation, reply to xY6z Q2);
+ *   - smoothing K, INT8 QK^T, per-block granularity (reply to wwcu W1;
+ *     SageAttn-B, reply to xY6z W1-(2), Q1);
+ *   - P~ and V in FP8, smoothing Q, two-level P~V accumulation (SageAttention2
+ *     abstract); microscaling FP4 attention and 8-bit forward + backward
+ *     (SageAttention3 abstract).
+ *
+ * Conventions for every entry point:
+ *   - Tensors are contiguous [B, H, N, d] (token-major per head), d in {64,128},
+ *     N >= 1 (queries and keys share N), all device pointers 16-byte aligned.
+ *   - Causal masking is top-left aligned: query i sees keys j <= i.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *     asynchronous on that stream; the caller synchronizes.
+ *   - The caller owns every buffer it passes; the library keeps no pointer
+ *     past the call.
+ *   - All argument checks run on the host before anything is launched.  On an
+ *     error nothing is launched, outputs are untouched, and sage_last_error()
+ *     (thread-local) describes the problem.  Device faults surface at the
+ *     caller's next synchronization.  No C++ exception crosses this boundary.
+ *   - NaN or Inf inputs are not errors; they propagate into the affected
+ *     scales and rows.
+ */
+#ifndef SAGE_ATTN_H
+#define SAGE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_ABI_VERSION 1
+
+typedef enum {
+    SAGE_OK = 0,
+    SAGE_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad scale, misaligned pointer */
+    SAGE_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement (d, format pair) */
+    SAGE_ERR_WORKSPACE = 3,     /* workspace or quant buffer smaller than required */
+    SAGE_ERR_OUT_OF_MEMORY = 4, /* internal device allocation failed */
+    SAGE_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
+} sage_status;
+
+/* Element formats.  INT8: symmetric +-127 codes with one fp32 step per 64-token
+ * block.  FP8: OCP E4M3FN.  MXFP4: OCP MX, E2M1 elements in 32-element blocks
+ * sharing an E8M0 (power-of-two) scale. */
+enum { SAGE_FMT_INT8 = 1, SAGE_FMT_FP8 = 2, SAGE_FMT_MXFP4 = 3 };
+
+/* I/O element types of Q, K, V, O, dO, dQ, dK, dV. */
+enum { SAGE_DT_BF16 = 0, SAGE_DT_F16 = 1 };
+
+/* Supported (qk_fmt, pv_fmt) pairs: (INT8, FP8), (MXFP4, FP8), (MXFP4, MXFP4). */
+typedef struct {
+    int B, H, N, d;
+    int causal;          /* 0 or 1 */
+    float sm_scale;      /* finite, > 0; typically 1/sqrt(d) */
+    int io_dtype;        /* SAGE_DT_* */
+    int qk_fmt, pv_fmt;  /* SAGE_FMT_* */
+} sage_problem;
+
+/*
+ * Byte offsets of each part inside a quantized buffer (see sage_quantize).
+ * Let BH = B*H, Np = N rounded up to a multiple of 128 (padding tokens carry
+ * zero codes), nb = Np/64.
+ *   mu_k      fp32 [BH, d]     channel mean of K over all N tokens
+ *   mu_q      fp32 [BH, d]     channel mean of Q (MXFP4 QK only)
+ *   q_codes   INT8: int8 [BH, Np, d];  MXFP4: packed E2M1 [BH, Np, d/2] of
+ *             Q - mu_q, element 2i in the low nibble of byte i
+ *   q_scales  INT8: fp32 [BH, nb] step of each 64-token block;
+ *             MXFP4: E8M0 bytes [BH, Np, d/32] per token per 32 channels
+ *   k_codes, k_scales   the same for K - mu_k
+ *   v_codes   FP8 V: E4M3 codes tiled [BH, Np/64, d, 64] (64 tokens of one
+ *             channel contiguous);  MXFP4 V: packed E2M1 [BH, Np/64, d, 32]
+ *   v_scales  FP8 V: fp32 [BH, d] per-channel step;  MXFP4 V: E8M0 bytes
+ *             [BH, Np/32, d] per 32-token group per channel
+ *   delta_s   fp32 [BH, Np]    mu_q . (k_t - mu_k), added to every score (MXFP4 QK)
+ *   lse_corr  fp32 [BH, N]     sm_scale * q_t . mu_k, added to the LSE only
+ *   stats     fp64 / uint32 scratch of the smoothing reduction
+ */
+typedef struct {
+    size_t mu_k, mu_q, q_codes, q_scales, k_codes, k_scales, v_codes, v_scales,
+           delta_s, lse_corr, stats, total;
+} sage_quant_layout;
+
+/*
+ * Forward attention, bf16 I/O, the one-call form.  q, k, v: device [B,H,N,d];
+ * o: device output [B,H,N,d].  qk_fmt/pv_fmt as above.  Takes its scratch with
+ * hipMallocAsync / hipFreeAsync on `stream` (stream-ordered).
+ */
+sage_status sage_attn_fwd(const void *q, const void *k, const void *v, void *o,
+                          int B, int H, int N, int d, int causal, float sm_scale,
+                          int qk_fmt, int pv_fmt, void *stream);
+
+/* Size and layout of the quantized buffer for `p`. */
+sage_status sage_quant_size(const sage_problem *p, size_t *bytes, sage_quant_layout *layout);
+
+/*
+ * Smoothing + quantization prologue: reads q, k, v (device [B,H,N,d] in
+ * p->io_dtype) and writes the codes, scales and correction terms into
+ * quant_buf (device, quant_bytes >= sage_quant_size's bytes), laid out as
+ * sage_quant_layout describes.
+ */
+sage_status sage_quantize(const void *q, const void *k, const void *v, const sage_problem *p,
+                          void *quant_buf, size_t quant_bytes, void *stream);
+
+/*
+ * Fused attention on a buffer written by sage_quantize for the same problem:
+ * o device [B,H,N,d] in p->io_dtype; lse device fp32 [B,H,N] or NULL
+ * (natural-log log-sum-exp of the true, unsmoothed scaled scores).
+ */
+sage_status sage_attn_fwd_quantized(const void *quant_buf, size_t quant_bytes, const sage_problem *p,
+                                    void *o, float *lse, void *stream);
+
+/* Workspace bytes needed by sage_attn_fwd_ex (the quantized buffer). */
+sage_status sage_attn_fwd_ws_size(const sage_problem *p, size_t *bytes);
+
+/* Forward with caller workspace: quantize into ws, then the fused kernel.  lse may be NULL. */
+sage_status sage_attn_fwd_ex(const sage_problem *p, const void *q, const void *k, const void *v,
+                             void *o, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes needed by sage_attn_bwd. */
+sage_status sage_attn_bwd_ws_size(const sage_problem *p, size_t *bytes);
+
+/*
+ * 8-bit backward.  q, k, v, o, dout: device [B,H,N,d] (bf16 or fp16 as
+ * p->io_dtype; o is the forward output); lse: device fp32 [B,H,N] from the
+ * forward; dq, dk, dv: device outputs [B,H,N,d].  p->qk_fmt must be INT8 and
+ * p->pv_fmt FP8.  ws: device workspace of at least sage_attn_bwd_ws_size bytes.
+ */
+sage_status sage_attn_bwd(const sage_problem *p, const void *q, const void *k, const void *v,
+                          const void *o, const void *dout, const float *lse,
+                          void *dq, void *dk, void *dv, void *ws, size_t ws_bytes, void *stream);
+
+const char *sage_status_string(sage_status s);
+const char *sage_last_error(void);
+int sage_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_ATTN_H */

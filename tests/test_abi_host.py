@@ -1,0 +1,109 @@
+"""Host-side tests of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_attention_smooth_amd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x100000)        # aligned, never dereferenced: validation fails or injects first
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "sage_attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = S.lib()
+    declared = _declared()
+    assert declared, "no declarations parsed"
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(S.EXPORTS) == declared
+    assert L.sage_abi_version() == 1
+
+
+def _p(**kw):
+    base = dict(B=1, H=2, N=100, d=128, causal=0, sm_scale=0.125, io_dtype=0, qk_fmt=1, pv_fmt=2)
+    base.update(kw)
+    return S.Problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), S.ERR_INVALID_ARG), (dict(N=0), S.ERR_INVALID_ARG), (dict(H=-1), S.ERR_INVALID_ARG),
+    (dict(d=96), S.ERR_UNSUPPORTED), (dict(d=256), S.ERR_UNSUPPORTED),
+    (dict(sm_scale=0.0), S.ERR_INVALID_ARG), (dict(sm_scale=float("nan")), S.ERR_INVALID_ARG),
+    (dict(sm_scale=float("inf")), S.ERR_INVALID_ARG), (dict(causal=2), S.ERR_INVALID_ARG),
+    (dict(io_dtype=7), S.ERR_INVALID_ARG), (dict(qk_fmt=9), S.ERR_INVALID_ARG),
+    (dict(qk_fmt=2, pv_fmt=2), S.ERR_UNSUPPORTED), (dict(qk_fmt=1, pv_fmt=3), S.ERR_UNSUPPORTED),
+])
+def test_problem_validation(kw, status):
+    L = S.lib()
+    n = ctypes.c_size_t(12345)
+    assert L.sage_quant_size(ctypes.byref(_p(**kw)), ctypes.byref(n), None) == status
+    assert n.value == 12345                       # output untouched on error
+    assert L.sage_last_error()                    # message set
+    st = L.sage_quantize(FAKE, FAKE, FAKE, ctypes.byref(_p(**kw)), FAKE, 1 << 40, None)
+    assert st == status
+
+
+def test_null_and_misaligned_pointers_rejected():
+    L = S.lib()
+    p = _p()
+    assert L.sage_quantize(None, FAKE, FAKE, ctypes.byref(p), FAKE, 1 << 40, None) == S.ERR_INVALID_ARG
+    assert L.sage_quantize(FAKE, FAKE, ctypes.c_void_p(0x100004), ctypes.byref(p), FAKE, 1 << 40, None) == S.ERR_INVALID_ARG
+    assert L.sage_attn_fwd_quantized(FAKE, 1 << 40, ctypes.byref(p), None, None, None) == S.ERR_INVALID_ARG
+    assert L.sage_attn_fwd(FAKE, FAKE, FAKE, None, 1, 2, 64, 128, 0, 0.1, 1, 2, None) == S.ERR_INVALID_ARG
+    assert L.sage_quant_size(None, None, None) == S.ERR_INVALID_ARG
+
+
+def test_workspace_too_small_rejected():
+    L = S.lib()
+    p = _p()
+    need, _ = S.quant_size(p)
+    assert L.sage_quantize(FAKE, FAKE, FAKE, ctypes.byref(p), FAKE, need - 1, None) == S.ERR_WORKSPACE
+    assert L.sage_attn_fwd_ex(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 1, None) == S.ERR_WORKSPACE
+    assert L.sage_attn_fwd_quantized(FAKE, need - 1, ctypes.byref(p), FAKE, None, None) == S.ERR_WORKSPACE
+    assert b"needs" in L.sage_last_error()
+
+
+def test_quant_layout_sizes():
+    """Offsets are 256-byte aligned, ordered, and each part has the documented size."""
+    for qk, pv in ((1, 2), (3, 2), (3, 3)):
+        for N in (1, 100, 4096):
+            p = _p(N=N, qk_fmt=qk, pv_fmt=pv)
+            total, lay = S.quant_size(p)
+            BH, d, Np = 2, 128, (N + 127) // 128 * 128
+            offs = [lay[k] for k in ("mu_k", "mu_q", "q_codes", "q_scales", "k_codes", "k_scales",
+                                     "v_codes", "v_scales", "delta_s", "lse_corr", "stats")]
+            assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+            codes = BH * Np * d // (2 if qk == 3 else 1)
+            assert lay["q_scales"] - lay["q_codes"] >= codes
+            assert lay["v_scales"] - lay["v_codes"] >= BH * Np * d // (2 if pv == 3 else 1)
+            assert total >= lay["stats"] + BH * d * 20
+
+
+def test_injected_allocation_failure(monkeypatch):
+    L = S.lib()
+    monkeypatch.setenv("SAGE_FAULT_INJECT", "alloc")
+    st = L.sage_attn_fwd(FAKE, FAKE, FAKE, FAKE, 1, 2, 64, 128, 0, 0.1, 1, 2, None)
+    assert st == S.ERR_OUT_OF_MEMORY
+    assert b"injected" in L.sage_last_error()
+
+
+def test_status_strings():
+    L = S.lib()
+    for s in range(6):
+        assert L.sage_status_string(s)
+    assert L.sage_status_string(99) == b"unknown status"
+
+
+def test_backward_rejects_non_int8_formats():
+    L = S.lib()
+    n = ctypes.c_size_t()
+    assert L.sage_attn_bwd_ws_size(ctypes.byref(_p(qk_fmt=3, pv_fmt=2)), ctypes.byref(n)) == S.ERR_UNSUPPORTED

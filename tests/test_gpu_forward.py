@@ -1,0 +1,206 @@
+"""GPU parity of the smoothing/quantization prologue and the fused forward
+against the CPU oracle: codes and scales bit-exact; O within max-abs 2e-2 and
+cosine >= 0.9999 of the oracle's simulation of the same quantization; cosine
+>= 0.99 (INT8 QK) / 0.98 (MXFP4 QK) against exact fp64 attention."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import banner, cos, device, sample_rows, to_np64, unpack_int8_fp8, unpack_mxfp4
+
+pytestmark = pytest.mark.gpu
+
+TILE = 64          # the fused kernel's K tile (the simulation must use the same tiling)
+
+
+@pytest.fixture(scope="module")
+def sage():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_attention_smooth_amd as S
+    S.lib()
+    return S
+
+
+def _inputs(B, H, N, d, dtype, seed, k_off=0.0, outliers=0.0, causal=False):
+    from bit_quantized_attention_smooth_amd.workloads import make_inputs, as_u16
+    import oracle
+    x = make_inputs(B, H, N, d, dtype=dtype, seed=seed, k_off_std=k_off, outlier_frac=outliers)
+    f = {n: oracle.widen(as_u16(x[n]), dtype).reshape(B * H, N, d) for n in "qkv"}
+    g = {n: x[n].to(device()) for n in "qkv"}
+    return f, g
+
+
+CASES = [
+    # name, B, H, N, d, dtype, causal, qk, pv, seed, k_off, outliers, sm
+    ("int8_b1h2n256d64_f16", 1, 2, 256, 64, "f16", False, "int8", "fp8", 0, 4.0, 0.0, 1 / 8),
+    ("int8_causal_ragged_d128", 1, 3, 1000, 128, "bf16", True, "int8", "fp8", 1, 5.0, 0.01, 1 / math.sqrt(128)),
+    ("int8_ragged_d64", 2, 2, 777, 64, "bf16", False, "int8", "fp8", 2, 3.0, 0.0, 1 / 8),
+    ("int8_causal_d64_f16", 1, 2, 300, 64, "f16", True, "int8", "fp8", 5, 2.0, 0.0, 1 / 8),
+    ("mxfp4_fp8_d128", 1, 3, 600, 128, "bf16", False, "mxfp4", "fp8", 3, 5.0, 0.0, 1 / math.sqrt(128)),
+    ("mxfp4_fp8_causal_d64", 1, 2, 333, 64, "bf16", True, "mxfp4", "fp8", 6, 5.0, 0.0, 1 / 8),
+]
+
+
+def _oracle_sim(f, qz_or, qk, pv, N, d, causal, sm, rows=None):
+    import oracle
+    if qk == "int8":
+        return oracle.attn_int8_fp8(qz_or, N, d, causal, sm, TILE, rows=rows)
+    return oracle.attn_mxfp4(qz_or, N, d, causal, sm, TILE, rows=rows)
+
+
+def _check_codes(r, qz, qk, pv):
+    if qk == "int8":
+        assert np.array_equal(r["mu_k"], qz["mu_k"])
+        assert np.array_equal(r["qs"], qz["qs"]) and np.array_equal(r["ks"], qz["ks"])
+        assert np.array_equal(r["qc"], qz["qc"]) and np.array_equal(r["kc"], qz["kc"])
+        assert not r["qc_all"][:, qz["qc"].shape[1]:].any() and not r["kc_all"][:, qz["kc"].shape[1]:].any()
+    else:
+        assert np.array_equal(r["mu_k"], qz["mu_k"]) and np.array_equal(r["mu_q"], qz["mu_q"])
+        assert np.array_equal(r["qe"], qz["qe"]) and np.array_equal(r["ke"], qz["ke"])
+        assert np.array_equal(r["qc"], qz["qc"]) and np.array_equal(r["kc"], qz["kc"])
+        assert np.allclose(r["dS"], qz["dS"], rtol=1e-6, atol=1e-6 * np.abs(qz["dS"]).max())
+    if pv == "fp8":
+        assert np.array_equal(r["vs"], qz["vs"])
+        assert np.array_equal(r["vc"], qz["vc"])
+    else:
+        assert np.array_equal(r["ve"], qz["ve"]) and np.array_equal(r["vc"], qz["vc"])
+    assert np.allclose(r["corr"], qz["corr"], rtol=1e-5, atol=1e-5 * (np.abs(qz["corr"]).max() + 1))
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prologue_codes_bit_exact(sage, case):
+    import oracle
+    name, B, H, N, d, dt, causal, qk, pv, seed, koff, outl, sm = case
+    banner(f"prologue {name}")
+    f, g = _inputs(B, H, N, d, dt, seed, koff, outl)
+    buf, p, lay = sage.quantize(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv)
+    torch.cuda.synchronize()
+    if qk == "int8":
+        r = unpack_int8_fp8(buf, p, lay)
+        qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm)
+    else:
+        r = unpack_mxfp4(buf, p, lay, pv)
+        qz = oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
+    _check_codes(r, qz, qk, pv)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_forward_matches_oracle(sage, case):
+    import oracle
+    name, B, H, N, d, dt, causal, qk, pv, seed, koff, outl, sm = case
+    banner(f"forward {name}")
+    f, g = _inputs(B, H, N, d, dt, seed, koff, outl)
+    o, lse = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv, return_lse=True)
+    torch.cuda.synchronize()
+    o = to_np64(o).reshape(B * H, N, d)
+    lse = lse.cpu().numpy().reshape(B * H, N).astype(np.float64)
+    qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm) if qk == "int8" else \
+        oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
+    o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
+    o_ref, lse_ref = oracle.attn_ref(f["q"], f["k"], f["v"], causal, sm)
+    assert np.abs(o - o_sim).max() <= 2e-2
+    assert cos(o, o_sim) >= 0.9999
+    assert cos(o, o_ref) >= (0.99 if qk == "int8" else 0.98)
+    assert np.allclose(lse, lse_sim, rtol=1e-4, atol=2e-3)
+
+
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 127, 129])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_edge_lengths(sage, N, causal):
+    import oracle
+    banner(f"edge N={N} causal={causal}")
+    for qk, d in (("int8", 64), ("int8", 128), ("mxfp4", 128)):
+        f, g = _inputs(1, 2, N, d, "bf16", 100 + N, 2.0)
+        sm = 1 / math.sqrt(d)
+        o, lse = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, return_lse=True)
+        torch.cuda.synchronize()
+        o = to_np64(o).reshape(2, N, d)
+        qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm) if qk == "int8" else \
+            oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt="fp8")
+        o_sim, lse_sim = _oracle_sim(f, qz, qk, "fp8", N, d, causal, sm)
+        assert np.abs(o - o_sim).max() <= 2e-2, (qk, d)
+        if N > 1:
+            assert cos(o, o_sim) >= 0.9999, (qk, d)
+        else:
+            # one key: O is the dequantized V row
+            assert np.allclose(o, o_sim, atol=2e-2)
+        assert np.allclose(lse.cpu().numpy().reshape(2, N), lse_sim, rtol=1e-4, atol=2e-3)
+
+
+@pytest.mark.parametrize("qk", ["int8", "mxfp4"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_constant_keys_closed_form(sage, qk, causal):
+    """K constant along tokens: every score is 0, so O_i is the mean (prefix mean if
+    causal) of the FP8-dequantized V rows -- exact up to the output rounding."""
+    import oracle
+    banner(f"constant keys {qk} causal={causal}")
+    B, H, N, d = 1, 2, 200, 128
+    f, g = _inputs(B, H, N, d, "bf16", 7)
+    g["k"] = g["k"][:, :, :1].expand(-1, -1, N, -1).contiguous()
+    f["k"] = np.repeat(f["k"][:, :1], N, axis=1)
+    o = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, qk_fmt=qk)
+    torch.cuda.synchronize()
+    o = to_np64(o).reshape(B * H, N, d)
+    qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], 0.1)
+    vdq = oracle.e4m3_decode(qz["vc"]) * qz["vs"][:, None, :].astype(np.float64)
+    want = np.cumsum(vdq, axis=1) / np.arange(1, N + 1)[None, :, None] if causal else \
+        np.broadcast_to(vdq.mean(axis=1, keepdims=True), vdq.shape)
+    # bf16 output rounding: half an ulp of |O| <= 2^-9 relative
+    assert np.all(np.abs(o - want) <= np.abs(want) * 2.0 ** -8 + 1e-6)
+
+
+FULL = ["int8_fp8_causal_b1h32n4096d128", "int8_fp8_b2h24n16384d64", "mxfp4_b4h32n8192d128",
+        "int8_fp8_b1h2n256d64"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_rows(sage, name):
+    """The named workloads at full size in the benchmark's launch configuration; the
+    oracle recomputes sampled rows of a few heads."""
+    import oracle
+    from bit_quantized_attention_smooth_amd.workloads import workload_inputs, as_u16
+    banner(f"full size {name}")
+    x, w = workload_inputs(name)
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    qk, sm, causal = w["qk_fmt"], w["sm_scale"], w["causal"]
+    pv = "fp8"
+    g = {n: x[n].to(device()) for n in "qkv"}
+    buf, p, lay = sage.quantize(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv)
+    o, lse = sage.attn_fwd_quantized(buf, p, dtype=g["q"].dtype, return_lse=True)
+    torch.cuda.synchronize()
+    heads = sorted({0, B * H // 2, B * H - 1})
+    sel = lambda t: t.reshape(B * H, N, d)[heads]
+    f = {n: oracle.widen(as_u16(sel(x[n])), w["dtype"]).reshape(len(heads), N, d) for n in "qkv"}
+    rows = sample_rows(N)
+    if qk == "int8":
+        qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm)
+        r = unpack_int8_fp8(buf, p, lay)
+        for key in ("qc", "kc", "vc", "qs", "ks", "vs", "mu_k"):
+            assert np.array_equal(r[key][heads], qz[key]), key
+    else:
+        qz = oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
+        r = unpack_mxfp4(buf, p, lay, pv)
+        for key in ("qc", "kc", "qe", "ke", "vc", "vs", "mu_k", "mu_q"):
+            assert np.array_equal(r[key][heads], qz[key]), key
+    o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm, rows=rows)
+    o_ref, _ = oracle.attn_ref(f["q"], f["k"], f["v"], causal, sm, rows=rows)
+    og = to_np64(o).reshape(B * H, N, d)[heads][:, rows]
+    lg = lse.cpu().numpy().reshape(B * H, N)[heads][:, rows]
+    assert np.abs(og - o_sim).max() <= 2e-2
+    assert cos(og, o_sim) >= 0.9999
+    assert cos(og, o_ref) >= (0.99 if qk == "int8" else 0.98)
+    assert np.allclose(lg, lse_sim, rtol=1e-4, atol=2e-3)
+    # every output finite at full size
+    assert torch.isfinite(o).all()
+
+
+def test_oneshot_entry_matches_ex(sage):
+    banner("one-call entry vs workspace entry")
+    f, g = _inputs(1, 4, 512, 128, "bf16", 11, 5.0)
+    a = sage.attn_fwd_oneshot(g["q"], g["k"], g["v"], causal=True)
+    b = sage.sageattn(g["q"], g["k"], g["v"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
