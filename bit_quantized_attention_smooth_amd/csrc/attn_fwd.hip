@@ -1,7 +1,7 @@
 // attn_fwd.hip -- fused quantized attention forward for gfx950.
 //
-// FlashAttention-style: one workgroup owns a 128-query tile of one (b,h) head
-// and streams 64-key tiles of K and V codes through LDS; per tile it forms the
+// FlashAttention-style: a workgroup owns a 128-query tile of one (b,h) head and
+// streams 64-key tiles of K and V codes through LDS; per tile it forms the
 // score tile with MFMA, applies the online-softmax update (running max m and
 // row sum l, rescale of the running output by exp(m_old - m_new)), quantizes
 // P to FP8 and accumulates P~V with MFMA; normalisation by l happens once,
@@ -11,26 +11,32 @@
 // FP4 (SageAttention3 abstract); P~ and V are FP8 (SageAttention2 abstract).
 //
 // Dequantization is folded into the softmax: t = S_int * (dQ_row * dK_tile *
-// sm * log2 e) for INT8, t = (S + dS_key) * sm * log2 e for MXFP4, and
-// p~ = E4M3(exp2(t - m + log2 448)) = E4M3(448 p).  l accumulates the
-// unquantized 448 p and the epilogue divides by it and multiplies by the
-// per-channel V step.
+// sm * log2 e) for INT8, t = S * sm * log2 e + dS_key * sm * log2 e for MXFP4,
+// and p~ = E4M3(exp2(t - m + log2 448)) = E4M3(448 p).  l accumulates the
+// unquantized 448 p; the epilogue divides by it and applies the per-channel V
+// step.
 //
 // Two-level P~V accumulation (SageAttention2 abstract): the pages accumulate
 // each tile's P~V in the matrix unit and add it to an fp32 running output.  On
 // gfx950 the FP8 MFMA rounds only inside each group of 8 products and adds the
 // group sums into its fp32 C operand at full fp32 precision, so the running O
-// is kept directly as the MFMA accumulator (rescaled by alpha before each tile):
-// the second level is the accumulator itself.
+// is kept directly as the MFMA accumulator (rescaled by alpha before a tile's
+// product is added): the second level is the accumulator itself.
 //
 // Layout per wave (4 waves, 32 queries each).  The QK MFMA computes
 // S^T = K Q^T: A rows are keys, B columns are the wave's 32 queries, so lane l
 // owns query l%32 and, across the two 32-key subtiles, the 32 keys
 // 32*(l/32) + [0, 32) of the 64-key tile (A rows are fed in the permuted key
-// order pi_s(m) that makes this true).  Row max and row sum are therefore
+// order key_perm(m, s) that makes this true).  Row max and row sum are
 // in-lane plus one exchange between wave halves, and the lane's 32 P~ bytes
 // are already the B operand of the PV MFMA O^T = V^T P~^T (A = V^T, rows =
 // channels, K = the same 32 keys).
+//
+// Pipeline: the QK MFMAs of tile j+1 are issued before the softmax of tile j,
+// so the matrix unit works while the vector unit runs the softmax; K runs one
+// tile ahead of V through two LDS buffers each, with one barrier per tile.
+// Causal: each workgroup takes a heavy and a light query tile (qt, nqt-1-qt),
+// so all workgroups carry the same number of key tiles.
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
 
@@ -47,101 +53,263 @@ struct FwdArgs {
   const float* lse_corr;
   void* o;
   float* lse;
-  int N, Np;
+  int N, Np, BH;
   float sm_log2e;
 };
 
 constexpr int kTK = 64;      // keys per tile (= the INT8 K block)
-constexpr int kQT = 128;     // queries per workgroup
+constexpr int kQT = 128;     // queries per workgroup pass
 
 template <int D, int QK>
-struct TileGeom {
-  static constexpr int KROW = QK == QK_INT8 ? D : D / 2;   // bytes per key row
-  static constexpr int KCH = KROW / 16;                      // 16-byte chunks per key row
+struct Geo {
+  static constexpr int KROW = QK == QK_INT8 ? D : D / 2;               // bytes per key row
+  static constexpr int KCH = KROW / 16;                                 // 16-byte chunks per key row
   static constexpr int KBYTES = kTK * KROW;
-  static constexpr int SBYTES = QK == QK_MXFP4 ? kTK * (D / 32) : 0;   // E8M0 bytes per tile
-  static constexpr int DSBYTES = QK == QK_MXFP4 ? kTK * 4 : 0;         // dS floats per tile
-  static constexpr int VBYTES = D * kTK;                               // FP8 V^T tile
-  static constexpr int STAGE = KBYTES + SBYTES + DSBYTES + VBYTES;
-  static constexpr int KLOADS = (KBYTES / 16 + 255) / 256;
+  static constexpr int SBYTES = QK == QK_MXFP4 ? kTK * (D / 32) : 0;    // E8M0 bytes per tile
+  static constexpr int DSBYTES = QK == QK_MXFP4 ? kTK * 4 : 0;          // scaled dS floats per tile
+  static constexpr int KSTAGE = KBYTES + SBYTES;
+  static constexpr int VBYTES = D * kTK;                                // FP8 V^T tile
+  static constexpr int VSTAGE = VBYTES + DSBYTES;                       // V^T tile + scaled dS
+  static constexpr int KCHUNKS = KBYTES / 16;                           // 16-byte chunks per K tile
+  static constexpr int KLOADS = (KCHUNKS + 255) / 256;
   static constexpr int VLOADS = VBYTES / 16 / 256;
+  static constexpr int NCB = D / 32;                                    // 32-channel output blocks
+  static constexpr int NQF = QK == QK_INT8 ? D / 32 : D / 64;           // QK MFMAs per 32-key subtile
 };
 
 // Key row fed to A-row m of subtile s, so that output lane half h holds keys 32h + 16s + r.
 __device__ __forceinline__ int key_perm(int m, int s) { return 32 * ((m >> 2) & 1) + 16 * s + 4 * (m >> 3) + (m & 3); }
 
-template <int D, int QK>
-struct Stage {
-  using G = TileGeom<D, QK>;
-  uint4 k[G::KLOADS];
-  uint4 v[G::VLOADS];
-  uint4 sd;   // MXFP4: scales (threads 0..15) or dS (threads 16..31)
+template <int DT>
+__device__ __forceinline__ uint32_t pack2_io(float a, float b) {
+  if (DT == 0) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    bf2 r = __builtin_convertvector(f2{a, b}, bf2);
+    return __builtin_bit_cast(uint32_t, r);
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    h2 r = __builtin_convertvector(f2{a, b}, h2);
+    return __builtin_bit_cast(uint32_t, r);
+  }
+}
 
-  __device__ __forceinline__ void load(const FwdArgs& a, int bh, int j) {
-    const int tid = threadIdx.x;
-    const uint8_t* kg = a.k_codes + ((size_t)bh * a.Np + (size_t)j * kTK) * G::KROW;
+// ---- K / V tile staging: direct global -> LDS loads (no staging registers) ----
+// A wave's 16-byte direct load puts lane L's data at LDS base + 16 L, so the XOR
+// swizzle of the 16-byte chunks within a row (which spreads the MFMA operand reads
+// over all LDS banks) is applied to the global source address instead.
+// K stage: codes (+ E8M0 scales).  V stage: V^T codes (+ dS * sm * log2 e, staged through
+// registers because it is rescaled on the way), read one step later than K.
+template <int D, int QK>
+__device__ __forceinline__ void issue_k(uint8_t* lds, const FwdArgs& a, int bh, int j) {
+  using G = Geo<D, QK>;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));   // recompute the per-lane source offsets here rather than pin them in registers
+  const int w = threadIdx.x >> 6;
+  const uint8_t* kg = a.k_codes + ((size_t)bh * a.Np + (size_t)j * kTK) * G::KROW;
 #pragma unroll
-    for (int i = 0; i < G::KLOADS; i++) {
-      int c = tid + 256 * i;
-      if (c < G::KBYTES / 16) k[i] = reinterpret_cast<const uint4*>(kg)[c];
-    }
-    const uint8_t* vg = a.v_codes + ((size_t)bh * (a.Np / kTK) + j) * G::VBYTES;
-#pragma unroll
-    for (int i = 0; i < G::VLOADS; i++) v[i] = reinterpret_cast<const uint4*>(vg)[tid + 256 * i];
-    if (QK == QK_MXFP4) {
-      if (tid < G::SBYTES / 16) {
-        const uint8_t* sg = reinterpret_cast<const uint8_t*>(a.k_scales) + ((size_t)bh * a.Np + (size_t)j * kTK) * (D / 32);
-        sd = reinterpret_cast<const uint4*>(sg)[tid];
-      } else if (tid >= 64 && tid < 64 + G::DSBYTES / 16) {
-        const float* dg = a.delta_s + (size_t)bh * a.Np + (size_t)j * kTK;
-        sd = reinterpret_cast<const uint4*>(dg)[tid - 64];
-      }
+  for (int i = 0; i < G::KLOADS; i++) {
+    const int pbase = 256 * i + 64 * w;
+    if (pbase < G::KCHUNKS) {
+      const int P = pbase + lane;
+      const int row = P / G::KCH, col = (P % G::KCH) ^ (row & (G::KCH - 1));
+      load_lds16(kg + row * G::KROW + col * 16, lds + pbase * 16);
     }
   }
-  __device__ __forceinline__ void store(uint8_t* lds) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < G::KLOADS; i++) {
-      int c = tid + 256 * i;
-      if (c < G::KBYTES / 16) {
-        int row = c / G::KCH, col = c % G::KCH;
-        *reinterpret_cast<uint4*>(lds + row * G::KROW + ((col ^ (row & (G::KCH - 1))) << 4)) = k[i];
-      }
-    }
-    uint8_t* lv = lds + G::KBYTES + G::SBYTES + G::DSBYTES;
-#pragma unroll
-    for (int i = 0; i < G::VLOADS; i++) {
-      int c = tid + 256 * i;
-      int row = c >> 2, col = c & 3;
-      *reinterpret_cast<uint4*>(lv + row * 64 + ((col ^ (row & 3)) << 4)) = v[i];
-    }
-    if (QK == QK_MXFP4) {
-      if (tid < G::SBYTES / 16)
-        reinterpret_cast<uint4*>(lds + G::KBYTES)[tid] = sd;
-      else if (tid >= 64 && tid < 64 + G::DSBYTES / 16)
-        reinterpret_cast<uint4*>(lds + G::KBYTES + G::SBYTES)[tid - 64] = sd;
-    }
+  if (QK == QK_MXFP4 && w == 0 && lane < G::SBYTES / 16) {
+    const uint8_t* sg = reinterpret_cast<const uint8_t*>(a.k_scales) + ((size_t)bh * a.Np + (size_t)j * kTK) * (D / 32);
+    load_lds16(sg + lane * 16, lds + G::KBYTES);
   }
+}
+
+template <int D, int QK>
+__device__ __forceinline__ void issue_v(uint8_t* lds, const FwdArgs& a, int bh, int j) {
+  using G = Geo<D, QK>;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int w = threadIdx.x >> 6;
+  const uint8_t* vg = a.v_codes + ((size_t)bh * (a.Np / kTK) + j) * G::VBYTES;
+#pragma unroll
+  for (int i = 0; i < G::VLOADS; i++) {
+    const int pbase = 256 * i + 64 * w;
+    const int P = pbase + lane;
+    const int row = P >> 2, col = (P & 3) ^ (row & 3);
+    load_lds16(vg + row * 64 + col * 16, lds + pbase * 16);
+  }
+}
+
+// MXFP4 dS strip of one tile (64 floats): fetched into registers, stored scaled.
+__device__ __forceinline__ uint4 load_ds(const FwdArgs& a, int bh, int j) {
+  return reinterpret_cast<const uint4*>(a.delta_s + (size_t)bh * a.Np + (size_t)j * kTK)[threadIdx.x & 15];
+}
+template <int D, int QK>
+__device__ __forceinline__ void store_ds(uint4 r, uint8_t* lds, float c) {
+  const v4f f = {__uint_as_float(r.x) * c, __uint_as_float(r.y) * c, __uint_as_float(r.z) * c, __uint_as_float(r.w) * c};
+  reinterpret_cast<v4f*>(lds + Geo<D, QK>::VBYTES)[threadIdx.x & 15] = f;
+}
+
+// Wait for this wave's outstanding global loads (the direct-to-LDS tiles) before a barrier.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ---- score tile: S^T = K Q^T for the two 32-key subtiles of a 64-key tile ----
+template <int D, int QK>
+struct Score {
+  v16i si[QK == QK_INT8 ? 2 : 1];
+  v16f sf[QK == QK_MXFP4 ? 2 : 1];
 };
 
-template <int D, int QK, bool CAUSAL, int DT>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
-  using G = TileGeom<D, QK>;
-  constexpr int NCB = D / 32;                          // 32-channel output blocks
-  constexpr int NQF = QK == QK_INT8 ? D / 32 : D / 64; // QK MFMAs per 32-key subtile
-  __shared__ __align__(16) uint8_t smem[2][G::STAGE];
+template <int D, int QK>
+__device__ __forceinline__ void qk_tile(Score<D, QK>& S, const uint8_t* lk, const v4i* qf, const v8i* qf4,
+                                        const int* qsc, int n, int hh) {
+  using G = Geo<D, QK>;
+#pragma unroll
+  for (int s = 0; s < 2; s++) {
+    const int row = key_perm(n, s);
+    const uint8_t* rp = lk + row * G::KROW;
+    if (QK == QK_INT8) {
+      v16i acc = v16i{};
+#pragma unroll
+      for (int c = 0; c < G::NQF; c++) {
+        const int col = 2 * c + hh;
+        const v4i ka = *reinterpret_cast<const v4i*>(rp + ((col ^ (row & (G::KCH - 1))) << 4));
+        acc = mfma_i8(ka, qf[c], acc);
+      }
+      S.si[s] = acc;
+    } else {
+      v16f acc = v16f{};
+      const uint8_t* lsc = lk + G::KBYTES + row * (D / 32);
+#pragma unroll
+      for (int c = 0; c < G::NQF; c++) {
+        const int col = 2 * c + hh;
+        const v4i lo = *reinterpret_cast<const v4i*>(rp + ((col ^ (row & (G::KCH - 1))) << 4));
+        const v8i ka = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+        acc = mfma_mxfp4(ka, qf4[c], acc, lsc[col], qsc[c]);
+      }
+      S.sf[s] = acc;
+    }
+  }
+}
 
-  const int nqt = a.Np / kQT;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = id / nqt;
-  const int qt = CAUSAL ? nqt - 1 - id % nqt : id % nqt;   // causal: longest rows first
+// Online-softmax state of one wave's 32 queries.
+template <int D>
+struct RowState {
+  v16f O[D / 32];
+  float m, l;
+};
+
+// Softmax of tile j from its score registers, then O^T += V^T P~^T.
+template <int D, int QK, bool CAUSAL>
+__device__ __forceinline__ void softmax_pv(RowState<D>& st, const Score<D, QK>& Sc, const uint8_t* vstage,
+                                           const float* kstep, float qstep, float sm_log2e, int j, int N, int qw,
+                                           int qrow, int n, int hh) {
+  using G = Geo<D, QK>;
+  constexpr int NCB = G::NCB;
+  const int kbase = j * kTK;
+  const bool need_mask = kbase + kTK > N || (CAUSAL && kbase + kTK - 1 > qw);
+  float t[32];
+  if (QK == QK_INT8) {
+    const float cst = qstep * kstep[j];
+    if (!need_mask) {
+      // integer row max (cst > 0), then one FMA per element into the exp2 argument
+      int im = Sc.si[0][0];
+#pragma unroll
+      for (int s = 0; s < 2; s++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) im = max(im, Sc.si[s][r]);
+      const float mt = half_max((float)im * cst);
+      const float mnew = fmaxf(st.m, mt);
+      if (__any(mnew > st.m)) {
+        const float alpha = fast_exp2(st.m - mnew);
+        st.l *= alpha;
+#pragma unroll
+        for (int c = 0; c < NCB; c++) st.O[c] *= alpha;
+      }
+      st.m = mnew;
+      const float off = kLog2_448 - mnew;
+#pragma unroll
+      for (int s = 0; s < 2; s++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) t[16 * s + r] = fmaf((float)Sc.si[s][r], cst, off);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; s++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) t[16 * s + r] = (float)Sc.si[s][r] * cst;
+    }
+  } else {
+    const float* dsl = reinterpret_cast<const float*>(vstage + G::VBYTES) + 32 * hh;
+#pragma unroll
+    for (int s = 0; s < 2; s++)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const v4f dv = *reinterpret_cast<const v4f*>(dsl + 16 * s + r);
+#pragma unroll
+        for (int i = 0; i < 4; i++) t[16 * s + r + i] = fmaf(Sc.sf[s][r + i], sm_log2e, dv[i]);
+      }
+  }
+  if (QK == QK_MXFP4 || need_mask) {
+    if (need_mask) {
+#pragma unroll
+      for (int i = 0; i < 32; i++) {
+        const int key = kbase + 32 * hh + i;
+        if (key >= N || (CAUSAL && key > qrow)) t[i] = -INFINITY;
+      }
+    }
+    float mt = fmaxf(t[0], t[1]);
+#pragma unroll
+    for (int i = 2; i < 32; i += 2) mt = fmaxf(mt, fmaxf(t[i], t[i + 1]));
+    mt = half_max(mt);
+    const float mnew = fmaxf(st.m, mt);
+    const float mref = mnew == -INFINITY ? 0.0f : mnew;
+    if (__any(mnew > st.m)) {
+      const float alpha = fast_exp2(st.m - mref);
+      st.l *= alpha;
+#pragma unroll
+      for (int c = 0; c < NCB; c++) st.O[c] *= alpha;
+    }
+    st.m = mnew;
+    const float off = kLog2_448 - mref;
+#pragma unroll
+    for (int i = 0; i < 32; i++) t[i] += off;
+  }
+  // p448 = exp2(t), row sum, FP8 pack
+  v8i pb;
+  float ps0 = 0.0f, ps1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; i += 4) {
+    const float p0 = fast_exp2(t[i]), p1 = fast_exp2(t[i + 1]);
+    const float p2 = fast_exp2(t[i + 2]), p3 = fast_exp2(t[i + 3]);
+    ps0 += p0 + p1;
+    ps1 += p2 + p3;
+    pb[i / 4] = pack_fp8x4(p0, p1, p2, p3);
+  }
+  st.l += ps0 + ps1;
+  __builtin_amdgcn_sched_barrier(0);
+  // O^T += V^T P~^T
+#pragma unroll
+  for (int c = 0; c < NCB; c++) {
+    const int row = 32 * c + n;
+    const uint8_t* rp = vstage + row * 64;
+    const v4i v0 = *reinterpret_cast<const v4i*>(rp + (((2 * hh) ^ (row & 3)) << 4));
+    const v4i v1 = *reinterpret_cast<const v4i*>(rp + (((2 * hh + 1) ^ (row & 3)) << 4));
+    const v8i va = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    st.O[c] = mfma_f8(va, pb, st.O[c]);
+  }
+}
+
+template <int D, int QK, bool CAUSAL, int DT>
+__device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint8_t (*lk)[Geo<D, QK>::KSTAGE],
+                                          uint8_t (*lv)[Geo<D, QK>::VSTAGE]) {
+  using G = Geo<D, QK>;
+  constexpr int NCB = G::NCB, NQF = G::NQF;
   const int qbase = qt * kQT;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 31, hh = lane >> 5;
   const int qw = qbase + 32 * w;          // first query of this wave
   const int qrow = qw + n;                // this lane's query
 
-  // Q fragments (B operand), resident for the whole loop
+  // Q fragments (B operand), resident for the whole pass
   v4i qf[QK == QK_INT8 ? NQF : 1];
   v8i qf4[QK == QK_MXFP4 ? NQF : 1];
   int qsc[QK == QK_MXFP4 ? NQF : 1];
@@ -156,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     const uint8_t* qe = reinterpret_cast<const uint8_t*>(a.q_scales) + ((size_t)bh * a.Np + qrow) * (D / 32) + hh;
 #pragma unroll
     for (int c = 0; c < NQF; c++) {
-      v4i lo = *reinterpret_cast<const v4i*>(qp + 32 * c);
+      const v4i lo = *reinterpret_cast<const v4i*>(qp + 32 * c);
       qf4[c] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
       qsc[c] = qe[2 * c];
     }
@@ -165,118 +333,56 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 
   int ntiles = (a.N + kTK - 1) / kTK;
   if (CAUSAL) ntiles = min(ntiles, (qbase + kQT - 1) / kTK + 1);
+  // tiles holding keys this wave may see (causal: later tiles are fully masked for it)
+  const int wtiles = CAUSAL ? min(ntiles, (qw + 31) / kTK + 1) : ntiles;
 
-  v16f O[NCB];
+  RowState<D> st;
 #pragma unroll
-  for (int c = 0; c < NCB; c++) O[c] = v16f{};
-  float m = -INFINITY, l = 0.0f;
+  for (int c = 0; c < NCB; c++) st.O[c] = v16f{};
+  st.m = -INFINITY;
+  st.l = 0.0f;
 
-  Stage<D, QK> st;
-  st.load(a, bh, 0);
-  st.store(smem[0]);
+  // prologue: K0 -> LDS, QK(0); then K1, V0 -> LDS
+  issue_k<D, QK>(lk[0], a, bh, 0);
+  wait_vmem();
+  __syncthreads();
+  Score<D, QK> Sa, Sb;
+  qk_tile<D, QK>(Sa, lk[0], qf, qf4, qsc, n, hh);
+  issue_k<D, QK>(lk[1], a, bh, min(1, ntiles - 1));
+  issue_v<D, QK>(lv[0], a, bh, 0);
+  if (QK == QK_MXFP4) store_ds<D, QK>(load_ds(a, bh, 0), lv[0], a.sm_log2e);
+  wait_vmem();
   __syncthreads();
 
-  for (int j = 0; j < ntiles; j++) {
-    const bool more = j + 1 < ntiles;
-    if (more) st.load(a, bh, j + 1);
-    const uint8_t* lds = smem[j & 1];
-    const int kbase = j * kTK;
-    // waves whose queries all precede this tile have nothing to do here
-    if (!(CAUSAL && kbase > qw + 31)) {
-      // ---- S^T = K Q^T for two 32-key subtiles ----
-      float t[32];
-      if (QK == QK_INT8) {
-        v16i S[2] = {v16i{}, v16i{}};
-#pragma unroll
-        for (int s = 0; s < 2; s++) {
-          const int row = key_perm(n, s);
-#pragma unroll
-          for (int c = 0; c < NQF; c++) {
-            const int col = 2 * c + hh;
-            v4i ka = *reinterpret_cast<const v4i*>(lds + row * G::KROW + ((col ^ (row & (G::KCH - 1))) << 4));
-            S[s] = mfma_i8(ka, qf[c], S[s]);
-          }
-        }
-        const float cst = qstep * kstep[j];
-#pragma unroll
-        for (int s = 0; s < 2; s++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) t[16 * s + r] = (float)S[s][r] * cst;
-      } else {
-        v16f S[2] = {v16f{}, v16f{}};
-        const uint8_t* lsc = lds + G::KBYTES;
-#pragma unroll
-        for (int s = 0; s < 2; s++) {
-          const int row = key_perm(n, s);
-#pragma unroll
-          for (int c = 0; c < NQF; c++) {
-            const int col = 2 * c + hh;
-            v4i lo = *reinterpret_cast<const v4i*>(lds + row * G::KROW + ((col ^ (row & (G::KCH - 1))) << 4));
-            v8i ka = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-            const int ksc = lsc[row * (D / 32) + col];
-            S[s] = mfma_mxfp4(ka, qf4[c], S[s], ksc, qsc[c]);
-          }
-        }
-        const float* lds_ds = reinterpret_cast<const float*>(lds + G::KBYTES + G::SBYTES) + 32 * hh;
-#pragma unroll
-        for (int s = 0; s < 2; s++)
-#pragma unroll
-          for (int r = 0; r < 16; r += 4) {
-            v4f dsv = *reinterpret_cast<const v4f*>(lds_ds + 16 * s + r);
-#pragma unroll
-            for (int i = 0; i < 4; i++) t[16 * s + r + i] = (S[s][r + i] + dsv[i]) * a.sm_log2e;
-          }
-      }
-      // ---- masking (tail tile, causal diagonal) ----
-      const bool need_mask = kbase + kTK > a.N || (CAUSAL && kbase + kTK - 1 > qw);
-      if (need_mask) {
-#pragma unroll
-        for (int i = 0; i < 32; i++) {
-          const int key = kbase + 32 * hh + i;
-          if (key >= a.N || (CAUSAL && key > qrow)) t[i] = -INFINITY;
-        }
-      }
-      // ---- online softmax ----
-      float mt = t[0];
-#pragma unroll
-      for (int i = 1; i < 32; i++) mt = fmaxf(mt, t[i]);
-      mt = half_max(mt);
-      const float mnew = fmaxf(m, mt);
-      const float mref = mnew == -INFINITY ? 0.0f : mnew;
-      const float alpha = fast_exp2(m - mref);
-      l *= alpha;
-#pragma unroll
-      for (int c = 0; c < NCB; c++) O[c] *= alpha;
-      const float off = kLog2_448 - mref;
-      v8i pb;
-      float ps = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; i += 4) {
-        const float p0 = fast_exp2(t[i] + off), p1 = fast_exp2(t[i + 1] + off);
-        const float p2 = fast_exp2(t[i + 2] + off), p3 = fast_exp2(t[i + 3] + off);
-        ps += (p0 + p1) + (p2 + p3);
-        pb[i / 4] = pack_fp8x4(p0, p1, p2, p3);
-      }
-      l += ps;
-      m = mnew;
-      // ---- O^T += V^T P~^T ----
-      const uint8_t* lv = lds + G::KBYTES + G::SBYTES + G::DSBYTES;
-#pragma unroll
-      for (int c = 0; c < NCB; c++) {
-        const int row = 32 * c + n;
-        const uint8_t* rp = lv + row * 64;
-        v4i v0 = *reinterpret_cast<const v4i*>(rp + (((2 * hh) ^ (row & 3)) << 4));
-        v4i v1 = *reinterpret_cast<const v4i*>(rp + (((2 * hh + 1) ^ (row & 3)) << 4));
-        v8i va = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        O[c] = mfma_f8(va, pb, O[c]);
-      }
-    }
-    if (more) st.store(smem[(j + 1) & 1]);
+  // One tile: prefetch K(j+2) into lk[j&1] and V(j+1) into lv[(j+1)&1] (both already
+  // consumed: tile j's K by QK(j) and tile j-1's V by PV(j-1), before the last barrier);
+  // issue QK(j+1) into Sn; softmax + PV of tile j from Sc; barrier.  Prefetch indices are
+  // clamped to the last tile, so the loads are unconditional.  Unrolled twice so Sa/Sb
+  // alternate without copies.
+  const int last = ntiles - 1;
+  auto step = [&](int j, const Score<D, QK>& Sc, Score<D, QK>& Sn) {
+    issue_k<D, QK>(lk[j & 1], a, bh, min(j + 2, last));
+    issue_v<D, QK>(lv[(j + 1) & 1], a, bh, min(j + 1, last));
+    uint4 dsr;
+    if (QK == QK_MXFP4) dsr = load_ds(a, bh, min(j + 1, last));
+    if (j + 1 < wtiles) qk_tile<D, QK>(Sn, lk[(j + 1) & 1], qf, qf4, qsc, n, hh);
+    // keep the phases apart: QK(j+1)'s operands die before the softmax starts (its MFMAs keep
+    // running underneath), so the live set stays within the 256-register budget of 2 waves/SIMD
+    __builtin_amdgcn_sched_barrier(0);
+    if (j < wtiles) softmax_pv<D, QK, CAUSAL>(st, Sc, lv[j & 1], kstep, qstep, a.sm_log2e, j, a.N, qw, qrow, n, hh);
+    if (QK == QK_MXFP4) store_ds<D, QK>(dsr, lv[(j + 1) & 1], a.sm_log2e);
+    wait_vmem();
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    step(j, Sa, Sb);
+    step(j + 1, Sb, Sa);
   }
+  if (j < ntiles) step(j, Sa, Sb);
 
   // ---- epilogue: O / l * dV, LSE ----
-  const float lt = half_sum(l);
+  const float lt = half_sum(st.l);
   if (qrow < a.N) {
     const float inv = 1.0f / lt;
     const float* vs = a.v_scales + (size_t)bh * D;
@@ -286,23 +392,45 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; g++) {
         const int ch = 32 * c + 8 * g + 4 * hh;
-        v4f sc = *reinterpret_cast<const v4f*>(vs + ch);
-        uint32_t lo = (uint32_t)to_io<DT>(O[c][4 * g] * sc[0] * inv) | ((uint32_t)to_io<DT>(O[c][4 * g + 1] * sc[1] * inv) << 16);
-        uint32_t hi = (uint32_t)to_io<DT>(O[c][4 * g + 2] * sc[2] * inv) | ((uint32_t)to_io<DT>(O[c][4 * g + 3] * sc[3] * inv) << 16);
+        const v4f sc = *reinterpret_cast<const v4f*>(vs + ch);
+        const uint32_t lo = pack2_io<DT>(st.O[c][4 * g] * (sc[0] * inv), st.O[c][4 * g + 1] * (sc[1] * inv));
+        const uint32_t hi = pack2_io<DT>(st.O[c][4 * g + 2] * (sc[2] * inv), st.O[c][4 * g + 3] * (sc[3] * inv));
         *reinterpret_cast<uint2*>(orow + ch) = make_uint2(lo, hi);
       }
     if (a.lse && hh == 0)
-      a.lse[(size_t)bh * a.N + qrow] = (m + __log2f(lt) - kLog2_448) * kLn2 + a.lse_corr[(size_t)bh * a.N + qrow];
+      a.lse[(size_t)bh * a.N + qrow] = (st.m + __log2f(lt) - kLog2_448) * kLn2 + a.lse_corr[(size_t)bh * a.N + qrow];
+  }
+}
+
+template <int D, int QK, bool CAUSAL, int DT>
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
+  using G = Geo<D, QK>;
+  __shared__ __align__(16) uint8_t lk[2][G::KSTAGE];
+  __shared__ __align__(16) uint8_t lv[2][G::VSTAGE];
+  const int nqt = a.Np / kQT;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  if (CAUSAL) {
+    // work item = (head, pair): heavy tile nqt-1-g then light tile g
+    const int npair = (nqt + 1) / 2;
+    const int bh = id / npair, g = id % npair;
+    const int heavy = nqt - 1 - g;
+    run_qtile<D, QK, CAUSAL, DT>(a, bh, heavy, lk, lv);
+    if (g < heavy) {
+      __syncthreads();
+      run_qtile<D, QK, CAUSAL, DT>(a, bh, g, lk, lv);
+    }
+  } else {
+    run_qtile<D, QK, CAUSAL, DT>(a, id / nqt, id % nqt, lk, lv);
   }
 }
 
 template <int D, int QK, int DT>
 static hipError_t fwd_dispatch(const Shape& s, const FwdArgs& a, hipStream_t st) {
-  const int grid = s.B * s.H * (s.Np / kQT);
+  const int nqt = s.Np / kQT;
   if (s.causal)
-    attn_fwd_kernel<D, QK, true, DT><<<grid, 256, 0, st>>>(a);
+    attn_fwd_kernel<D, QK, true, DT><<<s.B * s.H * ((nqt + 1) / 2), 256, 0, st>>>(a);
   else
-    attn_fwd_kernel<D, QK, false, DT><<<grid, 256, 0, st>>>(a);
+    attn_fwd_kernel<D, QK, false, DT><<<s.B * s.H * nqt, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -325,6 +453,7 @@ hipError_t launch_attn_fwd(const Shape& s, const QuantPtrs& qp, void* o, float* 
   a.lse = lse;
   a.N = s.N;
   a.Np = s.Np;
+  a.BH = s.B * s.H;
   a.sm_log2e = s.sm_scale * kLog2e;
   if (s.pv_fmt != PV_FP8) return hipErrorInvalidValue;   // MXFP4 P~V: not in this kernel
   if (s.qk_fmt == QK_INT8)

@@ -58,6 +58,14 @@ __device__ __forceinline__ float half_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte direct global -> LDS load: lane L's bytes land at lds + 16 L (the LDS pointer is
+// wave-uniform).  The builtin exists only in the device compilation pass.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+#endif
+}
+
 // Four floats -> four E4M3 bytes (RNE; inputs here never exceed 448).
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
