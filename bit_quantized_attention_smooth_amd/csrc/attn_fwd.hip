@@ -80,6 +80,19 @@ struct Geo {
 // Key row fed to A-row m of subtile s, so that output lane half h holds keys 32h + 16s + r.
 __device__ __forceinline__ int key_perm(int m, int s) { return 32 * ((m >> 2) & 1) + 16 * s + 4 * (m >> 3) + (m & 3); }
 
+// LDS swizzles: the 16-byte chunk c of row r is stored at chunk c ^ swz(r).  One ds_read_b128
+// serves 16 lanes per LDS cycle; with 64 banks of 4 bytes a chunk's bank group is fixed by
+// (row bits below the 256-byte period, chunk).  The K operand read by lanes 0-15 touches rows
+// {0..3, 32..35, 4..7, 36..39} (+8, +16, ... for the other lane groups and subtiles); the V^T
+// read touches 16 consecutive rows.  Each swizzle makes those 16 bank groups distinct.
+template <int ROWBYTES>
+__device__ __forceinline__ int swz(int r) {
+  if (ROWBYTES == 128) return ((r >> 1) & 3) | (((r >> 5) & 1) << 2);   // 8 chunks, bank period 2 rows
+  if (ROWBYTES == 64) return ((r >> 2) & 1) | (((r >> 5) & 1) << 1);    // 4 chunks, period 4 rows
+  return (r >> 5) & 1;                                                   // 32-byte rows, 2 chunks
+}
+__device__ __forceinline__ int swz_v(int r) { return (r >> 2) & 3; }     // V^T rows of 64 bytes
+
 template <int DT>
 __device__ __forceinline__ uint32_t pack2_io(float a, float b) {
   if (DT == 0) {
@@ -101,21 +114,77 @@ __device__ __forceinline__ uint32_t pack2_io(float a, float b) {
 // over all LDS banks) is applied to the global source address instead.
 // K stage: codes (+ E8M0 scales).  V stage: V^T codes (+ dS * sm * log2 e, staged through
 // registers because it is rescaled on the way), read one step later than K.
+// Per-lane byte offsets, computed once per query-tile pass and pinned in registers (the
+// tile base addresses are wave-uniform, so every access is uniform base + lane offset).
 template <int D, int QK>
-__device__ __forceinline__ void issue_k(uint8_t* lds, const FwdArgs& a, int bh, int j) {
+struct LaneOffs {
   using G = Geo<D, QK>;
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));   // recompute the per-lane source offsets here rather than pin them in registers
-  const int w = threadIdx.x >> 6;
+  uint32_t kld[G::KLOADS];          // direct-load source offsets inside a K tile
+  uint32_t vld[G::VLOADS];          // direct-load source offsets inside a V^T tile
+  uint32_t kop[2][G::NQF];          // LDS offsets of the K operand reads (subtile, chunk)
+  uint32_t ksc[2][G::NQF];          // MXFP4: LDS offsets of the K scale bytes
+  uint32_t vop[G::NCB][2];          // LDS offsets of the V^T operand reads (block, half)
+
+  __device__ __forceinline__ void init(int w, int lane, int n, int hh) {
+#pragma unroll
+    for (int i = 0; i < G::KLOADS; i++) {
+      const int P = (256 * i + 64 * w + lane) % G::KCHUNKS;
+      const int row = P / G::KCH, col = (P % G::KCH) ^ swz<G::KROW>(row);
+      kld[i] = row * G::KROW + col * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < G::VLOADS; i++) {
+      const int P = 256 * i + 64 * w + lane;
+      const int row = P >> 2, col = (P & 3) ^ swz_v(row);
+      vld[i] = row * 64 + col * 16;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+      const int row = key_perm(n, s);
+#pragma unroll
+      for (int c = 0; c < G::NQF; c++) {
+        const int col = 2 * c + hh;
+        kop[s][c] = row * G::KROW + ((col ^ swz<G::KROW>(row)) << 4);
+        ksc[s][c] = G::KBYTES + row * (D / 32) + col;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < G::NCB; c++) {
+      const int row = 32 * c + n;
+      vop[c][0] = row * 64 + (((2 * hh) ^ swz_v(row)) << 4);
+      vop[c][1] = row * 64 + (((2 * hh + 1) ^ swz_v(row)) << 4);
+    }
+    // opaque to the optimizer: keep these in registers instead of recomputing them every tile
+#pragma unroll
+    for (int i = 0; i < G::KLOADS; i++) asm volatile("" : "+v"(kld[i]));
+#pragma unroll
+    for (int i = 0; i < G::VLOADS; i++) asm volatile("" : "+v"(vld[i]));
+#pragma unroll
+    for (int s = 0; s < 2; s++)
+#pragma unroll
+      for (int c = 0; c < G::NQF; c++) {
+        asm volatile("" : "+v"(kop[s][c]));
+        if (QK == QK_MXFP4) asm volatile("" : "+v"(ksc[s][c]));
+      }
+#pragma unroll
+    for (int c = 0; c < G::NCB; c++) asm volatile("" : "+v"(vop[c][0]), "+v"(vop[c][1]));
+  }
+};
+
+// ---- K / V tile staging: direct global -> LDS loads (no staging registers) ----
+// A wave's 16-byte direct load puts lane L's data at LDS base + 16 L, so the swizzle is
+// applied to the global source offset instead.  K stage: codes (+ E8M0 scales).  V stage:
+// V^T codes (+ dS * sm * log2 e, staged through registers because it is rescaled on the
+// way), read one step later than K.
+template <int D, int QK>
+__device__ __forceinline__ void issue_k(uint8_t* lds, const FwdArgs& a, int bh, int j, const LaneOffs<D, QK>& lo,
+                                        int w, int lane) {
+  using G = Geo<D, QK>;
   const uint8_t* kg = a.k_codes + ((size_t)bh * a.Np + (size_t)j * kTK) * G::KROW;
 #pragma unroll
   for (int i = 0; i < G::KLOADS; i++) {
     const int pbase = 256 * i + 64 * w;
-    if (pbase < G::KCHUNKS) {
-      const int P = pbase + lane;
-      const int row = P / G::KCH, col = (P % G::KCH) ^ (row & (G::KCH - 1));
-      load_lds16(kg + row * G::KROW + col * 16, lds + pbase * 16);
-    }
+    if (pbase < G::KCHUNKS) load_lds16(kg + lo.kld[i], lds + pbase * 16);
   }
   if (QK == QK_MXFP4 && w == 0 && lane < G::SBYTES / 16) {
     const uint8_t* sg = reinterpret_cast<const uint8_t*>(a.k_scales) + ((size_t)bh * a.Np + (size_t)j * kTK) * (D / 32);
@@ -124,19 +193,12 @@ __device__ __forceinline__ void issue_k(uint8_t* lds, const FwdArgs& a, int bh, 
 }
 
 template <int D, int QK>
-__device__ __forceinline__ void issue_v(uint8_t* lds, const FwdArgs& a, int bh, int j) {
+__device__ __forceinline__ void issue_v(uint8_t* lds, const FwdArgs& a, int bh, int j, const LaneOffs<D, QK>& lo,
+                                        int w) {
   using G = Geo<D, QK>;
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));
-  const int w = threadIdx.x >> 6;
   const uint8_t* vg = a.v_codes + ((size_t)bh * (a.Np / kTK) + j) * G::VBYTES;
 #pragma unroll
-  for (int i = 0; i < G::VLOADS; i++) {
-    const int pbase = 256 * i + 64 * w;
-    const int P = pbase + lane;
-    const int row = P >> 2, col = (P & 3) ^ (row & 3);
-    load_lds16(vg + row * 64 + col * 16, lds + pbase * 16);
-  }
+  for (int i = 0; i < G::VLOADS; i++) load_lds16(vg + lo.vld[i], lds + (256 * i + 64 * w) * 16);
 }
 
 // MXFP4 dS strip of one tile (64 floats): fetched into registers, stored scaled.
@@ -161,30 +223,25 @@ struct Score {
 
 template <int D, int QK>
 __device__ __forceinline__ void qk_tile(Score<D, QK>& S, const uint8_t* lk, const v4i* qf, const v8i* qf4,
-                                        const int* qsc, int n, int hh) {
+                                        const int* qsc, const LaneOffs<D, QK>& lo) {
   using G = Geo<D, QK>;
 #pragma unroll
   for (int s = 0; s < 2; s++) {
-    const int row = key_perm(n, s);
-    const uint8_t* rp = lk + row * G::KROW;
     if (QK == QK_INT8) {
       v16i acc = v16i{};
 #pragma unroll
       for (int c = 0; c < G::NQF; c++) {
-        const int col = 2 * c + hh;
-        const v4i ka = *reinterpret_cast<const v4i*>(rp + ((col ^ (row & (G::KCH - 1))) << 4));
+        const v4i ka = *reinterpret_cast<const v4i*>(lk + lo.kop[s][c]);
         acc = mfma_i8(ka, qf[c], acc);
       }
       S.si[s] = acc;
     } else {
       v16f acc = v16f{};
-      const uint8_t* lsc = lk + G::KBYTES + row * (D / 32);
 #pragma unroll
       for (int c = 0; c < G::NQF; c++) {
-        const int col = 2 * c + hh;
-        const v4i lo = *reinterpret_cast<const v4i*>(rp + ((col ^ (row & (G::KCH - 1))) << 4));
-        const v8i ka = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
-        acc = mfma_mxfp4(ka, qf4[c], acc, lsc[col], qsc[c]);
+        const v4i k4 = *reinterpret_cast<const v4i*>(lk + lo.kop[s][c]);
+        const v8i ka = v8i{k4[0], k4[1], k4[2], k4[3], 0, 0, 0, 0};
+        acc = mfma_mxfp4(ka, qf4[c], acc, lk[lo.ksc[s][c]], qsc[c]);
       }
       S.sf[s] = acc;
     }
@@ -199,45 +256,57 @@ struct RowState {
 };
 
 // Softmax of tile j from its score registers, then O^T += V^T P~^T.
+//   u_i = S_i (INT8: converted to fp32) or S_i + dS_i / c (MXFP4), with c = the positive
+//   log2-domain scale; masked entries are set to -inf; the row max is taken on u, and
+//   p448_i = exp2(u_i * c + (log2 448 - m)) comes out of one FMA and one exp2 per element.
 template <int D, int QK, bool CAUSAL>
 __device__ __forceinline__ void softmax_pv(RowState<D>& st, const Score<D, QK>& Sc, const uint8_t* vstage,
                                            const float* kstep, float qstep, float sm_log2e, int j, int N, int qw,
-                                           int qrow, int n, int hh) {
+                                           int qrow, int hh, const LaneOffs<D, QK>& lo) {
   using G = Geo<D, QK>;
   constexpr int NCB = G::NCB;
   const int kbase = j * kTK;
   const bool need_mask = kbase + kTK > N || (CAUSAL && kbase + kTK - 1 > qw);
-  float t[32];
+  float u[32];
+  float c;
+  float mt;
   if (QK == QK_INT8) {
-    const float cst = qstep * kstep[j];
-    if (!need_mask) {
-      // integer row max (cst > 0), then one FMA per element into the exp2 argument
-      int im = Sc.si[0][0];
+    c = qstep * kstep[j];
+    // a zero block step means every code of that block is 0, so every unmasked score is 0
+    // for any c; keep c positive so that masked entries (-inf) stay -inf after scaling
+    c = c == 0.0f ? 1.0f : c;
+    int im;
+    if (need_mask) {
+      asm volatile("" ::: "memory");   // a real branch: the rare masked tiles must not cost every tile
+      const int lim = (CAUSAL ? min(N, qrow + 1) : N) - (kbase + 32 * hh);   // keys i < lim are visible
+      im = INT_MIN;
 #pragma unroll
       for (int s = 0; s < 2; s++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) im = max(im, Sc.si[s][r]);
-      const float mt = half_max((float)im * cst);
-      const float mnew = fmaxf(st.m, mt);
-      if (__any(mnew > st.m)) {
-        const float alpha = fast_exp2(st.m - mnew);
-        st.l *= alpha;
-#pragma unroll
-        for (int c = 0; c < NCB; c++) st.O[c] *= alpha;
-      }
-      st.m = mnew;
-      const float off = kLog2_448 - mnew;
-#pragma unroll
-      for (int s = 0; s < 2; s++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) t[16 * s + r] = fmaf((float)Sc.si[s][r], cst, off);
+        for (int r = 0; r < 16; r++) {
+          const int i = 16 * s + r;
+          const bool ok = i < lim;
+          im = ok ? max(im, Sc.si[s][r]) : im;
+          u[i] = ok ? (float)Sc.si[s][r] : -INFINITY;
+        }
+      const int imo = __builtin_bit_cast(int, other_half(__builtin_bit_cast(float, im)));
+      im = max(im, imo);
+      mt = im == INT_MIN ? -INFINITY : (float)im * c;
     } else {
+      // the row max on the integer scores (c > 0): exact, no NaN handling
+      im = Sc.si[0][0];
 #pragma unroll
       for (int s = 0; s < 2; s++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) t[16 * s + r] = (float)Sc.si[s][r] * cst;
+        for (int r = 0; r < 16; r++) {
+          im = max(im, Sc.si[s][r]);
+          u[16 * s + r] = (float)Sc.si[s][r];
+        }
+      const int imo = __builtin_bit_cast(int, other_half(__builtin_bit_cast(float, im)));
+      mt = (float)max(im, imo) * c;
     }
   } else {
+    // dS arrives pre-multiplied by sm * log2 e; u = S * sm * log2 e + dS * sm * log2 e, c = 1
     const float* dsl = reinterpret_cast<const float*>(vstage + G::VBYTES) + 32 * hh;
 #pragma unroll
     for (int s = 0; s < 2; s++)
@@ -245,41 +314,37 @@ __device__ __forceinline__ void softmax_pv(RowState<D>& st, const Score<D, QK>& 
       for (int r = 0; r < 16; r += 4) {
         const v4f dv = *reinterpret_cast<const v4f*>(dsl + 16 * s + r);
 #pragma unroll
-        for (int i = 0; i < 4; i++) t[16 * s + r + i] = fmaf(Sc.sf[s][r + i], sm_log2e, dv[i]);
+        for (int i = 0; i < 4; i++) u[16 * s + r + i] = fmaf(Sc.sf[s][r + i], sm_log2e, dv[i]);
       }
-  }
-  if (QK == QK_MXFP4 || need_mask) {
+    c = 1.0f;
     if (need_mask) {
+      asm volatile("" ::: "memory");
+      const int lim = (CAUSAL ? min(N, qrow + 1) : N) - (kbase + 32 * hh);
 #pragma unroll
-      for (int i = 0; i < 32; i++) {
-        const int key = kbase + 32 * hh + i;
-        if (key >= N || (CAUSAL && key > qrow)) t[i] = -INFINITY;
-      }
+      for (int i = 0; i < 32; i++) u[i] = i < lim ? u[i] : -INFINITY;
     }
-    float mt = fmaxf(t[0], t[1]);
+    float mu = fmaxf(u[0], u[1]);
 #pragma unroll
-    for (int i = 2; i < 32; i += 2) mt = fmaxf(mt, fmaxf(t[i], t[i + 1]));
-    mt = half_max(mt);
-    const float mnew = fmaxf(st.m, mt);
-    const float mref = mnew == -INFINITY ? 0.0f : mnew;
-    if (__any(mnew > st.m)) {
-      const float alpha = fast_exp2(st.m - mref);
-      st.l *= alpha;
-#pragma unroll
-      for (int c = 0; c < NCB; c++) st.O[c] *= alpha;
-    }
-    st.m = mnew;
-    const float off = kLog2_448 - mref;
-#pragma unroll
-    for (int i = 0; i < 32; i++) t[i] += off;
+    for (int i = 2; i < 32; i += 2) mu = fmaxf(mu, fmaxf(u[i], u[i + 1]));
+    mt = half_max(mu);
   }
-  // p448 = exp2(t), row sum, FP8 pack
+  const float mnew = fmaxf(st.m, mt);
+  const float mref = mnew == -INFINITY ? 0.0f : mnew;
+  if (__any(mnew > st.m)) {
+    const float alpha = fast_exp2(st.m - mref);
+    st.l *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < NCB; cb++) st.O[cb] *= alpha;
+  }
+  st.m = mnew;
+  const float off = kLog2_448 - mref;
+  // p448 = exp2(u c + off), row sum, FP8 pack
   v8i pb;
   float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; i += 4) {
-    const float p0 = fast_exp2(t[i]), p1 = fast_exp2(t[i + 1]);
-    const float p2 = fast_exp2(t[i + 2]), p3 = fast_exp2(t[i + 3]);
+    const float p0 = fast_exp2(fmaf(u[i], c, off)), p1 = fast_exp2(fmaf(u[i + 1], c, off));
+    const float p2 = fast_exp2(fmaf(u[i + 2], c, off)), p3 = fast_exp2(fmaf(u[i + 3], c, off));
     ps0 += p0 + p1;
     ps1 += p2 + p3;
     pb[i / 4] = pack_fp8x4(p0, p1, p2, p3);
@@ -288,13 +353,11 @@ __device__ __forceinline__ void softmax_pv(RowState<D>& st, const Score<D, QK>& 
   __builtin_amdgcn_sched_barrier(0);
   // O^T += V^T P~^T
 #pragma unroll
-  for (int c = 0; c < NCB; c++) {
-    const int row = 32 * c + n;
-    const uint8_t* rp = vstage + row * 64;
-    const v4i v0 = *reinterpret_cast<const v4i*>(rp + (((2 * hh) ^ (row & 3)) << 4));
-    const v4i v1 = *reinterpret_cast<const v4i*>(rp + (((2 * hh + 1) ^ (row & 3)) << 4));
+  for (int cb = 0; cb < NCB; cb++) {
+    const v4i v0 = *reinterpret_cast<const v4i*>(vstage + lo.vop[cb][0]);
+    const v4i v1 = *reinterpret_cast<const v4i*>(vstage + lo.vop[cb][1]);
     const v8i va = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-    st.O[c] = mfma_f8(va, pb, st.O[c]);
+    st.O[cb] = mfma_f8(va, pb, st.O[cb]);
   }
 }
 
@@ -304,10 +367,13 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
   using G = Geo<D, QK>;
   constexpr int NCB = G::NCB, NQF = G::NQF;
   const int qbase = qt * kQT;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int n = lane & 31, hh = lane >> 5;
   const int qw = qbase + 32 * w;          // first query of this wave
   const int qrow = qw + n;                // this lane's query
+  LaneOffs<D, QK> lo;
+  lo.init(w, lane, n, hh);
 
   // Q fragments (B operand), resident for the whole pass
   v4i qf[QK == QK_INT8 ? NQF : 1];
@@ -343,13 +409,13 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
   st.l = 0.0f;
 
   // prologue: K0 -> LDS, QK(0); then K1, V0 -> LDS
-  issue_k<D, QK>(lk[0], a, bh, 0);
+  issue_k<D, QK>(lk[0], a, bh, 0, lo, w, lane);
   wait_vmem();
   __syncthreads();
   Score<D, QK> Sa, Sb;
-  qk_tile<D, QK>(Sa, lk[0], qf, qf4, qsc, n, hh);
-  issue_k<D, QK>(lk[1], a, bh, min(1, ntiles - 1));
-  issue_v<D, QK>(lv[0], a, bh, 0);
+  qk_tile<D, QK>(Sa, lk[0], qf, qf4, qsc, lo);
+  issue_k<D, QK>(lk[1], a, bh, min(1, ntiles - 1), lo, w, lane);
+  issue_v<D, QK>(lv[0], a, bh, 0, lo, w);
   if (QK == QK_MXFP4) store_ds<D, QK>(load_ds(a, bh, 0), lv[0], a.sm_log2e);
   wait_vmem();
   __syncthreads();
@@ -361,15 +427,15 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
   // alternate without copies.
   const int last = ntiles - 1;
   auto step = [&](int j, const Score<D, QK>& Sc, Score<D, QK>& Sn) {
-    issue_k<D, QK>(lk[j & 1], a, bh, min(j + 2, last));
-    issue_v<D, QK>(lv[(j + 1) & 1], a, bh, min(j + 1, last));
+    issue_k<D, QK>(lk[j & 1], a, bh, min(j + 2, last), lo, w, lane);
+    issue_v<D, QK>(lv[(j + 1) & 1], a, bh, min(j + 1, last), lo, w);
     uint4 dsr;
     if (QK == QK_MXFP4) dsr = load_ds(a, bh, min(j + 1, last));
-    if (j + 1 < wtiles) qk_tile<D, QK>(Sn, lk[(j + 1) & 1], qf, qf4, qsc, n, hh);
+    if (j + 1 < wtiles) qk_tile<D, QK>(Sn, lk[(j + 1) & 1], qf, qf4, qsc, lo);
     // keep the phases apart: QK(j+1)'s operands die before the softmax starts (its MFMAs keep
     // running underneath), so the live set stays within the 256-register budget of 2 waves/SIMD
     __builtin_amdgcn_sched_barrier(0);
-    if (j < wtiles) softmax_pv<D, QK, CAUSAL>(st, Sc, lv[j & 1], kstep, qstep, a.sm_log2e, j, a.N, qw, qrow, n, hh);
+    if (j < wtiles) softmax_pv<D, QK, CAUSAL>(st, Sc, lv[j & 1], kstep, qstep, a.sm_log2e, j, a.N, qw, qrow, hh, lo);
     if (QK == QK_MXFP4) store_ds<D, QK>(dsr, lv[(j + 1) & 1], a.sm_log2e);
     wait_vmem();
     __syncthreads();
