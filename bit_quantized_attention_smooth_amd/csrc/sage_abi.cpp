@@ -252,7 +252,10 @@ sage_status sage_attn_bwd_ws_size(const sage_problem* p, size_t* bytes) {
   if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
   if (p->qk_fmt != SAGE_FMT_INT8 || p->pv_fmt != SAGE_FMT_FP8)
     return fail(SAGE_ERR_UNSUPPORTED, "the backward supports qk_fmt=INT8, pv_fmt=FP8 only");
-  *bytes = sage::attn_bwd_ws_bytes(to_shape(p));
+  if (p->d != 64) return fail(SAGE_ERR_UNSUPPORTED, "the backward supports head dim 64 only in this build");
+  sage_quant_layout L;
+  compute_layout(p, &L);
+  *bytes = L.total + sage::attn_bwd_ws_bytes(to_shape(p));
   return SAGE_OK;
 }
 
@@ -264,7 +267,10 @@ sage_status sage_attn_bwd(const sage_problem* p, const void* q, const void* k, c
   if (s != SAGE_OK) return s;
   if ((s = check_tensors({q, k, v, o, dout, lse, dq, dk, dv, ws})) != SAGE_OK) return s;
   if (ws_bytes < need) return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
-  hipError_t e = sage::launch_attn_bwd(to_shape(p), q, k, v, o, dout, lse, dq, dk, dv, ws, (hipStream_t)stream);
+  sage_quant_layout L;
+  compute_layout(p, &L);
+  hipError_t e = sage::launch_attn_bwd(to_shape(p), q, k, v, o, dout, lse, dq, dk, dv, ws, L.total,
+                                       resolve(ws, p, L), (hipStream_t)stream);
   return e == hipSuccess ? SAGE_OK : hip_fail(e, "backward launch");
 }
 

@@ -7,10 +7,10 @@
 namespace sage {
 
 enum { QK_INT8 = 1, QK_MXFP4 = 3 };
+enum { PV_FP8 = 2, PV_MXFP4 = 3 };
 
 // Padding of the token axis in every quantized buffer (a multiple of the Q tile).
 constexpr int kTokenPad = 128;
-enum { PV_FP8 = 2, PV_MXFP4 = 3 };
 
 // Device pointers of one quantized buffer (offsets resolved on the host).
 struct QuantPtrs {
@@ -37,10 +37,11 @@ hipError_t launch_prologue(const void* q, const void* k, const void* v, const Sh
                            const QuantPtrs& qp, hipStream_t stream);
 hipError_t launch_attn_fwd(const Shape& s, const QuantPtrs& qp, void* o, float* lse, hipStream_t stream);
 
-// Backward: workspace layout is decided by the launcher; returns required bytes when ws == nullptr.
+// Backward: the workspace is [forward quant buffer (qbytes) | backward extras];
+// attn_bwd_ws_bytes gives the size of the extras.  Head dim 64 only.
 size_t attn_bwd_ws_bytes(const Shape& s);
 hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
-                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           void* ws, hipStream_t stream);
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv, void* ws,
+                           size_t qbytes, const QuantPtrs& qp, hipStream_t stream);
 
 }  // namespace sage

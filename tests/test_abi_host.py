@@ -103,7 +103,16 @@ def test_status_strings():
     assert L.sage_status_string(99) == b"unknown status"
 
 
-def test_backward_rejects_non_int8_formats():
+def test_backward_rejects_unsupported_problems():
     L = S.lib()
     n = ctypes.c_size_t()
     assert L.sage_attn_bwd_ws_size(ctypes.byref(_p(qk_fmt=3, pv_fmt=2)), ctypes.byref(n)) == S.ERR_UNSUPPORTED
+    assert L.sage_attn_bwd_ws_size(ctypes.byref(_p(d=128)), ctypes.byref(n)) == S.ERR_UNSUPPORTED
+    assert L.sage_attn_bwd_ws_size(ctypes.byref(_p(d=64)), ctypes.byref(n)) == S.OK
+    quant, _ = S.quant_size(_p(d=64))
+    assert n.value > quant
+    p = _p(d=64)
+    assert L.sage_attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n.value - 1,
+                           None) == S.ERR_WORKSPACE
+    assert L.sage_attn_bwd(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n.value,
+                           None) == S.ERR_INVALID_ARG
