@@ -9,23 +9,29 @@
 // abstract); microscaling FP4 (SageAttention3 abstract) in the OCP MX layout.
 //
 // Two passes over the inputs:
-//   stats:  exact fp64 per-channel token sums of K (and Q), and max |V| per
-//           channel.  Every partial sum of bf16/fp16 values at these sizes is
-//           exactly representable in fp64, so the atomics make the result
-//           independent of order.
-//   codes:  one workgroup per 64-token block: smoothed values, block scales,
-//           codes, the dS / LSE correction terms, V transposed into tiles.
+//   stats:  per token chunk (kChunks chunks per head) exact fp64 per-channel
+//           token sums of K (and Q) and max |V| per channel.  Every partial sum
+//           of bf16/fp16 values at these sizes is exactly representable in fp64,
+//           so the result does not depend on summation order.
+//   codes:  one workgroup per 64-token block reduces the chunk partials (fixed
+//           order), then writes smoothed values' block scales and codes, the
+//           dS / LSE correction terms, and V transposed into tiles.
+// Quotients x / step are formed as q0 = x * r, q = q0 + r * (x - step * q0) with
+// r = 1 / step correctly rounded once per block: for quotients in the normal range
+// this gives the correctly rounded x / step (Markstein's theorem), i.e. the same
+// value as one IEEE division, at a fraction of the cost.
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
 
 namespace sage {
 
-constexpr int kStatRows = 256;   // tokens per stats workgroup
+constexpr int kChunks = kStatChunks;
 
-__global__ void zero_stats_kernel(double* sums, int nsum, uint32_t* amax, int namax) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nsum) sums[i] = 0.0;
-  if (i < namax) amax[i] = 0u;
+// Correctly rounded x / d given r = RN(1 / d) (d > 0, quotient in the normal range).  The
+// correction step turns x = -0 into +0, so the sign is taken from x (d > 0: a no-op for x != 0).
+__device__ __forceinline__ float div_rn(float x, float d, float r) {
+  const float q0 = x * r;
+  return copysignf(fmaf(r, fmaf(-d, q0, x), q0), x);
 }
 
 // 16 bytes = 8 contiguous 16-bit inputs.
@@ -40,20 +46,24 @@ __device__ __forceinline__ void load8(const uint16_t* p, float* x) {
   }
 }
 
-// grid (ceil(N/kStatRows), BH), 256 threads.  Sums K (and Q when SUMQ), max |V| when AMAXV.
+// grid (kChunks, BH), 256 threads.  Chunk c covers tokens [c*CH, (c+1)*CH) with
+// CH = ceil(N / kChunks).  Writes partial sums of K (and Q when SUMQ) and max |V| when
+// AMAXV into sums[c][BH][D] (K), sums[kChunks + c][BH][D] (Q), amax[c][BH][D].
 template <int DT, int D, bool SUMQ, bool AMAXV>
 __global__ __launch_bounds__(256) void stats_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                     const uint16_t* __restrict__ v, int N, int BH,
                                                     double* __restrict__ sums, uint32_t* __restrict__ amax_v) {
   constexpr int C8 = D / 8, RP = 256 / C8;
-  const int bh = blockIdx.y, t0 = blockIdx.x * kStatRows;
+  const int bh = blockIdx.y, c = blockIdx.x;
+  const int CH = (N + kChunks - 1) / kChunks;
+  const int t0 = c * CH, t1 = min(N, t0 + CH);
   const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
   const size_t base = (size_t)bh * N * D;
   double sk[8] = {}, sq[8] = {};
   uint32_t av[8] = {};
-  for (int r = t0 + r0; r < t0 + kStatRows && r < N; r += RP) {
+  for (int r = t0 + r0; r < t1; r += RP) {
     float x[8];
-    load8<DT>(reinterpret_cast<const uint16_t*>(k) + base + (size_t)r * D + c0, x);
+    load8<DT>(k + base + (size_t)r * D + c0, x);
 #pragma unroll
     for (int i = 0; i < 8; i++) sk[i] += (double)x[i];
     if (SUMQ) {
@@ -85,37 +95,57 @@ __global__ __launch_bounds__(256) void stats_kernel(const uint16_t* __restrict__
       if (SUMQ) b += s_q[r][tid];
       if (AMAXV) m = max(m, s_v[r][tid]);
     }
-    atomicAdd(&sums[(size_t)bh * D + tid], a);
-    if (SUMQ) atomicAdd(&sums[(size_t)(BH + bh) * D + tid], b);
-    if (AMAXV) atomicMax(&amax_v[(size_t)bh * D + tid], m);
+    sums[((size_t)c * BH + bh) * D + tid] = a;
+    if (SUMQ) sums[((size_t)(kChunks + c) * BH + bh) * D + tid] = b;
+    if (AMAXV) amax_v[((size_t)c * BH + bh) * D + tid] = m;
   }
 }
 
-// Block-wide max of non-negative float bit patterns (NaN-propagating), 256 threads.
-__device__ __forceinline__ uint32_t block_umax(uint32_t x, uint32_t* red) {
+// Reductions of the chunk partials for channel ch of head bh (fixed order).
+__device__ __forceinline__ float chunk_mean(const double* sums, int part, int BH, int bh, int D, int ch, int N) {
+  double s = 0.0;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  x = max(max(red[0], red[1]), max(red[2], red[3]));
-  __syncthreads();
-  return x;
+  for (int c = 0; c < kChunks; c++) s += sums[((size_t)(part * kChunks + c) * BH + bh) * D + ch];
+  return (float)(s / (double)N);
+}
+__device__ __forceinline__ float chunk_amax(const uint32_t* amax, int BH, int bh, int D, int ch) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int c = 0; c < kChunks; c++) m = max(m, amax[((size_t)c * BH + bh) * D + ch]);
+  return __uint_as_float(m);
 }
 
-__device__ __forceinline__ int8_t int8_code(float x, float delta) {
-  if (delta == 0.0f) return 0;
-  float n = rintf(x / delta);             // correctly rounded fp32 division, then RNE
+// Block-wide max of two non-negative float bit patterns at once (NaN-propagating), 256 threads.
+__device__ __forceinline__ void block_umax2(uint32_t& x, uint32_t& y, uint32_t* red) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    x = max(x, (uint32_t)__shfl_xor((int)x, o));
+    y = max(y, (uint32_t)__shfl_xor((int)y, o));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6] = x;
+    red[4 + (threadIdx.x >> 6)] = y;
+  }
+  __syncthreads();
+  x = max(max(red[0], red[1]), max(red[2], red[3]));
+  y = max(max(red[4], red[5]), max(red[6], red[7]));
+}
+
+// clamp(rne(x / step), -127, 127), x / step correctly rounded via r = 1 / step.
+__device__ __forceinline__ int8_t int8_code(float x, float step, float r) {
+  if (step == 0.0f) return 0;
+  float n = rintf(div_rn(x, step, r));
   n = fminf(fmaxf(n, -127.0f), 127.0f);
   return (int8_t)n;
 }
 
 // Writes this thread's 8 FP8 V codes of token row `rl` into the [D][64] LDS transpose tile.
-__device__ __forceinline__ void put_v_fp8(uint8_t* s_vt, int rl, int c0, const float* x, const float* dv) {
+__device__ __forceinline__ void put_v_fp8(uint8_t* s_vt, int rl, int c0, const float* x, const float* dv, const float* rv) {
 #pragma unroll
   for (int i = 0; i < 8; i += 2) {
-    float a = dv[i] == 0.0f ? 0.0f : x[i] / dv[i];
-    float b = dv[i + 1] == 0.0f ? 0.0f : x[i + 1] / dv[i + 1];
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    const float a = dv[i] == 0.0f ? 0.0f : div_rn(x[i], dv[i], rv[i]);
+    const float b = dv[i + 1] == 0.0f ? 0.0f : div_rn(x[i + 1], dv[i + 1], rv[i + 1]);
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     s_vt[(c0 + i) * 64 + rl] = (uint8_t)(w & 0xff);
     s_vt[(c0 + i + 1) * 64 + rl] = (uint8_t)((w >> 8) & 0xff);
   }
@@ -124,24 +154,32 @@ __device__ __forceinline__ void put_v_fp8(uint8_t* s_vt, int rl, int c0, const f
 // INT8 Q / K codes and FP8 V.  grid (Np/64, BH), 256 threads.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                             const uint16_t* __restrict__ v, int N, int Np, float sm,
-                                                             QuantPtrs qp) {
+                                                             const uint16_t* __restrict__ v, int N, int Np, int BH,
+                                                             float sm, QuantPtrs qp) {
   constexpr int C8 = D / 8, RP = 256 / C8, NP = 64 / RP;
   const int bh = blockIdx.y, blk = blockIdx.x, t0 = blk * 64;
   const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
   const size_t base = (size_t)bh * N * D;
-  __shared__ float s_mu[D];
-  __shared__ uint32_t s_red[4];
+  __shared__ float s_mu[D], s_dv[D];
+  __shared__ uint32_t s_red[8];
   __shared__ __align__(16) uint8_t s_vt[D * 64];
   if (tid < D) {
-    float mu = (float)(qp.sums[(size_t)bh * D + tid] / (double)N);
+    const float mu = chunk_mean(qp.sums, 0, BH, bh, D, tid, N);
+    const float dvs = chunk_amax(qp.amax_v, BH, bh, D, tid) / 448.0f;
     s_mu[tid] = mu;
-    if (blk == 0) qp.mu_k[(size_t)bh * D + tid] = mu;
+    s_dv[tid] = dvs;
+    if (blk == 0) {
+      qp.mu_k[(size_t)bh * D + tid] = mu;
+      reinterpret_cast<float*>(qp.v_scales)[(size_t)bh * D + tid] = dvs;
+    }
   }
   __syncthreads();
-  float dv[8];
+  float dv[8], rv[8];
 #pragma unroll
-  for (int i = 0; i < 8; i++) dv[i] = __uint_as_float(qp.amax_v[(size_t)bh * D + c0 + i]) / 448.0f;
+  for (int i = 0; i < 8; i++) {
+    dv[i] = s_dv[c0 + i];
+    rv[i] = 1.0f / dv[i];
+  }
   float xq[NP][8], xk[NP][8];
   uint32_t aq = 0, ak = 0;
 #pragma unroll
@@ -152,7 +190,7 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
       load8<DT>(q + base + (size_t)row * D + c0, xq[p]);
       load8<DT>(k + base + (size_t)row * D + c0, xk[p]);
       load8<DT>(v + base + (size_t)row * D + c0, xv);
-      put_v_fp8(s_vt, rl, c0, xv, dv);
+      put_v_fp8(s_vt, rl, c0, xv, dv, rv);
       float cs = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; i++) {
@@ -174,8 +212,9 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
       }
     }
   }
-  const float dq = __uint_as_float(block_umax(aq, s_red)) / 127.0f;
-  const float dk = __uint_as_float(block_umax(ak, s_red)) / 127.0f;
+  block_umax2(aq, ak, s_red);
+  const float dq = __uint_as_float(aq) / 127.0f, dk = __uint_as_float(ak) / 127.0f;
+  const float rq = 1.0f / dq, rk = 1.0f / dk;
   if (tid == 0) {
     reinterpret_cast<float*>(qp.q_scales)[(size_t)bh * (Np / 64) + blk] = dq;
     reinterpret_cast<float*>(qp.k_scales)[(size_t)bh * (Np / 64) + blk] = dk;
@@ -186,8 +225,8 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
     uint32_t wq[2] = {0, 0}, wk[2] = {0, 0};
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      wq[i / 4] |= (uint32_t)(uint8_t)int8_code(xq[p][i], dq) << (8 * (i % 4));
-      wk[i / 4] |= (uint32_t)(uint8_t)int8_code(xk[p][i], dk) << (8 * (i % 4));
+      wq[i / 4] |= (uint32_t)(uint8_t)int8_code(xq[p][i], dq, rq) << (8 * (i % 4));
+      wk[i / 4] |= (uint32_t)(uint8_t)int8_code(xk[p][i], dk, rk) << (8 * (i % 4));
     }
     const size_t off = ((size_t)bh * Np + row) * D + c0;
     *reinterpret_cast<uint2*>(qp.q_codes + off) = make_uint2(wq[0], wq[1]);
@@ -198,7 +237,6 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
   uint8_t* dst = qp.v_codes + ((size_t)bh * (Np / 64) + blk) * D * 64;
   for (int c = tid; c < D * 4; c += 256)
     *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(s_vt + c * 16);
-  if (blk == 0 && tid < D) reinterpret_cast<float*>(qp.v_scales)[(size_t)bh * D + tid] = __uint_as_float(qp.amax_v[(size_t)bh * D + tid]) / 448.0f;
 }
 
 // MXFP4 Q_s and K_s codes (32-channel blocks), dS and LSE correction; V in FP8
@@ -214,21 +252,27 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
   __shared__ float s_mk[D], s_mq[D];
   __shared__ __align__(16) uint8_t s_vt[PV == PV_FP8 ? D * 64 : 1];
   __shared__ float s_vf[PV == PV_MXFP4 ? 64 : 1][PV == PV_MXFP4 ? D + 1 : 1];
+  __shared__ float s_dv[PV == PV_FP8 ? D : 1];
   if (tid < D) {
-    float mk = (float)(qp.sums[(size_t)bh * D + tid] / (double)N);
-    float mq = (float)(qp.sums[(size_t)(BH + bh) * D + tid] / (double)N);
+    const float mk = chunk_mean(qp.sums, 0, BH, bh, D, tid, N);
+    const float mq = chunk_mean(qp.sums, 1, BH, bh, D, tid, N);
     s_mk[tid] = mk;
     s_mq[tid] = mq;
+    if (PV == PV_FP8) s_dv[tid] = chunk_amax(qp.amax_v, BH, bh, D, tid) / 448.0f;
     if (blk == 0) {
       qp.mu_k[(size_t)bh * D + tid] = mk;
       qp.mu_q[(size_t)bh * D + tid] = mq;
+      if (PV == PV_FP8) reinterpret_cast<float*>(qp.v_scales)[(size_t)bh * D + tid] = s_dv[tid];
     }
   }
   __syncthreads();
-  float dv[8];
+  float dv[8], rv[8];
   if (PV == PV_FP8) {
 #pragma unroll
-    for (int i = 0; i < 8; i++) dv[i] = __uint_as_float(qp.amax_v[(size_t)bh * D + c0 + i]) / 448.0f;
+    for (int i = 0; i < 8; i++) {
+      dv[i] = s_dv[c0 + i];
+      rv[i] = 1.0f / dv[i];
+    }
   }
   uint8_t* qe = reinterpret_cast<uint8_t*>(qp.q_scales);
   uint8_t* ke = reinterpret_cast<uint8_t*>(qp.k_scales);
@@ -284,7 +328,7 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
     }
     if (PV == PV_FP8) {
       if (row < N) {
-        put_v_fp8(s_vt, rl, c0, xv, dv);
+        put_v_fp8(s_vt, rl, c0, xv, dv, rv);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; i++) s_vt[(c0 + i) * 64 + rl] = 0;
@@ -299,8 +343,6 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
     uint8_t* dst = qp.v_codes + ((size_t)bh * (Np / 64) + blk) * D * 64;
     for (int c = tid; c < D * 4; c += 256)
       *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(s_vt + c * 16);
-    if (blk == 0 && tid < D)
-      reinterpret_cast<float*>(qp.v_scales)[(size_t)bh * D + tid] = __uint_as_float(qp.amax_v[(size_t)bh * D + tid]) / 448.0f;
   } else {
     // one thread per (channel, 32-token group)
     for (int w = tid; w < D * 2; w += 256) {
@@ -330,13 +372,11 @@ static hipError_t prologue_dispatch(const void* q, const void* k, const void* v,
                                     hipStream_t st) {
   const int BH = s.B * s.H;
   const uint16_t *Q = (const uint16_t*)q, *K = (const uint16_t*)k, *V = (const uint16_t*)v;
-  const int nsum = 2 * BH * D, namax = BH * D;
-  zero_stats_kernel<<<(nsum + 255) / 256, 256, 0, st>>>(qp.sums, nsum, qp.amax_v, namax);
-  dim3 sg((s.N + kStatRows - 1) / kStatRows, BH), qg(s.Np / 64, BH);
+  dim3 sg(kChunks, BH), qg(s.Np / 64, BH);
   const bool mx = s.qk_fmt == QK_MXFP4, fp8v = s.pv_fmt == PV_FP8;
   if (!mx) {
     stats_kernel<DT, D, false, true><<<sg, 256, 0, st>>>(Q, K, V, s.N, BH, qp.sums, qp.amax_v);
-    quant_int8_fp8_kernel<DT, D><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, s.sm_scale, qp);
+    quant_int8_fp8_kernel<DT, D><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BH, s.sm_scale, qp);
   } else if (fp8v) {
     stats_kernel<DT, D, true, true><<<sg, 256, 0, st>>>(Q, K, V, s.N, BH, qp.sums, qp.amax_v);
     quant_mxfp4_kernel<DT, D, PV_FP8><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BH, s.sm_scale, qp);

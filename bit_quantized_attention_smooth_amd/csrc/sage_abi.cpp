@@ -96,7 +96,7 @@ void compute_layout(const sage_problem* p, sage_quant_layout* L) {
   L->v_scales = take(mxv ? BH * (Np / 32) * d : BH * d * 4);
   L->delta_s = take(BH * Np * 4);
   L->lse_corr = take(BH * N * 4);
-  L->stats = take(BH * d * 8 * 2 + BH * d * 4);
+  L->stats = take(sage::kStatChunks * (BH * d * 8 * 2 + BH * d * 4));
   L->total = off;
 }
 
@@ -115,7 +115,7 @@ sage::QuantPtrs resolve(void* buf, const sage_problem* p, const sage_quant_layou
   q.delta_s = reinterpret_cast<float*>(b + L.delta_s);
   q.lse_corr = reinterpret_cast<float*>(b + L.lse_corr);
   q.sums = reinterpret_cast<double*>(b + L.stats);
-  q.amax_v = reinterpret_cast<uint32_t*>(b + L.stats + BH * p->d * 8 * 2);
+  q.amax_v = reinterpret_cast<uint32_t*>(b + L.stats + sage::kStatChunks * BH * p->d * 8 * 2);
   return q;
 }
 

@@ -11,6 +11,8 @@ enum { PV_FP8 = 2, PV_MXFP4 = 3 };
 
 // Padding of the token axis in every quantized buffer (a multiple of the Q tile).
 constexpr int kTokenPad = 128;
+// Token chunks per head of the smoothing statistics (partial sums are kept per chunk).
+constexpr int kStatChunks = 8;
 
 // Device pointers of one quantized buffer (offsets resolved on the host).
 struct QuantPtrs {

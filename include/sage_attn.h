@@ -87,7 +87,7 @@ typedef struct {
  *             [BH, Np/32, d] per 32-token group per channel
  *   delta_s   fp32 [BH, Np]    mu_q . (k_t - mu_k), added to every score (MXFP4 QK)
  *   lse_corr  fp32 [BH, N]     sm_scale * q_t . mu_k, added to the LSE only
- *   stats     fp64 / uint32 scratch of the smoothing reduction
+ *   stats     fp64 / uint32 per-chunk partials of the smoothing statistics (scratch)
  */
 typedef struct {
     size_t mu_k, mu_q, q_codes, q_scales, k_codes, k_scales, v_codes, v_scales,
@@ -136,8 +136,10 @@ sage_status sage_attn_bwd_ws_size(const sage_problem *p, size_t *bytes);
 /*
  * 8-bit backward.  q, k, v, o, dout: device [B,H,N,d] (bf16 or fp16 as
  * p->io_dtype; o is the forward output); lse: device fp32 [B,H,N] from the
- * forward; dq, dk, dv: device outputs [B,H,N,d].  p->qk_fmt must be INT8 and
- * p->pv_fmt FP8.  ws: device workspace of at least sage_attn_bwd_ws_size bytes.
+ * forward; dq, dk, dv: device outputs [B,H,N,d].  p->qk_fmt must be INT8,
+ * p->pv_fmt FP8 and p->d 64 (other problems: SAGE_ERR_UNSUPPORTED).  ws: device
+ * workspace of at least sage_attn_bwd_ws_size bytes (the forward's quantized
+ * buffer followed by the backward's operand tiles).
  */
 sage_status sage_attn_bwd(const sage_problem *p, const void *q, const void *k, const void *v,
                           const void *o, const void *dout, const float *lse,
