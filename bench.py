@@ -6,8 +6,17 @@ headline workload is the LLM-prefill shape (INT8 QK^T, FP8 P~V, causal,
 B=1 H=32 N=4096 d=128).  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra] [--copy-calib]
+  python bench.py --traffic FETCH_DIR WRITE_DIR   (turn two rocprofv3 --pmc runs into a profile summary)
+
+Roofline traffic: run this script twice under rocprofv3 with --copy-calib, once with
+--pmc FETCH_SIZE and once with --pmc WRITE_SIZE (--output-format csv), then
+--traffic on the two output directories.  The summary lands in profiles/ with a hash of
+the kernel sources; the bench reports it as roofline.traffic only while the hash matches.
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -22,6 +31,75 @@ METRIC = "attention TOPS (4·B·H·N²·d/s, ½ if causal) at d=128; % of MI355X
 # MI355X dense peaks (TFLOP/s or TOP/s)
 PEAK = {"int8_fp8": 5000.0, "mxfp4_fp8": 1.0 / (0.5 / 10100.0 + 0.5 / 5000.0), "mxfp4": 10100.0}
 HBM_PEAK_GBS = 8000.0
+COPY_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_int8_fp8_causal_b1h32n4096d128.txt")
+KERNEL_SOURCES = ["bit_quantized_attention_smooth_amd/csrc/attn_fwd.hip",
+                  "bit_quantized_attention_smooth_amd/csrc/sage_device.hpp"]
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the fused kernel from the committed counter summary, if current."""
+    try:
+        kv = dict(line.strip().split("=", 1) for line in open(TRAFFIC_FILE) if "=" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("source_sha256_16") != kernel_hash():
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def counters(path, name):
+    """Mean per-dispatch value of counter `name` for our fused kernel, and the copy kernel's value."""
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    per = {}
+    kname = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != name:
+                continue
+            key = (f, r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+            kname[key] = r["Kernel_Name"]
+    ours = [v for k, v in per.items() if "attn_fwd_kernel" in kname[k]]
+    others = [v for k, v in per.items() if "sage" not in kname[k]]
+    return sum(ours) / len(ours), max(others)
+
+
+def traffic_summary(fetch_dir, write_dir):
+    f_k, f_copy = counters(fetch_dir, "FETCH_SIZE")
+    w_k, w_copy = counters(write_dir, "WRITE_SIZE")
+    # the counters are in KiB; calibrate each by a plain copy of COPY_BYTES
+    ff = COPY_BYTES / (f_copy * 1024.0)
+    fw = COPY_BYTES / (w_copy * 1024.0)
+    total = f_k * 1024.0 * ff + w_k * 1024.0 * fw
+    lines = [
+        "# HBM traffic of attn_fwd_kernel<128, INT8, causal, bf16> on the headline workload",
+        "# (B=1 H=32 N=4096 d=128, causal, INT8-QK / FP8-PV), from two rocprofv3 counter runs:",
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python bench.py --steps 3 --warmup 1 --no-cpu --no-extra --copy-calib",
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python bench.py --steps 3 --warmup 1 --no-cpu --no-extra --copy-calib",
+        "#   python bench.py --traffic <fetch_dir> <write_dir>",
+        "# Each counter (KiB per dispatch, averaged over the kernel's dispatches) is scaled by",
+        f"# COPY_BYTES / (counter of a plain {COPY_BYTES >> 20} MiB device copy in the same run).",
+        f"fetch_kib_per_launch={f_k:.1f}",
+        f"write_kib_per_launch={w_k:.1f}",
+        f"copy_fetch_kib={f_copy:.1f}",
+        f"copy_write_kib={w_copy:.1f}",
+        f"fetch_scale={ff:.4f}",
+        f"write_scale={fw:.4f}",
+        f"hbm_bytes_per_launch={total:.0f}",
+        f"source_sha256_16={kernel_hash()}",
+    ]
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def attn_ops(B, H, N, d, causal):
@@ -91,6 +169,45 @@ def run_workload(name, S, torch, steps, warmup):
                 prologue_gbs=pro_bytes / (ms_pro * 1e-3) / 1e9)
 
 
+def run_backward(name, S, torch, steps, warmup):
+    """Forward (with LSE) and the 8-bit backward of the training workload."""
+    import ctypes
+    from bit_quantized_attention_smooth_amd.workloads import workload_inputs
+    x, w = workload_inputs(name)
+    dev = torch.device("cuda:0")
+    g = {n: x[n].to(dev) for n in ("q", "k", "v", "do")}
+    B, H, N, d, causal = w["B"], w["H"], w["N"], w["d"], w["causal"]
+    p = S.problem(B, H, N, d, causal=causal, sm_scale=w["sm_scale"], dtype=g["q"].dtype)
+    L = S.lib()
+    nf, nb = ctypes.c_size_t(), ctypes.c_size_t()
+    S._check(L.sage_attn_fwd_ws_size(ctypes.byref(p), ctypes.byref(nf)))
+    S._check(L.sage_attn_bwd_ws_size(ctypes.byref(p), ctypes.byref(nb)))
+    wsf = torch.empty(nf.value, dtype=torch.uint8, device=dev)
+    wsb = torch.empty(nb.value, dtype=torch.uint8, device=dev)
+    o = torch.empty_like(g["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(g["q"]) for _ in range(3))
+    st = S._stream()
+
+    def fwd():
+        S._check(L.sage_attn_fwd_ex(ctypes.byref(p), S._ptr(g["q"]), S._ptr(g["k"]), S._ptr(g["v"]), S._ptr(o),
+                                    S._ptr(lse), S._ptr(wsf), nf.value, st))
+
+    def bwd():
+        S._check(L.sage_attn_bwd(ctypes.byref(p), S._ptr(g["q"]), S._ptr(g["k"]), S._ptr(g["v"]), S._ptr(o),
+                                 S._ptr(g["do"]), S._ptr(lse), S._ptr(dq), S._ptr(dk), S._ptr(dv), S._ptr(wsb),
+                                 nb.value, st))
+
+    ms_f, _ = time_region(fwd, steps, warmup, torch)
+    fwd()
+    ms_b, _ = time_region(bwd, steps, warmup, torch)
+    ops_f = attn_ops(B, H, N, d, causal)
+    ops_b = 2.5 * ops_f          # 10 d ops per (query, key) pair vs 4 d in the forward
+    return {"fwd_ms": round(ms_f, 4), "fwd_tops": round(ops_f / (ms_f * 1e-3) / 1e12, 1),
+            "bwd_ms": round(ms_b, 4), "bwd_tops": round(ops_b / (ms_b * 1e-3) / 1e12, 1),
+            "bwd_frac": round(ops_b / (ms_b * 1e-3) / 1e12 / PEAK["int8_fp8"], 4)}
+
+
 def cpu_baseline(name):
     """The CPU oracle (prologue + tiled quantized forward) on a bounded sample of heads."""
     import numpy as np
@@ -126,7 +243,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--copy-calib", action="store_true", help="run one 1 GiB device copy at the end (counter calibration)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the roofline traffic summary from two rocprofv3 counter runs and exit")
     args = ap.parse_args()
+    if args.traffic:
+        traffic_summary(*args.traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (heads shard over GPUs without "
               f"exchange, so N GPUs would run N independent copies of this step)", file=sys.stderr)
@@ -147,7 +269,7 @@ def main():
         "config": {"workload": HEADLINE, "B": r["B"], "H": r["H"], "N": r["N"], "d": r["d"], "causal": r["causal"],
                    "qk_fmt": r["qk"], "pv_fmt": r["pv"], "io_dtype": r["dtype"], "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK[path], "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK[path], 4), "traffic": None,
+                     "frac": round(achieved / PEAK[path], 4), "traffic": read_traffic(),
                      "kernel": "attn_fwd_kernel<128, INT8, causal, bf16>", "kernel_ms": round(r["ms_kernel"], 5)},
         "prologue": {"ms": round(r["ms_prologue"], 5), "algorithmic_bytes": r["pro_bytes"],
                      "GB/s": round(r["prologue_gbs"], 1), "frac_of_hbm": round(r["prologue_gbs"] / HBM_PEAK_GBS, 4)},
@@ -163,15 +285,18 @@ def main():
                            "step_tops": round(e["step_tops"], 1), "kernel_ms": round(e["ms_kernel"], 4),
                            "prologue_GB/s": round(e["prologue_gbs"], 1)}
             torch.cuda.empty_cache()
+        log("[bench] secondary train_causal_b8h16n2048d64 (forward + 8-bit backward)")
+        extra["train_causal_b8h16n2048d64"] = run_backward("train_causal_b8h16n2048d64", S, torch,
+                                                           max(5, args.steps // 5), 3)
         out["other_workloads"] = extra
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(HEADLINE)
     if args.copy_calib:
-        log("[bench] copy calibration: 1 GiB device-to-device copy")
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        log("[bench] copy calibration: 1 GiB read + 1 GiB write elementwise kernel")
+        src = torch.zeros(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
     print(json.dumps(out), flush=True)
 
