@@ -10,21 +10,25 @@
 //   dP  = dO V^T         FP8, per-64-token-block steps of dO and V (they factor out of
 //                        the channel sum)
 //   dS  = P o (dP - D),  D_i = sum_c dO_ic O_ic
-//   dV  = P~^T dO        FP8: P~ = E4M3(448 P), dO per-channel steps (factor out of the
-//                        query sum)
-//   dK  = sm dS~^T Q     INT8: dS~ = INT8 codes of dS with one step per wave tile
-//   dQ  = sm (dS~ K_s - rowsum(dS) P K_s)  INT8.  With quantized dP the rows of dS no
-//                        longer sum to 0: rowsum(dS) = D^ - D, where D^ = sum_j P dP^ is
-//                        the value consistent with the quantized dP.  Replacing D by D^
-//                        turns dS into dS - P rowsum(dS); for dQ that is the second term
-//                        (the mu_k part of K = K_s + mu_k cancels since sum_j P = 1), and
-//                        the dQ kernel runs first and hands D^ to the dK/dV kernel.
-// Two kernels, both forward-shaped, so every operand reaches the MFMA straight from
-// registers or LDS: a key-stationary kernel (a wave owns 32 keys, loops over query
-// tiles, accumulates dK^T and dV^T) and a query-stationary kernel (a wave owns 32
-// queries, loops over key tiles, accumulates dQ^T).  A prologue writes the operand
-// layouts they need: dO and V in FP8 token-major with block steps, dO^T in FP8 with
-// channel steps, Q^T and K_s^T INT8 tiles, D and the smoothed-domain LSE in log2 units.
+//   dV  = P~^T dO        FP8: P~ = E4M3(448 P), dO^T with per-channel steps (they factor
+//                        out of the query sum)
+//   dK  = sm dS^T Q      FP8: Q^T with per-channel steps; dS in E4M3 with one power-of-two
+//                        scale per 32-element block (an MX block), applied by the scaled MFMA
+//   dQ  = sm (dS K_s - rowsum(dS) P K_s)  FP8 the same way, K_s^T with per-channel steps.
+//                        With quantized dP the rows of dS no longer sum to 0: rowsum(dS) =
+//                        D^ - D, where D^ = sum_j P dP^ is the value consistent with the
+//                        quantized dP.  Replacing D by D^ turns dS into dS - P rowsum(dS); for
+//                        dQ that is the second term (the mu_k part of K = K_s + mu_k cancels
+//                        since sum_j P = 1), and the dQ kernel runs first and hands D^ to the
+//                        dK/dV kernel.
+// Every step that varies from tile to tile is either a power of two taken by the scaled
+// MFMA or factors out of the whole contraction, so the accumulators never need a per-tile
+// rescale on the vector unit.  Two kernels, both forward-shaped, so every operand reaches
+// the MFMA straight from registers or LDS: a key-stationary kernel (a wave owns 32 keys,
+// loops over query tiles, accumulates dK^T and dV^T) and a query-stationary kernel (a wave
+// owns 32 queries, loops over key tiles, accumulates dQ^T).  A prologue writes the operand
+// layouts they need: dO and V in FP8 token-major with block steps, dO^T, Q^T and K_s^T in
+// FP8 with channel steps, D and the smoothed-domain LSE in log2 units.
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
 
@@ -33,6 +37,7 @@ namespace sage {
 namespace {
 
 constexpr int kT = 64;   // query / key tile (= INT8 and FP8 block)
+constexpr int kNT = 3;   // channel-step tensors: dO, Q, K_s
 
 // Row of the 64-row operand tile fed to MFMA A-row m in subtile s, so that output lane
 // half h holds tile positions 32h + 16s + r (r = register index).
@@ -52,17 +57,17 @@ struct BwdPtrs {
   const float* mu_k;
   const float* lse_corr;
   // backward prologue outputs
-  uint32_t* amax_do;      // [BH, d] max |dO| per channel (bit patterns)
+  uint32_t* amax_part;    // [3, kStatChunks, BH, d] max |x| per token chunk and channel (bit patterns)
+  float* chan_step;       // [3, BH, d] channel steps of dO^T, Q^T, K_s^T codes
   float* Dvec;            // [BH, Np]
-  float* lse2;            // [BH, Np] (LSE - c) log2 e; +inf for padding queries
+  float* lse2;            // [BH, Np] (LSE - c) log2 e - log2 448; +inf for padding queries
   uint8_t* do_codes;      // [BH, Np, d] E4M3, token-major
   float* do_step;         // [BH, nb]
-  uint8_t* doT_codes;     // [BH, Np/64, d, 64] E4M3 of dO / channel step
-  float* doT_step;        // [BH, d]
   uint8_t* v_codes;       // [BH, Np, d] E4M3, token-major
   float* v_step;          // [BH, nb]
-  int8_t* qT_codes;       // [BH, Np/64, d, 64]
-  int8_t* kT_codes;       // [BH, Np/64, d, 64]
+  uint8_t* doT_codes;     // [BH, Np/64, d, 64] E4M3 of dO / channel step
+  uint8_t* qT_codes;      // [BH, Np/64, d, 64] E4M3 of Q / channel step
+  uint8_t* kT_codes;      // [BH, Np/64, d, 64] E4M3 of (K - mu_k) / channel step
 };
 
 template <int DT>
@@ -76,31 +81,43 @@ __device__ __forceinline__ void load8io(const uint16_t* p, float* x) {
   }
 }
 
-__global__ void bwd_zero_kernel(uint32_t* p, int n) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
-
-// max |dO| per channel.  grid (ceil(N/256), BH), 256 threads.
+// max |dO|, |Q|, |K - mu_k| per channel over one of kStatChunks token chunks of a head;
+// partials, so no buffer needs clearing first.  grid (kStatChunks, BH), 256 threads.
 template <int DT, int D>
-__global__ __launch_bounds__(256) void bwd_stats_kernel(const uint16_t* __restrict__ dout, int N, uint32_t* amax) {
+__global__ __launch_bounds__(256) void bwd_stats_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict__ q,
+                                                        const uint16_t* __restrict__ k, const float* __restrict__ mu_k,
+                                                        int N, uint32_t* __restrict__ part) {
   constexpr int C8 = D / 8, RP = 256 / C8;
-  const int bh = blockIdx.y, t0 = blockIdx.x * 256, tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
-  uint32_t a[8] = {};
-  for (int r = t0 + r0; r < t0 + 256 && r < N; r += RP) {
-    float x[8];
-    load8io<DT>(dout + ((size_t)bh * N + r) * D + c0, x);
+  const int bh = blockIdx.y, ch = blockIdx.x, BH = gridDim.y, tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
+  const int len = (N + kStatChunks - 1) / kStatChunks, t0 = ch * len, t1 = min(N, t0 + len);
+  float mu[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) a[i] = max(a[i], __float_as_uint(fabsf(x[i])));
+  for (int i = 0; i < 8; i++) mu[i] = mu_k[(size_t)bh * D + c0 + i];
+  uint32_t a[kNT][8] = {};
+  for (int r = t0 + r0; r < t1; r += RP) {
+    const size_t off = ((size_t)bh * N + r) * D + c0;
+    float x[kNT][8];
+    load8io<DT>(dout + off, x[0]);
+    load8io<DT>(q + off, x[1]);
+    load8io<DT>(k + off, x[2]);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      a[0][i] = max(a[0][i], __float_as_uint(fabsf(x[0][i])));
+      a[1][i] = max(a[1][i], __float_as_uint(fabsf(x[1][i])));
+      a[2][i] = max(a[2][i], __float_as_uint(fabsf(x[2][i] - mu[i])));
+    }
   }
-  __shared__ uint32_t s_a[RP][D];
+  __shared__ uint32_t s_a[kNT][RP][D];
 #pragma unroll
-  for (int i = 0; i < 8; i++) s_a[r0][c0 + i] = a[i];
+  for (int t = 0; t < kNT; t++)
+#pragma unroll
+    for (int i = 0; i < 8; i++) s_a[t][r0][c0 + i] = a[t][i];
   __syncthreads();
-  if (tid < D) {
+  for (int j = tid; j < kNT * D; j += 256) {
+    const int t = j / D, c = j % D;
     uint32_t m = 0;
-    for (int r = 0; r < RP; r++) m = max(m, s_a[r][tid]);
-    atomicMax(&amax[(size_t)bh * D + tid], m);
+    for (int r = 0; r < RP; r++) m = max(m, s_a[t][r][c]);
+    part[(((size_t)t * kStatChunks + ch) * BH + bh) * D + c] = m;
   }
 }
 
@@ -114,86 +131,95 @@ __device__ __forceinline__ uint32_t block_umax4(uint32_t x, uint32_t* red) {
   return x;
 }
 
-// Per 64-token block: D, lse2, dO / V token-major FP8 with block steps, dO^T FP8 with
-// channel steps, Q^T and K_s^T INT8 tiles.  grid (Np/64, BH), 256 threads.
+// Per 64-token block: D, lse2, dO / V token-major FP8 with block steps, dO^T / Q^T / K_s^T
+// FP8 with channel steps.  grid (Np/64, BH), 256 threads.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-                                                       const uint16_t* __restrict__ v, const float* __restrict__ lse,
+                                                       const uint16_t* __restrict__ v, const uint16_t* __restrict__ q,
+                                                       const uint16_t* __restrict__ k, const float* __restrict__ lse,
                                                        int N, int Np, BwdPtrs bp) {
   constexpr int C8 = D / 8, RP = 256 / C8, NP = 64 / RP;
-  const int bh = blockIdx.y, blk = blockIdx.x, t0 = blk * 64;
+  const int bh = blockIdx.y, blk = blockIdx.x, t0 = blk * 64, BH = gridDim.y;
   const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
   const int nb = Np / 64;
   __shared__ uint32_t s_red[4];
-  __shared__ __align__(16) uint8_t s_doT[D * 64];
-  __shared__ __align__(16) int8_t s_qT[D * 64];
-  __shared__ __align__(16) int8_t s_kT[D * 64];
-  float dcs[8];
+  __shared__ float s_inv[kNT][D];
+  __shared__ __align__(16) uint8_t s_T[kNT][D * 64];
+  // channel steps from the chunk partials: code = x * 448 / amax
+  for (int j = tid; j < kNT * D; j += 256) {
+    const int t = j / D, c = j % D;
+    uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < 8; i++) dcs[i] = __uint_as_float(bp.amax_do[(size_t)bh * D + c0 + i]) / 448.0f;
+    for (int ch = 0; ch < kStatChunks; ch++) m = max(m, bp.amax_part[(((size_t)t * kStatChunks + ch) * BH + bh) * D + c]);
+    const float am = __uint_as_float(m);
+    s_inv[t][c] = am == 0.0f ? 0.0f : 448.0f / am;
+    if (blk == 0) bp.chan_step[((size_t)t * BH + bh) * D + c] = am / 448.0f;
+  }
+  float mu[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) mu[i] = bp.mu_k[(size_t)bh * D + c0 + i];
+  __syncthreads();
   float xd[NP][8], xv[NP][8];
   uint32_t ad = 0, av = 0;
 #pragma unroll
   for (int p = 0; p < NP; p++) {
     const int rl = r0 + p * RP, row = t0 + rl;
-    float dsum = 0.0f;
+    float dsum = 0.0f, xq[8], xk[8];
     if (row < N) {
       float xo[8];
       const size_t off = ((size_t)bh * N + row) * D + c0;
       load8io<DT>(dout + off, xd[p]);
       load8io<DT>(o + off, xo);
       load8io<DT>(v + off, xv[p]);
+      load8io<DT>(q + off, xq);
+      load8io<DT>(k + off, xk);
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         dsum += xd[p][i] * xo[i];
         ad = max(ad, __float_as_uint(fabsf(xd[p][i])));
         av = max(av, __float_as_uint(fabsf(xv[p][i])));
+        xk[i] -= mu[i];
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; i++) xd[p][i] = xv[p][i] = 0.0f;
+      for (int i = 0; i < 8; i++) xd[p][i] = xv[p][i] = xq[i] = xk[i] = 0.0f;
     }
 #pragma unroll
     for (int o2 = 1; o2 < C8; o2 <<= 1) dsum += __shfl_xor(dsum, o2);
     if ((tid % C8) == 0) {
       bp.Dvec[(size_t)bh * Np + row] = dsum;
       bp.lse2[(size_t)bh * Np + row] =
-          row < N ? (lse[(size_t)bh * N + row] - bp.lse_corr[(size_t)bh * N + row]) * kLog2e : INFINITY;
+          row < N ? (lse[(size_t)bh * N + row] - bp.lse_corr[(size_t)bh * N + row]) * kLog2e - kLog2_448 : INFINITY;
     }
-    // dO^T with per-channel steps, and the Q^T / K_s^T transposes, through LDS
+    // channel-step codes, transposed through LDS
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
-      const float a0 = dcs[i] == 0.0f ? 0.0f : xd[p][i] / dcs[i];
-      const float a1 = dcs[i + 1] == 0.0f ? 0.0f : xd[p][i + 1] / dcs[i + 1];
-      const int w2 = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
-      s_doT[(c0 + i) * 64 + rl] = (uint8_t)(w2 & 0xff);
-      s_doT[(c0 + i + 1) * 64 + rl] = (uint8_t)((w2 >> 8) & 0xff);
-    }
-    const uint2 qc = *reinterpret_cast<const uint2*>(bp.q_codes + ((size_t)bh * Np + row) * D + c0);
-    const uint2 kc = *reinterpret_cast<const uint2*>(bp.k_codes + ((size_t)bh * Np + row) * D + c0);
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      s_qT[(c0 + i) * 64 + rl] = (int8_t)(((i < 4 ? qc.x : qc.y) >> (8 * (i % 4))) & 0xff);
-      s_kT[(c0 + i) * 64 + rl] = (int8_t)(((i < 4 ? kc.x : kc.y) >> (8 * (i % 4))) & 0xff);
+      const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(xd[p][i] * s_inv[0][c0 + i], xd[p][i + 1] * s_inv[0][c0 + i + 1], 0, false);
+      const int wq = __builtin_amdgcn_cvt_pk_fp8_f32(xq[i] * s_inv[1][c0 + i], xq[i + 1] * s_inv[1][c0 + i + 1], 0, false);
+      const int wk = __builtin_amdgcn_cvt_pk_fp8_f32(xk[i] * s_inv[2][c0 + i], xk[i + 1] * s_inv[2][c0 + i + 1], 0, false);
+      s_T[0][(c0 + i) * 64 + rl] = (uint8_t)(wd & 0xff);
+      s_T[0][(c0 + i + 1) * 64 + rl] = (uint8_t)((wd >> 8) & 0xff);
+      s_T[1][(c0 + i) * 64 + rl] = (uint8_t)(wq & 0xff);
+      s_T[1][(c0 + i + 1) * 64 + rl] = (uint8_t)((wq >> 8) & 0xff);
+      s_T[2][(c0 + i) * 64 + rl] = (uint8_t)(wk & 0xff);
+      s_T[2][(c0 + i + 1) * 64 + rl] = (uint8_t)((wk >> 8) & 0xff);
     }
   }
-  const float sd = __uint_as_float(block_umax4(ad, s_red)) / 448.0f;
-  const float sv = __uint_as_float(block_umax4(av, s_red)) / 448.0f;
+  const uint32_t amd = block_umax4(ad, s_red), amv = block_umax4(av, s_red);
+  const float sd = __uint_as_float(amd) / 448.0f, sv = __uint_as_float(amv) / 448.0f;
+  const float id = amd == 0 ? 0.0f : 448.0f / __uint_as_float(amd), iv = amv == 0 ? 0.0f : 448.0f / __uint_as_float(amv);
   if (tid == 0) {
     bp.do_step[(size_t)bh * nb + blk] = sd;
     bp.v_step[(size_t)bh * nb + blk] = sv;
   }
-  if (blk == 0 && tid < D) bp.doT_step[(size_t)bh * D + tid] = __uint_as_float(bp.amax_do[(size_t)bh * D + tid]) / 448.0f;
 #pragma unroll
   for (int p = 0; p < NP; p++) {
     const int row = t0 + r0 + p * RP;
     uint32_t wd[2] = {0, 0}, wv[2] = {0, 0};
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
-      const float d0 = sd == 0.0f ? 0.0f : xd[p][i] / sd, d1 = sd == 0.0f ? 0.0f : xd[p][i + 1] / sd;
-      const float v0 = sv == 0.0f ? 0.0f : xv[p][i] / sv, v1 = sv == 0.0f ? 0.0f : xv[p][i + 1] / sv;
-      wd[i / 4] |= (uint32_t)(__builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false) & 0xffff) << (8 * (i % 4));
-      wv[i / 4] |= (uint32_t)(__builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false) & 0xffff) << (8 * (i % 4));
+      wd[i / 4] |= (uint32_t)(__builtin_amdgcn_cvt_pk_fp8_f32(xd[p][i] * id, xd[p][i + 1] * id, 0, false) & 0xffff) << (8 * (i % 4));
+      wv[i / 4] |= (uint32_t)(__builtin_amdgcn_cvt_pk_fp8_f32(xv[p][i] * iv, xv[p][i + 1] * iv, 0, false) & 0xffff) << (8 * (i % 4));
     }
     const size_t off = ((size_t)bh * Np + row) * D + c0;
     *reinterpret_cast<uint2*>(bp.do_codes + off) = make_uint2(wd[0], wd[1]);
@@ -202,13 +228,28 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
   __syncthreads();
   const size_t tb = ((size_t)bh * nb + blk) * D * 64;
   for (int c = tid; c < D * 4; c += 256) {
-    *reinterpret_cast<uint4*>(bp.doT_codes + tb + c * 16) = *reinterpret_cast<const uint4*>(s_doT + c * 16);
-    *reinterpret_cast<uint4*>(bp.qT_codes + tb + c * 16) = *reinterpret_cast<const uint4*>(s_qT + c * 16);
-    *reinterpret_cast<uint4*>(bp.kT_codes + tb + c * 16) = *reinterpret_cast<const uint4*>(s_kT + c * 16);
+    *reinterpret_cast<uint4*>(bp.doT_codes + tb + c * 16) = *reinterpret_cast<const uint4*>(&s_T[0][c * 16]);
+    *reinterpret_cast<uint4*>(bp.qT_codes + tb + c * 16) = *reinterpret_cast<const uint4*>(&s_T[1][c * 16]);
+    *reinterpret_cast<uint4*>(bp.kT_codes + tb + c * 16) = *reinterpret_cast<const uint4*>(&s_T[2][c * 16]);
   }
 }
 
 // ---- shared pieces of the two main kernels ----
+
+// Work item of a workgroup: the dispatcher deals workgroups round-robin to the 8 XCDs; each
+// XCD takes whole heads (their tiles then share its L2) and, within its heads, item 0 (the
+// heaviest under a causal mask) first, so the long items do not trail at the end.
+__device__ __forceinline__ void work_item(int hw_id, int BH, int nt, int& bh, int& t) {
+  constexpr int X = 8;
+  if (BH % X == 0) {
+    const int hpx = BH / X, local = hw_id / X;
+    t = local / hpx;
+    bh = (hw_id % X) * hpx + local % hpx;
+  } else {
+    bh = hw_id / nt;
+    t = hw_id % nt;
+  }
+}
 
 // Direct loads of one 64-row token-major tile (64 x D bytes) into LDS with the row swizzle.
 template <int D>
@@ -242,32 +283,60 @@ __device__ __forceinline__ int rowoff(int row, int chunk) {
 }
 __device__ __forceinline__ int coloff(int row, int chunk) { return row * 64 + ((chunk ^ swz_t64(row)) << 4); }
 
-__device__ __forceinline__ float wave_absmax(float x) {
-  uint32_t u = __float_as_uint(fabsf(x));
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) u = max(u, (uint32_t)__shfl_xor((int)u, o));
-  return __uint_as_float(u);
+__device__ __forceinline__ v8i lds_v8i(const uint8_t* p0, const uint8_t* p1) {
+  const v4i x0 = *reinterpret_cast<const v4i*>(p0), x1 = *reinterpret_cast<const v4i*>(p1);
+  return v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
 }
 
-__device__ __forceinline__ int q8(float x, float inv) {
-  return (int)fminf(fmaxf(rintf(x * inv), -127.0f), 127.0f);
+// O^T[32 x 32] += A[32 x 64] B[64 x 32] in E4M3, B scaled per 32-element K block by the
+// E8M0 byte `sb` (A unscaled).  The two K blocks of the scaled form are bytes 0-15 and
+// 16-31 of both lane halves; block b takes its scale from the lanes of half b.
+__device__ __forceinline__ v16f mfma_f8_sb(v8i a, v8i b, v16f c, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
 }
-__device__ __forceinline__ int pack_i8x4(int a, int b, int c, int d) {
-  return (a & 0xff) | ((b & 0xff) << 8) | ((c & 0xff) << 16) | ((d & 0xff) << 24);
+
+// E8M0 byte of the smallest power of two s with amax / s <= 448 (the E4M3 maximum), at
+// least 1 so that the scale is a normal float.  amax = 2^(E-127) (1 + f): E - 8 suffices
+// when 1 + f <= 1.75, else E - 7.
+__device__ __forceinline__ int e4m3_scale_byte(uint32_t amax_bits) {
+  const int e = (int)(amax_bits >> 23) - 8 + ((amax_bits & 0x7fffff) > 0x600000 ? 1 : 0);
+  return max(e, 1);
+}
+
+// A lane's 32 dS values (bytes 0-15: subtile 0, bytes 16-31: subtile 1) -> E4M3 B operand
+// with per-block scales.  a0 / a1: the lane's max |x| over each subtile.  Returns the
+// E8M0 byte this lane supplies to the MFMA (block hh of its column).
+__device__ __forceinline__ int quant_ds(const float* x, float a0, float a1, int hh, v8i& out) {
+  // block b spans both halves' subtile b: lane l < 32 gets block 0's max, lane l >= 32 block 1's
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
+  const uint32_t mine = max((uint32_t)sw[0], (uint32_t)sw[1]);
+  const uint32_t other = __float_as_uint(other_half(__uint_as_float(mine)));
+  const int bm = e4m3_scale_byte(mine), bo = e4m3_scale_byte(other);
+  const float sc0 = __uint_as_float((uint32_t)(hh ? bo : bm) << 23), sc1 = __uint_as_float((uint32_t)(hh ? bm : bo) << 23);
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float sc = i < 4 ? sc0 : sc1;
+    typedef short v2s __attribute__((ext_vector_type(2)));
+    v2s w = __builtin_bit_cast(v2s, __float_as_int(x[4 * i]));   // high half overwritten below
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x[4 * i], x[4 * i + 1], sc, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x[4 * i + 2], x[4 * i + 3], sc, true);
+    out[i] = __builtin_bit_cast(int, w);
+  }
+  return bm;
 }
 
 // ---- key-stationary kernel: dK and dV ----
 // Workgroup: 128 keys (4 waves x 32), loops over 64-query tiles.  LDS per stage:
 // Q rows, dO rows (token-major), dO^T and Q^T (channel rows), lse2 and D (64 floats each).
 template <int D, bool CAUSAL, int DT>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdPtrs bp, void* dk, void* dv, int N, int Np, float sm) {
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdPtrs bp, void* dk, void* dv, int N, int Np, int BH, float sm) {
   constexpr int TB = 64 * D;                          // one tile of 64 x D bytes
-  constexpr int STAGE = 4 * TB + 2 * 64 * 4;
+  constexpr int STAGE = 4 * TB + 2 * 64 * 4 + 16;   // + the tile's Q step and dO step
   constexpr int NCB = D / 32;
   __shared__ __align__(16) uint8_t lds[2][STAGE];
   const int nkt = Np / 128;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = id / nkt, kt = id % nkt;
+  int bh, kt;
+  work_item(blockIdx.x, BH, nkt, bh, kt);
   const int kbase = kt * 128;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, hh = lane >> 5;
@@ -284,10 +353,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdPtrs bp, void* dk, 
     for (int c = 0; c < D / 32; c++) kf[c] = *reinterpret_cast<const v4i*>(kp + 32 * c);
     const uint8_t* vp = bp.v_codes + ((size_t)bh * Np + key) * D + 32 * hh;
 #pragma unroll
-    for (int c = 0; c < D / 64; c++) {
-      const v4i a0 = *reinterpret_cast<const v4i*>(vp + 64 * c), a1 = *reinterpret_cast<const v4i*>(vp + 64 * c + 16);
-      vf[c] = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    }
+    for (int c = 0; c < D / 64; c++) vf[c] = lds_v8i(vp + 64 * c, vp + 64 * c + 16);
   }
   const float kstep = bp.k_step[(size_t)bh * nb + kw / 64];
   const float vstep = bp.v_step[(size_t)bh * nb + kw / 64];
@@ -296,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdPtrs bp, void* dk, 
 #pragma unroll
   for (int c = 0; c < NCB; c++) dV[c] = dK[c] = v16f{};
 
-  int qt0 = CAUSAL ? kbase / 64 : 0;
+  const int qt0 = CAUSAL ? kbase / 64 : 0;
   const int nqt = (N + 63) / 64;
   auto stage = [&](int buf, int qt) {
     uint8_t* L = lds[buf];
@@ -305,106 +371,109 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdPtrs bp, void* dk, 
     stage_rows<D>(L, reinterpret_cast<const uint8_t*>(bp.q_codes) + rb, w, lane);
     stage_rows<D>(L + TB, bp.do_codes + rb, w, lane);
     stage_cols<D>(L + 2 * TB, bp.doT_codes + tb, w, lane);
-    stage_cols<D>(L + 3 * TB, reinterpret_cast<const uint8_t*>(bp.qT_codes) + tb, w, lane);
+    stage_cols<D>(L + 3 * TB, bp.qT_codes + tb, w, lane);
     if (w == 0 && lane < 16) load_lds16(bp.lse2 + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 16 * lane);
     if (w == 1 && lane < 16) load_lds16(bp.Dvec + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 256 + 16 * lane);
+    if (w == 2 && lane < 2) load_lds4((lane ? bp.do_step : bp.q_step) + (size_t)bh * nb + qt, L + 4 * TB + 512);
+  };
+  // one query tile: S, dP on MFMA; P~ and dS on the vector unit; dV^T, dK^T on MFMA
+  auto tile = [&](const uint8_t* L, int qt, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int qb = qt * 64;
+    const float qstep = reinterpret_cast<const float*>(L + 4 * TB + 512)[0];
+    const float dostep = reinterpret_cast<const float*>(L + 4 * TB + 512)[1];
+    v16i S[2];
+    v16f G[2];
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+      const int row = tile_perm(n, s);
+      v16i a = v16i{};
+#pragma unroll
+      for (int c = 0; c < D / 32; c++) a = mfma_i8(*reinterpret_cast<const v4i*>(L + rowoff<D>(row, 2 * c + hh)), kf[c], a);
+      S[s] = a;
+      v16f b = v16f{};
+#pragma unroll
+      for (int c = 0; c < D / 64; c++)
+        b = mfma_f8(lds_v8i(L + TB + rowoff<D>(row, 4 * c + 2 * hh), L + TB + rowoff<D>(row, 4 * c + 2 * hh + 1)), vf[c], b);
+      G[s] = b;
+    }
+    // element r of subtile s: query qb + 32 hh + 16 s + r, key = this lane's key.
+    // p = 448 P (lse2 carries -log2 448); ds = p (dP - D) = 448 dS.
+    const float cS = qstep * kstep * smlog2e, cP = dostep * vstep;
+    const float* l2 = reinterpret_cast<const float*>(L + 4 * TB) + 32 * hh;
+    const float* Dv = reinterpret_cast<const float*>(L + 4 * TB + 256) + 32 * hh;
+    float p[32], ds[32], am[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 2; s++)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const v4f lv = *reinterpret_cast<const v4f*>(l2 + 16 * s + r);
+        const v4f dvv = *reinterpret_cast<const v4f*>(Dv + 16 * s + r);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float x = fmaf((float)S[s][r + i], cS, -lv[i]);
+          if (MASKED) x = key <= qb + 32 * hh + 16 * s + r + i ? x : -INFINITY;
+          const float e = fast_exp2(x);
+          const float d = e * fmaf(G[s][r + i], cP, -dvv[i]);
+          p[16 * s + r + i] = e;
+          ds[16 * s + r + i] = d;
+          am[s] = fmaxf(am[s], fabsf(d));
+        }
+      }
+    // dV^T += dO^T P~ (FP8, K = 64 queries)
+    v8i pb;
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) pb[i / 4] = pack_fp8x4(p[i], p[i + 1], p[i + 2], p[i + 3]);
+#pragma unroll
+    for (int cb = 0; cb < NCB; cb++) {
+      const int row = 32 * cb + n;
+      dV[cb] = mfma_f8(lds_v8i(L + 2 * TB + coloff(row, 2 * hh), L + 2 * TB + coloff(row, 2 * hh + 1)), pb, dV[cb]);
+    }
+    // dK^T += Q^T dS~ (dS in E4M3 with per-block power-of-two scales)
+    v8i db;
+    const int sb = quant_ds(ds, am[0], am[1], hh, db);
+#pragma unroll
+    for (int cb = 0; cb < NCB; cb++) {
+      const int row = 32 * cb + n;
+      dK[cb] = mfma_f8_sb(lds_v8i(L + 3 * TB + coloff(row, 2 * hh), L + 3 * TB + coloff(row, 2 * hh + 1)), db, dK[cb], sb);
+    }
+  };
+  // per-wave phases over the query tiles (wave-uniform bounds, so the accumulators never meet
+  // a branch join inside a loop): tiles whose queries all precede this wave's keys add nothing,
+  // then the diagonal tiles need the causal mask, then every pair is visible.  Keys >= N need
+  // no mask: their columns only reach their own (unstored) dK, dV rows.
+  const int qt_first = kw >= N ? nqt : (CAUSAL ? max(qt0, kw / 64) : qt0);
+  const int qt_open = kw >= N ? nqt : (CAUSAL ? max(qt_first, (kw + 94) / 64) : qt0);
+  auto iter = [&](int qt, auto mode) {
+    const int buf = (qt - qt0) & 1;
+    if (qt + 1 < nqt) stage(buf ^ 1, qt + 1);
+    if constexpr (decltype(mode)::value >= 0) tile(lds[buf], qt, std::bool_constant<decltype(mode)::value == 1>{});
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
   };
   if (qt0 < nqt) stage(0, qt0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  for (int qt = qt0; qt < nqt; qt++) {
-    const int buf = (qt - qt0) & 1;
-    if (qt + 1 < nqt) stage(buf ^ 1, qt + 1);
-    const uint8_t* L = lds[buf];
-    const int qb = qt * 64;
-    // causal: this wave's keys all exceed the tile's queries -> nothing to add
-    if (!(CAUSAL && kw > qb + 63) && kw < N) {
-      const float qstep = bp.q_step[(size_t)bh * nb + qt];
-      const float dostep = bp.do_step[(size_t)bh * nb + qt];
-      // S = Q K^T and dP = dO V^T (rows: tile queries in tile_perm order, cols: the wave's keys)
-      v16i S[2];
-      v16f P[2];
-#pragma unroll
-      for (int s = 0; s < 2; s++) {
-        const int row = tile_perm(n, s);
-        v16i a = v16i{};
-#pragma unroll
-        for (int c = 0; c < D / 32; c++)
-          a = mfma_i8(*reinterpret_cast<const v4i*>(L + rowoff<D>(row, 2 * c + hh)), kf[c], a);
-        S[s] = a;
-        v16f b = v16f{};
-#pragma unroll
-        for (int c = 0; c < D / 64; c++) {
-          const v4i x0 = *reinterpret_cast<const v4i*>(L + TB + rowoff<D>(row, 4 * c + 2 * hh));
-          const v4i x1 = *reinterpret_cast<const v4i*>(L + TB + rowoff<D>(row, 4 * c + 2 * hh + 1));
-          b = mfma_f8(v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]}, vf[c], b);
-        }
-        P[s] = b;   // dP accumulator for now
-      }
-      // P, dS (element r of subtile s = query qb + 32 hh + 16 s + r, key = this lane's key)
-      const float cS = qstep * kstep * smlog2e, cP = dostep * vstep;
-      const float* l2 = reinterpret_cast<const float*>(L + 4 * TB) + 32 * hh;
-      const float* Dv = reinterpret_cast<const float*>(L + 4 * TB + 256) + 32 * hh;
-      float pf[32], ds[32];
-      float amax = 0.0f;
-#pragma unroll
-      for (int s = 0; s < 2; s++)
-#pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          const v4f lv = *reinterpret_cast<const v4f*>(l2 + 16 * s + r);
-          const v4f dv = *reinterpret_cast<const v4f*>(Dv + 16 * s + r);
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int q = qb + 32 * hh + 16 * s + r + i;
-            const bool ok = key < N && (!CAUSAL || key <= q);
-            const float p = ok ? fast_exp2(fmaf((float)S[s][r + i], cS, -lv[i])) : 0.0f;
-            const float d = p * fmaf(P[s][r + i], cP, -dv[i]);
-            pf[16 * s + r + i] = p;
-            ds[16 * s + r + i] = d;
-            amax = fmaxf(amax, fabsf(d));
-          }
-        }
-      // dV^T += dO^T P~ (FP8, K = 64 queries)
-      v8i pb;
-#pragma unroll
-      for (int i = 0; i < 32; i += 4)
-        pb[i / 4] = pack_fp8x4(448.0f * pf[i], 448.0f * pf[i + 1], 448.0f * pf[i + 2], 448.0f * pf[i + 3]);
-#pragma unroll
-      for (int cb = 0; cb < NCB; cb++) {
-        const int row = 32 * cb + n;
-        const v4i x0 = *reinterpret_cast<const v4i*>(L + 2 * TB + coloff(row, 2 * hh));
-        const v4i x1 = *reinterpret_cast<const v4i*>(L + 2 * TB + coloff(row, 2 * hh + 1));
-        dV[cb] = mfma_f8(v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]}, pb, dV[cb]);
-      }
-      // dS~ (INT8, one step per wave tile), dK^T += Q^T dS~ (INT8, K = 32 queries per subtile)
-      const float am = wave_absmax(amax);
-      const float step = am / 127.0f, inv = am == 0.0f ? 0.0f : 127.0f / am;
-      const float kscale = step * qstep;
-#pragma unroll
-      for (int cb = 0; cb < NCB; cb++) {
-        const int row = 32 * cb + n;
-        v16i acc = v16i{};
-#pragma unroll
-        for (int s = 0; s < 2; s++) {
-          v4i db;
-#pragma unroll
-          for (int k = 0; k < 4; k++)
-            db[k] = pack_i8x4(q8(ds[16 * s + 4 * k], inv), q8(ds[16 * s + 4 * k + 1], inv), q8(ds[16 * s + 4 * k + 2], inv),
-                              q8(ds[16 * s + 4 * k + 3], inv));
-          acc = mfma_i8(*reinterpret_cast<const v4i*>(L + 3 * TB + coloff(row, 2 * hh + s)), db, acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; r++) dK[cb][r] = fmaf((float)acc[r], kscale, dK[cb][r]);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-  }
-  // epilogue: dK = sm dK^T, dV = dV^T * doT_step / 448; lane holds channels of its key
+  int qt = qt0;
+  for (; qt < min(qt_first, nqt); qt++) iter(qt, std::integral_constant<int, -1>{});
+  for (; qt < min(qt_open, nqt); qt++) iter(qt, std::integral_constant<int, 1>{});
+  for (; qt < nqt; qt++) iter(qt, std::integral_constant<int, 0>{});
+  // epilogue: dK = sm qT_step dK^T / 448, dV = doT_step dV^T / 448; lane holds channels
+  // 32 cb + 8 g + 4 hh + {0..3} of its key.  All factors are loaded before the first store.
   if (key < N) {
     uint16_t* dkr = reinterpret_cast<uint16_t*>(dk) + ((size_t)bh * N + key) * D;
     uint16_t* dvr = reinterpret_cast<uint16_t*>(dv) + ((size_t)bh * N + key) * D;
-    const float* dcs = bp.doT_step + (size_t)bh * D;
+    const float* cdo = bp.chan_step + (size_t)bh * D + 4 * hh;
+    const float* cq = bp.chan_step + ((size_t)BH + bh) * D + 4 * hh;
+    v4f fk[NCB][4], fv[NCB][4];
+#pragma unroll
+    for (int cb = 0; cb < NCB; cb++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        fk[cb][g] = *reinterpret_cast<const v4f*>(cq + 32 * cb + 8 * g);
+        fv[cb][g] = *reinterpret_cast<const v4f*>(cdo + 32 * cb + 8 * g);
+      }
+    const float kf448 = sm * (1.0f / 448.0f);
 #pragma unroll
     for (int cb = 0; cb < NCB; cb++)
 #pragma unroll
@@ -413,9 +482,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdPtrs bp, void* dk, 
         uint32_t k2[2], v2[2];
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-          k2[t] = (uint32_t)to_io<DT>(dK[cb][4 * g + 2 * t] * sm) | ((uint32_t)to_io<DT>(dK[cb][4 * g + 2 * t + 1] * sm) << 16);
-          v2[t] = (uint32_t)to_io<DT>(dV[cb][4 * g + 2 * t] * (dcs[ch + 2 * t] * (1.0f / 448.0f))) |
-                  ((uint32_t)to_io<DT>(dV[cb][4 * g + 2 * t + 1] * (dcs[ch + 2 * t + 1] * (1.0f / 448.0f))) << 16);
+          const int i0 = 2 * t, i1 = 2 * t + 1;
+          k2[t] = (uint32_t)to_io<DT>(dK[cb][4 * g + i0] * (fk[cb][g][i0] * kf448)) |
+                  ((uint32_t)to_io<DT>(dK[cb][4 * g + i1] * (fk[cb][g][i1] * kf448)) << 16);
+          v2[t] = (uint32_t)to_io<DT>(dV[cb][4 * g + i0] * (fv[cb][g][i0] * (1.0f / 448.0f))) |
+                  ((uint32_t)to_io<DT>(dV[cb][4 * g + i1] * (fv[cb][g][i1] * (1.0f / 448.0f))) << 16);
         }
         *reinterpret_cast<uint2*>(dkr + ch) = make_uint2(k2[0], k2[1]);
         *reinterpret_cast<uint2*>(dvr + ch) = make_uint2(v2[0], v2[1]);
@@ -425,17 +496,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdPtrs bp, void* dk, 
 
 // ---- query-stationary kernel: dQ ----
 // Workgroup: 128 queries (4 waves x 32), loops over 64-key tiles.  LDS per stage:
-// K_s rows (INT8), V rows (FP8), K_s^T (channel rows, INT8).
+// K_s rows (INT8), V rows (FP8), K_s^T (channel rows, FP8).
 template <int D, bool CAUSAL, int DT>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdPtrs bp, void* dq, int N, int Np, float sm) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdPtrs bp, void* dq, int N, int Np, int BH, float sm) {
   constexpr int TB = 64 * D;
-  constexpr int STAGE = 3 * TB;
+  constexpr int STAGE = 3 * TB + 16;   // + the tile's K step and V step
   constexpr int NCB = D / 32;
   __shared__ __align__(16) uint8_t lds[2][STAGE];
   const int nqt = Np / 128;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = id / nqt;
-  const int qt = CAUSAL ? nqt - 1 - id % nqt : id % nqt;
+  int bh, t;
+  work_item(blockIdx.x, BH, nqt, bh, t);
+  const int qt = CAUSAL ? nqt - 1 - t : t;   // causal: the longest rows first
   const int qbase = qt * 128;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, hh = lane >> 5;
@@ -452,10 +523,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdPtrs bp, void* dq, in
     for (int c = 0; c < D / 32; c++) qf[c] = *reinterpret_cast<const v4i*>(qp + 32 * c);
     const uint8_t* dp = bp.do_codes + ((size_t)bh * Np + q) * D + 32 * hh;
 #pragma unroll
-    for (int c = 0; c < D / 64; c++) {
-      const v4i a0 = *reinterpret_cast<const v4i*>(dp + 64 * c), a1 = *reinterpret_cast<const v4i*>(dp + 64 * c + 16);
-      df[c] = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    }
+    for (int c = 0; c < D / 64; c++) df[c] = lds_v8i(dp + 64 * c, dp + 64 * c + 16);
   }
   const float qstep = bp.q_step[(size_t)bh * nb + q / 64];
   const float dostep = bp.do_step[(size_t)bh * nb + q / 64];
@@ -475,95 +543,89 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdPtrs bp, void* dq, in
     const size_t tb = ((size_t)bh * nb + kt) * TB;
     stage_rows<D>(L, reinterpret_cast<const uint8_t*>(bp.k_codes) + rb, w, lane);
     stage_rows<D>(L + TB, bp.v_codes + rb, w, lane);
-    stage_cols<D>(L + 2 * TB, reinterpret_cast<const uint8_t*>(bp.kT_codes) + tb, w, lane);
+    stage_cols<D>(L + 2 * TB, bp.kT_codes + tb, w, lane);
+    if (w == 0 && lane < 2) load_lds4((lane ? bp.v_step : bp.k_step) + (size_t)bh * nb + kt, L + 3 * TB);
+  };
+  auto tile = [&](const uint8_t* L, int kt, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int kb = kt * 64;
+    const float kstep = reinterpret_cast<const float*>(L + 3 * TB)[0];
+    const float vstep = reinterpret_cast<const float*>(L + 3 * TB)[1];
+    v16i S[2];
+    v16f G[2];
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+      const int row = tile_perm(n, s);
+      v16i a = v16i{};
+#pragma unroll
+      for (int c = 0; c < D / 32; c++) a = mfma_i8(*reinterpret_cast<const v4i*>(L + rowoff<D>(row, 2 * c + hh)), qf[c], a);
+      S[s] = a;
+      v16f b = v16f{};
+#pragma unroll
+      for (int c = 0; c < D / 64; c++)
+        b = mfma_f8(lds_v8i(L + TB + rowoff<D>(row, 4 * c + 2 * hh), L + TB + rowoff<D>(row, 4 * c + 2 * hh + 1)), df[c], b);
+      G[s] = b;
+    }
+    // element r of subtile s: key kb + 32 hh + 16 s + r, query = this lane's query
+    const float cS = qstep * kstep * smlog2e, cP = dostep * vstep;
+    const int lim = min(N, CAUSAL ? q + 1 : N) - (kb + 32 * hh);   // keys i < lim are visible
+    float p[32], ds[32], am[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 2; s++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        float x = fmaf((float)S[s][r], cS, -l2);
+        if (MASKED) x = 16 * s + r < lim ? x : -INFINITY;
+        const float e = fast_exp2(x);
+        const float d = e * fmaf(G[s][r], cP, -Dq);
+        p[16 * s + r] = e;
+        ds[16 * s + r] = d;
+        rsum += d;
+        am[s] = fmaxf(am[s], fabsf(d));
+      }
+    v8i pb, db;
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) pb[i / 4] = pack_fp8x4(p[i], p[i + 1], p[i + 2], p[i + 3]);
+    const int sb = quant_ds(ds, am[0], am[1], hh, db);
+#pragma unroll
+    for (int cb = 0; cb < NCB; cb++) {
+      const int row = 32 * cb + n;
+      const v8i a = lds_v8i(L + 2 * TB + coloff(row, 2 * hh), L + 2 * TB + coloff(row, 2 * hh + 1));
+      dQ[cb] = mfma_f8_sb(a, db, dQ[cb], sb);
+      PK[cb] = mfma_f8(a, pb, PK[cb]);   // P K_s for the rowsum correction
+    }
+  };
+  // per-wave phases over the key tiles (wave-uniform bounds): fully visible tiles, then the
+  // diagonal / ragged-end tiles that need the mask, then tiles past this wave's last query
+  const int nkt_n = (N + 63) / 64;
+  const int nvis = CAUSAL ? min(nkt_n, (qw + 31) / 64 + 1) : nkt_n;
+  const int nfull = min(N / 64, CAUSAL ? (qw + 1) / 64 : nkt_n);
+  auto iter = [&](int kt, auto mode) {
+    const int buf = kt & 1;
+    if (kt + 1 < nkt) stage(buf ^ 1, kt + 1);
+    if constexpr (decltype(mode)::value >= 0) tile(lds[buf], kt, std::bool_constant<decltype(mode)::value == 1>{});
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
   };
   stage(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  for (int kt = 0; kt < nkt; kt++) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) stage(buf ^ 1, kt + 1);
-    const uint8_t* L = lds[buf];
-    const int kb = kt * 64;
-    if (!(CAUSAL && kb > qw + 31)) {
-      const float kstep = bp.k_step[(size_t)bh * nb + kt];
-      const float vstep = bp.v_step[(size_t)bh * nb + kt];
-      v16i S[2];
-      v16f G[2];
-#pragma unroll
-      for (int s = 0; s < 2; s++) {
-        const int row = tile_perm(n, s);
-        v16i a = v16i{};
-#pragma unroll
-        for (int c = 0; c < D / 32; c++)
-          a = mfma_i8(*reinterpret_cast<const v4i*>(L + rowoff<D>(row, 2 * c + hh)), qf[c], a);
-        S[s] = a;
-        v16f b = v16f{};
-#pragma unroll
-        for (int c = 0; c < D / 64; c++) {
-          const v4i x0 = *reinterpret_cast<const v4i*>(L + TB + rowoff<D>(row, 4 * c + 2 * hh));
-          const v4i x1 = *reinterpret_cast<const v4i*>(L + TB + rowoff<D>(row, 4 * c + 2 * hh + 1));
-          b = mfma_f8(v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]}, df[c], b);
-        }
-        G[s] = b;
-      }
-      const float cS = qstep * kstep * smlog2e, cP = dostep * vstep;
-      float ds[32];
-      int pc[32];
-      float amax = 0.0f;
-#pragma unroll
-      for (int s = 0; s < 2; s++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int k = kb + 32 * hh + 16 * s + r;
-          const bool ok = k < N && (!CAUSAL || k <= q);
-          const float p = ok ? fast_exp2(fmaf((float)S[s][r], cS, -l2)) : 0.0f;
-          const float d = p * fmaf(G[s][r], cP, -Dq);
-          ds[16 * s + r] = d;
-          pc[16 * s + r] = (int)rintf(p * 127.0f);   // P in [0, 1] as INT8 codes of step 1/127
-          rsum += d;
-          amax = fmaxf(amax, fabsf(d));
-        }
-      const float am = wave_absmax(amax);
-      const float step = am / 127.0f, inv = am == 0.0f ? 0.0f : 127.0f / am;
-      const float qscale = step * kstep;
-#pragma unroll
-      for (int cb = 0; cb < NCB; cb++) {
-        const int row = 32 * cb + n;
-        v16i acc = v16i{};
-#pragma unroll
-        for (int s = 0; s < 2; s++) {
-          v4i db;
-#pragma unroll
-          for (int k = 0; k < 4; k++)
-            db[k] = pack_i8x4(q8(ds[16 * s + 4 * k], inv), q8(ds[16 * s + 4 * k + 1], inv), q8(ds[16 * s + 4 * k + 2], inv),
-                              q8(ds[16 * s + 4 * k + 3], inv));
-          acc = mfma_i8(*reinterpret_cast<const v4i*>(L + 2 * TB + coloff(row, 2 * hh + s)), db, acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; r++) dQ[cb][r] = fmaf((float)acc[r], qscale, dQ[cb][r]);
-        // P K_s for the rowsum correction
-        v16i accp = v16i{};
-#pragma unroll
-        for (int s = 0; s < 2; s++) {
-          v4i pb;
-#pragma unroll
-          for (int k = 0; k < 4; k++)
-            pb[k] = pack_i8x4(pc[16 * s + 4 * k], pc[16 * s + 4 * k + 1], pc[16 * s + 4 * k + 2], pc[16 * s + 4 * k + 3]);
-          accp = mfma_i8(*reinterpret_cast<const v4i*>(L + 2 * TB + coloff(row, 2 * hh + s)), pb, accp);
-        }
-        const float pscale = kstep * (1.0f / 127.0f);
-#pragma unroll
-        for (int r = 0; r < 16; r++) PK[cb][r] = fmaf((float)accp[r], pscale, PK[cb][r]);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-  }
-  // epilogue: dQ = sm (dS K_s - rowsum(dS) P K_s); hand D^ = D + rowsum(dS) to the dK/dV kernel
-  const float rs = half_sum(rsum);
+  int kt = 0;
+  for (; kt < min(nfull, nkt); kt++) iter(kt, std::integral_constant<int, 0>{});
+  for (; kt < min(nvis, nkt); kt++) iter(kt, std::integral_constant<int, 1>{});
+  for (; kt < nkt; kt++) iter(kt, std::integral_constant<int, -1>{});
+  // epilogue: dQ = sm kT_step (dQ^T - rs PK^T) / 448 with rs = rowsum(dS); hand D^ = D + rs
+  // to the dK/dV kernel
+  const float rs = half_sum(rsum) * (1.0f / 448.0f);
   if (q < N) {
     uint16_t* dqr = reinterpret_cast<uint16_t*>(dq) + ((size_t)bh * N + q) * D;
+    const float* ck = bp.chan_step + ((size_t)2 * BH + bh) * D + 4 * hh;
+    v4f fq[NCB][4];
+#pragma unroll
+    for (int cb = 0; cb < NCB; cb++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) fq[cb][g] = *reinterpret_cast<const v4f*>(ck + 32 * cb + 8 * g);
+    const float f448 = sm * (1.0f / 448.0f);
 #pragma unroll
     for (int cb = 0; cb < NCB; cb++)
 #pragma unroll
@@ -571,9 +633,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdPtrs bp, void* dq, in
         const int ch = 32 * cb + 8 * g + 4 * hh;
         uint32_t w2[2];
 #pragma unroll
-        for (int t = 0; t < 2; t++)
-          w2[t] = (uint32_t)to_io<DT>(sm * fmaf(-rs, PK[cb][4 * g + 2 * t], dQ[cb][4 * g + 2 * t])) |
-                  ((uint32_t)to_io<DT>(sm * fmaf(-rs, PK[cb][4 * g + 2 * t + 1], dQ[cb][4 * g + 2 * t + 1])) << 16);
+        for (int t2 = 0; t2 < 2; t2++) {
+          const int i0 = 2 * t2, i1 = 2 * t2 + 1;
+          w2[t2] = (uint32_t)to_io<DT>(fq[cb][g][i0] * f448 * fmaf(-rs, PK[cb][4 * g + i0], dQ[cb][4 * g + i0])) |
+                   ((uint32_t)to_io<DT>(fq[cb][g][i1] * f448 * fmaf(-rs, PK[cb][4 * g + i1], dQ[cb][4 * g + i1])) << 16);
+        }
         *reinterpret_cast<uint2*>(dqr + ch) = make_uint2(w2[0], w2[1]);
       }
     if (hh == 0) bp.Dvec[(size_t)bh * Np + q] = Dq + rs;
@@ -583,7 +647,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdPtrs bp, void* dq, in
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct BwdLayout {
-  size_t amax_do, Dvec, lse2, do_codes, do_step, doT_codes, doT_step, v_codes, v_step, qT, kT, total;
+  size_t amax_part, chan_step, Dvec, lse2, do_codes, do_step, v_codes, v_step, doT, qT, kT, total;
 };
 
 BwdLayout bwd_layout(const Shape& s) {
@@ -591,15 +655,15 @@ BwdLayout bwd_layout(const Shape& s) {
   BwdLayout L;
   size_t off = 0;
   auto take = [&](size_t b) { size_t o = off; off = round256(off + b); return o; };
-  L.amax_do = take(BH * d * 4);
+  L.amax_part = take((size_t)kNT * kStatChunks * BH * d * 4);
+  L.chan_step = take((size_t)kNT * BH * d * 4);
   L.Dvec = take(BH * Np * 4);
   L.lse2 = take(BH * Np * 4);
   L.do_codes = take(BH * Np * d);
   L.do_step = take(BH * nb * 4);
-  L.doT_codes = take(BH * Np * d);
-  L.doT_step = take(BH * d * 4);
   L.v_codes = take(BH * Np * d);
   L.v_step = take(BH * nb * 4);
+  L.doT = take(BH * Np * d);
   L.qT = take(BH * Np * d);
   L.kT = take(BH * Np * d);
   L.total = off;
@@ -620,32 +684,33 @@ hipError_t bwd_run(const Shape& s, const void* q, const void* k, const void* v, 
   bp.k_step = reinterpret_cast<const float*>(qp.k_scales);
   bp.mu_k = qp.mu_k;
   bp.lse_corr = qp.lse_corr;
-  bp.amax_do = reinterpret_cast<uint32_t*>(b + L.amax_do);
+  bp.amax_part = reinterpret_cast<uint32_t*>(b + L.amax_part);
+  bp.chan_step = reinterpret_cast<float*>(b + L.chan_step);
   bp.Dvec = reinterpret_cast<float*>(b + L.Dvec);
   bp.lse2 = reinterpret_cast<float*>(b + L.lse2);
   bp.do_codes = b + L.do_codes;
   bp.do_step = reinterpret_cast<float*>(b + L.do_step);
-  bp.doT_codes = b + L.doT_codes;
-  bp.doT_step = reinterpret_cast<float*>(b + L.doT_step);
   bp.v_codes = b + L.v_codes;
   bp.v_step = reinterpret_cast<float*>(b + L.v_step);
-  bp.qT_codes = reinterpret_cast<int8_t*>(b + L.qT);
-  bp.kT_codes = reinterpret_cast<int8_t*>(b + L.kT);
+  bp.doT_codes = b + L.doT;
+  bp.qT_codes = b + L.qT;
+  bp.kT_codes = b + L.kT;
   // forward quantization of Q, K (the codes the forward used), then the backward prologue
   hipError_t e = launch_prologue(q, k, v, s, qp, st);
   if (e != hipSuccess) return e;
-  bwd_zero_kernel<<<(BH * D + 255) / 256, 256, 0, st>>>(bp.amax_do, BH * D);
-  bwd_stats_kernel<DT, D><<<dim3((s.N + 255) / 256, BH), 256, 0, st>>>((const uint16_t*)dout, s.N, bp.amax_do);
+  bwd_stats_kernel<DT, D><<<dim3(kStatChunks, BH), 256, 0, st>>>((const uint16_t*)dout, (const uint16_t*)q,
+                                                                (const uint16_t*)k, qp.mu_k, s.N, bp.amax_part);
   bwd_prep_kernel<DT, D><<<dim3(s.Np / 64, BH), 256, 0, st>>>((const uint16_t*)o, (const uint16_t*)dout,
-                                                             (const uint16_t*)v, lse, s.N, s.Np, bp);
+                                                             (const uint16_t*)v, (const uint16_t*)q,
+                                                             (const uint16_t*)k, lse, s.N, s.Np, bp);
   const int grid = BH * (s.Np / 128);
   // dQ first: it turns D into D^ = D + rowsum(dS), which the dK/dV kernel then uses
   if (s.causal) {
-    bwd_dq_kernel<D, true, DT><<<grid, 256, 0, st>>>(bp, dq, s.N, s.Np, s.sm_scale);
-    bwd_dkdv_kernel<D, true, DT><<<grid, 256, 0, st>>>(bp, dk, dv, s.N, s.Np, s.sm_scale);
+    bwd_dq_kernel<D, true, DT><<<grid, 256, 0, st>>>(bp, dq, s.N, s.Np, BH, s.sm_scale);
+    bwd_dkdv_kernel<D, true, DT><<<grid, 256, 0, st>>>(bp, dk, dv, s.N, s.Np, BH, s.sm_scale);
   } else {
-    bwd_dq_kernel<D, false, DT><<<grid, 256, 0, st>>>(bp, dq, s.N, s.Np, s.sm_scale);
-    bwd_dkdv_kernel<D, false, DT><<<grid, 256, 0, st>>>(bp, dk, dv, s.N, s.Np, s.sm_scale);
+    bwd_dq_kernel<D, false, DT><<<grid, 256, 0, st>>>(bp, dq, s.N, s.Np, BH, s.sm_scale);
+    bwd_dkdv_kernel<D, false, DT><<<grid, 256, 0, st>>>(bp, dk, dv, s.N, s.Np, BH, s.sm_scale);
   }
   return hipGetLastError();
 }

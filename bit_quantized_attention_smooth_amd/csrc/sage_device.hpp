@@ -67,9 +67,18 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
 #endif
 }
 
-// Four floats -> four E4M3 bytes (RNE; inputs here never exceed 448).
+// 4-byte direct global -> LDS load: lane L's dword lands at lds + 4 L.
+__device__ __forceinline__ void load_lds4(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+#endif
+}
+
+// Four floats -> four E4M3 bytes (RNE; inputs here never exceed 448).  The first conversion
+// writes the low half of a's own register (its high half is overwritten by the second), so no
+// zeroed register is needed when a is dead afterwards.
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -99,13 +108,8 @@ __device__ __forceinline__ float e8m0_to_float(unsigned b) {
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 __device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
-// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffff) > 0x7f800000) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fff + ((u >> 16) & 1);
-  return (uint16_t)(u >> 16);
-}
+// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN): the hardware conversion.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 __device__ __forceinline__ uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }   // RNE
 
 template <int DT> __device__ __forceinline__ float load_io(const uint16_t* p) {
