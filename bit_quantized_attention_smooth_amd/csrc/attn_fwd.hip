@@ -71,8 +71,9 @@ struct Geo {
   static constexpr int VBYTES = D * kTK;                                // FP8 V^T tile
   static constexpr int VSTAGE = VBYTES + DSBYTES;                       // V^T tile + scaled dS
   static constexpr int KCHUNKS = KBYTES / 16;                           // 16-byte chunks per K tile
-  static constexpr int KLOADS = (KCHUNKS + 255) / 256;
-  static constexpr int VLOADS = VBYTES / 16 / 256;
+  static constexpr int VCHUNKS = VBYTES / 16;                           // 16-byte chunks per V^T tile
+  template <int NT> static constexpr int kloads() { return (KCHUNKS + NT - 1) / NT; }   // per lane, NT threads
+  template <int NT> static constexpr int vloads() { return (VCHUNKS + NT - 1) / NT; }
   static constexpr int NCB = D / 32;                                    // 32-channel output blocks
   static constexpr int NQF = QK == QK_INT8 ? D / 32 : D / 64;           // QK MFMAs per 32-key subtile
 };
@@ -116,25 +117,26 @@ __device__ __forceinline__ uint32_t pack2_io(float a, float b) {
 // registers because it is rescaled on the way), read one step later than K.
 // Per-lane byte offsets, computed once per query-tile pass and pinned in registers (the
 // tile base addresses are wave-uniform, so every access is uniform base + lane offset).
-template <int D, int QK>
+template <int D, int QK, int NT = 256>
 struct LaneOffs {
   using G = Geo<D, QK>;
-  uint32_t kld[G::KLOADS];          // direct-load source offsets inside a K tile
-  uint32_t vld[G::VLOADS];          // direct-load source offsets inside a V^T tile
+  static constexpr int KL = G::template kloads<NT>(), VL = G::template vloads<NT>();
+  uint32_t kld[KL];                 // direct-load source offsets inside a K tile
+  uint32_t vld[VL];                 // direct-load source offsets inside a V^T tile
   uint32_t kop[2][G::NQF];          // LDS offsets of the K operand reads (subtile, chunk)
   uint32_t ksc[2][G::NQF];          // MXFP4: LDS offsets of the K scale bytes
   uint32_t vop[G::NCB][2];          // LDS offsets of the V^T operand reads (block, half)
 
   __device__ __forceinline__ void init(int w, int lane, int n, int hh) {
 #pragma unroll
-    for (int i = 0; i < G::KLOADS; i++) {
-      const int P = (256 * i + 64 * w + lane) % G::KCHUNKS;
+    for (int i = 0; i < KL; i++) {
+      const int P = (NT * i + 64 * w + lane) % G::KCHUNKS;
       const int row = P / G::KCH, col = (P % G::KCH) ^ swz<G::KROW>(row);
       kld[i] = row * G::KROW + col * 16;
     }
 #pragma unroll
-    for (int i = 0; i < G::VLOADS; i++) {
-      const int P = 256 * i + 64 * w + lane;
+    for (int i = 0; i < VL; i++) {
+      const int P = (NT * i + 64 * w + lane) % G::VCHUNKS;
       const int row = P >> 2, col = (P & 3) ^ swz_v(row);
       vld[i] = row * 64 + col * 16;
     }
@@ -156,9 +158,9 @@ struct LaneOffs {
     }
     // opaque to the optimizer: keep these in registers instead of recomputing them every tile
 #pragma unroll
-    for (int i = 0; i < G::KLOADS; i++) asm volatile("" : "+v"(kld[i]));
+    for (int i = 0; i < KL; i++) asm volatile("" : "+v"(kld[i]));
 #pragma unroll
-    for (int i = 0; i < G::VLOADS; i++) asm volatile("" : "+v"(vld[i]));
+    for (int i = 0; i < VL; i++) asm volatile("" : "+v"(vld[i]));
 #pragma unroll
     for (int s = 0; s < 2; s++)
 #pragma unroll
@@ -176,14 +178,14 @@ struct LaneOffs {
 // applied to the global source offset instead.  K stage: codes (+ E8M0 scales).  V stage:
 // V^T codes (+ dS * sm * log2 e, staged through registers because it is rescaled on the
 // way), read one step later than K.
-template <int D, int QK>
-__device__ __forceinline__ void issue_k(uint8_t* lds, const FwdArgs& a, int bh, int j, const LaneOffs<D, QK>& lo,
+template <int D, int QK, int NT>
+__device__ __forceinline__ void issue_k(uint8_t* lds, const FwdArgs& a, int bh, int j, const LaneOffs<D, QK, NT>& lo,
                                         int w, int lane) {
   using G = Geo<D, QK>;
   const uint8_t* kg = a.k_codes + ((size_t)bh * a.Np + (size_t)j * kTK) * G::KROW;
 #pragma unroll
-  for (int i = 0; i < G::KLOADS; i++) {
-    const int pbase = 256 * i + 64 * w;
+  for (int i = 0; i < LaneOffs<D, QK, NT>::KL; i++) {
+    const int pbase = NT * i + 64 * w;
     if (pbase < G::KCHUNKS) load_lds16(kg + lo.kld[i], lds + pbase * 16);
   }
   if (QK == QK_MXFP4 && w == 0 && lane < G::SBYTES / 16) {
@@ -192,13 +194,16 @@ __device__ __forceinline__ void issue_k(uint8_t* lds, const FwdArgs& a, int bh, 
   }
 }
 
-template <int D, int QK>
-__device__ __forceinline__ void issue_v(uint8_t* lds, const FwdArgs& a, int bh, int j, const LaneOffs<D, QK>& lo,
+template <int D, int QK, int NT>
+__device__ __forceinline__ void issue_v(uint8_t* lds, const FwdArgs& a, int bh, int j, const LaneOffs<D, QK, NT>& lo,
                                         int w) {
   using G = Geo<D, QK>;
   const uint8_t* vg = a.v_codes + ((size_t)bh * (a.Np / kTK) + j) * G::VBYTES;
 #pragma unroll
-  for (int i = 0; i < G::VLOADS; i++) load_lds16(vg + lo.vld[i], lds + (256 * i + 64 * w) * 16);
+  for (int i = 0; i < LaneOffs<D, QK, NT>::VL; i++) {
+    const int pbase = NT * i + 64 * w;
+    if (pbase < G::VCHUNKS) load_lds16(vg + lo.vld[i], lds + pbase * 16);
+  }
 }
 
 // MXFP4 dS strip of one tile (64 floats): fetched into registers, stored scaled.
@@ -221,9 +226,9 @@ struct Score {
   v16f sf[QK == QK_MXFP4 ? 2 : 1];
 };
 
-template <int D, int QK>
+template <int D, int QK, typename LO>
 __device__ __forceinline__ void qk_tile(Score<D, QK>& S, const uint8_t* lk, const v4i* qf, const v8i* qf4,
-                                        const int* qsc, const LaneOffs<D, QK>& lo) {
+                                        const int* qsc, const LO& lo) {
   using G = Geo<D, QK>;
 #pragma unroll
   for (int s = 0; s < 2; s++) {
@@ -260,15 +265,13 @@ struct RowState {
 //   log2-domain scale; masked entries are set to -inf; the row max is taken on u, and
 //   p448_i = exp2(u_i * c + (log2 448 - m)) comes out of one FMA and one exp2 per element.
 template <int D, int QK, bool CAUSAL>
-__device__ __forceinline__ void softmax_pv(RowState<D>& st, const Score<D, QK>& Sc, const uint8_t* vstage,
-                                           const float* kstep, float qstep, float sm_log2e, int j, int N, int qw,
-                                           int qrow, int hh, const LaneOffs<D, QK>& lo) {
+__device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>& Sc, const uint8_t* vstage,
+                                            const float* kstep, float qstep, float sm_log2e, int j, int N, int qw,
+                                            int qrow, int hh, float* u, float& c, float& off) {
   using G = Geo<D, QK>;
   constexpr int NCB = G::NCB;
   const int kbase = j * kTK;
   const bool need_mask = kbase + kTK > N || (CAUSAL && kbase + kTK - 1 > qw);
-  float u[32];
-  float c;
   float mt;
   if (QK == QK_INT8) {
     c = qstep * kstep[j];
@@ -337,8 +340,24 @@ __device__ __forceinline__ void softmax_pv(RowState<D>& st, const Score<D, QK>& 
     for (int cb = 0; cb < NCB; cb++) st.O[cb] *= alpha;
   }
   st.m = mnew;
-  const float off = kLog2_448 - mref;
-  // p448 = exp2(u c + off), row sum, FP8 pack
+  off = kLog2_448 - mref;
+}
+
+// Second half of tile j's softmax, p448 = exp2(u c + off), the row sum and the FP8 pack,
+// sharing one basic block with the QK MFMAs of tile j+1 (into Sn) and the PV MFMAs of tile
+// j.  The issue order is pinned: the K operand reads, then the QK MFMAs one at a time between
+// slices of the exp / pack stream (so the matrix core runs under the vector work of the same
+// wave instead of stalling its issue), then the V operand reads and the PV MFMAs.
+template <int D, int QK>
+__device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u, float c, float off, Score<D, QK>& Sn,
+                                                const uint8_t* lk_next, const uint8_t* vstage, const v4i* qf,
+                                                const v8i* qf4, const int* qsc, const LaneOffs<D, QK>& lo) {
+  using G = Geo<D, QK>;
+  constexpr int NCB = G::NCB;
+  constexpr int NQK = 2 * G::NQF;                          // QK MFMAs of one tile
+  constexpr int KREADS = NQK * (QK == QK_MXFP4 ? 2 : 1);   // their LDS reads (+ scale bytes)
+  constexpr int VSLOT = 112 / NQK;                         // vector instructions per MFMA slot
+  qk_tile<D, QK>(Sn, lk_next, qf, qf4, qsc, lo);
   v8i pb;
   float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
@@ -350,7 +369,6 @@ __device__ __forceinline__ void softmax_pv(RowState<D>& st, const Score<D, QK>& 
     pb[i / 4] = pack_fp8x4(p0, p1, p2, p3);
   }
   st.l += ps0 + ps1;
-  __builtin_amdgcn_sched_barrier(0);
   // O^T += V^T P~^T
 #pragma unroll
   for (int cb = 0; cb < NCB; cb++) {
@@ -359,6 +377,15 @@ __device__ __forceinline__ void softmax_pv(RowState<D>& st, const Score<D, QK>& 
     const v8i va = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     st.O[cb] = mfma_f8(va, pb, st.O[cb]);
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, KREADS, 0);     // DS reads: K operands
+#pragma unroll
+  for (int i = 0; i < NQK; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one QK MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, VSLOT, 0);    // vector work of tile j
+  }
+  __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);         // the rest of it
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * NCB, 0);    // DS reads: V operands
+  __builtin_amdgcn_sched_group_barrier(0x008, NCB, 0);        // PV MFMAs
 }
 
 template <int D, int QK, bool CAUSAL, int DT>
@@ -431,11 +458,13 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
     issue_v<D, QK>(lv[(j + 1) & 1], a, bh, min(j + 1, last), lo, w);
     uint4 dsr;
     if (QK == QK_MXFP4) dsr = load_ds(a, bh, min(j + 1, last));
-    if (j + 1 < wtiles) qk_tile<D, QK>(Sn, lk[(j + 1) & 1], qf, qf4, qsc, lo);
-    // keep the phases apart: QK(j+1)'s operands die before the softmax starts (its MFMAs keep
-    // running underneath), so the live set stays within the 256-register budget of 2 waves/SIMD
-    __builtin_amdgcn_sched_barrier(0);
-    if (j < wtiles) softmax_pv<D, QK, CAUSAL>(st, Sc, lv[j & 1], kstep, qstep, a.sm_log2e, j, a.N, qw, qrow, hh, lo);
+    // tiles past this wave's last visible one need neither softmax nor the next scores; the
+    // last tile computes scores of an already-loaded tile that nothing reads
+    if (j < wtiles) {
+      float u[32], c, off;
+      softmax_max<D, QK, CAUSAL>(st, Sc, lv[j & 1], kstep, qstep, a.sm_log2e, j, a.N, qw, qrow, hh, u, c, off);
+      softmax_body_pv<D, QK>(st, u, c, off, Sn, lk[(j + 1) & 1], lv[j & 1], qf, qf4, qsc, lo);
+    }
     if (QK == QK_MXFP4) store_ds<D, QK>(dsr, lv[(j + 1) & 1], a.sm_log2e);
     wait_vmem();
     __syncthreads();
