@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 HEADLINE = "int8_fp8_causal_b1h32n4096d128"
 METRIC = "attention TOPS (4·B·H·N²·d/s, ½ if causal) at d=128; % of MI355X MFMA peak"
 # MI355X dense peaks (TFLOP/s or TOP/s)
-PEAK = {"int8_fp8": 5000.0, "mxfp4_fp8": 1.0 / (0.5 / 10100.0 + 0.5 / 5000.0), "mxfp4": 10100.0}
+PEAK = {"int8_fp8": 5000.0, "mxfp4_fp8": 1.0 / (0.5 / 10100.0 + 0.5 / 5000.0), "mxfp4_mxfp4": 10100.0}
 HBM_PEAK_GBS = 8000.0
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_int8_fp8_causal_b1h32n4096d128.txt")
@@ -126,14 +126,14 @@ def time_region(fn, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def run_workload(name, S, torch, steps, warmup):
+def run_workload(name, S, torch, steps, warmup, pv="fp8"):
     """Times the full step, the fused kernel alone and the prologue alone (HIP events on the launch stream)."""
     from bit_quantized_attention_smooth_amd.workloads import workload_inputs
     x, w = workload_inputs(name)
     dev = torch.device("cuda:0")
     g = {n: x[n].to(dev) for n in "qkv"}
     B, H, N, d, causal = w["B"], w["H"], w["N"], w["d"], w["causal"]
-    qk, pv = w["qk_fmt"], "fp8"
+    qk = w["qk_fmt"]
     p = S.problem(B, H, N, d, causal=causal, sm_scale=w["sm_scale"], dtype=g["q"].dtype, qk_fmt=qk, pv_fmt=pv)
     nbytes, _ = S.quant_size(p)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -160,8 +160,11 @@ def run_workload(name, S, torch, steps, warmup):
     E = B * H * N * d
     # prologue algorithmic bytes: read Q, K, V once (2 B each); write codes (1 B INT8/FP8, 0.5 B MXFP4)
     # plus the scales (INT8: 4 B per 64 tokens; MXFP4: 1 B per 32 elements) and the per-token LSE term
-    code_b = (2 * E + E) if qk == "int8" else (2 * (E // 2 + E // 32) + E)
-    scale_b = (2 * 4 * B * H * ((N + 63) // 64) if qk == "int8" else 4 * B * H * N) + 4 * B * H * d + 4 * B * H * N
+    # (MXFP4 V: 0.5 B codes + 1 B per 32 tokens and channel; FP8 V: 1 B codes + a fp32 step per channel)
+    v_b = E if pv == "fp8" else E // 2 + E // 32
+    code_b = (2 * E + v_b) if qk == "int8" else (2 * (E // 2 + E // 32) + v_b)
+    scale_b = (2 * 4 * B * H * ((N + 63) // 64) if qk == "int8" else 4 * B * H * N) + \
+        (4 * B * H * d if pv == "fp8" else 0) + 4 * B * H * N
     pro_bytes = 3 * 2 * E + code_b + scale_b
     return dict(name=name, B=B, H=H, N=N, d=d, causal=causal, qk=qk, pv=pv, ms_step=ms_step, wall=wall,
                 ms_kernel=ms_kernel, ms_prologue=ms_pro, ops=ops, pro_bytes=pro_bytes, dtype=w["dtype"],
@@ -276,12 +279,14 @@ def main():
     }
     if not args.no_extra:
         extra = {}
-        for name in ("int8_fp8_b1h32n8192d128", "int8_fp8_causal_b1h32n16384d128", "mxfp4_b4h32n8192d128",
-                     "int8_fp8_b2h24n16384d64"):
-            log(f"[bench] secondary {name}")
-            e = run_workload(name, S, torch, max(5, args.steps // 5), 3)
-            pk = PEAK["int8_fp8" if e["qk"] == "int8" else "mxfp4_fp8"]
-            extra[name] = {"kernel_tops": round(e["kernel_tops"], 1), "frac": round(e["kernel_tops"] / pk, 4),
+        for name, pv in (("int8_fp8_b1h32n8192d128", "fp8"), ("int8_fp8_causal_b1h32n16384d128", "fp8"),
+                         ("mxfp4_b4h32n8192d128", "fp8"), ("mxfp4_b4h32n8192d128", "mxfp4"),
+                         ("int8_fp8_b2h24n16384d64", "fp8")):
+            log(f"[bench] secondary {name} (P~V {pv})")
+            e = run_workload(name, S, torch, max(5, args.steps // 5), 3, pv=pv)
+            pk = PEAK["int8_fp8" if e["qk"] == "int8" else ("mxfp4_fp8" if pv == "fp8" else "mxfp4_mxfp4")]
+            key = name if pv == "fp8" or e["qk"] == "int8" else name + "+pv_mxfp4"
+            extra[key] = {"kernel_tops": round(e["kernel_tops"], 1), "frac": round(e["kernel_tops"] / pk, 4),
                            "step_tops": round(e["step_tops"], 1), "kernel_ms": round(e["ms_kernel"], 4),
                            "prologue_GB/s": round(e["prologue_gbs"], 1)}
             torch.cuda.empty_cache()

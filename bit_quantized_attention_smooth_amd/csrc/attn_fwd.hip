@@ -57,10 +57,13 @@ struct FwdArgs {
   float sm_log2e;
 };
 
+#ifndef MFMA_IL_D128
+#define MFMA_IL_D128 0
+#endif
 constexpr int kTK = 64;      // keys per tile (= the INT8 K block)
 constexpr int kQT = 128;     // queries per workgroup pass
 
-template <int D, int QK>
+template <int D, int QK, int PV = PV_FP8>
 struct Geo {
   static constexpr int KROW = QK == QK_INT8 ? D : D / 2;               // bytes per key row
   static constexpr int KCH = KROW / 16;                                 // 16-byte chunks per key row
@@ -68,8 +71,12 @@ struct Geo {
   static constexpr int SBYTES = QK == QK_MXFP4 ? kTK * (D / 32) : 0;    // E8M0 bytes per tile
   static constexpr int DSBYTES = QK == QK_MXFP4 ? kTK * 4 : 0;          // scaled dS floats per tile
   static constexpr int KSTAGE = KBYTES + SBYTES;
-  static constexpr int VBYTES = D * kTK;                                // FP8 V^T tile
-  static constexpr int VSTAGE = VBYTES + DSBYTES;                       // V^T tile + scaled dS
+  // V^T tile: FP8 (64 bytes per channel) or MXFP4 (32 bytes per channel, then one E8M0 byte
+  // per channel for each of the two 32-key groups)
+  static constexpr int VBYTES = PV == PV_MXFP4 ? D * kTK / 2 : D * kTK;
+  static constexpr int VSB = PV == PV_MXFP4 ? 2 * D : 0;
+  static constexpr int DSOFF = VBYTES + VSB;                            // scaled dS after V
+  static constexpr int VSTAGE = DSOFF + DSBYTES;
   static constexpr int KCHUNKS = KBYTES / 16;                           // 16-byte chunks per K tile
   static constexpr int VCHUNKS = VBYTES / 16;                           // 16-byte chunks per V^T tile
   template <int NT> static constexpr int kloads() { return (KCHUNKS + NT - 1) / NT; }   // per lane, NT threads
@@ -93,6 +100,7 @@ __device__ __forceinline__ int swz(int r) {
   return (r >> 5) & 1;                                                   // 32-byte rows, 2 chunks
 }
 __device__ __forceinline__ int swz_v(int r) { return (r >> 2) & 3; }     // V^T rows of 64 bytes
+__device__ __forceinline__ int swz_v4(int r) { return (r >> 3) & 1; }    // MXFP4 V^T rows of 32 bytes
 
 template <int DT>
 __device__ __forceinline__ uint32_t pack2_io(float a, float b) {
@@ -117,15 +125,17 @@ __device__ __forceinline__ uint32_t pack2_io(float a, float b) {
 // registers because it is rescaled on the way), read one step later than K.
 // Per-lane byte offsets, computed once per query-tile pass and pinned in registers (the
 // tile base addresses are wave-uniform, so every access is uniform base + lane offset).
-template <int D, int QK, int NT = 256>
+template <int D, int QK, int NT = 256, int PV = PV_FP8>
 struct LaneOffs {
-  using G = Geo<D, QK>;
+  using G = Geo<D, QK, PV>;
+  static constexpr int NTHREADS = NT;
   static constexpr int KL = G::template kloads<NT>(), VL = G::template vloads<NT>();
   uint32_t kld[KL];                 // direct-load source offsets inside a K tile
   uint32_t vld[VL];                 // direct-load source offsets inside a V^T tile
   uint32_t kop[2][G::NQF];          // LDS offsets of the K operand reads (subtile, chunk)
   uint32_t ksc[2][G::NQF];          // MXFP4: LDS offsets of the K scale bytes
-  uint32_t vop[G::NCB][2];          // LDS offsets of the V^T operand reads (block, half)
+  uint32_t vop[G::NCB][2];          // LDS offsets of the V^T operand reads: FP8 (block, half);
+                                    // MXFP4 (block, {codes, scale byte})
 
   __device__ __forceinline__ void init(int w, int lane, int n, int hh) {
 #pragma unroll
@@ -137,8 +147,13 @@ struct LaneOffs {
 #pragma unroll
     for (int i = 0; i < VL; i++) {
       const int P = (NT * i + 64 * w + lane) % G::VCHUNKS;
-      const int row = P >> 2, col = (P & 3) ^ swz_v(row);
-      vld[i] = row * 64 + col * 16;
+      if (PV == PV_MXFP4) {
+        const int row = P >> 1, col = (P & 1) ^ swz_v4(row);
+        vld[i] = row * 32 + col * 16;
+      } else {
+        const int row = P >> 2, col = (P & 3) ^ swz_v(row);
+        vld[i] = row * 64 + col * 16;
+      }
     }
 #pragma unroll
     for (int s = 0; s < 2; s++) {
@@ -153,8 +168,13 @@ struct LaneOffs {
 #pragma unroll
     for (int c = 0; c < G::NCB; c++) {
       const int row = 32 * c + n;
-      vop[c][0] = row * 64 + (((2 * hh) ^ swz_v(row)) << 4);
-      vop[c][1] = row * 64 + (((2 * hh + 1) ^ swz_v(row)) << 4);
+      if (PV == PV_MXFP4) {
+        vop[c][0] = row * 32 + ((hh ^ swz_v4(row)) << 4);
+        vop[c][1] = G::VBYTES + hh * D + row;
+      } else {
+        vop[c][0] = row * 64 + (((2 * hh) ^ swz_v(row)) << 4);
+        vop[c][1] = row * 64 + (((2 * hh + 1) ^ swz_v(row)) << 4);
+      }
     }
     // opaque to the optimizer: keep these in registers instead of recomputing them every tile
 #pragma unroll
@@ -178,14 +198,13 @@ struct LaneOffs {
 // applied to the global source offset instead.  K stage: codes (+ E8M0 scales).  V stage:
 // V^T codes (+ dS * sm * log2 e, staged through registers because it is rescaled on the
 // way), read one step later than K.
-template <int D, int QK, int NT>
-__device__ __forceinline__ void issue_k(uint8_t* lds, const FwdArgs& a, int bh, int j, const LaneOffs<D, QK, NT>& lo,
-                                        int w, int lane) {
+template <int D, int QK, typename LO>
+__device__ __forceinline__ void issue_k(uint8_t* lds, const FwdArgs& a, int bh, int j, const LO& lo, int w, int lane) {
   using G = Geo<D, QK>;
   const uint8_t* kg = a.k_codes + ((size_t)bh * a.Np + (size_t)j * kTK) * G::KROW;
 #pragma unroll
-  for (int i = 0; i < LaneOffs<D, QK, NT>::KL; i++) {
-    const int pbase = NT * i + 64 * w;
+  for (int i = 0; i < LO::KL; i++) {
+    const int pbase = LO::NTHREADS * i + 64 * w;
     if (pbase < G::KCHUNKS) load_lds16(kg + lo.kld[i], lds + pbase * 16);
   }
   if (QK == QK_MXFP4 && w == 0 && lane < G::SBYTES / 16) {
@@ -194,15 +213,20 @@ __device__ __forceinline__ void issue_k(uint8_t* lds, const FwdArgs& a, int bh, 
   }
 }
 
-template <int D, int QK, int NT>
-__device__ __forceinline__ void issue_v(uint8_t* lds, const FwdArgs& a, int bh, int j, const LaneOffs<D, QK, NT>& lo,
-                                        int w) {
-  using G = Geo<D, QK>;
+template <int D, int QK, int NT, int PV>
+__device__ __forceinline__ void issue_v(uint8_t* lds, const FwdArgs& a, int bh, int j,
+                                        const LaneOffs<D, QK, NT, PV>& lo, int w, int lane) {
+  using G = Geo<D, QK, PV>;
   const uint8_t* vg = a.v_codes + ((size_t)bh * (a.Np / kTK) + j) * G::VBYTES;
 #pragma unroll
-  for (int i = 0; i < LaneOffs<D, QK, NT>::VL; i++) {
+  for (int i = 0; i < LaneOffs<D, QK, NT, PV>::VL; i++) {
     const int pbase = NT * i + 64 * w;
     if (pbase < G::VCHUNKS) load_lds16(vg + lo.vld[i], lds + pbase * 16);
+  }
+  if (PV == PV_MXFP4 && w == NT / 64 - 1 && lane < G::VSB / 16) {
+    // E8M0 bytes of the tile's two 32-key groups: [group][channel], contiguous in the buffer
+    const uint8_t* sg = reinterpret_cast<const uint8_t*>(a.v_scales) + ((size_t)bh * (a.Np / 32) + 2 * j) * D;
+    load_lds16(sg + 16 * lane, lds + G::VBYTES + 16 * lane);
   }
 }
 
@@ -210,10 +234,10 @@ __device__ __forceinline__ void issue_v(uint8_t* lds, const FwdArgs& a, int bh, 
 __device__ __forceinline__ uint4 load_ds(const FwdArgs& a, int bh, int j) {
   return reinterpret_cast<const uint4*>(a.delta_s + (size_t)bh * a.Np + (size_t)j * kTK)[threadIdx.x & 15];
 }
-template <int D, int QK>
+template <int D, int QK, int PV>
 __device__ __forceinline__ void store_ds(uint4 r, uint8_t* lds, float c) {
   const v4f f = {__uint_as_float(r.x) * c, __uint_as_float(r.y) * c, __uint_as_float(r.z) * c, __uint_as_float(r.w) * c};
-  reinterpret_cast<v4f*>(lds + Geo<D, QK>::VBYTES)[threadIdx.x & 15] = f;
+  reinterpret_cast<v4f*>(lds + Geo<D, QK, PV>::DSOFF)[threadIdx.x & 15] = f;
 }
 
 // Wait for this wave's outstanding global loads (the direct-to-LDS tiles) before a barrier.
@@ -258,17 +282,18 @@ template <int D>
 struct RowState {
   v16f O[D / 32];
   float m, l;
+  float mt;   // MXFP4 P~: the tile max that fixes the frame of O (see softmax_max)
 };
 
 // Softmax of tile j from its score registers, then O^T += V^T P~^T.
 //   u_i = S_i (INT8: converted to fp32) or S_i + dS_i / c (MXFP4), with c = the positive
 //   log2-domain scale; masked entries are set to -inf; the row max is taken on u, and
 //   p448_i = exp2(u_i * c + (log2 448 - m)) comes out of one FMA and one exp2 per element.
-template <int D, int QK, bool CAUSAL>
+template <int D, int QK, bool CAUSAL, int PV>
 __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>& Sc, const uint8_t* vstage,
                                             const float* kstep, float qstep, float sm_log2e, int j, int N, int qw,
-                                            int qrow, int hh, float* u, float& c, float& off) {
-  using G = Geo<D, QK>;
+                                            int qrow, int hh, float* u, float& c, float& off, float& lsc) {
+  using G = Geo<D, QK, PV>;
   constexpr int NCB = G::NCB;
   const int kbase = j * kTK;
   const bool need_mask = kbase + kTK > N || (CAUSAL && kbase + kTK - 1 > qw);
@@ -310,7 +335,7 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
     }
   } else {
     // dS arrives pre-multiplied by sm * log2 e; u = S * sm * log2 e + dS * sm * log2 e, c = 1
-    const float* dsl = reinterpret_cast<const float*>(vstage + G::VBYTES) + 32 * hh;
+    const float* dsl = reinterpret_cast<const float*>(vstage + G::DSOFF) + 32 * hh;
 #pragma unroll
     for (int s = 0; s < 2; s++)
 #pragma unroll
@@ -333,65 +358,121 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
   }
   const float mnew = fmaxf(st.m, mt);
   const float mref = mnew == -INFINITY ? 0.0f : mnew;
-  if (__any(mnew > st.m)) {
-    const float alpha = fast_exp2(st.m - mref);
-    st.l *= alpha;
+  if (PV == PV_FP8) {
+    if (__any(mnew > st.m)) {
+      const float alpha = fast_exp2(st.m - mref);
+      st.l *= alpha;
 #pragma unroll
-    for (int cb = 0; cb < NCB; cb++) st.O[cb] *= alpha;
+      for (int cb = 0; cb < NCB; cb++) st.O[cb] *= alpha;
+    }
+    off = kLog2_448 - mref;
+    lsc = 1.0f;
+  } else {
+    // MXFP4 P~: p' = sigma p with sigma = 6 / max_tile(p) = 6 exp2(m - mt), so p' = exp2(t - mt +
+    // log2 6) needs only the tile max mt.  O is kept as O' = sigma O (the frame of the last
+    // tile's sigma), so P~V accumulates into it directly and the frame moves by
+    // beta = sigma_j alpha_j / sigma_{j-1} = exp2(mt_{j-1} - mt_j).  A row whose tile is fully
+    // masked keeps its frame; mt is held within 64 of m (p' of such a tile is then < 6, its
+    // share of O < 2^-64, and the frame cannot overflow).  l' = 6 sum p = exp2(mt - m) sum p'.
+    const float mte = mt == -INFINITY ? st.mt : fmaxf(mt, mnew - 64.0f);
+    st.l *= fast_exp2(st.m - mref);
+    const float beta = mte == -INFINITY ? 1.0f : fast_exp2(st.mt - mte);
+    if (__any(beta != 1.0f)) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; cb++) st.O[cb] *= beta;
+    }
+    st.mt = mte;
+    const float mter = mte == -INFINITY ? 0.0f : mte;
+    off = kLog2_6 - mter;
+    lsc = fast_exp2(mter - mref);
   }
   st.m = mnew;
-  off = kLog2_448 - mref;
 }
 
-// Second half of tile j's softmax, p448 = exp2(u c + off), the row sum and the FP8 pack,
-// sharing one basic block with the QK MFMAs of tile j+1 (into Sn) and the PV MFMAs of tile
-// j.  The issue order is pinned: the K operand reads, then the QK MFMAs one at a time between
-// slices of the exp / pack stream (so the matrix core runs under the vector work of the same
-// wave instead of stalling its issue), then the V operand reads and the PV MFMAs.
-template <int D, int QK>
-__device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u, float c, float off, Score<D, QK>& Sn,
-                                                const uint8_t* lk_next, const uint8_t* vstage, const v4i* qf,
-                                                const v8i* qf4, const int* qsc, const LaneOffs<D, QK>& lo) {
-  using G = Geo<D, QK>;
+// Second half of tile j's softmax: p = exp2(u c + off) (FP8: 448 P; MXFP4: sigma P), the row
+// sum and the P~ pack, sharing one basic block with the QK MFMAs of tile j+1 (into Sn) and the
+// PV MFMAs of tile j.  The issue order is pinned: the K operand reads, then the QK MFMAs one at
+// a time between slices of the exp / pack stream (so the matrix core runs under the vector
+// work of the same wave instead of stalling its issue), then the V operand reads and the PV
+// MFMAs.  MXFP4 P~: each lane's 32 keys are one MX block (E8M0 from the block max, floor rule;
+// E2M1 RNE with saturation), and the scaled FP4 MFMA applies both operands' block scales.
+template <int D, int QK, int PV, bool IL, typename LO>
+__device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u, float c, float off, float lsc,
+                                                Score<D, QK>& Sn, const uint8_t* lk_next, const uint8_t* vstage,
+                                                const v4i* qf, const v8i* qf4, const int* qsc, const LO& lo) {
+  using G = Geo<D, QK, PV>;
   constexpr int NCB = G::NCB;
   constexpr int NQK = 2 * G::NQF;                          // QK MFMAs of one tile
   constexpr int KREADS = NQK * (QK == QK_MXFP4 ? 2 : 1);   // their LDS reads (+ scale bytes)
   constexpr int VSLOT = 112 / NQK;                         // vector instructions per MFMA slot
-  qk_tile<D, QK>(Sn, lk_next, qf, qf4, qsc, lo);
-  v8i pb;
+  if (IL) qk_tile<D, QK>(Sn, lk_next, qf, qf4, qsc, lo);
   float ps0 = 0.0f, ps1 = 0.0f;
+  if (PV == PV_FP8) {
+    v8i pb;
 #pragma unroll
-  for (int i = 0; i < 32; i += 4) {
-    const float p0 = fast_exp2(fmaf(u[i], c, off)), p1 = fast_exp2(fmaf(u[i + 1], c, off));
-    const float p2 = fast_exp2(fmaf(u[i + 2], c, off)), p3 = fast_exp2(fmaf(u[i + 3], c, off));
-    ps0 += p0 + p1;
-    ps1 += p2 + p3;
-    pb[i / 4] = pack_fp8x4(p0, p1, p2, p3);
-  }
-  st.l += ps0 + ps1;
-  // O^T += V^T P~^T
+    for (int i = 0; i < 32; i += 4) {
+      const float p0 = fast_exp2(fmaf(u[i], c, off)), p1 = fast_exp2(fmaf(u[i + 1], c, off));
+      const float p2 = fast_exp2(fmaf(u[i + 2], c, off)), p3 = fast_exp2(fmaf(u[i + 3], c, off));
+      ps0 += p0 + p1;
+      ps1 += p2 + p3;
+      pb[i / 4] = pack_fp8x4(p0, p1, p2, p3);
+    }
+    st.l += ps0 + ps1;
+    // O^T += V^T P~^T
 #pragma unroll
-  for (int cb = 0; cb < NCB; cb++) {
-    const v4i v0 = *reinterpret_cast<const v4i*>(vstage + lo.vop[cb][0]);
-    const v4i v1 = *reinterpret_cast<const v4i*>(vstage + lo.vop[cb][1]);
-    const v8i va = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-    st.O[cb] = mfma_f8(va, pb, st.O[cb]);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, KREADS, 0);     // DS reads: K operands
+    for (int cb = 0; cb < NCB; cb++) {
+      const v4i v0 = *reinterpret_cast<const v4i*>(vstage + lo.vop[cb][0]);
+      const v4i v1 = *reinterpret_cast<const v4i*>(vstage + lo.vop[cb][1]);
+      const v8i va = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      st.O[cb] = mfma_f8(va, pb, st.O[cb]);
+    }
+  } else {
+    float pf[32];
+    float am0 = 0.0f, am1 = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NQK; i++) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one QK MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, VSLOT, 0);    // vector work of tile j
+    for (int i = 0; i < 32; i += 4) {
+      pf[i] = fast_exp2(fmaf(u[i], c, off));
+      pf[i + 1] = fast_exp2(fmaf(u[i + 1], c, off));
+      pf[i + 2] = fast_exp2(fmaf(u[i + 2], c, off));
+      pf[i + 3] = fast_exp2(fmaf(u[i + 3], c, off));
+      ps0 += pf[i] + pf[i + 1];
+      ps1 += pf[i + 2] + pf[i + 3];
+      am0 = fmaxf(am0, fmaxf(pf[i], pf[i + 1]));
+      am1 = fmaxf(am1, fmaxf(pf[i + 2], pf[i + 3]));
+    }
+    st.l = fmaf(lsc, ps0 + ps1, st.l);
+    const int sb = (int)mx_fp4_scale_byte(fmaxf(am0, am1));
+    // byte 0 (an all-zero block, e.g. keys past the causal diagonal): codes 0 under any scale,
+    // so convert with 1 rather than the subnormal 2^-127
+    const float scl = sb == 0 ? 1.0f : e8m0_to_float((unsigned)sb);
+    v8i pb = v8i{};
+#pragma unroll
+    for (int k = 0; k < 4; k++) pb[k] = (int)pack_fp4x8(pf + 8 * k, scl);
+#pragma unroll
+    for (int cb = 0; cb < NCB; cb++) {
+      const v4i v0 = *reinterpret_cast<const v4i*>(vstage + lo.vop[cb][0]);
+      const int sa = vstage[lo.vop[cb][1]];
+      const v8i va = v8i{v0[0], v0[1], v0[2], v0[3], 0, 0, 0, 0};
+      st.O[cb] = mfma_mxfp4(va, pb, st.O[cb], sa, sb);
+    }
   }
-  __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);         // the rest of it
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * NCB, 0);    // DS reads: V operands
-  __builtin_amdgcn_sched_group_barrier(0x008, NCB, 0);        // PV MFMAs
+  if (IL) {
+    __builtin_amdgcn_sched_group_barrier(0x100, KREADS, 0);     // DS reads: K operands
+#pragma unroll
+    for (int i = 0; i < NQK; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one QK MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, VSLOT, 0);    // vector work of tile j
+    }
+    __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);         // the rest of it
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NCB, 0);    // DS reads: V operands
+    __builtin_amdgcn_sched_group_barrier(0x008, NCB, 0);        // PV MFMAs
+  }
 }
 
-template <int D, int QK, bool CAUSAL, int DT>
-__device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint8_t (*lk)[Geo<D, QK>::KSTAGE],
-                                          uint8_t (*lv)[Geo<D, QK>::VSTAGE]) {
-  using G = Geo<D, QK>;
+template <int D, int QK, bool CAUSAL, int DT, int PV>
+__device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint8_t (*lk)[Geo<D, QK, PV>::KSTAGE],
+                                          uint8_t (*lv)[Geo<D, QK, PV>::VSTAGE]) {
+  using G = Geo<D, QK, PV>;
   constexpr int NCB = G::NCB, NQF = G::NQF;
   const int qbase = qt * kQT;
   const int lane = threadIdx.x & 63;
@@ -399,7 +480,7 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
   const int n = lane & 31, hh = lane >> 5;
   const int qw = qbase + 32 * w;          // first query of this wave
   const int qrow = qw + n;                // this lane's query
-  LaneOffs<D, QK> lo;
+  LaneOffs<D, QK, 256, PV> lo;
   lo.init(w, lane, n, hh);
 
   // Q fragments (B operand), resident for the whole pass
@@ -434,6 +515,7 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
   for (int c = 0; c < NCB; c++) st.O[c] = v16f{};
   st.m = -INFINITY;
   st.l = 0.0f;
+  st.mt = -INFINITY;
 
   // prologue: K0 -> LDS, QK(0); then K1, V0 -> LDS
   issue_k<D, QK>(lk[0], a, bh, 0, lo, w, lane);
@@ -442,8 +524,8 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
   Score<D, QK> Sa, Sb;
   qk_tile<D, QK>(Sa, lk[0], qf, qf4, qsc, lo);
   issue_k<D, QK>(lk[1], a, bh, min(1, ntiles - 1), lo, w, lane);
-  issue_v<D, QK>(lv[0], a, bh, 0, lo, w);
-  if (QK == QK_MXFP4) store_ds<D, QK>(load_ds(a, bh, 0), lv[0], a.sm_log2e);
+  issue_v<D, QK>(lv[0], a, bh, 0, lo, w, lane);
+  if (QK == QK_MXFP4) store_ds<D, QK, PV>(load_ds(a, bh, 0), lv[0], a.sm_log2e);
   wait_vmem();
   __syncthreads();
 
@@ -453,19 +535,28 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
   // clamped to the last tile, so the loads are unconditional.  Unrolled twice so Sa/Sb
   // alternate without copies.
   const int last = ntiles - 1;
+  constexpr bool IL = !(D == 128 && QK == QK_INT8 && MFMA_IL_D128 == 0);
   auto step = [&](int j, const Score<D, QK>& Sc, Score<D, QK>& Sn) {
     issue_k<D, QK>(lk[j & 1], a, bh, min(j + 2, last), lo, w, lane);
-    issue_v<D, QK>(lv[(j + 1) & 1], a, bh, min(j + 1, last), lo, w);
+    issue_v<D, QK>(lv[(j + 1) & 1], a, bh, min(j + 1, last), lo, w, lane);
     uint4 dsr;
     if (QK == QK_MXFP4) dsr = load_ds(a, bh, min(j + 1, last));
-    // tiles past this wave's last visible one need neither softmax nor the next scores; the
-    // last tile computes scores of an already-loaded tile that nothing reads
-    if (j < wtiles) {
-      float u[32], c, off;
-      softmax_max<D, QK, CAUSAL>(st, Sc, lv[j & 1], kstep, qstep, a.sm_log2e, j, a.N, qw, qrow, hh, u, c, off);
-      softmax_body_pv<D, QK>(st, u, c, off, Sn, lk[(j + 1) & 1], lv[j & 1], qf, qf4, qsc, lo);
+    // tiles past this wave's last visible one need neither softmax nor the next scores.  With
+    // IL the next tile's QK MFMAs are spread through the exp / pack stream (the last tile then
+    // computes scores of an already-loaded tile that nothing reads); otherwise they are all
+    // issued before the softmax, whose vector work then runs under them.  Measured: IL is
+    // ahead at d = 64 (fewer, shorter QK MFMAs per tile), behind at d = 128 INT8.
+    if (!IL) {
+      if (j + 1 < wtiles) qk_tile<D, QK>(Sn, lk[(j + 1) & 1], qf, qf4, qsc, lo);
+      // keep the phases apart: QK(j+1)'s operands die before the softmax starts
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (QK == QK_MXFP4) store_ds<D, QK>(dsr, lv[(j + 1) & 1], a.sm_log2e);
+    if (j < wtiles) {
+      float u[32], c, off, lsc;
+      softmax_max<D, QK, CAUSAL, PV>(st, Sc, lv[j & 1], kstep, qstep, a.sm_log2e, j, a.N, qw, qrow, hh, u, c, off, lsc);
+      softmax_body_pv<D, QK, PV, IL>(st, u, c, off, lsc, Sn, lk[(j + 1) & 1], lv[j & 1], qf, qf4, qsc, lo);
+    }
+    if (QK == QK_MXFP4) store_ds<D, QK, PV>(dsr, lv[(j + 1) & 1], a.sm_log2e);
     wait_vmem();
     __syncthreads();
   };
@@ -476,30 +567,33 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
   }
   if (j < ntiles) step(j, Sa, Sb);
 
-  // ---- epilogue: O / l * dV, LSE ----
+  // ---- epilogue: O / l (FP8: times the V channel step), LSE ----
+  //   FP8 P~: O and l both carry the factor 448.  MXFP4 P~: O' = sigma O with sigma = 6 exp2(m - mt)
+  //   and l' = 6 sum p, so O / l = O' exp2(mt - m) / l'.
   const float lt = half_sum(st.l);
   if (qrow < a.N) {
-    const float inv = 1.0f / lt;
-    const float* vs = a.v_scales + (size_t)bh * D;
+    const float inv = PV == PV_FP8 ? 1.0f / lt : fast_exp2(st.mt - st.m) / lt;
     uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + ((size_t)bh * a.N + qrow) * D;
 #pragma unroll
     for (int c = 0; c < NCB; c++)
 #pragma unroll
       for (int g = 0; g < 4; g++) {
         const int ch = 32 * c + 8 * g + 4 * hh;
-        const v4f sc = *reinterpret_cast<const v4f*>(vs + ch);
-        const uint32_t lo = pack2_io<DT>(st.O[c][4 * g] * (sc[0] * inv), st.O[c][4 * g + 1] * (sc[1] * inv));
-        const uint32_t hi = pack2_io<DT>(st.O[c][4 * g + 2] * (sc[2] * inv), st.O[c][4 * g + 3] * (sc[3] * inv));
+        const v4f sc = PV == PV_FP8 ? *reinterpret_cast<const v4f*>(a.v_scales + (size_t)bh * D + ch) * inv
+                                    : v4f{inv, inv, inv, inv};
+        const uint32_t lo = pack2_io<DT>(st.O[c][4 * g] * sc[0], st.O[c][4 * g + 1] * sc[1]);
+        const uint32_t hi = pack2_io<DT>(st.O[c][4 * g + 2] * sc[2], st.O[c][4 * g + 3] * sc[3]);
         *reinterpret_cast<uint2*>(orow + ch) = make_uint2(lo, hi);
       }
     if (a.lse && hh == 0)
-      a.lse[(size_t)bh * a.N + qrow] = (st.m + __log2f(lt) - kLog2_448) * kLn2 + a.lse_corr[(size_t)bh * a.N + qrow];
+      a.lse[(size_t)bh * a.N + qrow] =
+          (st.m + __log2f(lt) - (PV == PV_FP8 ? kLog2_448 : kLog2_6)) * kLn2 + a.lse_corr[(size_t)bh * a.N + qrow];
   }
 }
 
-template <int D, int QK, bool CAUSAL, int DT>
+template <int D, int QK, bool CAUSAL, int DT, int PV>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
-  using G = Geo<D, QK>;
+  using G = Geo<D, QK, PV>;
   __shared__ __align__(16) uint8_t lk[2][G::KSTAGE];
   __shared__ __align__(16) uint8_t lv[2][G::VSTAGE];
   const int nqt = a.Np / kQT;
@@ -509,29 +603,29 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     const int npair = (nqt + 1) / 2;
     const int bh = id / npair, g = id % npair;
     const int heavy = nqt - 1 - g;
-    run_qtile<D, QK, CAUSAL, DT>(a, bh, heavy, lk, lv);
+    run_qtile<D, QK, CAUSAL, DT, PV>(a, bh, heavy, lk, lv);
     if (g < heavy) {
       __syncthreads();
-      run_qtile<D, QK, CAUSAL, DT>(a, bh, g, lk, lv);
+      run_qtile<D, QK, CAUSAL, DT, PV>(a, bh, g, lk, lv);
     }
   } else {
-    run_qtile<D, QK, CAUSAL, DT>(a, id / nqt, id % nqt, lk, lv);
+    run_qtile<D, QK, CAUSAL, DT, PV>(a, id / nqt, id % nqt, lk, lv);
   }
 }
 
-template <int D, int QK, int DT>
+template <int D, int QK, int DT, int PV>
 static hipError_t fwd_dispatch(const Shape& s, const FwdArgs& a, hipStream_t st) {
   const int nqt = s.Np / kQT;
   if (s.causal)
-    attn_fwd_kernel<D, QK, true, DT><<<s.B * s.H * ((nqt + 1) / 2), 256, 0, st>>>(a);
+    attn_fwd_kernel<D, QK, true, DT, PV><<<s.B * s.H * ((nqt + 1) / 2), 256, 0, st>>>(a);
   else
-    attn_fwd_kernel<D, QK, false, DT><<<s.B * s.H * nqt, 256, 0, st>>>(a);
+    attn_fwd_kernel<D, QK, false, DT, PV><<<s.B * s.H * nqt, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
-template <int QK, int DT>
+template <int QK, int DT, int PV>
 static hipError_t fwd_dispatch_d(const Shape& s, const FwdArgs& a, hipStream_t st) {
-  return s.d == 64 ? fwd_dispatch<64, QK, DT>(s, a, st) : fwd_dispatch<128, QK, DT>(s, a, st);
+  return s.d == 64 ? fwd_dispatch<64, QK, DT, PV>(s, a, st) : fwd_dispatch<128, QK, DT, PV>(s, a, st);
 }
 
 hipError_t launch_attn_fwd(const Shape& s, const QuantPtrs& qp, void* o, float* lse, hipStream_t st) {
@@ -550,10 +644,14 @@ hipError_t launch_attn_fwd(const Shape& s, const QuantPtrs& qp, void* o, float* 
   a.Np = s.Np;
   a.BH = s.B * s.H;
   a.sm_log2e = s.sm_scale * kLog2e;
-  if (s.pv_fmt != PV_FP8) return hipErrorInvalidValue;   // MXFP4 P~V: not in this kernel
-  if (s.qk_fmt == QK_INT8)
-    return s.io_dtype == 0 ? fwd_dispatch_d<QK_INT8, 0>(s, a, st) : fwd_dispatch_d<QK_INT8, 1>(s, a, st);
-  return s.io_dtype == 0 ? fwd_dispatch_d<QK_MXFP4, 0>(s, a, st) : fwd_dispatch_d<QK_MXFP4, 1>(s, a, st);
+  if (s.qk_fmt == QK_INT8) {
+    if (s.pv_fmt != PV_FP8) return hipErrorInvalidValue;
+    return s.io_dtype == 0 ? fwd_dispatch_d<QK_INT8, 0, PV_FP8>(s, a, st) : fwd_dispatch_d<QK_INT8, 1, PV_FP8>(s, a, st);
+  }
+  if (s.pv_fmt == PV_MXFP4)
+    return s.io_dtype == 0 ? fwd_dispatch_d<QK_MXFP4, 0, PV_MXFP4>(s, a, st)
+                           : fwd_dispatch_d<QK_MXFP4, 1, PV_MXFP4>(s, a, st);
+  return s.io_dtype == 0 ? fwd_dispatch_d<QK_MXFP4, 0, PV_FP8>(s, a, st) : fwd_dispatch_d<QK_MXFP4, 1, PV_FP8>(s, a, st);
 }
 
 }  // namespace sage

@@ -191,8 +191,6 @@ sage_status sage_attn_fwd_quantized(const void* quant_buf, size_t quant_bytes, c
   if (s != SAGE_OK) return s;
   if ((s = check_tensors({quant_buf, o})) != SAGE_OK) return s;
   if (lse && !aligned16(lse)) return fail(SAGE_ERR_INVALID_ARG, "lse must be 16-byte aligned");
-  if (p->pv_fmt == SAGE_FMT_MXFP4)
-    return fail(SAGE_ERR_UNSUPPORTED, "MXFP4 P~V is not implemented by the fused kernel in this build");
   sage_quant_layout L;
   compute_layout(p, &L);
   if (quant_bytes < L.total)
@@ -210,8 +208,6 @@ sage_status sage_attn_fwd_ex(const sage_problem* p, const void* q, const void* k
   if (s != SAGE_OK) return s;
   if ((s = check_tensors({q, k, v, o, ws})) != SAGE_OK) return s;
   if (lse && !aligned16(lse)) return fail(SAGE_ERR_INVALID_ARG, "lse must be 16-byte aligned");
-  if (p->pv_fmt == SAGE_FMT_MXFP4)
-    return fail(SAGE_ERR_UNSUPPORTED, "MXFP4 P~V is not implemented by the fused kernel in this build");
   sage_quant_layout L;
   compute_layout(p, &L);
   if (ws_bytes < L.total) return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
@@ -229,8 +225,6 @@ sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, 
   sage_status s = check_problem(&p);
   if (s != SAGE_OK) return s;
   if ((s = check_tensors({q, k, v, o})) != SAGE_OK) return s;
-  if (p.pv_fmt == SAGE_FMT_MXFP4)
-    return fail(SAGE_ERR_UNSUPPORTED, "MXFP4 P~V is not implemented by the fused kernel in this build");
   size_t bytes = 0;
   sage_quant_size(&p, &bytes, nullptr);
   void* ws = nullptr;

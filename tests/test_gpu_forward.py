@@ -1,7 +1,9 @@
 """GPU parity of the smoothing/quantization prologue and the fused forward
 against the CPU oracle: codes and scales bit-exact; O within max-abs 2e-2 and
 cosine >= 0.9999 of the oracle's simulation of the same quantization; cosine
->= 0.99 (INT8 QK) / 0.98 (MXFP4 QK) against exact fp64 attention."""
+against exact fp64 attention >= 0.99 (INT8 QK), 0.98 (MXFP4 QK, FP8 P~V) or
+0.965 (MXFP4 QK and P~V: the oracle's own simulation reaches about 0.972 on
+these inputs)."""
 import math
 
 import numpy as np
@@ -41,7 +43,17 @@ CASES = [
     ("int8_causal_d64_f16", 1, 2, 300, 64, "f16", True, "int8", "fp8", 5, 2.0, 0.0, 1 / 8),
     ("mxfp4_fp8_d128", 1, 3, 600, 128, "bf16", False, "mxfp4", "fp8", 3, 5.0, 0.0, 1 / math.sqrt(128)),
     ("mxfp4_fp8_causal_d64", 1, 2, 333, 64, "bf16", True, "mxfp4", "fp8", 6, 5.0, 0.0, 1 / 8),
+    ("mxfp4_mxfp4_d128", 1, 3, 600, 128, "bf16", False, "mxfp4", "mxfp4", 3, 5.0, 0.0, 1 / math.sqrt(128)),
+    ("mxfp4_mxfp4_causal_d64", 1, 2, 333, 64, "bf16", True, "mxfp4", "mxfp4", 6, 5.0, 0.0, 1 / 8),
+    ("mxfp4_mxfp4_d64_f16", 1, 2, 200, 64, "f16", False, "mxfp4", "mxfp4", 8, 2.0, 0.0, 1 / 8),
 ]
+
+
+def _ref_band(qk, pv):
+    """Cosine floor against exact fp64 attention for a format pair."""
+    if qk == "int8":
+        return 0.99
+    return 0.98 if pv == "fp8" else 0.965
 
 
 def _oracle_sim(f, qz_or, qk, pv, N, d, causal, sm, rows=None):
@@ -103,7 +115,7 @@ def test_forward_matches_oracle(sage, case):
     o_ref, lse_ref = oracle.attn_ref(f["q"], f["k"], f["v"], causal, sm)
     assert np.abs(o - o_sim).max() <= 2e-2
     assert cos(o, o_sim) >= 0.9999
-    assert cos(o, o_ref) >= (0.99 if qk == "int8" else 0.98)
+    assert cos(o, o_ref) >= _ref_band(qk, pv)
     assert np.allclose(lse, lse_sim, rtol=1e-4, atol=2e-3)
 
 
@@ -112,18 +124,19 @@ def test_forward_matches_oracle(sage, case):
 def test_forward_edge_lengths(sage, N, causal):
     import oracle
     banner(f"edge N={N} causal={causal}")
-    for qk, d in (("int8", 64), ("int8", 128), ("mxfp4", 128)):
+    for qk, d, pv in (("int8", 64, "fp8"), ("int8", 128, "fp8"), ("mxfp4", 128, "fp8"), ("mxfp4", 64, "mxfp4")):
         f, g = _inputs(1, 2, N, d, "bf16", 100 + N, 2.0)
         sm = 1 / math.sqrt(d)
-        o, lse = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, return_lse=True)
+        o, lse = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv,
+                               return_lse=True)
         torch.cuda.synchronize()
         o = to_np64(o).reshape(2, N, d)
         qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm) if qk == "int8" else \
-            oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt="fp8")
-        o_sim, lse_sim = _oracle_sim(f, qz, qk, "fp8", N, d, causal, sm)
-        assert np.abs(o - o_sim).max() <= 2e-2, (qk, d)
+            oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
+        o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
+        assert np.abs(o - o_sim).max() <= 2e-2, (qk, d, pv)
         if N > 1:
-            assert cos(o, o_sim) >= 0.9999, (qk, d)
+            assert cos(o, o_sim) >= 0.9999, (qk, d, pv)
         else:
             # one key: O is the dequantized V row
             assert np.allclose(o, o_sim, atol=2e-2)
@@ -152,12 +165,34 @@ def test_forward_constant_keys_closed_form(sage, qk, causal):
     assert np.all(np.abs(o - want) <= np.abs(want) * 2.0 ** -8 + 1e-6)
 
 
-FULL = ["int8_fp8_causal_b1h32n4096d128", "int8_fp8_b2h24n16384d64", "mxfp4_b4h32n8192d128",
-        "int8_fp8_b1h2n256d64"]
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_constant_keys_mxfp4_pv(sage, causal):
+    """MXFP4 QK and P~V with K constant along tokens: every p is 1, so sigma = 6/max p = 6 and
+    each P~ element is exactly E2M1 6 with block scale 2^0; O_i is then the (prefix) mean of
+    the MXFP4-dequantized V rows, exact up to fp32 accumulation and the output rounding."""
+    import oracle
+    banner(f"constant keys mxfp4 P~V causal={causal}")
+    B, H, N, d = 1, 2, 200, 128
+    f, g = _inputs(B, H, N, d, "bf16", 9)
+    g["k"] = g["k"][:, :, :1].expand(-1, -1, N, -1).contiguous()
+    f["k"] = np.repeat(f["k"][:, :1], N, axis=1)
+    o = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, qk_fmt="mxfp4", pv_fmt="mxfp4")
+    torch.cuda.synchronize()
+    o = to_np64(o).reshape(B * H, N, d)
+    qz = oracle.quant_mxfp4(f["q"], f["k"], f["v"], 0.1, pv_fmt="mxfp4")
+    ve = np.repeat(qz["ve"].astype(np.int64), 32, axis=1)[:, :N]            # [BH, N, d] E8M0 bytes
+    vdq = oracle.e2m1_decode(qz["vc"]) * np.ldexp(1.0, ve - 127)
+    want = np.cumsum(vdq, axis=1) / np.arange(1, N + 1)[None, :, None] if causal else \
+        np.broadcast_to(vdq.mean(axis=1, keepdims=True), vdq.shape)
+    assert np.all(np.abs(o - want) <= np.abs(want) * 2.0 ** -8 + 1e-5 * np.abs(vdq).max())
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_rows(sage, name):
+FULL = [("int8_fp8_causal_b1h32n4096d128", "fp8"), ("int8_fp8_b2h24n16384d64", "fp8"),
+        ("mxfp4_b4h32n8192d128", "fp8"), ("mxfp4_b4h32n8192d128", "mxfp4"), ("int8_fp8_b1h2n256d64", "fp8")]
+
+
+@pytest.mark.parametrize("name,pv", FULL, ids=[f"{n}-{p}" for n, p in FULL])
+def test_full_size_sampled_rows(sage, name, pv):
     """The named workloads at full size in the benchmark's launch configuration; the
     oracle recomputes sampled rows of a few heads."""
     import oracle
@@ -166,7 +201,6 @@ def test_full_size_sampled_rows(sage, name):
     x, w = workload_inputs(name)
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
     qk, sm, causal = w["qk_fmt"], w["sm_scale"], w["causal"]
-    pv = "fp8"
     g = {n: x[n].to(device()) for n in "qkv"}
     buf, p, lay = sage.quantize(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv)
     o, lse = sage.attn_fwd_quantized(buf, p, dtype=g["q"].dtype, return_lse=True)
@@ -183,7 +217,7 @@ def test_full_size_sampled_rows(sage, name):
     else:
         qz = oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
         r = unpack_mxfp4(buf, p, lay, pv)
-        for key in ("qc", "kc", "qe", "ke", "vc", "vs", "mu_k", "mu_q"):
+        for key in ("qc", "kc", "qe", "ke", "vc", "vs" if pv == "fp8" else "ve", "mu_k", "mu_q"):
             assert np.array_equal(r[key][heads], qz[key]), key
     o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm, rows=rows)
     o_ref, _ = oracle.attn_ref(f["q"], f["k"], f["v"], causal, sm, rows=rows)
@@ -191,7 +225,7 @@ def test_full_size_sampled_rows(sage, name):
     lg = lse.cpu().numpy().reshape(B * H, N)[heads][:, rows]
     assert np.abs(og - o_sim).max() <= 2e-2
     assert cos(og, o_sim) >= 0.9999
-    assert cos(og, o_ref) >= (0.99 if qk == "int8" else 0.98)
+    assert cos(og, o_ref) >= _ref_band(qk, pv)
     assert np.allclose(lg, lse_sim, rtol=1e-4, atol=2e-3)
     # every output finite at full size
     assert torch.isfinite(o).all()
