@@ -32,11 +32,11 @@
 // are already the B operand of the PV MFMA O^T = V^T P~^T (A = V^T, rows =
 // channels, K = the same 32 keys).
 //
-// Pipeline: the QK MFMAs of tile j+1 are issued before the softmax of tile j,
-// so the matrix unit works while the vector unit runs the softmax; K runs one
-// tile ahead of V through two LDS buffers each, with one barrier per tile.
-// Causal: each workgroup takes a heavy and a light query tile (qt, nqt-1-qt),
-// so all workgroups carry the same number of key tiles.
+// Pipeline: the QK MFMAs of tile j+1 overlap the softmax of tile j (issued before it,
+// or spread through its exp / pack stream where that measured faster), so the matrix
+// unit works while the vector unit runs the softmax; K runs one tile ahead of V
+// through two LDS buffers each, with one barrier per tile.
+// Causal: one query tile per workgroup, longest first (see attn_fwd_kernel).
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
 
@@ -517,16 +517,16 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
   st.l = 0.0f;
   st.mt = -INFINITY;
 
-  // prologue: K0 -> LDS, QK(0); then K1, V0 -> LDS
+  // prologue: K0, K1, V0 -> LDS in one round trip; QK(0); a barrier before the loop's first
+  // prefetch overwrites K0
   issue_k<D, QK>(lk[0], a, bh, 0, lo, w, lane);
-  wait_vmem();
-  __syncthreads();
-  Score<D, QK> Sa, Sb;
-  qk_tile<D, QK>(Sa, lk[0], qf, qf4, qsc, lo);
   issue_k<D, QK>(lk[1], a, bh, min(1, ntiles - 1), lo, w, lane);
   issue_v<D, QK>(lv[0], a, bh, 0, lo, w, lane);
   if (QK == QK_MXFP4) store_ds<D, QK, PV>(load_ds(a, bh, 0), lv[0], a.sm_log2e);
   wait_vmem();
+  __syncthreads();
+  Score<D, QK> Sa, Sb;
+  qk_tile<D, QK>(Sa, lk[0], qf, qf4, qsc, lo);
   __syncthreads();
 
   // One tile: prefetch K(j+2) into lk[j&1] and V(j+1) into lv[(j+1)&1] (both already
@@ -591,33 +591,42 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
   }
 }
 
+// One 128-query tile per workgroup.  Causal tiles differ in length, so they are dealt longest
+// first: the dispatcher starts workgroups in id order as slots free up, which makes this a
+// longest-first greedy schedule (a slot that runs faster, e.g. the older of the two
+// workgroups sharing a CU, simply takes more of the short tiles at the end).  Each XCD takes
+// whole heads, so a head's K/V tiles stay in one L2.
 template <int D, int QK, bool CAUSAL, int DT, int PV>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   using G = Geo<D, QK, PV>;
   __shared__ __align__(16) uint8_t lk[2][G::KSTAGE];
   __shared__ __align__(16) uint8_t lv[2][G::VSTAGE];
   const int nqt = a.Np / kQT;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  int bh, qt;
   if (CAUSAL) {
-    // work item = (head, pair): heavy tile nqt-1-g then light tile g
-    const int npair = (nqt + 1) / 2;
-    const int bh = id / npair, g = id % npair;
-    const int heavy = nqt - 1 - g;
-    run_qtile<D, QK, CAUSAL, DT, PV>(a, bh, heavy, lk, lv);
-    if (g < heavy) {
-      __syncthreads();
-      run_qtile<D, QK, CAUSAL, DT, PV>(a, bh, g, lk, lv);
+    constexpr int X = 8;
+    const int hw = blockIdx.x;
+    if (a.BH % X == 0) {
+      const int hpx = a.BH / X, local = hw / X;
+      bh = (hw % X) * hpx + local % hpx;
+      qt = nqt - 1 - local / hpx;
+    } else {
+      bh = hw % a.BH;
+      qt = nqt - 1 - hw / a.BH;
     }
   } else {
-    run_qtile<D, QK, CAUSAL, DT, PV>(a, id / nqt, id % nqt, lk, lv);
+    const int id = xcd_remap(blockIdx.x, gridDim.x);
+    bh = id / nqt;
+    qt = id % nqt;
   }
+  run_qtile<D, QK, CAUSAL, DT, PV>(a, bh, qt, lk, lv);
 }
 
 template <int D, int QK, int DT, int PV>
 static hipError_t fwd_dispatch(const Shape& s, const FwdArgs& a, hipStream_t st) {
   const int nqt = s.Np / kQT;
   if (s.causal)
-    attn_fwd_kernel<D, QK, true, DT, PV><<<s.B * s.H * ((nqt + 1) / 2), 256, 0, st>>>(a);
+    attn_fwd_kernel<D, QK, true, DT, PV><<<s.B * s.H * nqt, 256, 0, st>>>(a);
   else
     attn_fwd_kernel<D, QK, false, DT, PV><<<s.B * s.H * nqt, 256, 0, st>>>(a);
   return hipGetLastError();
