@@ -106,12 +106,15 @@ def quant_int8_fp8(q, k, v, sm, blk=64):
     return r
 
 
+_PV = {"fp8": 2, "mxfp4": 3, "mxfp8": 4}
+
+
 def quant_mxfp4(q, k, v, sm, pv_fmt="mxfp4"):
     """Prologue of the MXFP4 path on [BH,N,d] float32 arrays (codes one per byte)."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     BH, N, d = q.shape
     ng, nvg = d // 32, (N + 31) // 32
-    pv = 3 if pv_fmt == "mxfp4" else 2
+    pv = _PV[pv_fmt]
     r = dict(mu_q=np.empty((BH, d), np.float32), mu_k=np.empty((BH, d), np.float32),
              qc=np.empty((BH, N, d), np.uint8), qe=np.empty((BH, N, ng), np.uint8),
              kc=np.empty((BH, N, d), np.uint8), ke=np.empty((BH, N, ng), np.uint8),
@@ -144,12 +147,12 @@ def attn_int8_fp8(qz, N, d, causal, sm, tile, rows=None, blk=64):
 
 
 def attn_mxfp4(qz, N, d, causal, sm, tile, rows=None):
-    """Tiled quantized forward (MXFP4 QK, MXFP4 or FP8 P~V) on a quant_mxfp4 result."""
+    """Tiled quantized forward (MXFP4 QK; P~V as MXFP4, FP8, or FP8 P~ with MXFP8 V)."""
     BH = qz["qc"].shape[0]
     rows = _rows(rows, N)
     out = np.empty((BH, len(rows), d), np.float64)
     lse = np.empty((BH, len(rows)), np.float64)
-    pv = 3 if qz["pv_fmt"] == "mxfp4" else 2
+    pv = _PV[qz["pv_fmt"]]
     lib().or_attn_mxfp4(_p(qz["qc"]), _p(qz["qe"]), _p(qz["kc"]), _p(qz["ke"]), _p(qz["dS"]), _p(qz["corr"]),
                         _p(qz["vc"]), _p(qz["ve"]), _p(qz["vs"]), pv, BH, N, d, tile, int(causal),
                         ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))

@@ -290,6 +290,7 @@ OR_API void or_quant_int8_fp8(const float *q, const float *k, const float *v,
  *   corr [BH,N] = sm * q_t . mu_k (fp64), added back to the LSE only.
  *   pv_fmt 3 (MXFP4): V codes [BH,N,d] E2M1 in 32-token groups per channel,
  *       E8M0 bytes ve [BH, ceil(N/32), d].
+ *   pv_fmt 4 (MXFP8): the same grouping with E4M3 elements (emax 8).
  *   pv_fmt 2 (FP8): V codes E4M3 with per-channel fp32 scale vs [BH,d].
  */
 OR_API void or_quant_mxfp4(const float *q, const float *k, const float *v,
@@ -329,12 +330,12 @@ OR_API void or_quant_mxfp4(const float *q, const float *k, const float *v,
             dS[(int64_t)h * N + t] = (float)s;
             corr[(int64_t)h * N + t] = sm * cq;
         }
-        if (pv_fmt == 3) {
+        if (pv_fmt == 3 || pv_fmt == 4) {
             for (int c = 0; c < d; c++)
                 for (int g = 0; g < nvg; g++) {
                     int t0 = 32 * g, n = N - t0 < 32 ? N - t0 : 32;
-                    quant_mx_group(V + (int64_t)t0 * d + c, n, d, 4, vc + off + (int64_t)t0 * d + c, d,
-                                   ve + ((int64_t)h * nvg + g) * d + c);
+                    quant_mx_group(V + (int64_t)t0 * d + c, n, d, pv_fmt == 3 ? 4 : 8,
+                                   vc + off + (int64_t)t0 * d + c, d, ve + ((int64_t)h * nvg + g) * d + c);
                 }
         } else {
             for (int c = 0; c < d; c++) {
@@ -357,7 +358,7 @@ OR_API void or_quant_mxfp4(const float *q, const float *k, const float *v,
 /* ------------------------------------------------------------------ */
 
 enum { QK_EXACT = 0, QK_INT8 = 1, QK_MXFP4 = 3 };
-enum { PV_EXACT = 0, PV_FP8 = 2, PV_MXFP4 = 3 };
+enum { PV_EXACT = 0, PV_FP8 = 2, PV_MXFP4 = 3, PV_MXFP8 = 4 };
 
 typedef struct {
     int N, d, causal, tile, blk;
@@ -374,9 +375,9 @@ typedef struct {
     const double *dSx;         /* same, fp64, exact mode */
     /* PV */
     const double *vx;          /* PV_EXACT */
-    const uint8_t *vc;         /* PV_FP8 codes or PV_MXFP4 codes */
+    const uint8_t *vc;         /* PV_FP8, PV_MXFP4 or PV_MXFP8 codes */
     const float *vs;           /* PV_FP8 per-channel scale */
-    const uint8_t *ve;         /* PV_MXFP4 E8M0 bytes [ceil(N/32), d] */
+    const uint8_t *ve;         /* PV_MXFP4 / PV_MXFP8 E8M0 bytes [ceil(N/32), d] */
     const double *corr;        /* per-row LSE correction (may be NULL) */
 } head_t;
 
@@ -418,7 +419,10 @@ static double vval(const head_t *H, int j, int c)
         return H->vx[idx];
     if (H->pv == PV_FP8)
         return or_e4m3_decode(H->vc[idx]);
-    return or_e2m1_decode(H->vc[idx]) * ldexp(1.0, (int)H->ve[(int64_t)(j / 32) * H->d + c] - 127);
+    double e = ldexp(1.0, (int)H->ve[(int64_t)(j / 32) * H->d + c] - 127);
+    if (H->pv == PV_MXFP8)
+        return or_e4m3_decode(H->vc[idx]) * e;
+    return or_e2m1_decode(H->vc[idx]) * e;
 }
 
 static void forward_row(const head_t *H, int i, double *o, double *lse)
@@ -459,7 +463,8 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
         if (H->pv == PV_EXACT) {
             for (int jj = 0; jj < n; jj++)
                 pq[jj] = p[jj];
-        } else if (H->pv == PV_FP8) {
+        } else if (H->pv == PV_FP8 || H->pv == PV_MXFP8) {
+            /* static x448 scale: p <= 1 fills the E4M3 range */
             for (int jj = 0; jj < n; jj++)
                 pq[jj] = or_e4m3_decode(or_e4m3_encode(448.0 * p[jj]));
         } else if (pmax == 0.0) {
@@ -499,6 +504,8 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
     for (int c = 0; c < d; c++) {
         if (H->pv == PV_FP8)
             o[c] = O[c] * (double)H->vs[c] / (448.0 * l);
+        else if (H->pv == PV_MXFP8)
+            o[c] = O[c] / (448.0 * l);
         else
             o[c] = O[c] / l;
     }
@@ -539,7 +546,8 @@ OR_API void or_attn_int8_fp8(const int8_t *qc, const float *qs, const int8_t *kc
     free(H);
 }
 
-/* Simulation of the MXFP4-QK forward; pv_fmt 3 = MXFP4 P~ and V, 2 = FP8 P~ and V. */
+/* Simulation of the MXFP4-QK forward; pv_fmt 3 = MXFP4 P~ and V, 2 = FP8 P~ and V,
+ * 4 = FP8 P~ with MXFP8 V. */
 OR_API void or_attn_mxfp4(const uint8_t *qc, const uint8_t *qe, const uint8_t *kc, const uint8_t *ke,
                           const float *dS, const double *corr,
                           const uint8_t *vc, const uint8_t *ve, const float *vs, int pv_fmt,
@@ -551,10 +559,10 @@ OR_API void or_attn_mxfp4(const uint8_t *qc, const uint8_t *qe, const uint8_t *k
     for (int h = 0; h < BH; h++) {
         int64_t off = (int64_t)h * N * d;
         H[h] = (head_t){.N = N, .d = d, .causal = causal, .tile = tile, .sm = sm,
-                        .qk = QK_MXFP4, .pv = pv_fmt == 3 ? PV_MXFP4 : PV_FP8,
+                        .qk = QK_MXFP4, .pv = pv_fmt == 3 ? PV_MXFP4 : pv_fmt == 4 ? PV_MXFP8 : PV_FP8,
                         .q4 = qc + off, .qe = qe + (int64_t)h * N * ng, .k4 = kc + off, .ke = ke + (int64_t)h * N * ng,
                         .dS = dS + (int64_t)h * N, .corr = corr + (int64_t)h * N, .vc = vc + off};
-        if (pv_fmt == 3)
+        if (pv_fmt == 3 || pv_fmt == 4)
             H[h].ve = ve + (int64_t)h * nvg * d;
         else
             H[h].vs = vs + (int64_t)h * d;

@@ -169,6 +169,26 @@ def _lossless_mx_v(rng, BH, N, d):
     return v.astype(np.float32)
 
 
+def _lossless_mx8_v(rng, BH, N, d):
+    """V on the E4M3 grid per 32-token group, each group's max magnitude in [256, 448] so the
+    E8M0 floor rule (emax 8) picks exactly the group's power of two."""
+    grid = _e4m3_grid()
+    v = rng.choice(grid, size=(BH, N, d)) * rng.choice([-1.0, 1.0], size=(BH, N, d))
+    for g0 in range(0, N, 32):
+        top = rng.choice([256.0, 288.0, 320.0, 384.0, 448.0], size=(BH, d))
+        v[:, g0, :] = top * rng.choice([-1.0, 1.0], size=(BH, d))
+        v[:, g0:g0 + 32, :] *= 2.0 ** rng.integers(-12, -4, size=(BH, 1, d))
+    return v.astype(np.float32)
+
+
+def _lossless_v(rng, BH, N, d, pv_fmt):
+    if pv_fmt == "mxfp4":
+        return _lossless_mx_v(rng, BH, N, d)
+    if pv_fmt == "mxfp8":
+        return _lossless_mx8_v(rng, BH, N, d)
+    return _lossless_fp8_v(rng, BH, N, d)
+
+
 def _int8_score_design(rng, BH, N, d, blk=64):
     """Q raw and K = Ks + mu with exact INT8 codes for Q and Ks (power-of-two block steps),
     Ks with zero channel means; the scores q.k are 0 or q_i2 in {1, 2}."""
@@ -252,12 +272,12 @@ def _mx_score_design(rng, BH, N, d):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("pv_fmt", ["mxfp4", "fp8"])
+@pytest.mark.parametrize("pv_fmt", ["mxfp4", "fp8", "mxfp8"])
 def test_mxfp4_sim_is_exact_on_lossless_grid(orc, causal, pv_fmt):
     rng = np.random.default_rng(31)
     BH, N, d = 2, 160, 64
     q, k = _mx_score_design(rng, BH, N, d)
-    v = _lossless_mx_v(rng, BH, N, d) if pv_fmt == "mxfp4" else _lossless_fp8_v(rng, BH, N, d)
+    v = _lossless_v(rng, BH, N, d, pv_fmt)
     sm = LN2
     qz = orc.quant_mxfp4(q, k, v, sm, pv_fmt=pv_fmt)
     assert np.array_equal(qz["mu_q"][:, 2], np.full(BH, 1.5, np.float32))
@@ -298,7 +318,7 @@ def test_mxfp4_scores_exact_on_random_lossless_codes(orc):
         assert np.allclose(lse, lse_ref, rtol=0, atol=1e-11)
 
 
-@pytest.mark.parametrize("path", ["int8_fp8", "mxfp4_mxfp4", "mxfp4_fp8"])
+@pytest.mark.parametrize("path", ["int8_fp8", "mxfp4_mxfp4", "mxfp4_fp8", "mxfp4_mxfp8"])
 def test_constant_keys_give_mean_of_values(orc, path):
     """K constant along tokens: smoothing zeroes it, every score is 0, p = 1, and O is
     the (prefix) mean of the dequantized V, exact on grid V."""
@@ -306,7 +326,7 @@ def test_constant_keys_give_mean_of_values(orc, path):
     BH, N, d = 2, 100, 64
     q = _rand((BH, N, d), 42)
     k = np.repeat(_rand((BH, 1, d), 43, 3.0), N, axis=1)
-    v = _lossless_mx_v(rng, BH, N, d) if path == "mxfp4_mxfp4" else _lossless_fp8_v(rng, BH, N, d)
+    v = _lossless_v(rng, BH, N, d, path.split("_")[1])
     for causal in (False, True):
         if path == "int8_fp8":
             qz = orc.quant_int8_fp8(q, k, v, 0.1)
@@ -371,7 +391,7 @@ def test_mxfp4_sim_accuracy_vs_exact(orc):
     # MXFP4 QK with FP8 P~V meets the 0.98 bar; with P~ and V also in MXFP4 the
     # single E2M1 mantissa bit on the probabilities costs about 1 % more (measured
     # 0.972 here), so that variant is held to a lower band.
-    for pv, bar in (("fp8", 0.98), ("mxfp4", 0.965)):
+    for pv, bar in (("fp8", 0.98), ("mxfp8", 0.98), ("mxfp4", 0.965)):
         qz = orc.quant_mxfp4(q, k, v, sm, pv_fmt=pv)
         o, _ = orc.attn_mxfp4(qz, 512, 128, False, sm, 64)
         assert _cos(o, o_ref) > bar, pv

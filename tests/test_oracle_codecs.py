@@ -131,3 +131,31 @@ def test_widen_matches_numpy_and_torch(orc):
     refb = torch.from_numpy(u.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
     okb = ~np.isnan(refb)
     assert np.array_equal(b[okb].view(np.uint32), refb[okb].view(np.uint32))
+
+
+def test_mx_e4m3_v_groups_against_frexp_and_torch(orc):
+    """MXFP8 V: per channel per 32-token group, E8M0 = floor(log2 amax) - 8 (from frexp) and
+    E4M3 codes of v * 2^-e, saturated at 448 (torch's float8_e4m3fn cast after clamping);
+    the last group is ragged."""
+    import torch
+    rng = np.random.default_rng(7)
+    BH, N, d = 2, 100, 64
+    v = (rng.standard_normal((BH, N, d)) * 2.0 ** rng.integers(-6, 6, size=(BH, 1, d))).astype(np.float32)
+    v[0, 40:64, 3] = 0.0
+    v[0, 32:40, 3] = 0.0                                       # one all-zero group
+    z = np.zeros_like(v)
+    r = orc.quant_mxfp4(z, z, v, 0.1, pv_fmt="mxfp8")
+    for h in range(BH):
+        for g0 in range(0, N, 32):
+            blk = v[h, g0:g0 + 32].astype(np.float64)            # [n, d]
+            for c in range(d):
+                a = np.abs(blk[:, c]).max()
+                if a == 0.0:
+                    assert r["ve"][h, g0 // 32, c] == 0
+                    assert not (r["vc"][h, g0:g0 + 32, c] & 0x7f).any()
+                    continue
+                e = math.frexp(a)[1] - 1 - 8
+                assert r["ve"][h, g0 // 32, c] == e + 127
+                y = np.clip(blk[:, c] * 2.0 ** -e, -448.0, 448.0)
+                want = torch.from_numpy(y.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+                assert np.array_equal(r["vc"][h, g0:g0 + 32, c], want)
