@@ -71,10 +71,10 @@ struct Geo {
   static constexpr int SBYTES = QK == QK_MXFP4 ? kTK * (D / 32) : 0;    // E8M0 bytes per tile
   static constexpr int DSBYTES = QK == QK_MXFP4 ? kTK * 4 : 0;          // scaled dS floats per tile
   static constexpr int KSTAGE = KBYTES + SBYTES;
-  // V^T tile: FP8 (64 bytes per channel) or MXFP4 (32 bytes per channel, then one E8M0 byte
-  // per channel for each of the two 32-key groups)
+  // V^T tile: FP8 / MXFP8 (64 bytes per channel) or MXFP4 (32 bytes per channel); the MX
+  // formats then carry one E8M0 byte per channel for each of the two 32-key groups
   static constexpr int VBYTES = PV == PV_MXFP4 ? D * kTK / 2 : D * kTK;
-  static constexpr int VSB = PV == PV_MXFP4 ? 2 * D : 0;
+  static constexpr int VSB = PV == PV_FP8 ? 0 : 2 * D;
   static constexpr int DSOFF = VBYTES + VSB;                            // scaled dS after V
   static constexpr int VSTAGE = DSOFF + DSBYTES;
   static constexpr int KCHUNKS = KBYTES / 16;                           // 16-byte chunks per K tile
@@ -85,8 +85,22 @@ struct Geo {
   static constexpr int NQF = QK == QK_INT8 ? D / 32 : D / 64;           // QK MFMAs per 32-key subtile
 };
 
-// Key row fed to A-row m of subtile s, so that output lane half h holds keys 32h + 16s + r.
-__device__ __forceinline__ int key_perm(int m, int s) { return 32 * ((m >> 2) & 1) + 16 * s + 4 * (m >> 3) + (m & 3); }
+// Which keys of a 64-key tile a lane's scores hold: lane half h, subtile s, register r holds
+// key KH h + KS s + r.  The default gives each half 32 consecutive keys.  MXFP8 V needs the
+// scaled FP8 MFMA's two 32-element K blocks (bytes [0, 16) and [16, 32) of both halves) to
+// be the tile's two 32-token scale groups, so there subtile s carries keys [32 s, 32 s + 32).
+template <int PV> struct KeyMap {
+  static constexpr int KH = PV == PV_MXFP8 ? 16 : 32;
+  static constexpr int KS = PV == PV_MXFP8 ? 32 : 16;
+  // key in-lane score i (= 16 s + r) of half h
+  static constexpr int lane_key(int i) { return (i / 16) * KS + (i % 16); }
+};
+// Key row fed to A-row m of subtile s: the output row of register r in half h is
+// 8 (r / 4) + 4 h + r % 4, so this puts key KH h + KS s + r there.
+template <int PV>
+__device__ __forceinline__ int key_perm(int m, int s) {
+  return KeyMap<PV>::KH * ((m >> 2) & 1) + KeyMap<PV>::KS * s + 4 * (m >> 3) + (m & 3);
+}
 
 // LDS swizzles: the 16-byte chunk c of row r is stored at chunk c ^ swz(r).  One ds_read_b128
 // serves 16 lanes per LDS cycle; with 64 banks of 4 bytes a chunk's bank group is fixed by
@@ -134,8 +148,9 @@ struct LaneOffs {
   uint32_t vld[VL];                 // direct-load source offsets inside a V^T tile
   uint32_t kop[2][G::NQF];          // LDS offsets of the K operand reads (subtile, chunk)
   uint32_t ksc[2][G::NQF];          // MXFP4: LDS offsets of the K scale bytes
-  uint32_t vop[G::NCB][2];          // LDS offsets of the V^T operand reads: FP8 (block, half);
-                                    // MXFP4 (block, {codes, scale byte})
+  uint32_t vop[G::NCB][2];          // LDS offsets of the V^T operand reads: FP8 / MXFP8 (block,
+                                    // 16-byte chunk); MXFP4 (block, {codes, scale byte})
+  uint32_t vsc;                     // MXFP8: LDS offset of block 0's E8M0 byte (+32 per block)
 
   __device__ __forceinline__ void init(int w, int lane, int n, int hh) {
 #pragma unroll
@@ -157,7 +172,7 @@ struct LaneOffs {
     }
 #pragma unroll
     for (int s = 0; s < 2; s++) {
-      const int row = key_perm(n, s);
+      const int row = key_perm<PV>(n, s);
 #pragma unroll
       for (int c = 0; c < G::NQF; c++) {
         const int col = 2 * c + hh;
@@ -171,11 +186,17 @@ struct LaneOffs {
       if (PV == PV_MXFP4) {
         vop[c][0] = row * 32 + ((hh ^ swz_v4(row)) << 4);
         vop[c][1] = G::VBYTES + hh * D + row;
+      } else if (PV == PV_MXFP8) {
+        // half hh: keys 16 hh + [0, 16) (block 0), then 32 + 16 hh + [0, 16) (block 1)
+        vop[c][0] = row * 64 + ((hh ^ swz_v(row)) << 4);
+        vop[c][1] = row * 64 + (((2 + hh) ^ swz_v(row)) << 4);
       } else {
         vop[c][0] = row * 64 + (((2 * hh) ^ swz_v(row)) << 4);
         vop[c][1] = row * 64 + (((2 * hh + 1) ^ swz_v(row)) << 4);
       }
     }
+    // the scale byte of (channel 32 c + n, key block hh), supplied by lane n + 32 hh
+    vsc = G::VBYTES + hh * D + n;
     // opaque to the optimizer: keep these in registers instead of recomputing them every tile
 #pragma unroll
     for (int i = 0; i < KL; i++) asm volatile("" : "+v"(kld[i]));
@@ -223,7 +244,7 @@ __device__ __forceinline__ void issue_v(uint8_t* lds, const FwdArgs& a, int bh, 
     const int pbase = NT * i + 64 * w;
     if (pbase < G::VCHUNKS) load_lds16(vg + lo.vld[i], lds + pbase * 16);
   }
-  if (PV == PV_MXFP4 && w == NT / 64 - 1 && lane < G::VSB / 16) {
+  if (PV != PV_FP8 && w == NT / 64 - 1 && lane < G::VSB / 16) {
     // E8M0 bytes of the tile's two 32-key groups: [group][channel], contiguous in the buffer
     const uint8_t* sg = reinterpret_cast<const uint8_t*>(a.v_scales) + ((size_t)bh * (a.Np / 32) + 2 * j) * D;
     load_lds16(sg + 16 * lane, lds + G::VBYTES + 16 * lane);
@@ -306,14 +327,15 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
     int im;
     if (need_mask) {
       asm volatile("" ::: "memory");   // a real branch: the rare masked tiles must not cost every tile
-      const int lim = (CAUSAL ? min(N, qrow + 1) : N) - (kbase + 32 * hh);   // keys i < lim are visible
+      // in-lane key offsets below lim are visible
+      const int lim = (CAUSAL ? min(N, qrow + 1) : N) - (kbase + KeyMap<PV>::KH * hh);
       im = INT_MIN;
 #pragma unroll
       for (int s = 0; s < 2; s++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int i = 16 * s + r;
-          const bool ok = i < lim;
+          const bool ok = KeyMap<PV>::lane_key(i) < lim;
           im = ok ? max(im, Sc.si[s][r]) : im;
           u[i] = ok ? (float)Sc.si[s][r] : -INFINITY;
         }
@@ -335,21 +357,21 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
     }
   } else {
     // dS arrives pre-multiplied by sm * log2 e; u = S * sm * log2 e + dS * sm * log2 e, c = 1
-    const float* dsl = reinterpret_cast<const float*>(vstage + G::DSOFF) + 32 * hh;
+    const float* dsl = reinterpret_cast<const float*>(vstage + G::DSOFF) + KeyMap<PV>::KH * hh;
 #pragma unroll
     for (int s = 0; s < 2; s++)
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
-        const v4f dv = *reinterpret_cast<const v4f*>(dsl + 16 * s + r);
+        const v4f dv = *reinterpret_cast<const v4f*>(dsl + KeyMap<PV>::KS * s + r);
 #pragma unroll
         for (int i = 0; i < 4; i++) u[16 * s + r + i] = fmaf(Sc.sf[s][r + i], sm_log2e, dv[i]);
       }
     c = 1.0f;
     if (need_mask) {
       asm volatile("" ::: "memory");
-      const int lim = (CAUSAL ? min(N, qrow + 1) : N) - (kbase + 32 * hh);
+      const int lim = (CAUSAL ? min(N, qrow + 1) : N) - (kbase + KeyMap<PV>::KH * hh);
 #pragma unroll
-      for (int i = 0; i < 32; i++) u[i] = i < lim ? u[i] : -INFINITY;
+      for (int i = 0; i < 32; i++) u[i] = KeyMap<PV>::lane_key(i) < lim ? u[i] : -INFINITY;
     }
     float mu = fmaxf(u[0], u[1]);
 #pragma unroll
@@ -358,7 +380,7 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
   }
   const float mnew = fmaxf(st.m, mt);
   const float mref = mnew == -INFINITY ? 0.0f : mnew;
-  if (PV == PV_FP8) {
+  if (PV != PV_MXFP4) {
     if (__any(mnew > st.m)) {
       const float alpha = fast_exp2(st.m - mref);
       st.l *= alpha;
@@ -407,7 +429,7 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
   constexpr int VSLOT = 112 / NQK;                         // vector instructions per MFMA slot
   if (IL) qk_tile<D, QK>(Sn, lk_next, qf, qf4, qsc, lo);
   float ps0 = 0.0f, ps1 = 0.0f;
-  if (PV == PV_FP8) {
+  if (PV != PV_MXFP4) {
     v8i pb;
 #pragma unroll
     for (int i = 0; i < 32; i += 4) {
@@ -424,7 +446,10 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
       const v4i v0 = *reinterpret_cast<const v4i*>(vstage + lo.vop[cb][0]);
       const v4i v1 = *reinterpret_cast<const v4i*>(vstage + lo.vop[cb][1]);
       const v8i va = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      st.O[cb] = mfma_f8(va, pb, st.O[cb]);
+      if (PV == PV_MXFP8)
+        st.O[cb] = mfma_f8_sa(va, pb, st.O[cb], vstage[lo.vsc + 32 * cb]);
+      else
+        st.O[cb] = mfma_f8(va, pb, st.O[cb]);
     }
   } else {
     float pf[32];
@@ -568,11 +593,12 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
   if (j < ntiles) step(j, Sa, Sb);
 
   // ---- epilogue: O / l (FP8: times the V channel step), LSE ----
-  //   FP8 P~: O and l both carry the factor 448.  MXFP4 P~: O' = sigma O with sigma = 6 exp2(m - mt)
-  //   and l' = 6 sum p, so O / l = O' exp2(mt - m) / l'.
+  //   FP8 P~ (V in FP8 or MXFP8): O and l both carry the factor 448; MXFP8's V block scales
+  //   are applied inside the MFMA.  MXFP4 P~: O' = sigma O with sigma = 6 exp2(m - mt) and
+  //   l' = 6 sum p, so O / l = O' exp2(mt - m) / l'.
   const float lt = half_sum(st.l);
   if (qrow < a.N) {
-    const float inv = PV == PV_FP8 ? 1.0f / lt : fast_exp2(st.mt - st.m) / lt;
+    const float inv = PV != PV_MXFP4 ? 1.0f / lt : fast_exp2(st.mt - st.m) / lt;
     uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + ((size_t)bh * a.N + qrow) * D;
 #pragma unroll
     for (int c = 0; c < NCB; c++)
@@ -587,7 +613,7 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
       }
     if (a.lse && hh == 0)
       a.lse[(size_t)bh * a.N + qrow] =
-          (st.m + __log2f(lt) - (PV == PV_FP8 ? kLog2_448 : kLog2_6)) * kLn2 + a.lse_corr[(size_t)bh * a.N + qrow];
+          (st.m + __log2f(lt) - (PV != PV_MXFP4 ? kLog2_448 : kLog2_6)) * kLn2 + a.lse_corr[(size_t)bh * a.N + qrow];
   }
 }
 
@@ -660,6 +686,9 @@ hipError_t launch_attn_fwd(const Shape& s, const QuantPtrs& qp, void* o, float* 
   if (s.pv_fmt == PV_MXFP4)
     return s.io_dtype == 0 ? fwd_dispatch_d<QK_MXFP4, 0, PV_MXFP4>(s, a, st)
                            : fwd_dispatch_d<QK_MXFP4, 1, PV_MXFP4>(s, a, st);
+  if (s.pv_fmt == PV_MXFP8)
+    return s.io_dtype == 0 ? fwd_dispatch_d<QK_MXFP4, 0, PV_MXFP8>(s, a, st)
+                           : fwd_dispatch_d<QK_MXFP4, 1, PV_MXFP8>(s, a, st);
   return s.io_dtype == 0 ? fwd_dispatch_d<QK_MXFP4, 0, PV_FP8>(s, a, st) : fwd_dispatch_d<QK_MXFP4, 1, PV_FP8>(s, a, st);
 }
 

@@ -240,7 +240,8 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
 }
 
 // MXFP4 Q_s and K_s codes (32-channel blocks), dS and LSE correction; V in FP8
-// (PV == PV_FP8) or MXFP4 (32-token blocks per channel).  grid (Np/64, BH), 256 threads.
+// (PV == PV_FP8), MXFP4 or MXFP8 (both in 32-token blocks per channel).  grid (Np/64, BH),
+// 256 threads.
 template <int DT, int D, int PV>
 __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, int N, int Np, int BH, float sm,
@@ -251,7 +252,8 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
   const size_t base = (size_t)bh * N * D;
   __shared__ float s_mk[D], s_mq[D];
   __shared__ __align__(16) uint8_t s_vt[PV == PV_FP8 ? D * 64 : 1];
-  __shared__ float s_vf[PV == PV_MXFP4 ? 64 : 1][PV == PV_MXFP4 ? D + 1 : 1];
+  constexpr bool MXV = PV == PV_MXFP4 || PV == PV_MXFP8;
+  __shared__ float s_vf[MXV ? 64 : 1][MXV ? D + 1 : 1];
   __shared__ float s_dv[PV == PV_FP8 ? D : 1];
   if (tid < D) {
     const float mk = chunk_mean(qp.sums, 0, BH, bh, D, tid, N);
@@ -354,15 +356,37 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
         x[i] = s_vf[32 * g + i][ch];
         a = max(a, __float_as_uint(fabsf(x[i])));
       }
-      const unsigned b = mx_fp4_scale_byte(__uint_as_float(a));
-      const float sc = b == 0 ? 1.0f : e8m0_to_float(b);
-      uint4 pk;
-      pk.x = pack_fp4x8(x, sc);
-      pk.y = pack_fp4x8(x + 8, sc);
-      pk.z = pack_fp4x8(x + 16, sc);
-      pk.w = pack_fp4x8(x + 24, sc);
-      *reinterpret_cast<uint4*>(qp.v_codes + (((size_t)bh * (Np / 64) + blk) * D + ch) * 32 + 16 * g) = pk;
-      reinterpret_cast<uint8_t*>(qp.v_scales)[((size_t)bh * (Np / 32) + 2 * blk + g) * D + ch] = (uint8_t)b;
+      if (PV == PV_MXFP4) {
+        const unsigned b = mx_fp4_scale_byte(__uint_as_float(a));
+        const float sc = b == 0 ? 1.0f : e8m0_to_float(b);
+        uint4 pk;
+        pk.x = pack_fp4x8(x, sc);
+        pk.y = pack_fp4x8(x + 8, sc);
+        pk.z = pack_fp4x8(x + 16, sc);
+        pk.w = pack_fp4x8(x + 24, sc);
+        *reinterpret_cast<uint4*>(qp.v_codes + (((size_t)bh * (Np / 64) + blk) * D + ch) * 32 + 16 * g) = pk;
+        reinterpret_cast<uint8_t*>(qp.v_scales)[((size_t)bh * (Np / 32) + 2 * blk + g) * D + ch] = (uint8_t)b;
+      } else {
+        // E4M3 elements: v * 2^-e is exact (b <= 246, so the factor 2^(127-b) is a normal
+        // float); the floor rule can put the block max up to 512, so saturate at 448 first
+        const unsigned b = mx_scale_byte<8>(__uint_as_float(a));
+        const float inv = __uint_as_float((254u - b) << 23);
+        float y[32];
+#pragma unroll
+        for (int i = 0; i < 32; i++) y[i] = fminf(fmaxf(x[i] * inv, -448.0f), 448.0f);
+        uint4 pk[2];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          pk[h].x = pack_fp8x4(y[16 * h], y[16 * h + 1], y[16 * h + 2], y[16 * h + 3]);
+          pk[h].y = pack_fp8x4(y[16 * h + 4], y[16 * h + 5], y[16 * h + 6], y[16 * h + 7]);
+          pk[h].z = pack_fp8x4(y[16 * h + 8], y[16 * h + 9], y[16 * h + 10], y[16 * h + 11]);
+          pk[h].w = pack_fp8x4(y[16 * h + 12], y[16 * h + 13], y[16 * h + 14], y[16 * h + 15]);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(qp.v_codes + (((size_t)bh * (Np / 64) + blk) * D + ch) * 64 + 32 * g);
+        dst[0] = pk[0];
+        dst[1] = pk[1];
+        reinterpret_cast<uint8_t*>(qp.v_scales)[((size_t)bh * (Np / 32) + 2 * blk + g) * D + ch] = (uint8_t)b;
+      }
     }
   }
 }
@@ -380,6 +404,9 @@ static hipError_t prologue_dispatch(const void* q, const void* k, const void* v,
   } else if (fp8v) {
     stats_kernel<DT, D, true, true><<<sg, 256, 0, st>>>(Q, K, V, s.N, BH, qp.sums, qp.amax_v);
     quant_mxfp4_kernel<DT, D, PV_FP8><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BH, s.sm_scale, qp);
+  } else if (s.pv_fmt == PV_MXFP8) {
+    stats_kernel<DT, D, true, false><<<sg, 256, 0, st>>>(Q, K, V, s.N, BH, qp.sums, qp.amax_v);
+    quant_mxfp4_kernel<DT, D, PV_MXFP8><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BH, s.sm_scale, qp);
   } else {
     stats_kernel<DT, D, true, false><<<sg, 256, 0, st>>>(Q, K, V, s.N, BH, qp.sums, qp.amax_v);
     quant_mxfp4_kernel<DT, D, PV_MXFP4><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BH, s.sm_scale, qp);

@@ -50,12 +50,13 @@ sage_status check_problem(const sage_problem* p) {
     return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   if (p->io_dtype != SAGE_DT_BF16 && p->io_dtype != SAGE_DT_F16)
     return fail(SAGE_ERR_INVALID_ARG, "io_dtype %d is not a SAGE_DT_* value", p->io_dtype);
-  const bool fmts_known = (p->qk_fmt == SAGE_FMT_INT8 || p->qk_fmt == SAGE_FMT_FP8 || p->qk_fmt == SAGE_FMT_MXFP4) &&
-                          (p->pv_fmt == SAGE_FMT_INT8 || p->pv_fmt == SAGE_FMT_FP8 || p->pv_fmt == SAGE_FMT_MXFP4);
+  auto known = [](int f) { return f >= SAGE_FMT_INT8 && f <= SAGE_FMT_MXFP8; };
+  const bool fmts_known = known(p->qk_fmt) && known(p->pv_fmt);
   if (!fmts_known) return fail(SAGE_ERR_INVALID_ARG, "qk_fmt/pv_fmt must be SAGE_FMT_* values");
   const bool pair_ok = (p->qk_fmt == SAGE_FMT_INT8 && p->pv_fmt == SAGE_FMT_FP8) ||
                        (p->qk_fmt == SAGE_FMT_MXFP4 && p->pv_fmt == SAGE_FMT_FP8) ||
-                       (p->qk_fmt == SAGE_FMT_MXFP4 && p->pv_fmt == SAGE_FMT_MXFP4);
+                       (p->qk_fmt == SAGE_FMT_MXFP4 && p->pv_fmt == SAGE_FMT_MXFP4) ||
+                       (p->qk_fmt == SAGE_FMT_MXFP4 && p->pv_fmt == SAGE_FMT_MXFP8);
   if (!pair_ok)
     return fail(SAGE_ERR_UNSUPPORTED, "format pair (qk=%d, pv=%d) is not supported", p->qk_fmt, p->pv_fmt);
   return SAGE_OK;
@@ -79,7 +80,7 @@ sage::Shape to_shape(const sage_problem* p) {
 void compute_layout(const sage_problem* p, sage_quant_layout* L) {
   const size_t BH = (size_t)p->B * p->H, d = p->d, N = p->N;
   const size_t Np = round_up(N, sage::kTokenPad), nb = Np / 64;
-  const bool mx = p->qk_fmt == SAGE_FMT_MXFP4, mxv = p->pv_fmt == SAGE_FMT_MXFP4;
+  const bool mx = p->qk_fmt == SAGE_FMT_MXFP4, mxv = p->pv_fmt == SAGE_FMT_MXFP4, mx8v = p->pv_fmt == SAGE_FMT_MXFP8;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -93,7 +94,7 @@ void compute_layout(const sage_problem* p, sage_quant_layout* L) {
   L->k_codes = take(mx ? BH * Np * d / 2 : BH * Np * d);
   L->k_scales = take(mx ? BH * Np * (d / 32) : BH * nb * 4);
   L->v_codes = take(mxv ? BH * Np * d / 2 : BH * Np * d);
-  L->v_scales = take(mxv ? BH * (Np / 32) * d : BH * d * 4);
+  L->v_scales = take(mxv || mx8v ? BH * (Np / 32) * d : BH * d * 4);
   L->delta_s = take(BH * Np * 4);
   L->lse_corr = take(BH * N * 4);
   L->stats = take(sage::kStatChunks * (BH * d * 8 * 2 + BH * d * 4));

@@ -38,6 +38,12 @@ __device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
 __device__ __forceinline__ v16f mfma_f8(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+// Scaled FP8 MFMA with E8M0 block scales on A only (B unscaled: byte 127 = 1.0).  The two
+// 32-element K blocks are bytes [0, 16) and [16, 32) of both lane halves; row m's scale for
+// block b comes from lane m + 32 b.
+__device__ __forceinline__ v16f mfma_f8_sa(v8i a, v8i b, v16f c, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, 127);
+}
 // Scaled MFMA, both operands MXFP4 (E2M1 with per-lane E8M0 scale byte).
 __device__ __forceinline__ v16f mfma_mxfp4(v8i a, v8i b, v16f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
@@ -93,14 +99,17 @@ __device__ __forceinline__ unsigned pack_fp4x8(const float* x, float scale) {
   return w;
 }
 
-// E8M0 byte of an MX block with element emax 2 (E2M1): floor(log2 amax) - 2 + 127,
-// clamped at 0; amax == 0 gives 0.  From the fp32 exponent field, so it is exact.
-__device__ __forceinline__ unsigned mx_fp4_scale_byte(float amax) {
+// E8M0 byte of an MX block whose element format has largest exponent EMAX (E2M1: 2, E4M3: 8):
+// floor(log2 amax) - EMAX + 127, clamped at 0; amax == 0 gives 0.  From the fp32 exponent
+// field, so it is exact.
+template <int EMAX>
+__device__ __forceinline__ unsigned mx_scale_byte(float amax) {
   int ef = (int)((__float_as_uint(amax) >> 23) & 0xff);
   if (ef == 0xff) return 0xff;
-  int b = ef - 2;
+  int b = ef - EMAX;
   return (unsigned)(b < 0 ? 0 : b);
 }
+__device__ __forceinline__ unsigned mx_fp4_scale_byte(float amax) { return mx_scale_byte<2>(amax); }
 __device__ __forceinline__ float e8m0_to_float(unsigned b) {
   return b == 0 ? 5.877471754111438e-39f : __uint_as_float(b << 23);   // 2^(b-127)
 }

@@ -7,7 +7,7 @@
 namespace sage {
 
 enum { QK_INT8 = 1, QK_MXFP4 = 3 };
-enum { PV_FP8 = 2, PV_MXFP4 = 3 };
+enum { PV_FP8 = 2, PV_MXFP4 = 3, PV_MXFP8 = 4 };
 
 // Padding of the token axis in every quantized buffer (a multiple of the Q tile).
 constexpr int kTokenPad = 128;
@@ -23,7 +23,7 @@ struct QuantPtrs {
   uint8_t* k_codes;
   void* k_scales;
   uint8_t* v_codes;
-  void* v_scales;     // fp32 [BH, d] (FP8) or uint8 E8M0 [BH, Np/32, d] (MXFP4)
+  void* v_scales;     // fp32 [BH, d] (FP8) or uint8 E8M0 [BH, Np/32, d] (MXFP4, MXFP8)
   float* delta_s;
   float* lse_corr;
   double* sums;       // [2, BH, d]: K then Q token sums

@@ -55,13 +55,17 @@ typedef enum {
 
 /* Element formats.  INT8: symmetric +-127 codes with one fp32 step per 64-token
  * block.  FP8: OCP E4M3FN.  MXFP4: OCP MX, E2M1 elements in 32-element blocks
- * sharing an E8M0 (power-of-two) scale. */
-enum { SAGE_FMT_INT8 = 1, SAGE_FMT_FP8 = 2, SAGE_FMT_MXFP4 = 3 };
+ * sharing an E8M0 (power-of-two) scale.  MXFP8: OCP MX with E4M3 elements
+ * (scale floor(log2 amax) - 8, elements saturated at 448); as pv_fmt it keeps
+ * P~ in FP8 with the static x448 scale (SageAttention3 abstract: microscaling
+ * FP4 attention, with 8-bit V as the higher-precision fallback). */
+enum { SAGE_FMT_INT8 = 1, SAGE_FMT_FP8 = 2, SAGE_FMT_MXFP4 = 3, SAGE_FMT_MXFP8 = 4 };
 
 /* I/O element types of Q, K, V, O, dO, dQ, dK, dV. */
 enum { SAGE_DT_BF16 = 0, SAGE_DT_F16 = 1 };
 
-/* Supported (qk_fmt, pv_fmt) pairs: (INT8, FP8), (MXFP4, FP8), (MXFP4, MXFP4). */
+/* Supported (qk_fmt, pv_fmt) pairs: (INT8, FP8), (MXFP4, FP8), (MXFP4, MXFP4),
+ * (MXFP4, MXFP8). */
 typedef struct {
     int B, H, N, d;
     int causal;          /* 0 or 1 */
@@ -81,10 +85,10 @@ typedef struct {
  *   q_scales  INT8: fp32 [BH, nb] step of each 64-token block;
  *             MXFP4: E8M0 bytes [BH, Np, d/32] per token per 32 channels
  *   k_codes, k_scales   the same for K - mu_k
- *   v_codes   FP8 V: E4M3 codes tiled [BH, Np/64, d, 64] (64 tokens of one
- *             channel contiguous);  MXFP4 V: packed E2M1 [BH, Np/64, d, 32]
- *   v_scales  FP8 V: fp32 [BH, d] per-channel step;  MXFP4 V: E8M0 bytes
- *             [BH, Np/32, d] per 32-token group per channel
+ *   v_codes   FP8 and MXFP8 V: E4M3 codes tiled [BH, Np/64, d, 64] (64 tokens
+ *             of one channel contiguous);  MXFP4 V: packed E2M1 [BH, Np/64, d, 32]
+ *   v_scales  FP8 V: fp32 [BH, d] per-channel step;  MXFP4 and MXFP8 V: E8M0
+ *             bytes [BH, Np/32, d] per 32-token group per channel
  *   delta_s   fp32 [BH, Np]    mu_q . (k_t - mu_k), added to every score (MXFP4 QK)
  *   lse_corr  fp32 [BH, N]     sm_scale * q_t . mu_k, added to the LSE only
  *   stats     fp64 / uint32 per-chunk partials of the smoothing statistics (scratch)

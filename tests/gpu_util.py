@@ -63,10 +63,15 @@ def unpack_mxfp4(buf, p, lay, pv_fmt):
     r["dS_all"] = part(b, lay, "delta_s", np.float32, BH * Np).reshape(BH, Np)
     r["dS"] = r["dS_all"][:, :N]
     r["corr"] = part(b, lay, "lse_corr", np.float32, BH * N).reshape(BH, N)
-    if pv_fmt == "fp8":
+    if pv_fmt in ("fp8", "mxfp8"):
         vt = part(b, lay, "v_codes", np.uint8, BH * Np * d).reshape(BH, Np // 64, d, 64)
-        r["vc"] = vt.transpose(0, 1, 3, 2).reshape(BH, Np, d)[:, :N]
-        r["vs"] = part(b, lay, "v_scales", np.float32, BH * d).reshape(BH, d)
+        r["vc_all"] = vt.transpose(0, 1, 3, 2).reshape(BH, Np, d)
+        r["vc"] = r["vc_all"][:, :N]
+        if pv_fmt == "fp8":
+            r["vs"] = part(b, lay, "v_scales", np.float32, BH * d).reshape(BH, d)
+        else:
+            ve = part(b, lay, "v_scales", np.uint8, BH * (Np // 32) * d).reshape(BH, Np // 32, d)
+            r["ve"] = ve[:, :(N + 31) // 32]
     else:
         vt = part(b, lay, "v_codes", np.uint8, BH * Np * d // 2).reshape(BH, Np // 64, d, 32)
         codes = unpack_nibbles(vt, 64)                       # [BH, Np/64, d, 64 tokens]

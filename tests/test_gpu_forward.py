@@ -1,9 +1,9 @@
 """GPU parity of the smoothing/quantization prologue and the fused forward
 against the CPU oracle: codes and scales bit-exact; O within max-abs 2e-2 and
 cosine >= 0.9999 of the oracle's simulation of the same quantization; cosine
-against exact fp64 attention >= 0.99 (INT8 QK), 0.98 (MXFP4 QK, FP8 P~V) or
-0.965 (MXFP4 QK and P~V: the oracle's own simulation reaches about 0.972 on
-these inputs)."""
+against exact fp64 attention >= 0.99 (INT8 QK), 0.98 (MXFP4 QK with FP8 P~ and
+FP8 or MXFP8 V) or 0.965 (MXFP4 QK and P~V: the oracle's own simulation reaches
+about 0.972 on these inputs)."""
 import math
 
 import numpy as np
@@ -46,6 +46,10 @@ CASES = [
     ("mxfp4_mxfp4_d128", 1, 3, 600, 128, "bf16", False, "mxfp4", "mxfp4", 3, 5.0, 0.0, 1 / math.sqrt(128)),
     ("mxfp4_mxfp4_causal_d64", 1, 2, 333, 64, "bf16", True, "mxfp4", "mxfp4", 6, 5.0, 0.0, 1 / 8),
     ("mxfp4_mxfp4_d64_f16", 1, 2, 200, 64, "f16", False, "mxfp4", "mxfp4", 8, 2.0, 0.0, 1 / 8),
+    ("mxfp4_mxfp8_d128", 1, 3, 600, 128, "bf16", False, "mxfp4", "mxfp8", 3, 5.0, 0.0, 1 / math.sqrt(128)),
+    ("mxfp4_mxfp8_causal_d64", 1, 2, 333, 64, "bf16", True, "mxfp4", "mxfp8", 6, 5.0, 0.0, 1 / 8),
+    ("mxfp4_mxfp8_causal_d128_f16", 1, 2, 700, 128, "f16", True, "mxfp4", "mxfp8", 10, 3.0, 0.01,
+     1 / math.sqrt(128)),
 ]
 
 
@@ -53,7 +57,7 @@ def _ref_band(qk, pv):
     """Cosine floor against exact fp64 attention for a format pair."""
     if qk == "int8":
         return 0.99
-    return 0.98 if pv == "fp8" else 0.965
+    return 0.965 if pv == "mxfp4" else 0.98
 
 
 def _oracle_sim(f, qz_or, qk, pv, N, d, causal, sm, rows=None):
@@ -79,6 +83,8 @@ def _check_codes(r, qz, qk, pv):
         assert np.array_equal(r["vc"], qz["vc"])
     else:
         assert np.array_equal(r["ve"], qz["ve"]) and np.array_equal(r["vc"], qz["vc"])
+    if pv == "mxfp8":
+        assert not r["vc_all"][:, qz["vc"].shape[1]:].any()      # padding tokens carry zero codes
     assert np.allclose(r["corr"], qz["corr"], rtol=1e-5, atol=1e-5 * (np.abs(qz["corr"]).max() + 1))
 
 
@@ -124,7 +130,8 @@ def test_forward_matches_oracle(sage, case):
 def test_forward_edge_lengths(sage, N, causal):
     import oracle
     banner(f"edge N={N} causal={causal}")
-    for qk, d, pv in (("int8", 64, "fp8"), ("int8", 128, "fp8"), ("mxfp4", 128, "fp8"), ("mxfp4", 64, "mxfp4")):
+    for qk, d, pv in (("int8", 64, "fp8"), ("int8", 128, "fp8"), ("mxfp4", 128, "fp8"), ("mxfp4", 64, "mxfp4"),
+                      ("mxfp4", 128, "mxfp8")):
         f, g = _inputs(1, 2, N, d, "bf16", 100 + N, 2.0)
         sm = 1 / math.sqrt(d)
         o, lse = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv,
@@ -165,30 +172,34 @@ def test_forward_constant_keys_closed_form(sage, qk, causal):
     assert np.all(np.abs(o - want) <= np.abs(want) * 2.0 ** -8 + 1e-6)
 
 
+@pytest.mark.parametrize("pv", ["mxfp4", "mxfp8"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_forward_constant_keys_mxfp4_pv(sage, causal):
-    """MXFP4 QK and P~V with K constant along tokens: every p is 1, so sigma = 6/max p = 6 and
-    each P~ element is exactly E2M1 6 with block scale 2^0; O_i is then the (prefix) mean of
-    the MXFP4-dequantized V rows, exact up to fp32 accumulation and the output rounding."""
+def test_forward_constant_keys_mx_pv(sage, causal, pv):
+    """MXFP4 QK with MX V and K constant along tokens: every p is 1.  MXFP4 P~: sigma = 6/max p
+    = 6 and each P~ element is exactly E2M1 6 with block scale 2^0.  MXFP8 V: each P~ element
+    is exactly E4M3 448.  O_i is then the (prefix) mean of the MX-dequantized V rows, exact up
+    to fp32 accumulation and the output rounding."""
     import oracle
-    banner(f"constant keys mxfp4 P~V causal={causal}")
+    banner(f"constant keys {pv} V causal={causal}")
     B, H, N, d = 1, 2, 200, 128
     f, g = _inputs(B, H, N, d, "bf16", 9)
     g["k"] = g["k"][:, :, :1].expand(-1, -1, N, -1).contiguous()
     f["k"] = np.repeat(f["k"][:, :1], N, axis=1)
-    o = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, qk_fmt="mxfp4", pv_fmt="mxfp4")
+    o = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, qk_fmt="mxfp4", pv_fmt=pv)
     torch.cuda.synchronize()
     o = to_np64(o).reshape(B * H, N, d)
-    qz = oracle.quant_mxfp4(f["q"], f["k"], f["v"], 0.1, pv_fmt="mxfp4")
+    qz = oracle.quant_mxfp4(f["q"], f["k"], f["v"], 0.1, pv_fmt=pv)
     ve = np.repeat(qz["ve"].astype(np.int64), 32, axis=1)[:, :N]            # [BH, N, d] E8M0 bytes
-    vdq = oracle.e2m1_decode(qz["vc"]) * np.ldexp(1.0, ve - 127)
+    dec = oracle.e2m1_decode if pv == "mxfp4" else oracle.e4m3_decode
+    vdq = dec(qz["vc"]) * np.ldexp(1.0, ve - 127)
     want = np.cumsum(vdq, axis=1) / np.arange(1, N + 1)[None, :, None] if causal else \
         np.broadcast_to(vdq.mean(axis=1, keepdims=True), vdq.shape)
     assert np.all(np.abs(o - want) <= np.abs(want) * 2.0 ** -8 + 1e-5 * np.abs(vdq).max())
 
 
 FULL = [("int8_fp8_causal_b1h32n4096d128", "fp8"), ("int8_fp8_b2h24n16384d64", "fp8"),
-        ("mxfp4_b4h32n8192d128", "fp8"), ("mxfp4_b4h32n8192d128", "mxfp4"), ("int8_fp8_b1h2n256d64", "fp8")]
+        ("mxfp4_b4h32n8192d128", "fp8"), ("mxfp4_b4h32n8192d128", "mxfp4"), ("mxfp4_b4h32n8192d128", "mxfp8"),
+        ("int8_fp8_b1h2n256d64", "fp8")]
 
 
 @pytest.mark.parametrize("name,pv", FULL, ids=[f"{n}-{p}" for n, p in FULL])
