@@ -92,17 +92,18 @@ def int8_encode(x, delta):
 
 
 def quant_int8_fp8(q, k, v, sm, blk=64):
-    """Prologue of the INT8/FP8 path on [BH,N,d] float32 arrays."""
+    """Prologue of the INT8/FP8 path: q [BH,Nq,d], k and v [BH,Nk,d] float32."""
     q, k, v = _f32(q), _f32(k), _f32(v)
-    BH, N, d = q.shape
-    nb = (N + blk - 1) // blk
-    r = dict(mu_k=np.empty((BH, d), np.float32), qc=np.empty((BH, N, d), np.int8),
-             qs=np.empty((BH, nb), np.float32), kc=np.empty((BH, N, d), np.int8),
-             ks=np.empty((BH, nb), np.float32), vc=np.empty((BH, N, d), np.uint8),
-             vs=np.empty((BH, d), np.float32), corr=np.empty((BH, N), np.float64))
-    lib().or_quant_int8_fp8(_p(q), _p(k), _p(v), BH, N, d, blk, ctypes.c_double(sm),
-                            _p(r["mu_k"]), _p(r["qc"]), _p(r["qs"]), _p(r["kc"]), _p(r["ks"]),
-                            _p(r["vc"]), _p(r["vs"]), _p(r["corr"]))
+    BH, Nq, d = q.shape
+    Nk = k.shape[1]
+    nbq, nbk = (Nq + blk - 1) // blk, (Nk + blk - 1) // blk
+    r = dict(mu_k=np.empty((BH, d), np.float32), qc=np.empty((BH, Nq, d), np.int8),
+             qs=np.empty((BH, nbq), np.float32), kc=np.empty((BH, Nk, d), np.int8),
+             ks=np.empty((BH, nbk), np.float32), vc=np.empty((BH, Nk, d), np.uint8),
+             vs=np.empty((BH, d), np.float32), corr=np.empty((BH, Nq), np.float64))
+    lib().or_quant_int8_fp8_x(_p(q), _p(k), _p(v), BH, Nq, Nk, d, blk, ctypes.c_double(sm),
+                              _p(r["mu_k"]), _p(r["qc"]), _p(r["qs"]), _p(r["kc"]), _p(r["ks"]),
+                              _p(r["vc"]), _p(r["vs"]), _p(r["corr"]))
     return r
 
 
@@ -110,18 +111,19 @@ _PV = {"fp8": 2, "mxfp4": 3, "mxfp8": 4}
 
 
 def quant_mxfp4(q, k, v, sm, pv_fmt="mxfp4"):
-    """Prologue of the MXFP4 path on [BH,N,d] float32 arrays (codes one per byte)."""
+    """Prologue of the MXFP4 path: q [BH,Nq,d], k and v [BH,Nk,d] float32 (codes one per byte)."""
     q, k, v = _f32(q), _f32(k), _f32(v)
-    BH, N, d = q.shape
-    ng, nvg = d // 32, (N + 31) // 32
+    BH, Nq, d = q.shape
+    Nk = k.shape[1]
+    ng, nvg = d // 32, (Nk + 31) // 32
     pv = _PV[pv_fmt]
     r = dict(mu_q=np.empty((BH, d), np.float32), mu_k=np.empty((BH, d), np.float32),
-             qc=np.empty((BH, N, d), np.uint8), qe=np.empty((BH, N, ng), np.uint8),
-             kc=np.empty((BH, N, d), np.uint8), ke=np.empty((BH, N, ng), np.uint8),
-             dS=np.empty((BH, N), np.float32), corr=np.empty((BH, N), np.float64),
-             vc=np.empty((BH, N, d), np.uint8), ve=np.zeros((BH, nvg, d), np.uint8),
+             qc=np.empty((BH, Nq, d), np.uint8), qe=np.empty((BH, Nq, ng), np.uint8),
+             kc=np.empty((BH, Nk, d), np.uint8), ke=np.empty((BH, Nk, ng), np.uint8),
+             dS=np.empty((BH, Nk), np.float32), corr=np.empty((BH, Nq), np.float64),
+             vc=np.empty((BH, Nk, d), np.uint8), ve=np.zeros((BH, nvg, d), np.uint8),
              vs=np.zeros((BH, d), np.float32))
-    lib().or_quant_mxfp4(_p(q), _p(k), _p(v), BH, N, d, pv, ctypes.c_double(sm),
+    lib().or_quant_mxfp4_x(_p(q), _p(k), _p(v), BH, Nq, Nk, d, pv, ctypes.c_double(sm),
                          _p(r["mu_q"]), _p(r["mu_k"]), _p(r["qc"]), _p(r["qe"]), _p(r["kc"]), _p(r["ke"]),
                          _p(r["dS"]), _p(r["corr"]), _p(r["vc"]), _p(r["ve"]), _p(r["vs"]))
     r["pv_fmt"] = pv_fmt
@@ -130,32 +132,34 @@ def quant_mxfp4(q, k, v, sm, pv_fmt="mxfp4"):
 
 def _rows(rows, N):
     rows = np.arange(N, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
-    assert rows.min() >= 0 and rows.max() < N
+    assert len(rows) == 0 or (rows.min() >= 0 and rows.max() < N)
     return rows
 
 
 def attn_int8_fp8(qz, N, d, causal, sm, tile, rows=None, blk=64):
-    """Tiled quantized forward (INT8 QK, FP8 P~V) on a quant_int8_fp8 result."""
-    BH = qz["qc"].shape[0]
+    """Tiled quantized forward (INT8 QK, FP8 P~V) on a quant_int8_fp8 result (N = query rows)."""
+    BH, Nq, Nk = qz["qc"].shape[0], qz["qc"].shape[1], qz["kc"].shape[1]
+    assert N == Nq
     rows = _rows(rows, N)
     out = np.empty((BH, len(rows), d), np.float64)
     lse = np.empty((BH, len(rows)), np.float64)
-    lib().or_attn_int8_fp8(_p(qz["qc"]), _p(qz["qs"]), _p(qz["kc"]), _p(qz["ks"]), _p(qz["vc"]),
-                           _p(qz["vs"]), _p(qz["corr"]), BH, N, d, blk, tile, int(causal),
-                           ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
+    lib().or_attn_int8_fp8_x(_p(qz["qc"]), _p(qz["qs"]), _p(qz["kc"]), _p(qz["ks"]), _p(qz["vc"]),
+                             _p(qz["vs"]), _p(qz["corr"]), BH, Nq, Nk, d, blk, tile, int(causal),
+                             ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
     return out, lse
 
 
 def attn_mxfp4(qz, N, d, causal, sm, tile, rows=None):
-    """Tiled quantized forward (MXFP4 QK; P~V as MXFP4, FP8, or FP8 P~ with MXFP8 V)."""
-    BH = qz["qc"].shape[0]
+    """Tiled quantized forward (MXFP4 QK; P~V as MXFP4, FP8, or FP8 P~ with MXFP8 V); N = query rows."""
+    BH, Nq, Nk = qz["qc"].shape[0], qz["qc"].shape[1], qz["kc"].shape[1]
+    assert N == Nq
     rows = _rows(rows, N)
     out = np.empty((BH, len(rows), d), np.float64)
     lse = np.empty((BH, len(rows)), np.float64)
     pv = _PV[qz["pv_fmt"]]
-    lib().or_attn_mxfp4(_p(qz["qc"]), _p(qz["qe"]), _p(qz["kc"]), _p(qz["ke"]), _p(qz["dS"]), _p(qz["corr"]),
-                        _p(qz["vc"]), _p(qz["ve"]), _p(qz["vs"]), pv, BH, N, d, tile, int(causal),
-                        ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
+    lib().or_attn_mxfp4_x(_p(qz["qc"]), _p(qz["qe"]), _p(qz["kc"]), _p(qz["ke"]), _p(qz["dS"]), _p(qz["corr"]),
+                          _p(qz["vc"]), _p(qz["ve"]), _p(qz["vs"]), pv, BH, Nq, Nk, d, tile, int(causal),
+                          ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
     return out, lse
 
 
@@ -172,14 +176,15 @@ def attn_tiled_exact(q, k, v, causal, sm, tile, smooth_q=False, rows=None):
 
 
 def attn_ref(q, k, v, causal, sm, rows=None):
-    """Exact fp64 two-pass attention and LSE for the listed rows."""
+    """Exact fp64 two-pass attention and LSE for the listed query rows (q [BH,Nq,d], k, v [BH,Nk,d])."""
     q, k, v = _f32(q), _f32(k), _f32(v)
-    BH, N, d = q.shape
-    rows = _rows(rows, N)
+    BH, Nq, d = q.shape
+    Nk = k.shape[1]
+    rows = _rows(rows, Nq)
     out = np.empty((BH, len(rows), d), np.float64)
     lse = np.empty((BH, len(rows)), np.float64)
-    lib().or_attn_ref(_p(q), _p(k), _p(v), BH, N, d, int(causal), ctypes.c_double(sm),
-                      _p(rows), len(rows), _p(out), _p(lse))
+    lib().or_attn_ref_x(_p(q), _p(k), _p(v), BH, Nq, Nk, d, int(causal), ctypes.c_double(sm),
+                        _p(rows), len(rows), _p(out), _p(lse))
     return out, lse
 
 
@@ -191,3 +196,45 @@ def attn_bwd_ref(q, k, v, do, causal, sm):
     lib().or_attn_bwd_ref(_p(q), _p(k), _p(v), _p(do), BH, N, d, int(causal), ctypes.c_double(sm),
                           _p(dq), _p(dk), _p(dv))
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------- packed sequences
+
+def _seq_heads(x, c0, c1, Hx, H):
+    """Rows [c0, c1) of a packed [total, Hx, d] array as [H, n, d]; with Hx < H each of the
+    Hx heads serves H / Hx consecutive query heads (grouped-query attention)."""
+    seg = np.ascontiguousarray(np.transpose(x[c0:c1], (1, 0, 2)))
+    return np.repeat(seg, H // Hx, axis=0) if Hx != H else seg
+
+
+def attn_varlen(q, k, v, cu_q, cu_k, causal, sm, qk_fmt="int8", pv_fmt="fp8", tile=64, exact=False):
+    """Packed sequences: q [total_q,H,d], k and v [total_k,Hkv,d], cu_q / cu_k [B+1].  Sequence b
+    is attention of q rows [cu_q[b], cu_q[b+1]) against k, v rows [cu_k[b], cu_k[b+1]), query head
+    h reading KV head h // (H / Hkv).  Returns o [total_q,H,d], lse [H,total_q] and the per-sequence
+    prologue results (None when exact: the exact fp64 reference)."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    total_q, H, d = q.shape
+    Hkv = k.shape[1]
+    assert H % Hkv == 0
+    o = np.zeros((total_q, H, d), np.float64)
+    lse = np.full((H, total_q), -np.inf)
+    quants = []
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if q1 == q0:
+            quants.append(None)
+            continue
+        qs, ks, vs = _seq_heads(q, q0, q1, H, H), _seq_heads(k, k0, k1, Hkv, H), _seq_heads(v, k0, k1, Hkv, H)
+        if exact:
+            ob, lb = attn_ref(qs, ks, vs, causal, sm)
+            qz = None
+        elif qk_fmt == "int8":
+            qz = quant_int8_fp8(qs, ks, vs, sm)
+            ob, lb = attn_int8_fp8(qz, q1 - q0, d, causal, sm, tile)
+        else:
+            qz = quant_mxfp4(qs, ks, vs, sm, pv_fmt=pv_fmt)
+            ob, lb = attn_mxfp4(qz, q1 - q0, d, causal, sm, tile)
+        o[q0:q1] = np.transpose(ob, (1, 0, 2))
+        lse[:, q0:q1] = lb
+        quants.append(qz)
+    return o, lse, quants

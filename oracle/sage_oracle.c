@@ -186,10 +186,15 @@ OR_API int8_t or_int8_encode(float x, float delta)
 /* Prologue: statistics and codes for one (b,h) head.                  */
 /* ------------------------------------------------------------------ */
 
-/* mu[c] = fl32( (sum_t x[t,c]) / N ), the sum in fp64 in token order. */
+/* mu[c] = fl32( (sum_t x[t,c]) / N ), the sum in fp64 in token order; an empty
+ * sequence (N = 0) has nothing to smooth and gets mu = 0. */
 static void channel_mean(const float *x, int N, int d, float *mu)
 {
     for (int c = 0; c < d; c++) {
+        if (N == 0) {
+            mu[c] = 0.0f;
+            continue;
+        }
         double s = 0.0;
         for (int t = 0; t < N; t++)
             s += (double)x[(int64_t)t * d + c];
@@ -239,60 +244,138 @@ static void quant_mx_group(const float *x, int n, int64_t stride, int elem_fmt,
 }
 
 /*
- * INT8-QK / FP8-PV prologue for BH heads of [N, d] fp32 inputs.
- *   mu_k [BH,d]; qc, kc [BH,N,d] int8; qs, ks [BH,nb] fp32 (nb = ceil(N/blk));
- *   vc [BH,N,d] E4M3 codes (token-major); vs [BH,d] fp32; corr [BH,N] fp64 =
- *   sm * q_i . mu_k (the per-row score shift removed by smoothing K).
+ * INT8-QK / FP8-PV prologue for BH heads: queries [BH,Nq,d], keys and values
+ * [BH,Nk,d] fp32 (Nq = Nk for self-attention).
+ *   mu_k [BH,d]; qc [BH,Nq,d], kc [BH,Nk,d] int8; qs [BH,nbq], ks [BH,nbk] fp32
+ *   (nb = ceil(N/blk)); vc [BH,Nk,d] E4M3 codes (token-major); vs [BH,d] fp32;
+ *   corr [BH,Nq] fp64 = sm * q_i . mu_k (the per-row score shift removed by
+ *   smoothing K).
  */
-OR_API void or_quant_int8_fp8(const float *q, const float *k, const float *v,
-                              int BH, int N, int d, int blk, double sm,
-                              float *mu_k, int8_t *qc, float *qs, int8_t *kc, float *ks,
-                              uint8_t *vc, float *vs, double *corr)
+OR_API void or_quant_int8_fp8_x(const float *q, const float *k, const float *v,
+                                int BH, int Nq, int Nk, int d, int blk, double sm,
+                                float *mu_k, int8_t *qc, float *qs, int8_t *kc, float *ks,
+                                uint8_t *vc, float *vs, double *corr)
 {
-    int nb = (N + blk - 1) / blk;
+    int nbq = (Nq + blk - 1) / blk, nbk = (Nk + blk - 1) / blk;
 #pragma omp parallel for schedule(dynamic)
     for (int h = 0; h < BH; h++) {
-        int64_t off = (int64_t)h * N * d;
-        const float *Q = q + off, *K = k + off, *V = v + off;
+        int64_t offq = (int64_t)h * Nq * d, offk = (int64_t)h * Nk * d;
+        const float *Q = q + offq, *K = k + offk, *V = v + offk;
         float *mu = mu_k + (int64_t)h * d;
-        channel_mean(K, N, d, mu);
-        float *Ks = malloc(sizeof(float) * (size_t)N * d);
-        for (int t = 0; t < N; t++)
+        channel_mean(K, Nk, d, mu);
+        float *Ks = malloc(sizeof(float) * ((size_t)Nk * d + 1));
+        for (int t = 0; t < Nk; t++)
             for (int c = 0; c < d; c++)
                 Ks[(int64_t)t * d + c] = K[(int64_t)t * d + c] - mu[c];
-        quant_int8_blocks(Q, N, d, blk, qc + off, qs + (int64_t)h * nb);
-        quant_int8_blocks(Ks, N, d, blk, kc + off, ks + (int64_t)h * nb);
+        quant_int8_blocks(Q, Nq, d, blk, qc + offq, qs + (int64_t)h * nbq);
+        quant_int8_blocks(Ks, Nk, d, blk, kc + offk, ks + (int64_t)h * nbk);
         for (int c = 0; c < d; c++) {
-            float a = absmax(V + c, N, d);
+            float a = absmax(V + c, Nk, d);
             float delta = a / 448.0f;
             vs[(int64_t)h * d + c] = delta;
-            for (int t = 0; t < N; t++) {
+            for (int t = 0; t < Nk; t++) {
                 float y = delta == 0.0f ? 0.0f : V[(int64_t)t * d + c] / delta;
-                vc[off + (int64_t)t * d + c] = or_e4m3_encode(y);
+                vc[offk + (int64_t)t * d + c] = or_e4m3_encode(y);
             }
         }
-        for (int t = 0; t < N; t++) {
+        for (int t = 0; t < Nq; t++) {
             double s = 0.0;
             for (int c = 0; c < d; c++)
                 s += (double)Q[(int64_t)t * d + c] * (double)mu[c];
-            corr[(int64_t)h * N + t] = sm * s;
+            corr[(int64_t)h * Nq + t] = sm * s;
         }
         free(Ks);
     }
 }
 
+OR_API void or_quant_int8_fp8(const float *q, const float *k, const float *v,
+                              int BH, int N, int d, int blk, double sm,
+                              float *mu_k, int8_t *qc, float *qs, int8_t *kc, float *ks,
+                              uint8_t *vc, float *vs, double *corr)
+{
+    or_quant_int8_fp8_x(q, k, v, BH, N, N, d, blk, sm, mu_k, qc, qs, kc, ks, vc, vs, corr);
+}
+
 /*
  * MXFP4-QK prologue.  Q and K are both smoothed by their channel means; the
  * smoothed rows are MX-quantized in 32-channel groups (E2M1 codes one per
- * byte, [BH,N,d]; E8M0 bytes [BH,N,d/32]).
- *   dS [BH,N] = fl32(sum_c mu_q[c] * Ks[t,c]) (fp64 sum in channel order):
+ * byte, [BH,Nq,d] and [BH,Nk,d]; E8M0 bytes [BH,Nq,d/32] and [BH,Nk,d/32]).
+ *   dS [BH,Nk] = fl32(sum_c mu_q[c] * Ks[t,c]) (fp64 sum in channel order):
  *       Q.Ks^T = Qs.Ks^T + 1 dS^T exactly, so dS is added back to every score.
- *   corr [BH,N] = sm * q_t . mu_k (fp64), added back to the LSE only.
- *   pv_fmt 3 (MXFP4): V codes [BH,N,d] E2M1 in 32-token groups per channel,
- *       E8M0 bytes ve [BH, ceil(N/32), d].
+ *   corr [BH,Nq] = sm * q_t . mu_k (fp64), added back to the LSE only.
+ *   pv_fmt 3 (MXFP4): V codes [BH,Nk,d] E2M1 in 32-token groups per channel,
+ *       E8M0 bytes ve [BH, ceil(Nk/32), d].
  *   pv_fmt 4 (MXFP8): the same grouping with E4M3 elements (emax 8).
  *   pv_fmt 2 (FP8): V codes E4M3 with per-channel fp32 scale vs [BH,d].
  */
+OR_API void or_quant_mxfp4_x(const float *q, const float *k, const float *v,
+                             int BH, int Nq, int Nk, int d, int pv_fmt, double sm,
+                             float *mu_q, float *mu_k,
+                             uint8_t *qc, uint8_t *qe, uint8_t *kc, uint8_t *ke,
+                             float *dS, double *corr,
+                             uint8_t *vc, uint8_t *ve, float *vs)
+{
+    int ng = d / 32, nvg = (Nk + 31) / 32;
+#pragma omp parallel for schedule(dynamic)
+    for (int h = 0; h < BH; h++) {
+        int64_t offq = (int64_t)h * Nq * d, offk = (int64_t)h * Nk * d;
+        const float *Q = q + offq, *K = k + offk, *V = v + offk;
+        float *muq = mu_q + (int64_t)h * d, *muk = mu_k + (int64_t)h * d;
+        channel_mean(Q, Nq, d, muq);
+        channel_mean(K, Nk, d, muk);
+        float *Qs = malloc(sizeof(float) * ((size_t)Nq * d + 1));
+        float *Ks = malloc(sizeof(float) * ((size_t)Nk * d + 1));
+        for (int t = 0; t < Nq; t++)
+            for (int c = 0; c < d; c++)
+                Qs[(int64_t)t * d + c] = Q[(int64_t)t * d + c] - muq[c];
+        for (int t = 0; t < Nk; t++)
+            for (int c = 0; c < d; c++)
+                Ks[(int64_t)t * d + c] = K[(int64_t)t * d + c] - muk[c];
+        for (int t = 0; t < Nq; t++)
+            for (int g = 0; g < ng; g++) {
+                int64_t e0 = (int64_t)t * d + 32 * g;
+                quant_mx_group(Qs + e0, 32, 1, 4, qc + offq + e0, 1, qe + ((int64_t)h * Nq + t) * ng + g);
+            }
+        for (int t = 0; t < Nk; t++)
+            for (int g = 0; g < ng; g++) {
+                int64_t e0 = (int64_t)t * d + 32 * g;
+                quant_mx_group(Ks + e0, 32, 1, 4, kc + offk + e0, 1, ke + ((int64_t)h * Nk + t) * ng + g);
+            }
+        for (int t = 0; t < Nk; t++) {
+            double s = 0.0;
+            for (int c = 0; c < d; c++)
+                s += (double)muq[c] * (double)Ks[(int64_t)t * d + c];
+            dS[(int64_t)h * Nk + t] = (float)s;
+        }
+        for (int t = 0; t < Nq; t++) {
+            double cq = 0.0;
+            for (int c = 0; c < d; c++)
+                cq += (double)Q[(int64_t)t * d + c] * (double)muk[c];
+            corr[(int64_t)h * Nq + t] = sm * cq;
+        }
+        if (pv_fmt == 3 || pv_fmt == 4) {
+            for (int c = 0; c < d; c++)
+                for (int g = 0; g < nvg; g++) {
+                    int t0 = 32 * g, n = Nk - t0 < 32 ? Nk - t0 : 32;
+                    quant_mx_group(V + (int64_t)t0 * d + c, n, d, pv_fmt == 3 ? 4 : 8,
+                                   vc + offk + (int64_t)t0 * d + c, d, ve + ((int64_t)h * nvg + g) * d + c);
+                }
+        } else {
+            for (int c = 0; c < d; c++) {
+                float a = absmax(V + c, Nk, d);
+                float delta = a / 448.0f;
+                vs[(int64_t)h * d + c] = delta;
+                for (int t = 0; t < Nk; t++) {
+                    float y = delta == 0.0f ? 0.0f : V[(int64_t)t * d + c] / delta;
+                    vc[offk + (int64_t)t * d + c] = or_e4m3_encode(y);
+                }
+            }
+        }
+        free(Qs);
+        free(Ks);
+    }
+}
+
 OR_API void or_quant_mxfp4(const float *q, const float *k, const float *v,
                            int BH, int N, int d, int pv_fmt, double sm,
                            float *mu_q, float *mu_k,
@@ -300,57 +383,7 @@ OR_API void or_quant_mxfp4(const float *q, const float *k, const float *v,
                            float *dS, double *corr,
                            uint8_t *vc, uint8_t *ve, float *vs)
 {
-    int ng = d / 32, nvg = (N + 31) / 32;
-#pragma omp parallel for schedule(dynamic)
-    for (int h = 0; h < BH; h++) {
-        int64_t off = (int64_t)h * N * d;
-        const float *Q = q + off, *K = k + off, *V = v + off;
-        float *muq = mu_q + (int64_t)h * d, *muk = mu_k + (int64_t)h * d;
-        channel_mean(Q, N, d, muq);
-        channel_mean(K, N, d, muk);
-        float *Qs = malloc(sizeof(float) * (size_t)N * d);
-        float *Ks = malloc(sizeof(float) * (size_t)N * d);
-        for (int t = 0; t < N; t++)
-            for (int c = 0; c < d; c++) {
-                Qs[(int64_t)t * d + c] = Q[(int64_t)t * d + c] - muq[c];
-                Ks[(int64_t)t * d + c] = K[(int64_t)t * d + c] - muk[c];
-            }
-        for (int t = 0; t < N; t++)
-            for (int g = 0; g < ng; g++) {
-                int64_t e0 = (int64_t)t * d + 32 * g;
-                quant_mx_group(Qs + e0, 32, 1, 4, qc + off + e0, 1, qe + ((int64_t)h * N + t) * ng + g);
-                quant_mx_group(Ks + e0, 32, 1, 4, kc + off + e0, 1, ke + ((int64_t)h * N + t) * ng + g);
-            }
-        for (int t = 0; t < N; t++) {
-            double s = 0.0, cq = 0.0;
-            for (int c = 0; c < d; c++) {
-                s += (double)muq[c] * (double)Ks[(int64_t)t * d + c];
-                cq += (double)Q[(int64_t)t * d + c] * (double)muk[c];
-            }
-            dS[(int64_t)h * N + t] = (float)s;
-            corr[(int64_t)h * N + t] = sm * cq;
-        }
-        if (pv_fmt == 3 || pv_fmt == 4) {
-            for (int c = 0; c < d; c++)
-                for (int g = 0; g < nvg; g++) {
-                    int t0 = 32 * g, n = N - t0 < 32 ? N - t0 : 32;
-                    quant_mx_group(V + (int64_t)t0 * d + c, n, d, pv_fmt == 3 ? 4 : 8,
-                                   vc + off + (int64_t)t0 * d + c, d, ve + ((int64_t)h * nvg + g) * d + c);
-                }
-        } else {
-            for (int c = 0; c < d; c++) {
-                float a = absmax(V + c, N, d);
-                float delta = a / 448.0f;
-                vs[(int64_t)h * d + c] = delta;
-                for (int t = 0; t < N; t++) {
-                    float y = delta == 0.0f ? 0.0f : V[(int64_t)t * d + c] / delta;
-                    vc[off + (int64_t)t * d + c] = or_e4m3_encode(y);
-                }
-            }
-        }
-        free(Qs);
-        free(Ks);
-    }
+    or_quant_mxfp4_x(q, k, v, BH, N, N, d, pv_fmt, sm, mu_q, mu_k, qc, qe, kc, ke, dS, corr, vc, ve, vs);
 }
 
 /* ------------------------------------------------------------------ */
@@ -361,7 +394,7 @@ enum { QK_EXACT = 0, QK_INT8 = 1, QK_MXFP4 = 3 };
 enum { PV_EXACT = 0, PV_FP8 = 2, PV_MXFP4 = 3, PV_MXFP8 = 4 };
 
 typedef struct {
-    int N, d, causal, tile, blk;
+    int N, d, causal, tile, blk;   /* N: keys (query rows are passed explicitly) */
     double sm;
     int qk, pv;
     /* QK_EXACT: fp64 (smoothed) rows and an optional additive key term */
@@ -501,6 +534,18 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
             O[c] = alpha * O[c] + acc[c] * post;
         m = mn;
     }
+    if (l == 0.0) {
+        /* no visible key (an empty key sequence): zero output, LSE -inf */
+        for (int c = 0; c < d; c++)
+            o[c] = 0.0;
+        *lse = -INFINITY;
+        free(O);
+        free(acc);
+        free(x);
+        free(p);
+        free(pq);
+        return;
+    }
     for (int c = 0; c < d; c++) {
         if (H->pv == PV_FP8)
             o[c] = O[c] * (double)H->vs[c] / (448.0 * l);
@@ -527,41 +572,50 @@ static void run_rows(const head_t *heads, int BH, const int *rows, int nrows, do
             forward_row(&heads[h], rows[r], out + ((int64_t)h * nrows + r) * d, lse + (int64_t)h * nrows + r);
 }
 
-/* Simulation of the INT8-QK / FP8-PV forward on codes from or_quant_int8_fp8. */
-OR_API void or_attn_int8_fp8(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks,
-                             const uint8_t *vc, const float *vs, const double *corr,
-                             int BH, int N, int d, int blk, int tile, int causal, double sm,
-                             const int *rows, int nrows, double *out, double *lse)
+/* Simulation of the INT8-QK / FP8-PV forward on codes from or_quant_int8_fp8_x
+ * (queries [BH,Nq], keys [BH,Nk]). */
+OR_API void or_attn_int8_fp8_x(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks,
+                               const uint8_t *vc, const float *vs, const double *corr,
+                               int BH, int Nq, int Nk, int d, int blk, int tile, int causal, double sm,
+                               const int *rows, int nrows, double *out, double *lse)
 {
-    int nb = (N + blk - 1) / blk;
+    int nbq = (Nq + blk - 1) / blk, nbk = (Nk + blk - 1) / blk;
     head_t *H = calloc((size_t)BH, sizeof(head_t));
     for (int h = 0; h < BH; h++) {
-        int64_t off = (int64_t)h * N * d;
-        H[h] = (head_t){.N = N, .d = d, .causal = causal, .tile = tile, .blk = blk, .sm = sm,
+        int64_t offq = (int64_t)h * Nq * d, offk = (int64_t)h * Nk * d;
+        H[h] = (head_t){.N = Nk, .d = d, .causal = causal, .tile = tile, .blk = blk, .sm = sm,
                         .qk = QK_INT8, .pv = PV_FP8,
-                        .qc = qc + off, .kc = kc + off, .qs = qs + (int64_t)h * nb, .ks = ks + (int64_t)h * nb,
-                        .vc = vc + off, .vs = vs + (int64_t)h * d, .corr = corr + (int64_t)h * N};
+                        .qc = qc + offq, .kc = kc + offk, .qs = qs + (int64_t)h * nbq, .ks = ks + (int64_t)h * nbk,
+                        .vc = vc + offk, .vs = vs + (int64_t)h * d, .corr = corr + (int64_t)h * Nq};
     }
     run_rows(H, BH, rows, nrows, out, lse);
     free(H);
 }
 
-/* Simulation of the MXFP4-QK forward; pv_fmt 3 = MXFP4 P~ and V, 2 = FP8 P~ and V,
- * 4 = FP8 P~ with MXFP8 V. */
-OR_API void or_attn_mxfp4(const uint8_t *qc, const uint8_t *qe, const uint8_t *kc, const uint8_t *ke,
-                          const float *dS, const double *corr,
-                          const uint8_t *vc, const uint8_t *ve, const float *vs, int pv_fmt,
-                          int BH, int N, int d, int tile, int causal, double sm,
-                          const int *rows, int nrows, double *out, double *lse)
+OR_API void or_attn_int8_fp8(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks,
+                             const uint8_t *vc, const float *vs, const double *corr,
+                             int BH, int N, int d, int blk, int tile, int causal, double sm,
+                             const int *rows, int nrows, double *out, double *lse)
 {
-    int ng = d / 32, nvg = (N + 31) / 32;
+    or_attn_int8_fp8_x(qc, qs, kc, ks, vc, vs, corr, BH, N, N, d, blk, tile, causal, sm, rows, nrows, out, lse);
+}
+
+/* Simulation of the MXFP4-QK forward; pv_fmt 3 = MXFP4 P~ and V, 2 = FP8 P~ and V,
+ * 4 = FP8 P~ with MXFP8 V.  Queries [BH,Nq], keys [BH,Nk]. */
+OR_API void or_attn_mxfp4_x(const uint8_t *qc, const uint8_t *qe, const uint8_t *kc, const uint8_t *ke,
+                            const float *dS, const double *corr,
+                            const uint8_t *vc, const uint8_t *ve, const float *vs, int pv_fmt,
+                            int BH, int Nq, int Nk, int d, int tile, int causal, double sm,
+                            const int *rows, int nrows, double *out, double *lse)
+{
+    int ng = d / 32, nvg = (Nk + 31) / 32;
     head_t *H = calloc((size_t)BH, sizeof(head_t));
     for (int h = 0; h < BH; h++) {
-        int64_t off = (int64_t)h * N * d;
-        H[h] = (head_t){.N = N, .d = d, .causal = causal, .tile = tile, .sm = sm,
+        int64_t offq = (int64_t)h * Nq * d, offk = (int64_t)h * Nk * d;
+        H[h] = (head_t){.N = Nk, .d = d, .causal = causal, .tile = tile, .sm = sm,
                         .qk = QK_MXFP4, .pv = pv_fmt == 3 ? PV_MXFP4 : pv_fmt == 4 ? PV_MXFP8 : PV_FP8,
-                        .q4 = qc + off, .qe = qe + (int64_t)h * N * ng, .k4 = kc + off, .ke = ke + (int64_t)h * N * ng,
-                        .dS = dS + (int64_t)h * N, .corr = corr + (int64_t)h * N, .vc = vc + off};
+                        .q4 = qc + offq, .qe = qe + (int64_t)h * Nq * ng, .k4 = kc + offk, .ke = ke + (int64_t)h * Nk * ng,
+                        .dS = dS + (int64_t)h * Nk, .corr = corr + (int64_t)h * Nq, .vc = vc + offk};
         if (pv_fmt == 3 || pv_fmt == 4)
             H[h].ve = ve + (int64_t)h * nvg * d;
         else
@@ -569,6 +623,16 @@ OR_API void or_attn_mxfp4(const uint8_t *qc, const uint8_t *qe, const uint8_t *k
     }
     run_rows(H, BH, rows, nrows, out, lse);
     free(H);
+}
+
+OR_API void or_attn_mxfp4(const uint8_t *qc, const uint8_t *qe, const uint8_t *kc, const uint8_t *ke,
+                          const float *dS, const double *corr,
+                          const uint8_t *vc, const uint8_t *ve, const float *vs, int pv_fmt,
+                          int BH, int N, int d, int tile, int causal, double sm,
+                          const int *rows, int nrows, double *out, double *lse)
+{
+    or_attn_mxfp4_x(qc, qe, kc, ke, dS, corr, vc, ve, vs, pv_fmt, BH, N, N, d, tile, causal, sm, rows, nrows,
+                    out, lse);
 }
 
 /*
@@ -634,10 +698,18 @@ OR_API void or_attn_tiled_exact(const float *q, const float *k, const float *v,
 /* Exact fp64 attention (two-pass softmax) and its backward.           */
 /* ------------------------------------------------------------------ */
 
+/* One query row against N keys; causal masking is top-left aligned (key j is
+ * visible to query i when j <= i).  No visible key: zero output, LSE -inf. */
 static void ref_row(const float *Q, const float *K, const float *V, int N, int d, int causal, double sm,
                     int i, double *x, double *o, double *lse)
 {
-    int n = causal ? i + 1 : N;
+    int n = causal && i + 1 < N ? i + 1 : N;
+    if (n == 0) {
+        for (int c = 0; c < d; c++)
+            o[c] = 0.0;
+        *lse = -INFINITY;
+        return;
+    }
     double mx = -INFINITY;
     for (int j = 0; j < n; j++) {
         double s = 0.0;
@@ -661,19 +733,26 @@ static void ref_row(const float *Q, const float *K, const float *V, int N, int d
     *lse = mx + log(l);
 }
 
-/* O = softmax(sm Q K^T + mask) V and LSE, exact in fp64, for the listed rows. */
-OR_API void or_attn_ref(const float *q, const float *k, const float *v, int BH, int N, int d,
-                        int causal, double sm, const int *rows, int nrows, double *out, double *lse)
+/* O = softmax(sm Q K^T + mask) V and LSE, exact in fp64, for the listed query
+ * rows; queries [BH,Nq,d], keys and values [BH,Nk,d]. */
+OR_API void or_attn_ref_x(const float *q, const float *k, const float *v, int BH, int Nq, int Nk, int d,
+                          int causal, double sm, const int *rows, int nrows, double *out, double *lse)
 {
 #pragma omp parallel for schedule(dynamic) collapse(2)
     for (int h = 0; h < BH; h++)
         for (int r = 0; r < nrows; r++) {
-            int64_t off = (int64_t)h * N * d;
-            double *x = malloc(sizeof(double) * (size_t)N);
-            ref_row(q + off, k + off, v + off, N, d, causal, sm, rows[r],
+            int64_t offq = (int64_t)h * Nq * d, offk = (int64_t)h * Nk * d;
+            double *x = malloc(sizeof(double) * ((size_t)Nk + 1));
+            ref_row(q + offq, k + offk, v + offk, Nk, d, causal, sm, rows[r],
                     x, out + ((int64_t)h * nrows + r) * d, lse + (int64_t)h * nrows + r);
             free(x);
         }
+}
+
+OR_API void or_attn_ref(const float *q, const float *k, const float *v, int BH, int N, int d,
+                        int causal, double sm, const int *rows, int nrows, double *out, double *lse)
+{
+    or_attn_ref_x(q, k, v, BH, N, N, d, causal, sm, rows, nrows, out, lse);
 }
 
 /*

@@ -474,3 +474,105 @@ def test_bwd_ref_invariants(orc, causal):
     assert np.allclose(dv.sum(axis=1), do.astype(np.float64).sum(axis=1), rtol=0, atol=1e-11)
     # rows of dS sum to zero: sum_j dK_j = 0
     assert np.abs(dk.sum(axis=1)).max() < 1e-11
+
+
+# ---------------------------------------------- unequal lengths, packed sequences, GQA
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(23, 57), (57, 23), (40, 40)])
+def test_ref_unequal_lengths_match_torch_sdpa_fp64(orc, causal, nq, nk):
+    """Query and key counts differ; torch's causal mask is the top-left-aligned lower triangle
+    of the Nq x Nk score matrix, the same reading as the oracle's."""
+    q, k, v = _rand((2, nq, 16), 4), _rand((2, nk, 16), 5, 3.0), _rand((2, nk, 16), 6)
+    sm = 0.3
+    o, lse = orc.attn_ref(q, k, v, causal, sm)
+    t = [torch.from_numpy(x).double() for x in (q, k, v)]
+    ot = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=causal, scale=sm).numpy()
+    s = (t[0] @ t[1].transpose(-1, -2)) * sm
+    if causal:
+        s = s.masked_fill(torch.ones(nq, nk, dtype=torch.bool).triu(1), float("-inf"))
+    assert np.allclose(o, ot, rtol=0, atol=1e-12)
+    assert np.allclose(lse, torch.logsumexp(s, -1).numpy(), rtol=0, atol=1e-12)
+
+
+def _packed(rng, lens_q, lens_k, H, Hkv, d):
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    q = rng.standard_normal((cu_q[-1], H, d)).astype(np.float32)
+    k = (rng.standard_normal((cu_k[-1], Hkv, d)) + rng.standard_normal((1, Hkv, d)) * 3).astype(np.float32)
+    v = rng.standard_normal((cu_k[-1], Hkv, d)).astype(np.float32)
+    return q, k, v, cu_q, cu_k
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_gqa_exact_matches_torch_sdpa_per_sequence(orc, causal):
+    """Packed sequences with grouped KV heads: each sequence equals torch's fp64 SDPA with
+    enable_gqa (query head h uses KV head h // (H / Hkv))."""
+    rng = np.random.default_rng(60)
+    H, Hkv, d = 6, 2, 16
+    lens_q, lens_k = [5, 70, 1, 33], [9, 70, 4, 20]
+    q, k, v, cu_q, cu_k = _packed(rng, lens_q, lens_k, H, Hkv, d)
+    sm = 0.25
+    o, lse, _ = orc.attn_varlen(q, k, v, cu_q, cu_k, causal, sm, exact=True)
+    for b in range(len(lens_q)):
+        sq, sk = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        t = [torch.from_numpy(np.ascontiguousarray(x[s].transpose(1, 0, 2))).double()
+             for x, s in ((q, sq), (k, sk), (v, sk))]
+        ot = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=causal, scale=sm, enable_gqa=True)
+        assert np.allclose(o[sq], ot.numpy().transpose(1, 0, 2), rtol=0, atol=1e-12)
+        kr = t[1].repeat_interleave(H // Hkv, 0)
+        s = (t[0] @ kr.transpose(-1, -2)) * sm
+        if causal:
+            s = s.masked_fill(torch.ones(lens_q[b], lens_k[b], dtype=torch.bool).triu(1), float("-inf"))
+        assert np.allclose(lse[:, sq], torch.logsumexp(s, -1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_varlen_empty_sequences(orc):
+    """An empty query sequence contributes nothing; a query sequence with no keys has no
+    visible key: zero output and LSE -inf (the softmax over an empty set, read as empty)."""
+    rng = np.random.default_rng(61)
+    q, k, v, cu_q, cu_k = _packed(rng, [3, 0, 4], [5, 6, 0], 2, 1, 32)
+    for exact in (True, False):
+        o, lse, _ = orc.attn_varlen(q, k, v, cu_q, cu_k, False, 0.2, exact=exact)
+        assert np.all(o[3:7] == 0.0) and np.all(np.isneginf(lse[:, 3:7]))
+        assert np.all(np.isfinite(lse[:, :3]))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_int8_fp8_sim_exact_on_lossless_grid_unequal_lengths(orc, causal):
+    """The lossless INT8/FP8 design with 96 queries against 160 keys: the simulation equals
+    exact attention, which pins the separate query and key extents of every prologue array."""
+    rng = np.random.default_rng(62)
+    BH, d = 2, 64
+    q, _ = _int8_score_design(rng, BH, 96, d)
+    _, k = _int8_score_design(rng, BH, 160, d)
+    v = _lossless_fp8_v(rng, BH, 160, d)
+    qz = orc.quant_int8_fp8(q, k, v, LN2)
+    o, lse = orc.attn_int8_fp8(qz, 96, d, causal, LN2, 64)
+    o_ref, lse_ref = orc.attn_ref(q, k, v, causal, LN2)
+    assert np.allclose(lse, lse_ref, rtol=0, atol=1e-12)
+    assert np.allclose(o, o_ref, rtol=1e-12, atol=1e-12 * np.abs(v).max())
+
+
+@pytest.mark.parametrize("pv_fmt", ["fp8", "mxfp4", "mxfp8"])
+def test_mxfp4_sim_exact_on_lossless_grid_unequal_lengths(orc, pv_fmt):
+    rng = np.random.default_rng(63)
+    BH, d = 2, 64
+    q, _ = _mx_score_design(rng, BH, 64, d)
+    _, k = _mx_score_design(rng, BH, 160, d)
+    v = _lossless_v(rng, BH, 160, d, pv_fmt)
+    qz = orc.quant_mxfp4(q, k, v, LN2, pv_fmt=pv_fmt)
+    for causal in (False, True):
+        o, lse = orc.attn_mxfp4(qz, 64, d, causal, LN2, 64)
+        o_ref, lse_ref = orc.attn_ref(q, k, v, causal, LN2)
+        assert np.allclose(lse, lse_ref, rtol=0, atol=1e-12)
+        assert np.allclose(o, o_ref, rtol=1e-12, atol=1e-12 * np.abs(v).max())
+
+
+def test_varlen_gqa_quantized_sim_accuracy(orc):
+    rng = np.random.default_rng(64)
+    q, k, v, cu_q, cu_k = _packed(rng, [100, 37, 200], [100, 37, 200], 4, 2, 64)
+    o_ref, _, _ = orc.attn_varlen(q, k, v, cu_q, cu_k, True, 0.125, exact=True)
+    for qk, pv, bar in (("int8", "fp8", 0.99), ("mxfp4", "fp8", 0.98), ("mxfp4", "mxfp8", 0.98)):
+        o, _, quants = orc.attn_varlen(q, k, v, cu_q, cu_k, True, 0.125, qk_fmt=qk, pv_fmt=pv)
+        assert _cos(o, o_ref) > bar, (qk, pv)
