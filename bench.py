@@ -212,6 +212,34 @@ def run_backward(name, S, torch, steps, warmup):
             "bwd_frac": round(ops_b / (ms_b * 1e-3) / 1e12 / PEAK["int8_fp8"], 4)}
 
 
+def run_varlen(name, S, torch, steps, warmup):
+    """Packed prefill step (prologue + fused kernel through sage_attn_varlen_fwd)."""
+    import ctypes
+    from bit_quantized_attention_smooth_amd.workloads import varlen_workload
+    x, w = varlen_workload(name)
+    dev = torch.device("cuda:0")
+    g = {n: x[n].to(dev) for n in ("q", "k", "v", "cu_q", "cu_k")}
+    T, H, Hkv, d = w["T"], w["H"], w["Hkv"], w["d"]
+    p = S.varlen_problem(w["B"], H, Hkv, d, T, T, w["max_seqlen"], w["max_seqlen"], causal=w["causal"],
+                         sm_scale=w["sm_scale"], dtype=g["q"].dtype)
+    L = S.lib()
+    n = ctypes.c_size_t()
+    S._check(L.sage_varlen_ws_size(ctypes.byref(p), ctypes.byref(n)))
+    ws = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    o = torch.empty_like(g["q"])
+    st = S._stream()
+
+    def step():
+        S._check(L.sage_attn_varlen_fwd(ctypes.byref(p), S._ptr(g["q"]), S._ptr(g["k"]), S._ptr(g["v"]),
+                                        S._ptr(g["cu_q"]), S._ptr(g["cu_k"]), S._ptr(o), None, S._ptr(ws), n.value,
+                                        st))
+
+    ms, _ = time_region(step, steps, warmup, torch)
+    ops = sum(attn_ops(1, H, n_b, d, w["causal"]) for n_b in w["lens"])
+    return {"step_ms": round(ms, 4), "step_tops": round(ops / (ms * 1e-3) / 1e12, 1),
+            "sequences": w["lens"], "heads": f"{H} query / {Hkv} KV"}
+
+
 def cpu_baseline(name):
     """The CPU oracle (prologue + tiled quantized forward) on a bounded sample of heads."""
     import numpy as np
@@ -292,6 +320,10 @@ def main():
                            "step_tops": round(e["step_tops"], 1), "kernel_ms": round(e["ms_kernel"], 4),
                            "prologue_GB/s": round(e["prologue_gbs"], 1)}
             torch.cuda.empty_cache()
+        log("[bench] secondary varlen_gqa_causal_b8h32kv8t16384d128 (packed sequences, grouped KV heads)")
+        extra["varlen_gqa_causal_b8h32kv8t16384d128"] = run_varlen("varlen_gqa_causal_b8h32kv8t16384d128", S, torch,
+                                                                   max(5, args.steps // 5), 3)
+        torch.cuda.empty_cache()
         log("[bench] secondary train_causal_b8h16n2048d64 (forward + 8-bit backward)")
         extra["train_causal_b8h16n2048d64"] = run_backward("train_causal_b8h16n2048d64", S, torch,
                                                            max(5, args.steps // 5), 3)

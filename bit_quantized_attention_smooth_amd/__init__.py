@@ -8,8 +8,9 @@ built, every entry point raises; there is no CPU fallback.
 
 Entry points follow the pages' names: ``sageattn`` (alias ``attn``) computes
 softmax(sm_scale Q K^T) V with INT8 or MXFP4 QK^T and FP8 P~V; ``quantize``
-and ``attn_fwd_quantized`` expose the two stages; ``attn_bwd`` and
-``SageAttnFn`` give the 8-bit backward.
+and ``attn_fwd_quantized`` expose the two stages; ``sageattn_varlen`` takes packed
+sequences (cu_seqlens) with grouped KV heads; ``attn_bwd`` and ``SageAttnFn`` give
+the 8-bit backward.
 """
 import ctypes
 import math
@@ -27,6 +28,7 @@ DT = {torch.bfloat16: 0, torch.float16: 1}
 # Every symbol the header declares (kept in sync by a CPU test that parses the header).
 EXPORTS = ["sage_attn_fwd", "sage_quant_size", "sage_quantize", "sage_attn_fwd_quantized",
            "sage_attn_fwd_ws_size", "sage_attn_fwd_ex", "sage_attn_bwd_ws_size", "sage_attn_bwd",
+           "sage_varlen_ws_size", "sage_attn_varlen_fwd",
            "sage_status_string", "sage_last_error", "sage_abi_version"]
 
 
@@ -40,6 +42,13 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int), ("d", ctypes.c_int),
                 ("causal", ctypes.c_int), ("sm_scale", ctypes.c_float), ("io_dtype", ctypes.c_int),
                 ("qk_fmt", ctypes.c_int), ("pv_fmt", ctypes.c_int)]
+
+
+class VarlenProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("H_kv", ctypes.c_int), ("d", ctypes.c_int),
+                ("causal", ctypes.c_int), ("sm_scale", ctypes.c_float), ("io_dtype", ctypes.c_int),
+                ("qk_fmt", ctypes.c_int), ("pv_fmt", ctypes.c_int), ("total_q", ctypes.c_int),
+                ("total_k", ctypes.c_int), ("max_seqlen_q", ctypes.c_int), ("max_seqlen_k", ctypes.c_int)]
 
 
 class QuantLayout(ctypes.Structure):
@@ -70,6 +79,8 @@ def lib():
             "sage_attn_fwd_ex": [P, vp, vp, vp, vp, vp, vp, sz, vp],
             "sage_attn_bwd_ws_size": [P, ctypes.POINTER(sz)],
             "sage_attn_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "sage_varlen_ws_size": [ctypes.POINTER(VarlenProblem), ctypes.POINTER(sz)],
+            "sage_attn_varlen_fwd": [ctypes.POINTER(VarlenProblem), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -155,6 +166,42 @@ def sageattn(q, k, v, *, causal=False, sm_scale=None, qk_fmt="int8", pv_fmt="fp8
 
 
 attn = sageattn
+
+
+def varlen_problem(B, H, H_kv, d, total_q, total_k, max_seqlen_q, max_seqlen_k, *, causal=False, sm_scale=None,
+                   dtype=torch.bfloat16, qk_fmt="int8", pv_fmt="fp8"):
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    return VarlenProblem(B, H, H_kv, d, int(bool(causal)), sm, DT[dtype], FMT[qk_fmt], FMT[pv_fmt],
+                         total_q, total_k, max_seqlen_q, max_seqlen_k)
+
+
+def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, causal=False,
+                    sm_scale=None, qk_fmt="int8", pv_fmt="fp8", return_lse=False):
+    """Packed sequences: q [total_q,H,d], k and v [total_k,H_kv,d] bf16/fp16 device tensors,
+    cu_seqlens_* int32 device tensors [B+1].  Returns O [total_q,H,d] (and LSE [H,total_q])."""
+    if not (q.is_cuda and k.is_cuda and v.is_cuda and cu_seqlens_q.is_cuda and cu_seqlens_k.is_cuda):
+        raise ValueError("q, k, v and the cu_seqlens must be device tensors")
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or q.shape[2] != k.shape[2]:
+        raise ValueError(f"expected q [total_q,H,d] and k, v [total_k,H_kv,d], got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if q.dtype not in DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be bfloat16 or all float16")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32 or \
+            cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q / cu_seqlens_k must be int32 tensors of the same length B+1 >= 2")
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    cu_q, cu_k = cu_seqlens_q.contiguous(), cu_seqlens_k.contiguous()
+    (total_q, H, d), (total_k, H_kv) = q.shape, k.shape[:2]
+    p = varlen_problem(cu_q.numel() - 1, H, H_kv, d, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k),
+                       causal=causal, sm_scale=sm_scale, dtype=q.dtype, qk_fmt=qk_fmt, pv_fmt=pv_fmt)
+    nbytes = ctypes.c_size_t()
+    _check(lib().sage_varlen_ws_size(ctypes.byref(p), ctypes.byref(nbytes)))
+    ws = torch.empty(max(nbytes.value, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib().sage_attn_varlen_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_q), _ptr(cu_k), _ptr(o),
+                                      _ptr(lse), _ptr(ws), ws.numel(), _stream()))
+    return (o, lse) if return_lse else o
 
 
 def attn_fwd_oneshot(q, k, v, *, causal=False, sm_scale=None, qk_fmt="int8", pv_fmt="fp8"):

@@ -53,7 +53,8 @@ struct FwdArgs {
   const float* lse_corr;
   void* o;
   float* lse;
-  int N, Np, BH;
+  SeqGeo g;
+  int nqt;            // query tiles per instance in the grid
   float sm_log2e;
 };
 
@@ -220,25 +221,25 @@ struct LaneOffs {
 // V^T codes (+ dS * sm * log2 e, staged through registers because it is rescaled on the
 // way), read one step later than K.
 template <int D, int QK, typename LO>
-__device__ __forceinline__ void issue_k(uint8_t* lds, const FwdArgs& a, int bh, int j, const LO& lo, int w, int lane) {
+__device__ __forceinline__ void issue_k(uint8_t* lds, const FwdArgs& a, size_t kt0, int j, const LO& lo, int w, int lane) {
   using G = Geo<D, QK>;
-  const uint8_t* kg = a.k_codes + ((size_t)bh * a.Np + (size_t)j * kTK) * G::KROW;
+  const uint8_t* kg = a.k_codes + (kt0 + (size_t)j * kTK) * G::KROW;
 #pragma unroll
   for (int i = 0; i < LO::KL; i++) {
     const int pbase = LO::NTHREADS * i + 64 * w;
     if (pbase < G::KCHUNKS) load_lds16(kg + lo.kld[i], lds + pbase * 16);
   }
   if (QK == QK_MXFP4 && w == 0 && lane < G::SBYTES / 16) {
-    const uint8_t* sg = reinterpret_cast<const uint8_t*>(a.k_scales) + ((size_t)bh * a.Np + (size_t)j * kTK) * (D / 32);
+    const uint8_t* sg = reinterpret_cast<const uint8_t*>(a.k_scales) + (kt0 + (size_t)j * kTK) * (D / 32);
     load_lds16(sg + lane * 16, lds + G::KBYTES);
   }
 }
 
 template <int D, int QK, int NT, int PV>
-__device__ __forceinline__ void issue_v(uint8_t* lds, const FwdArgs& a, int bh, int j,
+__device__ __forceinline__ void issue_v(uint8_t* lds, const FwdArgs& a, size_t kt0, int j,
                                         const LaneOffs<D, QK, NT, PV>& lo, int w, int lane) {
   using G = Geo<D, QK, PV>;
-  const uint8_t* vg = a.v_codes + ((size_t)bh * (a.Np / kTK) + j) * G::VBYTES;
+  const uint8_t* vg = a.v_codes + (kt0 / kTK + j) * G::VBYTES;
 #pragma unroll
   for (int i = 0; i < LaneOffs<D, QK, NT, PV>::VL; i++) {
     const int pbase = NT * i + 64 * w;
@@ -246,14 +247,14 @@ __device__ __forceinline__ void issue_v(uint8_t* lds, const FwdArgs& a, int bh, 
   }
   if (PV != PV_FP8 && w == NT / 64 - 1 && lane < G::VSB / 16) {
     // E8M0 bytes of the tile's two 32-key groups: [group][channel], contiguous in the buffer
-    const uint8_t* sg = reinterpret_cast<const uint8_t*>(a.v_scales) + ((size_t)bh * (a.Np / 32) + 2 * j) * D;
+    const uint8_t* sg = reinterpret_cast<const uint8_t*>(a.v_scales) + (kt0 / 32 + 2 * j) * D;
     load_lds16(sg + 16 * lane, lds + G::VBYTES + 16 * lane);
   }
 }
 
 // MXFP4 dS strip of one tile (64 floats): fetched into registers, stored scaled.
-__device__ __forceinline__ uint4 load_ds(const FwdArgs& a, int bh, int j) {
-  return reinterpret_cast<const uint4*>(a.delta_s + (size_t)bh * a.Np + (size_t)j * kTK)[threadIdx.x & 15];
+__device__ __forceinline__ uint4 load_ds(const FwdArgs& a, size_t ds0, int j) {
+  return reinterpret_cast<const uint4*>(a.delta_s + ds0 + (size_t)j * kTK)[threadIdx.x & 15];
 }
 template <int D, int QK, int PV>
 __device__ __forceinline__ void store_ds(uint4 r, uint8_t* lds, float c) {
@@ -495,11 +496,19 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
 }
 
 template <int D, int QK, bool CAUSAL, int DT, int PV>
-__device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint8_t (*lk)[Geo<D, QK, PV>::KSTAGE],
+__device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt, uint8_t (*lk)[Geo<D, QK, PV>::KSTAGE],
                                           uint8_t (*lv)[Geo<D, QK, PV>::VSTAGE]) {
   using G = Geo<D, QK, PV>;
   constexpr int NCB = G::NCB, NQF = G::NQF;
   const int qbase = qt * kQT;
+  // this query tile's instance, the KV instance its head reads, and its dS strip
+  const Inst qi = q_inst(a.g, b, h, D);
+  if (qbase >= qi.len) return;   // packed sequences: a tile past this sequence's end
+  const int hk = h / (a.g.H / a.g.Hkv);
+  const Inst ki = k_inst(a.g, b, hk, D);
+  const size_t kt0 = ki.tok0, kvid = (size_t)b * a.g.Hkv + hk;
+  const size_t ds0 = QK == QK_MXFP4 ? ds_base(a.g, b, h) : 0;
+  const int NK = ki.len;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int n = lane & 31, hh = lane >> 5;
@@ -514,13 +523,13 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
   int qsc[QK == QK_MXFP4 ? NQF : 1];
   float qstep = 0.0f;
   if (QK == QK_INT8) {
-    const uint8_t* qp = a.q_codes + ((size_t)bh * a.Np + qrow) * D + 16 * hh;
+    const uint8_t* qp = a.q_codes + (qi.tok0 + qrow) * D + 16 * hh;
 #pragma unroll
     for (int c = 0; c < NQF; c++) qf[c] = *reinterpret_cast<const v4i*>(qp + 32 * c);
-    qstep = reinterpret_cast<const float*>(a.q_scales)[(size_t)bh * (a.Np / kTK) + qrow / kTK] * a.sm_log2e;
+    qstep = reinterpret_cast<const float*>(a.q_scales)[qi.tok0 / kTK + qrow / kTK] * a.sm_log2e;
   } else {
-    const uint8_t* qp = a.q_codes + ((size_t)bh * a.Np + qrow) * (D / 2) + 16 * hh;
-    const uint8_t* qe = reinterpret_cast<const uint8_t*>(a.q_scales) + ((size_t)bh * a.Np + qrow) * (D / 32) + hh;
+    const uint8_t* qp = a.q_codes + (qi.tok0 + qrow) * (D / 2) + 16 * hh;
+    const uint8_t* qe = reinterpret_cast<const uint8_t*>(a.q_scales) + (qi.tok0 + qrow) * (D / 32) + hh;
 #pragma unroll
     for (int c = 0; c < NQF; c++) {
       const v4i lo = *reinterpret_cast<const v4i*>(qp + 32 * c);
@@ -528,9 +537,9 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
       qsc[c] = qe[2 * c];
     }
   }
-  const float* kstep = reinterpret_cast<const float*>(a.k_scales) + (size_t)bh * (a.Np / kTK);
+  const float* kstep = reinterpret_cast<const float*>(a.k_scales) + kt0 / kTK;
 
-  int ntiles = (a.N + kTK - 1) / kTK;
+  int ntiles = (NK + kTK - 1) / kTK;
   if (CAUSAL) ntiles = min(ntiles, (qbase + kQT - 1) / kTK + 1);
   // tiles holding keys this wave may see (causal: later tiles are fully masked for it)
   const int wtiles = CAUSAL ? min(ntiles, (qw + 31) / kTK + 1) : ntiles;
@@ -544,10 +553,22 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
 
   // prologue: K0, K1, V0 -> LDS in one round trip; QK(0); a barrier before the loop's first
   // prefetch overwrites K0
-  issue_k<D, QK>(lk[0], a, bh, 0, lo, w, lane);
-  issue_k<D, QK>(lk[1], a, bh, min(1, ntiles - 1), lo, w, lane);
-  issue_v<D, QK>(lv[0], a, bh, 0, lo, w, lane);
-  if (QK == QK_MXFP4) store_ds<D, QK, PV>(load_ds(a, bh, 0), lv[0], a.sm_log2e);
+  if (ntiles == 0) {
+    // no key in this sequence: a zero output and LSE -inf (the softmax over an empty set)
+    if (qrow < qi.len) {
+      uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + qi.io0 + (size_t)qrow * qi.ios;
+#pragma unroll
+      for (int c = 0; c < NCB; c++)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; g4++) *reinterpret_cast<uint2*>(orow + 32 * c + 8 * g4 + 4 * hh) = make_uint2(0, 0);
+      if (a.lse && hh == 0) a.lse[qi.lse0 + qrow] = -INFINITY;
+    }
+    return;
+  }
+  issue_k<D, QK>(lk[0], a, kt0, 0, lo, w, lane);
+  issue_k<D, QK>(lk[1], a, kt0, min(1, ntiles - 1), lo, w, lane);
+  issue_v<D, QK>(lv[0], a, kt0, 0, lo, w, lane);
+  if (QK == QK_MXFP4) store_ds<D, QK, PV>(load_ds(a, ds0, 0), lv[0], a.sm_log2e);
   wait_vmem();
   __syncthreads();
   Score<D, QK> Sa, Sb;
@@ -562,10 +583,10 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
   const int last = ntiles - 1;
   constexpr bool IL = !(D == 128 && QK == QK_INT8 && MFMA_IL_D128 == 0);
   auto step = [&](int j, const Score<D, QK>& Sc, Score<D, QK>& Sn) {
-    issue_k<D, QK>(lk[j & 1], a, bh, min(j + 2, last), lo, w, lane);
-    issue_v<D, QK>(lv[(j + 1) & 1], a, bh, min(j + 1, last), lo, w, lane);
+    issue_k<D, QK>(lk[j & 1], a, kt0, min(j + 2, last), lo, w, lane);
+    issue_v<D, QK>(lv[(j + 1) & 1], a, kt0, min(j + 1, last), lo, w, lane);
     uint4 dsr;
-    if (QK == QK_MXFP4) dsr = load_ds(a, bh, min(j + 1, last));
+    if (QK == QK_MXFP4) dsr = load_ds(a, ds0, min(j + 1, last));
     // tiles past this wave's last visible one need neither softmax nor the next scores.  With
     // IL the next tile's QK MFMAs are spread through the exp / pack stream (the last tile then
     // computes scores of an already-loaded tile that nothing reads); otherwise they are all
@@ -578,7 +599,7 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
     }
     if (j < wtiles) {
       float u[32], c, off, lsc;
-      softmax_max<D, QK, CAUSAL, PV>(st, Sc, lv[j & 1], kstep, qstep, a.sm_log2e, j, a.N, qw, qrow, hh, u, c, off, lsc);
+      softmax_max<D, QK, CAUSAL, PV>(st, Sc, lv[j & 1], kstep, qstep, a.sm_log2e, j, NK, qw, qrow, hh, u, c, off, lsc);
       softmax_body_pv<D, QK, PV, IL>(st, u, c, off, lsc, Sn, lk[(j + 1) & 1], lv[j & 1], qf, qf4, qsc, lo);
     }
     if (QK == QK_MXFP4) store_ds<D, QK, PV>(dsr, lv[(j + 1) & 1], a.sm_log2e);
@@ -597,23 +618,23 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int bh, int qt, uint
   //   are applied inside the MFMA.  MXFP4 P~: O' = sigma O with sigma = 6 exp2(m - mt) and
   //   l' = 6 sum p, so O / l = O' exp2(mt - m) / l'.
   const float lt = half_sum(st.l);
-  if (qrow < a.N) {
+  if (qrow < qi.len) {
     const float inv = PV != PV_MXFP4 ? 1.0f / lt : fast_exp2(st.mt - st.m) / lt;
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + ((size_t)bh * a.N + qrow) * D;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + qi.io0 + (size_t)qrow * qi.ios;
 #pragma unroll
     for (int c = 0; c < NCB; c++)
 #pragma unroll
       for (int g = 0; g < 4; g++) {
         const int ch = 32 * c + 8 * g + 4 * hh;
-        const v4f sc = PV == PV_FP8 ? *reinterpret_cast<const v4f*>(a.v_scales + (size_t)bh * D + ch) * inv
+        const v4f sc = PV == PV_FP8 ? *reinterpret_cast<const v4f*>(a.v_scales + kvid * D + ch) * inv
                                     : v4f{inv, inv, inv, inv};
         const uint32_t lo = pack2_io<DT>(st.O[c][4 * g] * sc[0], st.O[c][4 * g + 1] * sc[1]);
         const uint32_t hi = pack2_io<DT>(st.O[c][4 * g + 2] * sc[2], st.O[c][4 * g + 3] * sc[3]);
         *reinterpret_cast<uint2*>(orow + ch) = make_uint2(lo, hi);
       }
     if (a.lse && hh == 0)
-      a.lse[(size_t)bh * a.N + qrow] =
-          (st.m + __log2f(lt) - (PV != PV_MXFP4 ? kLog2_448 : kLog2_6)) * kLn2 + a.lse_corr[(size_t)bh * a.N + qrow];
+      a.lse[qi.lse0 + qrow] =
+          (st.m + __log2f(lt) - (PV != PV_MXFP4 ? kLog2_448 : kLog2_6)) * kLn2 + a.lse_corr[qi.row0 + qrow];
   }
 }
 
@@ -627,34 +648,34 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   using G = Geo<D, QK, PV>;
   __shared__ __align__(16) uint8_t lk[2][G::KSTAGE];
   __shared__ __align__(16) uint8_t lv[2][G::VSTAGE];
-  const int nqt = a.Np / kQT;
+  const int nqt = a.nqt, BH = a.g.B * a.g.H;
   int bh, qt;
   if (CAUSAL) {
     constexpr int X = 8;
     const int hw = blockIdx.x;
-    if (a.BH % X == 0) {
-      const int hpx = a.BH / X, local = hw / X;
+    if (BH % X == 0) {
+      const int hpx = BH / X, local = hw / X;
       bh = (hw % X) * hpx + local % hpx;
       qt = nqt - 1 - local / hpx;
     } else {
-      bh = hw % a.BH;
-      qt = nqt - 1 - hw / a.BH;
+      bh = hw % BH;
+      qt = nqt - 1 - hw / BH;
     }
   } else {
     const int id = xcd_remap(blockIdx.x, gridDim.x);
     bh = id / nqt;
     qt = id % nqt;
   }
-  run_qtile<D, QK, CAUSAL, DT, PV>(a, bh, qt, lk, lv);
+  run_qtile<D, QK, CAUSAL, DT, PV>(a, bh / a.g.H, bh % a.g.H, qt, lk, lv);
 }
 
 template <int D, int QK, int DT, int PV>
 static hipError_t fwd_dispatch(const Shape& s, const FwdArgs& a, hipStream_t st) {
-  const int nqt = s.Np / kQT;
+  const int grid = s.g.B * s.g.H * a.nqt;
   if (s.causal)
-    attn_fwd_kernel<D, QK, true, DT, PV><<<s.B * s.H * nqt, 256, 0, st>>>(a);
+    attn_fwd_kernel<D, QK, true, DT, PV><<<grid, 256, 0, st>>>(a);
   else
-    attn_fwd_kernel<D, QK, false, DT, PV><<<s.B * s.H * nqt, 256, 0, st>>>(a);
+    attn_fwd_kernel<D, QK, false, DT, PV><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -675,9 +696,8 @@ hipError_t launch_attn_fwd(const Shape& s, const QuantPtrs& qp, void* o, float* 
   a.lse_corr = qp.lse_corr;
   a.o = o;
   a.lse = lse;
-  a.N = s.N;
-  a.Np = s.Np;
-  a.BH = s.B * s.H;
+  a.g = s.g;
+  a.nqt = (s.g.nbq * 64) / kQT;   // tiles of 128 queries covering the longest query instance
   a.sm_log2e = s.sm_scale * kLog2e;
   if (s.qk_fmt == QK_INT8) {
     if (s.pv_fmt != PV_FP8) return hipErrorInvalidValue;

@@ -20,6 +20,8 @@
 // r = 1 / step correctly rounded once per block: for quotients in the normal range
 // this gives the correctly rounded x / step (Markstein's theorem), i.e. the same
 // value as one IEEE division, at a fraction of the cost.
+#include <type_traits>
+
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
 
@@ -34,7 +36,21 @@ __device__ __forceinline__ float div_rn(float x, float d, float r) {
   return copysignf(fmaf(r, fmaf(-d, q0, x), q0), x);
 }
 
-// 16 bytes = 8 contiguous 16-bit inputs.
+// 16 bytes = 8 contiguous 16-bit inputs, widened.
+template <int DT>
+__device__ __forceinline__ void unpack8(uint4 u, float* x) {
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    x[2 * i] = DT == 0 ? bf16_to_f32(w[i] & 0xffff) : f16_to_f32(w[i] & 0xffff);
+    x[2 * i + 1] = DT == 0 ? bf16_to_f32(w[i] >> 16) : f16_to_f32(w[i] >> 16);
+  }
+}
+// The raw 16 bytes of row `row` of an instance at channel c0, or zeros past its end.
+__device__ __forceinline__ uint4 row_raw(const uint16_t* x, const Inst& in, bool active, int row, int c0) {
+  return active && row < in.len ? *reinterpret_cast<const uint4*>(x + in.io0 + (size_t)row * in.ios + c0)
+                                : make_uint4(0, 0, 0, 0);
+}
 template <int DT>
 __device__ __forceinline__ void load8(const uint16_t* p, float* x) {
   uint4 u = *reinterpret_cast<const uint4*>(p);
@@ -46,72 +62,84 @@ __device__ __forceinline__ void load8(const uint16_t* p, float* x) {
   }
 }
 
-// grid (kChunks, BH), 256 threads.  Chunk c covers tokens [c*CH, (c+1)*CH) with
-// CH = ceil(N / kChunks).  Writes partial sums of K (and Q when SUMQ) and max |V| when
-// AMAXV into sums[c][BH][D] (K), sums[kChunks + c][BH][D] (Q), amax[c][BH][D].
-template <int DT, int D, bool SUMQ, bool AMAXV>
-__global__ __launch_bounds__(256) void stats_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                    const uint16_t* __restrict__ v, int N, int BH,
-                                                    double* __restrict__ sums, uint32_t* __restrict__ amax_v) {
+// Partial statistics of chunk c of one instance: tokens [c CH, (c+1) CH) with
+// CH = ceil(len / kChunks).  Per-channel fp64 sums of x into out_sum[D] and, when AMAXV,
+// max |v| bit patterns into out_amax[D].
+template <int DT, int D, bool AMAXV>
+__device__ __forceinline__ void chunk_stats(const uint16_t* __restrict__ x, const uint16_t* __restrict__ v,
+                                            const Inst& in, int c, double* out_sum, uint32_t* out_amax,
+                                            double (*s_x)[D], uint32_t (*s_v)[D]) {
   constexpr int C8 = D / 8, RP = 256 / C8;
-  const int bh = blockIdx.y, c = blockIdx.x;
-  const int CH = (N + kChunks - 1) / kChunks;
-  const int t0 = c * CH, t1 = min(N, t0 + CH);
+  const int CH = (in.len + kChunks - 1) / kChunks;
+  const int t0 = c * CH, t1 = min(in.len, t0 + CH);
   const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
-  const size_t base = (size_t)bh * N * D;
-  double sk[8] = {}, sq[8] = {};
+  double sx[8] = {};
   uint32_t av[8] = {};
   for (int r = t0 + r0; r < t1; r += RP) {
-    float x[8];
-    load8<DT>(k + base + (size_t)r * D + c0, x);
+    float y[8];
+    load8<DT>(x + in.io0 + (size_t)r * in.ios + c0, y);
 #pragma unroll
-    for (int i = 0; i < 8; i++) sk[i] += (double)x[i];
-    if (SUMQ) {
-      load8<DT>(q + base + (size_t)r * D + c0, x);
-#pragma unroll
-      for (int i = 0; i < 8; i++) sq[i] += (double)x[i];
-    }
+    for (int i = 0; i < 8; i++) sx[i] += (double)y[i];
     if (AMAXV) {
-      load8<DT>(v + base + (size_t)r * D + c0, x);
+      load8<DT>(v + in.io0 + (size_t)r * in.ios + c0, y);
 #pragma unroll
-      for (int i = 0; i < 8; i++) av[i] = max(av[i], __float_as_uint(fabsf(x[i])));  // NaN-propagating
+      for (int i = 0; i < 8; i++) av[i] = max(av[i], __float_as_uint(fabsf(y[i])));  // NaN-propagating
     }
   }
-  __shared__ double s_k[RP][D];
-  __shared__ double s_q[SUMQ ? RP : 1][D];
-  __shared__ uint32_t s_v[AMAXV ? RP : 1][D];
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    s_k[r0][c0 + i] = sk[i];
-    if (SUMQ) s_q[r0][c0 + i] = sq[i];
+    s_x[r0][c0 + i] = sx[i];
     if (AMAXV) s_v[r0][c0 + i] = av[i];
   }
   __syncthreads();
   if (tid < D) {
-    double a = 0.0, b = 0.0;
+    double a = 0.0;
     uint32_t m = 0;
     for (int r = 0; r < RP; r++) {
-      a += s_k[r][tid];
-      if (SUMQ) b += s_q[r][tid];
+      a += s_x[r][tid];
       if (AMAXV) m = max(m, s_v[r][tid]);
     }
-    sums[((size_t)c * BH + bh) * D + tid] = a;
-    if (SUMQ) sums[((size_t)(kChunks + c) * BH + bh) * D + tid] = b;
-    if (AMAXV) amax_v[((size_t)c * BH + bh) * D + tid] = m;
+    out_sum[tid] = a;
+    if (AMAXV) out_amax[tid] = m;
+  }
+  __syncthreads();   // s_x is reused by the next call
+}
+
+// grid (kChunks, B*H), 256 threads.  Block (c, i): chunk c of KV instance i (i < B*Hkv) --
+// sums of K into sums[c][i][D], max |V| (AMAXV) into amax[c][i][D] -- and, when SUMQ, of
+// query instance i: sums of Q into sums[kChunks + c][i][D].
+template <int DT, int D, bool SUMQ, bool AMAXV>
+__global__ __launch_bounds__(256) void stats_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                    const uint16_t* __restrict__ v, SeqGeo g,
+                                                    double* __restrict__ sums, uint32_t* __restrict__ amax_v) {
+  constexpr int RP = 256 / (D / 8);
+  const int i = blockIdx.y, c = blockIdx.x, BHm = g.B * g.H;
+  __shared__ double s_x[RP][D];
+  __shared__ uint32_t s_v[AMAXV ? RP : 1][D];
+  if (i < g.B * g.Hkv) {
+    const Inst ki = k_inst(g, i / g.Hkv, i % g.Hkv, D);
+    chunk_stats<DT, D, AMAXV>(k, v, ki, c, sums + ((size_t)c * BHm + i) * D, amax_v + ((size_t)c * BHm + i) * D,
+                              s_x, s_v);
+  }
+  if (SUMQ) {
+    const Inst qi = q_inst(g, i / g.H, i % g.H, D);
+    chunk_stats<DT, D, false>(q, nullptr, qi, c, sums + ((size_t)(kChunks + c) * BHm + i) * D, nullptr, s_x, s_v);
   }
 }
 
-// Reductions of the chunk partials for channel ch of head bh (fixed order).
-__device__ __forceinline__ float chunk_mean(const double* sums, int part, int BH, int bh, int D, int ch, int N) {
+// Reductions of the chunk partials for channel ch of instance inst (fixed order); an empty
+// instance has mean 0.
+__device__ __forceinline__ float chunk_mean(const double* sums, int part, int BHm, int inst, int D, int ch, int N) {
+  if (N == 0) return 0.0f;
   double s = 0.0;
 #pragma unroll
-  for (int c = 0; c < kChunks; c++) s += sums[((size_t)(part * kChunks + c) * BH + bh) * D + ch];
+  for (int c = 0; c < kChunks; c++) s += sums[((size_t)(part * kChunks + c) * BHm + inst) * D + ch];
   return (float)(s / (double)N);
 }
-__device__ __forceinline__ float chunk_amax(const uint32_t* amax, int BH, int bh, int D, int ch) {
+__device__ __forceinline__ float chunk_amax(const uint32_t* amax, int BHm, int inst, int D, int ch) {
   uint32_t m = 0;
 #pragma unroll
-  for (int c = 0; c < kChunks; c++) m = max(m, amax[((size_t)c * BH + bh) * D + ch]);
+  for (int c = 0; c < kChunks; c++) m = max(m, amax[((size_t)c * BHm + inst) * D + ch]);
   return __uint_as_float(m);
 }
 
@@ -150,6 +178,9 @@ __device__ __forceinline__ void put_v_fp8(uint8_t* s_vt, int rl, int c0, const f
     s_vt[(c0 + i + 1) * 64 + rl] = (uint8_t)((w >> 8) & 0xff);
   }
 }
+
+// Fixed-length problems without grouped heads (every instance N tokens, query head bh reads
+// KV instance bh): the streamlined codes kernels.
 
 // INT8 Q / K codes and FP8 V.  grid (Np/64, BH), 256 threads.
 template <int DT, int D>
@@ -391,26 +422,362 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
   }
 }
 
+// Instances one codes block serves: query instance i and, when i < B*Hkv, KV instance i;
+// each role is active while its 64-token block lies inside the instance rounded up to 128.
+struct CodeBlock {
+  Inst qi, ki, kq;   // query instance i, KV instance i, the KV instance query head i reads
+  int bq, hq;        // sequence and head of query instance i
+  int bk, hk;        // sequence and head of KV instance i
+  bool qa, ka;
+};
+template <int D>
+__device__ __forceinline__ CodeBlock code_block(const SeqGeo& g, int i, int t0) {
+  CodeBlock cb;
+  cb.bq = i / g.H;
+  cb.hq = i % g.H;
+  const bool has_kv = i < g.B * g.Hkv;
+  cb.bk = has_kv ? i / g.Hkv : 0;
+  cb.hk = has_kv ? i % g.Hkv : 0;
+  cb.qi = q_inst(g, cb.bq, cb.hq, D);
+  cb.ki = k_inst(g, cb.bk, cb.hk, D);
+  cb.kq = k_inst(g, cb.bq, cb.hq / (g.H / g.Hkv), D);
+  cb.qa = t0 < ((cb.qi.len + 127) & ~127);
+  cb.ka = has_kv && t0 < ((cb.ki.len + 127) & ~127);
+  return cb;
+}
+
+// Packed sequences or grouped KV heads: INT8 Q / K codes and FP8 V.  grid (blocks of the
+// longest instance, B*H), 256 threads.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v, SeqGeo g, float sm,
+                                                             QuantPtrs qp) {
+  constexpr int C8 = D / 8, RP = 256 / C8, NP = 64 / RP;
+  const int i = blockIdx.y, blk = blockIdx.x, t0 = blk * 64, BHm = g.B * g.H;
+  const CodeBlock cb = code_block<D>(g, i, t0);
+  if (!cb.qa && !cb.ka) return;
+  const int kvq = cb.bq * g.Hkv + cb.hq / (g.H / g.Hkv);
+  const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
+  __shared__ float s_mu[D], s_muq[D], s_dv[D];
+  __shared__ uint32_t s_red[8];
+  __shared__ __align__(16) uint8_t s_vt[D * 64];
+  // the KV instance query head i reads is usually instance i itself (no grouping)
+  const bool own_kv = kvq == i && cb.ka;
+  if (tid < D) {
+    if (cb.ka) {
+      const float mu = chunk_mean(qp.sums, 0, BHm, i, D, tid, cb.ki.len);
+      const float dvs = chunk_amax(qp.amax_v, BHm, i, D, tid) / 448.0f;
+      s_mu[tid] = mu;
+      s_dv[tid] = dvs;
+      if (blk == 0) {
+        qp.mu_k[(size_t)i * D + tid] = mu;
+        reinterpret_cast<float*>(qp.v_scales)[(size_t)i * D + tid] = dvs;
+      }
+    }
+    if (cb.qa && !own_kv) s_muq[tid] = chunk_mean(qp.sums, 0, BHm, kvq, D, tid, cb.kq.len);
+  }
+  __syncthreads();
+  const float* muq = own_kv ? s_mu : s_muq;
+  float dv[8], rv[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    dv[i] = cb.ka ? s_dv[c0 + i] : 0.0f;
+    rv[i] = 1.0f / dv[i];
+  }
+  float xq[NP][8], xk[NP][8];
+  uint32_t aq = 0, ak = 0;
+#pragma unroll
+  for (int p = 0; p < NP; p++) {
+    const int rl = r0 + p * RP, row = t0 + rl;
+    // the row's three loads go out together; rows past an instance's end load as zeros (no
+    // effect on the maxima or the LSE term)
+    const uint4 gq = row_raw(q, cb.qi, cb.qa, row, c0);
+    const uint4 gk = row_raw(k, cb.ki, cb.ka, row, c0);
+    const uint4 gv = row_raw(v, cb.ki, cb.ka, row, c0);
+    float cs = 0.0f;
+    unpack8<DT>(gq, xq[p]);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      aq = max(aq, __float_as_uint(fabsf(xq[p][i])));
+      cs += xq[p][i] * muq[c0 + i];
+    }
+    if (cb.ka && row < cb.ki.len) {
+      float xv[8];
+      unpack8<DT>(gk, xk[p]);
+      unpack8<DT>(gv, xv);
+      put_v_fp8(s_vt, rl, c0, xv, dv, rv);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        xk[p][i] = xk[p][i] - s_mu[c0 + i];
+        ak = max(ak, __float_as_uint(fabsf(xk[p][i])));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        xk[p][i] = 0.0f;
+        s_vt[(c0 + i) * 64 + rl] = 0;
+      }
+    }
+    // LSE correction: sm * q_t . mu_k (reduced over the C8 threads of this row)
+#pragma unroll
+    for (int o = 1; o < C8; o <<= 1) cs += __shfl_xor(cs, o);
+    if ((tid % C8) == 0 && cb.qa && row < cb.qi.len) qp.lse_corr[cb.qi.row0 + row] = sm * cs;
+  }
+  block_umax2(aq, ak, s_red);
+  const float dq = __uint_as_float(aq) / 127.0f, dk = __uint_as_float(ak) / 127.0f;
+  const float rq = 1.0f / dq, rk = 1.0f / dk;
+  if (tid == 0) {
+    if (cb.qa) reinterpret_cast<float*>(qp.q_scales)[cb.qi.tok0 / 64 + blk] = dq;
+    if (cb.ka) reinterpret_cast<float*>(qp.k_scales)[cb.ki.tok0 / 64 + blk] = dk;
+  }
+#pragma unroll
+  for (int p = 0; p < NP; p++) {
+    const int row = t0 + r0 + p * RP;
+    uint32_t wq[2] = {0, 0}, wk[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      wq[i / 4] |= (uint32_t)(uint8_t)int8_code(xq[p][i], dq, rq) << (8 * (i % 4));
+      wk[i / 4] |= (uint32_t)(uint8_t)int8_code(xk[p][i], dk, rk) << (8 * (i % 4));
+    }
+    if (cb.qa) *reinterpret_cast<uint2*>(qp.q_codes + (cb.qi.tok0 + row) * D + c0) = make_uint2(wq[0], wq[1]);
+    if (cb.ka) *reinterpret_cast<uint2*>(qp.k_codes + (cb.ki.tok0 + row) * D + c0) = make_uint2(wk[0], wk[1]);
+  }
+  if (cb.ka) {
+    __syncthreads();
+    // V tile [D][64] -> the instance's tile blk of v_codes [..][D][64], coalesced 16-byte stores
+    uint8_t* dst = qp.v_codes + (cb.ki.tok0 / 64 + blk) * D * 64;
+    for (int c = tid; c < D * 4; c += 256)
+      *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(s_vt + c * 16);
+  }
+}
+
+// Packed sequences or grouped KV heads: MXFP4 Q_s and K_s codes (32-channel blocks), dS and
+// LSE correction; V in FP8 (PV == PV_FP8), MXFP4 or MXFP8 (both in 32-token blocks per
+// channel).  grid (blocks of the longest instance, B*H), 256 threads.  dS = mu_q . K_s is written for each query head that
+// reads KV instance i (one without grouped heads, in the row loop; H / Hkv of them after it).
+template <int DT, int D, int PV>
+__global__ __launch_bounds__(256) void quant_mxfp4_seq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v, SeqGeo g, float sm,
+                                                          QuantPtrs qp) {
+  constexpr int C8 = D / 8, RP = 256 / C8, NP = 64 / RP;
+  constexpr bool MXV = PV == PV_MXFP4 || PV == PV_MXFP8;
+  const int i = blockIdx.y, blk = blockIdx.x, t0 = blk * 64, BHm = g.B * g.H;
+  const CodeBlock cb = code_block<D>(g, i, t0);
+  if (!cb.qa && !cb.ka) return;
+  const int grp = g.H / g.Hkv;
+  const int kvq = cb.bq * g.Hkv + cb.hq / grp;
+  const bool own_kv = kvq == i && cb.ka;   // query head i reads KV instance i (no grouping)
+  const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
+  __shared__ float s_mk[D], s_mkq[D], s_mq[D];
+  __shared__ __align__(16) uint8_t s_vt[PV == PV_FP8 ? D * 64 : 1];
+  __shared__ float s_vf[MXV ? 64 : 1][MXV ? D + 1 : 1];
+  __shared__ float s_dv[PV == PV_FP8 ? D : 1];
+  if (tid < D) {
+    if (cb.ka) {
+      const float mk = chunk_mean(qp.sums, 0, BHm, i, D, tid, cb.ki.len);
+      s_mk[tid] = mk;
+      if (PV == PV_FP8) s_dv[tid] = chunk_amax(qp.amax_v, BHm, i, D, tid) / 448.0f;
+      if (blk == 0) {
+        qp.mu_k[(size_t)i * D + tid] = mk;
+        if (PV == PV_FP8) reinterpret_cast<float*>(qp.v_scales)[(size_t)i * D + tid] = s_dv[tid];
+      }
+    }
+    // mu_q of query instance i: its own smoothing, and (grp == 1) the dS of KV instance i,
+    // which that query head reads -- needed whenever either role is active
+    const float mq = chunk_mean(qp.sums, 1, BHm, i, D, tid, cb.qi.len);
+    s_mq[tid] = mq;
+    if (cb.qa) {
+      if (!own_kv) s_mkq[tid] = chunk_mean(qp.sums, 0, BHm, kvq, D, tid, cb.kq.len);
+      if (blk == 0) qp.mu_q[(size_t)i * D + tid] = mq;
+    }
+  }
+  __syncthreads();
+  const float* mkq = own_kv ? s_mk : s_mkq;
+  float dv[8], rv[8];
+  if (PV == PV_FP8) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      dv[i] = cb.ka ? s_dv[c0 + i] : 0.0f;
+      rv[i] = 1.0f / dv[i];
+    }
+  }
+  uint8_t* qe = reinterpret_cast<uint8_t*>(qp.q_scales);
+  uint8_t* ke = reinterpret_cast<uint8_t*>(qp.k_scales);
+  const size_t ds_own = ds_base(g, cb.bk, cb.hk * grp);   // grp == 1: query head (bk, hk)
+  float xk[NP][8];
+#pragma unroll
+  for (int p = 0; p < NP; p++) {
+    const int rl = r0 + p * RP, row = t0 + rl;
+    const bool qv = cb.qa && row < cb.qi.len, kv = cb.ka && row < cb.ki.len;
+    // the row's three loads go out together (zeros past an instance's end)
+    const uint4 gq = row_raw(q, cb.qi, cb.qa, row, c0);
+    const uint4 gk = row_raw(k, cb.ki, cb.ka, row, c0);
+    const uint4 gv = row_raw(v, cb.ki, cb.ka, row, c0);
+    float xq[8], xv[8];
+    unpack8<DT>(gq, xq);
+    unpack8<DT>(gk, xk[p]);
+    unpack8<DT>(gv, xv);
+    // branch-free: rows past an instance's end are zeros, and the 0/1 factors keep them zero
+    // after smoothing (so their codes, cs and ds are all 0)
+    const float fq = qv ? 1.0f : 0.0f, fk = kv ? 1.0f : 0.0f;
+    double cs = 0.0, ds = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      cs += (double)xq[i] * (double)mkq[c0 + i];
+      xq[i] = xq[i] - fq * s_mq[c0 + i];
+      xk[p][i] = xk[p][i] - fk * s_mk[c0 + i];
+      if (grp == 1) ds += (double)s_mq[c0 + i] * (double)xk[p][i];
+    }
+    // one MX block = 32 channels = 4 neighbouring threads
+    uint32_t aq = 0, ak = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      aq = max(aq, __float_as_uint(fabsf(xq[i])));
+      ak = max(ak, __float_as_uint(fabsf(xk[p][i])));
+    }
+#pragma unroll
+    for (int o = 1; o < 4; o <<= 1) {
+      aq = max(aq, (uint32_t)__shfl_xor((int)aq, o));
+      ak = max(ak, (uint32_t)__shfl_xor((int)ak, o));
+    }
+#pragma unroll
+    for (int o = 1; o < C8; o <<= 1) {
+      cs += __shfl_xor(cs, o);
+      ds += __shfl_xor(ds, o);
+    }
+    if (cb.qa) {
+      const unsigned bq = mx_fp4_scale_byte(__uint_as_float(aq));
+      const float sq = bq == 0 ? 1.0f : e8m0_to_float(bq);
+      *reinterpret_cast<uint32_t*>(qp.q_codes + (cb.qi.tok0 + row) * (D / 2) + c0 / 2) = pack_fp4x8(xq, sq);
+      if ((c0 % 32) == 0) qe[(cb.qi.tok0 + row) * (D / 32) + c0 / 32] = (uint8_t)bq;
+      if ((tid % C8) == 0 && qv) qp.lse_corr[cb.qi.row0 + row] = (float)(sm * cs);
+    }
+    if (cb.ka) {
+      const unsigned bk = mx_fp4_scale_byte(__uint_as_float(ak));
+      const float sk = bk == 0 ? 1.0f : e8m0_to_float(bk);
+      *reinterpret_cast<uint32_t*>(qp.k_codes + (cb.ki.tok0 + row) * (D / 2) + c0 / 2) = pack_fp4x8(xk[p], sk);
+      if ((c0 % 32) == 0) ke[(cb.ki.tok0 + row) * (D / 32) + c0 / 32] = (uint8_t)bk;
+      if (grp == 1 && (tid % C8) == 0) qp.delta_s[ds_own + row] = kv ? (float)ds : 0.0f;
+      if (PV == PV_FP8) {
+        if (kv) {
+          put_v_fp8(s_vt, rl, c0, xv, dv, rv);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; i++) s_vt[(c0 + i) * 64 + rl] = 0;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) s_vf[rl][c0 + i] = xv[i];
+      }
+    }
+  }
+  if (!cb.ka) return;
+  // grouped heads: dS for each query head of the group, with its own mu_q
+  if (grp > 1) {
+    const Inst qg = q_inst(g, cb.bk, cb.hk * grp, D);   // the group's query sequence
+    for (int r = 0; r < grp; r++) {
+      const int hq = cb.hk * grp + r, iq = cb.bk * g.H + hq;
+      __syncthreads();
+      if (tid < D) s_mq[tid] = chunk_mean(qp.sums, 1, BHm, iq, D, tid, qg.len);
+      __syncthreads();
+      const size_t ds0 = ds_base(g, cb.bk, hq);
+#pragma unroll
+      for (int p = 0; p < NP; p++) {
+        const int row = t0 + r0 + p * RP;
+        double ds = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) ds += (double)s_mq[c0 + i] * (double)xk[p][i];
+#pragma unroll
+        for (int o = 1; o < C8; o <<= 1) ds += __shfl_xor(ds, o);
+        if ((tid % C8) == 0) qp.delta_s[ds0 + row] = row < cb.ki.len ? (float)ds : 0.0f;
+      }
+    }
+  }
+  __syncthreads();
+  const size_t vt0 = cb.ki.tok0 / 64 + blk;   // the instance's V tile
+  if (PV == PV_FP8) {
+    uint8_t* dst = qp.v_codes + vt0 * D * 64;
+    for (int c = tid; c < D * 4; c += 256)
+      *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(s_vt + c * 16);
+  } else {
+    // one thread per (channel, 32-token group)
+    for (int w = tid; w < D * 2; w += 256) {
+      const int ch = w % D, gi = w / D;
+      float x[32];
+      uint32_t a = 0;
+#pragma unroll
+      for (int i = 0; i < 32; i++) {
+        x[i] = s_vf[32 * gi + i][ch];
+        a = max(a, __float_as_uint(fabsf(x[i])));
+      }
+      uint8_t* vsb = reinterpret_cast<uint8_t*>(qp.v_scales) + (cb.ki.tok0 / 32 + 2 * blk + gi) * D + ch;
+      if (PV == PV_MXFP4) {
+        const unsigned b = mx_fp4_scale_byte(__uint_as_float(a));
+        const float sc = b == 0 ? 1.0f : e8m0_to_float(b);
+        uint4 pk;
+        pk.x = pack_fp4x8(x, sc);
+        pk.y = pack_fp4x8(x + 8, sc);
+        pk.z = pack_fp4x8(x + 16, sc);
+        pk.w = pack_fp4x8(x + 24, sc);
+        *reinterpret_cast<uint4*>(qp.v_codes + (vt0 * D + ch) * 32 + 16 * gi) = pk;
+        *vsb = (uint8_t)b;
+      } else {
+        // E4M3 elements: v * 2^-e is exact (b <= 246, so the factor 2^(127-b) is a normal
+        // float); the floor rule can put the block max up to 512, so saturate at 448 first
+        const unsigned b = mx_scale_byte<8>(__uint_as_float(a));
+        const float inv = __uint_as_float((254u - b) << 23);
+        float y[32];
+#pragma unroll
+        for (int i = 0; i < 32; i++) y[i] = fminf(fmaxf(x[i] * inv, -448.0f), 448.0f);
+        uint4 pk[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+          pk[hh].x = pack_fp8x4(y[16 * hh], y[16 * hh + 1], y[16 * hh + 2], y[16 * hh + 3]);
+          pk[hh].y = pack_fp8x4(y[16 * hh + 4], y[16 * hh + 5], y[16 * hh + 6], y[16 * hh + 7]);
+          pk[hh].z = pack_fp8x4(y[16 * hh + 8], y[16 * hh + 9], y[16 * hh + 10], y[16 * hh + 11]);
+          pk[hh].w = pack_fp8x4(y[16 * hh + 12], y[16 * hh + 13], y[16 * hh + 14], y[16 * hh + 15]);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(qp.v_codes + (vt0 * D + ch) * 64 + 32 * gi);
+        dst[0] = pk[0];
+        dst[1] = pk[1];
+        *vsb = (uint8_t)b;
+      }
+    }
+  }
+}
+
 template <int DT, int D>
 static hipError_t prologue_dispatch(const void* q, const void* k, const void* v, const Shape& s, const QuantPtrs& qp,
                                     hipStream_t st) {
-  const int BH = s.B * s.H;
+  const SeqGeo& g = s.g;
+  const int BHm = g.B * g.H;
   const uint16_t *Q = (const uint16_t*)q, *K = (const uint16_t*)k, *V = (const uint16_t*)v;
-  dim3 sg(kChunks, BH), qg(s.Np / 64, BH);
-  const bool mx = s.qk_fmt == QK_MXFP4, fp8v = s.pv_fmt == PV_FP8;
+  // fixed length without grouped heads: the streamlined codes kernels (N, Np per instance)
+  const bool plain = g.cu_q == nullptr && g.Hkv == g.H;
+  dim3 sg(kChunks, BHm), qg(max(g.nbq, g.nbk), BHm);
+  const bool mx = s.qk_fmt == QK_MXFP4;
   if (!mx) {
-    stats_kernel<DT, D, false, true><<<sg, 256, 0, st>>>(Q, K, V, s.N, BH, qp.sums, qp.amax_v);
-    quant_int8_fp8_kernel<DT, D><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BH, s.sm_scale, qp);
-  } else if (fp8v) {
-    stats_kernel<DT, D, true, true><<<sg, 256, 0, st>>>(Q, K, V, s.N, BH, qp.sums, qp.amax_v);
-    quant_mxfp4_kernel<DT, D, PV_FP8><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BH, s.sm_scale, qp);
-  } else if (s.pv_fmt == PV_MXFP8) {
-    stats_kernel<DT, D, true, false><<<sg, 256, 0, st>>>(Q, K, V, s.N, BH, qp.sums, qp.amax_v);
-    quant_mxfp4_kernel<DT, D, PV_MXFP8><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BH, s.sm_scale, qp);
-  } else {
-    stats_kernel<DT, D, true, false><<<sg, 256, 0, st>>>(Q, K, V, s.N, BH, qp.sums, qp.amax_v);
-    quant_mxfp4_kernel<DT, D, PV_MXFP4><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BH, s.sm_scale, qp);
+    stats_kernel<DT, D, false, true><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
+    if (plain)
+      quant_int8_fp8_kernel<DT, D><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BHm, s.sm_scale, qp);
+    else
+      quant_int8_fp8_seq_kernel<DT, D><<<qg, 256, 0, st>>>(Q, K, V, g, s.sm_scale, qp);
+    return hipGetLastError();
   }
+  if (s.pv_fmt == PV_FP8)
+    stats_kernel<DT, D, true, true><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
+  else
+    stats_kernel<DT, D, true, false><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
+  auto codes = [&](auto pv) {
+    constexpr int PV = decltype(pv)::value;
+    if (plain)
+      quant_mxfp4_kernel<DT, D, PV><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BHm, s.sm_scale, qp);
+    else
+      quant_mxfp4_seq_kernel<DT, D, PV><<<qg, 256, 0, st>>>(Q, K, V, g, s.sm_scale, qp);
+  };
+  if (s.pv_fmt == PV_FP8) codes(std::integral_constant<int, PV_FP8>{});
+  else if (s.pv_fmt == PV_MXFP8) codes(std::integral_constant<int, PV_MXFP8>{});
+  else codes(std::integral_constant<int, PV_MXFP4>{});
   return hipGetLastError();
 }
 

@@ -37,33 +37,62 @@ bool inject_alloc_failure() {
   return e && strcmp(e, "alloc") == 0;
 }
 
+// Checks shared by the fixed-length and the packed problem descriptors.
+sage_status check_common(int d, int causal, float sm_scale, int io_dtype, int qk_fmt, int pv_fmt) {
+  if (d != 64 && d != 128) return fail(SAGE_ERR_UNSUPPORTED, "head dim d=%d is not supported (64 or 128)", d);
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  if (io_dtype != SAGE_DT_BF16 && io_dtype != SAGE_DT_F16)
+    return fail(SAGE_ERR_INVALID_ARG, "io_dtype %d is not a SAGE_DT_* value", io_dtype);
+  auto known = [](int f) { return f >= SAGE_FMT_INT8 && f <= SAGE_FMT_MXFP8; };
+  const bool fmts_known = known(qk_fmt) && known(pv_fmt);
+  if (!fmts_known) return fail(SAGE_ERR_INVALID_ARG, "qk_fmt/pv_fmt must be SAGE_FMT_* values");
+  const bool pair_ok = (qk_fmt == SAGE_FMT_INT8 && pv_fmt == SAGE_FMT_FP8) ||
+                       (qk_fmt == SAGE_FMT_MXFP4 && pv_fmt == SAGE_FMT_FP8) ||
+                       (qk_fmt == SAGE_FMT_MXFP4 && pv_fmt == SAGE_FMT_MXFP4) ||
+                       (qk_fmt == SAGE_FMT_MXFP4 && pv_fmt == SAGE_FMT_MXFP8);
+  if (!pair_ok) return fail(SAGE_ERR_UNSUPPORTED, "format pair (qk=%d, pv=%d) is not supported", qk_fmt, pv_fmt);
+  return SAGE_OK;
+}
+
+// The prologue grids put query / KV instances on the second grid axis.
+constexpr long long kMaxInstances = 65535;
+
 sage_status check_problem(const sage_problem* p) {
   if (!p) return fail(SAGE_ERR_INVALID_ARG, "problem descriptor is NULL");
   if (p->B < 1 || p->H < 1 || p->N < 1)
     return fail(SAGE_ERR_INVALID_ARG, "B, H and N must be >= 1 (got B=%d H=%d N=%d)", p->B, p->H, p->N);
-  if ((long long)p->B * p->H * ((long long)p->N + sage::kTokenPad) * p->d > (1LL << 40))
+  if ((long long)p->B * p->H * ((long long)p->N + sage::kTokenPad) * p->d > (1LL << 40) ||
+      (long long)p->B * p->H > kMaxInstances)
     return fail(SAGE_ERR_INVALID_ARG, "problem too large");
-  if (p->d != 64 && p->d != 128)
-    return fail(SAGE_ERR_UNSUPPORTED, "head dim d=%d is not supported (64 or 128)", p->d);
-  if (p->causal != 0 && p->causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (!std::isfinite(p->sm_scale) || !(p->sm_scale > 0.0f))
-    return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
-  if (p->io_dtype != SAGE_DT_BF16 && p->io_dtype != SAGE_DT_F16)
-    return fail(SAGE_ERR_INVALID_ARG, "io_dtype %d is not a SAGE_DT_* value", p->io_dtype);
-  auto known = [](int f) { return f >= SAGE_FMT_INT8 && f <= SAGE_FMT_MXFP8; };
-  const bool fmts_known = known(p->qk_fmt) && known(p->pv_fmt);
-  if (!fmts_known) return fail(SAGE_ERR_INVALID_ARG, "qk_fmt/pv_fmt must be SAGE_FMT_* values");
-  const bool pair_ok = (p->qk_fmt == SAGE_FMT_INT8 && p->pv_fmt == SAGE_FMT_FP8) ||
-                       (p->qk_fmt == SAGE_FMT_MXFP4 && p->pv_fmt == SAGE_FMT_FP8) ||
-                       (p->qk_fmt == SAGE_FMT_MXFP4 && p->pv_fmt == SAGE_FMT_MXFP4) ||
-                       (p->qk_fmt == SAGE_FMT_MXFP4 && p->pv_fmt == SAGE_FMT_MXFP8);
-  if (!pair_ok)
-    return fail(SAGE_ERR_UNSUPPORTED, "format pair (qk=%d, pv=%d) is not supported", p->qk_fmt, p->pv_fmt);
-  return SAGE_OK;
+  return check_common(p->d, p->causal, p->sm_scale, p->io_dtype, p->qk_fmt, p->pv_fmt);
+}
+
+// Packed problems: token extents per head of the quantized buffers (room for every sequence
+// rounded up to 128 tokens at a 64-aligned start, see SeqGeo).
+size_t packed_tokens(int total, int B) { return round_up((size_t)total, 64) + 256 * (size_t)B; }
+
+sage_status check_varlen(const sage_varlen_problem* p) {
+  if (!p) return fail(SAGE_ERR_INVALID_ARG, "problem descriptor is NULL");
+  if (p->B < 1 || p->H < 1 || p->H_kv < 1)
+    return fail(SAGE_ERR_INVALID_ARG, "B, H and H_kv must be >= 1 (got B=%d H=%d H_kv=%d)", p->B, p->H, p->H_kv);
+  if (p->H % p->H_kv != 0)
+    return fail(SAGE_ERR_INVALID_ARG, "H=%d is not a multiple of H_kv=%d", p->H, p->H_kv);
+  if (p->total_q < 0 || p->total_k < 0 || p->max_seqlen_q < 0 || p->max_seqlen_k < 0)
+    return fail(SAGE_ERR_INVALID_ARG, "total_q, total_k, max_seqlen_q and max_seqlen_k must be >= 0");
+  if (packed_tokens(p->total_q, p->B) > (size_t)INT32_MAX || packed_tokens(p->total_k, p->B) > (size_t)INT32_MAX)
+    return fail(SAGE_ERR_INVALID_ARG, "problem too large");
+  const long long toks = (long long)p->H * packed_tokens(p->total_q, p->B) +
+                         (long long)p->H_kv * packed_tokens(p->total_k, p->B) * 2;
+  if (toks * p->d > (1LL << 40) || (long long)p->B * p->H > kMaxInstances ||
+      (long long)p->B * p->H * ((p->max_seqlen_q + 127) / 128) > (1LL << 31) - 1)
+    return fail(SAGE_ERR_INVALID_ARG, "problem too large");
+  return check_common(p->d, p->causal, p->sm_scale, p->io_dtype, p->qk_fmt, p->pv_fmt);
 }
 
 sage::Shape to_shape(const sage_problem* p) {
-  sage::Shape s;
+  sage::Shape s{};
   s.B = p->B;
   s.H = p->H;
   s.N = p->N;
@@ -74,36 +103,89 @@ sage::Shape to_shape(const sage_problem* p) {
   s.qk_fmt = p->qk_fmt;
   s.pv_fmt = p->pv_fmt;
   s.sm_scale = p->sm_scale;
+  sage::SeqGeo& g = s.g;
+  g.cu_q = g.cu_k = nullptr;
+  g.B = p->B;
+  g.H = g.Hkv = p->H;
+  g.Nq = g.Nk = p->N;
+  g.Npq = g.Npk = s.Np;
+  g.nbq = g.nbk = s.Np / 64;
   return s;
 }
 
-void compute_layout(const sage_problem* p, sage_quant_layout* L) {
-  const size_t BH = (size_t)p->B * p->H, d = p->d, N = p->N;
-  const size_t Np = round_up(N, sage::kTokenPad), nb = Np / 64;
-  const bool mx = p->qk_fmt == SAGE_FMT_MXFP4, mxv = p->pv_fmt == SAGE_FMT_MXFP4, mx8v = p->pv_fmt == SAGE_FMT_MXFP8;
+sage::Shape to_shape(const sage_varlen_problem* p, const int* cu_q, const int* cu_k) {
+  sage::Shape s{};
+  s.B = p->B;
+  s.H = p->H;
+  s.d = p->d;
+  s.causal = p->causal;
+  s.io_dtype = p->io_dtype;
+  s.qk_fmt = p->qk_fmt;
+  s.pv_fmt = p->pv_fmt;
+  s.sm_scale = p->sm_scale;
+  sage::SeqGeo& g = s.g;
+  g.cu_q = cu_q;
+  g.cu_k = cu_k;
+  g.B = p->B;
+  g.H = p->H;
+  g.Hkv = p->H_kv;
+  g.Tq = (int)packed_tokens(p->total_q, p->B);
+  g.Tk = (int)packed_tokens(p->total_k, p->B);
+  g.total_q = p->total_q;
+  g.total_k = p->total_k;
+  g.max_q = p->max_seqlen_q;
+  g.max_k = p->max_seqlen_k;
+  g.nbq = (int)(round_up((size_t)p->max_seqlen_q, sage::kTokenPad) / 64);
+  g.nbk = (int)(round_up((size_t)p->max_seqlen_k, sage::kTokenPad) / 64);
+  return s;
+}
+
+// Token extents of a quantized buffer.
+struct Extents {
+  size_t inst_q, inst_kv;   // query / KV instances (per-instance arrays: means, FP8 V steps)
+  size_t tq, tk;            // tokens over all query / KV instances (multiples of 64)
+  size_t ds, corr;          // dS floats (query heads x key tokens), LSE-term floats
+  size_t stats_inst;        // instances of the statistics partials (B*H)
+};
+
+Extents extents(const sage_problem* p) {
+  const size_t BH = (size_t)p->B * p->H, Np = round_up((size_t)p->N, sage::kTokenPad);
+  return Extents{BH, BH, BH * Np, BH * Np, BH * Np, BH * (size_t)p->N, BH};
+}
+Extents extents(const sage_varlen_problem* p) {
+  const size_t Tq = packed_tokens(p->total_q, p->B), Tk = packed_tokens(p->total_k, p->B);
+  const size_t BH = (size_t)p->B * p->H;
+  return Extents{BH, (size_t)p->B * p->H_kv, p->H * Tq, p->H_kv * Tk, p->H * Tk, p->H * Tq, BH};
+}
+
+void compute_layout(const Extents& E, int d_, int qk_fmt, int pv_fmt, sage_quant_layout* L) {
+  const size_t d = d_;
+  const bool mx = qk_fmt == SAGE_FMT_MXFP4, mxv = pv_fmt == SAGE_FMT_MXFP4, mx8v = pv_fmt == SAGE_FMT_MXFP8;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
     off = round_up(off + bytes, 256);
     return o;
   };
-  L->mu_k = take(BH * d * 4);
-  L->mu_q = take(BH * d * 4);
-  L->q_codes = take(mx ? BH * Np * d / 2 : BH * Np * d);
-  L->q_scales = take(mx ? BH * Np * (d / 32) : BH * nb * 4);
-  L->k_codes = take(mx ? BH * Np * d / 2 : BH * Np * d);
-  L->k_scales = take(mx ? BH * Np * (d / 32) : BH * nb * 4);
-  L->v_codes = take(mxv ? BH * Np * d / 2 : BH * Np * d);
-  L->v_scales = take(mxv || mx8v ? BH * (Np / 32) * d : BH * d * 4);
-  L->delta_s = take(BH * Np * 4);
-  L->lse_corr = take(BH * N * 4);
-  L->stats = take(sage::kStatChunks * (BH * d * 8 * 2 + BH * d * 4));
+  L->mu_k = take(E.inst_kv * d * 4);
+  L->mu_q = take(E.inst_q * d * 4);
+  L->q_codes = take(mx ? E.tq * d / 2 : E.tq * d);
+  L->q_scales = take(mx ? E.tq * (d / 32) : E.tq / 64 * 4);
+  L->k_codes = take(mx ? E.tk * d / 2 : E.tk * d);
+  L->k_scales = take(mx ? E.tk * (d / 32) : E.tk / 64 * 4);
+  L->v_codes = take(mxv ? E.tk * d / 2 : E.tk * d);
+  L->v_scales = take(mxv || mx8v ? E.tk / 32 * d : E.inst_kv * d * 4);
+  L->delta_s = take(E.ds * 4);
+  L->lse_corr = take(E.corr * 4);
+  L->stats = take(sage::kStatChunks * (E.stats_inst * d * 8 * 2 + E.stats_inst * d * 4));
   L->total = off;
 }
+void compute_layout(const sage_problem* p, sage_quant_layout* L) {
+  compute_layout(extents(p), p->d, p->qk_fmt, p->pv_fmt, L);
+}
 
-sage::QuantPtrs resolve(void* buf, const sage_problem* p, const sage_quant_layout& L) {
+sage::QuantPtrs resolve(void* buf, size_t BH, int d, const sage_quant_layout& L) {
   uint8_t* b = static_cast<uint8_t*>(buf);
-  const size_t BH = (size_t)p->B * p->H;
   sage::QuantPtrs q;
   q.mu_k = reinterpret_cast<float*>(b + L.mu_k);
   q.mu_q = reinterpret_cast<float*>(b + L.mu_q);
@@ -116,8 +198,11 @@ sage::QuantPtrs resolve(void* buf, const sage_problem* p, const sage_quant_layou
   q.delta_s = reinterpret_cast<float*>(b + L.delta_s);
   q.lse_corr = reinterpret_cast<float*>(b + L.lse_corr);
   q.sums = reinterpret_cast<double*>(b + L.stats);
-  q.amax_v = reinterpret_cast<uint32_t*>(b + L.stats + sage::kStatChunks * BH * p->d * 8 * 2);
+  q.amax_v = reinterpret_cast<uint32_t*>(b + L.stats + sage::kStatChunks * BH * d * 8 * 2);
   return q;
+}
+sage::QuantPtrs resolve(void* buf, const sage_problem* p, const sage_quant_layout& L) {
+  return resolve(buf, (size_t)p->B * p->H, p->d, L);
 }
 
 sage_problem make_problem(int B, int H, int N, int d, int causal, float sm, int io, int qk, int pv) {
@@ -267,6 +352,40 @@ sage_status sage_attn_bwd(const sage_problem* p, const void* q, const void* k, c
   hipError_t e = sage::launch_attn_bwd(to_shape(p), q, k, v, o, dout, lse, dq, dk, dv, ws, L.total,
                                        resolve(ws, p, L), (hipStream_t)stream);
   return e == hipSuccess ? SAGE_OK : hip_fail(e, "backward launch");
+}
+
+sage_status sage_varlen_ws_size(const sage_varlen_problem* p, size_t* bytes) {
+  sage_status s = check_varlen(p);
+  if (s != SAGE_OK) return s;
+  if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
+  sage_quant_layout L;
+  compute_layout(extents(p), p->d, p->qk_fmt, p->pv_fmt, &L);
+  *bytes = L.total;
+  return SAGE_OK;
+}
+
+sage_status sage_attn_varlen_fwd(const sage_varlen_problem* p, const void* q, const void* k, const void* v,
+                                 const int* cu_seqlens_q, const int* cu_seqlens_k, void* o, float* lse, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  sage_status s = check_varlen(p);
+  if (s != SAGE_OK) return s;
+  if (!cu_seqlens_q || !cu_seqlens_k || (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return fail(SAGE_ERR_INVALID_ARG, "cu_seqlens_q / cu_seqlens_k must be non-NULL, 4-byte aligned");
+  if (p->total_q == 0) return SAGE_OK;   // no query rows: nothing to compute
+  if ((s = check_tensors({q, o, ws})) != SAGE_OK) return s;
+  if (p->total_k > 0 && (s = check_tensors({k, v})) != SAGE_OK) return s;
+  if (lse && !aligned16(lse)) return fail(SAGE_ERR_INVALID_ARG, "lse must be 16-byte aligned");
+  sage_quant_layout L;
+  compute_layout(extents(p), p->d, p->qk_fmt, p->pv_fmt, &L);
+  if (ws_bytes < L.total) return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  const sage::Shape sh = to_shape(p, cu_seqlens_q, cu_seqlens_k);
+  const sage::QuantPtrs qp = resolve(ws, (size_t)p->B * p->H, p->d, L);
+  hipError_t e = sage::launch_prologue(q, k, v, sh, qp, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  if (sh.g.nbq == 0) return SAGE_OK;     // max_seqlen_q == 0: every sequence is empty
+  e = sage::launch_attn_fwd(sh, qp, o, lse, (hipStream_t)stream);
+  return e == hipSuccess ? SAGE_OK : hip_fail(e, "attention launch");
 }
 
 }  // extern "C"

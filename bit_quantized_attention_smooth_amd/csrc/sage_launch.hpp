@@ -26,13 +26,104 @@ struct QuantPtrs {
   void* v_scales;     // fp32 [BH, d] (FP8) or uint8 E8M0 [BH, Np/32, d] (MXFP4, MXFP8)
   float* delta_s;
   float* lse_corr;
-  double* sums;       // [2, BH, d]: K then Q token sums
-  uint32_t* amax_v;   // [BH, d] bit patterns of max |V| per channel
+  double* sums;       // [2, kStatChunks, B*H, d]: K then Q token sums per chunk (K by KV instance)
+  uint32_t* amax_v;   // [kStatChunks, B*H, d] bit patterns of max |V| per channel (by KV instance)
 };
+
+// Token geometry of a problem.  Fixed length: B sequences of Nq query and Nk key tokens in
+// [B,H,Nq,d] / [B,Hkv,Nk,d] tensors; instance (b, h) owns Npq (Npk) consecutive tokens of
+// the quantized buffers from (b H + h) Npq on.  Packed (cu_q != null): sequence b is rows
+// [cu[b], cu[b+1]) of [total,H,d] / [total,Hkv,d] tensors, and head h of sequence b owns
+// the tokens from h T + roundup64(cu[b]) + 256 b on: room for the sequence rounded up to
+// 128 tokens, found without a prefix sum over the batch.
+struct SeqGeo {
+  const int* cu_q;   // packed: device [B+1] query row offsets; null: fixed length
+  const int* cu_k;   // packed: device [B+1] key row offsets
+  int B, H, Hkv;     // H query heads; query head h reads KV head h / (H / Hkv)
+  int Nq, Nk;        // fixed length: tokens per sequence
+  int Npq, Npk;      // fixed length: tokens per instance in the quantized buffers
+  int Tq, Tk;        // packed: tokens per head in the quantized buffers
+  int total_q;       // packed: rows of q (the stride of the [H, total_q] LSE)
+  int total_k;       // packed: rows of k and v
+  int max_q, max_k;  // packed: the longest sequence the caller declares
+  int nbq, nbk;      // 64-token blocks covering the longest query / key instance (to 128 tokens)
+};
+
+// One (sequence, head) instance of Q or of K/V.
+struct Inst {
+  int len;           // tokens
+  size_t tok0;       // first token in the quantized buffers (a multiple of 64)
+  size_t io0;        // element offset of token 0 in the I/O tensor
+  int ios;           // elements from one token to the next in the I/O tensor
+  size_t row0;       // packed / fixed per-token fp32 arrays (LSE correction)
+  size_t lse0;       // LSE output: [B,H,Nq] fixed, [H,total_q] packed
+};
+
+#if defined(__HIPCC__)
+// Packed sequence b: its first row and length, clamped so that any offsets keep every access
+// inside the buffers (start in [0, total], length in [0, min(max_len, total - start)]).
+__device__ __forceinline__ void packed_seq(const int* cu, int b, int total, int max_len, int& s, int& len) {
+  s = min(max(cu[b], 0), total);
+  const int e = min(max(cu[b + 1], s), total);
+  len = min(e - s, max_len);
+}
+// First token of sequence b (starting at row s) in a head's packed region: a multiple of 64
+// with room for the sequence rounded up to 128 before the next sequence's start.
+__device__ __forceinline__ size_t packed_base(int s, int b) {
+  return (size_t)((s + 63) & ~63) + 256 * (size_t)b;
+}
+__device__ __forceinline__ Inst q_inst(const SeqGeo& g, int b, int h, int d) {
+  Inst r;
+  if (g.cu_q) {
+    int s;
+    packed_seq(g.cu_q, b, g.total_q, g.max_q, s, r.len);
+    r.tok0 = (size_t)h * g.Tq + packed_base(s, b);
+    r.io0 = ((size_t)s * g.H + h) * d;
+    r.ios = g.H * d;
+    r.row0 = r.tok0;
+    r.lse0 = (size_t)h * g.total_q + s;
+  } else {
+    const size_t i = (size_t)b * g.H + h;
+    r.len = g.Nq;
+    r.tok0 = i * g.Npq;
+    r.io0 = i * g.Nq * d;
+    r.ios = d;
+    r.row0 = i * g.Nq;
+    r.lse0 = r.row0;
+  }
+  return r;
+}
+__device__ __forceinline__ Inst k_inst(const SeqGeo& g, int b, int hk, int d) {
+  Inst r;
+  if (g.cu_k) {
+    int s;
+    packed_seq(g.cu_k, b, g.total_k, g.max_k, s, r.len);
+    r.tok0 = (size_t)hk * g.Tk + packed_base(s, b);
+    r.io0 = ((size_t)s * g.Hkv + hk) * d;
+    r.ios = g.Hkv * d;
+  } else {
+    const size_t i = (size_t)b * g.Hkv + hk;
+    r.len = g.Nk;
+    r.tok0 = i * g.Npk;
+    r.io0 = i * g.Nk * d;
+    r.ios = d;
+  }
+  r.row0 = r.lse0 = 0;
+  return r;
+}
+// First key token of query head h's dS strip (MXFP4 QK: mu_q(h) . K_s per key).
+__device__ __forceinline__ size_t ds_base(const SeqGeo& g, int b, int h) {
+  if (!g.cu_k) return ((size_t)b * g.H + h) * g.Npk;
+  int s, len;
+  packed_seq(g.cu_k, b, g.total_k, g.max_k, s, len);
+  return (size_t)h * g.Tk + packed_base(s, b);
+}
+#endif
 
 struct Shape {
   int B, H, N, d, Np, causal, io_dtype, qk_fmt, pv_fmt;
   float sm_scale;
+  SeqGeo g;          // N / Np above are the fixed-length Nq = Nk and Npq = Npk
 };
 
 hipError_t launch_prologue(const void* q, const void* k, const void* v, const Shape& s,

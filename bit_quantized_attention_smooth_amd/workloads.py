@@ -99,3 +99,37 @@ def workload_inputs(name, **override):
 def as_u16(t):
     """Raw 16-bit patterns of a bf16/fp16 CPU tensor as a numpy uint16 array (no copy of values)."""
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# Packed (cu_seqlens) workloads: a batch of prefill sequences of mixed lengths with grouped KV
+# heads, as an LLM serving step packs them.
+VARLEN_WORKLOADS = {
+    "varlen_gqa_causal_b8h32kv8t16384d128": dict(lens=[3072, 256, 4096, 1000, 2048, 777, 3135, 2000],
+                                                 H=32, Hkv=8, d=128, causal=True, dtype="bf16", seed=6,
+                                                 k_off_std=5.0, outlier_frac=0.01, sm_scale=1.0 / math.sqrt(128)),
+}
+
+
+def varlen_workload(name):
+    """Packed inputs: q [T,H,d], k and v [T,Hkv,d] CPU tensors, int32 cu_q = cu_k [B+1].
+    Draw order: Q, K, V, the per-(KV head, channel) K offsets, the outlier picks (Q, then K)."""
+    w = dict(VARLEN_WORKLOADS[name])
+    lens, H, Hkv, d = w["lens"], w["H"], w["Hkv"], w["d"]
+    T = int(sum(lens))
+    rng = np.random.default_rng(w["seed"])
+    q = rng.standard_normal((T, H, d), dtype=np.float32)
+    k = rng.standard_normal((T, Hkv, d), dtype=np.float32)
+    v = rng.standard_normal((T, Hkv, d), dtype=np.float32)
+    k += rng.normal(0.0, w["k_off_std"], size=(1, Hkv, d)).astype(np.float32)
+    for x in (q, k):
+        hc = x.shape[1] * d
+        n_out = int(round(w["outlier_frac"] * hc))
+        pick = rng.choice(hc, size=n_out, replace=False)
+        xv = x.reshape(T, hc)
+        xv[:, pick] *= 10.0
+    tdt = DTYPES[w["dtype"]]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    x = {"q": torch.from_numpy(q).to(tdt), "k": torch.from_numpy(k).to(tdt), "v": torch.from_numpy(v).to(tdt),
+         "cu_q": cu, "cu_k": cu.clone()}
+    w.update(B=len(lens), T=T, max_seqlen=int(max(lens)))
+    return x, w

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 1
+#define SAGE_ABI_VERSION 2
 
 typedef enum {
     SAGE_OK = 0,
@@ -148,6 +148,46 @@ sage_status sage_attn_bwd_ws_size(const sage_problem *p, size_t *bytes);
 sage_status sage_attn_bwd(const sage_problem *p, const void *q, const void *k, const void *v,
                           const void *o, const void *dout, const float *lse,
                           void *dq, void *dk, void *dv, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Packed variable-length sequences with grouped KV heads: the sageattn_varlen
+ * entry named on the SageAttention3 code-link page, in FlashAttention's
+ * cu_seqlens convention (the implementation builds on FlashAttention: review
+ * thread, reply to reviewer wwcu W1).
+ *   q, o           device [total_q, H, d]: the rows of all sequences back to back
+ *   k, v           device [total_k, H_kv, d]
+ *   cu_seqlens_q,  device int32 [B+1], non-decreasing, [0] = 0, [B] = total_q
+ *   cu_seqlens_k   (total_k): sequence b is rows [cu[b], cu[b+1]); query and key
+ *                  lengths may differ
+ *   lse            device fp32 [H, total_q] or NULL
+ * Query head h reads KV head h / (H / H_kv).  Every sequence is quantized on its
+ * own (K mean and V channel steps per sequence and KV head, 64-token INT8 blocks
+ * inside the sequence).  Causal masking is top-left aligned per sequence (query
+ * i sees keys j <= i).  A query with no key (an empty key sequence) gets a zero
+ * output and LSE -inf.  max_seqlen_q / max_seqlen_k bound every sequence's
+ * length (host values, as FlashAttention takes them); the kernels clamp the
+ * device offsets to [0, total] and the lengths to the bounds, so malformed
+ * offsets give unspecified values but no access outside the tensors.
+ * total_q = 0 returns SAGE_OK without launching; k and v may be NULL when
+ * total_k = 0.  ws: device workspace of at least sage_varlen_ws_size bytes.
+ */
+typedef struct {
+    int B;                  /* sequences */
+    int H, H_kv;            /* query heads, key/value heads (H % H_kv == 0) */
+    int d;
+    int causal;             /* 0 or 1 */
+    float sm_scale;         /* finite, > 0 */
+    int io_dtype;           /* SAGE_DT_* */
+    int qk_fmt, pv_fmt;     /* SAGE_FMT_*, the same pairs as sage_problem */
+    int total_q, total_k;   /* rows of q and of k / v */
+    int max_seqlen_q, max_seqlen_k;
+} sage_varlen_problem;
+
+sage_status sage_varlen_ws_size(const sage_varlen_problem *p, size_t *bytes);
+
+sage_status sage_attn_varlen_fwd(const sage_varlen_problem *p, const void *q, const void *k, const void *v,
+                                 const int *cu_seqlens_q, const int *cu_seqlens_k, void *o, float *lse,
+                                 void *ws, size_t ws_bytes, void *stream);
 
 const char *sage_status_string(sage_status s);
 const char *sage_last_error(void);

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(L, name), name
     assert sorted(S.EXPORTS) == declared
-    assert L.sage_abi_version() == 1
+    assert L.sage_abi_version() == 2
 
 
 def _p(**kw):
@@ -119,3 +119,56 @@ def test_backward_rejects_unsupported_problems():
                            None) == S.ERR_WORKSPACE
     assert L.sage_attn_bwd(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n.value,
                            None) == S.ERR_INVALID_ARG
+
+
+def _vp(**kw):
+    base = dict(B=2, H=4, H_kv=2, d=128, causal=0, sm_scale=0.125, io_dtype=0, qk_fmt=1, pv_fmt=2,
+                total_q=100, total_k=90, max_seqlen_q=60, max_seqlen_k=50)
+    base.update(kw)
+    return S.VarlenProblem(*[base[n] for n, _ in S.VarlenProblem._fields_])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), S.ERR_INVALID_ARG), (dict(H_kv=0), S.ERR_INVALID_ARG), (dict(H=6, H_kv=4), S.ERR_INVALID_ARG),
+    (dict(total_q=-1), S.ERR_INVALID_ARG), (dict(max_seqlen_k=-5), S.ERR_INVALID_ARG),
+    (dict(d=96), S.ERR_UNSUPPORTED), (dict(qk_fmt=1, pv_fmt=3), S.ERR_UNSUPPORTED),
+    (dict(sm_scale=float("nan")), S.ERR_INVALID_ARG), (dict(total_q=2 ** 31 - 1), S.ERR_INVALID_ARG),
+])
+def test_varlen_validation(kw, status):
+    L = S.lib()
+    n = ctypes.c_size_t(777)
+    assert L.sage_varlen_ws_size(ctypes.byref(_vp(**kw)), ctypes.byref(n)) == status
+    assert n.value == 777 and L.sage_last_error()
+    assert L.sage_attn_varlen_fwd(ctypes.byref(_vp(**kw)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                  1 << 40, None) == status
+
+
+def test_varlen_pointer_and_workspace_checks():
+    L = S.lib()
+    p = _vp()
+    n = ctypes.c_size_t()
+    assert L.sage_varlen_ws_size(ctypes.byref(p), ctypes.byref(n)) == S.OK
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE]
+    assert L.sage_attn_varlen_fwd(ctypes.byref(p), *args[:3], None, FAKE, *args[5:], n.value, None) == S.ERR_INVALID_ARG
+    assert L.sage_attn_varlen_fwd(ctypes.byref(p), *args[:3], ctypes.c_void_p(0x100002), FAKE, *args[5:], n.value,
+                                  None) == S.ERR_INVALID_ARG
+    assert L.sage_attn_varlen_fwd(ctypes.byref(p), *args, n.value - 1, None) == S.ERR_WORKSPACE
+    # no query rows: nothing to launch, every other pointer may be NULL
+    assert L.sage_attn_varlen_fwd(ctypes.byref(_vp(total_q=0)), None, None, None, FAKE, FAKE, None, None, None, 0,
+                                  None) == S.OK
+
+
+def test_varlen_workspace_covers_every_sequence_padding():
+    """Per head, each sequence gets a 64-aligned start and room for its length rounded up to 128
+    before the next one begins; the workspace grows with the batch size accordingly."""
+    L = S.lib()
+    sizes = []
+    for B in (1, 8, 64):
+        n = ctypes.c_size_t()
+        assert L.sage_varlen_ws_size(ctypes.byref(_vp(B=B, total_q=4096, total_k=4096, max_seqlen_q=4096,
+                                                      max_seqlen_k=4096)), ctypes.byref(n)) == S.OK
+        sizes.append(n.value)
+    # INT8 / FP8: per key token 2 B of K and V codes per KV head, per query token 1 B of Q codes
+    # per query head; 256 extra tokens per sequence
+    per_seq = 256 * (2 * 128 + 4 * 128)
+    assert sizes[1] - sizes[0] >= 7 * per_seq and sizes[2] - sizes[1] >= 56 * per_seq

@@ -1,0 +1,179 @@
+"""GPU parity of the packed-sequence entry (cu_seqlens, grouped KV heads) against the CPU
+oracle's per-sequence simulation, plus two properties that hold bit for bit at any size:
+equal-length packed sequences reproduce the fixed-length path, and grouped KV heads reproduce
+the same call with every KV head repeated for its query heads."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import banner, cos, device, to_np64
+
+pytestmark = pytest.mark.gpu
+
+TILE = 64
+
+
+@pytest.fixture(scope="module")
+def sage():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_attention_smooth_amd as S
+    S.lib()
+    return S
+
+
+def _packed(lens_q, lens_k, H, Hkv, d, seed, dtype=torch.bfloat16, k_off=3.0):
+    g = torch.Generator().manual_seed(seed)
+    cu_q = torch.tensor([0] + list(np.cumsum(lens_q)), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(np.cumsum(lens_k)), dtype=torch.int32)
+    q = torch.randn(int(cu_q[-1]), H, d, generator=g).to(dtype)
+    k = (torch.randn(int(cu_k[-1]), Hkv, d, generator=g) + k_off * torch.randn(1, Hkv, d, generator=g)).to(dtype)
+    v = torch.randn(int(cu_k[-1]), Hkv, d, generator=g).to(dtype)
+    return q, k, v, cu_q, cu_k
+
+
+def _run(sage, q, k, v, cu_q, cu_k, causal, sm, qk, pv, max_q=None, max_k=None):
+    dev = device()
+    lq = (cu_q[1:] - cu_q[:-1]).tolist()
+    lk = (cu_k[1:] - cu_k[:-1]).tolist()
+    o, lse = sage.sageattn_varlen(q.to(dev), k.to(dev), v.to(dev), cu_q.to(dev), cu_k.to(dev),
+                                  max(lq) if max_q is None else max_q, max(lk) if max_k is None else max_k,
+                                  causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv, return_lse=True)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _f32(t):
+    return t.float().numpy()
+
+
+PAIRS = [("int8", "fp8"), ("mxfp4", "fp8"), ("mxfp4", "mxfp4"), ("mxfp4", "mxfp8")]
+
+
+@pytest.mark.parametrize("qk,pv", PAIRS, ids=[f"{a}_{b}" for a, b in PAIRS])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_gqa_matches_oracle(sage, qk, pv, causal, d):
+    import oracle
+    banner(f"varlen {qk}/{pv} causal={causal} d={d}")
+    # ragged lengths: a 1-token sequence, lengths across tile and block edges, unequal q / k
+    lens_q = [1, 129, 300, 64, 77]
+    lens_k = [1, 129, 300, 200, 33] if not causal else lens_q
+    H, Hkv = 6, 2
+    q, k, v, cu_q, cu_k = _packed(lens_q, lens_k, H, Hkv, d, seed=10 + d + 2 * causal)
+    sm = 1 / math.sqrt(d)
+    o, lse = _run(sage, q, k, v, cu_q, cu_k, causal, sm, qk, pv)
+    o_sim, lse_sim, _ = oracle.attn_varlen(_f32(q), _f32(k), _f32(v), cu_q.numpy(), cu_k.numpy(), causal, sm,
+                                           qk_fmt=qk, pv_fmt=pv, tile=TILE)
+    o_ref, _, _ = oracle.attn_varlen(_f32(q), _f32(k), _f32(v), cu_q.numpy(), cu_k.numpy(), causal, sm, exact=True)
+    og = to_np64(o)
+    assert np.abs(og - o_sim).max() <= 2e-2
+    assert cos(og, o_sim) >= 0.9999
+    assert cos(og, o_ref) >= (0.99 if qk == "int8" else 0.965 if pv == "mxfp4" else 0.98)
+    assert np.allclose(lse.cpu().numpy(), lse_sim, rtol=1e-4, atol=2e-3)
+
+
+@pytest.mark.parametrize("pv", ["fp8", "mxfp4", "mxfp8"])
+def test_varlen_mxfp4_keys_longer_than_queries(sage, pv):
+    """MXFP4 QK without grouped heads, key sequences longer than their query sequences by more
+    than a 128-token tile: the dS of keys past the last query block must still use mu_q."""
+    import oracle
+    banner(f"varlen mxfp4/{pv} long keys")
+    lens_q, lens_k = [40, 130, 1], [400, 300, 260]
+    q, k, v, cu_q, cu_k = _packed(lens_q, lens_k, 4, 4, 128, seed=21)
+    q = (q.float() + 2.0 * torch.randn(1, 4, 128, generator=torch.Generator().manual_seed(22))).to(q.dtype)
+    o, lse = _run(sage, q, k, v, cu_q, cu_k, False, 0.09, "mxfp4", pv)
+    o_sim, lse_sim, _ = oracle.attn_varlen(_f32(q), _f32(k), _f32(v), cu_q.numpy(), cu_k.numpy(), False, 0.09,
+                                           qk_fmt="mxfp4", pv_fmt=pv, tile=TILE)
+    og = to_np64(o)
+    assert np.abs(og - o_sim).max() <= 2e-2
+    assert cos(og, o_sim) >= 0.9999
+    assert np.allclose(lse.cpu().numpy(), lse_sim, rtol=1e-4, atol=2e-3)
+
+
+def test_varlen_empty_sequences(sage):
+    """Empty query sequences write nothing; a query sequence with no keys gets zero output
+    and LSE -inf; the neighbours are unaffected."""
+    import oracle
+    banner("varlen empty sequences")
+    lens_q, lens_k = [3, 0, 70, 5], [40, 8, 0, 66]
+    q, k, v, cu_q, cu_k = _packed(lens_q, lens_k, 4, 4, 64, seed=3)
+    for qk, pv in PAIRS:
+        o, lse = _run(sage, q, k, v, cu_q, cu_k, False, 0.125, qk, pv)
+        og, lg = to_np64(o), lse.cpu().numpy()
+        assert np.all(og[3:73] == 0.0) and np.all(np.isneginf(lg[:, 3:73])), (qk, pv)
+        o_sim, lse_sim, _ = oracle.attn_varlen(_f32(q), _f32(k), _f32(v), cu_q.numpy(), cu_k.numpy(), False, 0.125,
+                                               qk_fmt=qk, pv_fmt=pv)
+        keep = np.r_[0:3, 73:78]
+        assert np.abs(og[keep] - o_sim[keep]).max() <= 2e-2
+        assert np.allclose(lg[:, keep], lse_sim[:, keep], rtol=1e-4, atol=2e-3)
+
+
+@pytest.mark.parametrize("qk,pv", PAIRS, ids=[f"{a}_{b}" for a, b in PAIRS])
+def test_equal_length_packed_equals_fixed_length(sage, qk, pv):
+    """B sequences of one length N, H_kv = H: the packed entry computes exactly what the
+    [B,H,N,d] entry does (same per-instance quantization and kernels), bit for bit."""
+    banner(f"packed == fixed {qk}/{pv}")
+    B, H, N, d = 3, 4, 333, 128
+    dev = device()
+    g = torch.Generator().manual_seed(5)
+    x = {n: torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).to(dev) for n in "qkv"}
+    for causal in (False, True):
+        of, lf = sage.sageattn(x["q"], x["k"], x["v"], causal=causal, qk_fmt=qk, pv_fmt=pv, return_lse=True)
+        pk = {n: x[n].permute(0, 2, 1, 3).reshape(B * N, H, d).contiguous() for n in "qkv"}
+        cu = torch.arange(0, B * N + 1, N, dtype=torch.int32, device=dev)
+        ov, lv = sage.sageattn_varlen(pk["q"], pk["k"], pk["v"], cu, cu, N, N, causal=causal, qk_fmt=qk, pv_fmt=pv,
+                                      return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ov.reshape(B, N, H, d).permute(0, 2, 1, 3), of)
+        assert torch.equal(lv.reshape(H, B, N).permute(1, 0, 2), lf)
+
+
+@pytest.mark.parametrize("qk,pv", PAIRS, ids=[f"{a}_{b}" for a, b in PAIRS])
+def test_gqa_equals_repeated_kv_heads(sage, qk, pv):
+    """Grouped KV heads give the same bits as the same call with each KV head repeated for
+    its query heads (the per-instance prologue sees identical data either way)."""
+    banner(f"gqa == repeated kv {qk}/{pv}")
+    lens = [500, 3, 129, 1024]
+    H, Hkv, d = 8, 2, 128
+    q, k, v, cu_q, cu_k = _packed(lens, lens, H, Hkv, d, seed=9)
+    kr, vr = (t.repeat_interleave(H // Hkv, dim=1).contiguous() for t in (k, v))
+    for causal in (False, True):
+        a = _run(sage, q, k, v, cu_q, cu_k, causal, 0.09, qk, pv)
+        b = _run(sage, q, kr, vr, cu_q, cu_k, causal, 0.09, qk, pv)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_varlen_loose_max_seqlen_bounds(sage):
+    """max_seqlen larger than every sequence only adds idle workgroups."""
+    banner("varlen loose bounds")
+    q, k, v, cu_q, cu_k = _packed([100, 250], [100, 250], 4, 1, 64, seed=12)
+    a = _run(sage, q, k, v, cu_q, cu_k, True, 0.125, "int8", "fp8")
+    b = _run(sage, q, k, v, cu_q, cu_k, True, 0.125, "int8", "fp8", max_q=1000, max_k=777)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_varlen_full_size_llm_prefill_sampled(sage):
+    """A packed prefill batch at full size (8 sequences, 16384 tokens, 32 query / 8 KV heads,
+    d = 128, causal) in the benchmark's configuration; the oracle recomputes two sequences."""
+    import oracle
+    from bit_quantized_attention_smooth_amd.workloads import varlen_workload
+    banner("varlen full size")
+    x, w = varlen_workload("varlen_gqa_causal_b8h32kv8t16384d128")
+    dev = device()
+    o = sage.sageattn_varlen(x["q"].to(dev), x["k"].to(dev), x["v"].to(dev), x["cu_q"].to(dev), x["cu_k"].to(dev),
+                             w["max_seqlen"], w["max_seqlen"], causal=True, sm_scale=w["sm_scale"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    cu = x["cu_q"].numpy()
+    for b in (0, len(cu) - 2):
+        sl = slice(cu[b], cu[b + 1])
+        sub = {n: _f32(x[n][sl]) for n in "qkv"}
+        n = cu[b + 1] - cu[b]
+        c = np.array([0, n], np.int32)
+        o_sim, _, _ = oracle.attn_varlen(sub["q"], sub["k"], sub["v"], c, c, True, w["sm_scale"], tile=TILE)
+        og = to_np64(o[sl])
+        assert np.abs(og - o_sim).max() <= 2e-2
+        assert cos(og, o_sim) >= 0.9999
