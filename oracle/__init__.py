@@ -41,6 +41,10 @@ def lib():
         L.or_e2m1_encode.argtypes = [ctypes.c_double]
         L.or_mx_scale_byte.restype = ctypes.c_uint8
         L.or_mx_scale_byte.argtypes = [ctypes.c_double, ctypes.c_int]
+        L.or_f16_decode.restype = ctypes.c_double
+        L.or_f16_decode.argtypes = [ctypes.c_uint16]
+        L.or_f16_encode.restype = ctypes.c_uint16
+        L.or_f16_encode.argtypes = [ctypes.c_double]
         L.or_int8_encode.restype = ctypes.c_int8
         L.or_int8_encode.argtypes = [ctypes.c_float, ctypes.c_float]
         _lib = L
@@ -87,12 +91,23 @@ def mx_scale_byte(amax, emax):
     return int(lib().or_mx_scale_byte(float(amax), int(emax)))
 
 
+def f16_encode(x):
+    f = lib().or_f16_encode
+    return np.array([f(float(v)) for v in np.ravel(x)], np.uint16).reshape(np.shape(x))
+
+
+def f16_decode(c):
+    f = lib().or_f16_decode
+    return np.array([f(int(v)) for v in np.ravel(c)], np.float64).reshape(np.shape(c))
+
+
 def int8_encode(x, delta):
     return int(lib().or_int8_encode(float(x), float(delta)))
 
 
-def quant_int8_fp8(q, k, v, sm, blk=64):
-    """Prologue of the INT8/FP8 path: q [BH,Nq,d], k and v [BH,Nk,d] float32."""
+def quant_int8_fp8(q, k, v, sm, blk=64, pv_fmt="fp8"):
+    """Prologue of the INT8 path: q [BH,Nq,d], k and v [BH,Nk,d] float32.  pv_fmt "fp8": FP8 V
+    codes with per-channel steps; "f16": V as fp16 codes (vh) for the 16-bit P~V fallback."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     BH, Nq, d = q.shape
     Nk = k.shape[1]
@@ -104,6 +119,10 @@ def quant_int8_fp8(q, k, v, sm, blk=64):
     lib().or_quant_int8_fp8_x(_p(q), _p(k), _p(v), BH, Nq, Nk, d, blk, ctypes.c_double(sm),
                               _p(r["mu_k"]), _p(r["qc"]), _p(r["qs"]), _p(r["kc"]), _p(r["ks"]),
                               _p(r["vc"]), _p(r["vs"]), _p(r["corr"]))
+    r["pv_fmt"] = pv_fmt
+    if pv_fmt == "f16":
+        r["vh"] = np.empty((BH, Nk, d), np.uint16)
+        lib().or_quant_v_f16(_p(v), ctypes.c_int64(v.size), _p(r["vh"]))
     return r
 
 
@@ -137,15 +156,20 @@ def _rows(rows, N):
 
 
 def attn_int8_fp8(qz, N, d, causal, sm, tile, rows=None, blk=64):
-    """Tiled quantized forward (INT8 QK, FP8 P~V) on a quant_int8_fp8 result (N = query rows)."""
+    """Tiled quantized forward (INT8 QK; FP8 or fp16 P~V) on a quant_int8_fp8 result (N = query rows)."""
     BH, Nq, Nk = qz["qc"].shape[0], qz["qc"].shape[1], qz["kc"].shape[1]
     assert N == Nq
     rows = _rows(rows, N)
     out = np.empty((BH, len(rows), d), np.float64)
     lse = np.empty((BH, len(rows)), np.float64)
-    lib().or_attn_int8_fp8_x(_p(qz["qc"]), _p(qz["qs"]), _p(qz["kc"]), _p(qz["ks"]), _p(qz["vc"]),
-                             _p(qz["vs"]), _p(qz["corr"]), BH, Nq, Nk, d, blk, tile, int(causal),
-                             ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
+    if qz.get("pv_fmt", "fp8") == "f16":
+        lib().or_attn_int8_f16_x(_p(qz["qc"]), _p(qz["qs"]), _p(qz["kc"]), _p(qz["ks"]), _p(qz["vh"]),
+                                 _p(qz["corr"]), BH, Nq, Nk, d, blk, tile, int(causal),
+                                 ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
+    else:
+        lib().or_attn_int8_fp8_x(_p(qz["qc"]), _p(qz["qs"]), _p(qz["kc"]), _p(qz["ks"]), _p(qz["vc"]),
+                                 _p(qz["vs"]), _p(qz["corr"]), BH, Nq, Nk, d, blk, tile, int(causal),
+                                 ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
     return out, lse
 
 
@@ -229,7 +253,7 @@ def attn_varlen(q, k, v, cu_q, cu_k, causal, sm, qk_fmt="int8", pv_fmt="fp8", ti
             ob, lb = attn_ref(qs, ks, vs, causal, sm)
             qz = None
         elif qk_fmt == "int8":
-            qz = quant_int8_fp8(qs, ks, vs, sm)
+            qz = quant_int8_fp8(qs, ks, vs, sm, pv_fmt=pv_fmt)
             ob, lb = attn_int8_fp8(qz, q1 - q0, d, causal, sm, tile)
         else:
             qz = quant_mxfp4(qs, ks, vs, sm, pv_fmt=pv_fmt)

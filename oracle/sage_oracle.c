@@ -125,6 +125,53 @@ OR_API uint8_t or_e4m3_encode(double x)
     return s | (uint8_t)(((Ev + 7) << 3) | mant);
 }
 
+/* IEEE binary16 decode: bias 15, 10 mantissa bits, subnormals, e = 31 inf / NaN. */
+OR_API double or_f16_decode(uint16_t c)
+{
+    int s = c >> 15, e = (c >> 10) & 31, m = c & 1023;
+    double v;
+    if (e == 31)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -24);                 /* m/1024 * 2^-14 */
+    else
+        v = ldexp((double)(1024 + m), e - 25);     /* (1 + m/1024) * 2^(e-15) */
+    return s ? -v : v;
+}
+
+/* IEEE binary16 encode: round to nearest, ties to even; magnitudes that round past the
+ * largest finite value (65504) become infinity, as IEEE rounding does. */
+OR_API uint16_t or_f16_encode(double x)
+{
+    uint16_t s = signbit(x) ? 0x8000 : 0x0000;
+    if (isnan(x))
+        return s | 0x7E00;
+    double a = fabs(x);
+    if (a == 0.0)
+        return s;
+    int E = floor_log2(a);
+    if (E < -14)
+        E = -14;                                   /* subnormal range shares 2^-14's quantum */
+    double quantum = ldexp(1.0, E - 10);
+    double v = rint(a / quantum) * quantum;        /* RNE to 11 significant bits */
+    if (v >= 65536.0)
+        return s | 0x7C00;                         /* overflow: infinity */
+    if (v == 0.0)
+        return s;
+    int Ev = floor_log2(v);
+    if (Ev < -14)
+        return s | (uint16_t)(v / ldexp(1.0, -24));  /* subnormal: exponent field 0 */
+    int mant = (int)(v / ldexp(1.0, Ev - 10)) - 1024;
+    return s | (uint16_t)(((Ev + 15) << 10) | mant);
+}
+
+/* V as fp16 codes (the 16-bit P~V fallback): out[i] = fl16(v[i]). */
+OR_API void or_quant_v_f16(const float *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = or_f16_encode((double)v[i]);
+}
+
 /* E2M1 decode: magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}. */
 OR_API double or_e2m1_decode(uint8_t c)
 {
@@ -391,7 +438,7 @@ OR_API void or_quant_mxfp4(const float *q, const float *k, const float *v,
 /* ------------------------------------------------------------------ */
 
 enum { QK_EXACT = 0, QK_INT8 = 1, QK_MXFP4 = 3 };
-enum { PV_EXACT = 0, PV_FP8 = 2, PV_MXFP4 = 3, PV_MXFP8 = 4 };
+enum { PV_EXACT = 0, PV_FP8 = 2, PV_MXFP4 = 3, PV_MXFP8 = 4, PV_F16 = 5 };
 
 typedef struct {
     int N, d, causal, tile, blk;   /* N: keys (query rows are passed explicitly) */
@@ -411,6 +458,7 @@ typedef struct {
     const uint8_t *vc;         /* PV_FP8, PV_MXFP4 or PV_MXFP8 codes */
     const float *vs;           /* PV_FP8 per-channel scale */
     const uint8_t *ve;         /* PV_MXFP4 / PV_MXFP8 E8M0 bytes [ceil(N/32), d] */
+    const uint16_t *vh;        /* PV_F16 fp16 codes */
     const double *corr;        /* per-row LSE correction (may be NULL) */
 } head_t;
 
@@ -452,6 +500,8 @@ static double vval(const head_t *H, int j, int c)
         return H->vx[idx];
     if (H->pv == PV_FP8)
         return or_e4m3_decode(H->vc[idx]);
+    if (H->pv == PV_F16)
+        return or_f16_decode(H->vh[idx]);
     double e = ldexp(1.0, (int)H->ve[(int64_t)(j / 32) * H->d + c] - 127);
     if (H->pv == PV_MXFP8)
         return or_e4m3_decode(H->vc[idx]) * e;
@@ -500,6 +550,10 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
             /* static x448 scale: p <= 1 fills the E4M3 range */
             for (int jj = 0; jj < n; jj++)
                 pq[jj] = or_e4m3_decode(or_e4m3_encode(448.0 * p[jj]));
+        } else if (H->pv == PV_F16) {
+            /* 16-bit P~: p itself rounded to fp16 */
+            for (int jj = 0; jj < n; jj++)
+                pq[jj] = or_f16_decode(or_f16_encode(p[jj]));
         } else if (pmax == 0.0) {
             for (int jj = 0; jj < n; jj++)
                 pq[jj] = 0.0;
@@ -587,6 +641,25 @@ OR_API void or_attn_int8_fp8_x(const int8_t *qc, const float *qs, const int8_t *
                         .qk = QK_INT8, .pv = PV_FP8,
                         .qc = qc + offq, .kc = kc + offk, .qs = qs + (int64_t)h * nbq, .ks = ks + (int64_t)h * nbk,
                         .vc = vc + offk, .vs = vs + (int64_t)h * d, .corr = corr + (int64_t)h * Nq};
+    }
+    run_rows(H, BH, rows, nrows, out, lse);
+    free(H);
+}
+
+/* The same with fp16 P~ and V (vh [BH,Nk,d] fp16 codes from or_quant_v_f16). */
+OR_API void or_attn_int8_f16_x(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks,
+                               const uint16_t *vh, const double *corr,
+                               int BH, int Nq, int Nk, int d, int blk, int tile, int causal, double sm,
+                               const int *rows, int nrows, double *out, double *lse)
+{
+    int nbq = (Nq + blk - 1) / blk, nbk = (Nk + blk - 1) / blk;
+    head_t *H = calloc((size_t)BH, sizeof(head_t));
+    for (int h = 0; h < BH; h++) {
+        int64_t offq = (int64_t)h * Nq * d, offk = (int64_t)h * Nk * d;
+        H[h] = (head_t){.N = Nk, .d = d, .causal = causal, .tile = tile, .blk = blk, .sm = sm,
+                        .qk = QK_INT8, .pv = PV_F16,
+                        .qc = qc + offq, .kc = kc + offk, .qs = qs + (int64_t)h * nbq, .ks = ks + (int64_t)h * nbk,
+                        .vh = vh + offk, .corr = corr + (int64_t)h * Nq};
     }
     run_rows(H, BH, rows, nrows, out, lse);
     free(H);

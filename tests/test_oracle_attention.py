@@ -181,11 +181,19 @@ def _lossless_mx8_v(rng, BH, N, d):
     return v.astype(np.float32)
 
 
+def _lossless_f16_v(rng, BH, N, d):
+    """V exactly on the fp16 grid (11 significant bits, normal range)."""
+    m = rng.integers(1024, 2048, size=(BH, N, d)) * rng.choice([-1.0, 1.0], size=(BH, N, d))
+    return (m * 2.0 ** rng.integers(-14, -4, size=(BH, N, d))).astype(np.float32)
+
+
 def _lossless_v(rng, BH, N, d, pv_fmt):
     if pv_fmt == "mxfp4":
         return _lossless_mx_v(rng, BH, N, d)
     if pv_fmt == "mxfp8":
         return _lossless_mx8_v(rng, BH, N, d)
+    if pv_fmt == "f16":
+        return _lossless_f16_v(rng, BH, N, d)
     return _lossless_fp8_v(rng, BH, N, d)
 
 
@@ -212,13 +220,14 @@ def _int8_score_design(rng, BH, N, d, blk=64):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("tile", [32, 64, 128])
-def test_int8_fp8_sim_is_exact_on_lossless_grid(orc, causal, tile):
+@pytest.mark.parametrize("pv_fmt", ["fp8", "f16"])
+def test_int8_fp8_sim_is_exact_on_lossless_grid(orc, causal, tile, pv_fmt):
     rng = np.random.default_rng(21)
     BH, N, d = 2, 160, 64
     q, k = _int8_score_design(rng, BH, N, d)
-    v = _lossless_fp8_v(rng, BH, N, d)
+    v = _lossless_v(rng, BH, N, d, pv_fmt)
     sm = LN2                                               # p takes the values 2^0, 2^-1, 2^-2
-    qz = orc.quant_int8_fp8(q, k, v, sm)
+    qz = orc.quant_int8_fp8(q, k, v, sm, pv_fmt=pv_fmt)
     o, lse = orc.attn_int8_fp8(qz, N, d, causal, sm, tile)
     o_ref, lse_ref = orc.attn_ref(q, k, v, causal, sm)
     assert np.allclose(lse, lse_ref, rtol=0, atol=1e-12)
@@ -318,7 +327,7 @@ def test_mxfp4_scores_exact_on_random_lossless_codes(orc):
         assert np.allclose(lse, lse_ref, rtol=0, atol=1e-11)
 
 
-@pytest.mark.parametrize("path", ["int8_fp8", "mxfp4_mxfp4", "mxfp4_fp8", "mxfp4_mxfp8"])
+@pytest.mark.parametrize("path", ["int8_fp8", "int8_f16", "mxfp4_mxfp4", "mxfp4_fp8", "mxfp4_mxfp8"])
 def test_constant_keys_give_mean_of_values(orc, path):
     """K constant along tokens: smoothing zeroes it, every score is 0, p = 1, and O is
     the (prefix) mean of the dequantized V, exact on grid V."""
@@ -328,8 +337,8 @@ def test_constant_keys_give_mean_of_values(orc, path):
     k = np.repeat(_rand((BH, 1, d), 43, 3.0), N, axis=1)
     v = _lossless_v(rng, BH, N, d, path.split("_")[1])
     for causal in (False, True):
-        if path == "int8_fp8":
-            qz = orc.quant_int8_fp8(q, k, v, 0.1)
+        if path.startswith("int8"):
+            qz = orc.quant_int8_fp8(q, k, v, 0.1, pv_fmt=path.split("_")[1])
             assert not qz["kc"].any()
             o, _ = orc.attn_int8_fp8(qz, N, d, causal, 0.1, 64)
         else:
@@ -375,11 +384,16 @@ def test_int8_fp8_sim_accuracy_vs_exact(orc):
     x = make_inputs(1, 2, 256, 64, dtype="f16", seed=0, k_off_std=4.0)
     q, k, v = (orc.widen(as_u16(x[n]), "f16").reshape(2, 256, 64) for n in "qkv")
     for causal in (False, True):
-        qz = orc.quant_int8_fp8(q, k, v, 0.125)
-        o, lse = orc.attn_int8_fp8(qz, 256, 64, causal, 0.125, 64)
-        o_ref, lse_ref = orc.attn_ref(q, k, v, causal, 0.125)
-        assert _cos(o, o_ref) > 0.999
-        assert np.abs(lse - lse_ref).max() < 0.05
+        cs = {}
+        for pv in ("fp8", "f16"):
+            qz = orc.quant_int8_fp8(q, k, v, 0.125, pv_fmt=pv)
+            o, lse = orc.attn_int8_fp8(qz, 256, 64, causal, 0.125, 64)
+            o_ref, lse_ref = orc.attn_ref(q, k, v, causal, 0.125)
+            cs[pv] = _cos(o, o_ref)
+            assert cs[pv] > 0.999
+            assert np.abs(lse - lse_ref).max() < 0.05
+        # the 16-bit P~V fallback is the more accurate one: only QK is quantized coarsely
+        assert cs["f16"] > cs["fp8"]
 
 
 def test_mxfp4_sim_accuracy_vs_exact(orc):

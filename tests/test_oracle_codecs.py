@@ -159,3 +159,30 @@ def test_mx_e4m3_v_groups_against_frexp_and_torch(orc):
                 y = np.clip(blk[:, c] * 2.0 ** -e, -448.0, 448.0)
                 want = torch.from_numpy(y.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
                 assert np.array_equal(r["vc"][h, g0:g0 + 32, c], want)
+
+
+def test_f16_decode_all_codes_against_numpy(orc):
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    want = codes.view(np.float16).astype(np.float64)
+    got = orc.f16_decode(codes)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_f16_encode_against_numpy_rounding(orc):
+    """Round to nearest even with subnormals and overflow to infinity, checked against
+    numpy's float64 -> float16 conversion on random values, exact ties and the edges."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(20000) * 2.0 ** rng.integers(-30, 18, size=20000)
+    grid = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    grid = grid[np.isfinite(grid)]
+    g = np.sort(np.unique(np.abs(grid)))
+    ties = (g[:-1] + g[1:]) / 2                              # exact midpoints (ties)
+    edges = np.array([65504.0, 65519.99, 65520.0, 65536.0, 1e6, 2.0 ** -24, 2.0 ** -25, 2.0 ** -26, 0.0, -0.0])
+    x = np.concatenate([x, ties[::7], -ties[::11], edges, -edges])
+    with np.errstate(over="ignore"):                          # the overflow cases are intended
+        want = x.astype(np.float16).view(np.uint16)
+    got = orc.f16_encode(x)
+    assert np.array_equal(got, want)
