@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 HEADLINE = "int8_fp8_causal_b1h32n4096d128"
 METRIC = "attention TOPS (4·B·H·N²·d/s, ½ if causal) at d=128; % of MI355X MFMA peak"
 # MI355X dense peaks (TFLOP/s or TOP/s)
-PEAK = {"int8_fp8": 5000.0, "mxfp4_fp8": 1.0 / (0.5 / 10100.0 + 0.5 / 5000.0), "mxfp4_mxfp4": 10100.0}
+PEAK = {"int8_fp8": 5000.0, "mxfp4_fp8": 1.0 / (0.5 / 10100.0 + 0.5 / 5000.0), "mxfp4_mxfp4": 10100.0,
+        "int8_f16": 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0)}   # half the ops on each product's matrix path
 HBM_PEAK_GBS = 8000.0
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_int8_fp8_causal_b1h32n4096d128.txt")
@@ -162,7 +163,7 @@ def run_workload(name, S, torch, steps, warmup, pv="fp8"):
     # plus the scales (INT8: 4 B per 64 tokens; MXFP4: 1 B per 32 elements) and the per-token LSE term
     # (MXFP4 V: 0.5 B codes + 1 B per 32 tokens and channel; MXFP8 V: 1 B codes + the same E8M0 bytes;
     # FP8 V: 1 B codes + a fp32 step per channel)
-    v_b = E if pv == "fp8" else (E // 2 if pv == "mxfp4" else E) + E // 32
+    v_b = {"fp8": E, "f16": 2 * E}.get(pv, (E // 2 if pv == "mxfp4" else E) + E // 32)
     code_b = (2 * E + v_b) if qk == "int8" else (2 * (E // 2 + E // 32) + v_b)
     scale_b = (2 * 4 * B * H * ((N + 63) // 64) if qk == "int8" else 4 * B * H * N) + \
         (4 * B * H * d if pv == "fp8" else 0) + 4 * B * H * N
@@ -308,14 +309,16 @@ def main():
     }
     if not args.no_extra:
         extra = {}
-        for name, pv in (("int8_fp8_b1h32n8192d128", "fp8"), ("int8_fp8_causal_b1h32n16384d128", "fp8"),
+        for name, pv in (("int8_fp8_b1h32n8192d128", "fp8"), ("int8_fp8_b1h32n8192d128", "f16"),
+                         ("int8_fp8_causal_b1h32n16384d128", "fp8"),
                          ("mxfp4_b4h32n8192d128", "fp8"), ("mxfp4_b4h32n8192d128", "mxfp4"),
                          ("mxfp4_b4h32n8192d128", "mxfp8"), ("int8_fp8_b2h24n16384d64", "fp8")):
             log(f"[bench] secondary {name} (P~V {pv})")
             e = run_workload(name, S, torch, max(5, args.steps // 5), 3, pv=pv)
             # FP8 and MXFP8 V both run the P~V product on the FP8 matrix path
-            pk = PEAK["int8_fp8" if e["qk"] == "int8" else ("mxfp4_mxfp4" if pv == "mxfp4" else "mxfp4_fp8")]
-            key = name if pv == "fp8" or e["qk"] == "int8" else name + "+pv_" + pv
+            pk = PEAK[("int8_f16" if pv == "f16" else "int8_fp8") if e["qk"] == "int8" else
+                      ("mxfp4_mxfp4" if pv == "mxfp4" else "mxfp4_fp8")]
+            key = name if pv == "fp8" else name + "+pv_" + pv
             extra[key] = {"kernel_tops": round(e["kernel_tops"], 1), "frac": round(e["kernel_tops"] / pk, 4),
                            "step_tops": round(e["step_tops"], 1), "kernel_ms": round(e["ms_kernel"], 4),
                            "prologue_GB/s": round(e["prologue_gbs"], 1)}

@@ -72,10 +72,15 @@ struct Geo {
   static constexpr int SBYTES = QK == QK_MXFP4 ? kTK * (D / 32) : 0;    // E8M0 bytes per tile
   static constexpr int DSBYTES = QK == QK_MXFP4 ? kTK * 4 : 0;          // scaled dS floats per tile
   static constexpr int KSTAGE = KBYTES + SBYTES;
-  // V^T tile: FP8 / MXFP8 (64 bytes per channel) or MXFP4 (32 bytes per channel); the MX
-  // formats then carry one E8M0 byte per channel for each of the two 32-key groups
-  static constexpr int VBYTES = PV == PV_MXFP4 ? D * kTK / 2 : D * kTK;
-  static constexpr int VSB = PV == PV_FP8 ? 0 : 2 * D;
+  // V^T tile: FP8 / MXFP8 (64 bytes per channel), MXFP4 (32 bytes per channel) or fp16 (128
+  // bytes per channel); the MX formats then carry one E8M0 byte per channel for each of the
+  // two 32-key groups
+  static constexpr int VBYTES = PV == PV_MXFP4 ? D * kTK / 2 : PV == PV_F16 ? D * kTK * 2 : D * kTK;
+  static constexpr int VSB = PV == PV_MXFP4 || PV == PV_MXFP8 ? 2 * D : 0;
+  static constexpr int VOPS = PV == PV_F16 ? 4 : 2;                    // V operand reads per block
+  static constexpr int PVM = PV == PV_F16 ? 4 : 1;                     // PV MFMAs per block and tile
+  // log2 of the static P~ scale folded into exp2: 448 fills E4M3; fp16 takes p itself
+  static constexpr float PLOG2 = PV == PV_F16 ? 0.0f : kLog2_448;
   static constexpr int DSOFF = VBYTES + VSB;                            // scaled dS after V
   static constexpr int VSTAGE = DSOFF + DSBYTES;
   static constexpr int KCHUNKS = KBYTES / 16;                           // 16-byte chunks per K tile
@@ -116,6 +121,7 @@ __device__ __forceinline__ int swz(int r) {
 }
 __device__ __forceinline__ int swz_v(int r) { return (r >> 2) & 3; }     // V^T rows of 64 bytes
 __device__ __forceinline__ int swz_v4(int r) { return (r >> 3) & 1; }    // MXFP4 V^T rows of 32 bytes
+__device__ __forceinline__ int swz_v16(int r) { return (r >> 1) & 7; }   // fp16 V^T rows of 128 bytes
 
 template <int DT>
 __device__ __forceinline__ uint32_t pack2_io(float a, float b) {
@@ -149,8 +155,8 @@ struct LaneOffs {
   uint32_t vld[VL];                 // direct-load source offsets inside a V^T tile
   uint32_t kop[2][G::NQF];          // LDS offsets of the K operand reads (subtile, chunk)
   uint32_t ksc[2][G::NQF];          // MXFP4: LDS offsets of the K scale bytes
-  uint32_t vop[G::NCB][2];          // LDS offsets of the V^T operand reads: FP8 / MXFP8 (block,
-                                    // 16-byte chunk); MXFP4 (block, {codes, scale byte})
+  uint32_t vop[G::NCB][G::VOPS];    // LDS offsets of the V^T operand reads: FP8 / MXFP8 / fp16
+                                    // (block, 16-byte chunk); MXFP4 (block, {codes, scale byte})
   uint32_t vsc;                     // MXFP8: LDS offset of block 0's E8M0 byte (+32 per block)
 
   __device__ __forceinline__ void init(int w, int lane, int n, int hh) {
@@ -166,6 +172,9 @@ struct LaneOffs {
       if (PV == PV_MXFP4) {
         const int row = P >> 1, col = (P & 1) ^ swz_v4(row);
         vld[i] = row * 32 + col * 16;
+      } else if (PV == PV_F16) {
+        const int row = P >> 3, col = (P & 7) ^ swz_v16(row);
+        vld[i] = row * 128 + col * 16;
       } else {
         const int row = P >> 2, col = (P & 3) ^ swz_v(row);
         vld[i] = row * 64 + col * 16;
@@ -191,6 +200,10 @@ struct LaneOffs {
         // half hh: keys 16 hh + [0, 16) (block 0), then 32 + 16 hh + [0, 16) (block 1)
         vop[c][0] = row * 64 + ((hh ^ swz_v(row)) << 4);
         vop[c][1] = row * 64 + (((2 + hh) ^ swz_v(row)) << 4);
+      } else if (PV == PV_F16) {
+        // half hh: keys 32 hh + 8 t + [0, 8) for the t-th K = 16 product
+#pragma unroll
+        for (int t = 0; t < G::VOPS; t++) vop[c][t] = row * 128 + (((4 * hh + t) ^ swz_v16(row)) << 4);
       } else {
         vop[c][0] = row * 64 + (((2 * hh) ^ swz_v(row)) << 4);
         vop[c][1] = row * 64 + (((2 * hh + 1) ^ swz_v(row)) << 4);
@@ -211,7 +224,9 @@ struct LaneOffs {
         if (QK == QK_MXFP4) asm volatile("" : "+v"(ksc[s][c]));
       }
 #pragma unroll
-    for (int c = 0; c < G::NCB; c++) asm volatile("" : "+v"(vop[c][0]), "+v"(vop[c][1]));
+    for (int c = 0; c < G::NCB; c++)
+#pragma unroll
+      for (int t = 0; t < G::VOPS; t++) asm volatile("" : "+v"(vop[c][t]));
   }
 };
 
@@ -388,7 +403,7 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
 #pragma unroll
       for (int cb = 0; cb < NCB; cb++) st.O[cb] *= alpha;
     }
-    off = kLog2_448 - mref;
+    off = G::PLOG2 - mref;
     lsc = 1.0f;
   } else {
     // MXFP4 P~: p' = sigma p with sigma = 6 / max_tile(p) = 6 exp2(m - mt), so p' = exp2(t - mt +
@@ -430,7 +445,25 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
   constexpr int VSLOT = 112 / NQK;                         // vector instructions per MFMA slot
   if (IL) qk_tile<D, QK>(Sn, lk_next, qf, qf4, qsc, lo);
   float ps0 = 0.0f, ps1 = 0.0f;
-  if (PV != PV_MXFP4) {
+  if (PV == PV_F16) {
+    // fp16 P~ = p (RNE), eight keys per K = 16 product, fp32 accumulation
+    v4i ph[4];
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {
+      const float p0 = fast_exp2(fmaf(u[i], c, off)), p1 = fast_exp2(fmaf(u[i + 1], c, off));
+      const float p2 = fast_exp2(fmaf(u[i + 2], c, off)), p3 = fast_exp2(fmaf(u[i + 3], c, off));
+      ps0 += p0 + p1;
+      ps1 += p2 + p3;
+      ph[i / 8][(i % 8) / 2] = pack_f16x2(p0, p1);
+      ph[i / 8][(i % 8) / 2 + 1] = pack_f16x2(p2, p3);
+    }
+    st.l += ps0 + ps1;
+#pragma unroll
+    for (int cb = 0; cb < NCB; cb++)
+#pragma unroll
+      for (int t = 0; t < 4; t++)
+        st.O[cb] = mfma_f16(*reinterpret_cast<const v4i*>(vstage + lo.vop[cb][t]), ph[t], st.O[cb]);
+  } else if (PV != PV_MXFP4) {
     v8i pb;
 #pragma unroll
     for (int i = 0; i < 32; i += 4) {
@@ -490,8 +523,8 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
       __builtin_amdgcn_sched_group_barrier(0x002, VSLOT, 0);    // vector work of tile j
     }
     __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);         // the rest of it
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NCB, 0);    // DS reads: V operands
-    __builtin_amdgcn_sched_group_barrier(0x008, NCB, 0);        // PV MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, G::VOPS * NCB, 0);   // DS reads: V operands
+    __builtin_amdgcn_sched_group_barrier(0x008, G::PVM * NCB, 0);    // PV MFMAs
   }
 }
 
@@ -634,7 +667,7 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
       }
     if (a.lse && hh == 0)
       a.lse[qi.lse0 + qrow] =
-          (st.m + __log2f(lt) - (PV != PV_MXFP4 ? kLog2_448 : kLog2_6)) * kLn2 + a.lse_corr[qi.row0 + qrow];
+          (st.m + __log2f(lt) - (PV != PV_MXFP4 ? G::PLOG2 : kLog2_6)) * kLn2 + a.lse_corr[qi.row0 + qrow];
   }
 }
 
@@ -642,7 +675,8 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
 // first: the dispatcher starts workgroups in id order as slots free up, which makes this a
 // longest-first greedy schedule (a slot that runs faster, e.g. the older of the two
 // workgroups sharing a CU, simply takes more of the short tiles at the end).  Each XCD takes
-// whole heads, so a head's K/V tiles stay in one L2.
+// whole heads, so a head's K/V tiles stay in one L2 (packed sequences: whole KV groups,
+// dealt round-robin so that every XCD gets a share of every sequence).
 template <int D, int QK, bool CAUSAL, int DT, int PV>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   using G = Geo<D, QK, PV>;
@@ -650,7 +684,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   __shared__ __align__(16) uint8_t lv[2][G::VSTAGE];
   const int nqt = a.nqt, BH = a.g.B * a.g.H;
   int bh, qt;
-  if (CAUSAL) {
+  const int nkv = a.g.B * a.g.Hkv;
+  if (a.g.cu_q && nkv % 8 == 0) {
+    // packed sequences differ in length, so an XCD must not take whole sequences: KV instance
+    // x + 8 m goes to XCD x (each XCD gets one KV group of every sequence, and the query heads
+    // sharing a KV head stay in one L2); tiles run longest (highest) first
+    constexpr int X = 8;
+    const int hw = blockIdx.x, x = hw % X, local = hw / X, per = BH / X, grp = a.g.H / a.g.Hkv;
+    qt = nqt - 1 - local / per;
+    const int j = local % per, kv = x + X * (j / grp);
+    bh = (kv / a.g.Hkv) * a.g.H + (kv % a.g.Hkv) * grp + j % grp;
+  } else if (CAUSAL) {
     constexpr int X = 8;
     const int hw = blockIdx.x;
     if (BH % X == 0) {
@@ -700,6 +744,8 @@ hipError_t launch_attn_fwd(const Shape& s, const QuantPtrs& qp, void* o, float* 
   a.nqt = (s.g.nbq * 64) / kQT;   // tiles of 128 queries covering the longest query instance
   a.sm_log2e = s.sm_scale * kLog2e;
   if (s.qk_fmt == QK_INT8) {
+    if (s.pv_fmt == PV_F16)
+      return s.io_dtype == 0 ? fwd_dispatch_d<QK_INT8, 0, PV_F16>(s, a, st) : fwd_dispatch_d<QK_INT8, 1, PV_F16>(s, a, st);
     if (s.pv_fmt != PV_FP8) return hipErrorInvalidValue;
     return s.io_dtype == 0 ? fwd_dispatch_d<QK_INT8, 0, PV_FP8>(s, a, st) : fwd_dispatch_d<QK_INT8, 1, PV_FP8>(s, a, st);
   }

@@ -182,8 +182,14 @@ __device__ __forceinline__ void put_v_fp8(uint8_t* s_vt, int rl, int c0, const f
 // Fixed-length problems without grouped heads (every instance N tokens, query head bh reads
 // KV instance bh): the streamlined codes kernels.
 
-// INT8 Q / K codes and FP8 V.  grid (Np/64, BH), 256 threads.
-template <int DT, int D>
+// Writes this thread's 8 fp16 V values (RNE) of token row `rl` into the [D][64] LDS transpose tile.
+__device__ __forceinline__ void put_v_f16(uint16_t* s_vt, int rl, int c0, const float* x) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) s_vt[(c0 + i) * 64 + rl] = __builtin_bit_cast(uint16_t, (_Float16)x[i]);
+}
+
+// INT8 Q / K codes and FP8 (PV == PV_FP8) or fp16 (PV_F16) V.  grid (Np/64, BH), 256 threads.
+template <int DT, int D, int PV>
 __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                              const uint16_t* __restrict__ v, int N, int Np, int BH,
                                                              float sm, QuantPtrs qp) {
@@ -193,7 +199,8 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
   const size_t base = (size_t)bh * N * D;
   __shared__ float s_mu[D], s_dv[D];
   __shared__ uint32_t s_red[8];
-  __shared__ __align__(16) uint8_t s_vt[D * 64];
+  constexpr int VB = PV == PV_F16 ? 2 : 1;   // bytes per V element
+  __shared__ __align__(16) uint8_t s_vt[D * 64 * VB];
   if (tid < D) {
     const float mu = chunk_mean(qp.sums, 0, BH, bh, D, tid, N);
     const float dvs = chunk_amax(qp.amax_v, BH, bh, D, tid) / 448.0f;
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
     s_dv[tid] = dvs;
     if (blk == 0) {
       qp.mu_k[(size_t)bh * D + tid] = mu;
-      reinterpret_cast<float*>(qp.v_scales)[(size_t)bh * D + tid] = dvs;
+      if (PV == PV_FP8) reinterpret_cast<float*>(qp.v_scales)[(size_t)bh * D + tid] = dvs;
     }
   }
   __syncthreads();
@@ -221,7 +228,10 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
       load8<DT>(q + base + (size_t)row * D + c0, xq[p]);
       load8<DT>(k + base + (size_t)row * D + c0, xk[p]);
       load8<DT>(v + base + (size_t)row * D + c0, xv);
-      put_v_fp8(s_vt, rl, c0, xv, dv, rv);
+      if (PV == PV_F16)
+        put_v_f16(reinterpret_cast<uint16_t*>(s_vt), rl, c0, xv);
+      else
+        put_v_fp8(s_vt, rl, c0, xv, dv, rv);
       float cs = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; i++) {
@@ -239,7 +249,10 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
       for (int i = 0; i < 8; i++) {
         xq[p][i] = 0.0f;
         xk[p][i] = 0.0f;
-        s_vt[(c0 + i) * 64 + rl] = 0;
+        if (PV == PV_F16)
+          reinterpret_cast<uint16_t*>(s_vt)[(c0 + i) * 64 + rl] = 0;
+        else
+          s_vt[(c0 + i) * 64 + rl] = 0;
       }
     }
   }
@@ -265,8 +278,8 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
   }
   __syncthreads();
   // V tile [D][64] -> v_codes[bh][blk][D][64], coalesced 16-byte stores
-  uint8_t* dst = qp.v_codes + ((size_t)bh * (Np / 64) + blk) * D * 64;
-  for (int c = tid; c < D * 4; c += 256)
+  uint8_t* dst = qp.v_codes + ((size_t)bh * (Np / 64) + blk) * D * 64 * VB;
+  for (int c = tid; c < D * 4 * VB; c += 256)
     *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(s_vt + c * 16);
 }
 
@@ -448,7 +461,7 @@ __device__ __forceinline__ CodeBlock code_block(const SeqGeo& g, int i, int t0) 
 
 // Packed sequences or grouped KV heads: INT8 Q / K codes and FP8 V.  grid (blocks of the
 // longest instance, B*H), 256 threads.
-template <int DT, int D>
+template <int DT, int D, int PV>
 __global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                              const uint16_t* __restrict__ v, SeqGeo g, float sm,
                                                              QuantPtrs qp) {
@@ -460,7 +473,8 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t*
   const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
   __shared__ float s_mu[D], s_muq[D], s_dv[D];
   __shared__ uint32_t s_red[8];
-  __shared__ __align__(16) uint8_t s_vt[D * 64];
+  constexpr int VB = PV == PV_F16 ? 2 : 1;   // bytes per V element
+  __shared__ __align__(16) uint8_t s_vt[D * 64 * VB];
   // the KV instance query head i reads is usually instance i itself (no grouping)
   const bool own_kv = kvq == i && cb.ka;
   if (tid < D) {
@@ -471,7 +485,7 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t*
       s_dv[tid] = dvs;
       if (blk == 0) {
         qp.mu_k[(size_t)i * D + tid] = mu;
-        reinterpret_cast<float*>(qp.v_scales)[(size_t)i * D + tid] = dvs;
+        if (PV == PV_FP8) reinterpret_cast<float*>(qp.v_scales)[(size_t)i * D + tid] = dvs;
       }
     }
     if (cb.qa && !own_kv) s_muq[tid] = chunk_mean(qp.sums, 0, BHm, kvq, D, tid, cb.kq.len);
@@ -505,7 +519,10 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t*
       float xv[8];
       unpack8<DT>(gk, xk[p]);
       unpack8<DT>(gv, xv);
-      put_v_fp8(s_vt, rl, c0, xv, dv, rv);
+      if (PV == PV_F16)
+        put_v_f16(reinterpret_cast<uint16_t*>(s_vt), rl, c0, xv);
+      else
+        put_v_fp8(s_vt, rl, c0, xv, dv, rv);
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         xk[p][i] = xk[p][i] - s_mu[c0 + i];
@@ -515,7 +532,10 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t*
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         xk[p][i] = 0.0f;
-        s_vt[(c0 + i) * 64 + rl] = 0;
+        if (PV == PV_F16)
+          reinterpret_cast<uint16_t*>(s_vt)[(c0 + i) * 64 + rl] = 0;
+        else
+          s_vt[(c0 + i) * 64 + rl] = 0;
       }
     }
     // LSE correction: sm * q_t . mu_k (reduced over the C8 threads of this row)
@@ -545,8 +565,8 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t*
   if (cb.ka) {
     __syncthreads();
     // V tile [D][64] -> the instance's tile blk of v_codes [..][D][64], coalesced 16-byte stores
-    uint8_t* dst = qp.v_codes + (cb.ki.tok0 / 64 + blk) * D * 64;
-    for (int c = tid; c < D * 4; c += 256)
+    uint8_t* dst = qp.v_codes + (cb.ki.tok0 / 64 + blk) * D * 64 * VB;
+    for (int c = tid; c < D * 4 * VB; c += 256)
       *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(s_vt + c * 16);
   }
 }
@@ -754,14 +774,20 @@ static hipError_t prologue_dispatch(const void* q, const void* k, const void* v,
   const uint16_t *Q = (const uint16_t*)q, *K = (const uint16_t*)k, *V = (const uint16_t*)v;
   // fixed length without grouped heads: the streamlined codes kernels (N, Np per instance)
   const bool plain = g.cu_q == nullptr && g.Hkv == g.H;
-  dim3 sg(kChunks, BHm), qg(max(g.nbq, g.nbk), BHm);
+  const dim3 sg(kChunks, BHm), qg(max(g.nbq, g.nbk), BHm);
   const bool mx = s.qk_fmt == QK_MXFP4;
   if (!mx) {
-    stats_kernel<DT, D, false, true><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
-    if (plain)
-      quant_int8_fp8_kernel<DT, D><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BHm, s.sm_scale, qp);
-    else
-      quant_int8_fp8_seq_kernel<DT, D><<<qg, 256, 0, st>>>(Q, K, V, g, s.sm_scale, qp);
+    auto codes = [&](auto pv) {
+      constexpr int PV = decltype(pv)::value;
+      // fp16 V needs no channel maxima
+      stats_kernel<DT, D, false, PV == PV_FP8><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
+      if (plain)
+        quant_int8_fp8_kernel<DT, D, PV><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BHm, s.sm_scale, qp);
+      else
+        quant_int8_fp8_seq_kernel<DT, D, PV><<<qg, 256, 0, st>>>(Q, K, V, g, s.sm_scale, qp);
+    };
+    if (s.pv_fmt == PV_F16) codes(std::integral_constant<int, PV_F16>{});
+    else codes(std::integral_constant<int, PV_FP8>{});
     return hipGetLastError();
   }
   if (s.pv_fmt == PV_FP8)

@@ -38,6 +38,16 @@ __device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
 __device__ __forceinline__ v16f mfma_f8(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+// O^T[32 x 32] += A[32 x 16] * B[16 x 32], fp16 in (eight per lane), fp32 accumulate.
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v16f mfma_f16(v4i a, v4i b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+}
+// Two floats -> two fp16 (RNE) in one dword, a in the low half.
+__device__ __forceinline__ int pack_f16x2(float a, float b) {
+  return (int)((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16));
+}
 // Scaled FP8 MFMA with E8M0 block scales on A only (B unscaled: byte 127 = 1.0).  The two
 // 32-element K blocks are bytes [0, 16) and [16, 32) of both lane halves; row m's scale for
 // block b comes from lane m + 32 b.

@@ -7,7 +7,7 @@
 namespace sage {
 
 enum { QK_INT8 = 1, QK_MXFP4 = 3 };
-enum { PV_FP8 = 2, PV_MXFP4 = 3, PV_MXFP8 = 4 };
+enum { PV_FP8 = 2, PV_MXFP4 = 3, PV_MXFP8 = 4, PV_F16 = 5 };
 
 // Padding of the token axis in every quantized buffer (a multiple of the Q tile).
 constexpr int kTokenPad = 128;

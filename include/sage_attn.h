@@ -58,14 +58,18 @@ typedef enum {
  * sharing an E8M0 (power-of-two) scale.  MXFP8: OCP MX with E4M3 elements
  * (scale floor(log2 amax) - 8, elements saturated at 448); as pv_fmt it keeps
  * P~ in FP8 with the static x448 scale (SageAttention3 abstract: microscaling
- * FP4 attention, with 8-bit V as the higher-precision fallback). */
-enum { SAGE_FMT_INT8 = 1, SAGE_FMT_FP8 = 2, SAGE_FMT_MXFP4 = 3, SAGE_FMT_MXFP8 = 4 };
+ * FP4 attention, with 8-bit V as the higher-precision fallback).  F16 (as
+ * pv_fmt, with INT8 QK): the 16-bit P~V fallback of the original SageAttention
+ * (INT8 QK^T with FP16 P and V, review thread, reply to reviewer wwcu W1): P~ and
+ * V rounded to IEEE fp16 (RNE, overflow to infinity), fp32 accumulation -- the
+ * matrix cores have no fp16-accumulating form. */
+enum { SAGE_FMT_INT8 = 1, SAGE_FMT_FP8 = 2, SAGE_FMT_MXFP4 = 3, SAGE_FMT_MXFP8 = 4, SAGE_FMT_F16 = 5 };
 
 /* I/O element types of Q, K, V, O, dO, dQ, dK, dV. */
 enum { SAGE_DT_BF16 = 0, SAGE_DT_F16 = 1 };
 
-/* Supported (qk_fmt, pv_fmt) pairs: (INT8, FP8), (MXFP4, FP8), (MXFP4, MXFP4),
- * (MXFP4, MXFP8). */
+/* Supported (qk_fmt, pv_fmt) pairs: (INT8, FP8), (INT8, F16), (MXFP4, FP8),
+ * (MXFP4, MXFP4), (MXFP4, MXFP8). */
 typedef struct {
     int B, H, N, d;
     int causal;          /* 0 or 1 */
@@ -86,7 +90,8 @@ typedef struct {
  *             MXFP4: E8M0 bytes [BH, Np, d/32] per token per 32 channels
  *   k_codes, k_scales   the same for K - mu_k
  *   v_codes   FP8 and MXFP8 V: E4M3 codes tiled [BH, Np/64, d, 64] (64 tokens
- *             of one channel contiguous);  MXFP4 V: packed E2M1 [BH, Np/64, d, 32]
+ *             of one channel contiguous);  MXFP4 V: packed E2M1 [BH, Np/64, d, 32];
+ *             F16 V: fp16 tiled [BH, Np/64, d, 64]
  *   v_scales  FP8 V: fp32 [BH, d] per-channel step;  MXFP4 and MXFP8 V: E8M0
  *             bytes [BH, Np/32, d] per 32-token group per channel
  *   delta_s   fp32 [BH, Np]    mu_q . (k_t - mu_k), added to every score (MXFP4 QK)

@@ -26,8 +26,8 @@ def unpack_nibbles(packed, n):
     return out[..., :n]
 
 
-def unpack_int8_fp8(buf, p, lay):
-    """Device quant buffer (INT8 QK, FP8 V) -> dict of oracle-shaped arrays."""
+def unpack_int8_fp8(buf, p, lay, pv="fp8"):
+    """Device quant buffer (INT8 QK; FP8 or fp16 V) -> dict of oracle-shaped arrays."""
     b = buf.cpu().numpy()
     BH, N, d = p.B * p.H, p.N, p.d
     Np = (N + 127) // 128 * 128
@@ -40,10 +40,15 @@ def unpack_int8_fp8(buf, p, lay):
     r["ks_all"] = part(b, lay, "k_scales", np.float32, BH * nb).reshape(BH, nb)
     nbn = (N + 63) // 64
     r["qs"], r["ks"] = r["qs_all"][:, :nbn], r["ks_all"][:, :nbn]
-    vt = part(b, lay, "v_codes", np.uint8, BH * Np * d).reshape(BH, Np // 64, d, 64)
-    r["vc_all"] = vt.transpose(0, 1, 3, 2).reshape(BH, Np, d)
-    r["vc"] = r["vc_all"][:, :N]
-    r["vs"] = part(b, lay, "v_scales", np.float32, BH * d).reshape(BH, d)
+    if pv == "f16":
+        vt = part(b, lay, "v_codes", np.uint16, BH * Np * d).reshape(BH, Np // 64, d, 64)
+        r["vh_all"] = vt.transpose(0, 1, 3, 2).reshape(BH, Np, d)
+        r["vh"] = r["vh_all"][:, :N]
+    else:
+        vt = part(b, lay, "v_codes", np.uint8, BH * Np * d).reshape(BH, Np // 64, d, 64)
+        r["vc_all"] = vt.transpose(0, 1, 3, 2).reshape(BH, Np, d)
+        r["vc"] = r["vc_all"][:, :N]
+        r["vs"] = part(b, lay, "v_scales", np.float32, BH * d).reshape(BH, d)
     r["corr"] = part(b, lay, "lse_corr", np.float32, BH * N).reshape(BH, N)
     return r
 

@@ -50,6 +50,9 @@ CASES = [
     ("mxfp4_mxfp8_causal_d64", 1, 2, 333, 64, "bf16", True, "mxfp4", "mxfp8", 6, 5.0, 0.0, 1 / 8),
     ("mxfp4_mxfp8_causal_d128_f16", 1, 2, 700, 128, "f16", True, "mxfp4", "mxfp8", 10, 3.0, 0.01,
      1 / math.sqrt(128)),
+    ("int8_f16pv_causal_ragged_d128", 1, 3, 1000, 128, "bf16", True, "int8", "f16", 1, 5.0, 0.01,
+     1 / math.sqrt(128)),
+    ("int8_f16pv_ragged_d64_f16", 2, 2, 777, 64, "f16", False, "int8", "f16", 2, 3.0, 0.0, 1 / 8),
 ]
 
 
@@ -70,6 +73,8 @@ def _oracle_sim(f, qz_or, qk, pv, N, d, causal, sm, rows=None):
 def _check_codes(r, qz, qk, pv):
     if qk == "int8":
         assert np.array_equal(r["mu_k"], qz["mu_k"])
+        if pv == "f16":
+            assert np.array_equal(r["vh"], qz["vh"]) and not r["vh_all"][:, qz["vh"].shape[1]:].any()
         assert np.array_equal(r["qs"], qz["qs"]) and np.array_equal(r["ks"], qz["ks"])
         assert np.array_equal(r["qc"], qz["qc"]) and np.array_equal(r["kc"], qz["kc"])
         assert not r["qc_all"][:, qz["qc"].shape[1]:].any() and not r["kc_all"][:, qz["kc"].shape[1]:].any()
@@ -78,7 +83,9 @@ def _check_codes(r, qz, qk, pv):
         assert np.array_equal(r["qe"], qz["qe"]) and np.array_equal(r["ke"], qz["ke"])
         assert np.array_equal(r["qc"], qz["qc"]) and np.array_equal(r["kc"], qz["kc"])
         assert np.allclose(r["dS"], qz["dS"], rtol=1e-6, atol=1e-6 * np.abs(qz["dS"]).max())
-    if pv == "fp8":
+    if pv == "f16":
+        pass
+    elif pv == "fp8":
         assert np.array_equal(r["vs"], qz["vs"])
         assert np.array_equal(r["vc"], qz["vc"])
     else:
@@ -97,8 +104,8 @@ def test_prologue_codes_bit_exact(sage, case):
     buf, p, lay = sage.quantize(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv)
     torch.cuda.synchronize()
     if qk == "int8":
-        r = unpack_int8_fp8(buf, p, lay)
-        qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm)
+        r = unpack_int8_fp8(buf, p, lay, pv)
+        qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
     else:
         r = unpack_mxfp4(buf, p, lay, pv)
         qz = oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
@@ -115,7 +122,7 @@ def test_forward_matches_oracle(sage, case):
     torch.cuda.synchronize()
     o = to_np64(o).reshape(B * H, N, d)
     lse = lse.cpu().numpy().reshape(B * H, N).astype(np.float64)
-    qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm) if qk == "int8" else \
+    qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm, pv_fmt=pv) if qk == "int8" else \
         oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
     o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
     o_ref, lse_ref = oracle.attn_ref(f["q"], f["k"], f["v"], causal, sm)
@@ -131,14 +138,14 @@ def test_forward_edge_lengths(sage, N, causal):
     import oracle
     banner(f"edge N={N} causal={causal}")
     for qk, d, pv in (("int8", 64, "fp8"), ("int8", 128, "fp8"), ("mxfp4", 128, "fp8"), ("mxfp4", 64, "mxfp4"),
-                      ("mxfp4", 128, "mxfp8")):
+                      ("mxfp4", 128, "mxfp8"), ("int8", 128, "f16")):
         f, g = _inputs(1, 2, N, d, "bf16", 100 + N, 2.0)
         sm = 1 / math.sqrt(d)
         o, lse = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv,
                                return_lse=True)
         torch.cuda.synchronize()
         o = to_np64(o).reshape(2, N, d)
-        qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm) if qk == "int8" else \
+        qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm, pv_fmt=pv) if qk == "int8" else \
             oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
         o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
         assert np.abs(o - o_sim).max() <= 2e-2, (qk, d, pv)
@@ -197,7 +204,27 @@ def test_forward_constant_keys_mx_pv(sage, causal, pv):
     assert np.all(np.abs(o - want) <= np.abs(want) * 2.0 ** -8 + 1e-5 * np.abs(vdq).max())
 
 
+def test_forward_constant_keys_f16_pv(sage):
+    """INT8 QK with the 16-bit P~V fallback and K constant along tokens: every p is 1 and
+    P~ = fp16(1) = 1 exactly, so O_i is the (prefix) mean of the fp16-rounded V rows."""
+    import oracle
+    for causal in (False, True):
+        banner(f"constant keys f16 P~V causal={causal}")
+        B, H, N, d = 1, 2, 200, 128
+        f, g = _inputs(B, H, N, d, "bf16", 13)
+        g["k"] = g["k"][:, :, :1].expand(-1, -1, N, -1).contiguous()
+        f["k"] = np.repeat(f["k"][:, :1], N, axis=1)
+        o = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, qk_fmt="int8", pv_fmt="f16")
+        torch.cuda.synchronize()
+        o = to_np64(o).reshape(B * H, N, d)
+        vdq = f["v"].astype(np.float16).astype(np.float64)
+        want = np.cumsum(vdq, axis=1) / np.arange(1, N + 1)[None, :, None] if causal else \
+            np.broadcast_to(vdq.mean(axis=1, keepdims=True), vdq.shape)
+        assert np.all(np.abs(o - want) <= np.abs(want) * 2.0 ** -8 + 1e-5 * np.abs(vdq).max())
+
+
 FULL = [("int8_fp8_causal_b1h32n4096d128", "fp8"), ("int8_fp8_b2h24n16384d64", "fp8"),
+        ("int8_fp8_b1h32n8192d128", "f16"),
         ("mxfp4_b4h32n8192d128", "fp8"), ("mxfp4_b4h32n8192d128", "mxfp4"), ("mxfp4_b4h32n8192d128", "mxfp8"),
         ("int8_fp8_b1h2n256d64", "fp8")]
 
@@ -221,9 +248,9 @@ def test_full_size_sampled_rows(sage, name, pv):
     f = {n: oracle.widen(as_u16(sel(x[n])), w["dtype"]).reshape(len(heads), N, d) for n in "qkv"}
     rows = sample_rows(N)
     if qk == "int8":
-        qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm)
-        r = unpack_int8_fp8(buf, p, lay)
-        for key in ("qc", "kc", "vc", "qs", "ks", "vs", "mu_k"):
+        qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
+        r = unpack_int8_fp8(buf, p, lay, pv)
+        for key in ("qc", "kc", "qs", "ks", "mu_k") + (("vh",) if pv == "f16" else ("vc", "vs")):
             assert np.array_equal(r[key][heads], qz[key]), key
     else:
         qz = oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
