@@ -105,21 +105,25 @@ def int8_encode(x, delta):
     return int(lib().or_int8_encode(float(x), float(delta)))
 
 
-def quant_int8_fp8(q, k, v, sm, blk=64, pv_fmt="fp8"):
-    """Prologue of the INT8 path: q [BH,Nq,d], k and v [BH,Nk,d] float32.  pv_fmt "fp8": FP8 V
-    codes with per-channel steps; "f16": V as fp16 codes (vh) for the 16-bit P~V fallback."""
+def quant_int8_fp8(q, k, v, sm, blk=64, pv_fmt="fp8", qblk=None, kblk=None):
+    """Prologue of the INT8 path: q [BH,Nq,d], k and v [BH,Nk,d] float32.  One step per qblk
+    query tokens and per kblk key tokens (both blk unless given).  pv_fmt "fp8": FP8 V codes with
+    per-channel steps; "f16": V as fp16 codes (vh) for the 16-bit P~V fallback."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     BH, Nq, d = q.shape
     Nk = k.shape[1]
-    nbq, nbk = (Nq + blk - 1) // blk, (Nk + blk - 1) // blk
+    qblk = blk if qblk is None else qblk
+    kblk = blk if kblk is None else kblk
+    nbq, nbk = (Nq + qblk - 1) // qblk, (Nk + kblk - 1) // kblk
     r = dict(mu_k=np.empty((BH, d), np.float32), qc=np.empty((BH, Nq, d), np.int8),
              qs=np.empty((BH, nbq), np.float32), kc=np.empty((BH, Nk, d), np.int8),
              ks=np.empty((BH, nbk), np.float32), vc=np.empty((BH, Nk, d), np.uint8),
              vs=np.empty((BH, d), np.float32), corr=np.empty((BH, Nq), np.float64))
-    lib().or_quant_int8_fp8_x(_p(q), _p(k), _p(v), BH, Nq, Nk, d, blk, ctypes.c_double(sm),
+    lib().or_quant_int8_fp8_x(_p(q), _p(k), _p(v), BH, Nq, Nk, d, qblk, kblk, ctypes.c_double(sm),
                               _p(r["mu_k"]), _p(r["qc"]), _p(r["qs"]), _p(r["kc"]), _p(r["ks"]),
                               _p(r["vc"]), _p(r["vs"]), _p(r["corr"]))
     r["pv_fmt"] = pv_fmt
+    r["qblk"], r["kblk"] = qblk, kblk
     if pv_fmt == "f16":
         r["vh"] = np.empty((BH, Nk, d), np.uint16)
         lib().or_quant_v_f16(_p(v), ctypes.c_int64(v.size), _p(r["vh"]))
@@ -162,13 +166,14 @@ def attn_int8_fp8(qz, N, d, causal, sm, tile, rows=None, blk=64):
     rows = _rows(rows, N)
     out = np.empty((BH, len(rows), d), np.float64)
     lse = np.empty((BH, len(rows)), np.float64)
+    qblk, kblk = qz.get("qblk", blk), qz.get("kblk", blk)
     if qz.get("pv_fmt", "fp8") == "f16":
         lib().or_attn_int8_f16_x(_p(qz["qc"]), _p(qz["qs"]), _p(qz["kc"]), _p(qz["ks"]), _p(qz["vh"]),
-                                 _p(qz["corr"]), BH, Nq, Nk, d, blk, tile, int(causal),
+                                 _p(qz["corr"]), BH, Nq, Nk, d, qblk, kblk, tile, int(causal),
                                  ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
     else:
         lib().or_attn_int8_fp8_x(_p(qz["qc"]), _p(qz["qs"]), _p(qz["kc"]), _p(qz["ks"]), _p(qz["vc"]),
-                                 _p(qz["vs"]), _p(qz["corr"]), BH, Nq, Nk, d, blk, tile, int(causal),
+                                 _p(qz["vs"]), _p(qz["corr"]), BH, Nq, Nk, d, qblk, kblk, tile, int(causal),
                                  ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
     return out, lse
 
@@ -252,8 +257,9 @@ def attn_varlen(q, k, v, cu_q, cu_k, causal, sm, qk_fmt="int8", pv_fmt="fp8", ti
         if exact:
             ob, lb = attn_ref(qs, ks, vs, causal, sm)
             qz = None
-        elif qk_fmt == "int8":
-            qz = quant_int8_fp8(qs, ks, vs, sm, pv_fmt=pv_fmt)
+        elif qk_fmt in ("int8", "int8_token"):
+            fine = qk_fmt == "int8_token"
+            qz = quant_int8_fp8(qs, ks, vs, sm, pv_fmt=pv_fmt, qblk=1 if fine else 64, kblk=32 if fine else 64)
             ob, lb = attn_int8_fp8(qz, q1 - q0, d, causal, sm, tile)
         else:
             qz = quant_mxfp4(qs, ks, vs, sm, pv_fmt=pv_fmt)

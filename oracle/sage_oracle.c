@@ -294,16 +294,17 @@ static void quant_mx_group(const float *x, int n, int64_t stride, int elem_fmt,
  * INT8-QK / FP8-PV prologue for BH heads: queries [BH,Nq,d], keys and values
  * [BH,Nk,d] fp32 (Nq = Nk for self-attention).
  *   mu_k [BH,d]; qc [BH,Nq,d], kc [BH,Nk,d] int8; qs [BH,nbq], ks [BH,nbk] fp32
- *   (nb = ceil(N/blk)); vc [BH,Nk,d] E4M3 codes (token-major); vs [BH,d] fp32;
+ *   (nbq = ceil(Nq/qblk), nbk = ceil(Nk/kblk): a step per qblk query tokens and per
+ *   kblk key tokens); vc [BH,Nk,d] E4M3 codes (token-major); vs [BH,d] fp32;
  *   corr [BH,Nq] fp64 = sm * q_i . mu_k (the per-row score shift removed by
  *   smoothing K).
  */
 OR_API void or_quant_int8_fp8_x(const float *q, const float *k, const float *v,
-                                int BH, int Nq, int Nk, int d, int blk, double sm,
+                                int BH, int Nq, int Nk, int d, int qblk, int kblk, double sm,
                                 float *mu_k, int8_t *qc, float *qs, int8_t *kc, float *ks,
                                 uint8_t *vc, float *vs, double *corr)
 {
-    int nbq = (Nq + blk - 1) / blk, nbk = (Nk + blk - 1) / blk;
+    int nbq = (Nq + qblk - 1) / qblk, nbk = (Nk + kblk - 1) / kblk;
 #pragma omp parallel for schedule(dynamic)
     for (int h = 0; h < BH; h++) {
         int64_t offq = (int64_t)h * Nq * d, offk = (int64_t)h * Nk * d;
@@ -314,8 +315,8 @@ OR_API void or_quant_int8_fp8_x(const float *q, const float *k, const float *v,
         for (int t = 0; t < Nk; t++)
             for (int c = 0; c < d; c++)
                 Ks[(int64_t)t * d + c] = K[(int64_t)t * d + c] - mu[c];
-        quant_int8_blocks(Q, Nq, d, blk, qc + offq, qs + (int64_t)h * nbq);
-        quant_int8_blocks(Ks, Nk, d, blk, kc + offk, ks + (int64_t)h * nbk);
+        quant_int8_blocks(Q, Nq, d, qblk, qc + offq, qs + (int64_t)h * nbq);
+        quant_int8_blocks(Ks, Nk, d, kblk, kc + offk, ks + (int64_t)h * nbk);
         for (int c = 0; c < d; c++) {
             float a = absmax(V + c, Nk, d);
             float delta = a / 448.0f;
@@ -340,7 +341,7 @@ OR_API void or_quant_int8_fp8(const float *q, const float *k, const float *v,
                               float *mu_k, int8_t *qc, float *qs, int8_t *kc, float *ks,
                               uint8_t *vc, float *vs, double *corr)
 {
-    or_quant_int8_fp8_x(q, k, v, BH, N, N, d, blk, sm, mu_k, qc, qs, kc, ks, vc, vs, corr);
+    or_quant_int8_fp8_x(q, k, v, BH, N, N, d, blk, blk, sm, mu_k, qc, qs, kc, ks, vc, vs, corr);
 }
 
 /*
@@ -441,7 +442,8 @@ enum { QK_EXACT = 0, QK_INT8 = 1, QK_MXFP4 = 3 };
 enum { PV_EXACT = 0, PV_FP8 = 2, PV_MXFP4 = 3, PV_MXFP8 = 4, PV_F16 = 5 };
 
 typedef struct {
-    int N, d, causal, tile, blk;   /* N: keys (query rows are passed explicitly) */
+    int N, d, causal, tile;        /* N: keys (query rows are passed explicitly) */
+    int qblk, kblk;                /* INT8: tokens per query / key step */
     double sm;
     int qk, pv;
     /* QK_EXACT: fp64 (smoothed) rows and an optional additive key term */
@@ -476,7 +478,7 @@ static double score(const head_t *H, int i, int j)
         int64_t acc = 0;
         for (int c = 0; c < d; c++)
             acc += (int64_t)H->qc[(int64_t)i * d + c] * (int64_t)H->kc[(int64_t)j * d + c];
-        s = (double)H->qs[i / H->blk] * (double)H->ks[j / H->blk] * (double)acc;
+        s = (double)H->qs[i / H->qblk] * (double)H->ks[j / H->kblk] * (double)acc;
     } else {
         int ng = d / 32;
         for (int g = 0; g < ng; g++) {
@@ -630,14 +632,14 @@ static void run_rows(const head_t *heads, int BH, const int *rows, int nrows, do
  * (queries [BH,Nq], keys [BH,Nk]). */
 OR_API void or_attn_int8_fp8_x(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks,
                                const uint8_t *vc, const float *vs, const double *corr,
-                               int BH, int Nq, int Nk, int d, int blk, int tile, int causal, double sm,
+                               int BH, int Nq, int Nk, int d, int qblk, int kblk, int tile, int causal, double sm,
                                const int *rows, int nrows, double *out, double *lse)
 {
-    int nbq = (Nq + blk - 1) / blk, nbk = (Nk + blk - 1) / blk;
+    int nbq = (Nq + qblk - 1) / qblk, nbk = (Nk + kblk - 1) / kblk;
     head_t *H = calloc((size_t)BH, sizeof(head_t));
     for (int h = 0; h < BH; h++) {
         int64_t offq = (int64_t)h * Nq * d, offk = (int64_t)h * Nk * d;
-        H[h] = (head_t){.N = Nk, .d = d, .causal = causal, .tile = tile, .blk = blk, .sm = sm,
+        H[h] = (head_t){.N = Nk, .d = d, .causal = causal, .tile = tile, .qblk = qblk, .kblk = kblk, .sm = sm,
                         .qk = QK_INT8, .pv = PV_FP8,
                         .qc = qc + offq, .kc = kc + offk, .qs = qs + (int64_t)h * nbq, .ks = ks + (int64_t)h * nbk,
                         .vc = vc + offk, .vs = vs + (int64_t)h * d, .corr = corr + (int64_t)h * Nq};
@@ -649,14 +651,14 @@ OR_API void or_attn_int8_fp8_x(const int8_t *qc, const float *qs, const int8_t *
 /* The same with fp16 P~ and V (vh [BH,Nk,d] fp16 codes from or_quant_v_f16). */
 OR_API void or_attn_int8_f16_x(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks,
                                const uint16_t *vh, const double *corr,
-                               int BH, int Nq, int Nk, int d, int blk, int tile, int causal, double sm,
+                               int BH, int Nq, int Nk, int d, int qblk, int kblk, int tile, int causal, double sm,
                                const int *rows, int nrows, double *out, double *lse)
 {
-    int nbq = (Nq + blk - 1) / blk, nbk = (Nk + blk - 1) / blk;
+    int nbq = (Nq + qblk - 1) / qblk, nbk = (Nk + kblk - 1) / kblk;
     head_t *H = calloc((size_t)BH, sizeof(head_t));
     for (int h = 0; h < BH; h++) {
         int64_t offq = (int64_t)h * Nq * d, offk = (int64_t)h * Nk * d;
-        H[h] = (head_t){.N = Nk, .d = d, .causal = causal, .tile = tile, .blk = blk, .sm = sm,
+        H[h] = (head_t){.N = Nk, .d = d, .causal = causal, .tile = tile, .qblk = qblk, .kblk = kblk, .sm = sm,
                         .qk = QK_INT8, .pv = PV_F16,
                         .qc = qc + offq, .kc = kc + offk, .qs = qs + (int64_t)h * nbq, .ks = ks + (int64_t)h * nbk,
                         .vh = vh + offk, .corr = corr + (int64_t)h * Nq};
@@ -670,7 +672,7 @@ OR_API void or_attn_int8_fp8(const int8_t *qc, const float *qs, const int8_t *kc
                              int BH, int N, int d, int blk, int tile, int causal, double sm,
                              const int *rows, int nrows, double *out, double *lse)
 {
-    or_attn_int8_fp8_x(qc, qs, kc, ks, vc, vs, corr, BH, N, N, d, blk, tile, causal, sm, rows, nrows, out, lse);
+    or_attn_int8_fp8_x(qc, qs, kc, ks, vc, vs, corr, BH, N, N, d, blk, blk, tile, causal, sm, rows, nrows, out, lse);
 }
 
 /* Simulation of the MXFP4-QK forward; pv_fmt 3 = MXFP4 P~ and V, 2 = FP8 P~ and V,

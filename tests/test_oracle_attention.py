@@ -433,6 +433,42 @@ def test_sim_accuracy_on_the_pages_stress_distribution(orc):
     assert rel_l1 <= table["FlashAttention3-fp8"][1]
 
 
+def test_token_granularity_at_least_as_accurate_as_block(orc):
+    """The pages rank SageAttention-T (finer Q/K steps) above SageAttention-B (per-block steps) on
+    the stress distribution (tests/golden/kernel_accuracy_table.txt).  The oracle's fine variant --
+    a step per query token and per 32 keys -- must be at least as accurate as 64-token blocks
+    there, in cosine and in relative L1."""
+    from bit_quantized_attention_smooth_amd.workloads import make_inputs, as_u16
+    x = make_inputs(1, 2, 1024, 64, dtype="bf16", seed=9, stress=True)
+    q, k, v = (orc.widen(as_u16(x[n]), "bf16").reshape(2, 1024, 64) for n in "qkv")
+    rows = np.arange(0, 1024, 4, dtype=np.int32)
+    o_ref, _ = orc.attn_ref(q, k, v, False, 0.125, rows=rows)
+    res = {}
+    for name, qb, kb in (("block", 64, 64), ("token", 1, 32)):
+        qz = orc.quant_int8_fp8(q, k, v, 0.125, qblk=qb, kblk=kb)
+        o, _ = orc.attn_int8_fp8(qz, 1024, 64, False, 0.125, 64, rows=rows)
+        res[name] = (_cos(o, o_ref), np.abs(o - o_ref).sum() / np.abs(o_ref).sum())
+    assert res["token"][0] >= res["block"][0]
+    assert res["token"][1] <= res["block"][1]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_int8_token_granularity_sim_exact_on_lossless_grid(orc, causal):
+    """A power-of-two step on every query row (a 127 * 2^-a spike in a channel K leaves at 0)
+    and on every 32-key group: the per-token / per-32-key simulation equals exact attention."""
+    rng = np.random.default_rng(65)
+    BH, N, d = 2, 160, 64
+    q, k = _int8_score_design(rng, BH, N, d, blk=32)
+    q[:, :, 0] = 127 * 2.0 ** -rng.integers(0, 6, size=(BH, N))
+    v = _lossless_fp8_v(rng, BH, N, d)
+    qz = orc.quant_int8_fp8(q, k, v, LN2, qblk=1, kblk=32)
+    assert qz["qs"].shape == (BH, N) and qz["ks"].shape == (BH, N // 32)
+    o, lse = orc.attn_int8_fp8(qz, N, d, causal, LN2, 64)
+    o_ref, lse_ref = orc.attn_ref(q, k, v, causal, LN2)
+    assert np.allclose(lse, lse_ref, rtol=0, atol=1e-12)
+    assert np.allclose(o, o_ref, rtol=1e-12, atol=1e-12 * np.abs(v).max())
+
+
 # ---------------------------------------------------------------- exact backward
 
 def _torch_grads(q, k, v, do, causal, sm):
