@@ -464,6 +464,19 @@ typedef struct {
     const double *corr;        /* per-row LSE correction (may be NULL) */
 } head_t;
 
+/* INT8 QK: the exact integer dot product of the codes of query i and key j. */
+static int64_t int8_dot(const head_t *H, int i, int j)
+{
+    int64_t acc = 0;
+    for (int c = 0; c < H->d; c++)
+        acc += (int64_t)H->qc[(int64_t)i * H->d + c] * (int64_t)H->kc[(int64_t)j * H->d + c];
+    return acc;
+}
+
+/* Whether P~ codes are decided in fp32 from the INT8 scores (see forward_row). */
+static int g_p32 = 1;
+OR_API void or_set_p_decision_fp32(int on) { g_p32 = on; }
+
 /* Unscaled score s_ij (sm not applied). */
 static double score(const head_t *H, int i, int j)
 {
@@ -519,6 +532,7 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
     double *p = malloc(sizeof(double) * (size_t)T);
     double *pq = malloc(sizeof(double) * (size_t)T);
     double m = -INFINITY, l = 0.0;
+    float m32 = -INFINITY;         /* INT8 P~ decisions: the kernel's fp32 running max */
     for (int j0 = 0; j0 < N; j0 += T) {
         if (H->causal && j0 > i)
             break;
@@ -543,6 +557,40 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
                 pmax = p[jj];
         }
         l = alpha * l + psum;
+        /* The P~ codes are quantized values that floating point decides, so on the INT8 paths
+         * (where every input of that decision is reproducible) they are decided in the fused
+         * kernel's fp32 arithmetic: c = fl32(fl32(step_q * fl32(sm * log2 e)) * step_k), the
+         * tile max fl32(score * c) folded into an fp32 running max m, and p = exp2 of the fp32
+         * FMA score * c + (log2 s - m), rounded to fp32 (s = 448 for FP8, 1 for fp16).  Only
+         * the codes come from this; the row sum, the rescales and the LSE stay fp64. */
+        float *p32 = NULL;
+        if (g_p32 && H->qk == QK_INT8 && (H->pv == PV_FP8 || H->pv == PV_F16)) {
+            p32 = malloc(sizeof(float) * (size_t)n);
+            const float sml2e = (float)H->sm * 1.4426950408889634f;
+            const float qstep = H->qs[i / H->qblk] * sml2e;
+            float mt32 = -INFINITY;
+            float *c32 = malloc(sizeof(float) * (size_t)n);
+            int64_t *a32 = malloc(sizeof(int64_t) * (size_t)n);
+            for (int jj = 0; jj < n; jj++) {
+                int j = j0 + jj;
+                float c = qstep * H->ks[j / H->kblk];
+                c32[jj] = c == 0.0f ? 1.0f : c;
+                a32[jj] = int8_dot(H, i, j);
+                if (x[jj] != -INFINITY) {
+                    float t = (float)a32[jj] * c32[jj];
+                    if (t > mt32)
+                        mt32 = t;
+                }
+            }
+            float mnew = m32 > mt32 ? m32 : mt32;
+            m32 = mnew;
+            float mref = mnew == -INFINITY ? 0.0f : mnew;
+            float off = (H->pv == PV_F16 ? 0.0f : 8.807354922057604f) - mref;
+            for (int jj = 0; jj < n; jj++)
+                p32[jj] = x[jj] == -INFINITY ? 0.0f : (float)exp2((double)fmaf((float)a32[jj], c32[jj], off));
+            free(c32);
+            free(a32);
+        }
         /* P~: quantize the tile row */
         double post = 1.0;
         if (H->pv == PV_EXACT) {
@@ -551,11 +599,11 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
         } else if (H->pv == PV_FP8 || H->pv == PV_MXFP8) {
             /* static x448 scale: p <= 1 fills the E4M3 range */
             for (int jj = 0; jj < n; jj++)
-                pq[jj] = or_e4m3_decode(or_e4m3_encode(448.0 * p[jj]));
+                pq[jj] = or_e4m3_decode(or_e4m3_encode(p32 ? (double)p32[jj] : 448.0 * p[jj]));
         } else if (H->pv == PV_F16) {
             /* 16-bit P~: p itself rounded to fp16 */
             for (int jj = 0; jj < n; jj++)
-                pq[jj] = or_f16_decode(or_f16_encode(p[jj]));
+                pq[jj] = or_f16_decode(or_f16_encode(p32 ? (double)p32[jj] : p[jj]));
         } else if (pmax == 0.0) {
             for (int jj = 0; jj < n; jj++)
                 pq[jj] = 0.0;
@@ -589,6 +637,7 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
         for (int c = 0; c < d; c++)
             O[c] = alpha * O[c] + acc[c] * post;
         m = mn;
+        free(p32);
     }
     if (l == 0.0) {
         /* no visible key (an empty key sequence): zero output, LSE -inf */
