@@ -127,14 +127,14 @@ def time_region(fn, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def run_workload(name, S, torch, steps, warmup, pv="fp8"):
+def run_workload(name, S, torch, steps, warmup, pv="fp8", qk=None):
     """Times the full step, the fused kernel alone and the prologue alone (HIP events on the launch stream)."""
     from bit_quantized_attention_smooth_amd.workloads import workload_inputs
     x, w = workload_inputs(name)
     dev = torch.device("cuda:0")
     g = {n: x[n].to(dev) for n in "qkv"}
     B, H, N, d, causal = w["B"], w["H"], w["N"], w["d"], w["causal"]
-    qk = w["qk_fmt"]
+    qk = qk or w["qk_fmt"]
     p = S.problem(B, H, N, d, causal=causal, sm_scale=w["sm_scale"], dtype=g["q"].dtype, qk_fmt=qk, pv_fmt=pv)
     nbytes, _ = S.quant_size(p)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -164,8 +164,9 @@ def run_workload(name, S, torch, steps, warmup, pv="fp8"):
     # (MXFP4 V: 0.5 B codes + 1 B per 32 tokens and channel; MXFP8 V: 1 B codes + the same E8M0 bytes;
     # FP8 V: 1 B codes + a fp32 step per channel)
     v_b = {"fp8": E, "f16": 2 * E}.get(pv, (E // 2 if pv == "mxfp4" else E) + E // 32)
-    code_b = (2 * E + v_b) if qk == "int8" else (2 * (E // 2 + E // 32) + v_b)
-    scale_b = (2 * 4 * B * H * ((N + 63) // 64) if qk == "int8" else 4 * B * H * N) + \
+    code_b = (2 * E + v_b) if qk.startswith("int8") else (2 * (E // 2 + E // 32) + v_b)
+    scale_b = ({"int8": 2 * 4 * B * H * ((N + 63) // 64), "int8_token": 4 * B * H * (N + (N + 31) // 32)}
+               .get(qk, 4 * B * H * N)) + \
         (4 * B * H * d if pv == "fp8" else 0) + 4 * B * H * N
     pro_bytes = 3 * 2 * E + code_b + scale_b
     return dict(name=name, B=B, H=H, N=N, d=d, causal=causal, qk=qk, pv=pv, ms_step=ms_step, wall=wall,
@@ -309,16 +310,18 @@ def main():
     }
     if not args.no_extra:
         extra = {}
-        for name, pv in (("int8_fp8_b1h32n8192d128", "fp8"), ("int8_fp8_b1h32n8192d128", "f16"),
-                         ("int8_fp8_causal_b1h32n16384d128", "fp8"),
+        for name, pv, *qk in (("int8_fp8_b1h32n8192d128", "fp8"), ("int8_fp8_b1h32n8192d128", "f16"),
+                              ("int8_fp8_causal_b1h32n4096d128", "fp8", "int8_token"),
+                              ("int8_fp8_causal_b1h32n16384d128", "fp8"),
                          ("mxfp4_b4h32n8192d128", "fp8"), ("mxfp4_b4h32n8192d128", "mxfp4"),
                          ("mxfp4_b4h32n8192d128", "mxfp8"), ("int8_fp8_b2h24n16384d64", "fp8")):
-            log(f"[bench] secondary {name} (P~V {pv})")
-            e = run_workload(name, S, torch, max(5, args.steps // 5), 3, pv=pv)
+            qk = qk[0] if qk else None
+            log(f"[bench] secondary {name} (P~V {pv}{', QK ' + qk if qk else ''})")
+            e = run_workload(name, S, torch, max(5, args.steps // 5), 3, pv=pv, qk=qk)
             # FP8 and MXFP8 V both run the P~V product on the FP8 matrix path
-            pk = PEAK[("int8_f16" if pv == "f16" else "int8_fp8") if e["qk"] == "int8" else
+            pk = PEAK[("int8_f16" if pv == "f16" else "int8_fp8") if e["qk"].startswith("int8") else
                       ("mxfp4_mxfp4" if pv == "mxfp4" else "mxfp4_fp8")]
-            key = name if pv == "fp8" else name + "+pv_" + pv
+            key = (name if pv == "fp8" else name + "+pv_" + pv) + ("+qk_" + qk if qk else "")
             extra[key] = {"kernel_tops": round(e["kernel_tops"], 1), "frac": round(e["kernel_tops"] / pk, 4),
                            "step_tops": round(e["step_tops"], 1), "kernel_ms": round(e["ms_kernel"], 4),
                            "prologue_GB/s": round(e["prologue_gbs"], 1)}

@@ -326,7 +326,7 @@ struct RowState {
 //   u_i = S_i (INT8: converted to fp32) or S_i + dS_i / c (MXFP4), with c = the positive
 //   log2-domain scale; masked entries are set to -inf; the row max is taken on u, and
 //   p448_i = exp2(u_i * c + (log2 448 - m)) comes out of one FMA and one exp2 per element.
-template <int D, int QK, bool CAUSAL, int PV>
+template <int D, int QK, bool CAUSAL, int PV, bool FINE>
 __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>& Sc, const uint8_t* vstage,
                                             const float* kstep, float qstep, float sm_log2e, int j, int N, int qw,
                                             int qrow, int hh, float* u, float& c, float& off, float& lsc) {
@@ -336,7 +336,8 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
   const bool need_mask = kbase + kTK > N || (CAUSAL && kbase + kTK - 1 > qw);
   float mt;
   if (QK == QK_INT8) {
-    c = qstep * kstep[j];
+    // FINE: this lane's half holds the tile's 32-key group hh, with its own step
+    c = FINE ? qstep * (hh ? kstep[2 * j + 1] : kstep[2 * j]) : qstep * kstep[j];
     // a zero block step means every code of that block is 0, so every unmasked score is 0
     // for any c; keep c positive so that masked entries (-inf) stay -inf after scaling
     c = c == 0.0f ? 1.0f : c;
@@ -355,9 +356,15 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
           im = ok ? max(im, Sc.si[s][r]) : im;
           u[i] = ok ? (float)Sc.si[s][r] : -INFINITY;
         }
-      const int imo = __builtin_bit_cast(int, other_half(__builtin_bit_cast(float, im)));
-      im = max(im, imo);
-      mt = im == INT_MIN ? -INFINITY : (float)im * c;
+      if (FINE) {
+        // the halves scale differently: the row max is taken on the scaled scores
+        const float mo = im == INT_MIN ? -INFINITY : (float)im * c;
+        mt = fmaxf(mo, other_half(mo));
+      } else {
+        const int imo = __builtin_bit_cast(int, other_half(__builtin_bit_cast(float, im)));
+        im = max(im, imo);
+        mt = im == INT_MIN ? -INFINITY : (float)im * c;
+      }
     } else {
       // the row max on the integer scores (c > 0): exact, no NaN handling
       im = Sc.si[0][0];
@@ -368,8 +375,13 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
           im = max(im, Sc.si[s][r]);
           u[16 * s + r] = (float)Sc.si[s][r];
         }
-      const int imo = __builtin_bit_cast(int, other_half(__builtin_bit_cast(float, im)));
-      mt = (float)max(im, imo) * c;
+      if (FINE) {
+        const float mo = (float)im * c;
+        mt = fmaxf(mo, other_half(mo));
+      } else {
+        const int imo = __builtin_bit_cast(int, other_half(__builtin_bit_cast(float, im)));
+        mt = (float)max(im, imo) * c;
+      }
     }
   } else {
     // dS arrives pre-multiplied by sm * log2 e; u = S * sm * log2 e + dS * sm * log2 e, c = 1
@@ -528,7 +540,7 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
   }
 }
 
-template <int D, int QK, bool CAUSAL, int DT, int PV>
+template <int D, int QK, bool CAUSAL, int DT, int PV, bool FINE>
 __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt, uint8_t (*lk)[Geo<D, QK, PV>::KSTAGE],
                                           uint8_t (*lv)[Geo<D, QK, PV>::VSTAGE]) {
   using G = Geo<D, QK, PV>;
@@ -559,7 +571,9 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
     const uint8_t* qp = a.q_codes + (qi.tok0 + qrow) * D + 16 * hh;
 #pragma unroll
     for (int c = 0; c < NQF; c++) qf[c] = *reinterpret_cast<const v4i*>(qp + 32 * c);
-    qstep = reinterpret_cast<const float*>(a.q_scales)[qi.tok0 / kTK + qrow / kTK] * a.sm_log2e;
+    // FINE: a step per query token; else one per 64-token block
+    qstep = reinterpret_cast<const float*>(a.q_scales)[FINE ? qi.tok0 + qrow : qi.tok0 / kTK + qrow / kTK] *
+            a.sm_log2e;
   } else {
     const uint8_t* qp = a.q_codes + (qi.tok0 + qrow) * (D / 2) + 16 * hh;
     const uint8_t* qe = reinterpret_cast<const uint8_t*>(a.q_scales) + (qi.tok0 + qrow) * (D / 32) + hh;
@@ -570,7 +584,8 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
       qsc[c] = qe[2 * c];
     }
   }
-  const float* kstep = reinterpret_cast<const float*>(a.k_scales) + kt0 / kTK;
+  // K steps: one per 64-key tile, or (FINE) one per 32 keys
+  const float* kstep = reinterpret_cast<const float*>(a.k_scales) + (FINE ? kt0 / 32 : kt0 / kTK);
 
   int ntiles = (NK + kTK - 1) / kTK;
   if (CAUSAL) ntiles = min(ntiles, (qbase + kQT - 1) / kTK + 1);
@@ -632,7 +647,7 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
     }
     if (j < wtiles) {
       float u[32], c, off, lsc;
-      softmax_max<D, QK, CAUSAL, PV>(st, Sc, lv[j & 1], kstep, qstep, a.sm_log2e, j, NK, qw, qrow, hh, u, c, off, lsc);
+      softmax_max<D, QK, CAUSAL, PV, FINE>(st, Sc, lv[j & 1], kstep, qstep, a.sm_log2e, j, NK, qw, qrow, hh, u, c, off, lsc);
       softmax_body_pv<D, QK, PV, IL>(st, u, c, off, lsc, Sn, lk[(j + 1) & 1], lv[j & 1], qf, qf4, qsc, lo);
     }
     if (QK == QK_MXFP4) store_ds<D, QK, PV>(dsr, lv[(j + 1) & 1], a.sm_log2e);
@@ -677,7 +692,7 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
 // workgroups sharing a CU, simply takes more of the short tiles at the end).  Each XCD takes
 // whole heads, so a head's K/V tiles stay in one L2 (packed sequences: whole KV groups,
 // dealt round-robin so that every XCD gets a share of every sequence).
-template <int D, int QK, bool CAUSAL, int DT, int PV>
+template <int D, int QK, bool CAUSAL, int DT, int PV, bool FINE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   using G = Geo<D, QK, PV>;
   __shared__ __align__(16) uint8_t lk[2][G::KSTAGE];
@@ -710,22 +725,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     bh = id / nqt;
     qt = id % nqt;
   }
-  run_qtile<D, QK, CAUSAL, DT, PV>(a, bh / a.g.H, bh % a.g.H, qt, lk, lv);
+  run_qtile<D, QK, CAUSAL, DT, PV, FINE>(a, bh / a.g.H, bh % a.g.H, qt, lk, lv);
 }
 
-template <int D, int QK, int DT, int PV>
+template <int D, int QK, int DT, int PV, bool FINE>
 static hipError_t fwd_dispatch(const Shape& s, const FwdArgs& a, hipStream_t st) {
   const int grid = s.g.B * s.g.H * a.nqt;
   if (s.causal)
-    attn_fwd_kernel<D, QK, true, DT, PV><<<grid, 256, 0, st>>>(a);
+    attn_fwd_kernel<D, QK, true, DT, PV, FINE><<<grid, 256, 0, st>>>(a);
   else
-    attn_fwd_kernel<D, QK, false, DT, PV><<<grid, 256, 0, st>>>(a);
+    attn_fwd_kernel<D, QK, false, DT, PV, FINE><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
-template <int QK, int DT, int PV>
+template <int QK, int DT, int PV, bool FINE = false>
 static hipError_t fwd_dispatch_d(const Shape& s, const FwdArgs& a, hipStream_t st) {
-  return s.d == 64 ? fwd_dispatch<64, QK, DT, PV>(s, a, st) : fwd_dispatch<128, QK, DT, PV>(s, a, st);
+  return s.d == 64 ? fwd_dispatch<64, QK, DT, PV, FINE>(s, a, st) : fwd_dispatch<128, QK, DT, PV, FINE>(s, a, st);
+}
+// INT8 QK: per-64-token steps (QK_INT8) or per-token / per-32-key steps (QK_INT8T)
+template <int DT, int PV>
+static hipError_t fwd_dispatch_int8(const Shape& s, const FwdArgs& a, hipStream_t st) {
+  return s.qk_fmt == QK_INT8T ? fwd_dispatch_d<QK_INT8, DT, PV, true>(s, a, st) : fwd_dispatch_d<QK_INT8, DT, PV>(s, a, st);
 }
 
 hipError_t launch_attn_fwd(const Shape& s, const QuantPtrs& qp, void* o, float* lse, hipStream_t st) {
@@ -743,11 +763,11 @@ hipError_t launch_attn_fwd(const Shape& s, const QuantPtrs& qp, void* o, float* 
   a.g = s.g;
   a.nqt = (s.g.nbq * 64) / kQT;   // tiles of 128 queries covering the longest query instance
   a.sm_log2e = s.sm_scale * kLog2e;
-  if (s.qk_fmt == QK_INT8) {
+  if (s.qk_fmt == QK_INT8 || s.qk_fmt == QK_INT8T) {
     if (s.pv_fmt == PV_F16)
-      return s.io_dtype == 0 ? fwd_dispatch_d<QK_INT8, 0, PV_F16>(s, a, st) : fwd_dispatch_d<QK_INT8, 1, PV_F16>(s, a, st);
+      return s.io_dtype == 0 ? fwd_dispatch_int8<0, PV_F16>(s, a, st) : fwd_dispatch_int8<1, PV_F16>(s, a, st);
     if (s.pv_fmt != PV_FP8) return hipErrorInvalidValue;
-    return s.io_dtype == 0 ? fwd_dispatch_d<QK_INT8, 0, PV_FP8>(s, a, st) : fwd_dispatch_d<QK_INT8, 1, PV_FP8>(s, a, st);
+    return s.io_dtype == 0 ? fwd_dispatch_int8<0, PV_FP8>(s, a, st) : fwd_dispatch_int8<1, PV_FP8>(s, a, st);
   }
   if (s.pv_fmt == PV_MXFP4)
     return s.io_dtype == 0 ? fwd_dispatch_d<QK_MXFP4, 0, PV_MXFP4>(s, a, st)

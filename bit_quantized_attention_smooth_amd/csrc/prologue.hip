@@ -189,7 +189,7 @@ __device__ __forceinline__ void put_v_f16(uint16_t* s_vt, int rl, int c0, const 
 }
 
 // INT8 Q / K codes and FP8 (PV == PV_FP8) or fp16 (PV_F16) V.  grid (Np/64, BH), 256 threads.
-template <int DT, int D, int PV>
+template <int DT, int D, int PV, bool FINE>
 __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                              const uint16_t* __restrict__ v, int N, int Np, int BH,
                                                              float sm, QuantPtrs qp) {
@@ -220,6 +220,7 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
   }
   float xq[NP][8], xk[NP][8];
   uint32_t aq = 0, ak = 0;
+  uint32_t akg[2] = {0, 0};   // FINE: |K_s| maxima of the block's two 32-token groups
 #pragma unroll
   for (int p = 0; p < NP; p++) {
     const int rl = r0 + p * RP, row = t0 + rl;
@@ -238,6 +239,7 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
         xk[p][i] = xk[p][i] - s_mu[c0 + i];
         aq = max(aq, __float_as_uint(fabsf(xq[p][i])));
         ak = max(ak, __float_as_uint(fabsf(xk[p][i])));
+        if (FINE) akg[(p * RP) / 32] = max(akg[(p * RP) / 32], __float_as_uint(fabsf(xk[p][i])));
         cs += xq[p][i] * s_mu[c0 + i];
       }
       // LSE correction: sm * q_t . mu_k (reduced over the C8 threads of this row)
@@ -256,12 +258,44 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
       }
     }
   }
-  block_umax2(aq, ak, s_red);
-  const float dq = __uint_as_float(aq) / 127.0f, dk = __uint_as_float(ak) / 127.0f;
-  const float rq = 1.0f / dq, rk = 1.0f / dk;
-  if (tid == 0) {
-    reinterpret_cast<float*>(qp.q_scales)[(size_t)bh * (Np / 64) + blk] = dq;
-    reinterpret_cast<float*>(qp.k_scales)[(size_t)bh * (Np / 64) + blk] = dk;
+  // steps: one per 64-token block for Q and K, or (FINE) one per query token -- the row's
+  // maximum over its C8 threads -- and one per 32-key group
+  float dq_r[NP], rq_r[NP], dk_g[2], rk_g[2];
+  if (FINE) {
+#pragma unroll
+    for (int p = 0; p < NP; p++) {
+      uint32_t a = 0;
+#pragma unroll
+      for (int i = 0; i < 8; i++) a = max(a, __float_as_uint(fabsf(xq[p][i])));
+#pragma unroll
+      for (int o = 1; o < C8; o <<= 1) a = max(a, (uint32_t)__shfl_xor((int)a, o));
+      dq_r[p] = __uint_as_float(a) / 127.0f;
+      rq_r[p] = 1.0f / dq_r[p];
+    }
+    block_umax2(akg[0], akg[1], s_red);
+#pragma unroll
+    for (int g = 0; g < 2; g++) {
+      dk_g[g] = __uint_as_float(akg[g]) / 127.0f;
+      rk_g[g] = 1.0f / dk_g[g];
+    }
+  } else {
+    block_umax2(aq, ak, s_red);
+#pragma unroll
+    for (int p = 0; p < NP; p++) {
+      dq_r[p] = __uint_as_float(aq) / 127.0f;
+      rq_r[p] = 1.0f / dq_r[p];
+    }
+    dk_g[0] = dk_g[1] = __uint_as_float(ak) / 127.0f;
+    rk_g[0] = rk_g[1] = 1.0f / dk_g[0];
+  }
+  if (FINE) {
+#pragma unroll
+    for (int p = 0; p < NP; p++)
+      if ((tid % C8) == 0) reinterpret_cast<float*>(qp.q_scales)[(size_t)bh * Np + t0 + r0 + p * RP] = dq_r[p];
+    if (tid < 2) reinterpret_cast<float*>(qp.k_scales)[(size_t)bh * (Np / 32) + 2 * blk + tid] = dk_g[tid];
+  } else if (tid == 0) {
+    reinterpret_cast<float*>(qp.q_scales)[(size_t)bh * (Np / 64) + blk] = dq_r[0];
+    reinterpret_cast<float*>(qp.k_scales)[(size_t)bh * (Np / 64) + blk] = dk_g[0];
   }
 #pragma unroll
   for (int p = 0; p < NP; p++) {
@@ -269,8 +303,8 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
     uint32_t wq[2] = {0, 0}, wk[2] = {0, 0};
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      wq[i / 4] |= (uint32_t)(uint8_t)int8_code(xq[p][i], dq, rq) << (8 * (i % 4));
-      wk[i / 4] |= (uint32_t)(uint8_t)int8_code(xk[p][i], dk, rk) << (8 * (i % 4));
+      wq[i / 4] |= (uint32_t)(uint8_t)int8_code(xq[p][i], dq_r[p], rq_r[p]) << (8 * (i % 4));
+      wk[i / 4] |= (uint32_t)(uint8_t)int8_code(xk[p][i], dk_g[(p * RP) / 32], rk_g[(p * RP) / 32]) << (8 * (i % 4));
     }
     const size_t off = ((size_t)bh * Np + row) * D + c0;
     *reinterpret_cast<uint2*>(qp.q_codes + off) = make_uint2(wq[0], wq[1]);
@@ -461,7 +495,7 @@ __device__ __forceinline__ CodeBlock code_block(const SeqGeo& g, int i, int t0) 
 
 // Packed sequences or grouped KV heads: INT8 Q / K codes and FP8 V.  grid (blocks of the
 // longest instance, B*H), 256 threads.
-template <int DT, int D, int PV>
+template <int DT, int D, int PV, bool FINE>
 __global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                              const uint16_t* __restrict__ v, SeqGeo g, float sm,
                                                              QuantPtrs qp) {
@@ -500,6 +534,7 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t*
   }
   float xq[NP][8], xk[NP][8];
   uint32_t aq = 0, ak = 0;
+  uint32_t akg[2] = {0, 0};   // FINE: |K_s| maxima of the block's two 32-token groups
 #pragma unroll
   for (int p = 0; p < NP; p++) {
     const int rl = r0 + p * RP, row = t0 + rl;
@@ -527,6 +562,7 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t*
       for (int i = 0; i < 8; i++) {
         xk[p][i] = xk[p][i] - s_mu[c0 + i];
         ak = max(ak, __float_as_uint(fabsf(xk[p][i])));
+        if (FINE) akg[(p * RP) / 32] = max(akg[(p * RP) / 32], __float_as_uint(fabsf(xk[p][i])));
       }
     } else {
 #pragma unroll
@@ -543,12 +579,44 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t*
     for (int o = 1; o < C8; o <<= 1) cs += __shfl_xor(cs, o);
     if ((tid % C8) == 0 && cb.qa && row < cb.qi.len) qp.lse_corr[cb.qi.row0 + row] = sm * cs;
   }
-  block_umax2(aq, ak, s_red);
-  const float dq = __uint_as_float(aq) / 127.0f, dk = __uint_as_float(ak) / 127.0f;
-  const float rq = 1.0f / dq, rk = 1.0f / dk;
-  if (tid == 0) {
-    if (cb.qa) reinterpret_cast<float*>(qp.q_scales)[cb.qi.tok0 / 64 + blk] = dq;
-    if (cb.ka) reinterpret_cast<float*>(qp.k_scales)[cb.ki.tok0 / 64 + blk] = dk;
+  // steps: one per 64-token block for Q and K, or (FINE) one per query token -- the row's
+  // maximum over its C8 threads -- and one per 32-key group
+  float dq_r[NP], rq_r[NP], dk_g[2], rk_g[2];
+  if (FINE) {
+#pragma unroll
+    for (int p = 0; p < NP; p++) {
+      uint32_t a = 0;
+#pragma unroll
+      for (int i = 0; i < 8; i++) a = max(a, __float_as_uint(fabsf(xq[p][i])));
+#pragma unroll
+      for (int o = 1; o < C8; o <<= 1) a = max(a, (uint32_t)__shfl_xor((int)a, o));
+      dq_r[p] = __uint_as_float(a) / 127.0f;
+      rq_r[p] = 1.0f / dq_r[p];
+    }
+    block_umax2(akg[0], akg[1], s_red);
+#pragma unroll
+    for (int g = 0; g < 2; g++) {
+      dk_g[g] = __uint_as_float(akg[g]) / 127.0f;
+      rk_g[g] = 1.0f / dk_g[g];
+    }
+  } else {
+    block_umax2(aq, ak, s_red);
+#pragma unroll
+    for (int p = 0; p < NP; p++) {
+      dq_r[p] = __uint_as_float(aq) / 127.0f;
+      rq_r[p] = 1.0f / dq_r[p];
+    }
+    dk_g[0] = dk_g[1] = __uint_as_float(ak) / 127.0f;
+    rk_g[0] = rk_g[1] = 1.0f / dk_g[0];
+  }
+  if (FINE) {
+#pragma unroll
+    for (int p = 0; p < NP; p++)
+      if ((tid % C8) == 0 && cb.qa) reinterpret_cast<float*>(qp.q_scales)[cb.qi.tok0 + t0 + r0 + p * RP] = dq_r[p];
+    if (tid < 2 && cb.ka) reinterpret_cast<float*>(qp.k_scales)[cb.ki.tok0 / 32 + 2 * blk + tid] = dk_g[tid];
+  } else if (tid == 0) {
+    if (cb.qa) reinterpret_cast<float*>(qp.q_scales)[cb.qi.tok0 / 64 + blk] = dq_r[0];
+    if (cb.ka) reinterpret_cast<float*>(qp.k_scales)[cb.ki.tok0 / 64 + blk] = dk_g[0];
   }
 #pragma unroll
   for (int p = 0; p < NP; p++) {
@@ -556,8 +624,8 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t*
     uint32_t wq[2] = {0, 0}, wk[2] = {0, 0};
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      wq[i / 4] |= (uint32_t)(uint8_t)int8_code(xq[p][i], dq, rq) << (8 * (i % 4));
-      wk[i / 4] |= (uint32_t)(uint8_t)int8_code(xk[p][i], dk, rk) << (8 * (i % 4));
+      wq[i / 4] |= (uint32_t)(uint8_t)int8_code(xq[p][i], dq_r[p], rq_r[p]) << (8 * (i % 4));
+      wk[i / 4] |= (uint32_t)(uint8_t)int8_code(xk[p][i], dk_g[(p * RP) / 32], rk_g[(p * RP) / 32]) << (8 * (i % 4));
     }
     if (cb.qa) *reinterpret_cast<uint2*>(qp.q_codes + (cb.qi.tok0 + row) * D + c0) = make_uint2(wq[0], wq[1]);
     if (cb.ka) *reinterpret_cast<uint2*>(qp.k_codes + (cb.ki.tok0 + row) * D + c0) = make_uint2(wk[0], wk[1]);
@@ -775,19 +843,24 @@ static hipError_t prologue_dispatch(const void* q, const void* k, const void* v,
   // fixed length without grouped heads: the streamlined codes kernels (N, Np per instance)
   const bool plain = g.cu_q == nullptr && g.Hkv == g.H;
   const dim3 sg(kChunks, BHm), qg(max(g.nbq, g.nbk), BHm);
-  const bool mx = s.qk_fmt == QK_MXFP4;
+  const bool mx = s.qk_fmt == QK_MXFP4;   // else INT8 (QK_INT8, or QK_INT8T with finer steps)
   if (!mx) {
-    auto codes = [&](auto pv) {
+    auto codes = [&](auto pv, auto fine) {
       constexpr int PV = decltype(pv)::value;
+      constexpr bool FINE = decltype(fine)::value;
       // fp16 V needs no channel maxima
       stats_kernel<DT, D, false, PV == PV_FP8><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
       if (plain)
-        quant_int8_fp8_kernel<DT, D, PV><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BHm, s.sm_scale, qp);
+        quant_int8_fp8_kernel<DT, D, PV, FINE><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BHm, s.sm_scale, qp);
       else
-        quant_int8_fp8_seq_kernel<DT, D, PV><<<qg, 256, 0, st>>>(Q, K, V, g, s.sm_scale, qp);
+        quant_int8_fp8_seq_kernel<DT, D, PV, FINE><<<qg, 256, 0, st>>>(Q, K, V, g, s.sm_scale, qp);
     };
-    if (s.pv_fmt == PV_F16) codes(std::integral_constant<int, PV_F16>{});
-    else codes(std::integral_constant<int, PV_FP8>{});
+    auto with_pv = [&](auto fine) {
+      if (s.pv_fmt == PV_F16) codes(std::integral_constant<int, PV_F16>{}, fine);
+      else codes(std::integral_constant<int, PV_FP8>{}, fine);
+    };
+    if (s.qk_fmt == QK_INT8T) with_pv(std::true_type{});
+    else with_pv(std::false_type{});
     return hipGetLastError();
   }
   if (s.pv_fmt == PV_FP8)

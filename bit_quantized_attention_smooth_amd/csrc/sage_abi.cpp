@@ -46,11 +46,11 @@ sage_status check_common(int d, int causal, float sm_scale, int io_dtype, int qk
     return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   if (io_dtype != SAGE_DT_BF16 && io_dtype != SAGE_DT_F16)
     return fail(SAGE_ERR_INVALID_ARG, "io_dtype %d is not a SAGE_DT_* value", io_dtype);
-  auto known = [](int f) { return f >= SAGE_FMT_INT8 && f <= SAGE_FMT_F16; };
+  auto known = [](int f) { return f >= SAGE_FMT_INT8 && f <= SAGE_FMT_INT8_TOKEN; };
   const bool fmts_known = known(qk_fmt) && known(pv_fmt);
   if (!fmts_known) return fail(SAGE_ERR_INVALID_ARG, "qk_fmt/pv_fmt must be SAGE_FMT_* values");
-  const bool pair_ok = (qk_fmt == SAGE_FMT_INT8 && pv_fmt == SAGE_FMT_FP8) ||
-                       (qk_fmt == SAGE_FMT_INT8 && pv_fmt == SAGE_FMT_F16) ||
+  const bool int8 = qk_fmt == SAGE_FMT_INT8 || qk_fmt == SAGE_FMT_INT8_TOKEN;
+  const bool pair_ok = (int8 && pv_fmt == SAGE_FMT_FP8) || (int8 && pv_fmt == SAGE_FMT_F16) ||
                        (qk_fmt == SAGE_FMT_MXFP4 && pv_fmt == SAGE_FMT_FP8) ||
                        (qk_fmt == SAGE_FMT_MXFP4 && pv_fmt == SAGE_FMT_MXFP4) ||
                        (qk_fmt == SAGE_FMT_MXFP4 && pv_fmt == SAGE_FMT_MXFP8);
@@ -172,9 +172,10 @@ void compute_layout(const Extents& E, int d_, int qk_fmt, int pv_fmt, sage_quant
   L->mu_k = take(E.inst_kv * d * 4);
   L->mu_q = take(E.inst_q * d * 4);
   L->q_codes = take(mx ? E.tq * d / 2 : E.tq * d);
-  L->q_scales = take(mx ? E.tq * (d / 32) : E.tq / 64 * 4);
+  const bool tok = qk_fmt == SAGE_FMT_INT8_TOKEN;
+  L->q_scales = take(mx ? E.tq * (d / 32) : tok ? E.tq * 4 : E.tq / 64 * 4);
   L->k_codes = take(mx ? E.tk * d / 2 : E.tk * d);
-  L->k_scales = take(mx ? E.tk * (d / 32) : E.tk / 64 * 4);
+  L->k_scales = take(mx ? E.tk * (d / 32) : tok ? E.tk / 32 * 4 : E.tk / 64 * 4);
   L->v_codes = take(mxv ? E.tk * d / 2 : pv_fmt == SAGE_FMT_F16 ? E.tk * d * 2 : E.tk * d);
   L->v_scales = take(mxv || mx8v ? E.tk / 32 * d : E.inst_kv * d * 4);
   L->delta_s = take(E.ds * 4);

@@ -6,7 +6,8 @@
 
 namespace sage {
 
-enum { QK_INT8 = 1, QK_MXFP4 = 3 };
+// QK_INT8T: INT8 codes with a step per query token and per 32 keys (instead of per 64 tokens)
+enum { QK_INT8 = 1, QK_MXFP4 = 3, QK_INT8T = 6 };
 enum { PV_FP8 = 2, PV_MXFP4 = 3, PV_MXFP8 = 4, PV_F16 = 5 };
 
 // Padding of the token axis in every quantized buffer (a multiple of the Q tile).
@@ -19,7 +20,7 @@ struct QuantPtrs {
   float* mu_k;
   float* mu_q;
   uint8_t* q_codes;
-  void* q_scales;     // fp32 [BH, nb] (INT8) or uint8 E8M0 [BH, Np, d/32] (MXFP4)
+  void* q_scales;     // fp32 [BH, nb] (INT8), fp32 [BH, Np] (INT8T) or uint8 E8M0 [BH, Np, d/32] (MXFP4)
   uint8_t* k_codes;
   void* k_scales;
   uint8_t* v_codes;

@@ -62,14 +62,19 @@ typedef enum {
  * pv_fmt, with INT8 QK): the 16-bit P~V fallback of the original SageAttention
  * (INT8 QK^T with FP16 P and V, review thread, reply to reviewer wwcu W1): P~ and
  * V rounded to IEEE fp16 (RNE, overflow to infinity), fp32 accumulation -- the
- * matrix cores have no fp16-accumulating form. */
-enum { SAGE_FMT_INT8 = 1, SAGE_FMT_FP8 = 2, SAGE_FMT_MXFP4 = 3, SAGE_FMT_MXFP8 = 4, SAGE_FMT_F16 = 5 };
+ * matrix cores have no fp16-accumulating form.  INT8_TOKEN (as qk_fmt): INT8
+ * codes with finer steps -- one per query token and one per 32 keys -- the
+ * granularity each lane's scores share in the fused kernel (the finer
+ * SageAttention-T / thread-level variants, review thread accuracy table in the
+ * reply to tyTT W1, SageAttention2 abstract). */
+enum { SAGE_FMT_INT8 = 1, SAGE_FMT_FP8 = 2, SAGE_FMT_MXFP4 = 3, SAGE_FMT_MXFP8 = 4, SAGE_FMT_F16 = 5,
+       SAGE_FMT_INT8_TOKEN = 6 };
 
 /* I/O element types of Q, K, V, O, dO, dQ, dK, dV. */
 enum { SAGE_DT_BF16 = 0, SAGE_DT_F16 = 1 };
 
-/* Supported (qk_fmt, pv_fmt) pairs: (INT8, FP8), (INT8, F16), (MXFP4, FP8),
- * (MXFP4, MXFP4), (MXFP4, MXFP8). */
+/* Supported (qk_fmt, pv_fmt) pairs: (INT8, FP8), (INT8, F16), (INT8_TOKEN, FP8),
+ * (INT8_TOKEN, F16), (MXFP4, FP8), (MXFP4, MXFP4), (MXFP4, MXFP8). */
 typedef struct {
     int B, H, N, d;
     int causal;          /* 0 or 1 */
@@ -86,9 +91,11 @@ typedef struct {
  *   mu_q      fp32 [BH, d]     channel mean of Q (MXFP4 QK only)
  *   q_codes   INT8: int8 [BH, Np, d];  MXFP4: packed E2M1 [BH, Np, d/2] of
  *             Q - mu_q, element 2i in the low nibble of byte i
- *   q_scales  INT8: fp32 [BH, nb] step of each 64-token block;
+ *   q_scales  INT8: fp32 [BH, nb] step of each 64-token block; INT8_TOKEN:
+ *             fp32 [BH, Np] step of each token;
  *             MXFP4: E8M0 bytes [BH, Np, d/32] per token per 32 channels
- *   k_codes, k_scales   the same for K - mu_k
+ *   k_codes, k_scales   the same for K - mu_k (INT8_TOKEN: fp32 [BH, Np/32], a step
+ *             per 32 keys)
  *   v_codes   FP8 and MXFP8 V: E4M3 codes tiled [BH, Np/64, d, 64] (64 tokens
  *             of one channel contiguous);  MXFP4 V: packed E2M1 [BH, Np/64, d, 32];
  *             F16 V: fp16 tiled [BH, Np/64, d, 64]

@@ -26,8 +26,9 @@ def unpack_nibbles(packed, n):
     return out[..., :n]
 
 
-def unpack_int8_fp8(buf, p, lay, pv="fp8"):
-    """Device quant buffer (INT8 QK; FP8 or fp16 V) -> dict of oracle-shaped arrays."""
+def unpack_int8_fp8(buf, p, lay, pv="fp8", fine=False):
+    """Device quant buffer (INT8 QK; FP8 or fp16 V) -> dict of oracle-shaped arrays.  fine: a step
+    per query token and per 32 keys instead of per 64 tokens."""
     b = buf.cpu().numpy()
     BH, N, d = p.B * p.H, p.N, p.d
     Np = (N + 127) // 128 * 128
@@ -36,10 +37,11 @@ def unpack_int8_fp8(buf, p, lay, pv="fp8"):
     r["qc_all"] = part(b, lay, "q_codes", np.int8, BH * Np * d).reshape(BH, Np, d)
     r["kc_all"] = part(b, lay, "k_codes", np.int8, BH * Np * d).reshape(BH, Np, d)
     r["qc"], r["kc"] = r["qc_all"][:, :N], r["kc_all"][:, :N]
-    r["qs_all"] = part(b, lay, "q_scales", np.float32, BH * nb).reshape(BH, nb)
-    r["ks_all"] = part(b, lay, "k_scales", np.float32, BH * nb).reshape(BH, nb)
-    nbn = (N + 63) // 64
-    r["qs"], r["ks"] = r["qs_all"][:, :nbn], r["ks_all"][:, :nbn]
+    nq, nk = (Np, Np // 32) if fine else (nb, nb)
+    r["qs_all"] = part(b, lay, "q_scales", np.float32, BH * nq).reshape(BH, nq)
+    r["ks_all"] = part(b, lay, "k_scales", np.float32, BH * nk).reshape(BH, nk)
+    r["qs"] = r["qs_all"][:, :N] if fine else r["qs_all"][:, :(N + 63) // 64]
+    r["ks"] = r["ks_all"][:, :(N + 31) // 32] if fine else r["ks_all"][:, :(N + 63) // 64]
     if pv == "f16":
         vt = part(b, lay, "v_codes", np.uint16, BH * Np * d).reshape(BH, Np // 64, d, 64)
         r["vh_all"] = vt.transpose(0, 1, 3, 2).reshape(BH, Np, d)

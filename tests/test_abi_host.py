@@ -41,7 +41,8 @@ def _p(**kw):
     (dict(sm_scale=float("inf")), S.ERR_INVALID_ARG), (dict(causal=2), S.ERR_INVALID_ARG),
     (dict(io_dtype=7), S.ERR_INVALID_ARG), (dict(qk_fmt=9), S.ERR_INVALID_ARG),
     (dict(qk_fmt=2, pv_fmt=2), S.ERR_UNSUPPORTED), (dict(qk_fmt=1, pv_fmt=3), S.ERR_UNSUPPORTED),
-    (dict(qk_fmt=1, pv_fmt=4), S.ERR_UNSUPPORTED), (dict(pv_fmt=6), S.ERR_INVALID_ARG),
+    (dict(qk_fmt=1, pv_fmt=4), S.ERR_UNSUPPORTED), (dict(pv_fmt=7), S.ERR_INVALID_ARG),
+    (dict(qk_fmt=6, pv_fmt=3), S.ERR_UNSUPPORTED), (dict(qk_fmt=2, pv_fmt=6), S.ERR_UNSUPPORTED),
     (dict(qk_fmt=3, pv_fmt=5), S.ERR_UNSUPPORTED),
 ])
 def test_problem_validation(kw, status):
@@ -76,7 +77,7 @@ def test_workspace_too_small_rejected():
 
 def test_quant_layout_sizes():
     """Offsets are 256-byte aligned, ordered, and each part has the documented size."""
-    for qk, pv in ((1, 2), (1, 5), (3, 2), (3, 3), (3, 4)):
+    for qk, pv in ((1, 2), (1, 5), (6, 2), (6, 5), (3, 2), (3, 3), (3, 4)):
         for N in (1, 100, 4096):
             p = _p(N=N, qk_fmt=qk, pv_fmt=pv)
             total, lay = S.quant_size(p)
@@ -86,6 +87,9 @@ def test_quant_layout_sizes():
             assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
             codes = BH * Np * d // (2 if qk == 3 else 1)
             assert lay["q_scales"] - lay["q_codes"] >= codes
+            if qk == 6:      # a step per query token and per 32 keys
+                assert lay["k_codes"] - lay["q_scales"] >= BH * Np * 4
+                assert lay["v_codes"] - lay["k_scales"] >= BH * Np // 32 * 4
             assert lay["v_scales"] - lay["v_codes"] >= BH * Np * d * {3: 1, 5: 4}.get(pv, 2) // 2
             if pv in (3, 4):    # E8M0 byte per channel per 32 tokens
                 assert lay["delta_s"] - lay["v_scales"] >= BH * (Np // 32) * d

@@ -53,25 +53,46 @@ CASES = [
     ("int8_f16pv_causal_ragged_d128", 1, 3, 1000, 128, "bf16", True, "int8", "f16", 1, 5.0, 0.01,
      1 / math.sqrt(128)),
     ("int8_f16pv_ragged_d64_f16", 2, 2, 777, 64, "f16", False, "int8", "f16", 2, 3.0, 0.0, 1 / 8),
+    ("int8tok_causal_ragged_d128", 1, 3, 1000, 128, "bf16", True, "int8_token", "fp8", 1, 5.0, 0.01,
+     1 / math.sqrt(128)),
+    ("int8tok_f16pv_ragged_d64", 2, 2, 777, 64, "bf16", False, "int8_token", "f16", 2, 3.0, 0.01, 1 / 8),
+    ("int8tok_d64_f16", 1, 2, 256, 64, "f16", False, "int8_token", "fp8", 0, 4.0, 0.0, 1 / 8),
 ]
 
 
 def _ref_band(qk, pv):
     """Cosine floor against exact fp64 attention for a format pair."""
-    if qk == "int8":
+    if qk.startswith("int8"):
         return 0.99
     return 0.965 if pv == "mxfp4" else 0.98
 
 
+def _oracle_quant(f, qk, pv, sm):
+    """The oracle's prologue for a format pair (INT8 steps per 64 tokens, or per query token and
+    per 32 keys for int8_token)."""
+    import oracle
+    if qk.startswith("int8"):
+        fine = qk == "int8_token"
+        return oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm, pv_fmt=pv, qblk=1 if fine else 64,
+                                     kblk=32 if fine else 64)
+    return oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
+
+
+def _unpack(buf, p, lay, qk, pv):
+    if qk.startswith("int8"):
+        return unpack_int8_fp8(buf, p, lay, pv, fine=qk == "int8_token")
+    return unpack_mxfp4(buf, p, lay, pv)
+
+
 def _oracle_sim(f, qz_or, qk, pv, N, d, causal, sm, rows=None):
     import oracle
-    if qk == "int8":
+    if qk.startswith("int8"):
         return oracle.attn_int8_fp8(qz_or, N, d, causal, sm, TILE, rows=rows)
     return oracle.attn_mxfp4(qz_or, N, d, causal, sm, TILE, rows=rows)
 
 
 def _check_codes(r, qz, qk, pv):
-    if qk == "int8":
+    if qk.startswith("int8"):
         assert np.array_equal(r["mu_k"], qz["mu_k"])
         if pv == "f16":
             assert np.array_equal(r["vh"], qz["vh"]) and not r["vh_all"][:, qz["vh"].shape[1]:].any()
@@ -103,12 +124,8 @@ def test_prologue_codes_bit_exact(sage, case):
     f, g = _inputs(B, H, N, d, dt, seed, koff, outl)
     buf, p, lay = sage.quantize(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv)
     torch.cuda.synchronize()
-    if qk == "int8":
-        r = unpack_int8_fp8(buf, p, lay, pv)
-        qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
-    else:
-        r = unpack_mxfp4(buf, p, lay, pv)
-        qz = oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
+    r = _unpack(buf, p, lay, qk, pv)
+    qz = _oracle_quant(f, qk, pv, sm)
     _check_codes(r, qz, qk, pv)
 
 
@@ -122,8 +139,7 @@ def test_forward_matches_oracle(sage, case):
     torch.cuda.synchronize()
     o = to_np64(o).reshape(B * H, N, d)
     lse = lse.cpu().numpy().reshape(B * H, N).astype(np.float64)
-    qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm, pv_fmt=pv) if qk == "int8" else \
-        oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
+    qz = _oracle_quant(f, qk, pv, sm)
     o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
     o_ref, lse_ref = oracle.attn_ref(f["q"], f["k"], f["v"], causal, sm)
     assert np.abs(o - o_sim).max() <= 2e-2
@@ -138,15 +154,15 @@ def test_forward_edge_lengths(sage, N, causal):
     import oracle
     banner(f"edge N={N} causal={causal}")
     for qk, d, pv in (("int8", 64, "fp8"), ("int8", 128, "fp8"), ("mxfp4", 128, "fp8"), ("mxfp4", 64, "mxfp4"),
-                      ("mxfp4", 128, "mxfp8"), ("int8", 128, "f16")):
+                      ("mxfp4", 128, "mxfp8"), ("int8", 128, "f16"), ("int8_token", 128, "fp8"),
+                      ("int8_token", 64, "f16")):
         f, g = _inputs(1, 2, N, d, "bf16", 100 + N, 2.0)
         sm = 1 / math.sqrt(d)
         o, lse = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv,
                                return_lse=True)
         torch.cuda.synchronize()
         o = to_np64(o).reshape(2, N, d)
-        qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm, pv_fmt=pv) if qk == "int8" else \
-            oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
+        qz = _oracle_quant(f, qk, pv, sm)
         o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
         assert np.abs(o - o_sim).max() <= 2e-2, (qk, d, pv)
         if N > 1:
@@ -224,21 +240,22 @@ def test_forward_constant_keys_f16_pv(sage):
 
 
 FULL = [("int8_fp8_causal_b1h32n4096d128", "fp8"), ("int8_fp8_b2h24n16384d64", "fp8"),
-        ("int8_fp8_b1h32n8192d128", "f16"),
+        ("int8_fp8_b1h32n8192d128", "f16"), ("int8_fp8_causal_b1h32n4096d128", "fp8", "int8_token"),
         ("mxfp4_b4h32n8192d128", "fp8"), ("mxfp4_b4h32n8192d128", "mxfp4"), ("mxfp4_b4h32n8192d128", "mxfp8"),
         ("int8_fp8_b1h2n256d64", "fp8")]
 
 
-@pytest.mark.parametrize("name,pv", FULL, ids=[f"{n}-{p}" for n, p in FULL])
-def test_full_size_sampled_rows(sage, name, pv):
+@pytest.mark.parametrize("spec", FULL, ids=["-".join(c[::-1]) for c in FULL])
+def test_full_size_sampled_rows(sage, spec):
     """The named workloads at full size in the benchmark's launch configuration; the
     oracle recomputes sampled rows of a few heads."""
     import oracle
     from bit_quantized_attention_smooth_amd.workloads import workload_inputs, as_u16
-    banner(f"full size {name}")
+    name, pv = spec[:2]
+    banner(f"full size {spec}")
     x, w = workload_inputs(name)
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
-    qk, sm, causal = w["qk_fmt"], w["sm_scale"], w["causal"]
+    qk, sm, causal = (spec[2] if len(spec) > 2 else w["qk_fmt"]), w["sm_scale"], w["causal"]
     g = {n: x[n].to(device()) for n in "qkv"}
     buf, p, lay = sage.quantize(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv)
     o, lse = sage.attn_fwd_quantized(buf, p, dtype=g["q"].dtype, return_lse=True)
@@ -247,14 +264,12 @@ def test_full_size_sampled_rows(sage, name, pv):
     sel = lambda t: t.reshape(B * H, N, d)[heads]
     f = {n: oracle.widen(as_u16(sel(x[n])), w["dtype"]).reshape(len(heads), N, d) for n in "qkv"}
     rows = sample_rows(N)
-    if qk == "int8":
-        qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
-        r = unpack_int8_fp8(buf, p, lay, pv)
+    qz = _oracle_quant(f, qk, pv, sm)
+    r = _unpack(buf, p, lay, qk, pv)
+    if qk.startswith("int8"):
         for key in ("qc", "kc", "qs", "ks", "mu_k") + (("vh",) if pv == "f16" else ("vc", "vs")):
             assert np.array_equal(r[key][heads], qz[key]), key
     else:
-        qz = oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
-        r = unpack_mxfp4(buf, p, lay, pv)
         for key in ("qc", "kc", "qe", "ke", "vc", "vs" if pv == "fp8" else "ve", "mu_k", "mu_q"):
             assert np.array_equal(r[key][heads], qz[key]), key
     o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm, rows=rows)
