@@ -133,23 +133,28 @@ def quant_int8_fp8(q, k, v, sm, blk=64, pv_fmt="fp8", qblk=None, kblk=None):
 _PV = {"fp8": 2, "mxfp4": 3, "mxfp8": 4}
 
 
-def quant_mxfp4(q, k, v, sm, pv_fmt="mxfp4"):
-    """Prologue of the MXFP4 path: q [BH,Nq,d], k and v [BH,Nk,d] float32 (codes one per byte)."""
+def quant_mxfp4(q, k, v, sm, pv_fmt="mxfp4", qsb=0):
+    """Prologue of the MXFP4 path: q [BH,Nq,d], k and v [BH,Nk,d] float32 (codes one per byte).
+    qsb > 0 smooths Q per block of qsb query tokens: mu_q [BH,nqb,d] and dS [BH,nqb,Nk]."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     BH, Nq, d = q.shape
     Nk = k.shape[1]
     ng, nvg = d // 32, (Nk + 31) // 32
     pv = _PV[pv_fmt]
-    r = dict(mu_q=np.empty((BH, d), np.float32), mu_k=np.empty((BH, d), np.float32),
+    nqb = max(1, (Nq + qsb - 1) // qsb) if qsb else 1
+    r = dict(mu_q=np.empty((BH, nqb, d), np.float32), mu_k=np.empty((BH, d), np.float32),
              qc=np.empty((BH, Nq, d), np.uint8), qe=np.empty((BH, Nq, ng), np.uint8),
              kc=np.empty((BH, Nk, d), np.uint8), ke=np.empty((BH, Nk, ng), np.uint8),
-             dS=np.empty((BH, Nk), np.float32), corr=np.empty((BH, Nq), np.float64),
+             dS=np.empty((BH, nqb, Nk), np.float32), corr=np.empty((BH, Nq), np.float64),
              vc=np.empty((BH, Nk, d), np.uint8), ve=np.zeros((BH, nvg, d), np.uint8),
              vs=np.zeros((BH, d), np.float32))
-    lib().or_quant_mxfp4_x(_p(q), _p(k), _p(v), BH, Nq, Nk, d, pv, ctypes.c_double(sm),
+    lib().or_quant_mxfp4_x(_p(q), _p(k), _p(v), BH, Nq, Nk, d, pv, int(qsb), ctypes.c_double(sm),
                          _p(r["mu_q"]), _p(r["mu_k"]), _p(r["qc"]), _p(r["qe"]), _p(r["kc"]), _p(r["ke"]),
                          _p(r["dS"]), _p(r["corr"]), _p(r["vc"]), _p(r["ve"]), _p(r["vs"]))
     r["pv_fmt"] = pv_fmt
+    r["qsb"] = int(qsb)
+    if not qsb:                          # one block: the per-head shapes
+        r["mu_q"], r["dS"] = r["mu_q"][:, 0], r["dS"][:, 0]
     return r
 
 
@@ -186,8 +191,9 @@ def attn_mxfp4(qz, N, d, causal, sm, tile, rows=None):
     out = np.empty((BH, len(rows), d), np.float64)
     lse = np.empty((BH, len(rows)), np.float64)
     pv = _PV[qz["pv_fmt"]]
-    lib().or_attn_mxfp4_x(_p(qz["qc"]), _p(qz["qe"]), _p(qz["kc"]), _p(qz["ke"]), _p(qz["dS"]), _p(qz["corr"]),
-                          _p(qz["vc"]), _p(qz["ve"]), _p(qz["vs"]), pv, BH, Nq, Nk, d, tile, int(causal),
+    dS = np.ascontiguousarray(qz["dS"])
+    lib().or_attn_mxfp4_x(_p(qz["qc"]), _p(qz["qe"]), _p(qz["kc"]), _p(qz["ke"]), _p(dS), _p(qz["corr"]),
+                          _p(qz["vc"]), _p(qz["ve"]), _p(qz["vs"]), pv, qz.get("qsb", 0), BH, Nq, Nk, d, tile, int(causal),
                           ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
     return out, lse
 

@@ -355,27 +355,36 @@ OR_API void or_quant_int8_fp8(const float *q, const float *k, const float *v,
  *       E8M0 bytes ve [BH, ceil(Nk/32), d].
  *   pv_fmt 4 (MXFP8): the same grouping with E4M3 elements (emax 8).
  *   pv_fmt 2 (FP8): V codes E4M3 with per-channel fp32 scale vs [BH,d].
+ *   qsb: Q is smoothed per block of qsb query tokens (0: one block, the whole sequence);
+ *       mu_q is then [BH, nqb, d] and dS [BH, nqb, Nk] with nqb = ceil(Nq / qsb): the key
+ *       term of query block b is mu_q[b] . Ks[t].
  */
 OR_API void or_quant_mxfp4_x(const float *q, const float *k, const float *v,
-                             int BH, int Nq, int Nk, int d, int pv_fmt, double sm,
+                             int BH, int Nq, int Nk, int d, int pv_fmt, int qsb, double sm,
                              float *mu_q, float *mu_k,
                              uint8_t *qc, uint8_t *qe, uint8_t *kc, uint8_t *ke,
                              float *dS, double *corr,
                              uint8_t *vc, uint8_t *ve, float *vs)
 {
     int ng = d / 32, nvg = (Nk + 31) / 32;
+    int bq = qsb > 0 ? qsb : (Nq > 0 ? Nq : 1), nqb = (Nq + bq - 1) / bq;
+    if (nqb < 1)
+        nqb = 1;
 #pragma omp parallel for schedule(dynamic)
     for (int h = 0; h < BH; h++) {
         int64_t offq = (int64_t)h * Nq * d, offk = (int64_t)h * Nk * d;
         const float *Q = q + offq, *K = k + offk, *V = v + offk;
-        float *muq = mu_q + (int64_t)h * d, *muk = mu_k + (int64_t)h * d;
-        channel_mean(Q, Nq, d, muq);
+        float *muq = mu_q + (int64_t)h * nqb * d, *muk = mu_k + (int64_t)h * d;
+        for (int b = 0; b < nqb; b++) {
+            int t0 = b * bq, n = Nq - t0 < bq ? Nq - t0 : bq;
+            channel_mean(Q + (int64_t)t0 * d, n > 0 ? n : 0, d, muq + (int64_t)b * d);
+        }
         channel_mean(K, Nk, d, muk);
         float *Qs = malloc(sizeof(float) * ((size_t)Nq * d + 1));
         float *Ks = malloc(sizeof(float) * ((size_t)Nk * d + 1));
         for (int t = 0; t < Nq; t++)
             for (int c = 0; c < d; c++)
-                Qs[(int64_t)t * d + c] = Q[(int64_t)t * d + c] - muq[c];
+                Qs[(int64_t)t * d + c] = Q[(int64_t)t * d + c] - muq[(int64_t)(t / bq) * d + c];
         for (int t = 0; t < Nk; t++)
             for (int c = 0; c < d; c++)
                 Ks[(int64_t)t * d + c] = K[(int64_t)t * d + c] - muk[c];
@@ -389,12 +398,13 @@ OR_API void or_quant_mxfp4_x(const float *q, const float *k, const float *v,
                 int64_t e0 = (int64_t)t * d + 32 * g;
                 quant_mx_group(Ks + e0, 32, 1, 4, kc + offk + e0, 1, ke + ((int64_t)h * Nk + t) * ng + g);
             }
-        for (int t = 0; t < Nk; t++) {
-            double s = 0.0;
-            for (int c = 0; c < d; c++)
-                s += (double)muq[c] * (double)Ks[(int64_t)t * d + c];
-            dS[(int64_t)h * Nk + t] = (float)s;
-        }
+        for (int b = 0; b < nqb; b++)
+            for (int t = 0; t < Nk; t++) {
+                double s = 0.0;
+                for (int c = 0; c < d; c++)
+                    s += (double)muq[(int64_t)b * d + c] * (double)Ks[(int64_t)t * d + c];
+                dS[((int64_t)h * nqb + b) * Nk + t] = (float)s;
+            }
         for (int t = 0; t < Nq; t++) {
             double cq = 0.0;
             for (int c = 0; c < d; c++)
@@ -431,7 +441,7 @@ OR_API void or_quant_mxfp4(const float *q, const float *k, const float *v,
                            float *dS, double *corr,
                            uint8_t *vc, uint8_t *ve, float *vs)
 {
-    or_quant_mxfp4_x(q, k, v, BH, N, N, d, pv_fmt, sm, mu_q, mu_k, qc, qe, kc, ke, dS, corr, vc, ve, vs);
+    or_quant_mxfp4_x(q, k, v, BH, N, N, d, pv_fmt, 0, sm, mu_q, mu_k, qc, qe, kc, ke, dS, corr, vc, ve, vs);
 }
 
 /* ------------------------------------------------------------------ */
@@ -453,7 +463,8 @@ typedef struct {
     const float *qs, *ks;
     /* QK_MXFP4 */
     const uint8_t *q4, *qe, *k4, *ke;
-    const float *dS;           /* per-key additive score term (may be NULL) */
+    const float *dS;           /* additive score term [nqb][N] per query block and key (may be NULL) */
+    int qsb;                   /* query tokens per dS block (0: one block) */
     const double *dSx;         /* same, fp64, exact mode */
     /* PV */
     const double *vx;          /* PV_EXACT */
@@ -502,7 +513,7 @@ static double score(const head_t *H, int i, int j)
                       * ldexp(1.0, (int)H->ke[(int64_t)j * ng + g] - 127);
         }
         if (H->dS)
-            s += (double)H->dS[j];
+            s += (double)H->dS[(int64_t)(H->qsb ? i / H->qsb : 0) * H->N + j];
     }
     return s;
 }
@@ -728,18 +739,22 @@ OR_API void or_attn_int8_fp8(const int8_t *qc, const float *qs, const int8_t *kc
  * 4 = FP8 P~ with MXFP8 V.  Queries [BH,Nq], keys [BH,Nk]. */
 OR_API void or_attn_mxfp4_x(const uint8_t *qc, const uint8_t *qe, const uint8_t *kc, const uint8_t *ke,
                             const float *dS, const double *corr,
-                            const uint8_t *vc, const uint8_t *ve, const float *vs, int pv_fmt,
+                            const uint8_t *vc, const uint8_t *ve, const float *vs, int pv_fmt, int qsb,
                             int BH, int Nq, int Nk, int d, int tile, int causal, double sm,
                             const int *rows, int nrows, double *out, double *lse)
 {
     int ng = d / 32, nvg = (Nk + 31) / 32;
+    int nqb = qsb > 0 ? (Nq + qsb - 1) / qsb : 1;
+    if (nqb < 1)
+        nqb = 1;
     head_t *H = calloc((size_t)BH, sizeof(head_t));
     for (int h = 0; h < BH; h++) {
         int64_t offq = (int64_t)h * Nq * d, offk = (int64_t)h * Nk * d;
         H[h] = (head_t){.N = Nk, .d = d, .causal = causal, .tile = tile, .sm = sm,
                         .qk = QK_MXFP4, .pv = pv_fmt == 3 ? PV_MXFP4 : pv_fmt == 4 ? PV_MXFP8 : PV_FP8,
                         .q4 = qc + offq, .qe = qe + (int64_t)h * Nq * ng, .k4 = kc + offk, .ke = ke + (int64_t)h * Nk * ng,
-                        .dS = dS + (int64_t)h * Nk, .corr = corr + (int64_t)h * Nq, .vc = vc + offk};
+                        .dS = dS + (int64_t)h * nqb * Nk, .qsb = qsb, .corr = corr + (int64_t)h * Nq,
+                        .vc = vc + offk};
         if (pv_fmt == 3 || pv_fmt == 4)
             H[h].ve = ve + (int64_t)h * nvg * d;
         else
@@ -755,7 +770,7 @@ OR_API void or_attn_mxfp4(const uint8_t *qc, const uint8_t *qe, const uint8_t *k
                           int BH, int N, int d, int tile, int causal, double sm,
                           const int *rows, int nrows, double *out, double *lse)
 {
-    or_attn_mxfp4_x(qc, qe, kc, ke, dS, corr, vc, ve, vs, pv_fmt, BH, N, N, d, tile, causal, sm, rows, nrows,
+    or_attn_mxfp4_x(qc, qe, kc, ke, dS, corr, vc, ve, vs, pv_fmt, 0, BH, N, N, d, tile, causal, sm, rows, nrows,
                     out, lse);
 }
 

@@ -626,3 +626,72 @@ def test_varlen_gqa_quantized_sim_accuracy(orc):
     for qk, pv, bar in (("int8", "fp8", 0.99), ("mxfp4", "fp8", 0.98), ("mxfp4", "mxfp8", 0.98)):
         o, _, quants = orc.attn_varlen(q, k, v, cu_q, cu_k, True, 0.125, qk_fmt=qk, pv_fmt=pv)
         assert _cos(o, o_ref) > bar, (qk, pv)
+
+
+# ---------------------------------------------------------------- per-block Q smoothing
+
+@pytest.mark.parametrize("pv_fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_q_smoothing_sim_exact_on_lossless_grid(orc, pv_fmt, causal):
+    """Q channel 3 (where K is 0, so no score depends on it) takes a_b -+ 0.5 in equal numbers
+    inside each 128-query block b: smoothing per block leaves exactly -+0.5 there (on the E2M1
+    grid), smoothing over the sequence does not.  The per-block simulation equals exact
+    attention; the block means are exactly a_b."""
+    rng = np.random.default_rng(66)
+    BH, N, d, qsb = 2, 320, 64, 128
+    q, k = _mx_score_design(rng, BH, N, d)
+    a = rng.integers(1, 5, size=(BH, (N + qsb - 1) // qsb)).astype(np.float64)
+    for h in range(BH):
+        for b in range(a.shape[1]):
+            t0, t1 = b * qsb, min(N, b * qsb + qsb)
+            q[h, t0:t1, 3] = a[h, b] - 0.5 + rng.permutation(np.arange(t1 - t0) % 2)
+            q[h, t0:t1, 2] = 1.0 + rng.permutation(np.arange(t1 - t0) % 2)   # {1, 2}, mean 1.5 per block
+    v = _lossless_v(rng, BH, N, d, pv_fmt)
+    qz = orc.quant_mxfp4(q, k, v, LN2, pv_fmt=pv_fmt, qsb=qsb)
+    assert np.array_equal(qz["mu_q"][:, :, 3], a.astype(np.float32))
+    o, lse = orc.attn_mxfp4(qz, N, d, causal, LN2, 64)
+    o_ref, lse_ref = orc.attn_ref(q, k, v, causal, LN2)
+    assert np.allclose(lse, lse_ref, rtol=0, atol=1e-12)
+    assert np.allclose(o, o_ref, rtol=1e-12, atol=1e-12 * np.abs(v).max())
+
+
+def test_block_q_smoothing_reduces_to_global_for_equal_block_means(orc):
+    """Every 128-query block with the same channel means: per-block and per-sequence smoothing
+    give the same codes, the same dS rows and the same output."""
+    rng = np.random.default_rng(67)
+    BH, N, d = 2, 256, 64
+    base = rng.integers(-8, 8, size=(BH, 64, d)) / 4.0
+    base -= base.mean(axis=1, keepdims=True)                   # each 64-row half: mean exactly 0
+    q = (np.concatenate([base] * 4, axis=1) + rng.integers(-4, 4, size=(BH, 1, d)) / 2.0).astype(np.float32)
+    k = _rand((BH, N, d), 68, 2.0)
+    v = _rand((BH, N, d), 69)
+    g = orc.quant_mxfp4(q, k, v, 0.1, pv_fmt="fp8")
+    b = orc.quant_mxfp4(q, k, v, 0.1, pv_fmt="fp8", qsb=128)
+    assert np.array_equal(b["mu_q"][:, 0], g["mu_q"]) and np.array_equal(b["mu_q"][:, 1], g["mu_q"])
+    assert np.array_equal(b["qc"], g["qc"]) and np.array_equal(b["qe"], g["qe"])
+    assert np.array_equal(b["dS"][:, 0], g["dS"]) and np.array_equal(b["dS"][:, 1], g["dS"])
+    for causal in (False, True):
+        og, _ = orc.attn_mxfp4(g, N, d, causal, 0.1, 64)
+        ob, _ = orc.attn_mxfp4(b, N, d, causal, 0.1, 64)
+        assert np.array_equal(og, ob)
+
+
+def test_block_q_smoothing_more_accurate_under_drift(orc):
+    """Q whose channel offsets drift along the sequence: the per-block means track the drift,
+    so the 4-bit Q codes carry less of it and the output is closer to exact attention."""
+    rng = np.random.default_rng(70)
+    BH, N, d = 2, 1024, 128
+    q = rng.standard_normal((BH, N, d))
+    q += np.linspace(-1, 1, N)[None, :, None] * rng.normal(0, 6, size=(BH, 1, d))   # drifting offsets
+    k = rng.standard_normal((BH, N, d)) + rng.normal(0, 4, size=(BH, 1, d))
+    v = rng.standard_normal((BH, N, d))
+    q, k, v = (x.astype(np.float32) for x in (q, k, v))
+    sm = 1 / math.sqrt(d)
+    rows = np.arange(0, N, 8, dtype=np.int32)
+    o_ref, _ = orc.attn_ref(q, k, v, False, sm, rows=rows)
+    cs = {}
+    for qsb in (0, 128):
+        qz = orc.quant_mxfp4(q, k, v, sm, pv_fmt="fp8", qsb=qsb)
+        o, _ = orc.attn_mxfp4(qz, N, d, False, sm, 64, rows=rows)
+        cs[qsb] = _cos(o, o_ref)
+    assert cs[128] > cs[0]
