@@ -165,8 +165,9 @@ def run_workload(name, S, torch, steps, warmup, pv="fp8", qk=None):
     # FP8 V: 1 B codes + a fp32 step per channel)
     v_b = {"fp8": E, "f16": 2 * E}.get(pv, (E // 2 if pv == "mxfp4" else E) + E // 32)
     code_b = (2 * E + v_b) if qk.startswith("int8") else (2 * (E // 2 + E // 32) + v_b)
-    scale_b = ({"int8": 2 * 4 * B * H * ((N + 63) // 64), "int8_token": 4 * B * H * (N + (N + 31) // 32)}
-               .get(qk, 4 * B * H * N)) + \
+    nqb = (N + 127) // 128     # per-block Q smoothing: a dS row per 128-query block
+    scale_b = ({"int8": 2 * 4 * B * H * ((N + 63) // 64), "int8_token": 4 * B * H * (N + (N + 31) // 32),
+                "mxfp4_qblock": 4 * B * H * N * nqb}.get(qk, 4 * B * H * N)) + \
         (4 * B * H * d if pv == "fp8" else 0) + 4 * B * H * N
     pro_bytes = 3 * 2 * E + code_b + scale_b
     return dict(name=name, B=B, H=H, N=N, d=d, causal=causal, qk=qk, pv=pv, ms_step=ms_step, wall=wall,
@@ -313,7 +314,8 @@ def main():
         for name, pv, *qk in (("int8_fp8_b1h32n8192d128", "fp8"), ("int8_fp8_b1h32n8192d128", "f16"),
                               ("int8_fp8_causal_b1h32n4096d128", "fp8", "int8_token"),
                               ("int8_fp8_causal_b1h32n16384d128", "fp8"),
-                         ("mxfp4_b4h32n8192d128", "fp8"), ("mxfp4_b4h32n8192d128", "mxfp4"),
+                         ("mxfp4_b4h32n8192d128", "fp8"), ("mxfp4_b4h32n8192d128", "fp8", "mxfp4_qblock"),
+                         ("mxfp4_b4h32n8192d128", "mxfp4"),
                          ("mxfp4_b4h32n8192d128", "mxfp8"), ("int8_fp8_b2h24n16384d64", "fp8")):
             qk = qk[0] if qk else None
             log(f"[bench] secondary {name} (P~V {pv}{', QK ' + qk if qk else ''})")

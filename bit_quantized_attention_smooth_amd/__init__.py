@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsage_attn.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_OUT_OF_MEMORY, ERR_HIP = range(6)
-FMT = {"int8": 1, "fp8": 2, "mxfp4": 3, "mxfp8": 4, "f16": 5, "int8_token": 6}
+FMT = {"int8": 1, "fp8": 2, "mxfp4": 3, "mxfp8": 4, "f16": 5, "int8_token": 6, "mxfp4_qblock": 7}
 DT = {torch.bfloat16: 0, torch.float16: 1}
 
 # Every symbol the header declares (kept in sync by a CPU test that parses the header).

@@ -55,6 +55,7 @@ struct FwdArgs {
   float* lse;
   SeqGeo g;
   int nqt;            // query tiles per instance in the grid
+  int nqb;            // MXFP4 with per-block Q smoothing: dS rows per instance (one per query tile); else 0
   float sm_log2e;
 };
 
@@ -552,7 +553,9 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
   const int hk = h / (a.g.H / a.g.Hkv);
   const Inst ki = k_inst(a.g, b, hk, D);
   const size_t kt0 = ki.tok0, kvid = (size_t)b * a.g.Hkv + hk;
-  const size_t ds0 = QK == QK_MXFP4 ? ds_base(a.g, b, h) : 0;
+  // dS strip: per key, or (per-block Q smoothing) the row of this query tile's block
+  const size_t ds0 = QK != QK_MXFP4 ? 0
+                     : a.nqb ? (((size_t)b * a.g.H + h) * a.nqb + qt) * a.g.Npk : ds_base(a.g, b, h);
   const int NK = ki.len;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -762,6 +765,7 @@ hipError_t launch_attn_fwd(const Shape& s, const QuantPtrs& qp, void* o, float* 
   a.lse = lse;
   a.g = s.g;
   a.nqt = (s.g.nbq * 64) / kQT;   // tiles of 128 queries covering the longest query instance
+  a.nqb = s.qk_fmt == QK_MXFP4B ? s.Np / kQT : 0;
   a.sm_log2e = s.sm_scale * kLog2e;
   if (s.qk_fmt == QK_INT8 || s.qk_fmt == QK_INT8T) {
     if (s.pv_fmt == PV_F16)
@@ -769,6 +773,7 @@ hipError_t launch_attn_fwd(const Shape& s, const QuantPtrs& qp, void* o, float* 
     if (s.pv_fmt != PV_FP8) return hipErrorInvalidValue;
     return s.io_dtype == 0 ? fwd_dispatch_int8<0, PV_FP8>(s, a, st) : fwd_dispatch_int8<1, PV_FP8>(s, a, st);
   }
+  if (s.qk_fmt != QK_MXFP4 && s.qk_fmt != QK_MXFP4B) return hipErrorInvalidValue;
   if (s.pv_fmt == PV_MXFP4)
     return s.io_dtype == 0 ? fwd_dispatch_d<QK_MXFP4, 0, PV_MXFP4>(s, a, st)
                            : fwd_dispatch_d<QK_MXFP4, 1, PV_MXFP4>(s, a, st);

@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
 // MXFP4 Q_s and K_s codes (32-channel blocks), dS and LSE correction; V in FP8
 // (PV == PV_FP8), MXFP4 or MXFP8 (both in 32-token blocks per channel).  grid (Np/64, BH),
 // 256 threads.
-template <int DT, int D, int PV>
+template <int DT, int D, int PV, bool QB>
 __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, int N, int Np, int BH, float sm,
                                                           QuantPtrs qp) {
@@ -335,13 +335,14 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
   __shared__ float s_dv[PV == PV_FP8 ? D : 1];
   if (tid < D) {
     const float mk = chunk_mean(qp.sums, 0, BH, bh, D, tid, N);
-    const float mq = chunk_mean(qp.sums, 1, BH, bh, D, tid, N);
+    // QB: the mean of this 64-token block's 128-query block (from qblock_mean_kernel)
+    const float mq = QB ? qp.mu_q[((size_t)bh * (Np / 128) + blk / 2) * D + tid] : chunk_mean(qp.sums, 1, BH, bh, D, tid, N);
     s_mk[tid] = mk;
     s_mq[tid] = mq;
     if (PV == PV_FP8) s_dv[tid] = chunk_amax(qp.amax_v, BH, bh, D, tid) / 448.0f;
     if (blk == 0) {
       qp.mu_k[(size_t)bh * D + tid] = mk;
-      qp.mu_q[(size_t)bh * D + tid] = mq;
+      if (!QB) qp.mu_q[(size_t)bh * D + tid] = mq;
       if (PV == PV_FP8) reinterpret_cast<float*>(qp.v_scales)[(size_t)bh * D + tid] = s_dv[tid];
     }
   }
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
         cs += (double)xq[i] * (double)s_mk[c0 + i];
         xq[i] = xq[i] - s_mq[c0 + i];
         xk[i] = xk[i] - s_mk[c0 + i];
-        ds += (double)s_mq[c0 + i] * (double)xk[i];
+        if (!QB) ds += (double)s_mq[c0 + i] * (double)xk[i];   // QB: dS comes from qblock_ds_kernel
       }
     } else {
 #pragma unroll
@@ -403,7 +404,7 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
       cs += __shfl_xor(cs, o);
     }
     if ((tid % C8) == 0) {
-      qp.delta_s[(size_t)bh * Np + row] = row < N ? (float)ds : 0.0f;
+      if (!QB) qp.delta_s[(size_t)bh * Np + row] = row < N ? (float)ds : 0.0f;
       if (row < N) qp.lse_corr[(size_t)bh * N + row] = (float)(sm * cs);
     }
     if (PV == PV_FP8) {
@@ -466,6 +467,67 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
         reinterpret_cast<uint8_t*>(qp.v_scales)[((size_t)bh * (Np / 32) + 2 * blk + g) * D + ch] = (uint8_t)b;
       }
     }
+  }
+}
+
+// Per-block Q smoothing (MXFP4 QK): the mean of Q over each 128-query block -- the fused
+// kernel's query tile -- from exact fp64 sums.  grid (Np/128, BH), 256 threads; writes
+// mu_q[bh][b][D].
+template <int DT, int D>
+__global__ __launch_bounds__(256) void qblock_mean_kernel(const uint16_t* __restrict__ q, int N, int Np,
+                                                          float* __restrict__ mu_q) {
+  constexpr int C8 = D / 8, RP = 256 / C8;
+  const int bh = blockIdx.y, b = blockIdx.x, t0 = b * 128, t1 = min(N, t0 + 128);
+  const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
+  double sx[8] = {};
+  for (int r = t0 + r0; r < t1; r += RP) {
+    float y[8];
+    load8<DT>(q + ((size_t)bh * N + r) * D + c0, y);
+#pragma unroll
+    for (int i = 0; i < 8; i++) sx[i] += (double)y[i];
+  }
+  __shared__ double s_x[RP][D];
+#pragma unroll
+  for (int i = 0; i < 8; i++) s_x[r0][c0 + i] = sx[i];
+  __syncthreads();
+  if (tid < D) {
+    double a = 0.0;
+    for (int r = 0; r < RP; r++) a += s_x[r][tid];
+    mu_q[((size_t)bh * (Np / 128) + b) * D + tid] = (float)(a / (double)(t1 - t0));   // t1 > t0: Np < N + 128
+  }
+}
+
+// Per-block Q smoothing: dS[bh][b][j] = fl32(sum_c mu_q[b][c] * Ks[j][c]) for every 128-query
+// block b and key j, Ks = fl32(K - mu_k) as the codes kernel forms it, summed in fp64 in channel
+// order (0 past N).  grid (Np/64, BH), 256 threads: 64 keys per workgroup, a wave per block b.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void qblock_ds_kernel(const uint16_t* __restrict__ k, int N, int Np,
+                                                        const float* __restrict__ mu_k, const float* __restrict__ mu_q,
+                                                        float* __restrict__ delta_s) {
+  constexpr int C8 = D / 8;
+  const int bh = blockIdx.y, t0 = blockIdx.x * 64, NB = Np / 128;
+  __shared__ float s_ks[64][D + 1];   // one padding column: the 64 lanes' rows fall in distinct banks
+  for (int e = threadIdx.x; e < 64 * C8; e += 256) {
+    const int r = e / C8, c0 = (e % C8) * 8, row = t0 + r;
+    float y[8];
+    if (row < N) {
+      load8<DT>(k + ((size_t)bh * N + row) * D + c0, y);
+#pragma unroll
+      for (int i = 0; i < 8; i++) y[i] = y[i] - mu_k[(size_t)bh * D + c0 + i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) y[i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) s_ks[r][c0 + i] = y[i];
+  }
+  __syncthreads();
+  const int j = threadIdx.x & 63;
+  for (int b = threadIdx.x >> 6; b < NB; b += 4) {
+    const float* m = mu_q + ((size_t)bh * NB + b) * D;   // wave-uniform
+    double acc = 0.0;
+    for (int c = 0; c < D; c++) acc += (double)m[c] * (double)s_ks[j][c];
+    delta_s[((size_t)bh * NB + b) * Np + t0 + j] = t0 + j < N ? (float)acc : 0.0f;
   }
 }
 
@@ -843,7 +905,8 @@ static hipError_t prologue_dispatch(const void* q, const void* k, const void* v,
   // fixed length without grouped heads: the streamlined codes kernels (N, Np per instance)
   const bool plain = g.cu_q == nullptr && g.Hkv == g.H;
   const dim3 sg(kChunks, BHm), qg(max(g.nbq, g.nbk), BHm);
-  const bool mx = s.qk_fmt == QK_MXFP4;   // else INT8 (QK_INT8, or QK_INT8T with finer steps)
+  // else INT8 (QK_INT8, or QK_INT8T with finer steps)
+  const bool mx = s.qk_fmt == QK_MXFP4 || s.qk_fmt == QK_MXFP4B;
   if (!mx) {
     auto codes = [&](auto pv, auto fine) {
       constexpr int PV = decltype(pv)::value;
@@ -863,20 +926,35 @@ static hipError_t prologue_dispatch(const void* q, const void* k, const void* v,
     else with_pv(std::false_type{});
     return hipGetLastError();
   }
-  if (s.pv_fmt == PV_FP8)
+  // QB (per-128-query-block Q smoothing, fixed length only): block means replace the Q sums
+  const bool qb = s.qk_fmt == QK_MXFP4B;
+  if (qb) {
+    if (!plain) return hipErrorInvalidValue;
+    if (s.pv_fmt == PV_FP8)
+      stats_kernel<DT, D, false, true><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
+    else
+      stats_kernel<DT, D, false, false><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
+    qblock_mean_kernel<DT, D><<<dim3(s.Np / 128, BHm), 256, 0, st>>>(Q, s.N, s.Np, qp.mu_q);
+  } else if (s.pv_fmt == PV_FP8) {
     stats_kernel<DT, D, true, true><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
-  else
+  } else {
     stats_kernel<DT, D, true, false><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
+  }
   auto codes = [&](auto pv) {
     constexpr int PV = decltype(pv)::value;
-    if (plain)
-      quant_mxfp4_kernel<DT, D, PV><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BHm, s.sm_scale, qp);
+    if (qb)
+      quant_mxfp4_kernel<DT, D, PV, true><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BHm, s.sm_scale, qp);
+    else if (plain)
+      quant_mxfp4_kernel<DT, D, PV, false><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BHm, s.sm_scale, qp);
     else
       quant_mxfp4_seq_kernel<DT, D, PV><<<qg, 256, 0, st>>>(Q, K, V, g, s.sm_scale, qp);
   };
   if (s.pv_fmt == PV_FP8) codes(std::integral_constant<int, PV_FP8>{});
   else if (s.pv_fmt == PV_MXFP8) codes(std::integral_constant<int, PV_MXFP8>{});
   else codes(std::integral_constant<int, PV_MXFP4>{});
+  // QB: dS per (query block, key), after the codes kernel has written mu_k
+  if (qb)
+    qblock_ds_kernel<DT, D><<<dim3(s.Np / 64, BHm), 256, 0, st>>>(K, s.N, s.Np, qp.mu_k, qp.mu_q, qp.delta_s);
   return hipGetLastError();
 }
 

@@ -46,14 +46,13 @@ sage_status check_common(int d, int causal, float sm_scale, int io_dtype, int qk
     return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   if (io_dtype != SAGE_DT_BF16 && io_dtype != SAGE_DT_F16)
     return fail(SAGE_ERR_INVALID_ARG, "io_dtype %d is not a SAGE_DT_* value", io_dtype);
-  auto known = [](int f) { return f >= SAGE_FMT_INT8 && f <= SAGE_FMT_INT8_TOKEN; };
+  auto known = [](int f) { return f >= SAGE_FMT_INT8 && f <= SAGE_FMT_MXFP4_QBLOCK; };
   const bool fmts_known = known(qk_fmt) && known(pv_fmt);
   if (!fmts_known) return fail(SAGE_ERR_INVALID_ARG, "qk_fmt/pv_fmt must be SAGE_FMT_* values");
   const bool int8 = qk_fmt == SAGE_FMT_INT8 || qk_fmt == SAGE_FMT_INT8_TOKEN;
+  const bool mx4 = qk_fmt == SAGE_FMT_MXFP4 || qk_fmt == SAGE_FMT_MXFP4_QBLOCK;
   const bool pair_ok = (int8 && pv_fmt == SAGE_FMT_FP8) || (int8 && pv_fmt == SAGE_FMT_F16) ||
-                       (qk_fmt == SAGE_FMT_MXFP4 && pv_fmt == SAGE_FMT_FP8) ||
-                       (qk_fmt == SAGE_FMT_MXFP4 && pv_fmt == SAGE_FMT_MXFP4) ||
-                       (qk_fmt == SAGE_FMT_MXFP4 && pv_fmt == SAGE_FMT_MXFP8);
+                       (mx4 && (pv_fmt == SAGE_FMT_FP8 || pv_fmt == SAGE_FMT_MXFP4 || pv_fmt == SAGE_FMT_MXFP8));
   if (!pair_ok) return fail(SAGE_ERR_UNSUPPORTED, "format pair (qk=%d, pv=%d) is not supported", qk_fmt, pv_fmt);
   return SAGE_OK;
 }
@@ -90,6 +89,8 @@ sage_status check_varlen(const sage_varlen_problem* p) {
   if (toks * p->d > (1LL << 40) || (long long)p->B * p->H > kMaxInstances ||
       (long long)p->B * p->H * ((p->max_seqlen_q + 127) / 128) > (1LL << 31) - 1)
     return fail(SAGE_ERR_INVALID_ARG, "problem too large");
+  if (p->qk_fmt == SAGE_FMT_MXFP4_QBLOCK)
+    return fail(SAGE_ERR_UNSUPPORTED, "per-block Q smoothing (MXFP4_QBLOCK) is for fixed-length problems only");
   return check_common(p->d, p->causal, p->sm_scale, p->io_dtype, p->qk_fmt, p->pv_fmt);
 }
 
@@ -162,7 +163,8 @@ Extents extents(const sage_varlen_problem* p) {
 
 void compute_layout(const Extents& E, int d_, int qk_fmt, int pv_fmt, sage_quant_layout* L) {
   const size_t d = d_;
-  const bool mx = qk_fmt == SAGE_FMT_MXFP4, mxv = pv_fmt == SAGE_FMT_MXFP4, mx8v = pv_fmt == SAGE_FMT_MXFP8;
+  const bool qblk = qk_fmt == SAGE_FMT_MXFP4_QBLOCK;
+  const bool mx = qk_fmt == SAGE_FMT_MXFP4 || qblk, mxv = pv_fmt == SAGE_FMT_MXFP4, mx8v = pv_fmt == SAGE_FMT_MXFP8;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -170,7 +172,10 @@ void compute_layout(const Extents& E, int d_, int qk_fmt, int pv_fmt, sage_quant
     return o;
   };
   L->mu_k = take(E.inst_kv * d * 4);
-  L->mu_q = take(E.inst_q * d * 4);
+  // per-block Q smoothing: a mean per 128-query block, a dS row per block (fixed length: tq, tk
+  // are the instances' padded token counts)
+  const size_t nqb = qblk ? E.tq / E.inst_q / 128 : 1;
+  L->mu_q = take(E.inst_q * nqb * d * 4);
   L->q_codes = take(mx ? E.tq * d / 2 : E.tq * d);
   const bool tok = qk_fmt == SAGE_FMT_INT8_TOKEN;
   L->q_scales = take(mx ? E.tq * (d / 32) : tok ? E.tq * 4 : E.tq / 64 * 4);
@@ -178,7 +183,7 @@ void compute_layout(const Extents& E, int d_, int qk_fmt, int pv_fmt, sage_quant
   L->k_scales = take(mx ? E.tk * (d / 32) : tok ? E.tk / 32 * 4 : E.tk / 64 * 4);
   L->v_codes = take(mxv ? E.tk * d / 2 : pv_fmt == SAGE_FMT_F16 ? E.tk * d * 2 : E.tk * d);
   L->v_scales = take(mxv || mx8v ? E.tk / 32 * d : E.inst_kv * d * 4);
-  L->delta_s = take(E.ds * 4);
+  L->delta_s = take(E.ds * nqb * 4);
   L->lse_corr = take(E.corr * 4);
   L->stats = take(sage::kStatChunks * (E.stats_inst * d * 8 * 2 + E.stats_inst * d * 4));
   L->total = off;

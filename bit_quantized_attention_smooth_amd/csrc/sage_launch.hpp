@@ -6,8 +6,9 @@
 
 namespace sage {
 
-// QK_INT8T: INT8 codes with a step per query token and per 32 keys (instead of per 64 tokens)
-enum { QK_INT8 = 1, QK_MXFP4 = 3, QK_INT8T = 6 };
+// QK_INT8T: INT8 codes with a step per query token and per 32 keys (instead of per 64 tokens);
+// QK_MXFP4B: MXFP4 with Q smoothed per 128-query block (dS per block and key)
+enum { QK_INT8 = 1, QK_MXFP4 = 3, QK_INT8T = 6, QK_MXFP4B = 7 };
 enum { PV_FP8 = 2, PV_MXFP4 = 3, PV_MXFP8 = 4, PV_F16 = 5 };
 
 // Padding of the token axis in every quantized buffer (a multiple of the Q tile).
@@ -18,14 +19,14 @@ constexpr int kStatChunks = 8;
 // Device pointers of one quantized buffer (offsets resolved on the host).
 struct QuantPtrs {
   float* mu_k;
-  float* mu_q;
+  float* mu_q;        // [BH, d], or [BH, Np/128, d] per 128-query block (QK_MXFP4B)
   uint8_t* q_codes;
   void* q_scales;     // fp32 [BH, nb] (INT8), fp32 [BH, Np] (INT8T) or uint8 E8M0 [BH, Np, d/32] (MXFP4)
   uint8_t* k_codes;
   void* k_scales;
   uint8_t* v_codes;
   void* v_scales;     // fp32 [BH, d] (FP8) or uint8 E8M0 [BH, Np/32, d] (MXFP4, MXFP8)
-  float* delta_s;
+  float* delta_s;     // [BH, Np], or [BH, Np/128, Np] per query block (QK_MXFP4B)
   float* lse_corr;
   double* sums;       // [2, kStatChunks, B*H, d]: K then Q token sums per chunk (K by KV instance)
   uint32_t* amax_v;   // [kStatChunks, B*H, d] bit patterns of max |V| per channel (by KV instance)

@@ -66,15 +66,19 @@ typedef enum {
  * codes with finer steps -- one per query token and one per 32 keys -- the
  * granularity each lane's scores share in the fused kernel (the finer
  * SageAttention-T / thread-level variants, review thread accuracy table in the
- * reply to tyTT W1, SageAttention2 abstract). */
+ * reply to tyTT W1, SageAttention2 abstract).  MXFP4_QBLOCK (as qk_fmt): MXFP4
+ * with Q smoothed by the mean of each 128-query block instead of the whole
+ * sequence (the pages leave the form of "smooth Q" open, SageAttention2
+ * abstract); the removed part returns as dS = mu_q(block) . K_s per block and
+ * key.  Fixed-length problems only (the packed entry returns UNSUPPORTED). */
 enum { SAGE_FMT_INT8 = 1, SAGE_FMT_FP8 = 2, SAGE_FMT_MXFP4 = 3, SAGE_FMT_MXFP8 = 4, SAGE_FMT_F16 = 5,
-       SAGE_FMT_INT8_TOKEN = 6 };
+       SAGE_FMT_INT8_TOKEN = 6, SAGE_FMT_MXFP4_QBLOCK = 7 };
 
 /* I/O element types of Q, K, V, O, dO, dQ, dK, dV. */
 enum { SAGE_DT_BF16 = 0, SAGE_DT_F16 = 1 };
 
 /* Supported (qk_fmt, pv_fmt) pairs: (INT8, FP8), (INT8, F16), (INT8_TOKEN, FP8),
- * (INT8_TOKEN, F16), (MXFP4, FP8), (MXFP4, MXFP4), (MXFP4, MXFP8). */
+ * (INT8_TOKEN, F16), (MXFP4 or MXFP4_QBLOCK, FP8 or MXFP4 or MXFP8). */
 typedef struct {
     int B, H, N, d;
     int causal;          /* 0 or 1 */
@@ -88,7 +92,8 @@ typedef struct {
  * Let BH = B*H, Np = N rounded up to a multiple of 128 (padding tokens carry
  * zero codes), nb = Np/64.
  *   mu_k      fp32 [BH, d]     channel mean of K over all N tokens
- *   mu_q      fp32 [BH, d]     channel mean of Q (MXFP4 QK only)
+ *   mu_q      fp32 [BH, d]     channel mean of Q (MXFP4 QK only; MXFP4_QBLOCK:
+ *             [BH, Np/128, d], the mean of each 128-query block)
  *   q_codes   INT8: int8 [BH, Np, d];  MXFP4: packed E2M1 [BH, Np, d/2] of
  *             Q - mu_q, element 2i in the low nibble of byte i
  *   q_scales  INT8: fp32 [BH, nb] step of each 64-token block; INT8_TOKEN:
@@ -101,7 +106,8 @@ typedef struct {
  *             F16 V: fp16 tiled [BH, Np/64, d, 64]
  *   v_scales  FP8 V: fp32 [BH, d] per-channel step;  MXFP4 and MXFP8 V: E8M0
  *             bytes [BH, Np/32, d] per 32-token group per channel
- *   delta_s   fp32 [BH, Np]    mu_q . (k_t - mu_k), added to every score (MXFP4 QK)
+ *   delta_s   fp32 [BH, Np]    mu_q . (k_t - mu_k), added to every score (MXFP4 QK;
+ *             MXFP4_QBLOCK: [BH, Np/128, Np], one row per query block)
  *   lse_corr  fp32 [BH, N]     sm_scale * q_t . mu_k, added to the LSE only
  *   stats     fp64 / uint32 per-chunk partials of the smoothing statistics (scratch)
  */

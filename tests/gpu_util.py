@@ -55,20 +55,26 @@ def unpack_int8_fp8(buf, p, lay, pv="fp8", fine=False):
     return r
 
 
-def unpack_mxfp4(buf, p, lay, pv_fmt):
+def unpack_mxfp4(buf, p, lay, pv_fmt, qblock=False):
+    """qblock: Q smoothed per 128-query block (mu_q [BH, NB, d], dS [BH, NB, N])."""
     b = buf.cpu().numpy()
     BH, N, d = p.B * p.H, p.N, p.d
     Np = (N + 127) // 128 * 128
+    nb = Np // 128 if qblock else 1
     r = {"mu_k": part(b, lay, "mu_k", np.float32, BH * d).reshape(BH, d),
-         "mu_q": part(b, lay, "mu_q", np.float32, BH * d).reshape(BH, d)}
+         "mu_q": part(b, lay, "mu_q", np.float32, BH * nb * d).reshape((BH, nb, d) if qblock else (BH, d))}
     for t in ("q", "k"):
         pk = part(b, lay, f"{t}_codes", np.uint8, BH * Np * d // 2).reshape(BH, Np, d // 2)
         r[f"{t}c_all"] = unpack_nibbles(pk, d)
         r[f"{t}c"] = r[f"{t}c_all"][:, :N]
         r[f"{t}e_all"] = part(b, lay, f"{t}_scales", np.uint8, BH * Np * d // 32).reshape(BH, Np, d // 32)
         r[f"{t}e"] = r[f"{t}e_all"][:, :N]
-    r["dS_all"] = part(b, lay, "delta_s", np.float32, BH * Np).reshape(BH, Np)
-    r["dS"] = r["dS_all"][:, :N]
+    if qblock:
+        r["dS_all"] = part(b, lay, "delta_s", np.float32, BH * nb * Np).reshape(BH, nb, Np)
+        r["dS"] = r["dS_all"][:, :, :N]
+    else:
+        r["dS_all"] = part(b, lay, "delta_s", np.float32, BH * Np).reshape(BH, Np)
+        r["dS"] = r["dS_all"][:, :N]
     r["corr"] = part(b, lay, "lse_corr", np.float32, BH * N).reshape(BH, N)
     if pv_fmt in ("fp8", "mxfp8"):
         vt = part(b, lay, "v_codes", np.uint8, BH * Np * d).reshape(BH, Np // 64, d, 64)

@@ -41,7 +41,8 @@ def _p(**kw):
     (dict(sm_scale=float("inf")), S.ERR_INVALID_ARG), (dict(causal=2), S.ERR_INVALID_ARG),
     (dict(io_dtype=7), S.ERR_INVALID_ARG), (dict(qk_fmt=9), S.ERR_INVALID_ARG),
     (dict(qk_fmt=2, pv_fmt=2), S.ERR_UNSUPPORTED), (dict(qk_fmt=1, pv_fmt=3), S.ERR_UNSUPPORTED),
-    (dict(qk_fmt=1, pv_fmt=4), S.ERR_UNSUPPORTED), (dict(pv_fmt=7), S.ERR_INVALID_ARG),
+    (dict(qk_fmt=1, pv_fmt=4), S.ERR_UNSUPPORTED), (dict(pv_fmt=8), S.ERR_INVALID_ARG),
+    (dict(qk_fmt=7, pv_fmt=5), S.ERR_UNSUPPORTED), (dict(qk_fmt=1, pv_fmt=7), S.ERR_UNSUPPORTED),
     (dict(qk_fmt=6, pv_fmt=3), S.ERR_UNSUPPORTED), (dict(qk_fmt=2, pv_fmt=6), S.ERR_UNSUPPORTED),
     (dict(qk_fmt=3, pv_fmt=5), S.ERR_UNSUPPORTED),
 ])
@@ -77,7 +78,7 @@ def test_workspace_too_small_rejected():
 
 def test_quant_layout_sizes():
     """Offsets are 256-byte aligned, ordered, and each part has the documented size."""
-    for qk, pv in ((1, 2), (1, 5), (6, 2), (6, 5), (3, 2), (3, 3), (3, 4)):
+    for qk, pv in ((1, 2), (1, 5), (6, 2), (6, 5), (3, 2), (3, 3), (3, 4), (7, 2), (7, 3)):
         for N in (1, 100, 4096):
             p = _p(N=N, qk_fmt=qk, pv_fmt=pv)
             total, lay = S.quant_size(p)
@@ -85,8 +86,11 @@ def test_quant_layout_sizes():
             offs = [lay[k] for k in ("mu_k", "mu_q", "q_codes", "q_scales", "k_codes", "k_scales",
                                      "v_codes", "v_scales", "delta_s", "lse_corr", "stats")]
             assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
-            codes = BH * Np * d // (2 if qk == 3 else 1)
+            codes = BH * Np * d // (2 if qk in (3, 7) else 1)
             assert lay["q_scales"] - lay["q_codes"] >= codes
+            if qk == 7:      # a Q mean per 128-query block, a dS row per block
+                assert lay["q_codes"] - lay["mu_q"] >= BH * (Np // 128) * d * 4
+                assert lay["lse_corr"] - lay["delta_s"] >= BH * (Np // 128) * Np * 4
             if qk == 6:      # a step per query token and per 32 keys
                 assert lay["k_codes"] - lay["q_scales"] >= BH * Np * 4
                 assert lay["v_codes"] - lay["k_scales"] >= BH * Np // 32 * 4
@@ -138,6 +142,7 @@ def _vp(**kw):
     (dict(total_q=-1), S.ERR_INVALID_ARG), (dict(max_seqlen_k=-5), S.ERR_INVALID_ARG),
     (dict(d=96), S.ERR_UNSUPPORTED), (dict(qk_fmt=1, pv_fmt=3), S.ERR_UNSUPPORTED),
     (dict(sm_scale=float("nan")), S.ERR_INVALID_ARG), (dict(total_q=2 ** 31 - 1), S.ERR_INVALID_ARG),
+    (dict(qk_fmt=7, pv_fmt=2), S.ERR_UNSUPPORTED),
 ])
 def test_varlen_validation(kw, status):
     L = S.lib()

@@ -57,6 +57,10 @@ CASES = [
      1 / math.sqrt(128)),
     ("int8tok_f16pv_ragged_d64", 2, 2, 777, 64, "bf16", False, "int8_token", "f16", 2, 3.0, 0.01, 1 / 8),
     ("int8tok_d64_f16", 1, 2, 256, 64, "f16", False, "int8_token", "fp8", 0, 4.0, 0.0, 1 / 8),
+    ("mxfp4qb_fp8_d128", 1, 3, 600, 128, "bf16", False, "mxfp4_qblock", "fp8", 3, 5.0, 0.0, 1 / math.sqrt(128)),
+    ("mxfp4qb_mxfp4_causal_d64", 1, 2, 333, 64, "bf16", True, "mxfp4_qblock", "mxfp4", 6, 5.0, 0.0, 1 / 8),
+    ("mxfp4qb_mxfp8_causal_d128_f16", 1, 2, 700, 128, "f16", True, "mxfp4_qblock", "mxfp8", 10, 3.0, 0.01,
+     1 / math.sqrt(128)),
 ]
 
 
@@ -75,13 +79,13 @@ def _oracle_quant(f, qk, pv, sm):
         fine = qk == "int8_token"
         return oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm, pv_fmt=pv, qblk=1 if fine else 64,
                                      kblk=32 if fine else 64)
-    return oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv)
+    return oracle.quant_mxfp4(f["q"], f["k"], f["v"], sm, pv_fmt=pv, qsb=128 if qk == "mxfp4_qblock" else 0)
 
 
 def _unpack(buf, p, lay, qk, pv):
     if qk.startswith("int8"):
         return unpack_int8_fp8(buf, p, lay, pv, fine=qk == "int8_token")
-    return unpack_mxfp4(buf, p, lay, pv)
+    return unpack_mxfp4(buf, p, lay, pv, qblock=qk == "mxfp4_qblock")
 
 
 def _oracle_sim(f, qz_or, qk, pv, N, d, causal, sm, rows=None):
@@ -155,7 +159,7 @@ def test_forward_edge_lengths(sage, N, causal):
     banner(f"edge N={N} causal={causal}")
     for qk, d, pv in (("int8", 64, "fp8"), ("int8", 128, "fp8"), ("mxfp4", 128, "fp8"), ("mxfp4", 64, "mxfp4"),
                       ("mxfp4", 128, "mxfp8"), ("int8", 128, "f16"), ("int8_token", 128, "fp8"),
-                      ("int8_token", 64, "f16")):
+                      ("int8_token", 64, "f16"), ("mxfp4_qblock", 128, "fp8")):
         f, g = _inputs(1, 2, N, d, "bf16", 100 + N, 2.0)
         sm = 1 / math.sqrt(d)
         o, lse = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv,
@@ -239,8 +243,36 @@ def test_forward_constant_keys_f16_pv(sage):
         assert np.all(np.abs(o - want) <= np.abs(want) * 2.0 ** -8 + 1e-5 * np.abs(vdq).max())
 
 
+@pytest.mark.parametrize("pv", ["fp8", "mxfp4"])
+def test_forward_block_q_smoothing_under_drift(sage, pv):
+    """Q with channel offsets that drift along the sequence: the per-block smoothing path matches
+    the oracle and is closer to exact attention than smoothing over the whole sequence."""
+    import oracle
+    banner(f"block Q smoothing drift {pv}")
+    B, H, N, d = 1, 2, 1000, 128
+    g0 = torch.Generator().manual_seed(31)
+    q = torch.randn(B, H, N, d, generator=g0) + torch.linspace(-1, 1, N)[None, None, :, None] * \
+        6 * torch.randn(B, H, 1, d, generator=g0)
+    k = torch.randn(B, H, N, d, generator=g0) + 4 * torch.randn(B, H, 1, d, generator=g0)
+    v = torch.randn(B, H, N, d, generator=g0)
+    x = {n: t.to(torch.bfloat16) for n, t in zip("qkv", (q, k, v))}
+    f = {n: x[n].float().numpy().reshape(B * H, N, d) for n in "qkv"}
+    sm = 1 / math.sqrt(d)
+    o_ref, _ = oracle.attn_ref(f["q"], f["k"], f["v"], False, sm)
+    cs = {}
+    for qk in ("mxfp4", "mxfp4_qblock"):
+        o = sage.sageattn(*(x[n].to(device()) for n in "qkv"), sm_scale=sm, qk_fmt=qk, pv_fmt=pv)
+        torch.cuda.synchronize()
+        o = to_np64(o).reshape(B * H, N, d)
+        o_sim, _ = _oracle_sim(f, _oracle_quant(f, qk, pv, sm), qk, pv, N, d, False, sm)
+        assert np.abs(o - o_sim).max() <= 2e-2 and cos(o, o_sim) >= 0.9999, qk
+        cs[qk] = cos(o, o_ref)
+    assert cs["mxfp4_qblock"] > cs["mxfp4"]
+
+
 FULL = [("int8_fp8_causal_b1h32n4096d128", "fp8"), ("int8_fp8_b2h24n16384d64", "fp8"),
         ("int8_fp8_b1h32n8192d128", "f16"), ("int8_fp8_causal_b1h32n4096d128", "fp8", "int8_token"),
+        ("mxfp4_b4h32n8192d128", "fp8", "mxfp4_qblock"),
         ("mxfp4_b4h32n8192d128", "fp8"), ("mxfp4_b4h32n8192d128", "mxfp4"), ("mxfp4_b4h32n8192d128", "mxfp8"),
         ("int8_fp8_b1h2n256d64", "fp8")]
 
