@@ -57,6 +57,80 @@ def read_traffic():
     return float(kv["hbm_bytes_per_launch"])
 
 
+def _short(kname):
+    return kname.replace("void ", "").split("(")[0]
+
+
+def dispatch_counters(path):
+    """{(kernel, grid): {counter: [per-dispatch values]}} plus per-dispatch durations (ns)."""
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    per, dur = {}, {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]) // int(r["Workgroup_Size"]))
+            d = per.setdefault(key, {}).setdefault(r["Counter_Name"], {})
+            did = (f, r["Dispatch_Id"])
+            d[did] = d.get(did, 0.0) + float(r["Counter_Value"])
+            dur.setdefault(key, {})[did] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return ({k: {c: list(v.values()) for c, v in cs.items()} for k, cs in per.items()},
+            {k: list(v.values()) for k, v in dur.items()})
+
+
+def counter_summary(sq_dir, fetch_dir, write_dir, out_path):
+    """Markdown profile: MFMA busy share per fused-kernel launch shape (SQ counters) and the
+    prologue kernels' HBM bytes (FETCH_SIZE / WRITE_SIZE, copy-calibrated) per launch."""
+    mean = lambda v: sum(v) / len(v)
+    sq, _ = dispatch_counters(sq_dir)
+    lines = ["# MFMA busy share of the fused kernels and HBM bytes of the prologue", "",
+             "Commands (repository root, one MI355X):", "",
+             "    rocprofv3 --pmc SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_VALU "
+             "SQ_INSTS_MFMA SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES SQ_WAIT_ANY --output-format csv -d <sq_dir> -- "
+             "python bench.py --steps 5 --warmup 2 --no-cpu",
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python bench.py --steps 3 --warmup 1 "
+             "--no-cpu --no-extra --copy-calib",
+             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python bench.py --steps 3 --warmup 1 "
+             "--no-cpu --no-extra --copy-calib",
+             "    python bench.py --counters <sq_dir> <fetch_dir> <write_dir>", "",
+             "## Fused kernels: MFMA busy share", "",
+             "SQ_BUSY_CYCLES is summed over the 32 shader engines and SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs,",
+             "so MFMA busy = MFMA_BUSY / (1024 * BUSY / 32): the share of the kernel's time the matrix cores of",
+             "an average SIMD were busy.  Co-exec is the share of MFMA busy time that overlapped vector issue.",
+             "Template arguments: <head dim, QK format (1 INT8, 3 MXFP4), causal, I/O dtype, P~V format (2 FP8,",
+             "3 MXFP4, 4 MXFP8, 5 fp16), finer INT8 steps>.", "",
+             "| kernel | workgroups | dispatches | MFMA busy | co-exec | VALU instr. per MFMA | wait share of wave cycles |",
+             "|---|---|---|---|---|---|---|"]
+    for (k, g), cs in sorted(sq.items(), key=lambda kv: (kv[0][0], -kv[0][1])):
+        if "attn_fwd_kernel" not in k or "SQ_BUSY_CYCLES" not in cs:
+            continue
+        busy = mean(cs["SQ_BUSY_CYCLES"]) / 32.0
+        mfma = mean(cs.get("SQ_VALU_MFMA_BUSY_CYCLES", [0])) / 1024.0
+        coex = mean(cs.get("SQ_VALU_MFMA_COEXEC_CYCLES", [0])) / 1024.0
+        vpm = mean(cs.get("SQ_INSTS_VALU", [0])) / max(1.0, mean(cs.get("SQ_INSTS_MFMA", [1])))
+        wait = mean(cs.get("SQ_WAIT_ANY", [0])) / max(1.0, mean(cs.get("SQ_WAVE_CYCLES", [1])))
+        lines.append(f"| `{k}` | {g} | {len(cs['SQ_BUSY_CYCLES'])} | {100 * mfma / busy:.1f} % | "
+                     f"{100 * coex / max(mfma, 1e-9):.0f} % | {vpm:.1f} | {100 * wait:.0f} % |")
+    fe, fdur = dispatch_counters(fetch_dir)
+    wr, _ = dispatch_counters(write_dir)
+    copy = lambda d, c: max(mean(v[c]) for k, v in d.items() if "sage" not in k[0] and c in v)
+    ff = COPY_BYTES / (copy(fe, "FETCH_SIZE") * 1024.0)
+    fw = COPY_BYTES / (copy(wr, "WRITE_SIZE") * 1024.0)
+    lines += ["", "## Prologue kernels on the headline workload (B=1 H=32 N=4096 d=128, INT8-QK / FP8-PV)", "",
+              f"FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by {ff:.4f} and {fw:.4f}: the byte counts a",
+              f"plain {COPY_BYTES >> 20} MiB device copy reads and writes in the same runs.  The durations are the",
+              "counter runs' own dispatch timestamps (serialised dispatches), so the rates are a floor.", "",
+              "| kernel | workgroups | HBM read (MB) | HBM write (MB) | duration (us) | GB/s |", "|---|---|---|---|---|---|"]
+    for (k, g), cs in sorted(fe.items()):
+        if not ("stats_kernel" in k or "quant_" in k) or (k, g) not in wr:
+            continue
+        rd = mean(cs["FETCH_SIZE"]) * 1024.0 * ff / 1e6
+        wt = mean(wr[(k, g)]["WRITE_SIZE"]) * 1024.0 * fw / 1e6
+        us = mean(fdur[(k, g)]) / 1e3
+        lines.append(f"| `{k}` | {g} | {rd:.1f} | {wt:.1f} | {us:.1f} | {(rd + wt) * 1e3 / us:.0f} |")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def counters(path, name):
     """Mean per-dispatch value of counter `name` for our fused kernel, and the copy kernel's value."""
     files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
@@ -280,7 +354,12 @@ def main():
     ap.add_argument("--copy-calib", action="store_true", help="run one 1 GiB device copy at the end (counter calibration)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the roofline traffic summary from two rocprofv3 counter runs and exit")
+    ap.add_argument("--counters", nargs=3, metavar=("SQ_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the MFMA-busy / prologue-HBM profile summary from rocprofv3 counter runs and exit")
     args = ap.parse_args()
+    if args.counters:
+        counter_summary(*args.counters, os.path.join(ROOT, "profiles", "counters_attn_fwd_and_prologue.md"))
+        return
     if args.traffic:
         traffic_summary(*args.traffic)
         return
