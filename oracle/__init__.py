@@ -51,6 +51,12 @@ def lib():
     return _lib
 
 
+def set_p_decision_fp32(on):
+    """P~ codes decided in the fused kernel's fp32 arithmetic (on, the default) or from the fp64
+    scores (off).  A process-wide switch: whoever turns it off turns it back on."""
+    lib().or_set_p_decision_fp32(int(bool(on)))
+
+
 def _p(a):
     return a.ctypes.data_as(ctypes.c_void_p)
 

@@ -488,6 +488,22 @@ static int64_t int8_dot(const head_t *H, int i, int j)
 static int g_p32 = 1;
 OR_API void or_set_p_decision_fp32(int on) { g_p32 = on; }
 
+/* MXFP4 QK: the dot product of the decoded MX codes of query i and key j.  Each 32-channel
+ * block sums to a multiple of 2^-2 times its scale pair, below 2^11 of it, so fp64 holds the
+ * total exactly while the scale pairs of a row lie within 40 binades of each other. */
+static double mx_dot(const head_t *H, int i, int j)
+{
+    int d = H->d, ng = d / 32;
+    double s = 0.0;
+    for (int g = 0; g < ng; g++) {
+        double part = 0.0;
+        for (int c = 32 * g; c < 32 * g + 32; c++)
+            part += or_e2m1_decode(H->q4[(int64_t)i * d + c]) * or_e2m1_decode(H->k4[(int64_t)j * d + c]);
+        s += part * ldexp(1.0, (int)H->qe[(int64_t)i * ng + g] - 127) * ldexp(1.0, (int)H->ke[(int64_t)j * ng + g] - 127);
+    }
+    return s;
+}
+
 /* Unscaled score s_ij (sm not applied). */
 static double score(const head_t *H, int i, int j)
 {
@@ -504,14 +520,7 @@ static double score(const head_t *H, int i, int j)
             acc += (int64_t)H->qc[(int64_t)i * d + c] * (int64_t)H->kc[(int64_t)j * d + c];
         s = (double)H->qs[i / H->qblk] * (double)H->ks[j / H->kblk] * (double)acc;
     } else {
-        int ng = d / 32;
-        for (int g = 0; g < ng; g++) {
-            double part = 0.0;
-            for (int c = 32 * g; c < 32 * g + 32; c++)
-                part += or_e2m1_decode(H->q4[(int64_t)i * d + c]) * or_e2m1_decode(H->k4[(int64_t)j * d + c]);
-            s += part * ldexp(1.0, (int)H->qe[(int64_t)i * ng + g] - 127)
-                      * ldexp(1.0, (int)H->ke[(int64_t)j * ng + g] - 127);
-        }
+        s = mx_dot(H, i, j);
         if (H->dS)
             s += (double)H->dS[(int64_t)(H->qsb ? i / H->qsb : 0) * H->N + j];
     }
@@ -569,26 +578,36 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
         }
         l = alpha * l + psum;
         /* The P~ codes are quantized values that floating point decides, so on the INT8 paths
-         * (where every input of that decision is reproducible) they are decided in the fused
-         * kernel's fp32 arithmetic: c = fl32(fl32(step_q * fl32(sm * log2 e)) * step_k), the
-         * tile max fl32(score * c) folded into an fp32 running max m, and p = exp2 of the fp32
-         * FMA score * c + (log2 s - m), rounded to fp32 (s = 448 for FP8, 1 for fp16).  Only
-         * the codes come from this; the row sum, the rescales and the LSE stay fp64. */
+         * and on the MXFP4-QK paths with FP8 P~ (where every input of that decision is
+         * reproducible) they are decided in the fused kernel's fp32 arithmetic.  The exp2
+         * argument is the fp32 FMA a * c + (log2 s - m), with (a, c) = (the INT8 code dot
+         * product, fl32(fl32(step_q * fl32(sm * log2 e)) * step_k)) or (u, 1) for MXFP4, where
+         * u = fma(fl32(S), fl32(sm * log2 e), fl32(dS * fl32(sm * log2 e))) and S is the exact
+         * MX code dot product; the tile max fl32(a * c) is folded into an fp32 running max m,
+         * and p = exp2(...) is rounded to fp32 (s = 448 for FP8, 1 for fp16).  Only the codes
+         * come from this; the row sums, the rescales and the LSE stay fp64. */
         float *p32 = NULL;
-        if (g_p32 && H->qk == QK_INT8 && (H->pv == PV_FP8 || H->pv == PV_F16)) {
+        int dec32 = (H->qk == QK_INT8 && (H->pv == PV_FP8 || H->pv == PV_F16)) ||
+                    (H->qk == QK_MXFP4 && (H->pv == PV_FP8 || H->pv == PV_MXFP8));
+        if (g_p32 && dec32) {
             p32 = malloc(sizeof(float) * (size_t)n);
             const float sml2e = (float)H->sm * 1.4426950408889634f;
-            const float qstep = H->qs[i / H->qblk] * sml2e;
             float mt32 = -INFINITY;
             float *c32 = malloc(sizeof(float) * (size_t)n);
-            int64_t *a32 = malloc(sizeof(int64_t) * (size_t)n);
+            float *a32 = malloc(sizeof(float) * (size_t)n);
             for (int jj = 0; jj < n; jj++) {
                 int j = j0 + jj;
-                float c = qstep * H->ks[j / H->kblk];
-                c32[jj] = c == 0.0f ? 1.0f : c;
-                a32[jj] = int8_dot(H, i, j);
+                if (H->qk == QK_INT8) {
+                    float c = H->qs[i / H->qblk] * sml2e * H->ks[j / H->kblk];
+                    c32[jj] = c == 0.0f ? 1.0f : c;
+                    a32[jj] = (float)int8_dot(H, i, j);     /* |a| < 2^24: exact */
+                } else {
+                    float ds = H->dS ? H->dS[(int64_t)(H->qsb ? i / H->qsb : 0) * H->N + j] * sml2e : 0.0f;
+                    c32[jj] = 1.0f;
+                    a32[jj] = fmaf((float)mx_dot(H, i, j), sml2e, ds);
+                }
                 if (x[jj] != -INFINITY) {
-                    float t = (float)a32[jj] * c32[jj];
+                    float t = a32[jj] * c32[jj];
                     if (t > mt32)
                         mt32 = t;
                 }
@@ -598,7 +617,7 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
             float mref = mnew == -INFINITY ? 0.0f : mnew;
             float off = (H->pv == PV_F16 ? 0.0f : 8.807354922057604f) - mref;
             for (int jj = 0; jj < n; jj++)
-                p32[jj] = x[jj] == -INFINITY ? 0.0f : (float)exp2((double)fmaf((float)a32[jj], c32[jj], off));
+                p32[jj] = x[jj] == -INFINITY ? 0.0f : (float)exp2((double)fmaf(a32[jj], c32[jj], off));
             free(c32);
             free(a32);
         }

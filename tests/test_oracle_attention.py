@@ -351,6 +351,80 @@ def test_constant_keys_give_mean_of_values(orc, path):
         assert np.allclose(o, want, rtol=1e-14, atol=1e-14 * np.abs(v64).max())
 
 
+@pytest.mark.parametrize("path", ["int8_fp8", "mxfp4_fp8", "mxfp4_mxfp8"])
+def test_fp8_p_worked_example(orc, path):
+    """A worked example of the FP8 P~ reading, computed by hand.  Two keys whose smoothed
+    scores are +-1.25 in log2 units (sm = ln 2): p = (1, 2^-2.5), so 448 p = (448, 79.196), whose
+    nearest E4M3 values are 448 and 80 (step 8 in [64, 128)).  The output divides by the
+    unquantized sum 448 (1 + 2^-2.5) = 527.196: V rows e0 and e1 give (0.849783, 0.151746) -- the
+    exact weight for the max key, the rounded one for the other (exact: 0.150217; dividing by
+    the quantized sum 528 would give 0.848485, 0.151515).  A causal first row sees one key and
+    is exact.  The LSE is exact attention's."""
+    BH, N, d = 1, 2, 64
+    q = np.zeros((BH, N, d), np.float32)
+    q[:, :, 0] = 1.0
+    k = np.zeros((BH, N, d), np.float32)
+    k[0, 0, 0], k[0, 1, 0] = 1.25, -1.25
+    v = np.zeros((BH, N, d), np.float32)
+    v[0, 0, 0], v[0, 1, 1] = 1.0, 1.0
+    sm = LN2
+    qk, pv = path.split("_")
+    l = 448.0 * (1.0 + 2.0 ** -2.5)
+    want = [448.0 / l, 80.0 / l]
+    for causal in (False, True):
+        if qk == "int8":
+            qz = orc.quant_int8_fp8(q, k, v, sm, pv_fmt=pv)
+            o, lse = orc.attn_int8_fp8(qz, N, d, causal, sm, 64)
+        else:
+            qz = orc.quant_mxfp4(q, k, v, sm, pv_fmt=pv)
+            o, lse = orc.attn_mxfp4(qz, N, d, causal, sm, 64)
+        _, lse_ref = orc.attn_ref(q, k, v, causal, sm)
+        assert np.allclose(lse, lse_ref, rtol=0, atol=1e-6)
+        assert np.allclose(o[0, 1, :2], want, rtol=1e-6, atol=0)
+        assert np.allclose(o[0, 0, :2], [1.0, 0.0] if causal else want, rtol=1e-6, atol=1e-7)
+        assert not o[0, :, 2:].any()
+
+
+@pytest.mark.parametrize("path", ["int8_fp8", "int8_f16", "mxfp4_fp8", "mxfp4_mxfp8"])
+def test_fp32_p_decisions_agree_with_fp64_scores(orc, path):
+    """On these paths the P~ codes are decided in the fused kernel's fp32 arithmetic.  Taken
+    instead from the fp64 scores, a code can only move where an fp32 rounding of the exp2
+    argument crosses an E4M3 (fp16) rounding midpoint, and then by one step of one weight: with
+    E4M3's 2^-4 relative step almost every row is identical; fp16's 2^-11 step is crossed more
+    often, by a much smaller amount.  A slip in the fp32 path's formula (a dropped dS, a missing
+    log2 e, the wrong step) would move every row by far more."""
+    rng = np.random.default_rng(61)
+    BH, N, d = 2, 200, 64
+    q = rng.standard_normal((BH, N, d)).astype(np.float32)
+    k = (rng.standard_normal((BH, N, d)) + 2.0 * rng.standard_normal((BH, 1, d))).astype(np.float32)
+    v = rng.standard_normal((BH, N, d)).astype(np.float32)
+    q += 1.5 * rng.standard_normal((BH, 1, d)).astype(np.float32)
+    sm = 1.0 / math.sqrt(d)
+    qk, pv = path.split("_")
+    outs = []
+    for on in (1, 0):
+        orc.set_p_decision_fp32(on)
+        try:
+            for causal in (False, True):
+                if qk == "int8":
+                    qz = orc.quant_int8_fp8(q, k, v, sm, pv_fmt=pv)
+                    outs.append(orc.attn_int8_fp8(qz, N, d, causal, sm, 64))
+                else:
+                    qz = orc.quant_mxfp4(q, k, v, sm, pv_fmt=pv)
+                    outs.append(orc.attn_mxfp4(qz, N, d, causal, sm, 64))
+        finally:
+            orc.set_p_decision_fp32(1)
+    for (o32, l32), (o64, l64) in zip(outs[:2], outs[2:]):
+        assert np.array_equal(l32, l64)                    # the row sums and LSE stay fp64
+        same = np.all(o32 == o64, axis=-1)
+        if pv == "f16":
+            assert same.mean() >= 0.5
+            assert np.abs(o32 - o64).max() <= 2.0 ** -10 * np.abs(v).max()
+        else:
+            assert same.mean() >= 0.98
+            assert np.abs(o32 - o64).max() <= 0.05 * np.abs(v).max()
+
+
 def test_int8_fp8_key_shift_gives_identical_codes_and_output(orc):
     """Smoothing K removes a per-channel shift shared by all tokens: shifted inputs give the
     same codes and the same output (inputs chosen so the shift is exact in fp32)."""
