@@ -414,6 +414,10 @@ def main():
         log("[bench] secondary train_causal_b8h16n2048d64 (forward + 8-bit backward)")
         extra["train_causal_b8h16n2048d64"] = run_backward("train_causal_b8h16n2048d64", S, torch,
                                                            max(5, args.steps // 5), 3)
+        torch.cuda.empty_cache()
+        log("[bench] secondary train_causal_b8h16n2048d128 (forward + 8-bit backward, d = 128)")
+        extra["train_causal_b8h16n2048d128"] = run_backward("train_causal_b8h16n2048d128", S, torch,
+                                                            max(5, args.steps // 5), 3)
         out["other_workloads"] = extra
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle)")

@@ -328,8 +328,10 @@ __device__ __forceinline__ int quant_ds(const float* x, float a0, float a1, int 
 // ---- key-stationary kernel: dK and dV ----
 // Workgroup: 128 keys (4 waves x 32), loops over 64-query tiles.  LDS per stage:
 // Q rows, dO rows (token-major), dO^T and Q^T (channel rows), lse2 and D (64 floats each).
+// d = 128 doubles the accumulators (dK^T, dV^T: 128 registers) and the operand tiles, so one
+// workgroup runs per CU there, with the accumulators in the AGPR half of the register file.
 template <int D, bool CAUSAL, int DT>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdPtrs bp, void* dk, void* dv, int N, int Np, int BH, float sm) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdPtrs bp, void* dk, void* dv, int N, int Np, int BH, float sm) {
   constexpr int TB = 64 * D;                          // one tile of 64 x D bytes
   constexpr int STAGE = 4 * TB + 2 * 64 * 4 + 16;   // + the tile's Q step and dO step
   constexpr int NCB = D / 32;
@@ -496,9 +498,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdPtrs bp, void* dk, 
 
 // ---- query-stationary kernel: dQ ----
 // Workgroup: 128 queries (4 waves x 32), loops over 64-key tiles.  LDS per stage:
-// K_s rows (INT8), V rows (FP8), K_s^T (channel rows, FP8).
+// K_s rows (INT8), V rows (FP8), K_s^T (channel rows, FP8).  One workgroup per CU at d = 128,
+// as for the dK/dV kernel.
 template <int D, bool CAUSAL, int DT>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdPtrs bp, void* dq, int N, int Np, int BH, float sm) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdPtrs bp, void* dq, int N, int Np, int BH, float sm) {
   constexpr int TB = 64 * D;
   constexpr int STAGE = 3 * TB + 16;   // + the tile's K step and V step
   constexpr int NCB = D / 32;
@@ -723,9 +726,11 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
                            const void* dout, const float* lse, void* dq, void* dk, void* dv, void* ws,
                            size_t qbytes, const QuantPtrs& qp, hipStream_t stream) {
   uint8_t* w = static_cast<uint8_t*>(ws);
-  if (s.d != 64) return hipErrorNotSupported;
-  return s.io_dtype == 0 ? bwd_run<0, 64>(s, q, k, v, o, dout, lse, dq, dk, dv, w, qbytes, qp, stream)
-                         : bwd_run<1, 64>(s, q, k, v, o, dout, lse, dq, dk, dv, w, qbytes, qp, stream);
+  if (s.d == 64)
+    return s.io_dtype == 0 ? bwd_run<0, 64>(s, q, k, v, o, dout, lse, dq, dk, dv, w, qbytes, qp, stream)
+                           : bwd_run<1, 64>(s, q, k, v, o, dout, lse, dq, dk, dv, w, qbytes, qp, stream);
+  return s.io_dtype == 0 ? bwd_run<0, 128>(s, q, k, v, o, dout, lse, dq, dk, dv, w, qbytes, qp, stream)
+                         : bwd_run<1, 128>(s, q, k, v, o, dout, lse, dq, dk, dv, w, qbytes, qp, stream);
 }
 
 }  // namespace sage

@@ -340,7 +340,6 @@ sage_status sage_attn_bwd_ws_size(const sage_problem* p, size_t* bytes) {
   if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
   if (p->qk_fmt != SAGE_FMT_INT8 || p->pv_fmt != SAGE_FMT_FP8)
     return fail(SAGE_ERR_UNSUPPORTED, "the backward supports qk_fmt=INT8, pv_fmt=FP8 only");
-  if (p->d != 64) return fail(SAGE_ERR_UNSUPPORTED, "the backward supports head dim 64 only in this build");
   sage_quant_layout L;
   compute_layout(p, &L);
   *bytes = L.total + sage::attn_bwd_ws_bytes(to_shape(p));

@@ -46,6 +46,10 @@ WORKLOADS = {
     "train_causal_b8h16n2048d64": dict(B=8, H=16, N=2048, d=64, causal=True, dtype="bf16",
                                        qk_fmt="int8", pv_fmt="fp8", seed=4, k_off_std=0.0,
                                        outlier_frac=0.0, sm_scale=1.0 / 8, with_do=True),
+    # The same training shape at head dimension 128.
+    "train_causal_b8h16n2048d128": dict(B=8, H=16, N=2048, d=128, causal=True, dtype="bf16",
+                                        qk_fmt="int8", pv_fmt="fp8", seed=7, k_off_std=0.0,
+                                        outlier_frac=0.0, sm_scale=1.0 / math.sqrt(128), with_do=True),
     # Long-sequence d=128 INT8/FP8 sweep points (LLM-prefill generator).
     "int8_fp8_b1h32n8192d128": dict(B=1, H=32, N=8192, d=128, causal=False, dtype="bf16",
                                     qk_fmt="int8", pv_fmt="fp8", seed=5, k_off_std=5.0,

@@ -158,8 +158,8 @@ sage_status sage_attn_bwd_ws_size(const sage_problem *p, size_t *bytes);
 /*
  * 8-bit backward.  q, k, v, o, dout: device [B,H,N,d] (bf16 or fp16 as
  * p->io_dtype; o is the forward output); lse: device fp32 [B,H,N] from the
- * forward; dq, dk, dv: device outputs [B,H,N,d].  p->qk_fmt must be INT8,
- * p->pv_fmt FP8 and p->d 64 (other problems: SAGE_ERR_UNSUPPORTED).  ws: device
+ * forward; dq, dk, dv: device outputs [B,H,N,d].  p->qk_fmt must be INT8 and
+ * p->pv_fmt FP8 (other pairs: SAGE_ERR_UNSUPPORTED); d is 64 or 128.  ws: device
  * workspace of at least sage_attn_bwd_ws_size bytes (the forward's quantized
  * buffer followed by the backward's operand tiles).
  */

@@ -119,7 +119,13 @@ def test_backward_rejects_unsupported_problems():
     L = S.lib()
     n = ctypes.c_size_t()
     assert L.sage_attn_bwd_ws_size(ctypes.byref(_p(qk_fmt=3, pv_fmt=2)), ctypes.byref(n)) == S.ERR_UNSUPPORTED
-    assert L.sage_attn_bwd_ws_size(ctypes.byref(_p(d=128)), ctypes.byref(n)) == S.ERR_UNSUPPORTED
+    assert L.sage_attn_bwd_ws_size(ctypes.byref(_p(d=96)), ctypes.byref(n)) == S.ERR_UNSUPPORTED
+    assert L.sage_attn_bwd_ws_size(ctypes.byref(_p(d=128)), ctypes.byref(n)) == S.OK
+    # the forward's quantized buffer, then five 8-bit operand tensors (dO, V token-major; dO^T,
+    # Q^T, K_s^T) of BH x Np x d bytes each, plus steps, D and the log2-domain LSE
+    quant128, _ = S.quant_size(_p(d=128))
+    BH, Np = 2, 128
+    assert n.value >= quant128 + 5 * BH * Np * 128 + 2 * BH * Np * 4
     assert L.sage_attn_bwd_ws_size(ctypes.byref(_p(d=64)), ctypes.byref(n)) == S.OK
     quant, _ = S.quant_size(_p(d=64))
     assert n.value > quant

@@ -1,6 +1,6 @@
 """GPU 8-bit backward (dQ, dK, dV) against exact fp64 gradients of softmax attention:
-cosine >= 0.99 per gradient, on small ragged cases and on the training workload
-(B=8 H=16 N=2048 d=64, causal) for sampled heads."""
+cosine >= 0.99 per gradient, on small ragged cases at d = 64 and 128, on the training
+workload (B=8 H=16 N=2048 d=64, causal) and on a d = 128 causal case, for sampled heads."""
 import math
 
 import numpy as np
@@ -29,13 +29,14 @@ def _run(S, x, causal, sm):
     return o, lse, dq, dk, dv
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N,dtype", [(300, "bf16"), (64, "bf16"), (129, "f16")])
-def test_backward_matches_fp64(sage, causal, N, dtype):
+def test_backward_matches_fp64(sage, causal, N, dtype, d):
     import oracle
     from bit_quantized_attention_smooth_amd.workloads import make_inputs, as_u16
-    banner(f"backward N={N} causal={causal} {dtype}")
-    B, H, d, sm = 1, 2, 64, 1 / 8
+    banner(f"backward N={N} causal={causal} {dtype} d={d}")
+    B, H, sm = 1, 2, 1 / math.sqrt(d)
     x = make_inputs(B, H, N, d, dtype=dtype, seed=40 + N, k_off_std=2.0, with_do=True)
     _, _, dq, dk, dv = _run(sage, x, causal, sm)
     f = {n: oracle.widen(as_u16(x[n]), dtype).reshape(B * H, N, d) for n in ("q", "k", "v", "do")}
@@ -46,12 +47,13 @@ def test_backward_matches_fp64(sage, causal, N, dtype):
         assert cos(g, ref) >= 0.99, (name, cos(g, ref))
 
 
-def test_backward_dv_column_sum(sage):
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_dv_column_sum(sage, d):
     """Rows of P sum to one, so sum_j dV_j = sum_i dO_i per head and channel."""
     from bit_quantized_attention_smooth_amd.workloads import make_inputs
-    banner("backward dV column sum")
-    x = make_inputs(1, 2, 512, 64, dtype="bf16", seed=77, with_do=True)
-    _, _, _, _, dv = _run(sage, x, False, 1 / 8)
+    banner(f"backward dV column sum d={d}")
+    x = make_inputs(1, 2, 512, d, dtype="bf16", seed=77, with_do=True)
+    _, _, _, _, dv = _run(sage, x, False, 1 / math.sqrt(d))
     got = dv.float().sum(dim=2).cpu().numpy()
     want = x["do"].float().sum(dim=2).numpy()
     assert np.allclose(got, want, rtol=0.03, atol=0.03 * np.abs(want).max())
@@ -63,6 +65,26 @@ def test_backward_training_workload_sampled_heads(sage):
     banner("backward training workload b8h16n2048d64 causal")
     x, w = workload_inputs("train_causal_b8h16n2048d64")
     B, H, N, d, sm = w["B"], w["H"], w["N"], w["d"], w["sm_scale"]
+    o, lse, dq, dk, dv = _run(sage, x, True, sm)
+    heads = [0, B * H - 1]
+    sel = lambda t: t.reshape(B * H, N, d)[heads]
+    f = {n: oracle.widen(as_u16(sel(x[n])), "bf16").reshape(len(heads), N, d) for n in ("q", "k", "v", "do")}
+    rq, rk, rv = oracle.attn_bwd_ref(f["q"], f["k"], f["v"], f["do"], True, sm)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        g = to_np64(sel(got))
+        assert cos(g, ref) >= 0.99, (name, cos(g, ref))
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+
+
+def test_backward_d128_causal_sampled_heads(sage):
+    """Head dimension 128 at a prefill-like size (B=2 H=8 N=2048, causal), two heads checked."""
+    import oracle
+    from bit_quantized_attention_smooth_amd.workloads import make_inputs, as_u16
+    banner("backward b2h8n2048d128 causal")
+    B, H, N, d = 2, 8, 2048, 128
+    sm = 1 / math.sqrt(d)
+    x = make_inputs(B, H, N, d, dtype="bf16", seed=79, k_off_std=2.0, with_do=True)
     o, lse, dq, dk, dv = _run(sage, x, True, sm)
     heads = [0, B * H - 1]
     sel = lambda t: t.reshape(B * H, N, d)[heads]
