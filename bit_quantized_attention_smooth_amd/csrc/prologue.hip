@@ -472,12 +472,14 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
 
 // Per-block Q smoothing (MXFP4 QK): the mean of Q over each 128-query block -- the fused
 // kernel's query tile -- from exact fp64 sums.  grid (Np/128, BH), 256 threads; writes
-// mu_q[bh][b][D].
+// mu_q[bh][b][D] and the same fp32 values widened to fp64, muD[bh][b][D] with NBP >= Np/128
+// rows (the last block's workgroup zeroes the padding rows), the dS kernel's MFMA operand.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void qblock_mean_kernel(const uint16_t* __restrict__ q, int N, int Np,
-                                                          float* __restrict__ mu_q) {
+                                                          float* __restrict__ mu_q, double* __restrict__ muD,
+                                                          int NBP) {
   constexpr int C8 = D / 8, RP = 256 / C8;
-  const int bh = blockIdx.y, b = blockIdx.x, t0 = b * 128, t1 = min(N, t0 + 128);
+  const int bh = blockIdx.y, b = blockIdx.x, t0 = b * 128, t1 = min(N, t0 + 128), NB = Np / 128;
   const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
   double sx[8] = {};
   for (int r = t0 + r0; r < t1; r += RP) {
@@ -493,20 +495,34 @@ __global__ __launch_bounds__(256) void qblock_mean_kernel(const uint16_t* __rest
   if (tid < D) {
     double a = 0.0;
     for (int r = 0; r < RP; r++) a += s_x[r][tid];
-    mu_q[((size_t)bh * (Np / 128) + b) * D + tid] = (float)(a / (double)(t1 - t0));   // t1 > t0: Np < N + 128
+    const float m = (float)(a / (double)(t1 - t0));   // t1 > t0: Np < N + 128
+    mu_q[((size_t)bh * NB + b) * D + tid] = m;
+    double* md = muD + (size_t)bh * NBP * D + tid;
+    md[(size_t)b * D] = (double)m;
+    if (b == NB - 1)
+      for (int p = NB; p < NBP; p++) md[(size_t)p * D] = 0.0;
   }
 }
 
 // Per-block Q smoothing: dS[bh][b][j] = fl32(sum_c mu_q[b][c] * Ks[j][c]) for every 128-query
-// block b and key j, Ks = fl32(K - mu_k) as the codes kernel forms it, summed in fp64 in channel
-// order (0 past N).  grid (Np/64, BH), 256 threads: 64 keys per workgroup, a wave per block b.
+// block b and key j, Ks = fl32(K - mu_k) as the codes kernel forms it, summed in fp64 in
+// channel order (0 past N).  A dense fp64 contraction, so it runs on the fp64 MFMA
+// (16 x 16 x 4): its result is the FMA chain c + a0 b0 + a1 b1 + a2 b2 + a3 b3 in k order
+// (checked bit for bit against that chain on the GPU), so chaining it over the channels in
+// order is exactly the sequential fp64 sum.  grid (Np/64, BH), 256 threads: 64 keys per
+// workgroup, Ks staged in LDS; wave w takes the 16-block groups g = w, w + 4, ... against all
+// 64 keys (four 16-key column tiles).  Operands: A lane l = (block 16 g + l % 16, channel
+// c + l / 16) from the fp64 means muD; B lane l = (channel c + l / 16, key 16 u + l % 16).
+// Result lane l, register r = (block 16 g + l / 16 + 4 r, key 16 u + l % 16).
+typedef double v4d __attribute__((ext_vector_type(4)));
 template <int DT, int D>
 __global__ __launch_bounds__(256) void qblock_ds_kernel(const uint16_t* __restrict__ k, int N, int Np,
-                                                        const float* __restrict__ mu_k, const float* __restrict__ mu_q,
+                                                        const float* __restrict__ mu_k,
+                                                        const double* __restrict__ muD, int NBP,
                                                         float* __restrict__ delta_s) {
-  constexpr int C8 = D / 8;
+  constexpr int C8 = D / 8, KS = D + 4;   // row pitch: the B reads (16 rows x 4 channels) spread over the banks
   const int bh = blockIdx.y, t0 = blockIdx.x * 64, NB = Np / 128;
-  __shared__ float s_ks[64][D + 1];   // one padding column: the 64 lanes' rows fall in distinct banks
+  __shared__ float s_ks[64 * KS];
   for (int e = threadIdx.x; e < 64 * C8; e += 256) {
     const int r = e / C8, c0 = (e % C8) * 8, row = t0 + r;
     float y[8];
@@ -519,15 +535,34 @@ __global__ __launch_bounds__(256) void qblock_ds_kernel(const uint16_t* __restri
       for (int i = 0; i < 8; i++) y[i] = 0.0f;
     }
 #pragma unroll
-    for (int i = 0; i < 8; i++) s_ks[r][c0 + i] = y[i];
+    for (int i = 0; i < 8; i++) s_ks[r * KS + c0 + i] = y[i];
   }
   __syncthreads();
-  const int j = threadIdx.x & 63;
-  for (int b = threadIdx.x >> 6; b < NB; b += 4) {
-    const float* m = mu_q + ((size_t)bh * NB + b) * D;   // wave-uniform
-    double acc = 0.0;
-    for (int c = 0; c < D; c++) acc += (double)m[c] * (double)s_ks[j][c];
-    delta_s[((size_t)bh * NB + b) * Np + t0 + j] = t0 + j < N ? (float)acc : 0.0f;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lk = lane >> 4;
+  for (int g = w; 16 * g < NB; g += 4) {
+    const double* ma = muD + ((size_t)bh * NBP + 16 * g + li) * D + lk;
+    v4d acc[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) acc[u] = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+    for (int c = 0; c < D; c += 4) {
+      const double av = ma[c];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const double bv = (double)s_ks[(16 * u + li) * KS + c + lk];
+        acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[u], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int key = t0 + 16 * u + li;
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int blk = 16 * g + lk + 4 * r;
+        if (blk < NB) delta_s[((size_t)bh * NB + blk) * Np + key] = key < N ? (float)acc[u][r] : 0.0f;
+      }
+    }
   }
 }
 
@@ -928,13 +963,16 @@ static hipError_t prologue_dispatch(const void* q, const void* k, const void* v,
   }
   // QB (per-128-query-block Q smoothing, fixed length only): block means replace the Q sums
   const bool qb = s.qk_fmt == QK_MXFP4B;
+  // QB: the fp64 copy of the block means follows the fp32 ones in the mu_q region
+  const int nbp = qblock_padded(s.Np / 128);
+  double* muD = reinterpret_cast<double*>(qp.mu_q + (size_t)BHm * (s.Np / 128) * D);
   if (qb) {
     if (!plain) return hipErrorInvalidValue;
     if (s.pv_fmt == PV_FP8)
       stats_kernel<DT, D, false, true><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
     else
       stats_kernel<DT, D, false, false><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
-    qblock_mean_kernel<DT, D><<<dim3(s.Np / 128, BHm), 256, 0, st>>>(Q, s.N, s.Np, qp.mu_q);
+    qblock_mean_kernel<DT, D><<<dim3(s.Np / 128, BHm), 256, 0, st>>>(Q, s.N, s.Np, qp.mu_q, muD, nbp);
   } else if (s.pv_fmt == PV_FP8) {
     stats_kernel<DT, D, true, true><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
   } else {
@@ -954,7 +992,7 @@ static hipError_t prologue_dispatch(const void* q, const void* k, const void* v,
   else codes(std::integral_constant<int, PV_MXFP4>{});
   // QB: dS per (query block, key), after the codes kernel has written mu_k
   if (qb)
-    qblock_ds_kernel<DT, D><<<dim3(s.Np / 64, BHm), 256, 0, st>>>(K, s.N, s.Np, qp.mu_k, qp.mu_q, qp.delta_s);
+    qblock_ds_kernel<DT, D><<<dim3(s.Np / 64, BHm), 256, 0, st>>>(K, s.N, s.Np, qp.mu_k, muD, nbp, qp.delta_s);
   return hipGetLastError();
 }
 

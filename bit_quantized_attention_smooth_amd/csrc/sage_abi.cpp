@@ -175,7 +175,8 @@ void compute_layout(const Extents& E, int d_, int qk_fmt, int pv_fmt, sage_quant
   // per-block Q smoothing: a mean per 128-query block, a dS row per block (fixed length: tq, tk
   // are the instances' padded token counts)
   const size_t nqb = qblk ? E.tq / E.inst_q / 128 : 1;
-  L->mu_q = take(E.inst_q * nqb * d * 4);
+  // (QBLOCK: then the same means in fp64, transposed and padded: scratch of the dS step)
+  L->mu_q = take(E.inst_q * nqb * d * 4 + (qblk ? E.inst_q * d * sage::qblock_padded((int)nqb) * 8 : 0));
   L->q_codes = take(mx ? E.tq * d / 2 : E.tq * d);
   const bool tok = qk_fmt == SAGE_FMT_INT8_TOKEN;
   L->q_scales = take(mx ? E.tq * (d / 32) : tok ? E.tq * 4 : E.tq / 64 * 4);

@@ -16,10 +16,15 @@ constexpr int kTokenPad = 128;
 // Token chunks per head of the smoothing statistics (partial sums are kept per chunk).
 constexpr int kStatChunks = 8;
 
+// Per-block Q smoothing: the fp64 copy of the block means (the dS kernel's MFMA A operand)
+// has this many rows, a whole number of 16-block groups.
+inline int qblock_padded(int nb) { return (nb + 15) / 16 * 16; }
+
 // Device pointers of one quantized buffer (offsets resolved on the host).
 struct QuantPtrs {
   float* mu_k;
-  float* mu_q;        // [BH, d], or [BH, Np/128, d] per 128-query block (QK_MXFP4B)
+  float* mu_q;        // [BH, d], or [BH, Np/128, d] per 128-query block (QK_MXFP4B; then
+                      // followed by the fp64 copy [BH, qblock_padded(Np/128), d])
   uint8_t* q_codes;
   void* q_scales;     // fp32 [BH, nb] (INT8), fp32 [BH, Np] (INT8T) or uint8 E8M0 [BH, Np, d/32] (MXFP4)
   uint8_t* k_codes;

@@ -93,7 +93,9 @@ typedef struct {
  * zero codes), nb = Np/64.
  *   mu_k      fp32 [BH, d]     channel mean of K over all N tokens
  *   mu_q      fp32 [BH, d]     channel mean of Q (MXFP4 QK only; MXFP4_QBLOCK:
- *             [BH, Np/128, d], the mean of each 128-query block)
+ *             [BH, Np/128, d], the mean of each 128-query block, followed by the
+ *             same means in fp64 as [BH, Np/128 rounded up to 16, d], zero-padded:
+ *             scratch of the dS step)
  *   q_codes   INT8: int8 [BH, Np, d];  MXFP4: packed E2M1 [BH, Np, d/2] of
  *             Q - mu_q, element 2i in the low nibble of byte i
  *   q_scales  INT8: fp32 [BH, nb] step of each 64-token block; INT8_TOKEN:

@@ -88,8 +88,9 @@ def test_quant_layout_sizes():
             assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
             codes = BH * Np * d // (2 if qk in (3, 7) else 1)
             assert lay["q_scales"] - lay["q_codes"] >= codes
-            if qk == 7:      # a Q mean per 128-query block, a dS row per block
-                assert lay["q_codes"] - lay["mu_q"] >= BH * (Np // 128) * d * 4
+            if qk == 7:      # a Q mean per 128-query block (fp32, then fp64 over whole 16-block
+                nb = Np // 128   # groups), a dS row per block
+                assert lay["q_codes"] - lay["mu_q"] >= BH * nb * d * 4 + BH * ((nb + 15) // 16 * 16) * d * 8
                 assert lay["lse_corr"] - lay["delta_s"] >= BH * (Np // 128) * Np * 4
             if qk == 6:      # a step per query token and per 32 keys
                 assert lay["k_codes"] - lay["q_scales"] >= BH * Np * 4

@@ -107,7 +107,12 @@ def _check_codes(r, qz, qk, pv):
         assert np.array_equal(r["mu_k"], qz["mu_k"]) and np.array_equal(r["mu_q"], qz["mu_q"])
         assert np.array_equal(r["qe"], qz["qe"]) and np.array_equal(r["ke"], qz["ke"])
         assert np.array_equal(r["qc"], qz["qc"]) and np.array_equal(r["kc"], qz["kc"])
-        assert np.allclose(r["dS"], qz["dS"], rtol=1e-6, atol=1e-6 * np.abs(qz["dS"]).max())
+        if qk == "mxfp4_qblock":
+            # summed in channel order by chained fp64 MFMAs, as the oracle sums: the same bits
+            assert np.array_equal(r["dS"], qz["dS"])
+        else:
+            # one fp64 sum per key, reduced across lanes in tree order: equal up to the last bit
+            assert np.allclose(r["dS"], qz["dS"], rtol=1e-6, atol=1e-6 * np.abs(qz["dS"]).max())
     if pv == "f16":
         pass
     elif pv == "fp8":
