@@ -75,15 +75,26 @@ __device__ __forceinline__ void chunk_stats(const uint16_t* __restrict__ x, cons
   const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
   double sx[8] = {};
   uint32_t av[8] = {};
-  for (int r = t0 + r0; r < t1; r += RP) {
-    float y[8];
-    load8<DT>(x + in.io0 + (size_t)r * in.ios + c0, y);
+  // four rows per thread and step, all loads issued before any is used (the 16-bit sums are
+  // exact in fp64, so the order does not matter); a row past the chunk reads row t0 (valid)
+  // and counts as zero
+  constexpr int U = 4;
+  for (int r = t0 + r0; r < t1; r += U * RP) {
+    float y[U][8], z[U][8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) sx[i] += (double)y[i];
-    if (AMAXV) {
-      load8<DT>(v + in.io0 + (size_t)r * in.ios + c0, y);
+    for (int u = 0; u < U; u++) {
+      const int rr = r + u * RP < t1 ? r + u * RP : t0;
+      load8<DT>(x + in.io0 + (size_t)rr * in.ios + c0, y[u]);
+      if (AMAXV) load8<DT>(v + in.io0 + (size_t)rr * in.ios + c0, z[u]);
+    }
 #pragma unroll
-      for (int i = 0; i < 8; i++) av[i] = max(av[i], __float_as_uint(fabsf(y[i])));  // NaN-propagating
+    for (int u = 0; u < U; u++) {
+      const bool ok = r + u * RP < t1;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        sx[i] += ok ? (double)y[u][i] : 0.0;
+        if (AMAXV) av[i] = max(av[i], ok ? __float_as_uint(fabsf(z[u][i])) : 0u);   // NaN-propagating
+      }
     }
   }
 #pragma unroll
