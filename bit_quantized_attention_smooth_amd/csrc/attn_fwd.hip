@@ -315,6 +315,27 @@ __device__ __forceinline__ void qk_tile(Score<D, QK>& S, const uint8_t* lk, cons
   }
 }
 
+// Reductions of a lane's values as balanced trees: a wave issues a vector instruction that
+// depends on the previous one only after that one's latency, so a long chain (a running max
+// or sum) leaves the lane idle; a tree of 32 is 5 deep.  Measured 2 % faster on the MXFP4
+// kernels.  The fp32 row sum is not a quantization decision, so its order is free.
+template <int N>
+__device__ __forceinline__ float tree_max_f(float* x) {
+#pragma unroll
+  for (int w = N / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int r = 0; r < w; r++) x[r] = fmaxf(x[r], x[r + w]);
+  return x[0];
+}
+template <int N>
+__device__ __forceinline__ float tree_sum_f(float* x) {
+#pragma unroll
+  for (int w = N / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int r = 0; r < w; r++) x[r] = x[r] + x[r + w];
+  return x[0];
+}
+
 // Online-softmax state of one wave's 32 queries.
 template <int D>
 struct RowState {
@@ -368,6 +389,8 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
       }
     } else {
       // the row max on the integer scores (c > 0): exact, no NaN handling
+      // (a running max here: the hardware hides its chain under the converts, and a tree
+      // measured no faster while it costs 7 more instructions)
       im = Sc.si[0][0];
 #pragma unroll
       for (int s = 0; s < 2; s++)
@@ -402,10 +425,10 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
 #pragma unroll
       for (int i = 0; i < 32; i++) u[i] = KeyMap<PV>::lane_key(i) < lim ? u[i] : -INFINITY;
     }
-    float mu = fmaxf(u[0], u[1]);
+    float mx[32];
 #pragma unroll
-    for (int i = 2; i < 32; i += 2) mu = fmaxf(mu, fmaxf(u[i], u[i + 1]));
-    mt = half_max(mu);
+    for (int i = 0; i < 32; i++) mx[i] = u[i];
+    mt = half_max(tree_max_f<32>(mx));
   }
   const float mnew = fmaxf(st.m, mt);
   const float mref = mnew == -INFINITY ? 0.0f : mnew;
@@ -457,7 +480,7 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
   constexpr int KREADS = NQK * (QK == QK_MXFP4 ? 2 : 1);   // their LDS reads (+ scale bytes)
   constexpr int VSLOT = 112 / NQK;                         // vector instructions per MFMA slot
   if (IL) qk_tile<D, QK>(Sn, lk_next, qf, qf4, qsc, lo);
-  float ps0 = 0.0f, ps1 = 0.0f;
+  float ps[8];   // row-sum partials of 4 keys each, summed as a tree
   if (PV == PV_F16) {
     // fp16 P~ = p (RNE), eight keys per K = 16 product, fp32 accumulation
     v4i ph[4];
@@ -465,12 +488,11 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
     for (int i = 0; i < 32; i += 4) {
       const float p0 = fast_exp2(fmaf(u[i], c, off)), p1 = fast_exp2(fmaf(u[i + 1], c, off));
       const float p2 = fast_exp2(fmaf(u[i + 2], c, off)), p3 = fast_exp2(fmaf(u[i + 3], c, off));
-      ps0 += p0 + p1;
-      ps1 += p2 + p3;
+      ps[i / 4] = (p0 + p1) + (p2 + p3);
       ph[i / 8][(i % 8) / 2] = pack_f16x2(p0, p1);
       ph[i / 8][(i % 8) / 2 + 1] = pack_f16x2(p2, p3);
     }
-    st.l += ps0 + ps1;
+    st.l += tree_sum_f<8>(ps);
 #pragma unroll
     for (int cb = 0; cb < NCB; cb++)
 #pragma unroll
@@ -482,11 +504,10 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
     for (int i = 0; i < 32; i += 4) {
       const float p0 = fast_exp2(fmaf(u[i], c, off)), p1 = fast_exp2(fmaf(u[i + 1], c, off));
       const float p2 = fast_exp2(fmaf(u[i + 2], c, off)), p3 = fast_exp2(fmaf(u[i + 3], c, off));
-      ps0 += p0 + p1;
-      ps1 += p2 + p3;
+      ps[i / 4] = (p0 + p1) + (p2 + p3);
       pb[i / 4] = pack_fp8x4(p0, p1, p2, p3);
     }
-    st.l += ps0 + ps1;
+    st.l += tree_sum_f<8>(ps);
     // O^T += V^T P~^T
 #pragma unroll
     for (int cb = 0; cb < NCB; cb++) {
@@ -499,21 +520,18 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
         st.O[cb] = mfma_f8(va, pb, st.O[cb]);
     }
   } else {
-    float pf[32];
-    float am0 = 0.0f, am1 = 0.0f;
+    float pf[32], am[8];
 #pragma unroll
     for (int i = 0; i < 32; i += 4) {
       pf[i] = fast_exp2(fmaf(u[i], c, off));
       pf[i + 1] = fast_exp2(fmaf(u[i + 1], c, off));
       pf[i + 2] = fast_exp2(fmaf(u[i + 2], c, off));
       pf[i + 3] = fast_exp2(fmaf(u[i + 3], c, off));
-      ps0 += pf[i] + pf[i + 1];
-      ps1 += pf[i + 2] + pf[i + 3];
-      am0 = fmaxf(am0, fmaxf(pf[i], pf[i + 1]));
-      am1 = fmaxf(am1, fmaxf(pf[i + 2], pf[i + 3]));
+      ps[i / 4] = (pf[i] + pf[i + 1]) + (pf[i + 2] + pf[i + 3]);
+      am[i / 4] = fmaxf(fmaxf(pf[i], pf[i + 1]), fmaxf(pf[i + 2], pf[i + 3]));
     }
-    st.l = fmaf(lsc, ps0 + ps1, st.l);
-    const int sb = (int)mx_fp4_scale_byte(fmaxf(am0, am1));
+    st.l = fmaf(lsc, tree_sum_f<8>(ps), st.l);
+    const int sb = (int)mx_fp4_scale_byte(tree_max_f<8>(am));
     // byte 0 (an all-zero block, e.g. keys past the causal diagonal): codes 0 under any scale,
     // so convert with 1 rather than the subnormal 2^-127
     const float scl = sb == 0 ? 1.0f : e8m0_to_float((unsigned)sb);
