@@ -157,7 +157,7 @@ def test_forward_matches_oracle(sage, case):
     assert np.allclose(lse, lse_sim, rtol=1e-4, atol=2e-3)
 
 
-@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 127, 129])
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 127, 128, 129, 192])
 @pytest.mark.parametrize("causal", [False, True])
 def test_forward_edge_lengths(sage, N, causal):
     import oracle
@@ -180,6 +180,36 @@ def test_forward_edge_lengths(sage, N, causal):
             # one key: O is the dequantized V row
             assert np.allclose(o, o_sim, atol=2e-2)
         assert np.allclose(lse.cpu().numpy().reshape(2, N), lse_sim, rtol=1e-4, atol=2e-3)
+
+
+ZERO_PAIRS = [("int8", "fp8"), ("int8", "f16"), ("int8_token", "fp8"), ("mxfp4", "fp8"), ("mxfp4", "mxfp4"),
+              ("mxfp4", "mxfp8"), ("mxfp4_qblock", "fp8")]
+
+
+@pytest.mark.parametrize("qk,pv", ZERO_PAIRS, ids=[f"{a}_{b}" for a, b in ZERO_PAIRS])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_zero_inputs(sage, qk, pv, causal):
+    """Degenerate inputs: an all-zero Q or K has zero quantization steps, so every score is 0
+    and the weights are uniform (O is the (prefix) mean of the dequantized V); an all-zero V
+    gives O = 0.  Everything stays finite and matches the oracle's simulation."""
+    banner(f"zero inputs {qk}/{pv} causal={causal}")
+    B, H, N, d = 1, 2, 200, 64
+    sm = 1 / 8
+    for zero in "qkv":
+        f, g = _inputs(B, H, N, d, "bf16", 31, 2.0)
+        g[zero] = torch.zeros_like(g[zero])
+        f[zero] = np.zeros_like(f[zero])
+        o, lse = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv,
+                               return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all() and torch.isfinite(lse).all(), zero
+        o = to_np64(o).reshape(B * H, N, d)
+        qz = _oracle_quant(f, qk, pv, sm)
+        o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
+        assert np.abs(o - o_sim).max() <= 2e-2, zero
+        assert np.allclose(lse.cpu().numpy().reshape(B * H, N), lse_sim, rtol=1e-4, atol=2e-3), zero
+        if zero == "v":
+            assert not o.any()
 
 
 @pytest.mark.parametrize("qk", ["int8", "mxfp4"])
@@ -279,7 +309,7 @@ FULL = [("int8_fp8_causal_b1h32n4096d128", "fp8"), ("int8_fp8_b2h24n16384d64", "
         ("int8_fp8_b1h32n8192d128", "f16"), ("int8_fp8_causal_b1h32n4096d128", "fp8", "int8_token"),
         ("mxfp4_b4h32n8192d128", "fp8", "mxfp4_qblock"),
         ("mxfp4_b4h32n8192d128", "fp8"), ("mxfp4_b4h32n8192d128", "mxfp4"), ("mxfp4_b4h32n8192d128", "mxfp8"),
-        ("int8_fp8_b1h2n256d64", "fp8")]
+        ("int8_fp8_b1h2n256d64", "fp8"), ("int8_fp8_b1h32n8192d128", "fp8"), ("int8_fp8_causal_b1h32n16384d128", "fp8")]
 
 
 @pytest.mark.parametrize("spec", FULL, ids=["-".join(c[::-1]) for c in FULL])
