@@ -577,40 +577,76 @@ __global__ __launch_bounds__(256) void qblock_ds_kernel(const uint16_t* __restri
   }
 }
 
-// Instances one codes block serves: query instance i and, when i < B*Hkv, KV instance i;
-// each role is active while its 64-token block lies inside the instance rounded up to 128.
+// The instances one packed-sequence codes item serves: query head h of sequence b and, when
+// h < Hkv, KV head h of the same sequence; each role is active while the item's 64-token block
+// lies inside the instance rounded up to 128.
 struct CodeBlock {
-  Inst qi, ki, kq;   // query instance i, KV instance i, the KV instance query head i reads
-  int bq, hq;        // sequence and head of query instance i
-  int bk, hk;        // sequence and head of KV instance i
+  Inst qi, ki, kq;   // query instance (b, h), KV instance (b, h), the KV instance query head h reads
+  int bq, hq;        // sequence and head of the query instance
+  int bk, hk;        // sequence and head of the KV instance
+  int iq, ikv;       // their indices b H + h and b Hkv + h (statistics, means, V steps)
   bool qa, ka;
 };
 template <int D>
-__device__ __forceinline__ CodeBlock code_block(const SeqGeo& g, int i, int t0) {
+__device__ __forceinline__ CodeBlock code_block(const SeqGeo& g, int b, int h, int t0) {
   CodeBlock cb;
-  cb.bq = i / g.H;
-  cb.hq = i % g.H;
-  const bool has_kv = i < g.B * g.Hkv;
-  cb.bk = has_kv ? i / g.Hkv : 0;
-  cb.hk = has_kv ? i % g.Hkv : 0;
-  cb.qi = q_inst(g, cb.bq, cb.hq, D);
-  cb.ki = k_inst(g, cb.bk, cb.hk, D);
-  cb.kq = k_inst(g, cb.bq, cb.hq / (g.H / g.Hkv), D);
+  cb.bq = cb.bk = b;
+  cb.hq = h;
+  const bool has_kv = h < g.Hkv;
+  cb.hk = has_kv ? h : 0;
+  cb.iq = b * g.H + h;
+  cb.ikv = b * g.Hkv + cb.hk;
+  cb.qi = q_inst(g, b, h, D);
+  cb.ki = k_inst(g, b, cb.hk, D);
+  cb.kq = k_inst(g, b, h / (g.H / g.Hkv), D);
   cb.qa = t0 < ((cb.qi.len + 127) & ~127);
   cb.ka = has_kv && t0 < ((cb.ki.len + 127) & ~127);
   return cb;
 }
 
-// Packed sequences or grouped KV heads: INT8 Q / K codes and FP8 V.  grid (blocks of the
-// longest instance, B*H), 256 threads.
+// The (sequence, 64-token block) pairs of a packed batch, as a table the codes kernels walk:
+// tab[0].x = the count, tab[1 + e] = (b, block).  Sequence b has 2 ceil(max(len_q, len_k) /
+// 128) blocks.  One workgroup: a prefix sum over the sequences (each thread a contiguous run),
+// then each thread writes its runs' entries; writes stop at the capacity `cap`, so offsets
+// that overlap (malformed input) cannot run past the table.
+__global__ __launch_bounds__(256) void seq_blocks_kernel(SeqGeo g, int2* __restrict__ tab, int cap) {
+  __shared__ int s_n[256];
+  const int tid = threadIdx.x, chunk = (g.B + 255) / 256, b0 = min(g.B, tid * chunk), b1 = min(g.B, b0 + chunk);
+  auto nblocks = [&](int b) {
+    int s, lq, lk;
+    packed_seq(g.cu_q, b, g.total_q, g.max_q, s, lq);
+    packed_seq(g.cu_k, b, g.total_k, g.max_k, s, lk);
+    return 2 * ((max(lq, lk) + 127) / 128);
+  };
+  int n = 0;
+  for (int b = b0; b < b1; b++) n += nblocks(b);
+  s_n[tid] = n;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {   // inclusive scan
+    const int x = tid >= o ? s_n[tid - o] : 0;
+    __syncthreads();
+    s_n[tid] += x;
+    __syncthreads();
+  }
+  int idx = s_n[tid] - n;
+  for (int b = b0; b < b1; b++) {
+    const int nb = nblocks(b);
+    for (int j = 0; j < nb && idx < cap; j++, idx++) tab[1 + idx] = make_int2(b, j);
+  }
+  if (tid == 0) tab[0] = make_int2(min(s_n[255], cap), 0);
+}
+
+// Packed sequences: INT8 Q / K codes and FP8 (or fp16) V of one item (block blk of sequence b,
+// query head h and, when h < Hkv, KV head h); 256 threads.
 template <int DT, int D, int PV, bool FINE>
-__global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                             const uint16_t* __restrict__ v, SeqGeo g, float sm,
-                                                             QuantPtrs qp) {
+__device__ __forceinline__ void seq_int8_item(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                              const uint16_t* __restrict__ v, const SeqGeo& g, float sm,
+                                              const QuantPtrs& qp, int b, int blk, int h) {
   constexpr int C8 = D / 8, RP = 256 / C8, NP = 64 / RP;
-  const int i = blockIdx.y, blk = blockIdx.x, t0 = blk * 64, BHm = g.B * g.H;
-  const CodeBlock cb = code_block<D>(g, i, t0);
+  const int t0 = blk * 64, BHm = g.B * g.H;
+  const CodeBlock cb = code_block<D>(g, b, h, t0);
   if (!cb.qa && !cb.ka) return;
+  const int i = cb.ikv;   // the KV instance: its statistics, mean and V steps
   const int kvq = cb.bq * g.Hkv + cb.hq / (g.H / g.Hkv);
   const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
   __shared__ float s_mu[D], s_muq[D], s_dv[D];
@@ -746,23 +782,36 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t*
       *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(s_vt + c * 16);
   }
 }
+// grid (table capacity, H): workgroup (e, h) takes the table's item e for query head h.
+template <int DT, int D, int PV, bool FINE>
+__global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v, SeqGeo g, float sm,
+                                                             QuantPtrs qp) {
+  const int2* tab = reinterpret_cast<const int2*>(qp.blocks);
+  const int n = tab[0].x;
+  const int e = blockIdx.x;
+  if (e >= n) return;
+  const int2 it = tab[1 + e];
+  seq_int8_item<DT, D, PV, FINE>(q, k, v, g, sm, qp, it.x, it.y, blockIdx.y);
+}
 
 // Packed sequences or grouped KV heads: MXFP4 Q_s and K_s codes (32-channel blocks), dS and
 // LSE correction; V in FP8 (PV == PV_FP8), MXFP4 or MXFP8 (both in 32-token blocks per
 // channel).  grid (blocks of the longest instance, B*H), 256 threads.  dS = mu_q . K_s is written for each query head that
 // reads KV instance i (one without grouped heads, in the row loop; H / Hkv of them after it).
 template <int DT, int D, int PV>
-__global__ __launch_bounds__(256) void quant_mxfp4_seq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v, SeqGeo g, float sm,
-                                                          QuantPtrs qp) {
+__device__ __forceinline__ void seq_mxfp4_item(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                               const uint16_t* __restrict__ v, const SeqGeo& g, float sm,
+                                               const QuantPtrs& qp, int b, int blk, int h) {
   constexpr int C8 = D / 8, RP = 256 / C8, NP = 64 / RP;
   constexpr bool MXV = PV == PV_MXFP4 || PV == PV_MXFP8;
-  const int i = blockIdx.y, blk = blockIdx.x, t0 = blk * 64, BHm = g.B * g.H;
-  const CodeBlock cb = code_block<D>(g, i, t0);
+  const int t0 = blk * 64, BHm = g.B * g.H;
+  const CodeBlock cb = code_block<D>(g, b, h, t0);
   if (!cb.qa && !cb.ka) return;
+  const int i = cb.ikv, iq = cb.iq;   // KV instance (statistics, means, V steps), query instance
   const int grp = g.H / g.Hkv;
   const int kvq = cb.bq * g.Hkv + cb.hq / grp;
-  const bool own_kv = kvq == i && cb.ka;   // query head i reads KV instance i (no grouping)
+  const bool own_kv = kvq == i && cb.ka;   // query head h reads KV head h (no grouping)
   const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
   __shared__ float s_mk[D], s_mkq[D], s_mq[D];
   __shared__ __align__(16) uint8_t s_vt[PV == PV_FP8 ? D * 64 : 1];
@@ -778,13 +827,13 @@ __global__ __launch_bounds__(256) void quant_mxfp4_seq_kernel(const uint16_t* __
         if (PV == PV_FP8) reinterpret_cast<float*>(qp.v_scales)[(size_t)i * D + tid] = s_dv[tid];
       }
     }
-    // mu_q of query instance i: its own smoothing, and (grp == 1) the dS of KV instance i,
+    // mu_q of the query instance: its own smoothing, and (grp == 1) the dS of the KV instance,
     // which that query head reads -- needed whenever either role is active
-    const float mq = chunk_mean(qp.sums, 1, BHm, i, D, tid, cb.qi.len);
+    const float mq = chunk_mean(qp.sums, 1, BHm, iq, D, tid, cb.qi.len);
     s_mq[tid] = mq;
     if (cb.qa) {
       if (!own_kv) s_mkq[tid] = chunk_mean(qp.sums, 0, BHm, kvq, D, tid, cb.kq.len);
-      if (blk == 0) qp.mu_q[(size_t)i * D + tid] = mq;
+      if (blk == 0) qp.mu_q[(size_t)iq * D + tid] = mq;
     }
   }
   __syncthreads();
@@ -942,6 +991,19 @@ __global__ __launch_bounds__(256) void quant_mxfp4_seq_kernel(const uint16_t* __
   }
 }
 
+// grid (table capacity, H): workgroup (e, h) takes the table's item e for query head h.
+template <int DT, int D, int PV>
+__global__ __launch_bounds__(256) void quant_mxfp4_seq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v, SeqGeo g, float sm,
+                                                          QuantPtrs qp) {
+  const int2* tab = reinterpret_cast<const int2*>(qp.blocks);
+  const int n = tab[0].x;
+  const int e = blockIdx.x;
+  if (e >= n) return;
+  const int2 it = tab[1 + e];
+  seq_mxfp4_item<DT, D, PV>(q, k, v, g, sm, qp, it.x, it.y, blockIdx.y);
+}
+
 template <int DT, int D>
 static hipError_t prologue_dispatch(const void* q, const void* k, const void* v, const Shape& s, const QuantPtrs& qp,
                                     hipStream_t st) {
@@ -951,6 +1013,11 @@ static hipError_t prologue_dispatch(const void* q, const void* k, const void* v,
   // fixed length without grouped heads: the streamlined codes kernels (N, Np per instance)
   const bool plain = g.cu_q == nullptr && g.Hkv == g.H;
   const dim3 sg(kChunks, BHm), qg(max(g.nbq, g.nbk), BHm);
+  // packed sequences: one codes workgroup per entry of a table of the batch's (sequence, block)
+  // pairs and query head; the grid covers the table's capacity, and the workgroups past its
+  // count return at once
+  const dim3 pg(plain ? 1 : seq_block_capacity(g), g.H);
+  if (!plain) seq_blocks_kernel<<<1, 256, 0, st>>>(g, reinterpret_cast<int2*>(qp.blocks), seq_block_capacity(g));
   // else INT8 (QK_INT8, or QK_INT8T with finer steps)
   const bool mx = s.qk_fmt == QK_MXFP4 || s.qk_fmt == QK_MXFP4B;
   if (!mx) {
@@ -962,7 +1029,7 @@ static hipError_t prologue_dispatch(const void* q, const void* k, const void* v,
       if (plain)
         quant_int8_fp8_kernel<DT, D, PV, FINE><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BHm, s.sm_scale, qp);
       else
-        quant_int8_fp8_seq_kernel<DT, D, PV, FINE><<<qg, 256, 0, st>>>(Q, K, V, g, s.sm_scale, qp);
+        quant_int8_fp8_seq_kernel<DT, D, PV, FINE><<<pg, 256, 0, st>>>(Q, K, V, g, s.sm_scale, qp);
     };
     auto with_pv = [&](auto fine) {
       if (s.pv_fmt == PV_F16) codes(std::integral_constant<int, PV_F16>{}, fine);
@@ -996,7 +1063,7 @@ static hipError_t prologue_dispatch(const void* q, const void* k, const void* v,
     else if (plain)
       quant_mxfp4_kernel<DT, D, PV, false><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BHm, s.sm_scale, qp);
     else
-      quant_mxfp4_seq_kernel<DT, D, PV><<<qg, 256, 0, st>>>(Q, K, V, g, s.sm_scale, qp);
+      quant_mxfp4_seq_kernel<DT, D, PV><<<pg, 256, 0, st>>>(Q, K, V, g, s.sm_scale, qp);
   };
   if (s.pv_fmt == PV_FP8) codes(std::integral_constant<int, PV_FP8>{});
   else if (s.pv_fmt == PV_MXFP8) codes(std::integral_constant<int, PV_MXFP8>{});

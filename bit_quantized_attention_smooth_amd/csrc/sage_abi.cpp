@@ -149,16 +149,18 @@ struct Extents {
   size_t tq, tk;            // tokens over all query / KV instances (multiples of 64)
   size_t ds, corr;          // dS floats (query heads x key tokens), LSE-term floats
   size_t stats_inst;        // instances of the statistics partials (B*H)
+  size_t blk_cap;           // packed sequences: entries of the (sequence, block) table; else 0
 };
 
 Extents extents(const sage_problem* p) {
   const size_t BH = (size_t)p->B * p->H, Np = round_up((size_t)p->N, sage::kTokenPad);
-  return Extents{BH, BH, BH * Np, BH * Np, BH * Np, BH * (size_t)p->N, BH};
+  return Extents{BH, BH, BH * Np, BH * Np, BH * Np, BH * (size_t)p->N, BH, 0};
 }
 Extents extents(const sage_varlen_problem* p) {
   const size_t Tq = packed_tokens(p->total_q, p->B), Tk = packed_tokens(p->total_k, p->B);
   const size_t BH = (size_t)p->B * p->H;
-  return Extents{BH, (size_t)p->B * p->H_kv, p->H * Tq, p->H_kv * Tk, p->H * Tk, p->H * Tq, BH};
+  return Extents{BH, (size_t)p->B * p->H_kv, p->H * Tq, p->H_kv * Tk, p->H * Tk, p->H * Tq, BH,
+                 (size_t)sage::seq_block_capacity(p->total_q, p->total_k, p->B)};
 }
 
 void compute_layout(const Extents& E, int d_, int qk_fmt, int pv_fmt, sage_quant_layout* L) {
@@ -186,7 +188,9 @@ void compute_layout(const Extents& E, int d_, int qk_fmt, int pv_fmt, sage_quant
   L->v_scales = take(mxv || mx8v ? E.tk / 32 * d : E.inst_kv * d * 4);
   L->delta_s = take(E.ds * nqb * 4);
   L->lse_corr = take(E.corr * 4);
-  L->stats = take(sage::kStatChunks * (E.stats_inst * d * 8 * 2 + E.stats_inst * d * 4));
+  // statistics partials, then (packed sequences) the (sequence, block) table: int2 [1 + cap]
+  L->stats = take(sage::kStatChunks * (E.stats_inst * d * 8 * 2 + E.stats_inst * d * 4) +
+                  (E.blk_cap ? 8 * (E.blk_cap + 1) : 0));
   L->total = off;
 }
 void compute_layout(const sage_problem* p, sage_quant_layout* L) {
@@ -208,6 +212,7 @@ sage::QuantPtrs resolve(void* buf, size_t BH, int d, const sage_quant_layout& L)
   q.lse_corr = reinterpret_cast<float*>(b + L.lse_corr);
   q.sums = reinterpret_cast<double*>(b + L.stats);
   q.amax_v = reinterpret_cast<uint32_t*>(b + L.stats + sage::kStatChunks * BH * d * 8 * 2);
+  q.blocks = b + L.stats + sage::kStatChunks * BH * d * (8 * 2 + 4);
   return q;
 }
 sage::QuantPtrs resolve(void* buf, const sage_problem* p, const sage_quant_layout& L) {

@@ -35,6 +35,7 @@ struct QuantPtrs {
   float* lse_corr;
   double* sums;       // [2, kStatChunks, B*H, d]: K then Q token sums per chunk (K by KV instance)
   uint32_t* amax_v;   // [kStatChunks, B*H, d] bit patterns of max |V| per channel (by KV instance)
+  void* blocks;       // packed sequences: int2 [1 + seq_block_capacity] table of (sequence, block)
 };
 
 // Token geometry of a problem.  Fixed length: B sequences of Nq query and Nk key tokens in
@@ -65,6 +66,13 @@ struct Inst {
   size_t row0;       // packed / fixed per-token fp32 arrays (LSE correction)
   size_t lse0;       // LSE output: [B,H,Nq] fixed, [H,total_q] packed
 };
+
+// Packed sequences: the (sequence, 64-token block) pairs there can be -- each sequence b has
+// 2 ceil(max(len_q, len_k) / 128) <= (len_q + len_k) / 64 + 2 of them.
+inline int seq_block_capacity(long long total_q, long long total_k, long long B) {
+  return (int)((total_q + total_k) / 64 + 2 * B + 1);
+}
+inline int seq_block_capacity(const SeqGeo& g) { return seq_block_capacity(g.total_q, g.total_k, g.B); }
 
 #if defined(__HIPCC__)
 // Packed sequence b: its first row and length, clamped so that any offsets keep every access
@@ -138,7 +146,7 @@ hipError_t launch_prologue(const void* q, const void* k, const void* v, const Sh
 hipError_t launch_attn_fwd(const Shape& s, const QuantPtrs& qp, void* o, float* lse, hipStream_t stream);
 
 // Backward: the workspace is [forward quant buffer (qbytes) | backward extras];
-// attn_bwd_ws_bytes gives the size of the extras.  Head dim 64 only.
+// attn_bwd_ws_bytes gives the size of the extras.
 size_t attn_bwd_ws_bytes(const Shape& s);
 hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv, void* ws,

@@ -111,7 +111,8 @@ typedef struct {
  *   delta_s   fp32 [BH, Np]    mu_q . (k_t - mu_k), added to every score (MXFP4 QK;
  *             MXFP4_QBLOCK: [BH, Np/128, Np], one row per query block)
  *   lse_corr  fp32 [BH, N]     sm_scale * q_t . mu_k, added to the LSE only
- *   stats     fp64 / uint32 per-chunk partials of the smoothing statistics (scratch)
+ *   stats     fp64 / uint32 per-chunk partials of the smoothing statistics, then (packed
+ *             sequences) the batch's table of (sequence, 64-token block) pairs (scratch)
  */
 typedef struct {
     size_t mu_k, mu_q, q_codes, q_scales, k_codes, k_scales, v_codes, v_scales,
