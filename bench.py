@@ -324,7 +324,7 @@ def cpu_baseline(name):
     from bit_quantized_attention_smooth_amd.workloads import workload_inputs, as_u16
     x, w = workload_inputs(name)
     B, H, N, d, causal, sm = w["B"], w["H"], w["N"], w["d"], w["causal"], w["sm_scale"]
-    nh = 8
+    nh = min(20, B * H)   # about 10-15 s of oracle work on 16 host cores
     f = {n: oracle.widen(as_u16(x[n].reshape(B * H, N, d)[:nh]), w["dtype"]).reshape(nh, N, d) for n in "qkv"}
     oracle.lib()
     t0 = time.perf_counter()
