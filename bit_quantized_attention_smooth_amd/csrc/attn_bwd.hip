@@ -36,7 +36,6 @@ namespace sage {
 
 namespace {
 
-constexpr int kT = 64;   // query / key tile (= INT8 and FP8 block)
 constexpr int kNT = 3;   // channel-step tensors: dO, Q, K_s
 
 // Row of the 64-row operand tile fed to MFMA A-row m in subtile s, so that output lane
@@ -121,32 +120,55 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const uint16_t* __restri
   }
 }
 
-__device__ __forceinline__ uint32_t block_umax4(uint32_t x, uint32_t* red) {
+// Unpack 8 16-bit inputs (one 16-byte load) to fp32.
+template <int DT>
+__device__ __forceinline__ void unpack8io(const uint4 u, float* x) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  x = max(max(red[0], red[1]), max(red[2], red[3]));
-  __syncthreads();
-  return x;
+  for (int i = 0; i < 4; i++) {
+    x[2 * i] = DT == 0 ? bf16_to_f32(w[i] & 0xffff) : f16_to_f32(w[i] & 0xffff);
+    x[2 * i + 1] = DT == 0 ? bf16_to_f32(w[i] >> 16) : f16_to_f32(w[i] >> 16);
+  }
 }
 
 // Per 64-token block: D, lse2, dO / V token-major FP8 with block steps, dO^T / Q^T / K_s^T
-// FP8 with channel steps.  grid (Np/64, BH), 256 threads.
+// FP8 with channel steps.  grid (Np/64, BH), 2*D threads.  A thread holds channels
+// 8 cidx .. 8 cidx + 7 of the block's rows 4 rg .. 4 rg + 3, so one channel's four codes are
+// one dword of the transposed [channel][token] layout; a wave covers 8 channel groups x 8
+// row groups (8 rows of 128 contiguous bytes per load).  The transposed dwords pass through
+// LDS rows of 17 dwords (one pad dword), which puts the 64 lanes of a write on 64 distinct
+// banks, and leave as 16-byte stores of whole token rows.
 template <int DT, int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-                                                       const uint16_t* __restrict__ v, const uint16_t* __restrict__ q,
-                                                       const uint16_t* __restrict__ k, const float* __restrict__ lse,
-                                                       int N, int Np, BwdPtrs bp) {
-  constexpr int C8 = D / 8, RP = 256 / C8, NP = 64 / RP;
+__global__ __launch_bounds__(2 * D) void bwd_prep_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+                                                         const uint16_t* __restrict__ v, const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ k, const float* __restrict__ lse,
+                                                         int N, int Np, BwdPtrs bp) {
+  constexpr int NTH = 2 * D, CG = D / 64, NW = NTH / 64, RS = 17;
   const int bh = blockIdx.y, blk = blockIdx.x, t0 = blk * 64, BH = gridDim.y;
-  const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int cidx = 8 * (w % CG) + (lane & 7), rg = 8 * (w / CG) + (lane >> 3), c0 = 8 * cidx;
   const int nb = Np / 64;
-  __shared__ uint32_t s_red[4];
   __shared__ float s_inv[kNT][D];
-  __shared__ __align__(16) uint8_t s_T[kNT][D * 64];
+  __shared__ uint32_t s_red[2][NW];
+  __shared__ float s_dsum[CG][64];
+  __shared__ uint32_t s_T[kNT][D * RS];
+  // the thread's raw inputs, all loads issued first (rows past N read as zero)
+  uint4 rd[4], ro[4], rv[4], rq[4], rk[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const int row = t0 + 4 * rg + r;
+    rd[r] = ro[r] = rv[r] = rq[r] = rk[r] = make_uint4(0, 0, 0, 0);
+    if (row < N) {
+      const size_t off = ((size_t)bh * N + row) * D + c0;
+      rd[r] = *reinterpret_cast<const uint4*>(dout + off);
+      ro[r] = *reinterpret_cast<const uint4*>(o + off);
+      rv[r] = *reinterpret_cast<const uint4*>(v + off);
+      rq[r] = *reinterpret_cast<const uint4*>(q + off);
+      rk[r] = *reinterpret_cast<const uint4*>(k + off);
+    }
+  }
   // channel steps from the chunk partials: code = x * 448 / amax
-  for (int j = tid; j < kNT * D; j += 256) {
+  for (int j = tid; j < kNT * D; j += NTH) {
     const int t = j / D, c = j % D;
     uint32_t m = 0;
 #pragma unroll
@@ -159,79 +181,117 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 #pragma unroll
   for (int i = 0; i < 8; i++) mu[i] = bp.mu_k[(size_t)bh * D + c0 + i];
   __syncthreads();
-  float xd[NP][8], xv[NP][8];
+  // row sums dO.O, max |dO| and |V|, and the channel-step codes, two rows at a time
+  uint32_t tw[kNT][8];
   uint32_t ad = 0, av = 0;
 #pragma unroll
-  for (int p = 0; p < NP; p++) {
-    const int rl = r0 + p * RP, row = t0 + rl;
-    float dsum = 0.0f, xq[8], xk[8];
-    if (row < N) {
-      float xo[8];
-      const size_t off = ((size_t)bh * N + row) * D + c0;
-      load8io<DT>(dout + off, xd[p]);
-      load8io<DT>(o + off, xo);
-      load8io<DT>(v + off, xv[p]);
-      load8io<DT>(q + off, xq);
-      load8io<DT>(k + off, xk);
+  for (int h = 0; h < 2; h++) {
+#pragma unroll
+    for (int r2 = 0; r2 < 2; r2++) {
+      const int r = 2 * h + r2;
+      float xd[8], xo[8], xv[8];
+      unpack8io<DT>(rd[r], xd);
+      unpack8io<DT>(ro[r], xo);
+      unpack8io<DT>(rv[r], xv);
+      float dsum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        dsum += xd[p][i] * xo[i];
-        ad = max(ad, __float_as_uint(fabsf(xd[p][i])));
-        av = max(av, __float_as_uint(fabsf(xv[p][i])));
-        xk[i] -= mu[i];
+        dsum += xd[i] * xo[i];
+        ad = max(ad, __float_as_uint(fabsf(xd[i])));
+        av = max(av, __float_as_uint(fabsf(xv[i])));
       }
-    } else {
+      // sum over the 8 lanes of this wave that share the row
 #pragma unroll
-      for (int i = 0; i < 8; i++) xd[p][i] = xv[p][i] = xq[i] = xk[i] = 0.0f;
+      for (int o2 = 1; o2 < 8; o2 <<= 1) dsum += __shfl_xor(dsum, o2);
+      if ((lane & 7) == 0) s_dsum[w % CG][4 * rg + r] = dsum;
+    }
+    const int r0 = 2 * h;
+    float xd[2][8], xq[2][8], xk[2][8];
+#pragma unroll
+    for (int r2 = 0; r2 < 2; r2++) {
+      unpack8io<DT>(rd[r0 + r2], xd[r2]);
+      unpack8io<DT>(rq[r0 + r2], xq[r2]);
+      unpack8io<DT>(rk[r0 + r2], xk[r2]);
+      const bool in = t0 + 4 * rg + r0 + r2 < N;   // padding rows stay zero (not -mu_k)
+#pragma unroll
+      for (int i = 0; i < 8; i++) xk[r2][i] = in ? xk[r2][i] - mu[i] : 0.0f;
     }
 #pragma unroll
-    for (int o2 = 1; o2 < C8; o2 <<= 1) dsum += __shfl_xor(dsum, o2);
-    if ((tid % C8) == 0) {
-      bp.Dvec[(size_t)bh * Np + row] = dsum;
-      bp.lse2[(size_t)bh * Np + row] =
-          row < N ? (lse[(size_t)bh * N + row] - bp.lse_corr[(size_t)bh * N + row]) * kLog2e - kLog2_448 : INFINITY;
-    }
-    // channel-step codes, transposed through LDS
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(xd[p][i] * s_inv[0][c0 + i], xd[p][i + 1] * s_inv[0][c0 + i + 1], 0, false);
-      const int wq = __builtin_amdgcn_cvt_pk_fp8_f32(xq[i] * s_inv[1][c0 + i], xq[i + 1] * s_inv[1][c0 + i + 1], 0, false);
-      const int wk = __builtin_amdgcn_cvt_pk_fp8_f32(xk[i] * s_inv[2][c0 + i], xk[i + 1] * s_inv[2][c0 + i + 1], 0, false);
-      s_T[0][(c0 + i) * 64 + rl] = (uint8_t)(wd & 0xff);
-      s_T[0][(c0 + i + 1) * 64 + rl] = (uint8_t)((wd >> 8) & 0xff);
-      s_T[1][(c0 + i) * 64 + rl] = (uint8_t)(wq & 0xff);
-      s_T[1][(c0 + i + 1) * 64 + rl] = (uint8_t)((wq >> 8) & 0xff);
-      s_T[2][(c0 + i) * 64 + rl] = (uint8_t)(wk & 0xff);
-      s_T[2][(c0 + i + 1) * 64 + rl] = (uint8_t)((wk >> 8) & 0xff);
+    for (int i = 0; i < 8; i++) {
+      const float s0 = s_inv[0][c0 + i], s1 = s_inv[1][c0 + i], s2 = s_inv[2][c0 + i];
+      if (h == 0) {   // rows 0, 1 -> bytes 0, 1
+        tw[0][i] = __builtin_amdgcn_cvt_pk_fp8_f32(xd[0][i] * s0, xd[1][i] * s0, 0, false);
+        tw[1][i] = __builtin_amdgcn_cvt_pk_fp8_f32(xq[0][i] * s1, xq[1][i] * s1, 0, false);
+        tw[2][i] = __builtin_amdgcn_cvt_pk_fp8_f32(xk[0][i] * s2, xk[1][i] * s2, 0, false);
+      } else {        // rows 2, 3 -> bytes 2, 3
+        tw[0][i] = __builtin_amdgcn_cvt_pk_fp8_f32(xd[0][i] * s0, xd[1][i] * s0, tw[0][i], true);
+        tw[1][i] = __builtin_amdgcn_cvt_pk_fp8_f32(xq[0][i] * s1, xq[1][i] * s1, tw[1][i], true);
+        tw[2][i] = __builtin_amdgcn_cvt_pk_fp8_f32(xk[0][i] * s2, xk[1][i] * s2, tw[2][i], true);
+      }
     }
   }
-  const uint32_t amd = block_umax4(ad, s_red), amv = block_umax4(av, s_red);
-  const float sd = __uint_as_float(amd) / 448.0f, sv = __uint_as_float(amv) / 448.0f;
+#pragma unroll
+  for (int t = 0; t < kNT; t++)
+#pragma unroll
+    for (int i = 0; i < 8; i++) s_T[t][(c0 + i) * RS + rg] = tw[t][i];
+  // block max |dO|, |V|
+#pragma unroll
+  for (int o2 = 1; o2 < 64; o2 <<= 1) {
+    ad = max(ad, (uint32_t)__shfl_xor((int)ad, o2));
+    av = max(av, (uint32_t)__shfl_xor((int)av, o2));
+  }
+  if (lane == 0) {
+    s_red[0][w] = ad;
+    s_red[1][w] = av;
+  }
+  __syncthreads();
+  uint32_t amd = 0, amv = 0;
+#pragma unroll
+  for (int j = 0; j < NW; j++) {
+    amd = max(amd, s_red[0][j]);
+    amv = max(amv, s_red[1][j]);
+  }
   const float id = amd == 0 ? 0.0f : 448.0f / __uint_as_float(amd), iv = amv == 0 ? 0.0f : 448.0f / __uint_as_float(amv);
-  if (tid == 0) {
-    bp.do_step[(size_t)bh * nb + blk] = sd;
-    bp.v_step[(size_t)bh * nb + blk] = sv;
-  }
-#pragma unroll
-  for (int p = 0; p < NP; p++) {
-    const int row = t0 + r0 + p * RP;
-    uint32_t wd[2] = {0, 0}, wv[2] = {0, 0};
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      wd[i / 4] |= (uint32_t)(__builtin_amdgcn_cvt_pk_fp8_f32(xd[p][i] * id, xd[p][i + 1] * id, 0, false) & 0xffff) << (8 * (i % 4));
-      wv[i / 4] |= (uint32_t)(__builtin_amdgcn_cvt_pk_fp8_f32(xv[p][i] * iv, xv[p][i + 1] * iv, 0, false) & 0xffff) << (8 * (i % 4));
+  if (tid < 64) {
+    const int row = t0 + tid;
+    float dsum = s_dsum[0][tid];
+    if (CG == 2) dsum += s_dsum[CG - 1][tid];
+    bp.Dvec[(size_t)bh * Np + row] = dsum;
+    bp.lse2[(size_t)bh * Np + row] =
+        row < N ? (lse[(size_t)bh * N + row] - bp.lse_corr[(size_t)bh * N + row]) * kLog2e - kLog2_448 : INFINITY;
+    if (tid == 0) {
+      bp.do_step[(size_t)bh * nb + blk] = __uint_as_float(amd) / 448.0f;
+      bp.v_step[(size_t)bh * nb + blk] = __uint_as_float(amv) / 448.0f;
     }
-    const size_t off = ((size_t)bh * Np + row) * D + c0;
+  }
+  // token-major dO and V codes with the block steps
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    float xd[8], xv[8];
+    unpack8io<DT>(rd[r], xd);
+    unpack8io<DT>(rv[r], xv);
+    uint32_t wd[2], wv[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      wd[j] = __builtin_amdgcn_cvt_pk_fp8_f32(xd[4 * j] * id, xd[4 * j + 1] * id, 0, false);
+      wd[j] = __builtin_amdgcn_cvt_pk_fp8_f32(xd[4 * j + 2] * id, xd[4 * j + 3] * id, wd[j], true);
+      wv[j] = __builtin_amdgcn_cvt_pk_fp8_f32(xv[4 * j] * iv, xv[4 * j + 1] * iv, 0, false);
+      wv[j] = __builtin_amdgcn_cvt_pk_fp8_f32(xv[4 * j + 2] * iv, xv[4 * j + 3] * iv, wv[j], true);
+    }
+    const size_t off = ((size_t)bh * Np + t0 + 4 * rg + r) * D + c0;
     *reinterpret_cast<uint2*>(bp.do_codes + off) = make_uint2(wd[0], wd[1]);
     *reinterpret_cast<uint2*>(bp.v_codes + off) = make_uint2(wv[0], wv[1]);
   }
-  __syncthreads();
+  // transposed codes: 16-byte chunks e (channel e/4, tokens 16(e%4) ..) of the [D][64] tile
   const size_t tb = ((size_t)bh * nb + blk) * D * 64;
-  for (int c = tid; c < D * 4; c += 256) {
-    *reinterpret_cast<uint4*>(bp.doT_codes + tb + c * 16) = *reinterpret_cast<const uint4*>(&s_T[0][c * 16]);
-    *reinterpret_cast<uint4*>(bp.qT_codes + tb + c * 16) = *reinterpret_cast<const uint4*>(&s_T[1][c * 16]);
-    *reinterpret_cast<uint4*>(bp.kT_codes + tb + c * 16) = *reinterpret_cast<const uint4*>(&s_T[2][c * 16]);
-  }
+  uint8_t* const dstT[kNT] = {bp.doT_codes, bp.qT_codes, bp.kT_codes};
+#pragma unroll
+  for (int t = 0; t < kNT; t++)
+#pragma unroll
+    for (int e = tid; e < D * 4; e += NTH) {
+      const uint32_t* src = &s_T[t][(e >> 2) * RS + 4 * (e & 3)];
+      *reinterpret_cast<uint4*>(dstT[t] + tb + (size_t)e * 16) = make_uint4(src[0], src[1], src[2], src[3]);
+    }
 }
 
 // ---- shared pieces of the two main kernels ----
@@ -703,7 +763,7 @@ hipError_t bwd_run(const Shape& s, const void* q, const void* k, const void* v, 
   if (e != hipSuccess) return e;
   bwd_stats_kernel<DT, D><<<dim3(kStatChunks, BH), 256, 0, st>>>((const uint16_t*)dout, (const uint16_t*)q,
                                                                 (const uint16_t*)k, qp.mu_k, s.N, bp.amax_part);
-  bwd_prep_kernel<DT, D><<<dim3(s.Np / 64, BH), 256, 0, st>>>((const uint16_t*)o, (const uint16_t*)dout,
+  bwd_prep_kernel<DT, D><<<dim3(s.Np / 64, BH), 2 * D, 0, st>>>((const uint16_t*)o, (const uint16_t*)dout,
                                                              (const uint16_t*)v, (const uint16_t*)q,
                                                              (const uint16_t*)k, lse, s.N, s.Np, bp);
   const int grid = BH * (s.Np / 128);
