@@ -758,8 +758,11 @@ hipError_t bwd_run(const Shape& s, const void* q, const void* k, const void* v, 
   bp.doT_codes = b + L.doT;
   bp.qT_codes = b + L.qT;
   bp.kT_codes = b + L.kT;
-  // forward quantization of Q, K (the codes the forward used), then the backward prologue
-  hipError_t e = launch_prologue(q, k, v, s, qp, st);
+  // forward quantization of Q, K (the codes the forward used; V's are not needed), then the
+  // backward prologue
+  Shape sqk = s;
+  sqk.pv_fmt = PV_NONE;
+  hipError_t e = launch_prologue(q, k, v, sqk, qp, st);
   if (e != hipSuccess) return e;
   bwd_stats_kernel<DT, D><<<dim3(kStatChunks, BH), 256, 0, st>>>((const uint16_t*)dout, (const uint16_t*)q,
                                                                 (const uint16_t*)k, qp.mu_k, s.N, bp.amax_part);

@@ -199,7 +199,8 @@ __device__ __forceinline__ void put_v_f16(uint16_t* s_vt, int rl, int c0, const 
   for (int i = 0; i < 8; i++) s_vt[(c0 + i) * 64 + rl] = __builtin_bit_cast(uint16_t, (_Float16)x[i]);
 }
 
-// INT8 Q / K codes and FP8 (PV == PV_FP8) or fp16 (PV_F16) V.  grid (Np/64, BH), 256 threads.
+// INT8 Q / K codes and FP8 (PV == PV_FP8) or fp16 (PV_F16) V, or no V at all (PV_NONE: the
+// backward's own quantization of Q and K).  grid (Np/64, BH), 256 threads.
 template <int DT, int D, int PV, bool FINE>
 __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                              const uint16_t* __restrict__ v, int N, int Np, int BH,
@@ -210,11 +211,12 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
   const size_t base = (size_t)bh * N * D;
   __shared__ float s_mu[D], s_dv[D];
   __shared__ uint32_t s_red[8];
+  constexpr bool HASV = PV != PV_NONE;
   constexpr int VB = PV == PV_F16 ? 2 : 1;   // bytes per V element
-  __shared__ __align__(16) uint8_t s_vt[D * 64 * VB];
+  __shared__ __align__(16) uint8_t s_vt[HASV ? D * 64 * VB : 16];
   if (tid < D) {
     const float mu = chunk_mean(qp.sums, 0, BH, bh, D, tid, N);
-    const float dvs = chunk_amax(qp.amax_v, BH, bh, D, tid) / 448.0f;
+    const float dvs = HASV ? chunk_amax(qp.amax_v, BH, bh, D, tid) / 448.0f : 0.0f;
     s_mu[tid] = mu;
     s_dv[tid] = dvs;
     if (blk == 0) {
@@ -239,11 +241,13 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
       float xv[8];
       load8<DT>(q + base + (size_t)row * D + c0, xq[p]);
       load8<DT>(k + base + (size_t)row * D + c0, xk[p]);
-      load8<DT>(v + base + (size_t)row * D + c0, xv);
-      if (PV == PV_F16)
-        put_v_f16(reinterpret_cast<uint16_t*>(s_vt), rl, c0, xv);
-      else
-        put_v_fp8(s_vt, rl, c0, xv, dv, rv);
+      if (HASV) {
+        load8<DT>(v + base + (size_t)row * D + c0, xv);
+        if (PV == PV_F16)
+          put_v_f16(reinterpret_cast<uint16_t*>(s_vt), rl, c0, xv);
+        else
+          put_v_fp8(s_vt, rl, c0, xv, dv, rv);
+      }
       float cs = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; i++) {
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
         xk[p][i] = 0.0f;
         if (PV == PV_F16)
           reinterpret_cast<uint16_t*>(s_vt)[(c0 + i) * 64 + rl] = 0;
-        else
+        else if (HASV)
           s_vt[(c0 + i) * 64 + rl] = 0;
       }
     }
@@ -321,6 +325,7 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
     *reinterpret_cast<uint2*>(qp.q_codes + off) = make_uint2(wq[0], wq[1]);
     *reinterpret_cast<uint2*>(qp.k_codes + off) = make_uint2(wk[0], wk[1]);
   }
+  if (!HASV) return;
   __syncthreads();
   // V tile [D][64] -> v_codes[bh][blk][D][64], coalesced 16-byte stores
   uint8_t* dst = qp.v_codes + ((size_t)bh * (Np / 64) + blk) * D * 64 * VB;
@@ -1018,6 +1023,13 @@ static hipError_t prologue_dispatch(const void* q, const void* k, const void* v,
   // count return at once
   const dim3 pg(plain ? 1 : seq_block_capacity(g), g.H);
   if (!plain) seq_blocks_kernel<<<1, 256, 0, st>>>(g, reinterpret_cast<int2*>(qp.blocks), seq_block_capacity(g));
+  // Q and K only (the backward's quantization; fixed length, INT8 with 64-token steps)
+  if (s.pv_fmt == PV_NONE) {
+    if (!plain || s.qk_fmt != QK_INT8) return hipErrorInvalidValue;
+    stats_kernel<DT, D, false, false><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
+    quant_int8_fp8_kernel<DT, D, PV_NONE, false><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BHm, s.sm_scale, qp);
+    return hipGetLastError();
+  }
   // else INT8 (QK_INT8, or QK_INT8T with finer steps)
   const bool mx = s.qk_fmt == QK_MXFP4 || s.qk_fmt == QK_MXFP4B;
   if (!mx) {

@@ -9,7 +9,8 @@ namespace sage {
 // QK_INT8T: INT8 codes with a step per query token and per 32 keys (instead of per 64 tokens);
 // QK_MXFP4B: MXFP4 with Q smoothed per 128-query block (dS per block and key)
 enum { QK_INT8 = 1, QK_MXFP4 = 3, QK_INT8T = 6, QK_MXFP4B = 7 };
-enum { PV_FP8 = 2, PV_MXFP4 = 3, PV_MXFP8 = 4, PV_F16 = 5 };
+// PV_NONE: quantize Q and K only (the backward needs no V codes)
+enum { PV_NONE = 0, PV_FP8 = 2, PV_MXFP4 = 3, PV_MXFP8 = 4, PV_F16 = 5 };
 
 // Padding of the token axis in every quantized buffer (a multiple of the Q tile).
 constexpr int kTokenPad = 128;
