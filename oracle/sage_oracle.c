@@ -215,17 +215,21 @@ OR_API uint8_t or_mx_scale_byte(double amax, int emax)
     return (uint8_t)(e + 127);
 }
 
+/* E8M0 byte -> 2^(b - 127); the byte 0xFF encodes NaN (OCP MX v1.0, the E8M0 scale format). */
+static double e8m0_decode(uint8_t b)
+{
+    return b == 0xFF ? NAN : ldexp(1.0, (int)b - 127);
+}
+
 /* INT8 symmetric code with step delta (fp32): clamp(rne(fl32(x / delta)), -127, 127). */
 OR_API int8_t or_int8_encode(float x, float delta)
 {
     if (delta == 0.0f)
         return 0;
     float r = x / delta;                           /* one correctly rounded fp32 division */
-    float n = rintf(r);
-    if (n > 127.0f)
-        n = 127.0f;
-    if (n < -127.0f)
-        n = -127.0f;
+    /* fmaxf / fminf return the non-NaN operand, so a NaN quotient (a NaN or infinite input
+     * or step) clamps to -127 instead of reaching an undefined float -> int conversion */
+    float n = fminf(fmaxf(rintf(r), -127.0f), 127.0f);
     return (int8_t)n;
 }
 
@@ -499,7 +503,7 @@ static double mx_dot(const head_t *H, int i, int j)
         double part = 0.0;
         for (int c = 32 * g; c < 32 * g + 32; c++)
             part += or_e2m1_decode(H->q4[(int64_t)i * d + c]) * or_e2m1_decode(H->k4[(int64_t)j * d + c]);
-        s += part * ldexp(1.0, (int)H->qe[(int64_t)i * ng + g] - 127) * ldexp(1.0, (int)H->ke[(int64_t)j * ng + g] - 127);
+        s += part * e8m0_decode(H->qe[(int64_t)i * ng + g]) * e8m0_decode(H->ke[(int64_t)j * ng + g]);
     }
     return s;
 }
@@ -537,7 +541,7 @@ static double vval(const head_t *H, int j, int c)
         return or_e4m3_decode(H->vc[idx]);
     if (H->pv == PV_F16)
         return or_f16_decode(H->vh[idx]);
-    double e = ldexp(1.0, (int)H->ve[(int64_t)(j / 32) * H->d + c] - 127);
+    double e = e8m0_decode(H->ve[(int64_t)(j / 32) * H->d + c]);
     if (H->pv == PV_MXFP8)
         return or_e4m3_decode(H->vc[idx]) * e;
     return or_e2m1_decode(H->vc[idx]) * e;
@@ -562,10 +566,10 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
         for (int jj = 0; jj < n; jj++) {
             int j = j0 + jj;
             x[jj] = (H->causal && j > i) ? -INFINITY : H->sm * score(H, i, j);
-            if (x[jj] > mt)
+            if (x[jj] > mt || isnan(x[jj]))        /* a NaN score makes the row max NaN */
                 mt = x[jj];
         }
-        double mn = m > mt ? m : mt;
+        double mn = (m > mt || isnan(m)) ? m : mt;
         if (mn == -INFINITY)
             continue;
         double alpha = (m == -INFINITY) ? 0.0 : exp(m - mn);
@@ -649,7 +653,7 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
                 uint8_t sb;
                 quant_mx_group(pf + g0, gn, 1, 4, codes + g0, 1, &sb);
                 for (int jj = g0; jj < g0 + gn; jj++)
-                    pq[jj] = or_e2m1_decode(codes[jj]) * ldexp(1.0, (int)sb - 127);
+                    pq[jj] = or_e2m1_decode(codes[jj]) * e8m0_decode(sb);
             }
             post = 1.0 / (double)sigma;
             free(pf);
@@ -658,12 +662,10 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
         /* first level: this tile's product; second level: the running O */
         for (int c = 0; c < d; c++)
             acc[c] = 0.0;
-        for (int jj = 0; jj < n; jj++) {
-            if (pq[jj] == 0.0)
-                continue;
+        /* every key of the tile, zero weights included: 0 * NaN = NaN, as in the matrix product */
+        for (int jj = 0; jj < n; jj++)
             for (int c = 0; c < d; c++)
                 acc[c] += pq[jj] * vval(H, j0 + jj, c);
-        }
         for (int c = 0; c < d; c++)
             O[c] = alpha * O[c] + acc[c] * post;
         m = mn;

@@ -212,6 +212,43 @@ def test_forward_zero_inputs(sage, qk, pv, causal):
             assert not o.any()
 
 
+# (tensor, head, row, channel, value): a NaN in Q, a NaN in K (it reaches the K mean, so the
+# whole head), an Inf in V (it reaches the channel's step or MX scale)
+NONFINITE = [("q", 0, 70, 5, float("nan")), ("k", 1, 10, 3, float("nan")), ("v", 0, 33, 7, float("inf")),
+             ("q", 1, 150, 60, float("inf"))]
+
+
+@pytest.mark.parametrize("qk,pv", ZERO_PAIRS, ids=[f"{a}_{b}" for a, b in ZERO_PAIRS])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_nonfinite_inputs(sage, qk, pv, causal):
+    """NaN or Inf inputs are not errors: they propagate into the scales and rows they reach.
+    The GPU and the oracle's simulation must agree on which outputs (O and LSE) are not finite,
+    the injected element must reach its own output row, and the finite outputs must match."""
+    banner(f"non-finite inputs {qk}/{pv} causal={causal}")
+    B, H, N, d = 1, 2, 200, 64
+    sm = 1 / 8
+    for t, h, row, ch, val in NONFINITE:
+        f, g = _inputs(B, H, N, d, "bf16", 41, 2.0)
+        g[t][0, h, row, ch] = val
+        f[t][h, row, ch] = val
+        o, lse = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv,
+                               return_lse=True)
+        torch.cuda.synchronize()
+        o = to_np64(o).reshape(B * H, N, d)
+        lse = lse.cpu().numpy().reshape(B * H, N).astype(np.float64)
+        with np.errstate(invalid="ignore", over="ignore"):
+            qz = _oracle_quant(f, qk, pv, sm)
+            o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
+        bad, bad_sim = ~np.isfinite(o), ~np.isfinite(o_sim)
+        assert np.array_equal(bad, bad_sim), (t, int(bad.sum()), int(bad_sim.sum()))
+        assert np.array_equal(~np.isfinite(lse), ~np.isfinite(np.asarray(lse_sim, np.float64))), t
+        assert bad[h, row].any() if t != "v" else bad[h, row:, ch].all(), t
+        ok = ~bad
+        assert np.abs(o[ok] - o_sim[ok]).max() <= 2e-2, t
+        okl = np.isfinite(lse)
+        assert np.allclose(lse[okl], np.asarray(lse_sim)[okl], rtol=1e-4, atol=2e-3), t
+
+
 @pytest.mark.parametrize("qk", ["int8", "mxfp4"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_forward_constant_keys_closed_form(sage, qk, causal):

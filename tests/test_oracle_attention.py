@@ -446,6 +446,53 @@ def test_int8_fp8_key_shift_gives_identical_codes_and_output(orc):
                                                        shift[:, 0].astype(np.float64)), rtol=0, atol=1e-10)
 
 
+@pytest.mark.parametrize("qk,pv", [("int8", "fp8"), ("int8", "f16"), ("mxfp4", "fp8"), ("mxfp4", "mxfp4")])
+@pytest.mark.parametrize("causal", [False, True])
+def test_nonfinite_inputs_reach_exactly_their_scales(orc, qk, pv, causal):
+    """A NaN or Inf input is not an error: it reaches the scale it enters and, through the
+    softmax (a NaN score makes its row's normaliser NaN) or the PV product (0 * NaN = NaN for
+    the tile's zero weights too), exactly the outputs that depend on that scale.  Everything
+    else is bit-identical to the run without it.
+      - NaN in Q: INT8 steps are per 64-token block, so that block's rows; MXFP4 smooths Q by
+        its per-head channel mean, so the whole head.
+      - NaN in K: the per-head K mean, so the whole head.
+      - Inf in V at channel c: its per-channel step (FP8), its 32-token MX scale or the value
+        itself (fp16) sits in the first key tile, which every row processes: channel c of
+        every row."""
+    BH, N, d, sm = 2, 200, 64, 0.125
+    q, k, v = _rand((BH, N, d), 81), _rand((BH, N, d), 82) + 2.0, _rand((BH, N, d), 83)
+
+    def run(q, k, v):
+        with np.errstate(invalid="ignore", over="ignore"):
+            if qk == "int8":
+                z = orc.quant_int8_fp8(q, k, v, sm, pv_fmt=pv)
+                return orc.attn_int8_fp8(z, N, d, causal, sm, 64)
+            z = orc.quant_mxfp4(q, k, v, sm, pv_fmt=pv)
+            return orc.attn_mxfp4(z, N, d, causal, sm, 64)
+
+    o0, l0 = run(q, k, v)
+    assert np.isfinite(o0).all() and np.isfinite(l0).all()
+    cases = [("q", 0, 70, 5, np.nan), ("k", 1, 10, 3, np.nan), ("v", 0, 33, 7, np.inf)]
+    for t, h, row, ch, val in cases:
+        x = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+        x[t][h, row, ch] = val
+        o, lse = run(x["q"], x["k"], x["v"])
+        want = np.zeros(o.shape, bool)
+        want_l = np.zeros(lse.shape, bool)
+        if t == "q":
+            rows = slice(64, 128) if qk == "int8" else slice(0, N)
+            want[h, rows] = True
+            want_l[h, rows] = True
+        elif t == "k":
+            want[h] = True
+            want_l[h] = True
+        else:
+            want[h, :, ch] = True
+        assert np.array_equal(~np.isfinite(o), want), t
+        assert np.array_equal(~np.isfinite(lse), want_l), t
+        assert np.array_equal(o[~want], o0[~want]) and np.array_equal(lse[~want_l], l0[~want_l]), t
+
+
 # ---------------------------------------------------------- accuracy on seeded data
 
 def _cos(a, b):

@@ -120,6 +120,17 @@ def test_int8_encode_properties(orc):
     assert orc.int8_encode(2.5, 1.0) == 2 and orc.int8_encode(3.5, 1.0) == 4 and orc.int8_encode(-2.5, 1.0) == -2
 
 
+def test_int8_encode_nonfinite(orc):
+    """Non-finite quotients: the clamp is fmax / fmin (IEEE maxNum / minNum return the non-NaN
+    operand), so NaN clamps to -127 and +-Inf to +-127; a finite x over an infinite step is 0."""
+    nan, inf = float("nan"), float("inf")
+    assert orc.int8_encode(nan, 0.5) == -127
+    assert orc.int8_encode(inf, 0.5) == 127 and orc.int8_encode(-inf, 0.5) == -127
+    assert orc.int8_encode(1.0, inf) == 0 and orc.int8_encode(-3.0, inf) == 0
+    assert orc.int8_encode(inf, inf) == -127          # inf / inf = NaN
+    assert orc.mx_scale_byte(nan, 2) == 0xFF and orc.mx_scale_byte(inf, 2) == 0xFF
+
+
 def test_widen_matches_numpy_and_torch(orc):
     u = np.arange(65536, dtype=np.uint16)
     f = orc.widen(u, "f16")
