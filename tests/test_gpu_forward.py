@@ -388,6 +388,39 @@ def test_full_size_sampled_rows(sage, spec):
     assert torch.isfinite(o).all()
 
 
+@pytest.mark.parametrize("qk", ["int8", "mxfp4"])
+def test_forward_beyond_2e31_elements(sage, qk):
+    """Each input holds more than 2^31 elements (B=1, H=128, N=131149 ragged, d=128, causal):
+    every offset into the inputs, the quantized buffer and the output must be 64-bit.  The
+    oracle recomputes sampled rows of the first and the last head."""
+    import oracle
+    B, H, N, d = 1, 128, 131149, 128
+    assert B * H * N * d > 2 ** 31
+    banner(f"beyond 2^31 elements {qk}")
+    sm = 1 / math.sqrt(d)
+    dev = device()
+    gen = torch.Generator(device=dev).manual_seed(77)
+    q = torch.randn(B, H, N, d, device=dev, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    k = (torch.randn(B, H, N, d, device=dev, generator=gen, dtype=torch.float32) +
+         3.0 * torch.randn(B, H, 1, d, device=dev, generator=gen, dtype=torch.float32)).to(torch.bfloat16)
+    v = torch.randn(B, H, N, d, device=dev, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    o, lse = sage.sageattn(q, k, v, causal=True, sm_scale=sm, qk_fmt=qk, pv_fmt="fp8", return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    heads = [0, H - 1]
+    f = {n: t[0, heads].float().cpu().numpy() for n, t in (("q", q), ("k", k), ("v", v))}
+    del q, k, v
+    rows = sample_rows(N, k=12, seed=3)
+    qz = _oracle_quant(f, qk, "fp8", sm)
+    o_sim, lse_sim = _oracle_sim(f, qz, qk, "fp8", N, d, True, sm, rows=rows)
+    ri = torch.as_tensor(rows, dtype=torch.long, device=dev)
+    og = to_np64(o[0, heads][:, ri])
+    lg = lse[0, heads][:, ri].cpu().numpy()
+    assert np.abs(og - o_sim).max() <= 2e-2
+    assert cos(og, o_sim) >= 0.9999
+    assert np.allclose(lg, lse_sim, rtol=1e-4, atol=2e-3)
+
+
 def test_oneshot_entry_matches_ex(sage):
     banner("one-call entry vs workspace entry")
     f, g = _inputs(1, 4, 512, 128, "bf16", 11, 5.0)
