@@ -107,3 +107,33 @@ def test_autograd_function(sage):
     out.backward(g["do"])
     _, _, dq, dk, dv = _run(sage, x, True, 1 / 8)
     assert torch.equal(q.grad, dq) and torch.equal(k.grad, dk) and torch.equal(v.grad, dv)
+
+
+def test_backward_beyond_2e31_elements_matches_heads_alone(sage):
+    """Each tensor holds more than 2^31 elements (B=1, H=128, N=131149 ragged, d=128, causal).
+    Heads are independent problems (their own statistics, steps and tiles), so the first and
+    the last head must come out bit-identical to the same two heads run alone: every offset
+    into the inputs, the workspace and the gradients must be 64-bit."""
+    B, H, N, d = 1, 128, 131149, 128
+    assert B * H * N * d > 2 ** 31
+    banner("backward beyond 2^31 elements")
+    sm = 1 / math.sqrt(d)
+    dev = device()
+    gen = torch.Generator(device=dev).manual_seed(78)
+    x = {}
+    for n in ("q", "k", "v", "do"):
+        t = torch.randn(B, H, N, d, device=dev, generator=gen, dtype=torch.float32)
+        if n == "k":
+            t += 2.0 * torch.randn(B, H, 1, d, device=dev, generator=gen, dtype=torch.float32)
+        x[n] = t.to(torch.bfloat16)
+        del t
+    heads = [0, H - 1]
+    small = {n: x[n][:, heads].contiguous() for n in x}
+    big = _run(sage, x, True, sm)
+    got = [t[:, heads].contiguous() for t in big]
+    del big, x
+    torch.cuda.empty_cache()
+    want = _run(sage, small, True, sm)
+    for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), got, want):
+        assert torch.isfinite(a).all(), name
+        assert torch.equal(a, b), name
