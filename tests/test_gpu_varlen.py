@@ -178,3 +178,29 @@ def test_varlen_full_size_llm_prefill_sampled(sage):
         og = to_np64(o[sl])
         assert np.abs(og - o_sim).max() <= 2e-2
         assert cos(og, o_sim) >= 0.9999
+
+
+@pytest.mark.parametrize("qk,pv", [("int8", "fp8"), ("mxfp4", "fp8")])
+def test_varlen_beyond_2e31_elements_equals_fixed_length(sage, qk, pv):
+    """Packed tensors of more than 2^31 elements (2 sequences of 65575 tokens, 128 heads,
+    d = 128, causal): bit-identical to the fixed-length entry on the same data, so every
+    packed offset is 64-bit."""
+    B, H, N, d = 2, 128, 65575, 128
+    assert B * N * H * d > 2 ** 31
+    banner(f"varlen beyond 2^31 elements {qk}/{pv}")
+    dev = device()
+    gen = torch.Generator(device=dev).manual_seed(79)
+    x = {n: torch.randn(B, H, N, d, device=dev, generator=gen, dtype=torch.float32).to(torch.bfloat16) for n in "qkv"}
+    of, lf = sage.sageattn(x["q"], x["k"], x["v"], causal=True, qk_fmt=qk, pv_fmt=pv, return_lse=True)
+    torch.cuda.synchronize()
+    pk = {}
+    for n in "qkv":
+        pk[n] = x[n].permute(0, 2, 1, 3).reshape(B * N, H, d).contiguous()
+        del x[n]
+    cu = torch.arange(0, B * N + 1, N, dtype=torch.int32, device=dev)
+    ov, lv = sage.sageattn_varlen(pk["q"], pk["k"], pk["v"], cu, cu, N, N, causal=True, qk_fmt=qk, pv_fmt=pv,
+                                  return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(of).all()
+    assert torch.equal(ov.reshape(B, N, H, d).permute(0, 2, 1, 3), of)
+    assert torch.equal(lv.reshape(H, B, N).permute(1, 0, 2), lf)
