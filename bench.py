@@ -186,10 +186,23 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# Untimed back-to-back work before every timed region.  The GPU's clocks need tens of
+# milliseconds of load to settle: measured on the headline step, the first 50-step region after
+# 10 warmup steps ran at 182 us per step, the same region after 45 ms of load at 152 us, and
+# after 2 s idle at 179 us again.  Throughput is quoted at the settled clocks.
+WARM_S = 0.25
+
+
 def time_region(fn, steps, warmup, torch):
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    """At least `warmup` untimed steps, continued in synchronized batches until WARM_S seconds
+    of back-to-back work have passed; then exactly `steps` steps timed with HIP events on the
+    launch stream (torch's current stream, the one the library launches on)."""
+    n, t_w = 0, time.perf_counter()
+    while n < warmup or time.perf_counter() - t_w < WARM_S:
+        for _ in range(20):
+            fn()
+        n += 20
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
@@ -379,6 +392,8 @@ def main():
         "metric": METRIC, "value": round(r["step_tops"], 2), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8+fp8",
+        "timing": f"each timed region follows >= {args.warmup} untimed steps and >= {WARM_S} s of back-to-back "
+                  f"untimed work (settled GPU clocks)",
         "data": "synthetic (seeded normal Q/K/V, K channel offsets, 1% outlier channels)",
         "config": {"workload": HEADLINE, "B": r["B"], "H": r["H"], "N": r["N"], "d": r["d"], "causal": r["causal"],
                    "qk_fmt": r["qk"], "pv_fmt": r["pv"], "io_dtype": r["dtype"], "parallelism": "single GPU"},
