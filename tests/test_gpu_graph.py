@@ -1,0 +1,64 @@
+"""HIP graph capture of the workspace entry points (fixed-length forward with LSE, 8-bit
+backward, packed-sequence forward): they launch kernels only (no allocation, no memset), so a
+captured graph replayed on new inputs must reproduce the eager calls bit for bit.  Each replay
+is followed by eager work and a synchronization, and every replay is checked."""
+import pytest
+import torch
+
+from gpu_util import banner, device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sage():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_attention_smooth_amd as S
+    S.lib()
+    return S
+
+
+def test_graph_capture_replays_match_eager(sage):
+    banner("graph capture: forward, backward, packed forward")
+    dev = device()
+    B, H, N, d = 1, 4, 1000, 128
+    gen = torch.Generator(device=dev).manual_seed(5)
+    cu = torch.tensor([0, 300, 301, N], dtype=torch.int32, device=dev)
+
+    def fresh():
+        x = {n: torch.randn(B, H, N, d, device=dev, generator=gen).to(torch.bfloat16) for n in ("q", "k", "v", "do")}
+        x["k"] += 2.0 * torch.randn(B, H, 1, d, device=dev, generator=gen).to(torch.bfloat16)
+        return x
+
+    def run(x):
+        o, lse = sage.sageattn(x["q"], x["k"], x["v"], causal=True, return_lse=True)
+        dq, dk, dv = sage.attn_bwd(x["q"], x["k"], x["v"], o, x["do"], lse, causal=True)
+        pk = {n: x[n][0].permute(1, 0, 2).contiguous() for n in "qkv"}   # [N, H, d]: 3 packed sequences
+        ov, lv = sage.sageattn_varlen(pk["q"], pk["k"][:, :2].contiguous(), pk["v"][:, :2].contiguous(), cu, cu,
+                                      699, 699, causal=True, qk_fmt="mxfp4", pv_fmt="mxfp8", return_lse=True)
+        return [o, lse, dq, dk, dv, ov, lv]
+
+    static = fresh()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(static)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = run(static)
+    torch.cuda.synchronize()
+    names = ("o", "lse", "dq", "dk", "dv", "o_packed", "lse_packed")
+    for rep in range(3):
+        x = fresh()
+        for n in x:
+            static[n].copy_(x[n])
+        graph.replay()
+        torch.cuda.synchronize()
+        want = run(x)
+        torch.cuda.synchronize()
+        for name, a, b in zip(names, outs, want):
+            assert torch.isfinite(a).all(), (rep, name)
+            assert torch.equal(a, b), (rep, name)
