@@ -1,7 +1,8 @@
-"""HIP graph capture of the workspace entry points (fixed-length forward with LSE, 8-bit
-backward, packed-sequence forward): they launch kernels only (no allocation, no memset), so a
-captured graph replayed on new inputs must reproduce the eager calls bit for bit.  Each replay
-is followed by eager work and a synchronization, and every replay is checked."""
+"""HIP graph capture and concurrent streams.  The workspace entry points (fixed-length forward
+with LSE, 8-bit backward, packed-sequence forward) launch kernels only (no allocation, no
+memset), so a captured graph replayed on new inputs must reproduce the eager calls bit for bit;
+each replay is followed by eager work and a synchronization, and every replay is checked.
+Calls on two streams at once must give the bits of the same calls run one after another."""
 import pytest
 import torch
 
@@ -62,3 +63,29 @@ def test_graph_capture_replays_match_eager(sage):
         for name, a, b in zip(names, outs, want):
             assert torch.isfinite(a).all(), (rep, name)
             assert torch.equal(a, b), (rep, name)
+
+
+def test_concurrent_streams_match_sequential(sage):
+    """Calls on two streams at once (each with its own workspace, and the one-call entry with its
+    stream-ordered scratch) give the same bits as the same calls run one after another."""
+    banner("two streams at once")
+    dev = device()
+    gen = torch.Generator(device=dev).manual_seed(6)
+    a = {n: torch.randn(1, 8, 2048, 128, device=dev, generator=gen).to(torch.bfloat16) for n in "qkv"}
+    b = {n: torch.randn(2, 4, 777, 64, device=dev, generator=gen).to(torch.bfloat16) for n in "qkv"}
+    want_a = sage.sageattn(a["q"], a["k"], a["v"], causal=True)
+    want_b = sage.attn_fwd_oneshot(b["q"], b["k"], b["v"])
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        s1.wait_stream(torch.cuda.current_stream())
+        s2.wait_stream(torch.cuda.current_stream())
+        outs_a, outs_b = [], []
+        for _ in range(4):
+            with torch.cuda.stream(s1):
+                outs_a.append(sage.sageattn(a["q"], a["k"], a["v"], causal=True))
+            with torch.cuda.stream(s2):
+                outs_b.append(sage.attn_fwd_oneshot(b["q"], b["k"], b["v"]))
+        torch.cuda.synchronize()
+        assert all(torch.equal(o, want_a) for o in outs_a)
+        assert all(torch.equal(o, want_b) for o in outs_b)
