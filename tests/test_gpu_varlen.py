@@ -76,6 +76,24 @@ def test_varlen_gqa_matches_oracle(sage, qk, pv, causal, d):
     assert np.allclose(lse.cpu().numpy(), lse_sim, rtol=1e-4, atol=2e-3)
 
 
+@pytest.mark.parametrize("qk,pv", PAIRS, ids=[f"{a}_{b}" for a, b in PAIRS])
+def test_varlen_f16_io_matches_oracle(sage, qk, pv):
+    """fp16 inputs and outputs on the packed path (ragged lengths, grouped KV heads, causal)."""
+    import oracle
+    banner(f"varlen f16 I/O {qk}/{pv}")
+    lens = [200, 1, 130, 64]
+    H, Hkv, d = 4, 2, 64
+    q, k, v, cu_q, cu_k = _packed(lens, lens, H, Hkv, d, seed=33, dtype=torch.float16)
+    o, lse = _run(sage, q, k, v, cu_q, cu_k, True, 0.125, qk, pv)
+    assert o.dtype == torch.float16
+    o_sim, lse_sim, _ = oracle.attn_varlen(_f32(q), _f32(k), _f32(v), cu_q.numpy(), cu_k.numpy(), True, 0.125,
+                                           qk_fmt=qk, pv_fmt=pv, tile=TILE)
+    og = to_np64(o)
+    assert np.abs(og - o_sim).max() <= 2e-2
+    assert cos(og, o_sim) >= 0.9999
+    assert np.allclose(lse.cpu().numpy(), lse_sim, rtol=1e-4, atol=2e-3)
+
+
 @pytest.mark.parametrize("pv", ["fp8", "mxfp4", "mxfp8"])
 def test_varlen_mxfp4_keys_longer_than_queries(sage, pv):
     """MXFP4 QK without grouped heads, key sequences longer than their query sequences by more
@@ -113,14 +131,15 @@ def test_varlen_empty_sequences(sage):
 
 
 @pytest.mark.parametrize("qk,pv", PAIRS, ids=[f"{a}_{b}" for a, b in PAIRS])
-def test_equal_length_packed_equals_fixed_length(sage, qk, pv):
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_equal_length_packed_equals_fixed_length(sage, qk, pv, dtype):
     """B sequences of one length N, H_kv = H: the packed entry computes exactly what the
     [B,H,N,d] entry does (same per-instance quantization and kernels), bit for bit."""
-    banner(f"packed == fixed {qk}/{pv}")
+    banner(f"packed == fixed {qk}/{pv} {dtype}")
     B, H, N, d = 3, 4, 333, 128
     dev = device()
     g = torch.Generator().manual_seed(5)
-    x = {n: torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).to(dev) for n in "qkv"}
+    x = {n: torch.randn(B, H, N, d, generator=g).to(dtype).to(dev) for n in "qkv"}
     for causal in (False, True):
         of, lf = sage.sageattn(x["q"], x["k"], x["v"], causal=causal, qk_fmt=qk, pv_fmt=pv, return_lse=True)
         pk = {n: x[n].permute(0, 2, 1, 3).reshape(B * N, H, d).contiguous() for n in "qkv"}
