@@ -49,8 +49,8 @@ def _f32(t):
     return t.float().numpy()
 
 
-PAIRS = [("int8", "fp8"), ("int8", "f16"), ("int8_token", "fp8"), ("mxfp4", "fp8"), ("mxfp4", "mxfp4"),
-         ("mxfp4", "mxfp8")]
+PAIRS = [("int8", "fp8"), ("int8", "f16"), ("int8_token", "fp8"), ("int8_token", "f16"), ("mxfp4", "fp8"),
+         ("mxfp4", "mxfp4"), ("mxfp4", "mxfp8")]
 
 
 @pytest.mark.parametrize("qk,pv", PAIRS, ids=[f"{a}_{b}" for a, b in PAIRS])
