@@ -58,7 +58,7 @@ def read_traffic():
 
 
 def _short(kname):
-    return kname.replace("void ", "").split("(")[0]
+    return kname.replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0]
 
 
 def dispatch_counters(path):
@@ -77,11 +77,12 @@ def dispatch_counters(path):
 
 
 def counter_summary(sq_dir, fetch_dir, write_dir, out_path):
-    """Markdown profile: MFMA busy share per fused-kernel launch shape (SQ counters) and the
-    prologue kernels' HBM bytes (FETCH_SIZE / WRITE_SIZE, copy-calibrated) per launch."""
+    """Markdown profile: MFMA busy share per fused-kernel launch shape and of the backward's main
+    kernels (SQ counters), and the prologue kernels' HBM bytes (FETCH_SIZE / WRITE_SIZE,
+    copy-calibrated) per launch."""
     mean = lambda v: sum(v) / len(v)
     sq, _ = dispatch_counters(sq_dir)
-    lines = ["# MFMA busy share of the fused kernels and HBM bytes of the prologue", "",
+    lines = ["# MFMA busy share of the fused forward and backward kernels, and HBM bytes of the prologue", "",
              "Commands (repository root, one MI355X):", "",
              "    rocprofv3 --pmc SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_VALU "
              "SQ_INSTS_MFMA SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES SQ_WAIT_ANY --output-format csv -d <sq_dir> -- "
@@ -99,16 +100,25 @@ def counter_summary(sq_dir, fetch_dir, write_dir, out_path):
              "3 MXFP4, 4 MXFP8, 5 fp16), finer INT8 steps>.", "",
              "| kernel | workgroups | dispatches | MFMA busy | co-exec | VALU instr. per MFMA | wait share of wave cycles |",
              "|---|---|---|---|---|---|---|"]
-    for (k, g), cs in sorted(sq.items(), key=lambda kv: (kv[0][0], -kv[0][1])):
-        if "attn_fwd_kernel" not in k or "SQ_BUSY_CYCLES" not in cs:
-            continue
-        busy = mean(cs["SQ_BUSY_CYCLES"]) / 32.0
-        mfma = mean(cs.get("SQ_VALU_MFMA_BUSY_CYCLES", [0])) / 1024.0
-        coex = mean(cs.get("SQ_VALU_MFMA_COEXEC_CYCLES", [0])) / 1024.0
-        vpm = mean(cs.get("SQ_INSTS_VALU", [0])) / max(1.0, mean(cs.get("SQ_INSTS_MFMA", [1])))
-        wait = mean(cs.get("SQ_WAIT_ANY", [0])) / max(1.0, mean(cs.get("SQ_WAVE_CYCLES", [1])))
-        lines.append(f"| `{k}` | {g} | {len(cs['SQ_BUSY_CYCLES'])} | {100 * mfma / busy:.1f} % | "
-                     f"{100 * coex / max(mfma, 1e-9):.0f} % | {vpm:.1f} | {100 * wait:.0f} % |")
+    def sq_rows(match):
+        for (k, g), cs in sorted(sq.items(), key=lambda kv: (kv[0][0], -kv[0][1])):
+            if not match(k) or "SQ_BUSY_CYCLES" not in cs:
+                continue
+            busy = mean(cs["SQ_BUSY_CYCLES"]) / 32.0
+            mfma = mean(cs.get("SQ_VALU_MFMA_BUSY_CYCLES", [0])) / 1024.0
+            coex = mean(cs.get("SQ_VALU_MFMA_COEXEC_CYCLES", [0])) / 1024.0
+            vpm = mean(cs.get("SQ_INSTS_VALU", [0])) / max(1.0, mean(cs.get("SQ_INSTS_MFMA", [1])))
+            wait = mean(cs.get("SQ_WAIT_ANY", [0])) / max(1.0, mean(cs.get("SQ_WAVE_CYCLES", [1])))
+            lines.append(f"| `{k}` | {g} | {len(cs['SQ_BUSY_CYCLES'])} | {100 * mfma / busy:.1f} % | "
+                         f"{100 * coex / max(mfma, 1e-9):.0f} % | {vpm:.1f} | {100 * wait:.0f} % |")
+
+    sq_rows(lambda k: "attn_fwd_kernel" in k)
+    lines += ["", "## Backward kernels (training workloads B=8 H=16 N=2048, causal; d = 64 and 128)", "",
+              "Template arguments: <head dim, causal, I/O dtype>.  At d = 128 one workgroup runs per CU (one wave",
+              "per SIMD).", "",
+              "| kernel | workgroups | dispatches | MFMA busy | co-exec | VALU instr. per MFMA | wait share of wave cycles |",
+              "|---|---|---|---|---|---|---|"]
+    sq_rows(lambda k: "bwd_dq_kernel" in k or "bwd_dkdv_kernel" in k)
     fe, fdur = dispatch_counters(fetch_dir)
     wr, _ = dispatch_counters(write_dir)
     copy = lambda d, c: max(mean(v[c]) for k, v in d.items() if "sage" not in k[0] and c in v)
