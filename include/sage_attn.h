@@ -47,7 +47,7 @@ extern "C" {
 typedef enum {
     SAGE_OK = 0,
     SAGE_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad scale, misaligned pointer */
-    SAGE_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement (d, format pair) */
+    SAGE_ERR_UNSUPPORTED = 2,   /* valid request the library does not implement (d, format pair) */
     SAGE_ERR_WORKSPACE = 3,     /* workspace or quant buffer smaller than required */
     SAGE_ERR_OUT_OF_MEMORY = 4, /* internal device allocation failed */
     SAGE_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
