@@ -157,6 +157,41 @@ def test_forward_matches_oracle(sage, case):
     assert np.allclose(lse, lse_sim, rtol=1e-4, atol=2e-3)
 
 
+SWEEP_PAIRS = [("int8", "fp8"), ("int8", "f16"), ("int8_token", "fp8"), ("int8_token", "f16"), ("mxfp4", "fp8"),
+               ("mxfp4", "mxfp4"), ("mxfp4", "mxfp8"), ("mxfp4_qblock", "fp8"), ("mxfp4_qblock", "mxfp4"),
+               ("mxfp4_qblock", "mxfp8")]
+
+
+def _sweep_case(i):
+    """Configuration i of a seeded random sweep over shapes, dtypes, masks and format pairs."""
+    rng = np.random.default_rng(1000 + i)
+    qk, pv = SWEEP_PAIRS[i % len(SWEEP_PAIRS)]
+    return dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 5)), N=int(rng.integers(1, 701)),
+                d=int(rng.choice([64, 128])), dt=str(rng.choice(["bf16", "f16"])), causal=bool(rng.integers(0, 2)),
+                qk=qk, pv=pv, koff=float(rng.choice([0.0, 3.0])), sm=float(rng.uniform(0.05, 0.2)))
+
+
+@pytest.mark.parametrize("i", range(120))
+def test_forward_random_sweep(sage, i):
+    """Seeded random configurations: codes bit-exact and outputs within the forward tolerances of
+    the oracle's simulation."""
+    c = _sweep_case(i)
+    banner(f"sweep {i}: {c}")
+    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
+    f, g = _inputs(B, H, N, d, c["dt"], 2000 + i, c["koff"])
+    buf, p, lay = sage.quantize(g["q"], g["k"], g["v"], causal=c["causal"], sm_scale=c["sm"], qk_fmt=c["qk"],
+                                pv_fmt=c["pv"])
+    o, lse = sage.attn_fwd_quantized(buf, p, dtype=g["q"].dtype, return_lse=True)
+    torch.cuda.synchronize()
+    qz = _oracle_quant(f, c["qk"], c["pv"], c["sm"])
+    _check_codes(_unpack(buf, p, lay, c["qk"], c["pv"]), qz, c["qk"], c["pv"])
+    o = to_np64(o).reshape(B * H, N, d)
+    o_sim, lse_sim = _oracle_sim(f, qz, c["qk"], c["pv"], N, d, c["causal"], c["sm"])
+    assert np.abs(o - o_sim).max() <= 2e-2
+    assert cos(o, o_sim) >= 0.9999
+    assert np.allclose(lse.cpu().numpy().reshape(B * H, N), lse_sim, rtol=1e-4, atol=2e-3)
+
+
 @pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 127, 128, 129, 192])
 @pytest.mark.parametrize("causal", [False, True])
 def test_forward_edge_lengths(sage, N, causal):
