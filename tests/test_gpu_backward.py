@@ -137,3 +137,26 @@ def test_backward_beyond_2e31_elements_matches_heads_alone(sage):
     for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), got, want):
         assert torch.isfinite(a).all(), name
         assert torch.equal(a, b), name
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_backward_random_sweep(sage, i):
+    """Seeded random configurations (B <= 2, H <= 3, N in [64, 400], d 64 or 128, bf16 or fp16,
+    causal or not, K channel offsets or not): every gradient within the backward band of the
+    exact fp64 gradients."""
+    import oracle
+    from bit_quantized_attention_smooth_amd.workloads import make_inputs, as_u16
+    rng = np.random.default_rng(3000 + i)
+    B, H, N = int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(64, 401))
+    d, dtype = int(rng.choice([64, 128])), str(rng.choice(["bf16", "f16"]))
+    causal, koff = bool(rng.integers(0, 2)), float(rng.choice([0.0, 2.0]))
+    sm = 1 / math.sqrt(d)
+    banner(f"backward sweep {i}: B={B} H={H} N={N} d={d} {dtype} causal={causal} koff={koff}")
+    x = make_inputs(B, H, N, d, dtype=dtype, seed=4000 + i, k_off_std=koff, with_do=True)
+    _, _, dq, dk, dv = _run(sage, x, causal, sm)
+    f = {n: oracle.widen(as_u16(x[n]), dtype).reshape(B * H, N, d) for n in ("q", "k", "v", "do")}
+    rq, rk, rv = oracle.attn_bwd_ref(f["q"], f["k"], f["v"], f["do"], causal, sm)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        g = to_np64(got).reshape(B * H, N, d)
+        assert np.isfinite(g).all(), name
+        assert cos(g, ref) >= 0.99, (name, cos(g, ref))

@@ -223,3 +223,38 @@ def test_varlen_beyond_2e31_elements_equals_fixed_length(sage, qk, pv):
     assert torch.isfinite(of).all()
     assert torch.equal(ov.reshape(B, N, H, d).permute(0, 2, 1, 3), of)
     assert torch.equal(lv.reshape(H, B, N).permute(1, 0, 2), lf)
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_varlen_random_sweep(sage, i):
+    """Seeded random packed batches: up to 4 sequences of 0..300 tokens (query and key lengths
+    equal when causal), grouped KV heads, d 64 or 128, bf16 or fp16, every format pair; within
+    the forward tolerances of the oracle's per-sequence simulation."""
+    import oracle
+    rng = np.random.default_rng(5000 + i)
+    qk, pv = PAIRS[i % len(PAIRS)]
+    nb = int(rng.integers(1, 5))
+    causal = bool(rng.integers(0, 2))
+    lens_q = [int(v) for v in rng.integers(0, 301, nb)]
+    lens_k = lens_q if causal else [int(v) for v in rng.integers(0, 301, nb)]
+    Hkv = int(rng.choice([1, 2]))
+    H = Hkv * int(rng.choice([1, 2, 3]))
+    d = int(rng.choice([64, 128]))
+    dtype = torch.float16 if rng.integers(0, 2) else torch.bfloat16
+    sm = float(rng.uniform(0.05, 0.2))
+    banner(f"varlen sweep {i}: {qk}/{pv} lens_q={lens_q} lens_k={lens_k} H={H}/{Hkv} d={d} {dtype} causal={causal}")
+    if sum(lens_q) == 0:   # the entry needs non-empty q, k and v tensors
+        lens_q = lens_q[:-1] + [1]
+        if causal:
+            lens_k = lens_q
+    if sum(lens_k) == 0:
+        lens_k = lens_k[:-1] + [1]
+    q, k, v, cu_q, cu_k = _packed(lens_q, lens_k, H, Hkv, d, seed=6000 + i, dtype=dtype)
+    o, lse = _run(sage, q, k, v, cu_q, cu_k, causal, sm, qk, pv, max_q=max(lens_q), max_k=max(max(lens_k), 1))
+    o_sim, lse_sim, _ = oracle.attn_varlen(_f32(q), _f32(k), _f32(v), cu_q.numpy(), cu_k.numpy(), causal, sm,
+                                           qk_fmt=qk, pv_fmt=pv, tile=TILE)
+    og = to_np64(o)
+    assert np.abs(og - o_sim).max() <= 2e-2
+    if np.abs(o_sim).max() > 0:
+        assert cos(og, o_sim) >= 0.9999
+    assert np.allclose(lse.cpu().numpy(), lse_sim, rtol=1e-4, atol=2e-3)
