@@ -33,7 +33,10 @@
  *   e = floor(log2 amax) - 2; P~ in the 4-bit path gets a per-row per-K-tile
  *   fp32 scale sigma = 6 / max_tile(p) before MX quantization over 32-key groups;
  *   the row sum l accumulates the unquantized p; LSE is natural-log over the
- *   true (unsmoothed) scores.
+ *   true (unsmoothed) scores.  Non-finite inputs follow IEEE arithmetic through
+ *   these steps: a NaN score makes its row's max and sum NaN (not a masked key),
+ *   the E8M0 byte 0xFF is NaN (OCP MX), the P~V sum takes every key of the tile
+ *   (0 * NaN = NaN), and INT8 codes clamp with fmaxf / fminf (NaN -> -127).
  */
 #include <math.h>
 #include <stdint.h>
