@@ -381,7 +381,7 @@ def main():
                     help="write the MFMA-busy / prologue-HBM profile summary from rocprofv3 counter runs and exit")
     args = ap.parse_args()
     if args.counters:
-        counter_summary(*args.counters, os.path.join(ROOT, "profiles", "counters_attn_fwd_and_prologue.md"))
+        counter_summary(*args.counters, os.path.join(ROOT, "profiles", "counters_attn_fwd_attn_bwd_and_prologue.md"))
         return
     if args.traffic:
         traffic_summary(*args.traffic)
