@@ -3,7 +3,9 @@
 Only the tests, the package smoke check and the benchmark's CPU-baseline leg
 use this package; the library's product path never imports it.  The numeric
 work is plain C in ``sage_oracle.c`` (fp64 unless the format fixes fp32),
-loaded here through ctypes; this file only marshals numpy arrays.
+loaded here through ctypes.  This file marshals numpy arrays to it and, for
+packed sequences, slices each sequence out of the packed arrays and repeats KV
+heads for grouped-query attention (attn_varlen); it holds no other arithmetic.
 """
 import ctypes
 import os
@@ -49,12 +51,6 @@ def lib():
         L.or_int8_encode.argtypes = [ctypes.c_float, ctypes.c_float]
         _lib = L
     return _lib
-
-
-def set_p_decision_fp32(on):
-    """P~ codes decided in the fused kernel's fp32 arithmetic (on, the default) or from the fp64
-    scores (off).  A process-wide switch: whoever turns it off turns it back on."""
-    lib().or_set_p_decision_fp32(int(bool(on)))
 
 
 def _p(a):
@@ -170,38 +166,43 @@ def _rows(rows, N):
     return rows
 
 
-def attn_int8_fp8(qz, N, d, causal, sm, tile, rows=None, blk=64):
-    """Tiled quantized forward (INT8 QK; FP8 or fp16 P~V) on a quant_int8_fp8 result (N = query rows)."""
+def attn_int8_fp8(qz, N, d, causal, sm, tile, rows=None, blk=64, slack=False):
+    """Tiled quantized forward (INT8 QK; FP8 or fp16 P~V) on a quant_int8_fp8 result (N = query rows).
+    Returns (out, lse), or (out, lse, slack) with slack: per output element, how far a different
+    choice among the admissible P~ codes could move it (zero for almost every element)."""
     BH, Nq, Nk = qz["qc"].shape[0], qz["qc"].shape[1], qz["kc"].shape[1]
     assert N == Nq
     rows = _rows(rows, N)
     out = np.empty((BH, len(rows), d), np.float64)
     lse = np.empty((BH, len(rows)), np.float64)
+    sl = np.empty((BH, len(rows), d), np.float64)
     qblk, kblk = qz.get("qblk", blk), qz.get("kblk", blk)
     if qz.get("pv_fmt", "fp8") == "f16":
         lib().or_attn_int8_f16_x(_p(qz["qc"]), _p(qz["qs"]), _p(qz["kc"]), _p(qz["ks"]), _p(qz["vh"]),
                                  _p(qz["corr"]), BH, Nq, Nk, d, qblk, kblk, tile, int(causal),
-                                 ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
+                                 ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse), _p(sl))
     else:
         lib().or_attn_int8_fp8_x(_p(qz["qc"]), _p(qz["qs"]), _p(qz["kc"]), _p(qz["ks"]), _p(qz["vc"]),
                                  _p(qz["vs"]), _p(qz["corr"]), BH, Nq, Nk, d, qblk, kblk, tile, int(causal),
-                                 ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
-    return out, lse
+                                 ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse), _p(sl))
+    return (out, lse, sl) if slack else (out, lse)
 
 
-def attn_mxfp4(qz, N, d, causal, sm, tile, rows=None):
-    """Tiled quantized forward (MXFP4 QK; P~V as MXFP4, FP8, or FP8 P~ with MXFP8 V); N = query rows."""
+def attn_mxfp4(qz, N, d, causal, sm, tile, rows=None, slack=False):
+    """Tiled quantized forward (MXFP4 QK; P~V as MXFP4, FP8, or FP8 P~ with MXFP8 V); N = query rows.
+    Returns (out, lse), or (out, lse, slack) as attn_int8_fp8."""
     BH, Nq, Nk = qz["qc"].shape[0], qz["qc"].shape[1], qz["kc"].shape[1]
     assert N == Nq
     rows = _rows(rows, N)
     out = np.empty((BH, len(rows), d), np.float64)
     lse = np.empty((BH, len(rows)), np.float64)
+    sl = np.empty((BH, len(rows), d), np.float64)
     pv = _PV[qz["pv_fmt"]]
     dS = np.ascontiguousarray(qz["dS"])
     lib().or_attn_mxfp4_x(_p(qz["qc"]), _p(qz["qe"]), _p(qz["kc"]), _p(qz["ke"]), _p(dS), _p(qz["corr"]),
                           _p(qz["vc"]), _p(qz["ve"]), _p(qz["vs"]), pv, qz.get("qsb", 0), BH, Nq, Nk, d, tile, int(causal),
-                          ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse))
-    return out, lse
+                          ctypes.c_double(sm), _p(rows), len(rows), _p(out), _p(lse), _p(sl))
+    return (out, lse, sl) if slack else (out, lse)
 
 
 def attn_tiled_exact(q, k, v, causal, sm, tile, smooth_q=False, rows=None):
@@ -248,16 +249,22 @@ def _seq_heads(x, c0, c1, Hx, H):
     return np.repeat(seg, H // Hx, axis=0) if Hx != H else seg
 
 
-def attn_varlen(q, k, v, cu_q, cu_k, causal, sm, qk_fmt="int8", pv_fmt="fp8", tile=64, exact=False):
+def attn_varlen(q, k, v, cu_q, cu_k, causal, sm, qk_fmt="int8", pv_fmt="fp8", tile=64, exact=False, slack=False):
     """Packed sequences: q [total_q,H,d], k and v [total_k,Hkv,d], cu_q / cu_k [B+1].  Sequence b
     is attention of q rows [cu_q[b], cu_q[b+1]) against k, v rows [cu_k[b], cu_k[b+1]), query head
     h reading KV head h // (H / Hkv).  Returns o [total_q,H,d], lse [H,total_q] and the per-sequence
-    prologue results (None when exact: the exact fp64 reference)."""
+    prologue results (None when exact: the exact fp64 reference); with slack, also the admissible
+    P~ slack of every output element ([total_q,H,d], zero for exact).
+
+    Beyond marshalling, this driver does the packed-sequence bookkeeping in numpy: it slices each
+    sequence out of the packed arrays and repeats each KV head for the query heads that share it,
+    then runs the per-sequence prologue and simulation above on the slices."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     total_q, H, d = q.shape
     Hkv = k.shape[1]
     assert H % Hkv == 0
     o = np.zeros((total_q, H, d), np.float64)
+    sl = np.zeros((total_q, H, d), np.float64)
     lse = np.full((H, total_q), -np.inf)
     quants = []
     for b in range(len(cu_q) - 1):
@@ -266,17 +273,20 @@ def attn_varlen(q, k, v, cu_q, cu_k, causal, sm, qk_fmt="int8", pv_fmt="fp8", ti
             quants.append(None)
             continue
         qs, ks, vs = _seq_heads(q, q0, q1, H, H), _seq_heads(k, k0, k1, Hkv, H), _seq_heads(v, k0, k1, Hkv, H)
+        sb = None
         if exact:
             ob, lb = attn_ref(qs, ks, vs, causal, sm)
             qz = None
         elif qk_fmt in ("int8", "int8_token"):
             fine = qk_fmt == "int8_token"
             qz = quant_int8_fp8(qs, ks, vs, sm, pv_fmt=pv_fmt, qblk=1 if fine else 64, kblk=32 if fine else 64)
-            ob, lb = attn_int8_fp8(qz, q1 - q0, d, causal, sm, tile)
+            ob, lb, sb = attn_int8_fp8(qz, q1 - q0, d, causal, sm, tile, slack=True)
         else:
             qz = quant_mxfp4(qs, ks, vs, sm, pv_fmt=pv_fmt)
-            ob, lb = attn_mxfp4(qz, q1 - q0, d, causal, sm, tile)
+            ob, lb, sb = attn_mxfp4(qz, q1 - q0, d, causal, sm, tile, slack=True)
         o[q0:q1] = np.transpose(ob, (1, 0, 2))
+        if sb is not None:
+            sl[q0:q1] = np.transpose(sb, (1, 0, 2))
         lse[:, q0:q1] = lb
         quants.append(qz)
-    return o, lse, quants
+    return (o, lse, quants, sl) if slack else (o, lse, quants)

@@ -33,7 +33,10 @@
  *   e = floor(log2 amax) - 2; P~ in the 4-bit path gets a per-row per-K-tile
  *   fp32 scale sigma = 6 / max_tile(p) before MX quantization over 32-key groups;
  *   the row sum l accumulates the unquantized p; LSE is natural-log over the
- *   true (unsmoothed) scores.  Non-finite inputs follow IEEE arithmetic through
+ *   true (unsmoothed) scores.  Every P~ code is decided from the fp64 p; a
+ *   weight whose p lies within a stated relative window of a rounding boundary
+ *   has a second admissible code, and the simulation reports, per output, how
+ *   far the other choice could move it (see p_window).  Non-finite inputs follow IEEE arithmetic through
  *   these steps: a NaN score makes its row's max and sum NaN (not a masked key),
  *   the E8M0 byte 0xFF is NaN (OCP MX), the P~V sum takes every key of the tile
  *   (0 * NaN = NaN), and INT8 codes clamp with fmaxf / fminf (NaN -> -127).
@@ -480,20 +483,9 @@ typedef struct {
     const uint8_t *ve;         /* PV_MXFP4 / PV_MXFP8 E8M0 bytes [ceil(N/32), d] */
     const uint16_t *vh;        /* PV_F16 fp16 codes */
     const double *corr;        /* per-row LSE correction (may be NULL) */
+    double *vdec;              /* vval of every (key, channel), decoded once per head by run_rows */
+    double *q4d, *k4d;         /* QK_MXFP4: the E2M1 element values of q4 and k4, decoded likewise */
 } head_t;
-
-/* INT8 QK: the exact integer dot product of the codes of query i and key j. */
-static int64_t int8_dot(const head_t *H, int i, int j)
-{
-    int64_t acc = 0;
-    for (int c = 0; c < H->d; c++)
-        acc += (int64_t)H->qc[(int64_t)i * H->d + c] * (int64_t)H->kc[(int64_t)j * H->d + c];
-    return acc;
-}
-
-/* Whether P~ codes are decided in fp32 from the INT8 scores (see forward_row). */
-static int g_p32 = 1;
-OR_API void or_set_p_decision_fp32(int on) { g_p32 = on; }
 
 /* MXFP4 QK: the dot product of the decoded MX codes of query i and key j.  Each 32-channel
  * block sums to a multiple of 2^-2 times its scale pair, below 2^11 of it, so fp64 holds the
@@ -504,15 +496,17 @@ static double mx_dot(const head_t *H, int i, int j)
     double s = 0.0;
     for (int g = 0; g < ng; g++) {
         double part = 0.0;
-        for (int c = 32 * g; c < 32 * g + 32; c++)
-            part += or_e2m1_decode(H->q4[(int64_t)i * d + c]) * or_e2m1_decode(H->k4[(int64_t)j * d + c]);
+        for (int c = 32 * g; c < 32 * g + 32; c++)   /* or_e2m1_decode of q4 and k4, read from tables */
+            part += H->q4d[(int64_t)i * d + c] * H->k4d[(int64_t)j * d + c];
         s += part * e8m0_decode(H->qe[(int64_t)i * ng + g]) * e8m0_decode(H->ke[(int64_t)j * ng + g]);
     }
     return s;
 }
 
-/* Unscaled score s_ij (sm not applied). */
-static double score(const head_t *H, int i, int j)
+/* Unscaled score s_ij (sm not applied).  *mag receives the magnitude the score is built
+ * from: |s| itself, or |Q_s K_s| + |dS| when the smoothing term dS is added to a dot product
+ * (the two may cancel). */
+static double score(const head_t *H, int i, int j, double *mag)
 {
     int d = H->d;
     double s = 0.0;
@@ -521,20 +515,24 @@ static double score(const head_t *H, int i, int j)
             s += H->qx[(int64_t)i * d + c] * H->kx[(int64_t)j * d + c];
         if (H->dSx)
             s += H->dSx[j];
+        *mag = fabs(s);
     } else if (H->qk == QK_INT8) {
         int64_t acc = 0;
         for (int c = 0; c < d; c++)
             acc += (int64_t)H->qc[(int64_t)i * d + c] * (int64_t)H->kc[(int64_t)j * d + c];
         s = (double)H->qs[i / H->qblk] * (double)H->ks[j / H->kblk] * (double)acc;
+        *mag = fabs(s);
     } else {
         s = mx_dot(H, i, j);
-        if (H->dS)
-            s += (double)H->dS[(int64_t)(H->qsb ? i / H->qsb : 0) * H->N + j];
+        double ds = H->dS ? (double)H->dS[(int64_t)(H->qsb ? i / H->qsb : 0) * H->N + j] : 0.0;
+        *mag = fabs(s) + fabs(ds);
+        s += ds;
     }
     return s;
 }
 
-/* Decoded V element (without the per-channel FP8 scale, which the epilogue applies). */
+/* Decoded V element (without the per-channel FP8 scale, which the epilogue applies).  run_rows
+ * evaluates it once per (key, channel) into H->vdec, which the row loop reads. */
 static double vval(const head_t *H, int j, int c)
 {
     int64_t idx = (int64_t)j * H->d + c;
@@ -550,16 +548,57 @@ static double vval(const head_t *H, int j, int c)
     return or_e2m1_decode(H->vc[idx]) * e;
 }
 
-static void forward_row(const head_t *H, int i, double *o, double *lse)
+/*
+ * Admissible P~ codes.  A P~ code is a value that floating point decides: the code of 448 p
+ * (FP8), of p (fp16) or of sigma p under an MX scale (MXFP4).  The pages fix no precision for
+ * p, so the oracle decides every code from its fp64 p, and states for each weight how far a
+ * correct evaluation in lower precision may move it.  An implementation that forms the exp
+ * argument from binary32 quantities (the scale product, the running max, the score and the
+ * smoothing term, each rounded a few times) and evaluates exp to a few ulps moves p by a
+ * relative amount below
+ *     eps = 2^-20 (8 + (|x| + |m| + |m_tile|) log2 e),
+ * with x the scaled score (or, with a smoothing term, the sum of the magnitudes it is built
+ * from) and m, m_tile the running and tile maxima, all in natural-log units: each binary32
+ * rounding of a log2-domain quantity of size A costs at most 2^-24 A, and the bound keeps a
+ * factor of about four over the sum of them.  Every code reachable from p (1 +- eps) is then
+ * admissible; `dq` receives the width of that set in the code's own units (0 for almost every
+ * weight: only values within eps of a rounding midpoint, of the E4M3 saturation point or of a
+ * power of two that fixes an MX scale have a second admissible code).
+ */
+static double p_window(double xmag, double m, double mt)
+{
+    double a = fabs(xmag) + (isfinite(m) ? fabs(m) : 0.0) + (isfinite(mt) ? fabs(mt) : 0.0);
+    return ldexp(8.0 + a * 1.4426950408889634, -20);
+}
+
+static double e4m3_round(double y) { return or_e4m3_decode(or_e4m3_encode(y)); }
+static double f16_round(double y) { return or_f16_decode(or_f16_encode(y)); }
+
+/* E2M1 value of y under the E8M0 byte sb (the MX element rule), in y's units. */
+static double e2m1_round_scaled(double y, uint8_t sb)
+{
+    double s = ldexp(1.0, (int)sb - 127);
+    return or_e2m1_decode(or_e2m1_encode(y / s)) * s;
+}
+
+/*
+ * One query row of the tiled quantized forward.  o [d] and lse; slack [d] (may be NULL): for
+ * each output channel, the largest change of o that a different choice among the admissible
+ * P~ codes (see p_window) can make -- sum over weights with two admissible codes of
+ * (width) |v| carried through the same rescales and normalisation as O.
+ */
+static void forward_row(const head_t *H, int i, double *o, double *lse, double *slack)
 {
     int N = H->N, d = H->d, T = H->tile;
     double *O = calloc((size_t)d, sizeof(double));
+    double *Sl = calloc((size_t)d, sizeof(double));
     double *acc = malloc(sizeof(double) * (size_t)d);
     double *x = malloc(sizeof(double) * (size_t)T);
+    double *xm = malloc(sizeof(double) * (size_t)T);
     double *p = malloc(sizeof(double) * (size_t)T);
     double *pq = malloc(sizeof(double) * (size_t)T);
+    double *dq = malloc(sizeof(double) * (size_t)T);
     double m = -INFINITY, l = 0.0;
-    float m32 = -INFINITY;         /* INT8 P~ decisions: the kernel's fp32 running max */
     for (int j0 = 0; j0 < N; j0 += T) {
         if (H->causal && j0 > i)
             break;
@@ -568,7 +607,9 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
         double mt = -INFINITY;
         for (int jj = 0; jj < n; jj++) {
             int j = j0 + jj;
-            x[jj] = (H->causal && j > i) ? -INFINITY : H->sm * score(H, i, j);
+            double mag = 0.0;
+            x[jj] = (H->causal && j > i) ? -INFINITY : H->sm * score(H, i, j, &mag);
+            xm[jj] = H->sm * mag;
             if (x[jj] > mt || isnan(x[jj]))        /* a NaN score makes the row max NaN */
                 mt = x[jj];
         }
@@ -584,63 +625,27 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
                 pmax = p[jj];
         }
         l = alpha * l + psum;
-        /* The P~ codes are quantized values that floating point decides, so on the INT8 paths
-         * and on the MXFP4-QK paths with FP8 P~ (where every input of that decision is
-         * reproducible) they are decided in the fused kernel's fp32 arithmetic.  The exp2
-         * argument is the fp32 FMA a * c + (log2 s - m), with (a, c) = (the INT8 code dot
-         * product, fl32(fl32(step_q * fl32(sm * log2 e)) * step_k)) or (u, 1) for MXFP4, where
-         * u = fma(fl32(S), fl32(sm * log2 e), fl32(dS * fl32(sm * log2 e))) and S is the exact
-         * MX code dot product; the tile max fl32(a * c) is folded into an fp32 running max m,
-         * and p = exp2(...) is rounded to fp32 (s = 448 for FP8, 1 for fp16).  Only the codes
-         * come from this; the row sums, the rescales and the LSE stay fp64. */
-        float *p32 = NULL;
-        int dec32 = (H->qk == QK_INT8 && (H->pv == PV_FP8 || H->pv == PV_F16)) ||
-                    (H->qk == QK_MXFP4 && (H->pv == PV_FP8 || H->pv == PV_MXFP8));
-        if (g_p32 && dec32) {
-            p32 = malloc(sizeof(float) * (size_t)n);
-            const float sml2e = (float)H->sm * 1.4426950408889634f;
-            float mt32 = -INFINITY;
-            float *c32 = malloc(sizeof(float) * (size_t)n);
-            float *a32 = malloc(sizeof(float) * (size_t)n);
-            for (int jj = 0; jj < n; jj++) {
-                int j = j0 + jj;
-                if (H->qk == QK_INT8) {
-                    float c = H->qs[i / H->qblk] * sml2e * H->ks[j / H->kblk];
-                    c32[jj] = c == 0.0f ? 1.0f : c;
-                    a32[jj] = (float)int8_dot(H, i, j);     /* |a| < 2^24: exact */
-                } else {
-                    float ds = H->dS ? H->dS[(int64_t)(H->qsb ? i / H->qsb : 0) * H->N + j] * sml2e : 0.0f;
-                    c32[jj] = 1.0f;
-                    a32[jj] = fmaf((float)mx_dot(H, i, j), sml2e, ds);
-                }
-                if (x[jj] != -INFINITY) {
-                    float t = a32[jj] * c32[jj];
-                    if (t > mt32)
-                        mt32 = t;
-                }
-            }
-            float mnew = m32 > mt32 ? m32 : mt32;
-            m32 = mnew;
-            float mref = mnew == -INFINITY ? 0.0f : mnew;
-            float off = (H->pv == PV_F16 ? 0.0f : 8.807354922057604f) - mref;
-            for (int jj = 0; jj < n; jj++)
-                p32[jj] = x[jj] == -INFINITY ? 0.0f : (float)exp2((double)fmaf(a32[jj], c32[jj], off));
-            free(c32);
-            free(a32);
-        }
-        /* P~: quantize the tile row */
+        /* P~: quantize the tile row; dq = width of each weight's admissible set */
         double post = 1.0;
+        for (int jj = 0; jj < n; jj++)
+            dq[jj] = 0.0;
         if (H->pv == PV_EXACT) {
             for (int jj = 0; jj < n; jj++)
                 pq[jj] = p[jj];
-        } else if (H->pv == PV_FP8 || H->pv == PV_MXFP8) {
-            /* static x448 scale: p <= 1 fills the E4M3 range */
-            for (int jj = 0; jj < n; jj++)
-                pq[jj] = or_e4m3_decode(or_e4m3_encode(p32 ? (double)p32[jj] : 448.0 * p[jj]));
-        } else if (H->pv == PV_F16) {
-            /* 16-bit P~: p itself rounded to fp16 */
-            for (int jj = 0; jj < n; jj++)
-                pq[jj] = or_f16_decode(or_f16_encode(p32 ? (double)p32[jj] : p[jj]));
+        } else if (H->pv == PV_FP8 || H->pv == PV_MXFP8 || H->pv == PV_F16) {
+            /* FP8: static x448 scale, p <= 1 fills the E4M3 range; fp16: p itself */
+            int f16 = H->pv == PV_F16;
+            double s = f16 ? 1.0 : 448.0;
+            for (int jj = 0; jj < n; jj++) {
+                double y = s * p[jj];
+                pq[jj] = f16 ? f16_round(y) : e4m3_round(y);
+                if (p[jj] > 0.0) {
+                    double e = p_window(xm[jj], mn, mt);
+                    double lo = f16 ? f16_round(y * (1.0 - e)) : e4m3_round(y * (1.0 - e));
+                    double hi = f16 ? f16_round(y * (1.0 + e)) : e4m3_round(y * (1.0 + e));
+                    dq[jj] = hi - lo;
+                }
+            }
         } else if (pmax == 0.0) {
             for (int jj = 0; jj < n; jj++)
                 pq[jj] = 0.0;
@@ -655,8 +660,28 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
                 int gn = n - g0 < 32 ? n - g0 : 32;
                 uint8_t sb;
                 quant_mx_group(pf + g0, gn, 1, 4, codes + g0, 1, &sb);
-                for (int jj = g0; jj < g0 + gn; jj++)
+                /* admissible scales: those of the group max moved by its window */
+                double a = 0.0, eg = 0.0;
+                for (int jj = g0; jj < g0 + gn; jj++) {
+                    double e = pf[jj] > 0.0f ? p_window(xm[jj], mn, mt) : 0.0;
+                    if (fabs((double)pf[jj]) > a)
+                        a = fabs((double)pf[jj]);
+                    if (e > eg)
+                        eg = e;
+                }
+                uint8_t sbs[2] = {or_mx_scale_byte(a * (1.0 - eg), 2), or_mx_scale_byte(a * (1.0 + eg), 2)};
+                for (int jj = g0; jj < g0 + gn; jj++) {
                     pq[jj] = or_e2m1_decode(codes[jj]) * e8m0_decode(sb);
+                    if (pf[jj] > 0.0f && a > 0.0) {
+                        double e = p_window(xm[jj], mn, mt), lo = INFINITY, hi = -INFINITY;
+                        for (int k = 0; k < 4; k++) {
+                            double v = e2m1_round_scaled((double)pf[jj] * (k & 1 ? 1.0 + e : 1.0 - e), sbs[k >> 1]);
+                            lo = v < lo ? v : lo;
+                            hi = v > hi ? v : hi;
+                        }
+                        dq[jj] = hi - lo;
+                    }
+                }
             }
             post = 1.0 / (double)sigma;
             free(pf);
@@ -668,48 +693,89 @@ static void forward_row(const head_t *H, int i, double *o, double *lse)
         /* every key of the tile, zero weights included: 0 * NaN = NaN, as in the matrix product */
         for (int jj = 0; jj < n; jj++)
             for (int c = 0; c < d; c++)
-                acc[c] += pq[jj] * vval(H, j0 + jj, c);
+                acc[c] += pq[jj] * H->vdec[(int64_t)(j0 + jj) * d + c];
         for (int c = 0; c < d; c++)
             O[c] = alpha * O[c] + acc[c] * post;
+        /* the slack rides through the same rescales as O */
+        for (int c = 0; c < d; c++)
+            Sl[c] = alpha * Sl[c];
+        for (int jj = 0; jj < n; jj++)
+            if (dq[jj] > 0.0)
+                for (int c = 0; c < d; c++)
+                    Sl[c] += dq[jj] * post * fabs(H->vdec[(int64_t)(j0 + jj) * d + c]);
         m = mn;
-        free(p32);
     }
     if (l == 0.0) {
         /* no visible key (an empty key sequence): zero output, LSE -inf */
-        for (int c = 0; c < d; c++)
+        for (int c = 0; c < d; c++) {
             o[c] = 0.0;
+            if (slack)
+                slack[c] = 0.0;
+        }
         *lse = -INFINITY;
-        free(O);
-        free(acc);
-        free(x);
-        free(p);
-        free(pq);
-        return;
+    } else {
+        for (int c = 0; c < d; c++) {
+            /* FP8 P~: O and l both carry 448; FP8 V adds its channel step */
+            double f = H->pv == PV_FP8 ? (double)H->vs[c] / (448.0 * l)
+                       : H->pv == PV_MXFP8 ? 1.0 / (448.0 * l) : 1.0 / l;
+            o[c] = O[c] * f;
+            if (slack)
+                slack[c] = Sl[c] * fabs(f);
+        }
+        *lse = m + log(l) + (H->corr ? H->corr[i] : 0.0);
     }
-    for (int c = 0; c < d; c++) {
-        if (H->pv == PV_FP8)
-            o[c] = O[c] * (double)H->vs[c] / (448.0 * l);
-        else if (H->pv == PV_MXFP8)
-            o[c] = O[c] / (448.0 * l);
-        else
-            o[c] = O[c] / l;
-    }
-    *lse = m + log(l) + (H->corr ? H->corr[i] : 0.0);
     free(O);
+    free(Sl);
     free(acc);
     free(x);
+    free(xm);
     free(p);
     free(pq);
+    free(dq);
 }
 
-/* rows: the query rows to compute (shared by every head); out [BH,nrows,d], lse [BH,nrows]. */
-static void run_rows(const head_t *heads, int BH, const int *rows, int nrows, double *out, double *lse)
+/* rows: the query rows to compute (shared by every head); out [BH,nrows,d], lse [BH,nrows],
+ * slack [BH,nrows,d] or NULL. */
+static void run_rows(const head_t *heads, int BH, const int *rows, int nrows, double *out, double *lse,
+                     double *slack)
 {
     int d = heads[0].d;
+    head_t *hs = malloc(sizeof(head_t) * (size_t)(BH > 0 ? BH : 1));
+    int nq = 0;
+    for (int r = 0; r < nrows; r++)
+        nq = rows[r] + 1 > nq ? rows[r] + 1 : nq;
+    for (int h = 0; h < BH; h++) {
+        hs[h] = heads[h];
+        hs[h].vdec = malloc(sizeof(double) * ((size_t)hs[h].N * d + 1));
+        hs[h].q4d = hs[h].k4d = NULL;
+        if (hs[h].qk == QK_MXFP4) {
+            hs[h].q4d = malloc(sizeof(double) * ((size_t)nq * d + 1));
+            hs[h].k4d = malloc(sizeof(double) * ((size_t)hs[h].N * d + 1));
+        }
+    }
+#pragma omp parallel for schedule(dynamic)
+    for (int h = 0; h < BH; h++) {
+        for (int j = 0; j < hs[h].N; j++)
+            for (int c = 0; c < d; c++)
+                hs[h].vdec[(int64_t)j * d + c] = vval(&hs[h], j, c);
+        if (hs[h].qk == QK_MXFP4) {
+            for (int64_t e = 0; e < (int64_t)nq * d; e++)
+                hs[h].q4d[e] = or_e2m1_decode(hs[h].q4[e]);
+            for (int64_t e = 0; e < (int64_t)hs[h].N * d; e++)
+                hs[h].k4d[e] = or_e2m1_decode(hs[h].k4[e]);
+        }
+    }
 #pragma omp parallel for schedule(dynamic) collapse(2)
     for (int h = 0; h < BH; h++)
         for (int r = 0; r < nrows; r++)
-            forward_row(&heads[h], rows[r], out + ((int64_t)h * nrows + r) * d, lse + (int64_t)h * nrows + r);
+            forward_row(&hs[h], rows[r], out + ((int64_t)h * nrows + r) * d, lse + (int64_t)h * nrows + r,
+                        slack ? slack + ((int64_t)h * nrows + r) * d : NULL);
+    for (int h = 0; h < BH; h++) {
+        free(hs[h].vdec);
+        free(hs[h].q4d);
+        free(hs[h].k4d);
+    }
+    free(hs);
 }
 
 /* Simulation of the INT8-QK / FP8-PV forward on codes from or_quant_int8_fp8_x
@@ -717,7 +783,7 @@ static void run_rows(const head_t *heads, int BH, const int *rows, int nrows, do
 OR_API void or_attn_int8_fp8_x(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks,
                                const uint8_t *vc, const float *vs, const double *corr,
                                int BH, int Nq, int Nk, int d, int qblk, int kblk, int tile, int causal, double sm,
-                               const int *rows, int nrows, double *out, double *lse)
+                               const int *rows, int nrows, double *out, double *lse, double *slack)
 {
     int nbq = (Nq + qblk - 1) / qblk, nbk = (Nk + kblk - 1) / kblk;
     head_t *H = calloc((size_t)BH, sizeof(head_t));
@@ -728,7 +794,7 @@ OR_API void or_attn_int8_fp8_x(const int8_t *qc, const float *qs, const int8_t *
                         .qc = qc + offq, .kc = kc + offk, .qs = qs + (int64_t)h * nbq, .ks = ks + (int64_t)h * nbk,
                         .vc = vc + offk, .vs = vs + (int64_t)h * d, .corr = corr + (int64_t)h * Nq};
     }
-    run_rows(H, BH, rows, nrows, out, lse);
+    run_rows(H, BH, rows, nrows, out, lse, slack);
     free(H);
 }
 
@@ -736,7 +802,7 @@ OR_API void or_attn_int8_fp8_x(const int8_t *qc, const float *qs, const int8_t *
 OR_API void or_attn_int8_f16_x(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks,
                                const uint16_t *vh, const double *corr,
                                int BH, int Nq, int Nk, int d, int qblk, int kblk, int tile, int causal, double sm,
-                               const int *rows, int nrows, double *out, double *lse)
+                               const int *rows, int nrows, double *out, double *lse, double *slack)
 {
     int nbq = (Nq + qblk - 1) / qblk, nbk = (Nk + kblk - 1) / kblk;
     head_t *H = calloc((size_t)BH, sizeof(head_t));
@@ -747,7 +813,7 @@ OR_API void or_attn_int8_f16_x(const int8_t *qc, const float *qs, const int8_t *
                         .qc = qc + offq, .kc = kc + offk, .qs = qs + (int64_t)h * nbq, .ks = ks + (int64_t)h * nbk,
                         .vh = vh + offk, .corr = corr + (int64_t)h * Nq};
     }
-    run_rows(H, BH, rows, nrows, out, lse);
+    run_rows(H, BH, rows, nrows, out, lse, slack);
     free(H);
 }
 
@@ -756,7 +822,8 @@ OR_API void or_attn_int8_fp8(const int8_t *qc, const float *qs, const int8_t *kc
                              int BH, int N, int d, int blk, int tile, int causal, double sm,
                              const int *rows, int nrows, double *out, double *lse)
 {
-    or_attn_int8_fp8_x(qc, qs, kc, ks, vc, vs, corr, BH, N, N, d, blk, blk, tile, causal, sm, rows, nrows, out, lse);
+    or_attn_int8_fp8_x(qc, qs, kc, ks, vc, vs, corr, BH, N, N, d, blk, blk, tile, causal, sm, rows, nrows, out, lse,
+                       NULL);
 }
 
 /* Simulation of the MXFP4-QK forward; pv_fmt 3 = MXFP4 P~ and V, 2 = FP8 P~ and V,
@@ -765,7 +832,7 @@ OR_API void or_attn_mxfp4_x(const uint8_t *qc, const uint8_t *qe, const uint8_t 
                             const float *dS, const double *corr,
                             const uint8_t *vc, const uint8_t *ve, const float *vs, int pv_fmt, int qsb,
                             int BH, int Nq, int Nk, int d, int tile, int causal, double sm,
-                            const int *rows, int nrows, double *out, double *lse)
+                            const int *rows, int nrows, double *out, double *lse, double *slack)
 {
     int ng = d / 32, nvg = (Nk + 31) / 32;
     int nqb = qsb > 0 ? (Nq + qsb - 1) / qsb : 1;
@@ -784,7 +851,7 @@ OR_API void or_attn_mxfp4_x(const uint8_t *qc, const uint8_t *qe, const uint8_t 
         else
             H[h].vs = vs + (int64_t)h * d;
     }
-    run_rows(H, BH, rows, nrows, out, lse);
+    run_rows(H, BH, rows, nrows, out, lse, slack);
     free(H);
 }
 
@@ -795,7 +862,7 @@ OR_API void or_attn_mxfp4(const uint8_t *qc, const uint8_t *qe, const uint8_t *k
                           const int *rows, int nrows, double *out, double *lse)
 {
     or_attn_mxfp4_x(qc, qe, kc, ke, dS, corr, vc, ve, vs, pv_fmt, 0, BH, N, N, d, tile, causal, sm, rows, nrows,
-                    out, lse);
+                    out, lse, NULL);
 }
 
 /*
@@ -850,7 +917,7 @@ OR_API void or_attn_tiled_exact(const float *q, const float *k, const float *v,
         bufs[h * 5 + 3] = dSx;
         bufs[h * 5 + 4] = corr;
     }
-    run_rows(H, BH, rows, nrows, out, lse);
+    run_rows(H, BH, rows, nrows, out, lse, NULL);
     for (int i = 0; i < BH * 5; i++)
         free(bufs[i]);
     free(bufs);
@@ -887,12 +954,14 @@ static void ref_row(const float *Q, const float *K, const float *V, int N, int d
         x[j] = exp(x[j] - mx);
         l += x[j];
     }
-    for (int c = 0; c < d; c++) {
-        double s = 0.0;
-        for (int j = 0; j < n; j++)
-            s += x[j] * (double)V[(int64_t)j * d + c];
-        o[c] = s / l;
-    }
+    /* o[c] = (sum_j x_j V[j,c]) / l, each channel's sum taken in key order */
+    for (int c = 0; c < d; c++)
+        o[c] = 0.0;
+    for (int j = 0; j < n; j++)
+        for (int c = 0; c < d; c++)
+            o[c] += x[j] * (double)V[(int64_t)j * d + c];
+    for (int c = 0; c < d; c++)
+        o[c] = o[c] / l;
     *lse = mx + log(l);
 }
 

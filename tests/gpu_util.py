@@ -113,3 +113,18 @@ def sample_rows(N, k=24, seed=0):
 
 def device():
     return torch.device("cuda:0")
+
+
+ATOL = 2e-2     # the forward's max-abs tolerance against the oracle's simulation
+
+
+def within(o, o_sim, slack, atol=ATOL):
+    """Element-wise |o - o_sim| <= atol + slack, where slack is the oracle's per-element bound on
+    what a different choice among the admissible P~ codes can change (zero almost everywhere)."""
+    o = np.asarray(o, np.float64)
+    return bool(np.all(np.abs(o - o_sim) <= atol + slack))
+
+
+def excess(o, o_sim, slack, atol=ATOL):
+    """The largest amount by which |o - o_sim| exceeds atol + slack (<= 0 when within)."""
+    return float((np.abs(np.asarray(o, np.float64) - o_sim) - atol - slack).max())

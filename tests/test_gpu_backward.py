@@ -1,6 +1,7 @@
 """GPU 8-bit backward (dQ, dK, dV) against exact fp64 gradients of softmax attention:
 cosine >= 0.99 per gradient, on small ragged cases at d = 64 and 128, on the training
-workload (B=8 H=16 N=2048 d=64, causal) and on a d = 128 causal case, for sampled heads."""
+workload (B=8 H=16 N=2048 d=64, causal; every head, with its forward O and LSE) and on a
+d = 128 causal case (every head)."""
 import math
 
 import numpy as np
@@ -59,40 +60,57 @@ def test_backward_dv_column_sum(sage, d):
     assert np.allclose(got, want, rtol=0.03, atol=0.03 * np.abs(want).max())
 
 
-def test_backward_training_workload_sampled_heads(sage):
+def _per_head_cos(got, ref):
+    return [cos(got[i], ref[i]) for i in range(got.shape[0])]
+
+
+def test_backward_training_workload_all_heads(sage):
+    """The training workload (B=8 H=16 N=2048 d=64, causal) in full: the forward's O and LSE on
+    every row of every head against the oracle's simulation (element-wise with the admissible-
+    code slack, cosine >= 0.9999) and against exact fp64 attention (cosine >= 0.99 per head), and
+    dQ, dK, dV of every head against the exact fp64 gradients at cosine >= 0.99 per head."""
     import oracle
     from bit_quantized_attention_smooth_amd.workloads import workload_inputs, as_u16
-    banner("backward training workload b8h16n2048d64 causal")
+    from gpu_util import excess, within
+    banner("backward training workload b8h16n2048d64 causal, all heads")
     x, w = workload_inputs("train_causal_b8h16n2048d64")
     B, H, N, d, sm = w["B"], w["H"], w["N"], w["d"], w["sm_scale"]
+    BH = B * H
     o, lse, dq, dk, dv = _run(sage, x, True, sm)
-    heads = [0, B * H - 1]
-    sel = lambda t: t.reshape(B * H, N, d)[heads]
-    f = {n: oracle.widen(as_u16(sel(x[n])), "bf16").reshape(len(heads), N, d) for n in ("q", "k", "v", "do")}
+    for t in (o, lse, dq, dk, dv):
+        assert torch.isfinite(t).all()
+    f = {n: oracle.widen(as_u16(x[n]), "bf16").reshape(BH, N, d) for n in ("q", "k", "v", "do")}
+    qz = oracle.quant_int8_fp8(f["q"], f["k"], f["v"], sm)
+    o_sim, lse_sim, sl = oracle.attn_int8_fp8(qz, N, d, True, sm, 64, slack=True)
+    o_ref, lse_ref = oracle.attn_ref(f["q"], f["k"], f["v"], True, sm)
+    og = to_np64(o).reshape(BH, N, d)
+    assert within(og, o_sim, sl), excess(og, o_sim, sl)
+    assert cos(og, o_sim) >= 0.9999
+    assert np.allclose(lse.cpu().numpy().reshape(BH, N), lse_sim, rtol=1e-4, atol=2e-3)
+    assert min(_per_head_cos(og, o_ref)) >= 0.99
     rq, rk, rv = oracle.attn_bwd_ref(f["q"], f["k"], f["v"], f["do"], True, sm)
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-        g = to_np64(sel(got))
-        assert cos(g, ref) >= 0.99, (name, cos(g, ref))
-    for t in (dq, dk, dv):
-        assert torch.isfinite(t).all()
+        ph = _per_head_cos(to_np64(got).reshape(BH, N, d), ref)
+        print(f"  {name}: per-head cosine min {min(ph):.5f} (head {int(np.argmin(ph))}), mean {np.mean(ph):.5f}",
+              flush=True)
+        assert min(ph) >= 0.99, (name, min(ph), int(np.argmin(ph)))
 
 
-def test_backward_d128_causal_sampled_heads(sage):
-    """Head dimension 128 at a prefill-like size (B=2 H=8 N=2048, causal), two heads checked."""
+def test_backward_d128_causal_all_heads(sage):
+    """Head dimension 128 at a prefill-like size (B=2 H=8 N=2048, causal): every head's
+    gradients at cosine >= 0.99 of the exact fp64 gradients."""
     import oracle
     from bit_quantized_attention_smooth_amd.workloads import make_inputs, as_u16
-    banner("backward b2h8n2048d128 causal")
+    banner("backward b2h8n2048d128 causal, all heads")
     B, H, N, d = 2, 8, 2048, 128
     sm = 1 / math.sqrt(d)
     x = make_inputs(B, H, N, d, dtype="bf16", seed=79, k_off_std=2.0, with_do=True)
     o, lse, dq, dk, dv = _run(sage, x, True, sm)
-    heads = [0, B * H - 1]
-    sel = lambda t: t.reshape(B * H, N, d)[heads]
-    f = {n: oracle.widen(as_u16(sel(x[n])), "bf16").reshape(len(heads), N, d) for n in ("q", "k", "v", "do")}
+    f = {n: oracle.widen(as_u16(x[n]), "bf16").reshape(B * H, N, d) for n in ("q", "k", "v", "do")}
     rq, rk, rv = oracle.attn_bwd_ref(f["q"], f["k"], f["v"], f["do"], True, sm)
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-        g = to_np64(sel(got))
-        assert cos(g, ref) >= 0.99, (name, cos(g, ref))
+        ph = _per_head_cos(to_np64(got).reshape(B * H, N, d), ref)
+        assert min(ph) >= 0.99, (name, min(ph), int(np.argmin(ph)))
     for t in (dq, dk, dv):
         assert torch.isfinite(t).all()
 

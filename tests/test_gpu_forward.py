@@ -1,6 +1,7 @@
 """GPU parity of the smoothing/quantization prologue and the fused forward
-against the CPU oracle: codes and scales bit-exact; O within max-abs 2e-2 and
-cosine >= 0.9999 of the oracle's simulation of the same quantization; cosine
+against the CPU oracle: codes and scales bit-exact; O within 2e-2 element-wise
+(plus the oracle's slack where a P~ weight has two admissible codes) and cosine
+>= 0.9999 of the oracle's simulation of the same quantization; cosine
 against exact fp64 attention >= 0.99 (INT8 QK), 0.98 (MXFP4 QK with FP8 P~ and
 FP8 or MXFP8 V) or 0.965 (MXFP4 QK and P~V: the oracle's own simulation reaches
 about 0.972 on these inputs)."""
@@ -10,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import banner, cos, device, sample_rows, to_np64, unpack_int8_fp8, unpack_mxfp4
+from gpu_util import banner, cos, device, excess, sample_rows, to_np64, unpack_int8_fp8, unpack_mxfp4, within
 
 pytestmark = pytest.mark.gpu
 
@@ -89,10 +90,11 @@ def _unpack(buf, p, lay, qk, pv):
 
 
 def _oracle_sim(f, qz_or, qk, pv, N, d, causal, sm, rows=None):
+    """The oracle's simulation: (O, LSE, slack), slack bounding the effect of admissible P~ codes."""
     import oracle
     if qk.startswith("int8"):
-        return oracle.attn_int8_fp8(qz_or, N, d, causal, sm, TILE, rows=rows)
-    return oracle.attn_mxfp4(qz_or, N, d, causal, sm, TILE, rows=rows)
+        return oracle.attn_int8_fp8(qz_or, N, d, causal, sm, TILE, rows=rows, slack=True)
+    return oracle.attn_mxfp4(qz_or, N, d, causal, sm, TILE, rows=rows, slack=True)
 
 
 def _check_codes(r, qz, qk, pv):
@@ -149,9 +151,9 @@ def test_forward_matches_oracle(sage, case):
     o = to_np64(o).reshape(B * H, N, d)
     lse = lse.cpu().numpy().reshape(B * H, N).astype(np.float64)
     qz = _oracle_quant(f, qk, pv, sm)
-    o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
+    o_sim, lse_sim, sl = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
     o_ref, lse_ref = oracle.attn_ref(f["q"], f["k"], f["v"], causal, sm)
-    assert np.abs(o - o_sim).max() <= 2e-2
+    assert within(o, o_sim, sl), excess(o, o_sim, sl)
     assert cos(o, o_sim) >= 0.9999
     assert cos(o, o_ref) >= _ref_band(qk, pv)
     assert np.allclose(lse, lse_sim, rtol=1e-4, atol=2e-3)
@@ -186,8 +188,8 @@ def test_forward_random_sweep(sage, i):
     qz = _oracle_quant(f, c["qk"], c["pv"], c["sm"])
     _check_codes(_unpack(buf, p, lay, c["qk"], c["pv"]), qz, c["qk"], c["pv"])
     o = to_np64(o).reshape(B * H, N, d)
-    o_sim, lse_sim = _oracle_sim(f, qz, c["qk"], c["pv"], N, d, c["causal"], c["sm"])
-    assert np.abs(o - o_sim).max() <= 2e-2
+    o_sim, lse_sim, sl = _oracle_sim(f, qz, c["qk"], c["pv"], N, d, c["causal"], c["sm"])
+    assert within(o, o_sim, sl), excess(o, o_sim, sl)
     assert cos(o, o_sim) >= 0.9999
     assert np.allclose(lse.cpu().numpy().reshape(B * H, N), lse_sim, rtol=1e-4, atol=2e-3)
 
@@ -207,13 +209,13 @@ def test_forward_edge_lengths(sage, N, causal):
         torch.cuda.synchronize()
         o = to_np64(o).reshape(2, N, d)
         qz = _oracle_quant(f, qk, pv, sm)
-        o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
-        assert np.abs(o - o_sim).max() <= 2e-2, (qk, d, pv)
+        o_sim, lse_sim, sl = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
+        assert within(o, o_sim, sl), (qk, d, pv, excess(o, o_sim, sl))
         if N > 1:
             assert cos(o, o_sim) >= 0.9999, (qk, d, pv)
         else:
             # one key: O is the dequantized V row
-            assert np.allclose(o, o_sim, atol=2e-2)
+            assert within(o, o_sim, sl)
         assert np.allclose(lse.cpu().numpy().reshape(2, N), lse_sim, rtol=1e-4, atol=2e-3)
 
 
@@ -240,11 +242,41 @@ def test_forward_zero_inputs(sage, qk, pv, causal):
         assert torch.isfinite(o).all() and torch.isfinite(lse).all(), zero
         o = to_np64(o).reshape(B * H, N, d)
         qz = _oracle_quant(f, qk, pv, sm)
-        o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
-        assert np.abs(o - o_sim).max() <= 2e-2, zero
+        o_sim, lse_sim, sl = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
+        assert within(o, o_sim, sl), (zero, excess(o, o_sim, sl))
         assert np.allclose(lse.cpu().numpy().reshape(B * H, N), lse_sim, rtol=1e-4, atol=2e-3), zero
         if zero == "v":
             assert not o.any()
+
+
+@pytest.mark.parametrize("qk,pv", SWEEP_PAIRS, ids=[f"{a}_{b}" for a, b in SWEEP_PAIRS])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_tiny_magnitude_inputs(sage, qk, pv, causal):
+    """Q and K with block maxima near 1e-21 (bf16 holds them; their codes are ordinary).  The
+    scores are below 1e-40, so exact attention is uniform: O is the (prefix) mean of V.  The
+    product of the two steps underflows binary32, which must not turn the integer code dot
+    products into log2-domain scores (that gives one-hot weights): every format pair must stay
+    within the forward tolerances of the oracle and at cosine >= 0.99 of exact attention."""
+    import oracle
+    banner(f"tiny-magnitude inputs {qk}/{pv} causal={causal}")
+    B, H, N, d = 1, 2, 300, 128
+    sm = 1 / math.sqrt(d)
+    f, g = _inputs(B, H, N, d, "bf16", 51, 2.0)
+    for n in "qk":
+        g[n] = (g[n].float() * 1e-21).to(torch.bfloat16)
+        f[n] = g[n].float().cpu().numpy().reshape(B * H, N, d)
+    assert 1e-22 < float(np.abs(f["q"]).max()) < 1e-20 and 1e-22 < float(np.abs(f["k"]).max()) < 1e-20
+    o, lse = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv,
+                           return_lse=True)
+    torch.cuda.synchronize()
+    o = to_np64(o).reshape(B * H, N, d)
+    qz = _oracle_quant(f, qk, pv, sm)
+    o_sim, lse_sim, sl = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
+    o_ref, lse_ref = oracle.attn_ref(f["q"], f["k"], f["v"], causal, sm)
+    assert within(o, o_sim, sl), excess(o, o_sim, sl)
+    assert cos(o, o_sim) >= 0.9999
+    assert cos(o, o_ref) >= 0.99, cos(o, o_ref)
+    assert np.allclose(lse.cpu().numpy().reshape(B * H, N), lse_ref, rtol=1e-4, atol=2e-3)
 
 
 # (tensor, head, row, channel, value): a NaN in Q, a NaN in K (it reaches the K mean, so the
@@ -273,13 +305,13 @@ def test_forward_nonfinite_inputs(sage, qk, pv, causal):
         lse = lse.cpu().numpy().reshape(B * H, N).astype(np.float64)
         with np.errstate(invalid="ignore", over="ignore"):
             qz = _oracle_quant(f, qk, pv, sm)
-            o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
+            o_sim, lse_sim, sl = _oracle_sim(f, qz, qk, pv, N, d, causal, sm)
         bad, bad_sim = ~np.isfinite(o), ~np.isfinite(o_sim)
         assert np.array_equal(bad, bad_sim), (t, int(bad.sum()), int(bad_sim.sum()))
         assert np.array_equal(~np.isfinite(lse), ~np.isfinite(np.asarray(lse_sim, np.float64))), t
         assert bad[h, row].any() if t != "v" else bad[h, row:, ch].all(), t
         ok = ~bad
-        assert np.abs(o[ok] - o_sim[ok]).max() <= 2e-2, t
+        assert within(o[ok], o_sim[ok], sl[ok]), t
         okl = np.isfinite(lse)
         assert np.allclose(lse[okl], np.asarray(lse_sim)[okl], rtol=1e-4, atol=2e-3), t
 
@@ -371,38 +403,63 @@ def test_forward_block_q_smoothing_under_drift(sage, pv):
         o = sage.sageattn(*(x[n].to(device()) for n in "qkv"), sm_scale=sm, qk_fmt=qk, pv_fmt=pv)
         torch.cuda.synchronize()
         o = to_np64(o).reshape(B * H, N, d)
-        o_sim, _ = _oracle_sim(f, _oracle_quant(f, qk, pv, sm), qk, pv, N, d, False, sm)
-        assert np.abs(o - o_sim).max() <= 2e-2 and cos(o, o_sim) >= 0.9999, qk
+        o_sim, _, sl = _oracle_sim(f, _oracle_quant(f, qk, pv, sm), qk, pv, N, d, False, sm)
+        assert within(o, o_sim, sl) and cos(o, o_sim) >= 0.9999, qk
         cs[qk] = cos(o, o_ref)
     assert cs["mxfp4_qblock"] > cs["mxfp4"]
 
 
-FULL = [("int8_fp8_causal_b1h32n4096d128", "fp8"), ("int8_fp8_b2h24n16384d64", "fp8"),
-        ("int8_fp8_b1h32n8192d128", "f16"), ("int8_fp8_causal_b1h32n4096d128", "fp8", "int8_token"),
-        ("mxfp4_b4h32n8192d128", "fp8", "mxfp4_qblock"),
-        ("mxfp4_b4h32n8192d128", "fp8"), ("mxfp4_b4h32n8192d128", "mxfp4"), ("mxfp4_b4h32n8192d128", "mxfp8"),
-        ("int8_fp8_b1h2n256d64", "fp8"), ("int8_fp8_b1h32n8192d128", "fp8"), ("int8_fp8_causal_b1h32n16384d128", "fp8")]
+# (workload, P~V format, QK format or None for the workload's own, heads compared): "all" compares
+# every row of every head; an integer n compares every row of n heads spread over the batch; "rows"
+# compares sampled rows of three heads.
+FULL = [("int8_fp8_b1h2n256d64", "fp8", None, "all"),
+        ("int8_fp8_causal_b1h32n4096d128", "fp8", None, "all"),
+        ("train_causal_b8h16n2048d64", "fp8", None, "all"),
+        ("int8_fp8_b2h24n16384d64", "fp8", None, 4),
+        ("mxfp4_b4h32n8192d128", "fp8", None, 4),
+        ("mxfp4_b4h32n8192d128", "mxfp4", None, 4),
+        ("mxfp4_b4h32n8192d128", "mxfp8", None, "rows"),
+        ("mxfp4_b4h32n8192d128", "fp8", "mxfp4_qblock", "rows"),
+        ("int8_fp8_causal_b1h32n4096d128", "fp8", "int8_token", "all"),
+        ("int8_fp8_b1h32n8192d128", "f16", None, "rows"),
+        ("int8_fp8_b1h32n8192d128", "fp8", None, 4),
+        ("int8_fp8_causal_b1h32n16384d128", "fp8", None, "rows")]
 
 
-@pytest.mark.parametrize("spec", FULL, ids=["-".join(c[::-1]) for c in FULL])
-def test_full_size_sampled_rows(sage, spec):
-    """The named workloads at full size in the benchmark's launch configuration; the
-    oracle recomputes sampled rows of a few heads."""
+def _full_id(c):
+    return "-".join(str(t) for t in (c[0], c[2] or "", c[1], c[3]) if t != "")
+
+
+@pytest.mark.parametrize("spec", FULL, ids=[_full_id(c) for c in FULL])
+def test_full_size_parity(sage, spec):
+    """The named workloads at full size in the benchmark's launch configuration.  The oracle
+    recomputes every row of every head (the small and training workloads and the causal
+    prefill), every row of four heads spread over the batch (the long workloads), or sampled
+    rows of three heads (the remaining format variants); codes, O and LSE are compared on all
+    of them, O per element with the admissible-code slack and by cosine, and the cosine against
+    exact attention per head."""
     import oracle
     from bit_quantized_attention_smooth_amd.workloads import workload_inputs, as_u16
-    name, pv = spec[:2]
+    name, pv, qk_over, which = spec
     banner(f"full size {spec}")
     x, w = workload_inputs(name)
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
-    qk, sm, causal = (spec[2] if len(spec) > 2 else w["qk_fmt"]), w["sm_scale"], w["causal"]
+    qk, sm, causal = (qk_over or w["qk_fmt"]), w["sm_scale"], w["causal"]
     g = {n: x[n].to(device()) for n in "qkv"}
     buf, p, lay = sage.quantize(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv)
     o, lse = sage.attn_fwd_quantized(buf, p, dtype=g["q"].dtype, return_lse=True)
     torch.cuda.synchronize()
-    heads = sorted({0, B * H // 2, B * H - 1})
-    sel = lambda t: t.reshape(B * H, N, d)[heads]
+    assert torch.isfinite(o).all()                # every output finite at full size
+    BH = B * H
+    if which == "all":
+        heads = list(range(BH))
+    elif which == "rows":
+        heads = sorted({0, BH // 2, BH - 1})
+    else:
+        heads = sorted({round(i * (BH - 1) / (which - 1)) for i in range(which)})
+    rows = sample_rows(N) if which == "rows" else None
+    sel = lambda t: t.reshape(BH, N, d)[heads]
     f = {n: oracle.widen(as_u16(sel(x[n])), w["dtype"]).reshape(len(heads), N, d) for n in "qkv"}
-    rows = sample_rows(N)
     qz = _oracle_quant(f, qk, pv, sm)
     r = _unpack(buf, p, lay, qk, pv)
     if qk.startswith("int8"):
@@ -411,16 +468,18 @@ def test_full_size_sampled_rows(sage, spec):
     else:
         for key in ("qc", "kc", "qe", "ke", "vc", "vs" if pv == "fp8" else "ve", "mu_k", "mu_q"):
             assert np.array_equal(r[key][heads], qz[key]), key
-    o_sim, lse_sim = _oracle_sim(f, qz, qk, pv, N, d, causal, sm, rows=rows)
+    o_sim, lse_sim, sl = _oracle_sim(f, qz, qk, pv, N, d, causal, sm, rows=rows)
     o_ref, _ = oracle.attn_ref(f["q"], f["k"], f["v"], causal, sm, rows=rows)
-    og = to_np64(o).reshape(B * H, N, d)[heads][:, rows]
-    lg = lse.cpu().numpy().reshape(B * H, N)[heads][:, rows]
-    assert np.abs(og - o_sim).max() <= 2e-2
+    og = to_np64(o).reshape(BH, N, d)[heads]
+    lg = lse.cpu().numpy().reshape(BH, N)[heads]
+    if rows is not None:
+        og, lg = og[:, rows], lg[:, rows]
+    assert within(og, o_sim, sl), excess(og, o_sim, sl)
     assert cos(og, o_sim) >= 0.9999
-    assert cos(og, o_ref) >= _ref_band(qk, pv)
     assert np.allclose(lg, lse_sim, rtol=1e-4, atol=2e-3)
-    # every output finite at full size
-    assert torch.isfinite(o).all()
+    band = _ref_band(qk, pv)
+    per_head = [cos(og[i], o_ref[i]) for i in range(len(heads))]
+    assert min(per_head) >= band, (min(per_head), int(np.argmin(per_head)))
 
 
 @pytest.mark.parametrize("qk", ["int8", "mxfp4"])
@@ -447,11 +506,11 @@ def test_forward_beyond_2e31_elements(sage, qk):
     del q, k, v
     rows = sample_rows(N, k=12, seed=3)
     qz = _oracle_quant(f, qk, "fp8", sm)
-    o_sim, lse_sim = _oracle_sim(f, qz, qk, "fp8", N, d, True, sm, rows=rows)
+    o_sim, lse_sim, sl = _oracle_sim(f, qz, qk, "fp8", N, d, True, sm, rows=rows)
     ri = torch.as_tensor(rows, dtype=torch.long, device=dev)
     og = to_np64(o[0, heads][:, ri])
     lg = lse[0, heads][:, ri].cpu().numpy()
-    assert np.abs(og - o_sim).max() <= 2e-2
+    assert within(og, o_sim, sl), excess(og, o_sim, sl)
     assert cos(og, o_sim) >= 0.9999
     assert np.allclose(lg, lse_sim, rtol=1e-4, atol=2e-3)
 

@@ -228,10 +228,12 @@ def test_int8_fp8_sim_is_exact_on_lossless_grid(orc, causal, tile, pv_fmt):
     v = _lossless_v(rng, BH, N, d, pv_fmt)
     sm = LN2                                               # p takes the values 2^0, 2^-1, 2^-2
     qz = orc.quant_int8_fp8(q, k, v, sm, pv_fmt=pv_fmt)
-    o, lse = orc.attn_int8_fp8(qz, N, d, causal, sm, tile)
+    o, lse, sl = orc.attn_int8_fp8(qz, N, d, causal, sm, tile, slack=True)
     o_ref, lse_ref = orc.attn_ref(q, k, v, causal, sm)
     assert np.allclose(lse, lse_ref, rtol=0, atol=1e-12)
     assert np.allclose(o, o_ref, rtol=1e-12, atol=1e-12 * np.abs(v).max())
+    # every weight is a grid value (448 p or p exact), far from any rounding midpoint
+    assert not sl.any()
 
 
 def test_int8_scores_exact_on_random_lossless_codes(orc):
@@ -292,10 +294,11 @@ def test_mxfp4_sim_is_exact_on_lossless_grid(orc, causal, pv_fmt):
     assert np.array_equal(qz["mu_q"][:, 2], np.full(BH, 1.5, np.float32))
     assert np.array_equal(qz["dS"], np.float32(1.5) * (k[:, :, 2] - np.float32(0.5)))
     for tile in (64, 128):
-        o, lse = orc.attn_mxfp4(qz, N, d, causal, sm, tile)
+        o, lse, sl = orc.attn_mxfp4(qz, N, d, causal, sm, tile, slack=True)
         o_ref, lse_ref = orc.attn_ref(q, k, v, causal, sm)
         assert np.allclose(lse, lse_ref, rtol=0, atol=1e-12)
         assert np.allclose(o, o_ref, rtol=1e-12, atol=1e-12 * np.abs(v).max())
+        assert not sl.any()
 
 
 def test_mxfp4_scores_exact_on_random_lossless_codes(orc):
@@ -385,44 +388,130 @@ def test_fp8_p_worked_example(orc, path):
         assert not o[0, :, 2:].any()
 
 
-@pytest.mark.parametrize("path", ["int8_fp8", "int8_f16", "mxfp4_fp8", "mxfp4_mxfp8"])
-def test_fp32_p_decisions_agree_with_fp64_scores(orc, path):
-    """On these paths the P~ codes are decided in the fused kernel's fp32 arithmetic.  Taken
-    instead from the fp64 scores, a code can only move where an fp32 rounding of the exp2
-    argument crosses an E4M3 (fp16) rounding midpoint, and then by one step of one weight: with
-    E4M3's 2^-4 relative step almost every row is identical; fp16's 2^-11 step is crossed more
-    often, by a much smaller amount.  A slip in the fp32 path's formula (a dropped dS, a missing
-    log2 e, the wrong step) would move every row by far more."""
-    rng = np.random.default_rng(61)
-    BH, N, d = 2, 200, 64
-    q = rng.standard_normal((BH, N, d)).astype(np.float32)
-    k = (rng.standard_normal((BH, N, d)) + 2.0 * rng.standard_normal((BH, 1, d))).astype(np.float32)
-    v = rng.standard_normal((BH, N, d)).astype(np.float32)
-    q += 1.5 * rng.standard_normal((BH, 1, d)).astype(np.float32)
-    sm = 1.0 / math.sqrt(d)
+def _two_key_row(orc, path, ratio):
+    """One query against two keys whose smoothed scores are +-1.25 (q = e0, k = +-1.25 e0), with
+    sm chosen so that the second weight is p = ratio exactly in real arithmetic, and V rows
+    e0, e1.  Returns the simulated output, its slack and l = 1 + ratio."""
+    BH, N, d = 1, 2, 64
+    q = np.zeros((BH, N, d), np.float32)
+    q[:, :, 0] = 1.0
+    k = np.zeros((BH, N, d), np.float32)
+    k[0, 0, 0], k[0, 1, 0] = 1.25, -1.25
+    v = np.zeros((BH, N, d), np.float32)
+    v[0, 0, 0], v[0, 1, 1] = 1.0, 1.0
+    sm = -math.log(ratio) / 2.5
     qk, pv = path.split("_")
-    outs = []
-    for on in (1, 0):
-        orc.set_p_decision_fp32(on)
-        try:
-            for causal in (False, True):
-                if qk == "int8":
-                    qz = orc.quant_int8_fp8(q, k, v, sm, pv_fmt=pv)
-                    outs.append(orc.attn_int8_fp8(qz, N, d, causal, sm, 64))
-                else:
-                    qz = orc.quant_mxfp4(q, k, v, sm, pv_fmt=pv)
-                    outs.append(orc.attn_mxfp4(qz, N, d, causal, sm, 64))
-        finally:
-            orc.set_p_decision_fp32(1)
-    for (o32, l32), (o64, l64) in zip(outs[:2], outs[2:]):
-        assert np.array_equal(l32, l64)                    # the row sums and LSE stay fp64
-        same = np.all(o32 == o64, axis=-1)
-        if pv == "f16":
-            assert same.mean() >= 0.5
-            assert np.abs(o32 - o64).max() <= 2.0 ** -10 * np.abs(v).max()
-        else:
-            assert same.mean() >= 0.98
-            assert np.abs(o32 - o64).max() <= 0.05 * np.abs(v).max()
+    if qk == "int8":
+        qz = orc.quant_int8_fp8(q, k, v, sm, pv_fmt=pv)
+        o, _, sl = orc.attn_int8_fp8(qz, N, d, False, sm, 64, slack=True)
+    else:
+        qz = orc.quant_mxfp4(q, k, v, sm, pv_fmt=pv)
+        o, _, sl = orc.attn_mxfp4(qz, N, d, False, sm, 64, slack=True)
+    return o[0], sl[0], 1.0 + ratio
+
+
+@pytest.mark.parametrize("path", ["int8_fp8", "mxfp4_fp8", "mxfp4_mxfp8", "int8_f16", "mxfp4_mxfp4"])
+def test_p_code_on_a_rounding_midpoint_has_two_admissible_codes(orc, path):
+    """A weight exactly on a rounding midpoint of its P~ format: either neighbouring code is a
+    correct result, and the slack must be the distance between the two outputs they give.
+      FP8 (x448): 448 p = 76, midway between the E4M3 values 72 and 80;
+      fp16: p = 0.75 + 2^-12, midway between 0.75 and 0.75 + 2^-11;
+      MXFP4 (sigma = 6 / max p = 6, group scale 2^0): sigma p = 5, midway between E2M1 4 and 6.
+    The max weight (p = 1) is exact and has no slack."""
+    pv = path.split("_")[1]
+    if pv in ("fp8", "mxfp8"):
+        ratio, lo, hi, unit = 76.0 / 448.0, 72.0 / 448.0, 80.0 / 448.0, 1.0
+    elif pv == "f16":
+        ratio, lo, hi, unit = 0.75 + 2.0 ** -12, 0.75, 0.75 + 2.0 ** -11, 1.0
+    else:
+        ratio, lo, hi, unit = 5.0 / 6.0, 4.0 / 6.0, 1.0, 1.0
+    o, sl, l = _two_key_row(orc, path, ratio)
+    want_lo, want_hi = lo * unit / l, hi * unit / l
+    for r in range(2):
+        # the oracle picked one of the two codes, and the slack spans both
+        assert min(abs(o[r, 1] - want_lo), abs(o[r, 1] - want_hi)) <= 1e-7, (o[r, 1], want_lo, want_hi)
+        assert abs(sl[r, 1] - (want_hi - want_lo)) <= 1e-7 * want_hi, (sl[r, 1], want_hi - want_lo)
+        assert sl[r, 0] == 0.0 and not sl[r, 2:].any()
+
+
+@pytest.mark.parametrize("path", ["int8_fp8", "mxfp4_fp8", "int8_f16", "mxfp4_mxfp4"])
+def test_p_code_off_midpoint_has_no_slack(orc, path):
+    """The worked example's weight 448 p = 79.196 (FP8), p = 0.7 (fp16) or sigma p = 4.6 (MXFP4) is
+    far from every rounding midpoint relative to the window: one admissible code, zero slack."""
+    ratio = {"fp8": 2.0 ** -2.5, "f16": 0.7, "mxfp4": 4.6 / 6.0}[path.split("_")[1]]
+    _, sl, _ = _two_key_row(orc, path, ratio)
+    assert not sl.any()
+
+
+def _fp32_decided_int8_fp8(orc, qz, N, d, sm, tile, causal):
+    """The INT8 / FP8 forward with every P~ code decided in binary32 the way a fused kernel forms
+    it: c = fl32(fl32(step_q * fl32(sm log2 e)) * step_k), a running max of fl32(a c) over the
+    integer dot products a, p448 = fl32(2^fl32(a c + fl32(log2 448 - m))).  Everything else
+    (row sums, rescales, output) stays fp64 as in the oracle, so the outputs may differ from the
+    oracle's only through P~ codes."""
+    f32 = np.float32
+    BH = qz["qc"].shape[0]
+    sml2e = f32(sm) * f32(1.4426950408889634)
+    L = f32(math.log2(448.0))
+    out = np.zeros((BH, N, d))
+    for h in range(BH):
+        a = qz["qc"][h].astype(np.int64) @ qz["kc"][h].astype(np.int64).T           # [N, N] exact
+        qs = qz["qs"][h][np.arange(N) // 64].astype(f32)
+        ks = qz["ks"][h][np.arange(N) // 64].astype(f32)
+        c = (qs * sml2e)[:, None] * ks[None, :]                                       # fl32 each step
+        x = sm * qz["qs"][h][np.arange(N) // 64][:, None].astype(np.float64) * \
+            qz["ks"][h][np.arange(N) // 64][None, :].astype(np.float64) * a            # fp64 scores
+        vdq = orc.e4m3_decode(qz["vc"][h])                                            # [N, d]
+        O = np.zeros((N, d))
+        m = np.full(N, -np.inf)
+        m32 = np.full(N, -np.inf, f32)
+        l = np.zeros(N)
+        for j0 in range(0, N, tile):
+            j1 = min(N, j0 + tile)
+            vis = np.ones((N, j1 - j0), bool)
+            if causal:
+                vis = np.arange(j0, j1)[None, :] <= np.arange(N)[:, None]
+            t32 = (a[:, j0:j1].astype(f32) * c[:, j0:j1]).astype(f32)
+            mt32 = np.where(vis, t32, -np.inf).max(axis=1).astype(f32)
+            xt = np.where(vis, x[:, j0:j1], -np.inf)
+            mn = np.maximum(m, xt.max(axis=1))
+            act = mn > -np.inf
+            m32 = np.maximum(m32, mt32)
+            off = (L - np.where(act, m32, f32(0))).astype(f32)
+            arg = (a[:, j0:j1].astype(np.float64) * c[:, j0:j1].astype(np.float64) + off[:, None]).astype(f32)
+            p448 = np.exp2(arg.astype(np.float64)).astype(f32)
+            pq = np.where(vis, orc.e4m3_decode(orc.e4m3_encode(p448)), 0.0)
+            alpha = np.where(m > -np.inf, np.exp(m - np.where(act, mn, 0.0)), 0.0)
+            p = np.where(vis, np.exp(xt - np.where(act, mn, 0.0)[:, None]), 0.0)
+            l = np.where(act, alpha * l + p.sum(axis=1), l)
+            O = np.where(act[:, None], alpha[:, None] * O + pq @ vdq[j0:j1], O)
+            m = np.where(act, mn, m)
+        out[h] = O * qz["vs"][h][None, :].astype(np.float64) / (448.0 * l[:, None])
+    return out
+
+
+def test_slack_covers_binary32_p_decisions(orc):
+    """The window the slack is built on must cover a binary32 evaluation of the exp argument.
+    Deciding every P~ code as a binary32 fused kernel would (the function above) may only move
+    an output within the oracle's slack of it.  Scores of magnitude up to about 40 (scale 4)
+    widen the window with them; on these seeded inputs the binary32 decisions flip at least one
+    code against the fp64 ones, and that output moves by exactly its slack."""
+    flips = 0
+    for scale, causal in ((1.0, False), (4.0, False), (4.0, True)):
+        rng = np.random.default_rng(62)
+        BH, N, d = 4, 512, 64
+        q = (scale * rng.standard_normal((BH, N, d))).astype(np.float32)
+        k = (scale * (rng.standard_normal((BH, N, d)) + 2.0 * rng.standard_normal((BH, 1, d)))).astype(np.float32)
+        v = rng.standard_normal((BH, N, d)).astype(np.float32)
+        sm = 1.0 / math.sqrt(d)
+        qz = orc.quant_int8_fp8(q, k, v, sm)
+        o, _, sl = orc.attn_int8_fp8(qz, N, d, causal, sm, 64, slack=True)
+        o32 = _fp32_decided_int8_fp8(orc, qz, N, d, sm, 64, causal)
+        diff = np.abs(o32 - o)
+        assert np.all(diff <= sl + 1e-12 * np.abs(o).max()), (scale, causal, float((diff - sl).max()))
+        assert (sl > 0).any()                    # the window is exercised
+        flips += int((diff > 1e-9).sum())
+    assert flips > 0
 
 
 def test_int8_fp8_key_shift_gives_identical_codes_and_output(orc):
