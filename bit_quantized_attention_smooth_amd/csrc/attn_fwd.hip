@@ -360,9 +360,12 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
   if (QK == QK_INT8) {
     // FINE: this lane's half holds the tile's 32-key group hh, with its own step
     c = FINE ? qstep * (hh ? kstep[2 * j + 1] : kstep[2 * j]) : qstep * kstep[j];
-    // a zero block step means every code of that block is 0, so every unmasked score is 0
-    // for any c; keep c positive so that masked entries (-inf) stay -inf after scaling
-    c = c == 0.0f ? 1.0f : c;
+    // c must stay positive so that masked entries (-inf) stay -inf after scaling.  A zero
+    // step (an all-zero block: every code 0) or a product of tiny steps that underflows
+    // binary32 is raised to the smallest normal float: a score times it is below 2^-100, as
+    // negligible as the true one, so tiny inputs keep near-uniform weights.  A NaN step
+    // fails the comparison and stays NaN.
+    c = c < __FLT_MIN__ ? __FLT_MIN__ : c;
     int im;
     if (need_mask) {
       asm volatile("" ::: "memory");   // a real branch: the rare masked tiles must not cost every tile
