@@ -29,11 +29,18 @@ namespace sage {
 
 constexpr int kChunks = kStatChunks;
 
-// Correctly rounded x / d given r = RN(1 / d) (d > 0, quotient in the normal range).  The
-// correction step turns x = -0 into +0, so the sign is taken from x (d > 0: a no-op for x != 0).
+// Correctly rounded x / d (d > 0) by one correction step of the reciprocal (Markstein).  A step
+// below 2^-64 (a block of subnormal or tiny inputs) has a reciprocal beyond binary32, so x and d
+// are first scaled by the same power of two s = div_scale(d), exactly; r = recip_rn(d) is the
+// reciprocal of the scaled step.  The correction turns x = -0 into +0, so the sign is taken
+// from x (d > 0: a no-op for x != 0).
+__device__ __forceinline__ float div_scale(float d) { return d < 0x1p-64f ? 0x1p64f : 1.0f; }
+__device__ __forceinline__ float recip_rn(float d) { return 1.0f / (d * div_scale(d)); }
 __device__ __forceinline__ float div_rn(float x, float d, float r) {
-  const float q0 = x * r;
-  return copysignf(fmaf(r, fmaf(-d, q0, x), q0), x);
+  const float s = div_scale(d);
+  const float xs = x * s, ds = d * s;
+  const float q0 = xs * r;
+  return copysignf(fmaf(r, fmaf(-ds, q0, xs), q0), x);
 }
 
 // 16 bytes = 8 contiguous 16-bit inputs, widened.
@@ -170,7 +177,7 @@ __device__ __forceinline__ void block_umax2(uint32_t& x, uint32_t& y, uint32_t* 
   y = max(max(red[4], red[5]), max(red[6], red[7]));
 }
 
-// clamp(rne(x / step), -127, 127), x / step correctly rounded via r = 1 / step.
+// clamp(rne(x / step), -127, 127), x / step correctly rounded via r = recip_rn(step).
 __device__ __forceinline__ int8_t int8_code(float x, float step, float r) {
   if (step == 0.0f) return 0;
   float n = rintf(div_rn(x, step, r));
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     dv[i] = s_dv[c0 + i];
-    rv[i] = 1.0f / dv[i];
+    rv[i] = recip_rn(dv[i]);
   }
   float xq[NP][8], xk[NP][8];
   uint32_t aq = 0, ak = 0;
@@ -285,23 +292,23 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
 #pragma unroll
       for (int o = 1; o < C8; o <<= 1) a = max(a, (uint32_t)__shfl_xor((int)a, o));
       dq_r[p] = __uint_as_float(a) / 127.0f;
-      rq_r[p] = 1.0f / dq_r[p];
+      rq_r[p] = recip_rn(dq_r[p]);
     }
     block_umax2(akg[0], akg[1], s_red);
 #pragma unroll
     for (int g = 0; g < 2; g++) {
       dk_g[g] = __uint_as_float(akg[g]) / 127.0f;
-      rk_g[g] = 1.0f / dk_g[g];
+      rk_g[g] = recip_rn(dk_g[g]);
     }
   } else {
     block_umax2(aq, ak, s_red);
 #pragma unroll
     for (int p = 0; p < NP; p++) {
       dq_r[p] = __uint_as_float(aq) / 127.0f;
-      rq_r[p] = 1.0f / dq_r[p];
+      rq_r[p] = recip_rn(dq_r[p]);
     }
     dk_g[0] = dk_g[1] = __uint_as_float(ak) / 127.0f;
-    rk_g[0] = rk_g[1] = 1.0f / dk_g[0];
+    rk_g[0] = rk_g[1] = recip_rn(dk_g[0]);
   }
   if (FINE) {
 #pragma unroll
@@ -368,7 +375,7 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       dv[i] = s_dv[c0 + i];
-      rv[i] = 1.0f / dv[i];
+      rv[i] = recip_rn(dv[i]);
     }
   }
   uint8_t* qe = reinterpret_cast<uint8_t*>(qp.q_scales);
@@ -679,7 +686,7 @@ __device__ __forceinline__ void seq_int8_item(const uint16_t* __restrict__ q, co
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     dv[i] = cb.ka ? s_dv[c0 + i] : 0.0f;
-    rv[i] = 1.0f / dv[i];
+    rv[i] = recip_rn(dv[i]);
   }
   float xq[NP][8], xk[NP][8];
   uint32_t aq = 0, ak = 0;
@@ -740,23 +747,23 @@ __device__ __forceinline__ void seq_int8_item(const uint16_t* __restrict__ q, co
 #pragma unroll
       for (int o = 1; o < C8; o <<= 1) a = max(a, (uint32_t)__shfl_xor((int)a, o));
       dq_r[p] = __uint_as_float(a) / 127.0f;
-      rq_r[p] = 1.0f / dq_r[p];
+      rq_r[p] = recip_rn(dq_r[p]);
     }
     block_umax2(akg[0], akg[1], s_red);
 #pragma unroll
     for (int g = 0; g < 2; g++) {
       dk_g[g] = __uint_as_float(akg[g]) / 127.0f;
-      rk_g[g] = 1.0f / dk_g[g];
+      rk_g[g] = recip_rn(dk_g[g]);
     }
   } else {
     block_umax2(aq, ak, s_red);
 #pragma unroll
     for (int p = 0; p < NP; p++) {
       dq_r[p] = __uint_as_float(aq) / 127.0f;
-      rq_r[p] = 1.0f / dq_r[p];
+      rq_r[p] = recip_rn(dq_r[p]);
     }
     dk_g[0] = dk_g[1] = __uint_as_float(ak) / 127.0f;
-    rk_g[0] = rk_g[1] = 1.0f / dk_g[0];
+    rk_g[0] = rk_g[1] = recip_rn(dk_g[0]);
   }
   if (FINE) {
 #pragma unroll
@@ -848,7 +855,7 @@ __device__ __forceinline__ void seq_mxfp4_item(const uint16_t* __restrict__ q, c
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       dv[i] = cb.ka ? s_dv[c0 + i] : 0.0f;
-      rv[i] = 1.0f / dv[i];
+      rv[i] = recip_rn(dv[i]);
     }
   }
   uint8_t* qe = reinterpret_cast<uint8_t*>(qp.q_scales);
