@@ -1,8 +1,8 @@
 // attn_bwd.hip -- 8-bit attention backward (dQ, dK, dV) for gfx950.
 //
-// The pages name an accurate and efficient 8-bit attention for both forward and
-// backward propagation (SageAttention3 abstract) and a trainable INT8 attention
-// (SageBwd, related-papers page of SageAttention2++), without the recipe.  This
+// The pages report that 8-bit attention can also serve training, with the backward
+// quantized as well as the forward (SageAttention3 abstract), and name a trainable INT8
+// attention (SageBwd, related-papers page of SageAttention2++); neither gives the recipe.  This
 // backward keeps the forward's quantization of QK^T and runs every product on
 // 8-bit MFMA with fp32 accumulation:
 //   S   = Q K_s^T        INT8 (the forward's codes: per-64-token steps, K smoothed)
@@ -149,6 +149,7 @@ __global__ __launch_bounds__(2 * D) void bwd_prep_kernel(const uint16_t* __restr
   const int cidx = 8 * (w % CG) + (lane & 7), rg = 8 * (w / CG) + (lane >> 3), c0 = 8 * cidx;
   const int nb = Np / 64;
   __shared__ float s_inv[kNT][D];
+  __shared__ float s_pre[kNT][D];   // power of two applied to x before the step's reciprocal
   __shared__ uint32_t s_red[2][NW];
   __shared__ float s_dsum[CG][64];
   __shared__ uint32_t s_T[kNT][D * RS];
@@ -174,7 +175,11 @@ __global__ __launch_bounds__(2 * D) void bwd_prep_kernel(const uint16_t* __restr
 #pragma unroll
     for (int ch = 0; ch < kStatChunks; ch++) m = max(m, bp.amax_part[(((size_t)t * kStatChunks + ch) * BH + bh) * D + c]);
     const float am = __uint_as_float(m);
-    s_inv[t][c] = am == 0.0f ? 0.0f : 448.0f / am;
+    // code = (x pre) * (448 / (amax pre)): pre = 2^64 for maxima below 2^-64, whose 448 / amax
+    // would exceed binary32 (x pre is exact; pre = 1 otherwise)
+    const float pre = am < 0x1p-64f ? 0x1p64f : 1.0f;
+    s_pre[t][c] = pre;
+    s_inv[t][c] = am == 0.0f ? 0.0f : 448.0f / (am * pre);
     if (blk == 0) bp.chan_step[((size_t)t * BH + bh) * D + c] = am / 448.0f;
   }
   float mu[8];
@@ -219,6 +224,12 @@ __global__ __launch_bounds__(2 * D) void bwd_prep_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       const float s0 = s_inv[0][c0 + i], s1 = s_inv[1][c0 + i], s2 = s_inv[2][c0 + i];
+#pragma unroll
+      for (int r2 = 0; r2 < 2; r2++) {
+        xd[r2][i] *= s_pre[0][c0 + i];
+        xq[r2][i] *= s_pre[1][c0 + i];
+        xk[r2][i] *= s_pre[2][c0 + i];
+      }
       if (h == 0) {   // rows 0, 1 -> bytes 0, 1
         tw[0][i] = __builtin_amdgcn_cvt_pk_fp8_f32(xd[0][i] * s0, xd[1][i] * s0, 0, false);
         tw[1][i] = __builtin_amdgcn_cvt_pk_fp8_f32(xq[0][i] * s1, xq[1][i] * s1, 0, false);
@@ -251,7 +262,10 @@ __global__ __launch_bounds__(2 * D) void bwd_prep_kernel(const uint16_t* __restr
     amd = max(amd, s_red[0][j]);
     amv = max(amv, s_red[1][j]);
   }
-  const float id = amd == 0 ? 0.0f : 448.0f / __uint_as_float(amd), iv = amv == 0 ? 0.0f : 448.0f / __uint_as_float(amv);
+  // block steps: the same pre-scaling for maxima below 2^-64
+  const float amdf = __uint_as_float(amd), amvf = __uint_as_float(amv);
+  const float pd = amdf < 0x1p-64f ? 0x1p64f : 1.0f, pv = amvf < 0x1p-64f ? 0x1p64f : 1.0f;
+  const float id = amd == 0 ? 0.0f : 448.0f / (amdf * pd), iv = amv == 0 ? 0.0f : 448.0f / (amvf * pv);
   if (tid < 64) {
     const int row = t0 + tid;
     float dsum = s_dsum[0][tid];
@@ -270,6 +284,11 @@ __global__ __launch_bounds__(2 * D) void bwd_prep_kernel(const uint16_t* __restr
     float xd[8], xv[8];
     unpack8io<DT>(rd[r], xd);
     unpack8io<DT>(rv[r], xv);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      xd[i] *= pd;
+      xv[i] *= pv;
+    }
     uint32_t wd[2], wv[2];
 #pragma unroll
     for (int j = 0; j < 2; j++) {
