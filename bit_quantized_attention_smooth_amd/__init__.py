@@ -19,7 +19,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsage_attn.so")
+# SAGE_ATTN_LIBRARY selects another build of the same library (the host-sanitized build the
+# ABI tests run under); there is no fallback: a missing library raises in lib().
+LIB_PATH = os.environ.get("SAGE_ATTN_LIBRARY") or os.path.join(_HERE, "libsage_attn.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_OUT_OF_MEMORY, ERR_HIP = range(6)
 FMT = {"int8": 1, "fp8": 2, "mxfp4": 3, "mxfp8": 4, "f16": 5, "int8_token": 6, "mxfp4_qblock": 7}
@@ -215,10 +217,25 @@ def attn_fwd_oneshot(q, k, v, *, causal=False, sm_scale=None, qk_fmt="int8", pv_
     return o
 
 
+def check_bwd_inputs(q, o, do, lse):
+    """The backward's C entry takes raw pointers: it reads O and dO with Q's offsets and dtype and
+    LSE as fp32 [B, H, N], so anything else would be read past its end.  Raises ValueError unless
+    o and do match q (shape, dtype, device) and lse is a float32 [B, H, N] tensor on q's device."""
+    B, H, N, _ = q.shape
+    for name, t in (("o", o), ("do", do)):
+        if not (torch.is_tensor(t) and t.device == q.device and t.shape == q.shape and t.dtype == q.dtype):
+            raise ValueError(f"{name} must be a {q.dtype} tensor of shape {tuple(q.shape)} on {q.device}")
+    if not (torch.is_tensor(lse) and lse.device == q.device and lse.dtype == torch.float32 and
+            tuple(lse.shape) == (B, H, N)):
+        raise ValueError(f"lse must be a float32 tensor of shape {(B, H, N)} on {q.device} "
+                         f"(the forward's LSE of fixed-length inputs)")
+
+
 def attn_bwd(q, k, v, o, do, lse, *, causal=False, sm_scale=None):
     """8-bit backward: returns dQ, dK, dV in the input dtype."""
     q, k, v = _qkv(q, k, v)
     B, H, N, d = q.shape
+    check_bwd_inputs(q, o, do, lse)
     p = problem(B, H, N, d, causal=causal, sm_scale=sm_scale, dtype=q.dtype)
     nbytes = ctypes.c_size_t()
     _check(lib().sage_attn_bwd_ws_size(ctypes.byref(p), ctypes.byref(nbytes)))

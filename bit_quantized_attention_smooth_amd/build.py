@@ -14,12 +14,25 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-u
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer (device code is not instrumented): a
+# separate build, loaded through SAGE_ATTN_LIBRARY with the sanitizer runtime preloaded, that the
+# host ABI tests run under.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZE_OUT = os.path.join(BUILD, "sanitize", "libsage_attn.so")
+
+
+def build(verbose=False, sanitize=False):
+    """Compile every source for gfx950 and link the library in-tree (sanitize: the host-sanitized
+    build under _build/sanitize, -O1)."""
+    bdir = os.path.join(BUILD, "sanitize") if sanitize else BUILD
+    target = SANITIZE_OUT if sanitize else OUT
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1"] + SANITIZE if sanitize else FLAGS
+    os.makedirs(bdir, exist_ok=True)
     procs, objs = [], []
     for src in SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC] + flags + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
@@ -35,10 +48,11 @@ def build(verbose=False):
             print("\n".join(lines))
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
-    tmp = OUT + ".tmp"
-    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
-    os.replace(tmp, OUT)
-    return OUT
+    tmp = target + ".tmp"
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + (SANITIZE[:4] if sanitize else [])
+    subprocess.check_call(link + ["-o", tmp] + objs)
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":

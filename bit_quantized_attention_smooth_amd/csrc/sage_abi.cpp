@@ -250,7 +250,11 @@ int sage_abi_version(void) { return SAGE_ABI_VERSION; }
 const char* sage_last_error(void) { return g_err; }
 
 const char* sage_status_string(sage_status s) {
-  switch (s) {
+  // a C caller may pass any int; reading it as the enum type would be undefined for values
+  // outside the enumerators' range, so take its bits as an int
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case SAGE_OK: return "ok";
     case SAGE_ERR_INVALID_ARG: return "invalid argument";
     case SAGE_ERR_UNSUPPORTED: return "unsupported";

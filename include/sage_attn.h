@@ -120,48 +120,94 @@ typedef struct {
 } sage_quant_layout;
 
 /*
- * Forward attention, bf16 I/O, the one-call form.  q, k, v: device [B,H,N,d];
- * o: device output [B,H,N,d].  qk_fmt/pv_fmt as above.  Takes its scratch with
- * hipMallocAsync / hipFreeAsync on `stream` (stream-ordered).
+ * Forward attention, bf16 I/O, the one-call form: smoothing of K (and Q on the
+ * MXFP4 path), per-block quantization, then the tiled online-softmax loop with
+ * P~V in the chosen format and the normalisation after the last tile.
+ * Passages: plug-and-play quantized attention on q, k, v with a causal flag
+ * (SageAttention3 abstract); smoothing K and INT8 QK^T (review thread, reply to
+ * reviewer wwcu W1); online softmax over K tiles and normalisation once at the
+ * end (reply to reviewer xY6z, Q3 and Q2); FP8 P~V with two-level accumulation
+ * and smoothing Q (SageAttention2 abstract); microscaled FP4 (SageAttention3
+ * abstract).
+ *   q, k, v   device bf16 [B,H,N,d], read only, owned by the caller
+ *   o         device bf16 [B,H,N,d], written
+ *   causal    0 or 1 (top-left aligned); sm_scale finite and > 0
+ *   qk_fmt, pv_fmt   a supported SAGE_FMT_* pair
+ * Takes its scratch (the quantized buffer) with hipMallocAsync / hipFreeAsync
+ * on `stream` (stream-ordered, so calls on different streams are independent).
+ * Errors: INVALID_ARG (null or misaligned pointer, bad size or scale),
+ * UNSUPPORTED (d or format pair), OUT_OF_MEMORY (the scratch), HIP (a launch).
  */
 sage_status sage_attn_fwd(const void *q, const void *k, const void *v, void *o,
                           int B, int H, int N, int d, int causal, float sm_scale,
                           int qk_fmt, int pv_fmt, void *stream);
 
-/* Size and layout of the quantized buffer for `p`. */
+/*
+ * Size and layout of the quantized buffer for `p` (the codes, steps and
+ * smoothing terms of the prologue: per-block INT8 steps, review thread, reply
+ * to reviewer xY6z W1-(2); MX blocks of 32 with E8M0 scales, SageAttention3
+ * abstract and the TetraJet abstract's per-group microscaling).  Host only:
+ * writes *bytes and, when layout is not NULL, the byte offsets of every part.
+ * Errors: INVALID_ARG (null bytes or a bad problem), UNSUPPORTED.
+ */
 sage_status sage_quant_size(const sage_problem *p, size_t *bytes, sage_quant_layout *layout);
 
 /*
- * Smoothing + quantization prologue: reads q, k, v (device [B,H,N,d] in
- * p->io_dtype) and writes the codes, scales and correction terms into
- * quant_buf (device, quant_bytes >= sage_quant_size's bytes), laid out as
- * sage_quant_layout describes.
+ * Smoothing + quantization prologue: the per-channel mean of K over the tokens
+ * (smoothing K, review thread, reply to reviewer wwcu W1; smoothing Q on the
+ * 4-bit path, SageAttention2 abstract), per-block INT8 or MXFP4 codes of Q and
+ * K, FP8 (or MX, or fp16) V, and the terms smoothing removes (dS added to the
+ * scores, the row shift added to the LSE).
+ *   q, k, v     device [B,H,N,d] in p->io_dtype, read only
+ *   quant_buf   device, quant_bytes >= sage_quant_size's bytes, written as
+ *               sage_quant_layout describes; owned by the caller, who may keep it
+ *               and pass it to sage_attn_fwd_quantized
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE (quant_bytes too small), HIP.
  */
 sage_status sage_quantize(const void *q, const void *k, const void *v, const sage_problem *p,
                           void *quant_buf, size_t quant_bytes, void *stream);
 
 /*
  * Fused attention on a buffer written by sage_quantize for the same problem:
- * o device [B,H,N,d] in p->io_dtype; lse device fp32 [B,H,N] or NULL
- * (natural-log log-sum-exp of the true, unsmoothed scaled scores).
+ * QK^T on INT8 or microscaled FP4 codes with the dequantization folded into the
+ * softmax scale, online softmax over 64-key tiles (review thread, reply to
+ * reviewer xY6z Q3), P~ quantized for the P~V product with fp32 accumulation
+ * across tiles (two-level accumulation, SageAttention2 abstract), O / l after
+ * the last tile (reply to xY6z Q2).
+ *   quant_buf   device, read only (quant_bytes as sage_quant_size gives)
+ *   o           device [B,H,N,d] in p->io_dtype, written
+ *   lse         device fp32 [B,H,N] or NULL: natural-log log-sum-exp of the
+ *               true, unsmoothed scaled scores
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
 sage_status sage_attn_fwd_quantized(const void *quant_buf, size_t quant_bytes, const sage_problem *p,
                                     void *o, float *lse, void *stream);
 
-/* Workspace bytes needed by sage_attn_fwd_ex (the quantized buffer). */
+/* Workspace bytes needed by sage_attn_fwd_ex (the quantized buffer of sage_quant_size).
+ * Host only.  Errors: INVALID_ARG, UNSUPPORTED. */
 sage_status sage_attn_fwd_ws_size(const sage_problem *p, size_t *bytes);
 
-/* Forward with caller workspace: quantize into ws, then the fused kernel.  lse may be NULL. */
+/*
+ * Forward with caller workspace: sage_quantize into ws, then
+ * sage_attn_fwd_quantized (the same passages).  bf16 or fp16 I/O as
+ * p->io_dtype; q, k, v read only; o written; lse device fp32 [B,H,N] or NULL;
+ * ws device, ws_bytes >= sage_attn_fwd_ws_size, owned by the caller.  Launches
+ * kernels only (no allocation, no memset), so a HIP graph may capture it.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
 sage_status sage_attn_fwd_ex(const sage_problem *p, const void *q, const void *k, const void *v,
                              void *o, float *lse, void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace bytes needed by sage_attn_bwd. */
+/* Workspace bytes needed by sage_attn_bwd.  Host only.  Errors: INVALID_ARG, UNSUPPORTED. */
 sage_status sage_attn_bwd_ws_size(const sage_problem *p, size_t *bytes);
 
 /*
- * 8-bit backward.  q, k, v, o, dout: device [B,H,N,d] (bf16 or fp16 as
- * p->io_dtype; o is the forward output); lse: device fp32 [B,H,N] from the
- * forward; dq, dk, dv: device outputs [B,H,N,d].  p->qk_fmt must be INT8 and
+ * 8-bit backward: dQ, dK, dV of softmax attention with every product on 8-bit
+ * matrix cores (8-bit attention for training, forward and backward,
+ * SageAttention3 abstract; SageBwd, SageAttention2++ related-papers page).
+ * q, k, v, o, dout: device [B,H,N,d] (bf16 or fp16 as p->io_dtype; o is the
+ * forward output), read only; lse: device fp32 [B,H,N] from the forward;
+ * dq, dk, dv: device outputs [B,H,N,d], written.  p->qk_fmt must be INT8 and
  * p->pv_fmt FP8 (other pairs: SAGE_ERR_UNSUPPORTED); d is 64 or 128.  ws: device
  * workspace of at least sage_attn_bwd_ws_size bytes (the forward's quantized
  * buffer followed by the backward's operand tiles).
@@ -204,12 +250,15 @@ typedef struct {
     int max_seqlen_q, max_seqlen_k;
 } sage_varlen_problem;
 
+/* Workspace bytes needed by sage_attn_varlen_fwd.  Host only.  Errors: INVALID_ARG, UNSUPPORTED. */
 sage_status sage_varlen_ws_size(const sage_varlen_problem *p, size_t *bytes);
 
 sage_status sage_attn_varlen_fwd(const sage_varlen_problem *p, const void *q, const void *k, const void *v,
                                  const int *cu_seqlens_q, const int *cu_seqlens_k, void *o, float *lse,
                                  void *ws, size_t ws_bytes, void *stream);
 
+/* Status text, the calling thread's last error message (empty when none; valid until the
+ * thread's next call into the library) and SAGE_ABI_VERSION.  Host only, never fail. */
 const char *sage_status_string(sage_status s);
 const char *sage_last_error(void);
 int sage_abi_version(void);

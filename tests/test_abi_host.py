@@ -189,3 +189,27 @@ def test_varlen_workspace_covers_every_sequence_padding():
     # per query head; 256 extra tokens per sequence
     per_seq = 256 * (2 * 128 + 4 * 128)
     assert sizes[1] - sizes[0] >= 7 * per_seq and sizes[2] - sizes[1] >= 56 * per_seq
+
+
+def test_backward_binding_rejects_mismatched_o_do_lse():
+    """The Python binding is the only guard of the backward's raw-pointer arguments: O and dO
+    must match Q, and LSE must be float32 [B, H, N] (a bf16 LSE, the packed path's [H, total]
+    LSE or a shorter dO would be read past their ends on the device)."""
+    import torch
+    import bit_quantized_attention_smooth_amd as S
+    B, H, N, d = 1, 2, 96, 64
+    q = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
+    good = dict(o=torch.zeros_like(q), do=torch.zeros_like(q), lse=torch.zeros(B, H, N))
+    S.check_bwd_inputs(q, **good)
+    bad = [("o", torch.zeros(B, H, N - 1, d, dtype=torch.bfloat16)),
+           ("o", torch.zeros(B, H, N, d, dtype=torch.float16)),
+           ("do", torch.zeros(B, H, N // 2, d, dtype=torch.bfloat16)),
+           ("do", torch.zeros(B, H, N, d)),
+           ("lse", torch.zeros(B, H, N, dtype=torch.bfloat16)),
+           ("lse", torch.zeros(H, B * N)),
+           ("lse", torch.zeros(B, H, N - 1)),
+           ("lse", None)]
+    for name, t in bad:
+        kw = dict(good, **{name: t})
+        with pytest.raises(ValueError):
+            S.check_bwd_inputs(q, **kw)
