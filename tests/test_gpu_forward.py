@@ -265,7 +265,7 @@ def test_forward_tiny_magnitude_inputs(sage, qk, pv, causal):
     for n in "qk":
         g[n] = (g[n].float() * 1e-21).to(torch.bfloat16)
         f[n] = g[n].float().cpu().numpy().reshape(B * H, N, d)
-    assert 1e-22 < float(np.abs(f["q"]).max()) < 1e-20 and 1e-22 < float(np.abs(f["k"]).max()) < 1e-20
+    assert 1e-22 < float(np.abs(f["q"]).max()) < 1e-19 and 1e-22 < float(np.abs(f["k"]).max()) < 1e-19
     o, lse = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv,
                            return_lse=True)
     torch.cuda.synchronize()

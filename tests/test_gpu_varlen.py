@@ -189,13 +189,13 @@ def test_varlen_full_size_llm_prefill_sampled(sage):
     assert torch.isfinite(o).all()
     cu = x["cu_q"].numpy()
     for b in (0, len(cu) - 2):
-        sl = slice(cu[b], cu[b + 1])
-        sub = {n: _f32(x[n][sl]) for n in "qkv"}
+        rows = slice(cu[b], cu[b + 1])
+        sub = {n: _f32(x[n][rows]) for n in "qkv"}
         n = cu[b + 1] - cu[b]
         c = np.array([0, n], np.int32)
         o_sim, _, _, sl = oracle.attn_varlen(sub["q"], sub["k"], sub["v"], c, c, True, w["sm_scale"], tile=TILE,
                                              slack=True)
-        og = to_np64(o[sl])
+        og = to_np64(o[rows])
         assert within(og, o_sim, sl), excess(og, o_sim, sl)
         assert cos(og, o_sim) >= 0.9999
 
