@@ -28,7 +28,7 @@ FMT = {"int8": 1, "fp8": 2, "mxfp4": 3, "mxfp8": 4, "f16": 5, "int8_token": 6, "
 DT = {torch.bfloat16: 0, torch.float16: 1}
 
 # Every symbol the header declares (kept in sync by a CPU test that parses the header).
-EXPORTS = ["sage_attn_fwd", "sage_quant_size", "sage_quantize", "sage_attn_fwd_quantized",
+EXPORTS = ["sage_attn_fwd", "sage_attn_fwd_noalloc", "sage_quant_size", "sage_quantize", "sage_attn_fwd_quantized",
            "sage_attn_fwd_ws_size", "sage_attn_fwd_ex", "sage_attn_bwd_ws_size", "sage_attn_bwd",
            "sage_varlen_ws_size", "sage_attn_varlen_fwd",
            "sage_status_string", "sage_last_error", "sage_abi_version"]
@@ -74,6 +74,7 @@ def lib():
         P = ctypes.POINTER(Problem)
         sigs = {
             "sage_attn_fwd": [vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp],
+            "sage_attn_fwd_noalloc": [vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp],
             "sage_quant_size": [P, ctypes.POINTER(sz), ctypes.POINTER(QuantLayout)],
             "sage_quantize": [vp, vp, vp, P, vp, sz, vp],
             "sage_attn_fwd_quantized": [vp, sz, P, vp, vp, vp],
@@ -214,6 +215,21 @@ def attn_fwd_oneshot(q, k, v, *, causal=False, sm_scale=None, qk_fmt="int8", pv_
     sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
     _check(lib().sage_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, int(bool(causal)), sm,
                                FMT[qk_fmt], FMT[pv_fmt], _stream()))
+    return o
+
+
+def attn_fwd_noalloc(q, k, v, *, causal=False, sm_scale=None, qk_fmt="int8", pv_fmt="fp8", out=None):
+    """The no-allocation C entry (bf16 only): its scratch is a fixed 64 MiB array the library
+    holds per GPU, shared by every call on that GPU.  `out` (bf16, q's shape) may be given so the
+    call allocates nothing here either."""
+    q, k, v = _qkv(q, k, v)
+    B, H, N, d = q.shape
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype or o.device != q.device or not o.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    _check(lib().sage_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, int(bool(causal)), sm,
+                                       FMT[qk_fmt], FMT[pv_fmt], _stream()))
     return o
 
 

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/sage_attn.h"
 #include "sage_launch.hpp"
@@ -241,6 +242,47 @@ sage_status check_tensors(std::initializer_list<const void*> ptrs) {
   return SAGE_OK;
 }
 
+// ---- scratch of the no-allocation forward (sage_attn_fwd_noalloc) ----
+// One fixed array per GPU, in the library's device code, holding the quantized buffer of one
+// problem.  Host code never passes the array's name to a kernel (on the host it is only a
+// stand-in): hipGetSymbolAddress gives its device address, once per device with that device
+// current, and that address is what the kernels receive.  Calls on one GPU share it, so
+// calls that overlap on one GPU race.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the device that runs `stream` (the current device
+// for the null stream), looked up on the first call for that device.
+sage_status scratch_for(void* stream, void** out) {
+  int cur = 0, dev = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice((hipStream_t)stream, &dev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(SAGE_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    hipError_t r = dev != cur ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    }
+    if (r != hipSuccess) return hip_fail(r, "hipSetDevice");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SAGE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -342,6 +384,22 @@ sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, 
   hipError_t f = hipFreeAsync(ws, (hipStream_t)stream);
   if (s == SAGE_OK && f != hipSuccess) return hip_fail(f, "hipFreeAsync");
   return s;
+}
+
+sage_status sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                                  int causal, float sm_scale, int qk_fmt, int pv_fmt, void* stream) {
+  sage_problem p = make_problem(B, H, N, d, causal, sm_scale, SAGE_DT_BF16, qk_fmt, pv_fmt);
+  sage_status s = check_problem(&p);
+  if (s != SAGE_OK) return s;
+  if ((s = check_tensors({q, k, v, o})) != SAGE_OK) return s;
+  size_t bytes = 0;
+  sage_quant_size(&p, &bytes, nullptr);
+  if (bytes > kScratchBytes)
+    return fail(SAGE_ERR_WORKSPACE, "the problem needs %zu bytes of scratch; the no-allocation entry holds %zu "
+                "(use sage_attn_fwd_ex with a caller workspace)", bytes, kScratchBytes);
+  void* ws = nullptr;
+  if ((s = scratch_for(stream, &ws)) != SAGE_OK) return s;
+  return sage_attn_fwd_ex(&p, q, k, v, o, nullptr, ws, bytes, stream);
 }
 
 sage_status sage_attn_bwd_ws_size(const sage_problem* p, size_t* bytes) {

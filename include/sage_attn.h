@@ -143,6 +143,21 @@ sage_status sage_attn_fwd(const void *q, const void *k, const void *v, void *o,
                           int qk_fmt, int pv_fmt, void *stream);
 
 /*
+ * The one-call forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, kernels and
+ * results as sage_attn_fwd, but the quantized buffer lives in a fixed array of 64 MiB that the
+ * library holds on each GPU it runs on until the process ends (found on the first call on a
+ * device); the call allocates and frees nothing.  Problems whose quantized buffer exceeds
+ * 64 MiB (sage_quant_size) return SAGE_ERR_WORKSPACE without launching.  Every call on one GPU
+ * uses that GPU's array, so calls that overlap on one GPU (other streams, other threads) race;
+ * calls on one stream are ordered.  Errors: as sage_attn_fwd, with WORKSPACE for the size and
+ * HIP if the array's address cannot be found.
+ */
+sage_status sage_attn_fwd_noalloc(const void *q, const void *k, const void *v, void *o,
+                                  int B, int H, int N, int d, int causal, float sm_scale,
+                                  int qk_fmt, int pv_fmt, void *stream);
+
+/*
  * Size and layout of the quantized buffer for `p` (the codes, steps and
  * smoothing terms of the prologue: per-block INT8 steps, review thread, reply
  * to reviewer xY6z W1-(2); MX blocks of 32 with E8M0 scales, SageAttention3

@@ -213,3 +213,18 @@ def test_backward_binding_rejects_mismatched_o_do_lse():
         kw = dict(good, **{name: t})
         with pytest.raises(ValueError):
             S.check_bwd_inputs(q, **kw)
+
+
+def test_noalloc_entry_rejects_problems_beyond_its_scratch():
+    """The no-allocation forward holds a 64 MiB quantized buffer per GPU: a problem that needs more
+    (B=1 H=32 N=8192 d=128, INT8 / FP8: about 99 MiB) is refused on the host, before any device
+    call, and a null pointer is still refused first."""
+    L = S.lib()
+    n = ctypes.c_size_t()
+    assert L.sage_quant_size(ctypes.byref(_p(B=1, H=32, N=8192, d=128)), ctypes.byref(n), None) == S.OK
+    assert n.value > 64 << 20
+    st = L.sage_attn_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, 1, 32, 8192, 128, 0, 0.088, 1, 2, None)
+    assert st == S.ERR_WORKSPACE, L.sage_last_error()
+    assert b"64" in L.sage_last_error() or b"67108864" in L.sage_last_error()
+    assert L.sage_attn_fwd_noalloc(None, FAKE, FAKE, FAKE, 1, 2, 100, 64, 0, 0.125, 1, 2, None) == S.ERR_INVALID_ARG
+    assert L.sage_attn_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, 1, 2, 100, 96, 0, 0.125, 1, 2, None) == S.ERR_UNSUPPORTED
