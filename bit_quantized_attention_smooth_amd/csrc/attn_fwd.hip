@@ -62,6 +62,17 @@ struct FwdArgs {
 #ifndef MFMA_IL_D128
 #define MFMA_IL_D128 0
 #endif
+#ifndef FWD_ONEBUF_D128
+#define FWD_ONEBUF_D128 1
+#endif
+// One score buffer per wave (QK(j) issued in tile j itself), which frees the registers of the
+// second buffer so that three workgroups (three waves per SIMD) fit on a CU: at head dim 128 with
+// INT8 QK and FP8 P~V the kernel is bound by vector issue, and a lone wave issues vector work at
+// half the SIMD's rate, so a third wave that keeps two of them ready pays more than the overlap
+// of the next tile's QK products inside one wave.  Measured: N = 8192 non-causal 712 -> 666 us,
+// the causal 4096-token prefill 110 -> 102 us.
+template <int D, int QK, int PV>
+constexpr bool kOneBuf = FWD_ONEBUF_D128 && D == 128 && QK == QK_INT8 && PV == PV_FP8;
 constexpr int kTK = 64;      // keys per tile (= the INT8 K block)
 constexpr int kQT = 128;     // queries per workgroup pass
 
@@ -154,11 +165,26 @@ struct LaneOffs {
   static constexpr int KL = G::template kloads<NT>(), VL = G::template vloads<NT>();
   uint32_t kld[KL];                 // direct-load source offsets inside a K tile
   uint32_t vld[VL];                 // direct-load source offsets inside a V^T tile
-  uint32_t kop[2][G::NQF];          // LDS offsets of the K operand reads (subtile, chunk)
-  uint32_t ksc[2][G::NQF];          // MXFP4: LDS offsets of the K scale bytes
-  uint32_t vop[G::NCB][G::VOPS];    // LDS offsets of the V^T operand reads: FP8 / MXFP8 / fp16
-                                    // (block, 16-byte chunk); MXFP4 (block, {codes, scale byte})
+  // Subtile 1's K rows are subtile 0's plus KS (16 rows, except MXFP8 V), and V^T block c's rows
+  // are block 0's plus 32 c; the swizzles below do not depend on those row bits, so the later
+  // offsets are the first ones plus a constant (an immediate of the LDS read), and only the
+  // first ones occupy registers.
+  static constexpr bool KOP_IMM = KeyMap<PV>::KS == 16;
+  static constexpr int VROWB = PV == PV_MXFP4 ? 32 : PV == PV_F16 ? 128 : 64;   // bytes per V^T row
+  uint32_t kop[KOP_IMM ? 1 : 2][G::NQF];   // LDS offsets of the K operand reads (subtile, chunk)
+  uint32_t ksc[G::NQF];             // MXFP4: LDS offsets of the K scale bytes (subtile 0)
+  uint32_t vop[G::VOPS];            // LDS offsets of the V^T operand reads of block 0: FP8 / MXFP8 /
+                                    // fp16 (16-byte chunk); MXFP4 ({codes, scale byte})
   uint32_t vsc;                     // MXFP8: LDS offset of block 0's E8M0 byte (+32 per block)
+
+  __device__ __forceinline__ uint32_t kop_at(int s, int c) const {
+    return KOP_IMM ? kop[0][c] + s * KeyMap<PV>::KS * G::KROW : kop[KOP_IMM ? 0 : s][c];
+  }
+  __device__ __forceinline__ uint32_t ksc_at(int s, int c) const { return ksc[c] + s * KeyMap<PV>::KS * (D / 32); }
+  // block c, read t: MXFP4's scale byte (t = 1) advances 32 bytes per block
+  __device__ __forceinline__ uint32_t vop_at(int c, int t) const {
+    return vop[t] + c * (PV == PV_MXFP4 && t == 1 ? 32 : 32 * VROWB);
+  }
 
   __device__ __forceinline__ void init(int w, int lane, int n, int hh) {
 #pragma unroll
@@ -182,32 +208,31 @@ struct LaneOffs {
       }
     }
 #pragma unroll
-    for (int s = 0; s < 2; s++) {
+    for (int s = 0; s < (KOP_IMM ? 1 : 2); s++) {
       const int row = key_perm<PV>(n, s);
 #pragma unroll
       for (int c = 0; c < G::NQF; c++) {
         const int col = 2 * c + hh;
         kop[s][c] = row * G::KROW + ((col ^ swz<G::KROW>(row)) << 4);
-        ksc[s][c] = G::KBYTES + row * (D / 32) + col;
+        if (s == 0) ksc[c] = G::KBYTES + row * (D / 32) + col;
       }
     }
-#pragma unroll
-    for (int c = 0; c < G::NCB; c++) {
-      const int row = 32 * c + n;
+    {
+      const int row = n;   // V^T block 0
       if (PV == PV_MXFP4) {
-        vop[c][0] = row * 32 + ((hh ^ swz_v4(row)) << 4);
-        vop[c][1] = G::VBYTES + hh * D + row;
+        vop[0] = row * 32 + ((hh ^ swz_v4(row)) << 4);
+        vop[1] = G::VBYTES + hh * D + row;
       } else if (PV == PV_MXFP8) {
         // half hh: keys 16 hh + [0, 16) (block 0), then 32 + 16 hh + [0, 16) (block 1)
-        vop[c][0] = row * 64 + ((hh ^ swz_v(row)) << 4);
-        vop[c][1] = row * 64 + (((2 + hh) ^ swz_v(row)) << 4);
+        vop[0] = row * 64 + ((hh ^ swz_v(row)) << 4);
+        vop[1] = row * 64 + (((2 + hh) ^ swz_v(row)) << 4);
       } else if (PV == PV_F16) {
         // half hh: keys 32 hh + 8 t + [0, 8) for the t-th K = 16 product
 #pragma unroll
-        for (int t = 0; t < G::VOPS; t++) vop[c][t] = row * 128 + (((4 * hh + t) ^ swz_v16(row)) << 4);
+        for (int t = 0; t < G::VOPS; t++) vop[t] = row * 128 + (((4 * hh + t) ^ swz_v16(row)) << 4);
       } else {
-        vop[c][0] = row * 64 + (((2 * hh) ^ swz_v(row)) << 4);
-        vop[c][1] = row * 64 + (((2 * hh + 1) ^ swz_v(row)) << 4);
+        vop[0] = row * 64 + (((2 * hh) ^ swz_v(row)) << 4);
+        vop[1] = row * 64 + (((2 * hh + 1) ^ swz_v(row)) << 4);
       }
     }
     // the scale byte of (channel 32 c + n, key block hh), supplied by lane n + 32 hh
@@ -218,16 +243,14 @@ struct LaneOffs {
 #pragma unroll
     for (int i = 0; i < VL; i++) asm volatile("" : "+v"(vld[i]));
 #pragma unroll
-    for (int s = 0; s < 2; s++)
+    for (int s = 0; s < (KOP_IMM ? 1 : 2); s++)
 #pragma unroll
-      for (int c = 0; c < G::NQF; c++) {
-        asm volatile("" : "+v"(kop[s][c]));
-        if (QK == QK_MXFP4) asm volatile("" : "+v"(ksc[s][c]));
-      }
+      for (int c = 0; c < G::NQF; c++) asm volatile("" : "+v"(kop[s][c]));
 #pragma unroll
-    for (int c = 0; c < G::NCB; c++)
+    for (int c = 0; c < G::NQF; c++)
+      if (QK == QK_MXFP4) asm volatile("" : "+v"(ksc[c]));
 #pragma unroll
-      for (int t = 0; t < G::VOPS; t++) asm volatile("" : "+v"(vop[c][t]));
+    for (int t = 0; t < G::VOPS; t++) asm volatile("" : "+v"(vop[t]));
   }
 };
 
@@ -243,11 +266,11 @@ __device__ __forceinline__ void issue_k(uint8_t* lds, const FwdArgs& a, size_t k
 #pragma unroll
   for (int i = 0; i < LO::KL; i++) {
     const int pbase = LO::NTHREADS * i + 64 * w;
-    if (pbase < G::KCHUNKS) load_lds16(kg + lo.kld[i], lds + pbase * 16);
+    if (pbase < G::KCHUNKS) load_lds16_async(kg + lo.kld[i], lds + pbase * 16);
   }
   if (QK == QK_MXFP4 && w == 0 && lane < G::SBYTES / 16) {
     const uint8_t* sg = reinterpret_cast<const uint8_t*>(a.k_scales) + (kt0 + (size_t)j * kTK) * (D / 32);
-    load_lds16(sg + lane * 16, lds + G::KBYTES);
+    load_lds16_async(sg + lane * 16, lds + G::KBYTES);
   }
 }
 
@@ -259,12 +282,12 @@ __device__ __forceinline__ void issue_v(uint8_t* lds, const FwdArgs& a, size_t k
 #pragma unroll
   for (int i = 0; i < LaneOffs<D, QK, NT, PV>::VL; i++) {
     const int pbase = NT * i + 64 * w;
-    if (pbase < G::VCHUNKS) load_lds16(vg + lo.vld[i], lds + pbase * 16);
+    if (pbase < G::VCHUNKS) load_lds16_async(vg + lo.vld[i], lds + pbase * 16);
   }
   if (PV != PV_FP8 && w == NT / 64 - 1 && lane < G::VSB / 16) {
     // E8M0 bytes of the tile's two 32-key groups: [group][channel], contiguous in the buffer
     const uint8_t* sg = reinterpret_cast<const uint8_t*>(a.v_scales) + (kt0 / 32 + 2 * j) * D;
-    load_lds16(sg + 16 * lane, lds + G::VBYTES + 16 * lane);
+    load_lds16_async(sg + 16 * lane, lds + G::VBYTES + 16 * lane);
   }
 }
 
@@ -298,7 +321,7 @@ __device__ __forceinline__ void qk_tile(Score<D, QK>& S, const uint8_t* lk, cons
       v16i acc = v16i{};
 #pragma unroll
       for (int c = 0; c < G::NQF; c++) {
-        const v4i ka = *reinterpret_cast<const v4i*>(lk + lo.kop[s][c]);
+        const v4i ka = *reinterpret_cast<const v4i*>(lk + lo.kop_at(s, c));
         acc = mfma_i8(ka, qf[c], acc);
       }
       S.si[s] = acc;
@@ -306,9 +329,9 @@ __device__ __forceinline__ void qk_tile(Score<D, QK>& S, const uint8_t* lk, cons
       v16f acc = v16f{};
 #pragma unroll
       for (int c = 0; c < G::NQF; c++) {
-        const v4i k4 = *reinterpret_cast<const v4i*>(lk + lo.kop[s][c]);
+        const v4i k4 = *reinterpret_cast<const v4i*>(lk + lo.kop_at(s, c));
         const v8i ka = v8i{k4[0], k4[1], k4[2], k4[3], 0, 0, 0, 0};
-        acc = mfma_mxfp4(ka, qf4[c], acc, lk[lo.ksc[s][c]], qsc[c]);
+        acc = mfma_mxfp4(ka, qf4[c], acc, lk[lo.ksc_at(s, c)], qsc[c]);
       }
       S.sf[s] = acc;
     }
@@ -350,7 +373,7 @@ struct RowState {
 //   p448_i = exp2(u_i * c + (log2 448 - m)) comes out of one FMA and one exp2 per element.
 template <int D, int QK, bool CAUSAL, int PV, bool FINE>
 __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>& Sc, const uint8_t* vstage,
-                                            const float* kstep, float qstep, float sm_log2e, int j, int N, int qw,
+                                            float kstep, float qstep, float sm_log2e, int j, int N, int qw,
                                             int qrow, int hh, float* u, float& c, float& off, float& lsc) {
   using G = Geo<D, QK, PV>;
   constexpr int NCB = G::NCB;
@@ -358,8 +381,8 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
   const bool need_mask = kbase + kTK > N || (CAUSAL && kbase + kTK - 1 > qw);
   float mt;
   if (QK == QK_INT8) {
-    // FINE: this lane's half holds the tile's 32-key group hh, with its own step
-    c = FINE ? qstep * (hh ? kstep[2 * j + 1] : kstep[2 * j]) : qstep * kstep[j];
+    // kstep: this tile's K step (FINE: the step of the 32-key group hh this lane's half holds)
+    c = qstep * kstep;
     // c must stay positive so that masked entries (-inf) stay -inf after scaling.  A zero
     // step (an all-zero block: every code 0) or a product of tiny steps that underflows
     // binary32 is raised to the smallest normal float: a score times it is below 2^-100, as
@@ -500,7 +523,7 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
     for (int cb = 0; cb < NCB; cb++)
 #pragma unroll
       for (int t = 0; t < 4; t++)
-        st.O[cb] = mfma_f16(*reinterpret_cast<const v4i*>(vstage + lo.vop[cb][t]), ph[t], st.O[cb]);
+        st.O[cb] = mfma_f16(*reinterpret_cast<const v4i*>(vstage + lo.vop_at(cb, t)), ph[t], st.O[cb]);
   } else if (PV != PV_MXFP4) {
     v8i pb;
 #pragma unroll
@@ -514,8 +537,8 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
     // O^T += V^T P~^T
 #pragma unroll
     for (int cb = 0; cb < NCB; cb++) {
-      const v4i v0 = *reinterpret_cast<const v4i*>(vstage + lo.vop[cb][0]);
-      const v4i v1 = *reinterpret_cast<const v4i*>(vstage + lo.vop[cb][1]);
+      const v4i v0 = *reinterpret_cast<const v4i*>(vstage + lo.vop_at(cb, 0));
+      const v4i v1 = *reinterpret_cast<const v4i*>(vstage + lo.vop_at(cb, 1));
       const v8i va = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       if (PV == PV_MXFP8)
         st.O[cb] = mfma_f8_sa(va, pb, st.O[cb], vstage[lo.vsc + 32 * cb]);
@@ -543,8 +566,8 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
     for (int k = 0; k < 4; k++) pb[k] = (int)pack_fp4x8(pf + 8 * k, scl);
 #pragma unroll
     for (int cb = 0; cb < NCB; cb++) {
-      const v4i v0 = *reinterpret_cast<const v4i*>(vstage + lo.vop[cb][0]);
-      const int sa = vstage[lo.vop[cb][1]];
+      const v4i v0 = *reinterpret_cast<const v4i*>(vstage + lo.vop_at(cb, 0));
+      const int sa = vstage[lo.vop_at(cb, 1)];
       const v8i va = v8i{v0[0], v0[1], v0[2], v0[3], 0, 0, 0, 0};
       st.O[cb] = mfma_mxfp4(va, pb, st.O[cb], sa, sb);
     }
@@ -562,9 +585,39 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
   }
 }
 
+// ---- epilogue: O / l (FP8: times the V channel step), LSE ----
+//   FP8 P~ (V in FP8 or MXFP8): O and l both carry the factor 448; MXFP8's V block scales are
+//   applied inside the MFMA.  MXFP4 P~: O' = sigma O with sigma = 6 exp2(m - mt) and
+//   l' = 6 sum p, so O / l = O' exp2(mt - m) / l'.
+template <int D, int QK, bool CAUSAL, int DT, int PV>
+__device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, const RowState<D>& st, const Inst& qi, int qrow, int hh,
+                                             const float* vsc) {
+  using G = Geo<D, QK, PV>;
+  constexpr int NCB = G::NCB;
+  const float lt = half_sum(st.l);
+  if (qrow < qi.len) {
+    const float inv = PV != PV_MXFP4 ? 1.0f / lt : fast_exp2(st.mt - st.m) / lt;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + qi.io0 + (size_t)qrow * qi.ios;
+#pragma unroll
+    for (int c = 0; c < NCB; c++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        const int ch = 32 * c + 8 * g + 4 * hh;
+        const v4f sc = PV == PV_FP8 ? *reinterpret_cast<const v4f*>(vsc + ch) * inv
+                                    : v4f{inv, inv, inv, inv};
+        const uint32_t lo = pack2_io<DT>(st.O[c][4 * g] * sc[0], st.O[c][4 * g + 1] * sc[1]);
+        const uint32_t hi = pack2_io<DT>(st.O[c][4 * g + 2] * sc[2], st.O[c][4 * g + 3] * sc[3]);
+        *reinterpret_cast<uint2*>(orow + ch) = make_uint2(lo, hi);
+      }
+    if (a.lse && hh == 0)
+      a.lse[qi.lse0 + qrow] =
+          (st.m + __log2f(lt) - (PV != PV_MXFP4 ? G::PLOG2 : kLog2_6)) * kLn2 + a.lse_corr[qi.row0 + qrow];
+  }
+}
+
 template <int D, int QK, bool CAUSAL, int DT, int PV, bool FINE>
 __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt, uint8_t (*lk)[Geo<D, QK, PV>::KSTAGE],
-                                          uint8_t (*lv)[Geo<D, QK, PV>::VSTAGE]) {
+                                          uint8_t (*lv)[Geo<D, QK, PV>::VSTAGE], float* vsc) {
   using G = Geo<D, QK, PV>;
   constexpr int NCB = G::NCB, NQF = G::NQF;
   const int qbase = qt * kQT;
@@ -608,8 +661,11 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
       qsc[c] = qe[2 * c];
     }
   }
-  // K steps: one per 64-key tile, or (FINE) one per 32 keys
-  const float* kstep = reinterpret_cast<const float*>(a.k_scales) + (FINE ? kt0 / 32 : kt0 / kTK);
+  // K steps: one per 64-key tile, or (FINE) one per 32 keys; a lane reads its half's step.  Each
+  // tile's step is loaded one tile ahead, so the load completes under the end-of-tile wait
+  // instead of stalling the tile that uses it.
+  const float* kstep = reinterpret_cast<const float*>(a.k_scales) + (FINE ? kt0 / 32 + hh : kt0 / kTK);
+  auto kstep_of = [&](int t) { return QK == QK_INT8 ? kstep[FINE ? 2 * t : t] : 0.0f; };
 
   int ntiles = (NK + kTK - 1) / kTK;
   if (CAUSAL) ntiles = min(ntiles, (qbase + kQT - 1) / kTK + 1);
@@ -637,6 +693,43 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
     }
     return;
   }
+  float ks_cur = kstep_of(0);
+  // FP8 V: the KV head's channel steps, staged in LDS for the epilogue (visible after the
+  // prologue's barrier), so the output stores do not wait on global loads one by one
+  if (PV == PV_FP8 && threadIdx.x < D) vsc[threadIdx.x] = a.v_scales[kvid * D + threadIdx.x];
+  const int last = ntiles - 1;
+  if constexpr (kOneBuf<D, QK, PV>) {
+    // K and V one tile ahead; tile j: prefetch K(j+1), V(j+1) into the buffers tile j-1 used,
+    // then QK(j), softmax and PV(j) from this tile's buffers; barrier
+    issue_k<D, QK>(lk[0], a, kt0, 0, lo, w, lane);
+    issue_v<D, QK>(lv[0], a, kt0, 0, lo, w, lane);
+    wait_vmem();
+    __syncthreads();
+    auto step1 = [&](int j) {
+      const float ks = ks_cur;
+      ks_cur = kstep_of(min(j + 1, last));
+      issue_k<D, QK>(lk[(j + 1) & 1], a, kt0, min(j + 1, last), lo, w, lane);
+      issue_v<D, QK>(lv[(j + 1) & 1], a, kt0, min(j + 1, last), lo, w, lane);
+      if (j < wtiles) {
+        Score<D, QK> Sc;
+        qk_tile<D, QK>(Sc, lk[j & 1], qf, qf4, qsc, lo);
+        float u[32], c, off, lsc;
+        softmax_max<D, QK, CAUSAL, PV, FINE>(st, Sc, lv[j & 1], ks, qstep, a.sm_log2e, j, NK, qw, qrow, hh, u, c, off,
+                                             lsc);
+        softmax_body_pv<D, QK, PV, false>(st, u, c, off, lsc, Sc, lk[(j + 1) & 1], lv[j & 1], qf, qf4, qsc, lo);
+      }
+      wait_vmem();
+      __syncthreads();
+    };
+    int j = 0;
+    for (; j + 1 < ntiles; j += 2) {
+      step1(j);
+      step1(j + 1);
+    }
+    if (j < ntiles) step1(j);
+    fwd_epilogue<D, QK, CAUSAL, DT, PV>(a, st, qi, qrow, hh, vsc);
+    return;
+  }
   issue_k<D, QK>(lk[0], a, kt0, 0, lo, w, lane);
   issue_k<D, QK>(lk[1], a, kt0, min(1, ntiles - 1), lo, w, lane);
   issue_v<D, QK>(lv[0], a, kt0, 0, lo, w, lane);
@@ -652,9 +745,10 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
   // issue QK(j+1) into Sn; softmax + PV of tile j from Sc; barrier.  Prefetch indices are
   // clamped to the last tile, so the loads are unconditional.  Unrolled twice so Sa/Sb
   // alternate without copies.
-  const int last = ntiles - 1;
   constexpr bool IL = !(D == 128 && QK == QK_INT8 && MFMA_IL_D128 == 0);
   auto step = [&](int j, const Score<D, QK>& Sc, Score<D, QK>& Sn) {
+    const float ks = ks_cur;
+    ks_cur = kstep_of(min(j + 1, last));
     issue_k<D, QK>(lk[j & 1], a, kt0, min(j + 2, last), lo, w, lane);
     issue_v<D, QK>(lv[(j + 1) & 1], a, kt0, min(j + 1, last), lo, w, lane);
     uint4 dsr;
@@ -671,7 +765,7 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
     }
     if (j < wtiles) {
       float u[32], c, off, lsc;
-      softmax_max<D, QK, CAUSAL, PV, FINE>(st, Sc, lv[j & 1], kstep, qstep, a.sm_log2e, j, NK, qw, qrow, hh, u, c, off, lsc);
+      softmax_max<D, QK, CAUSAL, PV, FINE>(st, Sc, lv[j & 1], ks, qstep, a.sm_log2e, j, NK, qw, qrow, hh, u, c, off, lsc);
       softmax_body_pv<D, QK, PV, IL>(st, u, c, off, lsc, Sn, lk[(j + 1) & 1], lv[j & 1], qf, qf4, qsc, lo);
     }
     if (QK == QK_MXFP4) store_ds<D, QK, PV>(dsr, lv[(j + 1) & 1], a.sm_log2e);
@@ -685,29 +779,7 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
   }
   if (j < ntiles) step(j, Sa, Sb);
 
-  // ---- epilogue: O / l (FP8: times the V channel step), LSE ----
-  //   FP8 P~ (V in FP8 or MXFP8): O and l both carry the factor 448; MXFP8's V block scales
-  //   are applied inside the MFMA.  MXFP4 P~: O' = sigma O with sigma = 6 exp2(m - mt) and
-  //   l' = 6 sum p, so O / l = O' exp2(mt - m) / l'.
-  const float lt = half_sum(st.l);
-  if (qrow < qi.len) {
-    const float inv = PV != PV_MXFP4 ? 1.0f / lt : fast_exp2(st.mt - st.m) / lt;
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + qi.io0 + (size_t)qrow * qi.ios;
-#pragma unroll
-    for (int c = 0; c < NCB; c++)
-#pragma unroll
-      for (int g = 0; g < 4; g++) {
-        const int ch = 32 * c + 8 * g + 4 * hh;
-        const v4f sc = PV == PV_FP8 ? *reinterpret_cast<const v4f*>(a.v_scales + kvid * D + ch) * inv
-                                    : v4f{inv, inv, inv, inv};
-        const uint32_t lo = pack2_io<DT>(st.O[c][4 * g] * sc[0], st.O[c][4 * g + 1] * sc[1]);
-        const uint32_t hi = pack2_io<DT>(st.O[c][4 * g + 2] * sc[2], st.O[c][4 * g + 3] * sc[3]);
-        *reinterpret_cast<uint2*>(orow + ch) = make_uint2(lo, hi);
-      }
-    if (a.lse && hh == 0)
-      a.lse[qi.lse0 + qrow] =
-          (st.m + __log2f(lt) - (PV != PV_MXFP4 ? G::PLOG2 : kLog2_6)) * kLn2 + a.lse_corr[qi.row0 + qrow];
-  }
+  fwd_epilogue<D, QK, CAUSAL, DT, PV>(a, st, qi, qrow, hh, vsc);
 }
 
 // One 128-query tile per workgroup.  Causal tiles differ in length, so they are dealt longest
@@ -717,10 +789,11 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
 // whole heads, so a head's K/V tiles stay in one L2 (packed sequences: whole KV groups,
 // dealt round-robin so that every XCD gets a share of every sequence).
 template <int D, int QK, bool CAUSAL, int DT, int PV, bool FINE>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, (kOneBuf<D, QK, PV> ? 3 : 2)) void attn_fwd_kernel(FwdArgs a) {
   using G = Geo<D, QK, PV>;
   __shared__ __align__(16) uint8_t lk[2][G::KSTAGE];
   __shared__ __align__(16) uint8_t lv[2][G::VSTAGE];
+  __shared__ __align__(16) float vsc[PV == PV_FP8 ? D : 4];
   const int nqt = a.nqt, BH = a.g.B * a.g.H;
   int bh, qt;
   const int nkv = a.g.B * a.g.Hkv;
@@ -749,7 +822,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     bh = id / nqt;
     qt = id % nqt;
   }
-  run_qtile<D, QK, CAUSAL, DT, PV, FINE>(a, bh / a.g.H, bh % a.g.H, qt, lk, lv);
+  run_qtile<D, QK, CAUSAL, DT, PV, FINE>(a, bh / a.g.H, bh % a.g.H, qt, lk, lv, vsc);
 }
 
 template <int D, int QK, int DT, int PV, bool FINE>

@@ -83,6 +83,21 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
 #endif
 }
 
+// The same 16-byte direct load, hidden from the compiler's tracking of LDS writes.  The builtin
+// form makes the compiler wait for every outstanding vector-memory load (s_waitcnt vmcnt(0))
+// before the next LDS read of any address, which in a prefetching loop exposes the full latency
+// of the load just issued.  Callers of this form order its LDS writes themselves: each wave waits
+// with s_waitcnt vmcnt(0) and the workgroup meets a barrier before any wave reads the bytes, and
+// nothing reads a buffer while a load into it is in flight.  The instruction has no register
+// result (it writes LDS at M0 + 16 lane); the compiler itself puts the wave-uniform base in M0.
+__device__ __forceinline__ void load_lds16_async(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)lds);
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(base) : "memory");
+#endif
+}
+
 // 4-byte direct global -> LDS load: lane L's dword lands at lds + 4 L.
 __device__ __forceinline__ void load_lds4(const void* g, void* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
