@@ -339,7 +339,7 @@ __device__ __forceinline__ void stage_rows(uint8_t* lds, const uint8_t* g, int w
     const int pbase = 256 * i + 64 * w;
     if (pbase < CHUNKS) {
       const int P = pbase + lane, row = P / CH, col = (P % CH) ^ (D == 64 ? swz_row64(row) : (((row >> 1) & 3) | (((row >> 5) & 1) << 2)));
-      load_lds16(g + row * D + col * 16, lds + pbase * 16);
+      load_lds16_async(g + row * D + col * 16, lds + pbase * 16);
     }
   }
 }
@@ -352,7 +352,7 @@ __device__ __forceinline__ void stage_cols(uint8_t* lds, const uint8_t* g, int w
     const int pbase = 256 * i + 64 * w;
     if (pbase < CHUNKS) {
       const int P = pbase + lane, row = P >> 2, col = (P & 3) ^ swz_t64(row);
-      load_lds16(g + row * 64 + col * 16, lds + pbase * 16);
+      load_lds16_async(g + row * 64 + col * 16, lds + pbase * 16);
     }
   }
 }
@@ -453,9 +453,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdPtrs 
     stage_rows<D>(L + TB, bp.do_codes + rb, w, lane);
     stage_cols<D>(L + 2 * TB, bp.doT_codes + tb, w, lane);
     stage_cols<D>(L + 3 * TB, bp.qT_codes + tb, w, lane);
-    if (w == 0 && lane < 16) load_lds16(bp.lse2 + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 16 * lane);
-    if (w == 1 && lane < 16) load_lds16(bp.Dvec + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 256 + 16 * lane);
-    if (w == 2 && lane < 2) load_lds4((lane ? bp.do_step : bp.q_step) + (size_t)bh * nb + qt, L + 4 * TB + 512);
+    if (w == 0 && lane < 16) load_lds16_async(bp.lse2 + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 16 * lane);
+    if (w == 1 && lane < 16) load_lds16_async(bp.Dvec + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 256 + 16 * lane);
+    if (w == 2 && lane < 2) load_lds4_async((lane ? bp.do_step : bp.q_step) + (size_t)bh * nb + qt, L + 4 * TB + 512);
   };
   // one query tile: S, dP on MFMA; P~ and dS on the vector unit; dV^T, dK^T on MFMA
   auto tile = [&](const uint8_t* L, int qt, auto masked_tag) {
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdPtrs bp
     stage_rows<D>(L, reinterpret_cast<const uint8_t*>(bp.k_codes) + rb, w, lane);
     stage_rows<D>(L + TB, bp.v_codes + rb, w, lane);
     stage_cols<D>(L + 2 * TB, bp.kT_codes + tb, w, lane);
-    if (w == 0 && lane < 2) load_lds4((lane ? bp.v_step : bp.k_step) + (size_t)bh * nb + kt, L + 3 * TB);
+    if (w == 0 && lane < 2) load_lds4_async((lane ? bp.v_step : bp.k_step) + (size_t)bh * nb + kt, L + 3 * TB);
   };
   auto tile = [&](const uint8_t* L, int kt, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;

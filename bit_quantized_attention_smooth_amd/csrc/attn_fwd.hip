@@ -72,7 +72,8 @@ struct FwdArgs {
 // of the next tile's QK products inside one wave.  Measured: N = 8192 non-causal 712 -> 666 us,
 // the causal 4096-token prefill 110 -> 102 us.
 template <int D, int QK, int PV>
-constexpr bool kOneBuf = FWD_ONEBUF_D128 && D == 128 && QK == QK_INT8 && PV == PV_FP8;
+constexpr bool kOneBuf = FWD_ONEBUF_D128 && D == 128 &&
+                         ((QK == QK_INT8 && PV == PV_FP8) || (QK == QK_MXFP4 && (PV == PV_FP8 || PV == PV_MXFP8)));
 constexpr int kTK = 64;      // keys per tile (= the INT8 K block)
 constexpr int kQT = 128;     // queries per workgroup pass
 
@@ -350,6 +351,18 @@ __device__ __forceinline__ float tree_max_f(float* x) {
     for (int r = 0; r < w; r++) x[r] = fmaxf(x[r], x[r + w]);
   return x[0];
 }
+// The maximum of 32 values as a tree of three-operand maxima (v_max3_f32): 11, then 4, 2 and 1
+// values, 17 instructions against 31 two-operand ones, still only four deep.
+__device__ __forceinline__ float tree_max3_32(const float* x) {
+  float a[11], b[4];
+#pragma unroll
+  for (int k = 0; k < 10; k++) a[k] = fmaxf(fmaxf(x[3 * k], x[3 * k + 1]), x[3 * k + 2]);
+  a[10] = fmaxf(x[30], x[31]);
+#pragma unroll
+  for (int k = 0; k < 3; k++) b[k] = fmaxf(fmaxf(a[3 * k], a[3 * k + 1]), a[3 * k + 2]);
+  b[3] = fmaxf(a[9], a[10]);
+  return fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3]));
+}
 template <int N>
 __device__ __forceinline__ float tree_sum_f(float* x) {
 #pragma unroll
@@ -451,10 +464,7 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
 #pragma unroll
       for (int i = 0; i < 32; i++) u[i] = KeyMap<PV>::lane_key(i) < lim ? u[i] : -INFINITY;
     }
-    float mx[32];
-#pragma unroll
-    for (int i = 0; i < 32; i++) mx[i] = u[i];
-    mt = half_max(tree_max_f<32>(mx));
+    mt = half_max(tree_max3_32(u));
   }
   const float mnew = fmaxf(st.m, mt);
   const float mref = mnew == -INFINITY ? 0.0f : mnew;
@@ -703,6 +713,7 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
     // then QK(j), softmax and PV(j) from this tile's buffers; barrier
     issue_k<D, QK>(lk[0], a, kt0, 0, lo, w, lane);
     issue_v<D, QK>(lv[0], a, kt0, 0, lo, w, lane);
+    if (QK == QK_MXFP4) store_ds<D, QK, PV>(load_ds(a, ds0, 0), lv[0], a.sm_log2e);
     wait_vmem();
     __syncthreads();
     auto step1 = [&](int j) {
@@ -710,6 +721,8 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
       ks_cur = kstep_of(min(j + 1, last));
       issue_k<D, QK>(lk[(j + 1) & 1], a, kt0, min(j + 1, last), lo, w, lane);
       issue_v<D, QK>(lv[(j + 1) & 1], a, kt0, min(j + 1, last), lo, w, lane);
+      uint4 dsr;
+      if (QK == QK_MXFP4) dsr = load_ds(a, ds0, min(j + 1, last));
       if (j < wtiles) {
         Score<D, QK> Sc;
         qk_tile<D, QK>(Sc, lk[j & 1], qf, qf4, qsc, lo);
@@ -718,6 +731,7 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
                                              lsc);
         softmax_body_pv<D, QK, PV, false>(st, u, c, off, lsc, Sc, lk[(j + 1) & 1], lv[j & 1], qf, qf4, qsc, lo);
       }
+      if (QK == QK_MXFP4) store_ds<D, QK, PV>(dsr, lv[(j + 1) & 1], a.sm_log2e);
       wait_vmem();
       __syncthreads();
     };

@@ -98,6 +98,15 @@ __device__ __forceinline__ void load_lds16_async(const void* g, void* lds) {
 #endif
 }
 
+// The 4-byte form of load_lds16_async (lane L's dword lands at lds + 4 L), same contract.
+__device__ __forceinline__ void load_lds4_async(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)lds);
+  asm volatile("global_load_lds_dword %0, off" : : "v"(g), "{m0}"(base) : "memory");
+#endif
+}
+
 // 4-byte direct global -> LDS load: lane L's dword lands at lds + 4 L.
 __device__ __forceinline__ void load_lds4(const void* g, void* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
