@@ -53,6 +53,12 @@ def lib():
     return _lib
 
 
+def set_threads(n):
+    """Host threads of the oracle's parallel loops (n <= 0 leaves them as they are); returns the
+    count in effect.  Results do not depend on it."""
+    return int(lib().or_set_threads(int(n)))
+
+
 def _p(a):
     return a.ctypes.data_as(ctypes.c_void_p)
 

@@ -48,6 +48,24 @@
 
 #define OR_API __attribute__((visibility("default")))
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Host threads the oracle's parallel loops use (n <= 0: the OpenMP default); returns the
+ * count in effect.  Timing aid for the CPU baseline; no effect on any result. */
+OR_API int or_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 /* ------------------------------------------------------------------ */
 /* Widening of the 16-bit input formats (exact).                       */
 /* ------------------------------------------------------------------ */
