@@ -206,6 +206,53 @@ __device__ __forceinline__ void put_v_f16(uint16_t* s_vt, int rl, int c0, const 
   for (int i = 0; i < 8; i++) s_vt[(c0 + i) * 64 + rl] = __builtin_bit_cast(uint16_t, (_Float16)x[i]);
 }
 
+// FP8 V of one 64-token block of a fixed-length instance (rows t0 .. t0 + 63 of `vin`, zero
+// codes past N) into its [D][64] tile of v_codes at `dst`, through an LDS tile of 68-byte rows.
+// Thread (c0, g) converts rows NP g .. NP g + NP - 1 at channels c0 .. c0 + 7, so a channel's NP
+// codes form one 32- or 16-bit word and a wave's LDS writes spread over the banks (one byte per
+// write, as the tile's natural order gives, puts 16 lanes on one bank).  Same codes as
+// put_v_fp8: every element is the same division and conversion.  Ends with a barrier and the
+// tile's coalesced 16-byte stores.
+constexpr int kVRow = 68;
+template <int DT, int D>
+__device__ __forceinline__ void v_block_fp8(const uint16_t* vin, int t0, int N, int c0, int g, const float* dv,
+                                            const float* rv, uint8_t* s_vt, uint8_t* dst) {
+  constexpr int NP = 64 / (256 / (D / 8));
+  uint32_t cw[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) cw[i] = 0;
+#pragma unroll
+  for (int j = 0; j < NP; j += 2) {
+    float x0[8], x1[8];
+    const int ra = t0 + NP * g + j;
+    if (ra < N) load8<DT>(vin + (size_t)ra * D + c0, x0);
+    else
+      for (int i = 0; i < 8; i++) x0[i] = 0.0f;
+    if (ra + 1 < N) load8<DT>(vin + (size_t)(ra + 1) * D + c0, x1);
+    else
+      for (int i = 0; i < 8; i++) x1[i] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float a = dv[i] == 0.0f ? 0.0f : div_rn(x0[i], dv[i], rv[i]);
+      const float b = dv[i] == 0.0f ? 0.0f : div_rn(x1[i], dv[i], rv[i]);
+      cw[i] = (uint32_t)(j == 0 ? __builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)cw[i], false)
+                                : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)cw[i], true));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    if (NP == 4) *reinterpret_cast<uint32_t*>(s_vt + (c0 + i) * kVRow + 4 * g) = cw[i];
+    else *reinterpret_cast<uint16_t*>(s_vt + (c0 + i) * kVRow + 2 * g) = (uint16_t)cw[i];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < D * 4; c += 256) {
+    const uint8_t* src = s_vt + (c / 4) * kVRow + 16 * (c % 4);
+    const uint4 w = make_uint4(*reinterpret_cast<const uint32_t*>(src), *reinterpret_cast<const uint32_t*>(src + 4),
+                               *reinterpret_cast<const uint32_t*>(src + 8), *reinterpret_cast<const uint32_t*>(src + 12));
+    *reinterpret_cast<uint4*>(dst + c * 16) = w;
+  }
+}
+
 // INT8 Q / K codes and FP8 (PV == PV_FP8) or fp16 (PV_F16) V, or no V at all (PV_NONE: the
 // backward's own quantization of Q and K).  grid (Np/64, BH), 256 threads.
 template <int DT, int D, int PV, bool FINE>
@@ -220,7 +267,7 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
   __shared__ uint32_t s_red[8];
   constexpr bool HASV = PV != PV_NONE;
   constexpr int VB = PV == PV_F16 ? 2 : 1;   // bytes per V element
-  __shared__ __align__(16) uint8_t s_vt[HASV ? D * 64 * VB : 16];
+  __shared__ __align__(16) uint8_t s_vt[PV == PV_FP8 ? D * kVRow : HASV ? D * 64 * VB : 16];
   if (tid < D) {
     const float mu = chunk_mean(qp.sums, 0, BH, bh, D, tid, N);
     const float dvs = HASV ? chunk_amax(qp.amax_v, BH, bh, D, tid) / 448.0f : 0.0f;
@@ -248,12 +295,9 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
       float xv[8];
       load8<DT>(q + base + (size_t)row * D + c0, xq[p]);
       load8<DT>(k + base + (size_t)row * D + c0, xk[p]);
-      if (HASV) {
+      if (PV == PV_F16) {
         load8<DT>(v + base + (size_t)row * D + c0, xv);
-        if (PV == PV_F16)
-          put_v_f16(reinterpret_cast<uint16_t*>(s_vt), rl, c0, xv);
-        else
-          put_v_fp8(s_vt, rl, c0, xv, dv, rv);
+        put_v_f16(reinterpret_cast<uint16_t*>(s_vt), rl, c0, xv);
       }
       float cs = 0.0f;
 #pragma unroll
@@ -273,10 +317,7 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
       for (int i = 0; i < 8; i++) {
         xq[p][i] = 0.0f;
         xk[p][i] = 0.0f;
-        if (PV == PV_F16)
-          reinterpret_cast<uint16_t*>(s_vt)[(c0 + i) * 64 + rl] = 0;
-        else if (HASV)
-          s_vt[(c0 + i) * 64 + rl] = 0;
+        if (PV == PV_F16) reinterpret_cast<uint16_t*>(s_vt)[(c0 + i) * 64 + rl] = 0;
       }
     }
   }
@@ -333,9 +374,13 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
     *reinterpret_cast<uint2*>(qp.k_codes + off) = make_uint2(wk[0], wk[1]);
   }
   if (!HASV) return;
-  __syncthreads();
   // V tile [D][64] -> v_codes[bh][blk][D][64], coalesced 16-byte stores
   uint8_t* dst = qp.v_codes + ((size_t)bh * (Np / 64) + blk) * D * 64 * VB;
+  if (PV == PV_FP8) {
+    v_block_fp8<DT, D>(v + base, t0, N, c0, r0, dv, rv, s_vt, dst);
+    return;
+  }
+  __syncthreads();
   for (int c = tid; c < D * 4 * VB; c += 256)
     *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(s_vt + c * 16);
 }
@@ -352,7 +397,7 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
   const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
   const size_t base = (size_t)bh * N * D;
   __shared__ float s_mk[D], s_mq[D];
-  __shared__ __align__(16) uint8_t s_vt[PV == PV_FP8 ? D * 64 : 1];
+  __shared__ __align__(16) uint8_t s_vt[PV == PV_FP8 ? D * kVRow : 1];
   constexpr bool MXV = PV == PV_MXFP4 || PV == PV_MXFP8;
   __shared__ float s_vf[MXV ? 64 : 1][MXV ? D + 1 : 1];
   __shared__ float s_dv[PV == PV_FP8 ? D : 1];
@@ -388,7 +433,7 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
     if (row < N) {
       load8<DT>(q + base + (size_t)row * D + c0, xq);
       load8<DT>(k + base + (size_t)row * D + c0, xk);
-      load8<DT>(v + base + (size_t)row * D + c0, xv);
+      if (PV != PV_FP8) load8<DT>(v + base + (size_t)row * D + c0, xv);
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         cs += (double)xq[i] * (double)s_mk[c0 + i];
@@ -430,24 +475,15 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
       if (!QB) qp.delta_s[(size_t)bh * Np + row] = row < N ? (float)ds : 0.0f;
       if (row < N) qp.lse_corr[(size_t)bh * N + row] = (float)(sm * cs);
     }
-    if (PV == PV_FP8) {
-      if (row < N) {
-        put_v_fp8(s_vt, rl, c0, xv, dv, rv);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; i++) s_vt[(c0 + i) * 64 + rl] = 0;
-      }
-    } else {
+    if (PV != PV_FP8) {
 #pragma unroll
       for (int i = 0; i < 8; i++) s_vf[rl][c0 + i] = xv[i];
     }
   }
-  __syncthreads();
   if (PV == PV_FP8) {
-    uint8_t* dst = qp.v_codes + ((size_t)bh * (Np / 64) + blk) * D * 64;
-    for (int c = tid; c < D * 4; c += 256)
-      *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(s_vt + c * 16);
+    v_block_fp8<DT, D>(v + base, t0, N, c0, r0, dv, rv, s_vt, qp.v_codes + ((size_t)bh * (Np / 64) + blk) * D * 64);
   } else {
+    __syncthreads();
     // one thread per (channel, 32-token group)
     for (int w = tid; w < D * 2; w += 256) {
       const int ch = w % D, g = w / D;
