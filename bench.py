@@ -96,10 +96,12 @@ def counter_summary(sq_dir, fetch_dir, write_dir, out_path):
              "SQ_BUSY_CYCLES is summed over the 32 shader engines and SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs,",
              "so MFMA busy = MFMA_BUSY / (1024 * BUSY / 32): the share of the kernel's time the matrix cores of",
              "an average SIMD were busy.  Co-exec is the share of MFMA busy time that overlapped vector issue.",
+             "VALU busy = 4 SQ_ACTIVE_INST_VALU / (1024 * BUSY / 32) (the counter is in quad-cycles): the share",
+             "of the kernel's time an average SIMD issued vector instructions.",
              "Template arguments: <head dim, QK format (1 INT8, 3 MXFP4), causal, I/O dtype, P~V format (2 FP8,",
              "3 MXFP4, 4 MXFP8, 5 fp16), finer INT8 steps>.", "",
-             "| kernel | workgroups | dispatches | MFMA busy | co-exec | VALU instr. per MFMA | wait share of wave cycles |",
-             "|---|---|---|---|---|---|---|"]
+             "| kernel | workgroups | dispatches | MFMA busy | VALU busy | co-exec | VALU instr. per MFMA | wait share of wave cycles |",
+             "|---|---|---|---|---|---|---|---|"]
     def sq_rows(match):
         for (k, g), cs in sorted(sq.items(), key=lambda kv: (kv[0][0], -kv[0][1])):
             if not match(k) or "SQ_BUSY_CYCLES" not in cs:
@@ -107,17 +109,19 @@ def counter_summary(sq_dir, fetch_dir, write_dir, out_path):
             busy = mean(cs["SQ_BUSY_CYCLES"]) / 32.0
             mfma = mean(cs.get("SQ_VALU_MFMA_BUSY_CYCLES", [0])) / 1024.0
             coex = mean(cs.get("SQ_VALU_MFMA_COEXEC_CYCLES", [0])) / 1024.0
+            valu = 4.0 * mean(cs.get("SQ_ACTIVE_INST_VALU", [0])) / 1024.0
             vpm = mean(cs.get("SQ_INSTS_VALU", [0])) / max(1.0, mean(cs.get("SQ_INSTS_MFMA", [1])))
             wait = mean(cs.get("SQ_WAIT_ANY", [0])) / max(1.0, mean(cs.get("SQ_WAVE_CYCLES", [1])))
             lines.append(f"| `{k}` | {g} | {len(cs['SQ_BUSY_CYCLES'])} | {100 * mfma / busy:.1f} % | "
-                         f"{100 * coex / max(mfma, 1e-9):.0f} % | {vpm:.1f} | {100 * wait:.0f} % |")
+                         f"{100 * valu / busy:.1f} % | {100 * coex / max(mfma, 1e-9):.0f} % | {vpm:.1f} | "
+                         f"{100 * wait:.0f} % |")
 
     sq_rows(lambda k: "attn_fwd_kernel" in k)
     lines += ["", "## Backward kernels (training workloads B=8 H=16 N=2048, causal; d = 64 and 128)", "",
               "Template arguments: <head dim, causal, I/O dtype>.  At d = 128 one workgroup runs per CU (one wave",
               "per SIMD).", "",
-              "| kernel | workgroups | dispatches | MFMA busy | co-exec | VALU instr. per MFMA | wait share of wave cycles |",
-              "|---|---|---|---|---|---|---|"]
+              "| kernel | workgroups | dispatches | MFMA busy | VALU busy | co-exec | VALU instr. per MFMA | wait share of wave cycles |",
+              "|---|---|---|---|---|---|---|---|"]
     sq_rows(lambda k: "bwd_dq_kernel" in k or "bwd_dkdv_kernel" in k)
     fe, fdur = dispatch_counters(fetch_dir)
     wr, _ = dispatch_counters(write_dir)

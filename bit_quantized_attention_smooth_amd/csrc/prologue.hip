@@ -225,12 +225,13 @@ __device__ __forceinline__ void v_block_fp8(const uint16_t* vin, int t0, int N, 
   for (int j = 0; j < NP; j += 2) {
     float x0[8], x1[8];
     const int ra = t0 + NP * g + j;
-    if (ra < N) load8<DT>(vin + (size_t)ra * D + c0, x0);
-    else
-      for (int i = 0; i < 8; i++) x0[i] = 0.0f;
-    if (ra + 1 < N) load8<DT>(vin + (size_t)(ra + 1) * D + c0, x1);
-    else
-      for (int i = 0; i < 8; i++) x1[i] = 0.0f;
+    load8<DT>(vin + (size_t)min(ra, N - 1) * D + c0, x0);
+    load8<DT>(vin + (size_t)min(ra + 1, N - 1) * D + c0, x1);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      x0[i] = ra < N ? x0[i] : 0.0f;
+      x1[i] = ra + 1 < N ? x1[i] : 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       const float a = dv[i] == 0.0f ? 0.0f : div_rn(x0[i], dv[i], rv[i]);
@@ -291,10 +292,12 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_kernel(const uint16_t* __r
 #pragma unroll
   for (int p = 0; p < NP; p++) {
     const int rl = r0 + p * RP, row = t0 + rl;
+    // every row loads (rows past N read row N - 1, then count as zero), so the loads of all
+    // passes can be in flight together
+    load8<DT>(q + base + (size_t)min(row, N - 1) * D + c0, xq[p]);
+    load8<DT>(k + base + (size_t)min(row, N - 1) * D + c0, xk[p]);
     if (row < N) {
       float xv[8];
-      load8<DT>(q + base + (size_t)row * D + c0, xq[p]);
-      load8<DT>(k + base + (size_t)row * D + c0, xk[p]);
       if (PV == PV_F16) {
         load8<DT>(v + base + (size_t)row * D + c0, xv);
         put_v_f16(reinterpret_cast<uint16_t*>(s_vt), rl, c0, xv);
