@@ -70,10 +70,12 @@ struct FwdArgs {
 // INT8 QK and FP8 P~V the kernel is bound by vector issue, and a lone wave issues vector work at
 // half the SIMD's rate, so a third wave that keeps two of them ready pays more than the overlap
 // of the next tile's QK products inside one wave.  Measured: N = 8192 non-causal 712 -> 666 us,
-// the causal 4096-token prefill 110 -> 102 us.
+// the causal 4096-token prefill 110 -> 102 us; MXFP4 QK and P~V at N = 8192 2724 -> 2629 us.
+// (fp16 P~V keeps two buffers: its 16-bit P~ operands do not fit three waves.)
 template <int D, int QK, int PV>
 constexpr bool kOneBuf = FWD_ONEBUF_D128 && D == 128 &&
-                         ((QK == QK_INT8 && PV == PV_FP8) || (QK == QK_MXFP4 && (PV == PV_FP8 || PV == PV_MXFP8)));
+                         ((QK == QK_INT8 && PV == PV_FP8) ||
+                          (QK == QK_MXFP4 && (PV == PV_FP8 || PV == PV_MXFP8 || PV == PV_MXFP4)));
 constexpr int kTK = 64;      // keys per tile (= the INT8 K block)
 constexpr int kQT = 128;     // queries per workgroup pass
 
@@ -378,6 +380,7 @@ struct RowState {
   v16f O[D / 32];
   float m, l;
   float mt;   // MXFP4 P~: the tile max that fixes the frame of O (see softmax_max)
+  float um;   // MXFP4 P~: the largest of this lane's scaled scores in the current tile
 };
 
 // Softmax of tile j from its score registers, then O^T += V^T P~^T.
@@ -464,7 +467,8 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
 #pragma unroll
       for (int i = 0; i < 32; i++) u[i] = KeyMap<PV>::lane_key(i) < lim ? u[i] : -INFINITY;
     }
-    mt = half_max(tree_max3_32(u));
+    st.um = tree_max3_32(u);
+    mt = half_max(st.um);
   }
   const float mnew = fmaxf(st.m, mt);
   const float mref = mnew == -INFINITY ? 0.0f : mnew;
@@ -556,24 +560,24 @@ __device__ __forceinline__ void softmax_body_pv(RowState<D>& st, const float* u,
         st.O[cb] = mfma_f8(va, pb, st.O[cb]);
     }
   } else {
-    float pf[32], am[8];
-#pragma unroll
-    for (int i = 0; i < 32; i += 4) {
-      pf[i] = fast_exp2(fmaf(u[i], c, off));
-      pf[i + 1] = fast_exp2(fmaf(u[i + 1], c, off));
-      pf[i + 2] = fast_exp2(fmaf(u[i + 2], c, off));
-      pf[i + 3] = fast_exp2(fmaf(u[i + 3], c, off));
-      ps[i / 4] = (pf[i] + pf[i + 1]) + (pf[i + 2] + pf[i + 3]);
-      am[i / 4] = fmaxf(fmaxf(pf[i], pf[i + 1]), fmaxf(pf[i + 2], pf[i + 3]));
-    }
-    st.l = fmaf(lsc, tree_sum_f<8>(ps), st.l);
-    const int sb = (int)mx_fp4_scale_byte(tree_max_f<8>(am));
+    // the block maximum of the lane's 32 weights is the weight of its largest score (the FMA
+    // and exp2 do not decrease), so the E8M0 scale is fixed before any weight is formed and
+    // the weights are packed eight at a time
+    const int sb = (int)mx_fp4_scale_byte(fast_exp2(fmaf(st.um, c, off)));
     // byte 0 (an all-zero block, e.g. keys past the causal diagonal): codes 0 under any scale,
     // so convert with 1 rather than the subnormal 2^-127
     const float scl = sb == 0 ? 1.0f : e8m0_to_float((unsigned)sb);
     v8i pb = v8i{};
 #pragma unroll
-    for (int k = 0; k < 4; k++) pb[k] = (int)pack_fp4x8(pf + 8 * k, scl);
+    for (int k = 0; k < 4; k++) {
+      float pf[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) pf[i] = fast_exp2(fmaf(u[8 * k + i], c, off));
+      ps[2 * k] = (pf[0] + pf[1]) + (pf[2] + pf[3]);
+      ps[2 * k + 1] = (pf[4] + pf[5]) + (pf[6] + pf[7]);
+      pb[k] = (int)pack_fp4x8(pf, scl);
+    }
+    st.l = fmaf(lsc, tree_sum_f<8>(ps), st.l);
 #pragma unroll
     for (int cb = 0; cb < NCB; cb++) {
       const v4i v0 = *reinterpret_cast<const v4i*>(vstage + lo.vop_at(cb, 0));
