@@ -76,6 +76,15 @@ template <int D, int QK, int PV>
 constexpr bool kOneBuf = FWD_ONEBUF_D128 && D == 128 &&
                          ((QK == QK_INT8 && PV == PV_FP8) ||
                           (QK == QK_MXFP4 && (PV == PV_FP8 || PV == PV_MXFP8 || PV == PV_MXFP4)));
+// MXFP4 QK in the one-buffer kernels: the per-key smoothing term dS is the initial accumulator
+// of the QK products (S^T = dS + K Q^T: the C operand of the first MFMA holds each output row's
+// dS), so a score takes one FMA (p = exp2(S' sm log2 e + off)) instead of two, and the row max
+// is taken on S' before scaling.  The only new rounding, of S + dS in the matrix core's fp32
+// accumulation, is bounded by 2^-24 (|S| + |dS|), which the P~ decision's admissible window
+// covers sixteen times over.  (The two-buffer kernels issue QK(j+1) before tile j+1's dS is in
+// LDS, so they keep the FMA.)
+template <int D, int QK, int PV>
+constexpr bool kDsAcc = QK == QK_MXFP4 && kOneBuf<D, QK, PV>;
 constexpr int kTK = 64;      // keys per tile (= the INT8 K block)
 constexpr int kQT = 128;     // queries per workgroup pass
 
@@ -314,9 +323,11 @@ struct Score {
   v16f sf[QK == QK_MXFP4 ? 2 : 1];
 };
 
-template <int D, int QK, typename LO>
+// dsl (MXFP4 with kDsAcc): this lane's dS values in LDS (the tile's dS floats from the lane
+// half's first key), the initial accumulator of each subtile; null otherwise.
+template <int D, int QK, typename LO, int KS = 16>
 __device__ __forceinline__ void qk_tile(Score<D, QK>& S, const uint8_t* lk, const v4i* qf, const v8i* qf4,
-                                        const int* qsc, const LO& lo) {
+                                        const int* qsc, const LO& lo, const float* dsl = nullptr) {
   using G = Geo<D, QK>;
 #pragma unroll
   for (int s = 0; s < 2; s++) {
@@ -330,6 +341,14 @@ __device__ __forceinline__ void qk_tile(Score<D, QK>& S, const uint8_t* lk, cons
       S.si[s] = acc;
     } else {
       v16f acc = v16f{};
+      if (dsl) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const v4f dv = *reinterpret_cast<const v4f*>(dsl + KS * s + r);
+#pragma unroll
+          for (int i = 0; i < 4; i++) acc[r + i] = dv[i];
+        }
+      }
 #pragma unroll
       for (int c = 0; c < G::NQF; c++) {
         const v4i k4 = *reinterpret_cast<const v4i*>(lk + lo.kop_at(s, c));
@@ -450,25 +469,37 @@ __device__ __forceinline__ void softmax_max(RowState<D>& st, const Score<D, QK>&
       }
     }
   } else {
-    // dS arrives pre-multiplied by sm * log2 e; u = S * sm * log2 e + dS * sm * log2 e, c = 1
-    const float* dsl = reinterpret_cast<const float*>(vstage + G::DSOFF) + KeyMap<PV>::KH * hh;
+    if (kDsAcc<D, QK, PV>) {
+      // the scores already hold dS (the QK accumulator's initial value): u = S + dS, and the
+      // positive scale c = sm log2 e applies with the exp's offset, as c does on the INT8 path
 #pragma unroll
-    for (int s = 0; s < 2; s++)
+      for (int s = 0; s < 2; s++)
 #pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        const v4f dv = *reinterpret_cast<const v4f*>(dsl + KeyMap<PV>::KS * s + r);
+        for (int r = 0; r < 16; r++) u[16 * s + r] = Sc.sf[s][r];
+      c = sm_log2e;
+    } else {
+      // dS arrives pre-multiplied by sm * log2 e; u = S * sm * log2 e + dS * sm * log2 e, c = 1
+      const float* dsl = reinterpret_cast<const float*>(vstage + G::DSOFF) + KeyMap<PV>::KH * hh;
 #pragma unroll
-        for (int i = 0; i < 4; i++) u[16 * s + r + i] = fmaf(Sc.sf[s][r + i], sm_log2e, dv[i]);
-      }
-    c = 1.0f;
+      for (int s = 0; s < 2; s++)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const v4f dv = *reinterpret_cast<const v4f*>(dsl + KeyMap<PV>::KS * s + r);
+#pragma unroll
+          for (int i = 0; i < 4; i++) u[16 * s + r + i] = fmaf(Sc.sf[s][r + i], sm_log2e, dv[i]);
+        }
+      c = 1.0f;
+    }
     if (need_mask) {
       asm volatile("" ::: "memory");
       const int lim = (CAUSAL ? min(N, qrow + 1) : N) - (kbase + KeyMap<PV>::KH * hh);
 #pragma unroll
       for (int i = 0; i < 32; i++) u[i] = KeyMap<PV>::lane_key(i) < lim ? u[i] : -INFINITY;
     }
+    // lane max of u (MXFP4 P~ takes its block scale from it with the same c and offset as the
+    // weights); the tile max in the scaled units (c > 0 keeps the order; c = 1 without kDsAcc)
     st.um = tree_max3_32(u);
-    mt = half_max(st.um);
+    mt = half_max(st.um) * c;
   }
   const float mnew = fmaxf(st.m, mt);
   const float mref = mnew == -INFINITY ? 0.0f : mnew;
@@ -717,7 +748,9 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
     // then QK(j), softmax and PV(j) from this tile's buffers; barrier
     issue_k<D, QK>(lk[0], a, kt0, 0, lo, w, lane);
     issue_v<D, QK>(lv[0], a, kt0, 0, lo, w, lane);
-    if (QK == QK_MXFP4) store_ds<D, QK, PV>(load_ds(a, ds0, 0), lv[0], a.sm_log2e);
+    // kDsAcc: dS unscaled (the QK accumulator adds it to S before the scale)
+    const float ds_scale = kDsAcc<D, QK, PV> ? 1.0f : a.sm_log2e;
+    if (QK == QK_MXFP4) store_ds<D, QK, PV>(load_ds(a, ds0, 0), lv[0], ds_scale);
     wait_vmem();
     __syncthreads();
     auto step1 = [&](int j) {
@@ -729,13 +762,15 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
       if (QK == QK_MXFP4) dsr = load_ds(a, ds0, min(j + 1, last));
       if (j < wtiles) {
         Score<D, QK> Sc;
-        qk_tile<D, QK>(Sc, lk[j & 1], qf, qf4, qsc, lo);
+        qk_tile<D, QK, decltype(lo), KeyMap<PV>::KS>(
+            Sc, lk[j & 1], qf, qf4, qsc, lo,
+            kDsAcc<D, QK, PV> ? reinterpret_cast<const float*>(lv[j & 1] + G::DSOFF) + KeyMap<PV>::KH * hh : nullptr);
         float u[32], c, off, lsc;
         softmax_max<D, QK, CAUSAL, PV, FINE>(st, Sc, lv[j & 1], ks, qstep, a.sm_log2e, j, NK, qw, qrow, hh, u, c, off,
                                              lsc);
         softmax_body_pv<D, QK, PV, false>(st, u, c, off, lsc, Sc, lk[(j + 1) & 1], lv[j & 1], qf, qf4, qsc, lo);
       }
-      if (QK == QK_MXFP4) store_ds<D, QK, PV>(dsr, lv[(j + 1) & 1], a.sm_log2e);
+      if (QK == QK_MXFP4) store_ds<D, QK, PV>(dsr, lv[(j + 1) & 1], ds_scale);
       wait_vmem();
       __syncthreads();
     };
