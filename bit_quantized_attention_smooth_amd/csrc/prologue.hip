@@ -185,17 +185,6 @@ __device__ __forceinline__ int8_t int8_code(float x, float step, float r) {
   return (int8_t)n;
 }
 
-// Writes this thread's 8 FP8 V codes of token row `rl` into the [D][64] LDS transpose tile.
-__device__ __forceinline__ void put_v_fp8(uint8_t* s_vt, int rl, int c0, const float* x, const float* dv, const float* rv) {
-#pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    const float a = dv[i] == 0.0f ? 0.0f : div_rn(x[i], dv[i], rv[i]);
-    const float b = dv[i + 1] == 0.0f ? 0.0f : div_rn(x[i + 1], dv[i + 1], rv[i + 1]);
-    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    s_vt[(c0 + i) * 64 + rl] = (uint8_t)(w & 0xff);
-    s_vt[(c0 + i + 1) * 64 + rl] = (uint8_t)((w >> 8) & 0xff);
-  }
-}
 
 // Fixed-length problems without grouped heads (every instance N tokens, query head bh reads
 // KV instance bh): the streamlined codes kernels.
@@ -206,17 +195,18 @@ __device__ __forceinline__ void put_v_f16(uint16_t* s_vt, int rl, int c0, const 
   for (int i = 0; i < 8; i++) s_vt[(c0 + i) * 64 + rl] = __builtin_bit_cast(uint16_t, (_Float16)x[i]);
 }
 
-// FP8 V of one 64-token block of a fixed-length instance (rows t0 .. t0 + 63 of `vin`, zero
-// codes past N) into its [D][64] tile of v_codes at `dst`, through an LDS tile of 68-byte rows.
-// Thread (c0, g) converts rows NP g .. NP g + NP - 1 at channels c0 .. c0 + 7, so a channel's NP
-// codes form one 32- or 16-bit word and a wave's LDS writes spread over the banks (one byte per
-// write, as the tile's natural order gives, puts 16 lanes on one bank).  Same codes as
-// put_v_fp8: every element is the same division and conversion.  Ends with a barrier and the
+// FP8 V of one 64-token block into its [D][64] tile of v_codes at `dst` (code = E4M3 of v over
+// the channel step, zero past the instance's end), through an LDS tile of 68-byte rows.  Thread
+// (c0, g) converts rows NP g .. NP g + NP - 1 at channels c0 .. c0 + 7, so a channel's NP codes
+// form one 32- or 16-bit word and a wave's LDS writes spread over the banks (one byte per write,
+// as the tile's natural order gives, puts 16 lanes on one bank).  Ends with a barrier and the
 // tile's coalesced 16-byte stores.
 constexpr int kVRow = 68;
-template <int DT, int D>
-__device__ __forceinline__ void v_block_fp8(const uint16_t* vin, int t0, int N, int c0, int g, const float* dv,
-                                            const float* rv, uint8_t* s_vt, uint8_t* dst) {
+// row8(j, x): the 8 inputs at channels c0 .. c0 + 7 of the block's token row NP g + j (zeros
+// past the instance's end)
+template <int D, typename RowLoad>
+__device__ __forceinline__ void v_block_fp8_rows(RowLoad row8, int c0, int g, const float* dv, const float* rv,
+                                                 uint8_t* s_vt, uint8_t* dst) {
   constexpr int NP = 64 / (256 / (D / 8));
   uint32_t cw[8];
 #pragma unroll
@@ -224,14 +214,8 @@ __device__ __forceinline__ void v_block_fp8(const uint16_t* vin, int t0, int N, 
 #pragma unroll
   for (int j = 0; j < NP; j += 2) {
     float x0[8], x1[8];
-    const int ra = t0 + NP * g + j;
-    load8<DT>(vin + (size_t)min(ra, N - 1) * D + c0, x0);
-    load8<DT>(vin + (size_t)min(ra + 1, N - 1) * D + c0, x1);
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      x0[i] = ra < N ? x0[i] : 0.0f;
-      x1[i] = ra + 1 < N ? x1[i] : 0.0f;
-    }
+    row8(j, x0);
+    row8(j + 1, x1);
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       const float a = dv[i] == 0.0f ? 0.0f : div_rn(x0[i], dv[i], rv[i]);
@@ -252,6 +236,19 @@ __device__ __forceinline__ void v_block_fp8(const uint16_t* vin, int t0, int N, 
                                *reinterpret_cast<const uint32_t*>(src + 8), *reinterpret_cast<const uint32_t*>(src + 12));
     *reinterpret_cast<uint4*>(dst + c * 16) = w;
   }
+}
+// A fixed-length instance: rows t0 .. t0 + 63 of `vin`, zero past N.
+template <int DT, int D>
+__device__ __forceinline__ void v_block_fp8(const uint16_t* vin, int t0, int N, int c0, int g, const float* dv,
+                                            const float* rv, uint8_t* s_vt, uint8_t* dst) {
+  constexpr int NP = 64 / (256 / (D / 8));
+  auto row8 = [&](int j, float* x) {
+    const int ra = t0 + NP * g + j;
+    load8<DT>(vin + (size_t)min(ra, N - 1) * D + c0, x);
+#pragma unroll
+    for (int i = 0; i < 8; i++) x[i] = ra < N ? x[i] : 0.0f;
+  };
+  v_block_fp8_rows<D>(row8, c0, g, dv, rv, s_vt, dst);
 }
 
 // INT8 Q / K codes and FP8 (PV == PV_FP8) or fp16 (PV_F16) V, or no V at all (PV_NONE: the
@@ -703,7 +700,7 @@ __device__ __forceinline__ void seq_int8_item(const uint16_t* __restrict__ q, co
   __shared__ float s_mu[D], s_muq[D], s_dv[D];
   __shared__ uint32_t s_red[8];
   constexpr int VB = PV == PV_F16 ? 2 : 1;   // bytes per V element
-  __shared__ __align__(16) uint8_t s_vt[D * 64 * VB];
+  __shared__ __align__(16) uint8_t s_vt[PV == PV_FP8 ? D * kVRow : D * 64 * VB];
   // the KV instance query head i reads is usually instance i itself (no grouping)
   const bool own_kv = kvq == i && cb.ka;
   if (tid < D) {
@@ -737,7 +734,7 @@ __device__ __forceinline__ void seq_int8_item(const uint16_t* __restrict__ q, co
     // effect on the maxima or the LSE term)
     const uint4 gq = row_raw(q, cb.qi, cb.qa, row, c0);
     const uint4 gk = row_raw(k, cb.ki, cb.ka, row, c0);
-    const uint4 gv = row_raw(v, cb.ki, cb.ka, row, c0);
+    const uint4 gv = PV == PV_F16 ? row_raw(v, cb.ki, cb.ka, row, c0) : make_uint4(0, 0, 0, 0);
     float cs = 0.0f;
     unpack8<DT>(gq, xq[p]);
 #pragma unroll
@@ -748,11 +745,10 @@ __device__ __forceinline__ void seq_int8_item(const uint16_t* __restrict__ q, co
     if (cb.ka && row < cb.ki.len) {
       float xv[8];
       unpack8<DT>(gk, xk[p]);
-      unpack8<DT>(gv, xv);
-      if (PV == PV_F16)
+      if (PV == PV_F16) {
+        unpack8<DT>(gv, xv);
         put_v_f16(reinterpret_cast<uint16_t*>(s_vt), rl, c0, xv);
-      else
-        put_v_fp8(s_vt, rl, c0, xv, dv, rv);
+      }
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         xk[p][i] = xk[p][i] - s_mu[c0 + i];
@@ -763,10 +759,7 @@ __device__ __forceinline__ void seq_int8_item(const uint16_t* __restrict__ q, co
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         xk[p][i] = 0.0f;
-        if (PV == PV_F16)
-          reinterpret_cast<uint16_t*>(s_vt)[(c0 + i) * 64 + rl] = 0;
-        else
-          s_vt[(c0 + i) * 64 + rl] = 0;
+        if (PV == PV_F16) reinterpret_cast<uint16_t*>(s_vt)[(c0 + i) * 64 + rl] = 0;
       }
     }
     // LSE correction: sm * q_t . mu_k (reduced over the C8 threads of this row)
@@ -826,9 +819,14 @@ __device__ __forceinline__ void seq_int8_item(const uint16_t* __restrict__ q, co
     if (cb.ka) *reinterpret_cast<uint2*>(qp.k_codes + (cb.ki.tok0 + row) * D + c0) = make_uint2(wk[0], wk[1]);
   }
   if (cb.ka) {
-    __syncthreads();
     // V tile [D][64] -> the instance's tile blk of v_codes [..][D][64], coalesced 16-byte stores
     uint8_t* dst = qp.v_codes + (cb.ki.tok0 / 64 + blk) * D * 64 * VB;
+    if (PV == PV_FP8) {
+      auto row8 = [&](int jr, float* x) { unpack8<DT>(row_raw(v, cb.ki, true, t0 + NP * r0 + jr, c0), x); };
+      v_block_fp8_rows<D>(row8, c0, r0, dv, rv, s_vt, dst);
+      return;
+    }
+    __syncthreads();
     for (int c = tid; c < D * 4 * VB; c += 256)
       *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(s_vt + c * 16);
   }
@@ -865,7 +863,7 @@ __device__ __forceinline__ void seq_mxfp4_item(const uint16_t* __restrict__ q, c
   const bool own_kv = kvq == i && cb.ka;   // query head h reads KV head h (no grouping)
   const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
   __shared__ float s_mk[D], s_mkq[D], s_mq[D];
-  __shared__ __align__(16) uint8_t s_vt[PV == PV_FP8 ? D * 64 : 1];
+  __shared__ __align__(16) uint8_t s_vt[PV == PV_FP8 ? D * kVRow : 1];
   __shared__ float s_vf[MXV ? 64 : 1][MXV ? D + 1 : 1];
   __shared__ float s_dv[PV == PV_FP8 ? D : 1];
   if (tid < D) {
@@ -908,7 +906,7 @@ __device__ __forceinline__ void seq_mxfp4_item(const uint16_t* __restrict__ q, c
     // the row's three loads go out together (zeros past an instance's end)
     const uint4 gq = row_raw(q, cb.qi, cb.qa, row, c0);
     const uint4 gk = row_raw(k, cb.ki, cb.ka, row, c0);
-    const uint4 gv = row_raw(v, cb.ki, cb.ka, row, c0);
+    const uint4 gv = PV != PV_FP8 ? row_raw(v, cb.ki, cb.ka, row, c0) : make_uint4(0, 0, 0, 0);
     float xq[8], xv[8];
     unpack8<DT>(gq, xq);
     unpack8<DT>(gk, xk[p]);
@@ -954,14 +952,7 @@ __device__ __forceinline__ void seq_mxfp4_item(const uint16_t* __restrict__ q, c
       *reinterpret_cast<uint32_t*>(qp.k_codes + (cb.ki.tok0 + row) * (D / 2) + c0 / 2) = pack_fp4x8(xk[p], sk);
       if ((c0 % 32) == 0) ke[(cb.ki.tok0 + row) * (D / 32) + c0 / 32] = (uint8_t)bk;
       if (grp == 1 && (tid % C8) == 0) qp.delta_s[ds_own + row] = kv ? (float)ds : 0.0f;
-      if (PV == PV_FP8) {
-        if (kv) {
-          put_v_fp8(s_vt, rl, c0, xv, dv, rv);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; i++) s_vt[(c0 + i) * 64 + rl] = 0;
-        }
-      } else {
+      if (PV != PV_FP8) {
 #pragma unroll
         for (int i = 0; i < 8; i++) s_vf[rl][c0 + i] = xv[i];
       }
@@ -989,13 +980,12 @@ __device__ __forceinline__ void seq_mxfp4_item(const uint16_t* __restrict__ q, c
       }
     }
   }
-  __syncthreads();
   const size_t vt0 = cb.ki.tok0 / 64 + blk;   // the instance's V tile
   if (PV == PV_FP8) {
-    uint8_t* dst = qp.v_codes + vt0 * D * 64;
-    for (int c = tid; c < D * 4; c += 256)
-      *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(s_vt + c * 16);
+    auto row8 = [&](int jr, float* x) { unpack8<DT>(row_raw(v, cb.ki, true, t0 + NP * r0 + jr, c0), x); };
+    v_block_fp8_rows<D>(row8, c0, r0, dv, rv, s_vt, qp.v_codes + vt0 * D * 64);
   } else {
+    __syncthreads();
     // one thread per (channel, 32-token group)
     for (int w = tid; w < D * 2; w += 256) {
       const int ch = w % D, gi = w / D;
