@@ -55,7 +55,8 @@ struct FwdArgs {
   float* lse;
   SeqGeo g;
   int nqt;            // query tiles per instance in the grid
-  int nqb;            // MXFP4 with per-block Q smoothing: dS rows per instance (one per query tile); else 0
+  int qbs;            // MXFP4 with per-block Q smoothing: keys per dS strip (one strip per query tile,
+                      // at qblock_slot); else 0
   float sm_log2e;
 };
 
@@ -674,7 +675,7 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
   const size_t kt0 = ki.tok0, kvid = (size_t)b * a.g.Hkv + hk;
   // dS strip: per key, or (per-block Q smoothing) the row of this query tile's block
   const size_t ds0 = QK != QK_MXFP4 ? 0
-                     : a.nqb ? (((size_t)b * a.g.H + h) * a.nqb + qt) * a.g.Npk : ds_base(a.g, b, h);
+                     : a.qbs ? qblock_slot(a.g, b, h, qt) * a.qbs : ds_base(a.g, b, h);
   const int NK = ki.len;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -912,7 +913,7 @@ hipError_t launch_attn_fwd(const Shape& s, const QuantPtrs& qp, void* o, float* 
   a.lse = lse;
   a.g = s.g;
   a.nqt = (s.g.nbq * 64) / kQT;   // tiles of 128 queries covering the longest query instance
-  a.nqb = s.qk_fmt == QK_MXFP4B ? s.Np / kQT : 0;
+  a.qbs = s.qk_fmt == QK_MXFP4B ? (int)qblock_strip(s.g) : 0;
   a.sm_log2e = s.sm_scale * kLog2e;
   if (s.qk_fmt == QK_INT8 || s.qk_fmt == QK_INT8T) {
     if (s.pv_fmt == PV_F16)

@@ -625,6 +625,115 @@ __global__ __launch_bounds__(256) void qblock_ds_kernel(const uint16_t* __restri
   }
 }
 
+// Per-block Q smoothing on packed sequences: the means of every 128-query block of every query
+// instance, formed as qblock_mean_kernel forms them (the same fp64 sums in the same order), at
+// the blocks' slots (qblock_slot).  grid (table capacity, H): workgroup (e, h) takes table item
+// e = (b, j) for even j -- query block j / 2 of query instance (b, h) -- and returns for odd j
+// and for blocks past the query sequence (the table covers the longer of its query and key
+// sequences).
+template <int DT, int D>
+__global__ __launch_bounds__(256) void seq_qblock_mean_kernel(const uint16_t* __restrict__ q, SeqGeo g,
+                                                              float* __restrict__ mu_q, double* __restrict__ muD,
+                                                              const int2* __restrict__ tab) {
+  constexpr int C8 = D / 8, RP = 256 / C8;
+  const int e = blockIdx.x;
+  if (e >= tab[0].x) return;
+  const int2 it = tab[1 + e];
+  if (it.y & 1) return;
+  const int b = it.x, qb = it.y / 2, h = blockIdx.y;
+  const Inst qi = q_inst(g, b, h, D);
+  const int t0 = qb * 128, t1 = min(qi.len, t0 + 128);
+  if (t0 >= t1) return;
+  const int tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
+  double sx[8] = {};
+  for (int r = t0 + r0; r < t1; r += RP) {
+    float y[8];
+    load8<DT>(q + qi.io0 + (size_t)r * qi.ios + c0, y);
+#pragma unroll
+    for (int i = 0; i < 8; i++) sx[i] += (double)y[i];
+  }
+  __shared__ double s_x[RP][D];
+#pragma unroll
+  for (int i = 0; i < 8; i++) s_x[r0][c0 + i] = sx[i];
+  __syncthreads();
+  if (tid < D) {
+    double a = 0.0;
+    for (int r = 0; r < RP; r++) a += s_x[r][tid];
+    const float m = (float)(a / (double)(t1 - t0));
+    const size_t slot = qblock_slot(g, b, h, qb);
+    mu_q[slot * D + tid] = m;
+    muD[slot * D + tid] = (double)m;
+  }
+}
+
+// Per-block Q smoothing on packed sequences: dS of every block of the query heads that read KV
+// head hk against keys [64 j, 64 j + 64) of KV instance (b, hk) (0 past the sequence's end),
+// formed as qblock_ds_kernel forms it (the same fp64 MFMA chain over the channels in order),
+// into the blocks' strips.  grid (table capacity, Hkv), item e = (b, j).  The A operand reads
+// the means of 16 consecutive slots from the sequence's first; slots past its blocks (the next
+// sequence's, or the 16 rows after the last head's) only feed result rows that are not stored.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void seq_qblock_ds_kernel(const uint16_t* __restrict__ k, SeqGeo g,
+                                                            const float* __restrict__ mu_k,
+                                                            const double* __restrict__ muD, size_t strip,
+                                                            float* __restrict__ delta_s,
+                                                            const int2* __restrict__ tab) {
+  constexpr int C8 = D / 8, KS = D + 4;
+  const int e = blockIdx.x;
+  if (e >= tab[0].x) return;
+  const int2 it = tab[1 + e];
+  const int b = it.x, hk = blockIdx.y, t0 = it.y * 64, grp = g.H / g.Hkv;
+  const Inst ki = k_inst(g, b, hk, D);
+  const int nqb = (q_inst(g, b, hk * grp, D).len + 127) / 128;
+  if (t0 >= ((ki.len + 127) & ~127) || nqb == 0) return;
+  __shared__ float s_ks[64 * KS];
+  const float* mk = mu_k + ((size_t)b * g.Hkv + hk) * D;
+  for (int x = threadIdx.x; x < 64 * C8; x += 256) {
+    const int r = x / C8, c0 = (x % C8) * 8, row = t0 + r;
+    float y[8];
+    if (row < ki.len) {
+      load8<DT>(k + ki.io0 + (size_t)row * ki.ios + c0, y);
+#pragma unroll
+      for (int i = 0; i < 8; i++) y[i] = y[i] - mk[c0 + i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) y[i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) s_ks[r * KS + c0 + i] = y[i];
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lk = lane >> 4;
+  for (int r = 0; r < grp; r++) {
+    const size_t slot0 = qblock_slot(g, b, hk * grp + r, 0);
+    for (int gq = w; 16 * gq < nqb; gq += 4) {
+      const double* ma = muD + (slot0 + 16 * gq + li) * D + lk;
+      v4d acc[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) acc[u] = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+      for (int c = 0; c < D; c += 4) {
+        const double av = ma[c];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const double bv = (double)s_ks[(16 * u + li) * KS + c + lk];
+          acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[u], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int key = t0 + 16 * u + li;
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) {
+          const int blk = 16 * gq + lk + 4 * rr;
+          if (blk < nqb) delta_s[(slot0 + blk) * strip + key] = key < ki.len ? (float)acc[u][rr] : 0.0f;
+        }
+      }
+    }
+  }
+}
+
 // The instances one packed-sequence codes item serves: query head h of sequence b and, when
 // h < Hkv, KV head h of the same sequence; each role is active while the item's 64-token block
 // lies inside the instance rounded up to 128.
@@ -848,7 +957,7 @@ __global__ __launch_bounds__(256) void quant_int8_fp8_seq_kernel(const uint16_t*
 // LSE correction; V in FP8 (PV == PV_FP8), MXFP4 or MXFP8 (both in 32-token blocks per
 // channel).  grid (blocks of the longest instance, B*H), 256 threads.  dS = mu_q . K_s is written for each query head that
 // reads KV instance i (one without grouped heads, in the row loop; H / Hkv of them after it).
-template <int DT, int D, int PV>
+template <int DT, int D, int PV, bool QB>
 __device__ __forceinline__ void seq_mxfp4_item(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                const uint16_t* __restrict__ v, const SeqGeo& g, float sm,
                                                const QuantPtrs& qp, int b, int blk, int h) {
@@ -877,13 +986,17 @@ __device__ __forceinline__ void seq_mxfp4_item(const uint16_t* __restrict__ q, c
       }
     }
     // mu_q of the query instance: its own smoothing, and (grp == 1) the dS of the KV instance,
-    // which that query head reads -- needed whenever either role is active
-    const float mq = chunk_mean(qp.sums, 1, BHm, iq, D, tid, cb.qi.len);
-    s_mq[tid] = mq;
-    if (cb.qa) {
-      if (!own_kv) s_mkq[tid] = chunk_mean(qp.sums, 0, BHm, kvq, D, tid, cb.kq.len);
-      if (blk == 0) qp.mu_q[(size_t)iq * D + tid] = mq;
+    // which that query head reads -- needed whenever either role is active.  QB: the mean of
+    // this block's 128-query block (seq_qblock_mean_kernel), and dS comes from
+    // seq_qblock_ds_kernel
+    if (QB) {
+      s_mq[tid] = cb.qa ? qp.mu_q[qblock_slot(g, b, h, blk / 2) * D + tid] : 0.0f;
+    } else {
+      const float mq = chunk_mean(qp.sums, 1, BHm, iq, D, tid, cb.qi.len);
+      s_mq[tid] = mq;
+      if (cb.qa && blk == 0) qp.mu_q[(size_t)iq * D + tid] = mq;
     }
+    if (cb.qa && !own_kv) s_mkq[tid] = chunk_mean(qp.sums, 0, BHm, kvq, D, tid, cb.kq.len);
   }
   __syncthreads();
   const float* mkq = own_kv ? s_mk : s_mkq;
@@ -920,7 +1033,7 @@ __device__ __forceinline__ void seq_mxfp4_item(const uint16_t* __restrict__ q, c
       cs += (double)xq[i] * (double)mkq[c0 + i];
       xq[i] = xq[i] - fq * s_mq[c0 + i];
       xk[p][i] = xk[p][i] - fk * s_mk[c0 + i];
-      if (grp == 1) ds += (double)s_mq[c0 + i] * (double)xk[p][i];
+      if (!QB && grp == 1) ds += (double)s_mq[c0 + i] * (double)xk[p][i];
     }
     // one MX block = 32 channels = 4 neighbouring threads
     uint32_t aq = 0, ak = 0;
@@ -951,7 +1064,7 @@ __device__ __forceinline__ void seq_mxfp4_item(const uint16_t* __restrict__ q, c
       const float sk = bk == 0 ? 1.0f : e8m0_to_float(bk);
       *reinterpret_cast<uint32_t*>(qp.k_codes + (cb.ki.tok0 + row) * (D / 2) + c0 / 2) = pack_fp4x8(xk[p], sk);
       if ((c0 % 32) == 0) ke[(cb.ki.tok0 + row) * (D / 32) + c0 / 32] = (uint8_t)bk;
-      if (grp == 1 && (tid % C8) == 0) qp.delta_s[ds_own + row] = kv ? (float)ds : 0.0f;
+      if (!QB && grp == 1 && (tid % C8) == 0) qp.delta_s[ds_own + row] = kv ? (float)ds : 0.0f;
       if (PV != PV_FP8) {
 #pragma unroll
         for (int i = 0; i < 8; i++) s_vf[rl][c0 + i] = xv[i];
@@ -960,7 +1073,7 @@ __device__ __forceinline__ void seq_mxfp4_item(const uint16_t* __restrict__ q, c
   }
   if (!cb.ka) return;
   // grouped heads: dS for each query head of the group, with its own mu_q
-  if (grp > 1) {
+  if (!QB && grp > 1) {
     const Inst qg = q_inst(g, cb.bk, cb.hk * grp, D);   // the group's query sequence
     for (int r = 0; r < grp; r++) {
       const int hq = cb.hk * grp + r, iq = cb.bk * g.H + hq;
@@ -1033,7 +1146,7 @@ __device__ __forceinline__ void seq_mxfp4_item(const uint16_t* __restrict__ q, c
 }
 
 // grid (table capacity, H): workgroup (e, h) takes the table's item e for query head h.
-template <int DT, int D, int PV>
+template <int DT, int D, int PV, bool QB>
 __global__ __launch_bounds__(256) void quant_mxfp4_seq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, SeqGeo g, float sm,
                                                           QuantPtrs qp) {
@@ -1042,7 +1155,7 @@ __global__ __launch_bounds__(256) void quant_mxfp4_seq_kernel(const uint16_t* __
   const int e = blockIdx.x;
   if (e >= n) return;
   const int2 it = tab[1 + e];
-  seq_mxfp4_item<DT, D, PV>(q, k, v, g, sm, qp, it.x, it.y, blockIdx.y);
+  seq_mxfp4_item<DT, D, PV, QB>(q, k, v, g, sm, qp, it.x, it.y, blockIdx.y);
 }
 
 template <int DT, int D>
@@ -1087,18 +1200,22 @@ static hipError_t prologue_dispatch(const void* q, const void* k, const void* v,
     else with_pv(std::false_type{});
     return hipGetLastError();
   }
-  // QB (per-128-query-block Q smoothing, fixed length only): block means replace the Q sums
+  // QB (per-128-query-block Q smoothing): block means replace the Q sums
   const bool qb = s.qk_fmt == QK_MXFP4B;
-  // QB: the fp64 copy of the block means follows the fp32 ones in the mu_q region
-  const int nbp = qblock_padded(s.Np / 128);
-  double* muD = reinterpret_cast<double*>(qp.mu_q + (size_t)BHm * (s.Np / 128) * D);
+  // QB: the fp64 copy of the block means follows the fp32 ones in the mu_q region (fixed
+  // length: per instance, padded to whole 16-block groups; packed: by slot, 16 rows of padding)
+  const int nbp = plain ? qblock_padded(s.Np / 128) : 0;
+  double* muD = reinterpret_cast<double*>(qp.mu_q + qblock_slots(g) * D);
+  const int2* tab = reinterpret_cast<const int2*>(qp.blocks);
   if (qb) {
-    if (!plain) return hipErrorInvalidValue;
     if (s.pv_fmt == PV_FP8)
       stats_kernel<DT, D, false, true><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
     else
       stats_kernel<DT, D, false, false><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
-    qblock_mean_kernel<DT, D><<<dim3(s.Np / 128, BHm), 256, 0, st>>>(Q, s.N, s.Np, qp.mu_q, muD, nbp);
+    if (plain)
+      qblock_mean_kernel<DT, D><<<dim3(s.Np / 128, BHm), 256, 0, st>>>(Q, s.N, s.Np, qp.mu_q, muD, nbp);
+    else
+      seq_qblock_mean_kernel<DT, D><<<pg, 256, 0, st>>>(Q, g, qp.mu_q, muD, tab);
   } else if (s.pv_fmt == PV_FP8) {
     stats_kernel<DT, D, true, true><<<sg, 256, 0, st>>>(Q, K, V, g, qp.sums, qp.amax_v);
   } else {
@@ -1106,19 +1223,24 @@ static hipError_t prologue_dispatch(const void* q, const void* k, const void* v,
   }
   auto codes = [&](auto pv) {
     constexpr int PV = decltype(pv)::value;
-    if (qb)
+    if (plain && qb)
       quant_mxfp4_kernel<DT, D, PV, true><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BHm, s.sm_scale, qp);
     else if (plain)
       quant_mxfp4_kernel<DT, D, PV, false><<<qg, 256, 0, st>>>(Q, K, V, s.N, s.Np, BHm, s.sm_scale, qp);
+    else if (qb)
+      quant_mxfp4_seq_kernel<DT, D, PV, true><<<pg, 256, 0, st>>>(Q, K, V, g, s.sm_scale, qp);
     else
-      quant_mxfp4_seq_kernel<DT, D, PV><<<pg, 256, 0, st>>>(Q, K, V, g, s.sm_scale, qp);
+      quant_mxfp4_seq_kernel<DT, D, PV, false><<<pg, 256, 0, st>>>(Q, K, V, g, s.sm_scale, qp);
   };
   if (s.pv_fmt == PV_FP8) codes(std::integral_constant<int, PV_FP8>{});
   else if (s.pv_fmt == PV_MXFP8) codes(std::integral_constant<int, PV_MXFP8>{});
   else codes(std::integral_constant<int, PV_MXFP4>{});
   // QB: dS per (query block, key), after the codes kernel has written mu_k
-  if (qb)
+  if (qb && plain)
     qblock_ds_kernel<DT, D><<<dim3(s.Np / 64, BHm), 256, 0, st>>>(K, s.N, s.Np, qp.mu_k, muD, nbp, qp.delta_s);
+  else if (qb)
+    seq_qblock_ds_kernel<DT, D><<<dim3(pg.x, g.Hkv), 256, 0, st>>>(K, g, qp.mu_k, muD, qblock_strip(g), qp.delta_s,
+                                                                   tab);
   return hipGetLastError();
 }
 

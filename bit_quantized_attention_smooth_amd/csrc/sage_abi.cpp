@@ -90,8 +90,11 @@ sage_status check_varlen(const sage_varlen_problem* p) {
   if (toks * p->d > (1LL << 40) || (long long)p->B * p->H > kMaxInstances ||
       (long long)p->B * p->H * ((p->max_seqlen_q + 127) / 128) > (1LL << 31) - 1)
     return fail(SAGE_ERR_INVALID_ARG, "problem too large");
-  if (p->qk_fmt == SAGE_FMT_MXFP4_QBLOCK)
-    return fail(SAGE_ERR_UNSUPPORTED, "per-block Q smoothing (MXFP4_QBLOCK) is for fixed-length problems only");
+  // per-block Q smoothing: a dS strip of max_seqlen_k keys per 128-query block slot
+  if (p->qk_fmt == SAGE_FMT_MXFP4_QBLOCK &&
+      (double)p->H * (double)sage::qblock_slots_per_head(p->total_q, p->B) * ((p->max_seqlen_k + 127) / 128 * 128.0) *
+              4.0 > (double)(1LL << 40))
+    return fail(SAGE_ERR_INVALID_ARG, "problem too large");
   return check_common(p->d, p->causal, p->sm_scale, p->io_dtype, p->qk_fmt, p->pv_fmt);
 }
 
@@ -151,17 +154,24 @@ struct Extents {
   size_t ds, corr;          // dS floats (query heads x key tokens), LSE-term floats
   size_t stats_inst;        // instances of the statistics partials (B*H)
   size_t blk_cap;           // packed sequences: entries of the (sequence, block) table; else 0
+  // per-block Q smoothing: slots (a mean and a dS strip per 128-query block, qblock_slot), rows
+  // of the means' fp64 copy, keys per dS strip
+  size_t qb_slots, qb_rows64, qb_strip;
 };
 
 Extents extents(const sage_problem* p) {
-  const size_t BH = (size_t)p->B * p->H, Np = round_up((size_t)p->N, sage::kTokenPad);
-  return Extents{BH, BH, BH * Np, BH * Np, BH * Np, BH * (size_t)p->N, BH, 0};
+  const size_t BH = (size_t)p->B * p->H, Np = round_up((size_t)p->N, sage::kTokenPad), nqb = Np / 128;
+  return Extents{BH, BH, BH * Np, BH * Np, BH * Np, BH * (size_t)p->N, BH, 0,
+                 BH * nqb, BH * (size_t)sage::qblock_padded((int)nqb), Np};
 }
+// (packed: the slots' fp64 rows plus 16, which the dS step's 16-slot operand reads may reach)
 Extents extents(const sage_varlen_problem* p) {
   const size_t Tq = packed_tokens(p->total_q, p->B), Tk = packed_tokens(p->total_k, p->B);
   const size_t BH = (size_t)p->B * p->H;
+  const size_t slots = (size_t)p->H * (size_t)sage::qblock_slots_per_head(p->total_q, p->B);
   return Extents{BH, (size_t)p->B * p->H_kv, p->H * Tq, p->H_kv * Tk, p->H * Tk, p->H * Tq, BH,
-                 (size_t)sage::seq_block_capacity(p->total_q, p->total_k, p->B)};
+                 (size_t)sage::seq_block_capacity(p->total_q, p->total_k, p->B),
+                 slots, slots + 16, round_up((size_t)p->max_seqlen_k, 128)};
 }
 
 void compute_layout(const Extents& E, int d_, int qk_fmt, int pv_fmt, sage_quant_layout* L) {
@@ -175,11 +185,9 @@ void compute_layout(const Extents& E, int d_, int qk_fmt, int pv_fmt, sage_quant
     return o;
   };
   L->mu_k = take(E.inst_kv * d * 4);
-  // per-block Q smoothing: a mean per 128-query block, a dS row per block (fixed length: tq, tk
-  // are the instances' padded token counts)
-  const size_t nqb = qblk ? E.tq / E.inst_q / 128 : 1;
-  // (QBLOCK: then the same means in fp64, transposed and padded: scratch of the dS step)
-  L->mu_q = take(E.inst_q * nqb * d * 4 + (qblk ? E.inst_q * d * sage::qblock_padded((int)nqb) * 8 : 0));
+  // per-block Q smoothing: a mean per 128-query block (then the same means in fp64, padded: the
+  // dS step's operand), a dS strip per block
+  L->mu_q = take(qblk ? E.qb_slots * d * 4 + E.qb_rows64 * d * 8 : E.inst_q * d * 4);
   L->q_codes = take(mx ? E.tq * d / 2 : E.tq * d);
   const bool tok = qk_fmt == SAGE_FMT_INT8_TOKEN;
   L->q_scales = take(mx ? E.tq * (d / 32) : tok ? E.tq * 4 : E.tq / 64 * 4);
@@ -187,7 +195,7 @@ void compute_layout(const Extents& E, int d_, int qk_fmt, int pv_fmt, sage_quant
   L->k_scales = take(mx ? E.tk * (d / 32) : tok ? E.tk / 32 * 4 : E.tk / 64 * 4);
   L->v_codes = take(mxv ? E.tk * d / 2 : pv_fmt == SAGE_FMT_F16 ? E.tk * d * 2 : E.tk * d);
   L->v_scales = take(mxv || mx8v ? E.tk / 32 * d : E.inst_kv * d * 4);
-  L->delta_s = take(E.ds * nqb * 4);
+  L->delta_s = take(qblk ? E.qb_slots * E.qb_strip * 4 : E.ds * 4);
   L->lse_corr = take(E.corr * 4);
   // statistics partials, then (packed sequences) the (sequence, block) table: int2 [1 + cap]
   L->stats = take(sage::kStatChunks * (E.stats_inst * d * 8 * 2 + E.stats_inst * d * 4) +

@@ -75,6 +75,19 @@ inline int seq_block_capacity(long long total_q, long long total_k, long long B)
 }
 inline int seq_block_capacity(const SeqGeo& g) { return seq_block_capacity(g.total_q, g.total_k, g.B); }
 
+// Per-block Q smoothing (QK_MXFP4B): query block qb of query instance (b, h) -- its 128
+// queries from the sequence's first one, the fused kernel's query tile qb -- owns row `slot` of
+// the block means and the dS strip [slot * strip, slot * strip + strip) over the KV instance's
+// keys.  Fixed length: slot (b H + h) Npq / 128 + qb, strips of Npk keys.  Packed: total_q / 128
+// + B + 1 slots per head, sequence b's from floor(start / 128) + b on (its ceil(len / 128)
+// blocks end before sequence b + 1's first slot, since floor(s / 128) + ceil(len / 128) <=
+// floor((s + len) / 128) + 1), strips of max_k rounded up to 128 keys.
+__host__ __device__ inline long long qblock_slots_per_head(long long total_q, long long B) { return total_q / 128 + B + 1; }
+inline size_t qblock_slots(const SeqGeo& g) {
+  return g.cu_q ? (size_t)g.H * qblock_slots_per_head(g.total_q, g.B) : (size_t)g.B * g.H * (g.Npq / 128);
+}
+inline size_t qblock_strip(const SeqGeo& g) { return g.cu_q ? ((size_t)g.max_k + 127) / 128 * 128 : (size_t)g.Npk; }
+
 #if defined(__HIPCC__)
 // Packed sequence b: its first row and length, clamped so that any offsets keep every access
 // inside the buffers (start in [0, total], length in [0, min(max_len, total - start)]).
@@ -126,6 +139,15 @@ __device__ __forceinline__ Inst k_inst(const SeqGeo& g, int b, int hk, int d) {
   }
   r.row0 = r.lse0 = 0;
   return r;
+}
+// Per-block Q smoothing: the slot of query block qb of query instance (b, h) (see
+// qblock_slots_per_head); packed starts and lengths are clamped as in packed_seq, so even
+// malformed offsets give slots below the head's count.
+__device__ __forceinline__ size_t qblock_slot(const SeqGeo& g, int b, int h, int qb) {
+  if (!g.cu_q) return ((size_t)b * g.H + h) * (g.Npq / 128) + qb;
+  int s, len;
+  packed_seq(g.cu_q, b, g.total_q, g.max_q, s, len);
+  return (size_t)h * (size_t)qblock_slots_per_head(g.total_q, g.B) + (size_t)(s / 128 + b + qb);
 }
 // First key token of query head h's dS strip (MXFP4 QK: mu_q(h) . K_s per key).
 __device__ __forceinline__ size_t ds_base(const SeqGeo& g, int b, int h) {

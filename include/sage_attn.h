@@ -70,7 +70,7 @@ typedef enum {
  * with Q smoothed by the mean of each 128-query block instead of the whole
  * sequence (the pages leave the form of "smooth Q" open, SageAttention2
  * abstract); the removed part returns as dS = mu_q(block) . K_s per block and
- * key.  Fixed-length problems only (the packed entry returns UNSUPPORTED). */
+ * key.  On packed sequences the blocks start at each sequence's first query. */
 enum { SAGE_FMT_INT8 = 1, SAGE_FMT_FP8 = 2, SAGE_FMT_MXFP4 = 3, SAGE_FMT_MXFP8 = 4, SAGE_FMT_F16 = 5,
        SAGE_FMT_INT8_TOKEN = 6, SAGE_FMT_MXFP4_QBLOCK = 7 };
 
@@ -244,7 +244,9 @@ sage_status sage_attn_bwd(const sage_problem *p, const void *q, const void *k, c
  *   lse            device fp32 [H, total_q] or NULL
  * Query head h reads KV head h / (H / H_kv).  Every sequence is quantized on its
  * own (K mean and V channel steps per sequence and KV head, 64-token INT8 blocks
- * inside the sequence).  Causal masking is top-left aligned per sequence (query
+ * inside the sequence; MXFP4_QBLOCK: 128-query blocks from the sequence's first
+ * query, with workspace for a dS strip of max_seqlen_k keys per block slot, about
+ * H * (total_q / 128 + B) * max_seqlen_k floats).  Causal masking is top-left aligned per sequence (query
  * i sees keys j <= i).  A query with no key (an empty key sequence) gets a zero
  * output and LSE -inf.  max_seqlen_q / max_seqlen_k bound every sequence's
  * length (host values, as FlashAttention takes them); the kernels clamp the

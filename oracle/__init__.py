@@ -288,7 +288,8 @@ def attn_varlen(q, k, v, cu_q, cu_k, causal, sm, qk_fmt="int8", pv_fmt="fp8", ti
             qz = quant_int8_fp8(qs, ks, vs, sm, pv_fmt=pv_fmt, qblk=1 if fine else 64, kblk=32 if fine else 64)
             ob, lb, sb = attn_int8_fp8(qz, q1 - q0, d, causal, sm, tile, slack=True)
         else:
-            qz = quant_mxfp4(qs, ks, vs, sm, pv_fmt=pv_fmt)
+            # mxfp4_qblock: Q smoothed per 128-query block counted from the sequence's first query
+            qz = quant_mxfp4(qs, ks, vs, sm, pv_fmt=pv_fmt, qsb=128 if qk_fmt == "mxfp4_qblock" else 0)
             ob, lb, sb = attn_mxfp4(qz, q1 - q0, d, causal, sm, tile, slack=True)
         o[q0:q1] = np.transpose(ob, (1, 0, 2))
         if sb is not None:

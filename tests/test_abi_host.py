@@ -149,7 +149,8 @@ def _vp(**kw):
     (dict(total_q=-1), S.ERR_INVALID_ARG), (dict(max_seqlen_k=-5), S.ERR_INVALID_ARG),
     (dict(d=96), S.ERR_UNSUPPORTED), (dict(qk_fmt=1, pv_fmt=3), S.ERR_UNSUPPORTED),
     (dict(sm_scale=float("nan")), S.ERR_INVALID_ARG), (dict(total_q=2 ** 31 - 1), S.ERR_INVALID_ARG),
-    (dict(qk_fmt=7, pv_fmt=2), S.ERR_UNSUPPORTED),
+    (dict(qk_fmt=7, pv_fmt=5), S.ERR_UNSUPPORTED),
+    (dict(qk_fmt=7, pv_fmt=2, total_q=2 ** 30, max_seqlen_k=2 ** 30), S.ERR_INVALID_ARG),
 ])
 def test_varlen_validation(kw, status):
     L = S.lib()
@@ -189,6 +190,23 @@ def test_varlen_workspace_covers_every_sequence_padding():
     # per query head; 256 extra tokens per sequence
     per_seq = 256 * (2 * 128 + 4 * 128)
     assert sizes[1] - sizes[0] >= 7 * per_seq and sizes[2] - sizes[1] >= 56 * per_seq
+
+
+def test_varlen_qblock_workspace_holds_every_block_strip():
+    """Per-block Q smoothing on packed sequences: per head, total_q / 128 + B + 1 block slots,
+    each with a mean (fp32, then fp64 with 16 rows of padding) and a dS strip of max_seqlen_k
+    keys rounded up to 128; the workspace is the plain MXFP4 one plus those."""
+    L = S.lib()
+    n_mx, n_qb = ctypes.c_size_t(), ctypes.c_size_t()
+    kw = dict(B=3, H=4, H_kv=2, d=128, total_q=1000, total_k=700, max_seqlen_q=500, max_seqlen_k=300)
+    assert L.sage_varlen_ws_size(ctypes.byref(_vp(qk_fmt=3, pv_fmt=2, **kw)), ctypes.byref(n_mx)) == S.OK
+    assert L.sage_varlen_ws_size(ctypes.byref(_vp(qk_fmt=7, pv_fmt=2, **kw)), ctypes.byref(n_qb)) == S.OK
+    slots = 4 * (1000 // 128 + 3 + 1)
+    # replaced: a mean per query instance (B H of them) and a dS row per query head over the
+    # packed key tokens (700 rounded up to 64, plus 256 per sequence)
+    plain = 12 * 128 * 4 + 4 * (704 + 3 * 256) * 4
+    extra = slots * 128 * 4 + (slots + 16) * 128 * 8 + slots * 384 * 4 - plain
+    assert abs(n_qb.value - n_mx.value - extra) <= 2 * 256
 
 
 def test_backward_binding_rejects_mismatched_o_do_lse():

@@ -50,7 +50,8 @@ def _f32(t):
 
 
 PAIRS = [("int8", "fp8"), ("int8", "f16"), ("int8_token", "fp8"), ("int8_token", "f16"), ("mxfp4", "fp8"),
-         ("mxfp4", "mxfp4"), ("mxfp4", "mxfp8")]
+         ("mxfp4", "mxfp4"), ("mxfp4", "mxfp8"), ("mxfp4_qblock", "fp8"), ("mxfp4_qblock", "mxfp4"),
+         ("mxfp4_qblock", "mxfp8")]
 
 
 @pytest.mark.parametrize("qk,pv", PAIRS, ids=[f"{a}_{b}" for a, b in PAIRS])
@@ -109,6 +110,36 @@ def test_varlen_mxfp4_keys_longer_than_queries(sage, pv):
     og = to_np64(o)
     assert within(og, o_sim, sl), excess(og, o_sim, sl)
     assert cos(og, o_sim) >= 0.9999
+    assert np.allclose(lse.cpu().numpy(), lse_sim, rtol=1e-4, atol=2e-3)
+
+
+@pytest.mark.parametrize("pv", ["fp8", "mxfp4", "mxfp8"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_qblock_drifting_queries(sage, pv, causal):
+    """Per-block Q smoothing on packed sequences: queries whose mean drifts along each sequence
+    (so the 128-query block means differ), sequences that start off the 128-row grid and span
+    several blocks, a partial last block, a 1-token sequence, keys longer and shorter than the
+    queries (non-causal), grouped KV heads; against the oracle's per-sequence simulation with
+    blocks counted from each sequence's first query, and against fp64 attention."""
+    import oracle
+    banner(f"varlen qblock drift {pv} causal={causal}")
+    lens_q = [300, 1, 129, 513, 77]
+    lens_k = lens_q if causal else [700, 40, 129, 200, 300]
+    H, Hkv, d = 6, 2, 128
+    q, k, v, cu_q, cu_k = _packed(lens_q, lens_k, H, Hkv, d, seed=41)
+    g = torch.Generator().manual_seed(42)
+    direction = torch.randn(1, H, d, generator=g)
+    t = torch.cat([torch.arange(n, dtype=torch.float32) for n in lens_q])
+    q = (q.float() + 2.5 * torch.sin(t / 90.0)[:, None, None] * direction).to(q.dtype)
+    sm = 1 / math.sqrt(d)
+    o, lse = _run(sage, q, k, v, cu_q, cu_k, causal, sm, "mxfp4_qblock", pv)
+    o_sim, lse_sim, _, sl = oracle.attn_varlen(_f32(q), _f32(k), _f32(v), cu_q.numpy(), cu_k.numpy(), causal, sm,
+                                               qk_fmt="mxfp4_qblock", pv_fmt=pv, tile=TILE, slack=True)
+    o_ref, _, _ = oracle.attn_varlen(_f32(q), _f32(k), _f32(v), cu_q.numpy(), cu_k.numpy(), causal, sm, exact=True)
+    og = to_np64(o)
+    assert within(og, o_sim, sl), excess(og, o_sim, sl)
+    assert cos(og, o_sim) >= 0.9999
+    assert cos(og, o_ref) >= (0.965 if pv == "mxfp4" else 0.98)
     assert np.allclose(lse.cpu().numpy(), lse_sim, rtol=1e-4, atol=2e-3)
 
 
