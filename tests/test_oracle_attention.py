@@ -330,6 +330,41 @@ def test_mxfp4_scores_exact_on_random_lossless_codes(orc):
         assert np.allclose(lse, lse_ref, rtol=0, atol=1e-11)
 
 
+def test_mxfp4_p_second_level_scale_worked_example(orc):
+    """A worked example of the MXFP4 P~ step (sigma = 6 / the tile's largest p, then MX E2M1 over
+    each 32-key group with the floor-rule E8M0 scale of OCP MX v1.0), derived by hand.  Q codes
+    are zero, so every score is its dS term and sm = 1 makes p_j = exp(dS_j); V is the identity
+    (key j carries channel j), so O_c l = the quantized weight of key c, P~_c / sigma.
+      keys 0-4 (group 0), p = 1, 0.5, 0.3, 0.22, 0.12: sigma = 6 gives 6, 3, 1.8, 1.32, 0.72;
+        the group max 6 sets the scale 2^(2 - 2) = 1; E2M1 (RNE) gives 6, 3, 2, 1.5, 0.5
+        -> weights 1, 1/2, 1/3, 1/4, 1/12;
+      keys 32-34 (group 1), p = 0.28, 0.2, 0.07: sigma p = 1.68, 1.2, 0.42; the group max 1.68
+        sets the scale 2^(0 - 2) = 1/4, so the elements are 6.72, 4.8, 1.68 -> 6 (saturated), 4,
+        1.5 -> values 1.5, 1, 0.375 -> weights 1/4, 1/6, 1/16;
+      every other key has p = exp(-30): code 0.
+    A sigma per 32-key group would give key 34 the weight 0.07 and key 33 0.1867; the ceil
+    scale rule (2^ceil(log2(amax / 6))) would give key 34 1/12; sigma from a fixed 448 or no
+    sigma would move group 0."""
+    N, d = 64, 64
+    p = np.full(N, math.exp(-30.0))
+    p[[0, 1, 2, 3, 4, 32, 33, 34]] = [1.0, 0.5, 0.3, 0.22, 0.12, 0.28, 0.2, 0.07]
+    dS = np.log(p).astype(np.float32)
+    dS[0] = 0.0
+    vc = np.zeros((1, N, d), np.uint8)
+    vc[0, np.arange(N), np.arange(d)] = orc.e2m1_encode(np.ones(1))[0]
+    qz = dict(qc=np.zeros((1, 1, d), np.uint8), qe=np.full((1, 1, d // 32), 127, np.uint8),
+              kc=np.zeros((1, N, d), np.uint8), ke=np.full((1, N, d // 32), 127, np.uint8),
+              dS=dS[None, :], corr=np.zeros((1, 1), np.float64), vc=vc,
+              ve=np.full((1, N // 32, d), 127, np.uint8), vs=np.zeros((1, d), np.float32), pv_fmt="mxfp4", qsb=0)
+    o, lse = orc.attn_mxfp4(qz, 1, d, False, 1.0, 64)
+    w = np.zeros(d)
+    w[[0, 1, 2, 3, 4, 32, 33, 34]] = [1.0, 1 / 2, 1 / 3, 1 / 4, 1 / 12, 1 / 4, 1 / 6, 1 / 16]
+    assert np.allclose(o[0, 0] / o[0, 0, 0], w, rtol=1e-14, atol=0)
+    l = np.exp(dS.astype(np.float64)).sum()
+    assert np.isclose(o[0, 0, 0] * l, 1.0, rtol=1e-12)
+    assert np.isclose(lse[0, 0], math.log(l), rtol=0, atol=1e-12)
+
+
 @pytest.mark.parametrize("path", ["int8_fp8", "int8_f16", "mxfp4_mxfp4", "mxfp4_fp8", "mxfp4_mxfp8"])
 def test_constant_keys_give_mean_of_values(orc, path):
     """K constant along tokens: smoothing zeroes it, every score is 0, p = 1, and O is
