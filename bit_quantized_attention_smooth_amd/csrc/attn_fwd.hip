@@ -11,8 +11,9 @@
 // FP4 (SageAttention3 abstract); P~ and V are FP8 (SageAttention2 abstract).
 //
 // Dequantization is folded into the softmax: t = S_int * (dQ_row * dK_tile *
-// sm * log2 e) for INT8, t = S * sm * log2 e + dS_key * sm * log2 e for MXFP4,
-// and p~ = E4M3(exp2(t - m + log2 448)) = E4M3(448 p).  l accumulates the
+// sm * log2 e) for INT8, t = (S + dS_key) * sm * log2 e for MXFP4 (dS enters as
+// the QK MFMA's initial accumulator in the one-buffer kernels), and
+// p~ = E4M3(exp2(t - m + log2 448)) = E4M3(448 p).  l accumulates the
 // unquantized 448 p; the epilogue divides by it and applies the per-channel V
 // step.
 //
@@ -32,10 +33,12 @@
 // are already the B operand of the PV MFMA O^T = V^T P~^T (A = V^T, rows =
 // channels, K = the same 32 keys).
 //
-// Pipeline: the QK MFMAs of tile j+1 overlap the softmax of tile j (issued before it,
-// or spread through its exp / pack stream where that measured faster), so the matrix
-// unit works while the vector unit runs the softmax; K runs one tile ahead of V
-// through two LDS buffers each, with one barrier per tile.
+// Pipeline, one barrier per tile.  Most kernels (kOneBuf) hold one score tile per wave:
+// tile j issues its own QK MFMAs, with K and V loaded one tile ahead into two LDS buffers,
+// and the registers saved fit three workgroups per CU, so other waves fill the matrix and
+// vector units while one waits.  The others (two workgroups per CU) hold two: the QK MFMAs
+// of tile j+1 overlap the softmax of tile j (issued before it, or spread through its exp /
+// pack stream where that measured faster), with K one tile ahead of V.
 // Causal: one query tile per workgroup, longest first (see attn_fwd_kernel).
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
