@@ -92,8 +92,8 @@ sage_status check_varlen(const sage_varlen_problem* p) {
     return fail(SAGE_ERR_INVALID_ARG, "problem too large");
   // per-block Q smoothing: a dS strip of max_seqlen_k keys per 128-query block slot
   if (p->qk_fmt == SAGE_FMT_MXFP4_QBLOCK &&
-      (double)p->H * (double)sage::qblock_slots_per_head(p->total_q, p->B) * ((p->max_seqlen_k + 127) / 128 * 128.0) *
-              4.0 > (double)(1LL << 40))
+      (double)p->H * (double)sage::qblock_slots_per_head(p->total_q, p->B) *
+              ((std::min(p->max_seqlen_k, p->total_k) + 127) / 128 * 128.0) * 4.0 > (double)(1LL << 40))
     return fail(SAGE_ERR_INVALID_ARG, "problem too large");
   return check_common(p->d, p->causal, p->sm_scale, p->io_dtype, p->qk_fmt, p->pv_fmt);
 }
@@ -171,7 +171,7 @@ Extents extents(const sage_varlen_problem* p) {
   const size_t slots = (size_t)p->H * (size_t)sage::qblock_slots_per_head(p->total_q, p->B);
   return Extents{BH, (size_t)p->B * p->H_kv, p->H * Tq, p->H_kv * Tk, p->H * Tk, p->H * Tq, BH,
                  (size_t)sage::seq_block_capacity(p->total_q, p->total_k, p->B),
-                 slots, slots + 16, round_up((size_t)p->max_seqlen_k, 128)};
+                 slots, slots + 16, round_up((size_t)std::min(p->max_seqlen_k, p->total_k), 128)};
 }
 
 void compute_layout(const Extents& E, int d_, int qk_fmt, int pv_fmt, sage_quant_layout* L) {

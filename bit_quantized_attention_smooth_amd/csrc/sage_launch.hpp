@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <algorithm>
 #include <stdint.h>
 
 namespace sage {
@@ -86,7 +87,10 @@ __host__ __device__ inline long long qblock_slots_per_head(long long total_q, lo
 inline size_t qblock_slots(const SeqGeo& g) {
   return g.cu_q ? (size_t)g.H * qblock_slots_per_head(g.total_q, g.B) : (size_t)g.B * g.H * (g.Npq / 128);
 }
-inline size_t qblock_strip(const SeqGeo& g) { return g.cu_q ? ((size_t)g.max_k + 127) / 128 * 128 : (size_t)g.Npk; }
+// (packed: every key length is clamped to max_k and cannot exceed total_k)
+inline size_t qblock_strip(const SeqGeo& g) {
+  return g.cu_q ? ((size_t)std::min(g.max_k, g.total_k) + 127) / 128 * 128 : (size_t)g.Npk;
+}
 
 #if defined(__HIPCC__)
 // Packed sequence b: its first row and length, clamped so that any offsets keep every access

@@ -245,8 +245,8 @@ sage_status sage_attn_bwd(const sage_problem *p, const void *q, const void *k, c
  * Query head h reads KV head h / (H / H_kv).  Every sequence is quantized on its
  * own (K mean and V channel steps per sequence and KV head, 64-token INT8 blocks
  * inside the sequence; MXFP4_QBLOCK: 128-query blocks from the sequence's first
- * query, with workspace for a dS strip of max_seqlen_k keys per block slot, about
- * H * (total_q / 128 + B) * max_seqlen_k floats).  Causal masking is top-left aligned per sequence (query
+ * query, with workspace for a dS strip of min(max_seqlen_k, total_k) keys per block
+ * slot, about H * (total_q / 128 + B) * min(max_seqlen_k, total_k) floats).  Causal masking is top-left aligned per sequence (query
  * i sees keys j <= i).  A query with no key (an empty key sequence) gets a zero
  * output and LSE -inf.  max_seqlen_q / max_seqlen_k bound every sequence's
  * length (host values, as FlashAttention takes them); the kernels clamp the

@@ -150,7 +150,7 @@ def _vp(**kw):
     (dict(d=96), S.ERR_UNSUPPORTED), (dict(qk_fmt=1, pv_fmt=3), S.ERR_UNSUPPORTED),
     (dict(sm_scale=float("nan")), S.ERR_INVALID_ARG), (dict(total_q=2 ** 31 - 1), S.ERR_INVALID_ARG),
     (dict(qk_fmt=7, pv_fmt=5), S.ERR_UNSUPPORTED),
-    (dict(qk_fmt=7, pv_fmt=2, total_q=2 ** 30, max_seqlen_k=2 ** 30), S.ERR_INVALID_ARG),
+    (dict(qk_fmt=7, pv_fmt=2, total_q=2 ** 28, total_k=2 ** 28, max_seqlen_k=2 ** 28), S.ERR_INVALID_ARG),
 ])
 def test_varlen_validation(kw, status):
     L = S.lib()
@@ -207,6 +207,14 @@ def test_varlen_qblock_workspace_holds_every_block_strip():
     plain = 12 * 128 * 4 + 4 * (704 + 3 * 256) * 4
     extra = slots * 128 * 4 + (slots + 16) * 128 * 8 + slots * 384 * 4 - plain
     assert abs(n_qb.value - n_mx.value - extra) <= 2 * 256
+    # the strip never exceeds total_k: a loose max_seqlen_k bound changes nothing
+    n_loose = ctypes.c_size_t()
+    loose = dict(kw, max_seqlen_k=2 ** 30)
+    assert L.sage_varlen_ws_size(ctypes.byref(_vp(qk_fmt=7, pv_fmt=2, **loose)), ctypes.byref(n_loose)) == S.OK
+    assert n_loose.value == n_qb.value + 4 * (1000 // 128 + 4) * (768 - 384) * 4
+    # the size guard is the per-block one: the same sizes without it are accepted
+    big = dict(total_q=2 ** 28, total_k=2 ** 28, max_seqlen_k=2 ** 28)
+    assert L.sage_varlen_ws_size(ctypes.byref(_vp(qk_fmt=3, pv_fmt=2, **big)), ctypes.byref(n_mx)) == S.OK
 
 
 def test_backward_binding_rejects_mismatched_o_do_lse():
