@@ -88,7 +88,7 @@ sage_status check_varlen(const sage_varlen_problem* p) {
   const long long toks = (long long)p->H * packed_tokens(p->total_q, p->B) +
                          (long long)p->H_kv * packed_tokens(p->total_k, p->B) * 2;
   if (toks * p->d > (1LL << 40) || (long long)p->B * p->H > kMaxInstances ||
-      (long long)p->B * p->H * ((p->max_seqlen_q + 127) / 128) > (1LL << 31) - 1)
+      (long long)p->B * p->H * (((long long)std::min(p->max_seqlen_q, p->total_q) + 127) / 128) > (1LL << 31) - 1)
     return fail(SAGE_ERR_INVALID_ARG, "problem too large");
   // per-block Q smoothing: a dS strip of max_seqlen_k keys per 128-query block slot
   if (p->qk_fmt == SAGE_FMT_MXFP4_QBLOCK &&
@@ -140,10 +140,11 @@ sage::Shape to_shape(const sage_varlen_problem* p, const int* cu_q, const int* c
   g.Tk = (int)packed_tokens(p->total_k, p->B);
   g.total_q = p->total_q;
   g.total_k = p->total_k;
-  g.max_q = p->max_seqlen_q;
-  g.max_k = p->max_seqlen_k;
-  g.nbq = (int)(round_up((size_t)p->max_seqlen_q, sage::kTokenPad) / 64);
-  g.nbk = (int)(round_up((size_t)p->max_seqlen_k, sage::kTokenPad) / 64);
+  // no sequence is longer than its tensor: a looser bound only sized idle grids
+  g.max_q = std::min(p->max_seqlen_q, p->total_q);
+  g.max_k = std::min(p->max_seqlen_k, p->total_k);
+  g.nbq = (int)(round_up((size_t)g.max_q, sage::kTokenPad) / 64);
+  g.nbk = (int)(round_up((size_t)g.max_k, sage::kTokenPad) / 64);
   return s;
 }
 

@@ -249,7 +249,8 @@ sage_status sage_attn_bwd(const sage_problem *p, const void *q, const void *k, c
  * slot, about H * (total_q / 128 + B) * min(max_seqlen_k, total_k) floats).  Causal masking is top-left aligned per sequence (query
  * i sees keys j <= i).  A query with no key (an empty key sequence) gets a zero
  * output and LSE -inf.  max_seqlen_q / max_seqlen_k bound every sequence's
- * length (host values, as FlashAttention takes them); the kernels clamp the
+ * length (host values, as FlashAttention takes them; bounds above total_q /
+ * total_k are clamped to them); the kernels clamp the
  * device offsets to [0, total] and the lengths to the bounds, so malformed
  * offsets give unspecified values but no access outside the tensors.
  * total_q = 0 returns SAGE_OK without launching; k and v may be NULL when

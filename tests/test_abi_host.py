@@ -176,6 +176,19 @@ def test_varlen_pointer_and_workspace_checks():
                                   None) == S.OK
 
 
+def test_varlen_bounds_beyond_the_totals_are_clamped():
+    """max_seqlen_q / max_seqlen_k up to INT32_MAX: no sequence can be longer than its tensor, so
+    the bounds are clamped to total_q / total_k (no integer overflow in the checks, the same
+    workspace as exact bounds, for every format pair)."""
+    L = S.lib()
+    for qk, pv in ((1, 2), (3, 2), (7, 3), (6, 5)):
+        a, b = ctypes.c_size_t(), ctypes.c_size_t()
+        assert L.sage_varlen_ws_size(ctypes.byref(_vp(qk_fmt=qk, pv_fmt=pv)), ctypes.byref(a)) == S.OK
+        loose = _vp(qk_fmt=qk, pv_fmt=pv, max_seqlen_q=2 ** 31 - 1, max_seqlen_k=2 ** 31 - 1)
+        assert L.sage_varlen_ws_size(ctypes.byref(loose), ctypes.byref(b)) == S.OK
+        assert b.value == a.value   # (per-block strips: 50 and 90 keys both round up to 128)
+
+
 def test_varlen_workspace_covers_every_sequence_padding():
     """Per head, each sequence gets a 64-aligned start and room for its length rounded up to 128
     before the next one begins; the workspace grows with the batch size accordingly."""
