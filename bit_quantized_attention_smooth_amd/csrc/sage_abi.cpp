@@ -65,8 +65,9 @@ sage_status check_problem(const sage_problem* p) {
   if (!p) return fail(SAGE_ERR_INVALID_ARG, "problem descriptor is NULL");
   if (p->B < 1 || p->H < 1 || p->N < 1)
     return fail(SAGE_ERR_INVALID_ARG, "B, H and N must be >= 1 (got B=%d H=%d N=%d)", p->B, p->H, p->N);
+  // (token indices inside an instance are 32-bit: N up to 2^30)
   if ((long long)p->B * p->H * ((long long)p->N + sage::kTokenPad) * p->d > (1LL << 40) ||
-      (long long)p->B * p->H > kMaxInstances)
+      (long long)p->B * p->H > kMaxInstances || p->N > (1 << 30))
     return fail(SAGE_ERR_INVALID_ARG, "problem too large");
   return check_common(p->d, p->causal, p->sm_scale, p->io_dtype, p->qk_fmt, p->pv_fmt);
 }

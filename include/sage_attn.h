@@ -80,7 +80,8 @@ enum { SAGE_DT_BF16 = 0, SAGE_DT_F16 = 1 };
 /* Supported (qk_fmt, pv_fmt) pairs: (INT8, FP8), (INT8, F16), (INT8_TOKEN, FP8),
  * (INT8_TOKEN, F16), (MXFP4 or MXFP4_QBLOCK, FP8 or MXFP4 or MXFP8). */
 typedef struct {
-    int B, H, N, d;
+    int B, H, N, d;      /* B, H, N >= 1 with B*H <= 65535, N <= 2^30 and B*H*(N+128)*d <= 2^40;
+                            d is 64 or 128 */
     int causal;          /* 0 or 1 */
     float sm_scale;      /* finite, > 0; typically 1/sqrt(d) */
     int io_dtype;        /* SAGE_DT_* */

@@ -36,6 +36,7 @@ def _p(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), S.ERR_INVALID_ARG), (dict(N=0), S.ERR_INVALID_ARG), (dict(H=-1), S.ERR_INVALID_ARG),
+    (dict(B=1, H=1, d=64, N=2 ** 31 - 1), S.ERR_INVALID_ARG), (dict(B=1, H=1, d=64, N=2 ** 30 + 1), S.ERR_INVALID_ARG),
     (dict(d=96), S.ERR_UNSUPPORTED), (dict(d=256), S.ERR_UNSUPPORTED),
     (dict(sm_scale=0.0), S.ERR_INVALID_ARG), (dict(sm_scale=float("nan")), S.ERR_INVALID_ARG),
     (dict(sm_scale=float("inf")), S.ERR_INVALID_ARG), (dict(causal=2), S.ERR_INVALID_ARG),
