@@ -33,12 +33,13 @@
 // are already the B operand of the PV MFMA O^T = V^T P~^T (A = V^T, rows =
 // channels, K = the same 32 keys).
 //
-// Pipeline, one barrier per tile.  Most kernels (kOneBuf) hold one score tile per wave:
-// tile j issues its own QK MFMAs, with K and V loaded one tile ahead into two LDS buffers,
-// and the registers saved fit three workgroups per CU, so other waves fill the matrix and
-// vector units while one waits.  The others (two workgroups per CU) hold two: the QK MFMAs
-// of tile j+1 overlap the softmax of tile j (issued before it, or spread through its exp /
-// pack stream where that measured faster), with K one tile ahead of V.
+// Pipeline, one barrier per tile.  At d = 128 (kOneBuf: every pair but fp16 P~V) a wave
+// holds one score tile: tile j issues its own QK MFMAs, with K and V loaded one tile ahead
+// into two LDS buffers, and the registers saved fit three workgroups per CU, so other waves
+// fill the matrix and vector units while one waits.  The others (d = 64, fp16 P~V; two
+// workgroups per CU) hold two: the QK MFMAs of tile j+1 overlap the softmax of tile j
+// (issued before it, or spread through its exp / pack stream where that measured faster),
+// with K one tile ahead of V.
 // Causal: one query tile per workgroup, longest first (see attn_fwd_kernel).
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
