@@ -231,6 +231,33 @@ def test_varlen_full_size_llm_prefill_sampled(sage):
         assert cos(og, o_sim) >= 0.9999
 
 
+def test_varlen_full_size_qblock_sampled(sage):
+    """Per-block Q smoothing on the full-size packed prefill batch (8 sequences from 256 to 4096
+    tokens at starts off the 128-row grid, 32 query / 8 KV heads, d = 128, causal): the oracle
+    recomputes the shortest and the last sequence."""
+    import oracle
+    from bit_quantized_attention_smooth_amd.workloads import varlen_workload
+    banner("varlen full size mxfp4_qblock")
+    x, w = varlen_workload("varlen_gqa_causal_b8h32kv8t16384d128")
+    dev = device()
+    o = sage.sageattn_varlen(x["q"].to(dev), x["k"].to(dev), x["v"].to(dev), x["cu_q"].to(dev), x["cu_k"].to(dev),
+                             w["max_seqlen"], w["max_seqlen"], causal=True, sm_scale=w["sm_scale"],
+                             qk_fmt="mxfp4_qblock", pv_fmt="fp8")
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    cu = x["cu_q"].numpy()
+    lens = cu[1:] - cu[:-1]
+    for b in (int(np.argmin(lens)), len(cu) - 2):
+        rows = slice(cu[b], cu[b + 1])
+        sub = {n: _f32(x[n][rows]) for n in "qkv"}
+        c = np.array([0, cu[b + 1] - cu[b]], np.int32)
+        o_sim, _, _, sl = oracle.attn_varlen(sub["q"], sub["k"], sub["v"], c, c, True, w["sm_scale"],
+                                             qk_fmt="mxfp4_qblock", pv_fmt="fp8", tile=TILE, slack=True)
+        og = to_np64(o[rows])
+        assert within(og, o_sim, sl), excess(og, o_sim, sl)
+        assert cos(og, o_sim) >= 0.9999
+
+
 @pytest.mark.parametrize("qk,pv", [("int8", "fp8"), ("mxfp4", "fp8")])
 def test_varlen_beyond_2e31_elements_equals_fixed_length(sage, qk, pv):
     """Packed tensors of more than 2^31 elements (2 sequences of 65575 tokens, 128 heads,
