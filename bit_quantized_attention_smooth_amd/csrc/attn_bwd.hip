@@ -791,11 +791,15 @@ hipError_t bwd_run(const Shape& s, const void* q, const void* k, const void* v, 
   const int grid = BH * (s.Np / 128);
   // dQ first: it turns D into D^ = D + rowsum(dS), which the dK/dV kernel then uses
   if (s.causal) {
-    bwd_dq_kernel<D, true, DT><<<grid, 256, 0, st>>>(bp, dq, s.N, s.Np, BH, s.sm_scale);
-    bwd_dkdv_kernel<D, true, DT><<<grid, 256, 0, st>>>(bp, dk, dv, s.N, s.Np, BH, s.sm_scale);
+    bwd_dq_kernel<D, true, DT><<<grid, 256, debug_lds_pad(bwd_dq_kernel<D, true, DT>), st>>>(bp, dq, s.N, s.Np, BH,
+                                                                                          s.sm_scale);
+    bwd_dkdv_kernel<D, true, DT><<<grid, 256, debug_lds_pad(bwd_dkdv_kernel<D, true, DT>), st>>>(bp, dk, dv, s.N, s.Np,
+                                                                                              BH, s.sm_scale);
   } else {
-    bwd_dq_kernel<D, false, DT><<<grid, 256, 0, st>>>(bp, dq, s.N, s.Np, BH, s.sm_scale);
-    bwd_dkdv_kernel<D, false, DT><<<grid, 256, 0, st>>>(bp, dk, dv, s.N, s.Np, BH, s.sm_scale);
+    bwd_dq_kernel<D, false, DT><<<grid, 256, debug_lds_pad(bwd_dq_kernel<D, false, DT>), st>>>(bp, dq, s.N, s.Np, BH,
+                                                                                          s.sm_scale);
+    bwd_dkdv_kernel<D, false, DT><<<grid, 256, debug_lds_pad(bwd_dkdv_kernel<D, false, DT>), st>>>(bp, dk, dv, s.N, s.Np,
+                                                                                              BH, s.sm_scale);
   }
   return hipGetLastError();
 }

@@ -887,9 +887,11 @@ template <int D, int QK, int DT, int PV, bool FINE>
 static hipError_t fwd_dispatch(const Shape& s, const FwdArgs& a, hipStream_t st) {
   const int grid = s.g.B * s.g.H * a.nqt;
   if (s.causal)
-    attn_fwd_kernel<D, QK, true, DT, PV, FINE><<<grid, 256, 0, st>>>(a);
+    attn_fwd_kernel<D, QK, true, DT, PV, FINE>
+        <<<grid, 256, debug_lds_pad(attn_fwd_kernel<D, QK, true, DT, PV, FINE>), st>>>(a);
   else
-    attn_fwd_kernel<D, QK, false, DT, PV, FINE><<<grid, 256, 0, st>>>(a);
+    attn_fwd_kernel<D, QK, false, DT, PV, FINE>
+        <<<grid, 256, debug_lds_pad(attn_fwd_kernel<D, QK, false, DT, PV, FINE>), st>>>(a);
   return hipGetLastError();
 }
 

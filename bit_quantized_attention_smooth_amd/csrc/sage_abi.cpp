@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <string>
 
 #include "../../include/sage_attn.h"
 #include "sage_launch.hpp"
@@ -293,6 +294,40 @@ sage_status scratch_for(void* stream, void** out) {
   return SAGE_OK;
 }
 
+// ---- SAGE_LOG=1: one line on stderr per outermost entry-point call (name, problem, status) ----
+bool log_on() {
+  const char* e = getenv("SAGE_LOG");
+  return e && strcmp(e, "1") == 0;
+}
+thread_local int g_depth = 0;   // entry points calling entry points log once
+struct CallScope {
+  CallScope() { ++g_depth; }
+  ~CallScope() { --g_depth; }
+};
+std::string describe(const sage_problem* p) {
+  if (!p) return "problem=NULL";
+  char b[160];
+  snprintf(b, sizeof b, "B=%d H=%d N=%d d=%d causal=%d sm=%g io=%d qk=%d pv=%d", p->B, p->H, p->N, p->d, p->causal,
+           (double)p->sm_scale, p->io_dtype, p->qk_fmt, p->pv_fmt);
+  return b;
+}
+std::string describe(const sage_varlen_problem* p) {
+  if (!p) return "problem=NULL";
+  char b[200];
+  snprintf(b, sizeof b, "B=%d H=%d H_kv=%d d=%d causal=%d sm=%g io=%d qk=%d pv=%d total_q=%d total_k=%d max_q=%d max_k=%d",
+           p->B, p->H, p->H_kv, p->d, p->causal, (double)p->sm_scale, p->io_dtype, p->qk_fmt, p->pv_fmt, p->total_q,
+           p->total_k, p->max_seqlen_q, p->max_seqlen_k);
+  return b;
+}
+// (the problem text is formatted only when the line is printed)
+template <typename Describe>
+sage_status logged(const char* fn, Describe what, sage_status s) {
+  if (g_depth == 1 && log_on())
+    fprintf(stderr, "sage: %s(%s) -> %s%s%s\n", fn, what().c_str(), sage_status_string(s), s == SAGE_OK ? "" : ": ",
+            s == SAGE_OK ? "" : g_err);
+  return s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -318,159 +353,199 @@ const char* sage_status_string(sage_status s) {
 }
 
 sage_status sage_quant_size(const sage_problem* p, size_t* bytes, sage_quant_layout* layout) {
-  sage_status s = check_problem(p);
-  if (s != SAGE_OK) return s;
-  if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
-  sage_quant_layout L;
-  compute_layout(p, &L);
-  *bytes = L.total;
-  if (layout) *layout = L;
-  return SAGE_OK;
+  CallScope cs_;
+  const sage_status st_ = [&]() -> sage_status {
+    sage_status s = check_problem(p);
+    if (s != SAGE_OK) return s;
+    if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
+    sage_quant_layout L;
+    compute_layout(p, &L);
+    *bytes = L.total;
+    if (layout) *layout = L;
+    return SAGE_OK;
+  }();
+  return logged(__func__, [&] { return describe(p); }, st_);
 }
 
 sage_status sage_quantize(const void* q, const void* k, const void* v, const sage_problem* p, void* quant_buf,
                           size_t quant_bytes, void* stream) {
-  sage_status s = check_problem(p);
-  if (s != SAGE_OK) return s;
-  if ((s = check_tensors({q, k, v, quant_buf})) != SAGE_OK) return s;
-  sage_quant_layout L;
-  compute_layout(p, &L);
-  if (quant_bytes < L.total)
-    return fail(SAGE_ERR_WORKSPACE, "quant buffer has %zu bytes, needs %zu", quant_bytes, L.total);
-  hipError_t e = sage::launch_prologue(q, k, v, to_shape(p), resolve(quant_buf, p, L), (hipStream_t)stream);
-  return e == hipSuccess ? SAGE_OK : hip_fail(e, "quantize launch");
+  CallScope cs_;
+  const sage_status st_ = [&]() -> sage_status {
+    sage_status s = check_problem(p);
+    if (s != SAGE_OK) return s;
+    if ((s = check_tensors({q, k, v, quant_buf})) != SAGE_OK) return s;
+    sage_quant_layout L;
+    compute_layout(p, &L);
+    if (quant_bytes < L.total)
+      return fail(SAGE_ERR_WORKSPACE, "quant buffer has %zu bytes, needs %zu", quant_bytes, L.total);
+    hipError_t e = sage::launch_prologue(q, k, v, to_shape(p), resolve(quant_buf, p, L), (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : hip_fail(e, "quantize launch");
+  }();
+  return logged(__func__, [&] { return describe(p); }, st_);
 }
 
 sage_status sage_attn_fwd_quantized(const void* quant_buf, size_t quant_bytes, const sage_problem* p, void* o,
                                     float* lse, void* stream) {
-  sage_status s = check_problem(p);
-  if (s != SAGE_OK) return s;
-  if ((s = check_tensors({quant_buf, o})) != SAGE_OK) return s;
-  if (lse && !aligned16(lse)) return fail(SAGE_ERR_INVALID_ARG, "lse must be 16-byte aligned");
-  sage_quant_layout L;
-  compute_layout(p, &L);
-  if (quant_bytes < L.total)
-    return fail(SAGE_ERR_WORKSPACE, "quant buffer has %zu bytes, needs %zu", quant_bytes, L.total);
-  hipError_t e = sage::launch_attn_fwd(to_shape(p), resolve(const_cast<void*>(quant_buf), p, L), o, lse,
-                                       (hipStream_t)stream);
-  return e == hipSuccess ? SAGE_OK : hip_fail(e, "attention launch");
+  CallScope cs_;
+  const sage_status st_ = [&]() -> sage_status {
+    sage_status s = check_problem(p);
+    if (s != SAGE_OK) return s;
+    if ((s = check_tensors({quant_buf, o})) != SAGE_OK) return s;
+    if (lse && !aligned16(lse)) return fail(SAGE_ERR_INVALID_ARG, "lse must be 16-byte aligned");
+    sage_quant_layout L;
+    compute_layout(p, &L);
+    if (quant_bytes < L.total)
+      return fail(SAGE_ERR_WORKSPACE, "quant buffer has %zu bytes, needs %zu", quant_bytes, L.total);
+    hipError_t e = sage::launch_attn_fwd(to_shape(p), resolve(const_cast<void*>(quant_buf), p, L), o, lse,
+                                         (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : hip_fail(e, "attention launch");
+  }();
+  return logged(__func__, [&] { return describe(p); }, st_);
 }
 
 sage_status sage_attn_fwd_ws_size(const sage_problem* p, size_t* bytes) { return sage_quant_size(p, bytes, nullptr); }
 
 sage_status sage_attn_fwd_ex(const sage_problem* p, const void* q, const void* k, const void* v, void* o, float* lse,
                              void* ws, size_t ws_bytes, void* stream) {
-  sage_status s = check_problem(p);
-  if (s != SAGE_OK) return s;
-  if ((s = check_tensors({q, k, v, o, ws})) != SAGE_OK) return s;
-  if (lse && !aligned16(lse)) return fail(SAGE_ERR_INVALID_ARG, "lse must be 16-byte aligned");
-  sage_quant_layout L;
-  compute_layout(p, &L);
-  if (ws_bytes < L.total) return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
-  const sage::Shape sh = to_shape(p);
-  const sage::QuantPtrs qp = resolve(ws, p, L);
-  hipError_t e = sage::launch_prologue(q, k, v, sh, qp, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "quantize launch");
-  e = sage::launch_attn_fwd(sh, qp, o, lse, (hipStream_t)stream);
-  return e == hipSuccess ? SAGE_OK : hip_fail(e, "attention launch");
+  CallScope cs_;
+  const sage_status st_ = [&]() -> sage_status {
+    sage_status s = check_problem(p);
+    if (s != SAGE_OK) return s;
+    if ((s = check_tensors({q, k, v, o, ws})) != SAGE_OK) return s;
+    if (lse && !aligned16(lse)) return fail(SAGE_ERR_INVALID_ARG, "lse must be 16-byte aligned");
+    sage_quant_layout L;
+    compute_layout(p, &L);
+    if (ws_bytes < L.total) return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+    const sage::Shape sh = to_shape(p);
+    const sage::QuantPtrs qp = resolve(ws, p, L);
+    hipError_t e = sage::launch_prologue(q, k, v, sh, qp, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    e = sage::launch_attn_fwd(sh, qp, o, lse, (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : hip_fail(e, "attention launch");
+  }();
+  return logged(__func__, [&] { return describe(p); }, st_);
 }
 
 sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int causal,
                           float sm_scale, int qk_fmt, int pv_fmt, void* stream) {
   sage_problem p = make_problem(B, H, N, d, causal, sm_scale, SAGE_DT_BF16, qk_fmt, pv_fmt);
-  sage_status s = check_problem(&p);
-  if (s != SAGE_OK) return s;
-  if ((s = check_tensors({q, k, v, o})) != SAGE_OK) return s;
-  size_t bytes = 0;
-  sage_quant_size(&p, &bytes, nullptr);
-  void* ws = nullptr;
-  if (inject_alloc_failure()) return fail(SAGE_ERR_OUT_OF_MEMORY, "injected allocation failure");
-  hipError_t e = hipMallocAsync(&ws, bytes, (hipStream_t)stream);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(SAGE_ERR_OUT_OF_MEMORY, "hipMallocAsync(%zu): %s", bytes, hipGetErrorString(e));
-  }
-  s = sage_attn_fwd_ex(&p, q, k, v, o, nullptr, ws, bytes, stream);
-  hipError_t f = hipFreeAsync(ws, (hipStream_t)stream);
-  if (s == SAGE_OK && f != hipSuccess) return hip_fail(f, "hipFreeAsync");
-  return s;
+  CallScope cs_;
+  const sage_status st_ = [&]() -> sage_status {
+    sage_status s = check_problem(&p);
+    if (s != SAGE_OK) return s;
+    if ((s = check_tensors({q, k, v, o})) != SAGE_OK) return s;
+    size_t bytes = 0;
+    sage_quant_size(&p, &bytes, nullptr);
+    void* ws = nullptr;
+    if (inject_alloc_failure()) return fail(SAGE_ERR_OUT_OF_MEMORY, "injected allocation failure");
+    hipError_t e = hipMallocAsync(&ws, bytes, (hipStream_t)stream);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(SAGE_ERR_OUT_OF_MEMORY, "hipMallocAsync(%zu): %s", bytes, hipGetErrorString(e));
+    }
+    s = sage_attn_fwd_ex(&p, q, k, v, o, nullptr, ws, bytes, stream);
+    hipError_t f = hipFreeAsync(ws, (hipStream_t)stream);
+    if (s == SAGE_OK && f != hipSuccess) return hip_fail(f, "hipFreeAsync");
+    return s;
+  }();
+  return logged(__func__, [&] { return describe(&p); }, st_);
 }
 
 sage_status sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
                                   int causal, float sm_scale, int qk_fmt, int pv_fmt, void* stream) {
   sage_problem p = make_problem(B, H, N, d, causal, sm_scale, SAGE_DT_BF16, qk_fmt, pv_fmt);
-  sage_status s = check_problem(&p);
-  if (s != SAGE_OK) return s;
-  if ((s = check_tensors({q, k, v, o})) != SAGE_OK) return s;
-  size_t bytes = 0;
-  sage_quant_size(&p, &bytes, nullptr);
-  if (bytes > kScratchBytes)
-    return fail(SAGE_ERR_WORKSPACE, "the problem needs %zu bytes of scratch; the no-allocation entry holds %zu "
-                "(use sage_attn_fwd_ex with a caller workspace)", bytes, kScratchBytes);
-  void* ws = nullptr;
-  if ((s = scratch_for(stream, &ws)) != SAGE_OK) return s;
-  return sage_attn_fwd_ex(&p, q, k, v, o, nullptr, ws, bytes, stream);
+  CallScope cs_;
+  const sage_status st_ = [&]() -> sage_status {
+    sage_status s = check_problem(&p);
+    if (s != SAGE_OK) return s;
+    if ((s = check_tensors({q, k, v, o})) != SAGE_OK) return s;
+    size_t bytes = 0;
+    sage_quant_size(&p, &bytes, nullptr);
+    if (bytes > kScratchBytes)
+      return fail(SAGE_ERR_WORKSPACE, "the problem needs %zu bytes of scratch; the no-allocation entry holds %zu "
+                  "(use sage_attn_fwd_ex with a caller workspace)", bytes, kScratchBytes);
+    void* ws = nullptr;
+    if ((s = scratch_for(stream, &ws)) != SAGE_OK) return s;
+    return sage_attn_fwd_ex(&p, q, k, v, o, nullptr, ws, bytes, stream);
+  }();
+  return logged(__func__, [&] { return describe(&p); }, st_);
 }
 
 sage_status sage_attn_bwd_ws_size(const sage_problem* p, size_t* bytes) {
-  sage_status s = check_problem(p);
-  if (s != SAGE_OK) return s;
-  if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
-  if (p->qk_fmt != SAGE_FMT_INT8 || p->pv_fmt != SAGE_FMT_FP8)
-    return fail(SAGE_ERR_UNSUPPORTED, "the backward supports qk_fmt=INT8, pv_fmt=FP8 only");
-  sage_quant_layout L;
-  compute_layout(p, &L);
-  *bytes = L.total + sage::attn_bwd_ws_bytes(to_shape(p));
-  return SAGE_OK;
+  CallScope cs_;
+  const sage_status st_ = [&]() -> sage_status {
+    sage_status s = check_problem(p);
+    if (s != SAGE_OK) return s;
+    if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
+    if (p->qk_fmt != SAGE_FMT_INT8 || p->pv_fmt != SAGE_FMT_FP8)
+      return fail(SAGE_ERR_UNSUPPORTED, "the backward supports qk_fmt=INT8, pv_fmt=FP8 only");
+    sage_quant_layout L;
+    compute_layout(p, &L);
+    *bytes = L.total + sage::attn_bwd_ws_bytes(to_shape(p));
+    return SAGE_OK;
+  }();
+  return logged(__func__, [&] { return describe(p); }, st_);
 }
 
 sage_status sage_attn_bwd(const sage_problem* p, const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
                           void* stream) {
-  size_t need = 0;
-  sage_status s = sage_attn_bwd_ws_size(p, &need);
-  if (s != SAGE_OK) return s;
-  if ((s = check_tensors({q, k, v, o, dout, lse, dq, dk, dv, ws})) != SAGE_OK) return s;
-  if (ws_bytes < need) return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
-  sage_quant_layout L;
-  compute_layout(p, &L);
-  hipError_t e = sage::launch_attn_bwd(to_shape(p), q, k, v, o, dout, lse, dq, dk, dv, ws, L.total,
-                                       resolve(ws, p, L), (hipStream_t)stream);
-  return e == hipSuccess ? SAGE_OK : hip_fail(e, "backward launch");
+  CallScope cs_;
+  const sage_status st_ = [&]() -> sage_status {
+    size_t need = 0;
+    sage_status s = sage_attn_bwd_ws_size(p, &need);
+    if (s != SAGE_OK) return s;
+    if ((s = check_tensors({q, k, v, o, dout, lse, dq, dk, dv, ws})) != SAGE_OK) return s;
+    if (ws_bytes < need) return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+    sage_quant_layout L;
+    compute_layout(p, &L);
+    hipError_t e = sage::launch_attn_bwd(to_shape(p), q, k, v, o, dout, lse, dq, dk, dv, ws, L.total,
+                                         resolve(ws, p, L), (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : hip_fail(e, "backward launch");
+  }();
+  return logged(__func__, [&] { return describe(p); }, st_);
 }
 
 sage_status sage_varlen_ws_size(const sage_varlen_problem* p, size_t* bytes) {
-  sage_status s = check_varlen(p);
-  if (s != SAGE_OK) return s;
-  if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
-  sage_quant_layout L;
-  compute_layout(extents(p), p->d, p->qk_fmt, p->pv_fmt, &L);
-  *bytes = L.total;
-  return SAGE_OK;
+  CallScope cs_;
+  const sage_status st_ = [&]() -> sage_status {
+    sage_status s = check_varlen(p);
+    if (s != SAGE_OK) return s;
+    if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
+    sage_quant_layout L;
+    compute_layout(extents(p), p->d, p->qk_fmt, p->pv_fmt, &L);
+    *bytes = L.total;
+    return SAGE_OK;
+  }();
+  return logged(__func__, [&] { return describe(p); }, st_);
 }
 
 sage_status sage_attn_varlen_fwd(const sage_varlen_problem* p, const void* q, const void* k, const void* v,
                                  const int* cu_seqlens_q, const int* cu_seqlens_k, void* o, float* lse, void* ws,
                                  size_t ws_bytes, void* stream) {
-  sage_status s = check_varlen(p);
-  if (s != SAGE_OK) return s;
-  if (!cu_seqlens_q || !cu_seqlens_k || (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
-      (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
-    return fail(SAGE_ERR_INVALID_ARG, "cu_seqlens_q / cu_seqlens_k must be non-NULL, 4-byte aligned");
-  if (p->total_q == 0) return SAGE_OK;   // no query rows: nothing to compute
-  if ((s = check_tensors({q, o, ws})) != SAGE_OK) return s;
-  if (p->total_k > 0 && (s = check_tensors({k, v})) != SAGE_OK) return s;
-  if (lse && !aligned16(lse)) return fail(SAGE_ERR_INVALID_ARG, "lse must be 16-byte aligned");
-  sage_quant_layout L;
-  compute_layout(extents(p), p->d, p->qk_fmt, p->pv_fmt, &L);
-  if (ws_bytes < L.total) return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
-  const sage::Shape sh = to_shape(p, cu_seqlens_q, cu_seqlens_k);
-  const sage::QuantPtrs qp = resolve(ws, (size_t)p->B * p->H, p->d, L);
-  hipError_t e = sage::launch_prologue(q, k, v, sh, qp, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "quantize launch");
-  if (sh.g.nbq == 0) return SAGE_OK;     // max_seqlen_q == 0: every sequence is empty
-  e = sage::launch_attn_fwd(sh, qp, o, lse, (hipStream_t)stream);
-  return e == hipSuccess ? SAGE_OK : hip_fail(e, "attention launch");
+  CallScope cs_;
+  const sage_status st_ = [&]() -> sage_status {
+    sage_status s = check_varlen(p);
+    if (s != SAGE_OK) return s;
+    if (!cu_seqlens_q || !cu_seqlens_k || (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
+        (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+      return fail(SAGE_ERR_INVALID_ARG, "cu_seqlens_q / cu_seqlens_k must be non-NULL, 4-byte aligned");
+    if (p->total_q == 0) return SAGE_OK;   // no query rows: nothing to compute
+    if ((s = check_tensors({q, o, ws})) != SAGE_OK) return s;
+    if (p->total_k > 0 && (s = check_tensors({k, v})) != SAGE_OK) return s;
+    if (lse && !aligned16(lse)) return fail(SAGE_ERR_INVALID_ARG, "lse must be 16-byte aligned");
+    sage_quant_layout L;
+    compute_layout(extents(p), p->d, p->qk_fmt, p->pv_fmt, &L);
+    if (ws_bytes < L.total) return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+    const sage::Shape sh = to_shape(p, cu_seqlens_q, cu_seqlens_k);
+    const sage::QuantPtrs qp = resolve(ws, (size_t)p->B * p->H, p->d, L);
+    hipError_t e = sage::launch_prologue(q, k, v, sh, qp, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    if (sh.g.nbq == 0) return SAGE_OK;     // max_seqlen_q == 0: every sequence is empty
+    e = sage::launch_attn_fwd(sh, qp, o, lse, (hipStream_t)stream);
+    return e == hipSuccess ? SAGE_OK : hip_fail(e, "attention launch");
+  }();
+  return logged(__func__, [&] { return describe(p); }, st_);
 }
 
 }  // extern "C"

@@ -4,6 +4,7 @@
 #include <stddef.h>
 #include <algorithm>
 #include <stdint.h>
+#include <stdlib.h>
 
 namespace sage {
 
@@ -161,6 +162,25 @@ __device__ __forceinline__ size_t ds_base(const SeqGeo& g, int b, int h) {
   return (size_t)h * g.Tk + packed_base(s, b);
 }
 #endif
+
+// SAGE_DEBUG_LDS_PAD=<bytes>: extra dynamic LDS on the fused forward and backward launches, up
+// to what one workgroup may hold, so that fewer workgroups share a CU.  For debugging: the
+// results must not change (a difference would reveal an LDS race or a timing dependence).
+template <typename Kernel>
+inline size_t debug_lds_pad(Kernel kernel) {
+  const char* e = getenv("SAGE_DEBUG_LDS_PAD");
+  const long want = e ? strtol(e, nullptr, 10) : 0;
+  if (want <= 0) return 0;
+  int dev = 0, cap = 0;
+  hipFuncAttributes at;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cap, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      hipFuncGetAttributes(&at, reinterpret_cast<const void*>(kernel)) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const size_t room = (size_t)cap > at.sharedSizeBytes ? (size_t)cap - at.sharedSizeBytes : 0;
+  return std::min((size_t)want, room);
+}
 
 struct Shape {
   int B, H, N, d, Np, causal, io_dtype, qk_fmt, pv_fmt;

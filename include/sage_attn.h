@@ -44,6 +44,12 @@ extern "C" {
 
 #define SAGE_ABI_VERSION 2
 
+/* Environment (debugging only; no effect on results): SAGE_LOG=1 prints one line on stderr per
+ * entry-point call (problem, status, error text); SAGE_DEBUG_LDS_PAD=<bytes> adds dynamic LDS
+ * to the fused forward and backward launches, lowering how many workgroups share a CU (a
+ * result that changed with it would reveal an LDS race); SAGE_FAULT_INJECT=alloc makes the
+ * allocating entry point fail its allocation. */
+
 typedef enum {
     SAGE_OK = 0,
     SAGE_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad scale, misaligned pointer */

@@ -268,3 +268,30 @@ def test_noalloc_entry_rejects_problems_beyond_its_scratch():
     assert b"64" in L.sage_last_error() or b"67108864" in L.sage_last_error()
     assert L.sage_attn_fwd_noalloc(None, FAKE, FAKE, FAKE, 1, 2, 100, 64, 0, 0.125, 1, 2, None) == S.ERR_INVALID_ARG
     assert L.sage_attn_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, 1, 2, 100, 96, 0, 0.125, 1, 2, None) == S.ERR_UNSUPPORTED
+
+
+def test_sage_log_prints_one_line_per_outermost_call():
+    """SAGE_LOG=1: each entry-point call prints one line on stderr (name, problem, status and
+    the error text); without it the library prints nothing.  A host-only call in a child
+    process, so the variable is read as a user would set it."""
+    import subprocess
+    import sys
+    code = ("import ctypes, bit_quantized_attention_smooth_amd as S\n"
+            "L = S.lib(); n = ctypes.c_size_t()\n"
+            "p = S.Problem(1, 2, 256, 64, 0, 0.125, 0, 1, 2)\n"
+            "assert L.sage_quant_size(ctypes.byref(p), ctypes.byref(n), None) == S.OK\n"
+            "p.d = 96\n"
+            "assert L.sage_quant_size(ctypes.byref(p), ctypes.byref(n), None) == S.ERR_UNSUPPORTED\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PYTHONPATH=root)
+    env.pop("SAGE_LOG", None)
+    quiet = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120)
+    assert quiet.returncode == 0, quiet.stderr
+    assert "sage:" not in quiet.stderr
+    env["SAGE_LOG"] = "1"
+    loud = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120)
+    assert loud.returncode == 0, loud.stderr
+    lines = [l for l in loud.stderr.splitlines() if l.startswith("sage:")]
+    assert len(lines) == 2, loud.stderr
+    assert lines[0].startswith("sage: sage_quant_size(B=1 H=2 N=256 d=64") and lines[0].endswith("-> ok")
+    assert "d=96" in lines[1] and "-> unsupported: head dim d=96" in lines[1]
