@@ -171,6 +171,13 @@ def sageattn(q, k, v, *, causal=False, sm_scale=None, qk_fmt="int8", pv_fmt="fp8
 attn = sageattn
 
 
+def sageattn_qk_int8_pv_fp16(q, k, v, *, causal=False, sm_scale=None, return_lse=False, workspace=None):
+    """The 16-bit P~V fallback under the entry name the SageAttention3 code-link page lists
+    (INT8 QK^T with IEEE fp16 P~ and V, fp32 accumulation on the matrix cores)."""
+    return sageattn(q, k, v, causal=causal, sm_scale=sm_scale, qk_fmt="int8", pv_fmt="f16", return_lse=return_lse,
+                    workspace=workspace)
+
+
 def varlen_problem(B, H, H_kv, d, total_q, total_k, max_seqlen_q, max_seqlen_k, *, causal=False, sm_scale=None,
                    dtype=torch.bfloat16, qk_fmt="int8", pv_fmt="fp8"):
     sm = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)

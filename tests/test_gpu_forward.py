@@ -522,3 +522,14 @@ def test_oneshot_entry_matches_ex(sage):
     b = sage.sageattn(g["q"], g["k"], g["v"], causal=True)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_named_fp16_pv_entry_is_the_f16_format(sage):
+    """sageattn_qk_int8_pv_fp16 (the entry name the code-link page lists) is the INT8 QK / fp16
+    P~V pair, bit for bit."""
+    banner("named fp16 P~V entry")
+    _, g = _inputs(1, 2, 300, 128, "bf16", seed=77, k_off=2.0)
+    a = sage.sageattn_qk_int8_pv_fp16(g["q"], g["k"], g["v"], causal=True, return_lse=True)
+    b = sage.sageattn(g["q"], g["k"], g["v"], causal=True, qk_fmt="int8", pv_fmt="f16", return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
