@@ -698,9 +698,14 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
     const uint8_t* qp = a.q_codes + (qi.tok0 + qrow) * D + 16 * hh;
 #pragma unroll
     for (int c = 0; c < NQF; c++) qf[c] = *reinterpret_cast<const v4i*>(qp + 32 * c);
-    // FINE: a step per query token; else one per 64-token block
-    qstep = reinterpret_cast<const float*>(a.q_scales)[FINE ? qi.tok0 + qrow : qi.tok0 / kTK + qrow / kTK] *
-            a.sm_log2e;
+    // FINE: a step per query token; else one per 64-token block, the same for the whole wave
+    // (its 32 queries lie in one block): a scalar register, not a vector one
+    if (FINE) {
+      qstep = reinterpret_cast<const float*>(a.q_scales)[qi.tok0 + qrow] * a.sm_log2e;
+    } else {
+      const float qs = reinterpret_cast<const float*>(a.q_scales)[qi.tok0 / kTK + qw / kTK] * a.sm_log2e;
+      qstep = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, qs)));
+    }
   } else {
     const uint8_t* qp = a.q_codes + (qi.tok0 + qrow) * (D / 2) + 16 * hh;
     const uint8_t* qe = reinterpret_cast<const uint8_t*>(a.q_scales) + (qi.tok0 + qrow) * (D / 32) + hh;
