@@ -716,11 +716,18 @@ __device__ __forceinline__ void run_qtile(const FwdArgs& a, int b, int h, int qt
       qsc[c] = qe[2 * c];
     }
   }
-  // K steps: one per 64-key tile, or (FINE) one per 32 keys; a lane reads its half's step.  Each
-  // tile's step is loaded one tile ahead, so the load completes under the end-of-tile wait
-  // instead of stalling the tile that uses it.
-  const float* kstep = reinterpret_cast<const float*>(a.k_scales) + (FINE ? kt0 / 32 + hh : kt0 / kTK);
-  auto kstep_of = [&](int t) { return QK == QK_INT8 ? kstep[FINE ? 2 * t : t] : 0.0f; };
+  // K steps: one per 64-key tile, or (FINE) one per 32 keys; a lane takes its half's step.  They
+  // are read-only during the kernel and the same for the whole wave (FINE: per lane half), so
+  // they come through the scalar cache (the constant address space) instead of as vector-memory
+  // loads, each tile's one tile ahead.
+  typedef __attribute__((address_space(4))) const float cfloat;
+  cfloat* kstep = (cfloat*)(uintptr_t)(reinterpret_cast<const float*>(a.k_scales) + (FINE ? kt0 / 32 : kt0 / kTK));
+  auto kstep_of = [&](int t) -> float {
+    if (QK != QK_INT8) return 0.0f;
+    if (!FINE) return kstep[t];
+    const float k0 = kstep[2 * t], k1 = kstep[2 * t + 1];
+    return hh ? k1 : k0;
+  };
 
   int ntiles = (NK + kTK - 1) / kTK;
   if (CAUSAL) ntiles = min(ntiles, (qbase + kQT - 1) / kTK + 1);
