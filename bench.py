@@ -366,14 +366,26 @@ def run_backward(name, S, torch, steps, warmup):
                                  S._ptr(g["do"]), S._ptr(lse), S._ptr(dq), S._ptr(dk), S._ptr(dv), S._ptr(wsb),
                                  nb.value, st))
 
+    def bwd_after_fwd():
+        # the training step's backward: the forward quantized into wsb (below), and that
+        # quantization of Q and K is reused (the backward does not modify it)
+        S._check(L.sage_attn_bwd_after_fwd(ctypes.byref(p), S._ptr(g["q"]), S._ptr(g["k"]), S._ptr(g["v"]), S._ptr(o),
+                                           S._ptr(g["do"]), S._ptr(lse), S._ptr(dq), S._ptr(dk), S._ptr(dv),
+                                           S._ptr(wsb), nb.value, st))
+
     ms_f, _ = time_region(fwd, steps, warmup, torch)
     fwd()
     ms_b, _ = time_region(bwd, steps, warmup, torch)
+    S._check(L.sage_attn_fwd_ex(ctypes.byref(p), S._ptr(g["q"]), S._ptr(g["k"]), S._ptr(g["v"]), S._ptr(o),
+                                S._ptr(lse), S._ptr(wsb), nb.value, st))
+    ms_r, _ = time_region(bwd_after_fwd, steps, warmup, torch)
     ops_f = attn_ops(B, H, N, d, causal)
     ops_b = 2.5 * ops_f          # 10 d ops per (query, key) pair vs 4 d in the forward
     return {"fwd_ms": round(ms_f, 4), "fwd_tops": round(ops_f / (ms_f * 1e-3) / 1e12, 1),
             "bwd_ms": round(ms_b, 4), "bwd_tops": round(ops_b / (ms_b * 1e-3) / 1e12, 1),
-            "bwd_frac": round(ops_b / (ms_b * 1e-3) / 1e12 / PEAK["int8_fp8"], 4)}
+            "bwd_frac": round(ops_b / (ms_b * 1e-3) / 1e12 / PEAK["int8_fp8"], 4),
+            "bwd_after_fwd_ms": round(ms_r, 4), "bwd_after_fwd_tops": round(ops_b / (ms_r * 1e-3) / 1e12, 1),
+            "bwd_after_fwd_frac": round(ops_b / (ms_r * 1e-3) / 1e12 / PEAK["int8_fp8"], 4)}
 
 
 def run_varlen(name, S, torch, steps, warmup):

@@ -30,6 +30,7 @@ DT = {torch.bfloat16: 0, torch.float16: 1}
 # Every symbol the header declares (kept in sync by a CPU test that parses the header).
 EXPORTS = ["sage_attn_fwd", "sage_attn_fwd_noalloc", "sage_quant_size", "sage_quantize", "sage_attn_fwd_quantized",
            "sage_attn_fwd_ws_size", "sage_attn_fwd_ex", "sage_attn_bwd_ws_size", "sage_attn_bwd",
+           "sage_attn_bwd_after_fwd",
            "sage_varlen_ws_size", "sage_attn_varlen_fwd",
            "sage_status_string", "sage_last_error", "sage_abi_version"]
 
@@ -82,6 +83,7 @@ def lib():
             "sage_attn_fwd_ex": [P, vp, vp, vp, vp, vp, vp, sz, vp],
             "sage_attn_bwd_ws_size": [P, ctypes.POINTER(sz)],
             "sage_attn_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "sage_attn_bwd_after_fwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "sage_varlen_ws_size": [ctypes.POINTER(VarlenProblem), ctypes.POINTER(sz)],
             "sage_attn_varlen_fwd": [ctypes.POINTER(VarlenProblem), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         }
@@ -254,19 +256,38 @@ def check_bwd_inputs(q, o, do, lse):
                          f"(the forward's LSE of fixed-length inputs)")
 
 
-def attn_bwd(q, k, v, o, do, lse, *, causal=False, sm_scale=None):
-    """8-bit backward: returns dQ, dK, dV in the input dtype."""
+def bwd_workspace(q, *, causal=False, sm_scale=None):
+    """A workspace for a training step: pass it to sageattn(..., workspace=) and then to
+    attn_bwd(..., fwd_workspace=), so the backward reuses the forward's quantization."""
+    B, H, N, d = q.shape
+    p = problem(B, H, N, d, causal=causal, sm_scale=sm_scale, dtype=q.dtype)
+    nbytes = ctypes.c_size_t()
+    _check(lib().sage_attn_bwd_ws_size(ctypes.byref(p), ctypes.byref(nbytes)))
+    return torch.empty(max(nbytes.value, 16), dtype=torch.uint8, device=q.device)
+
+
+def attn_bwd(q, k, v, o, do, lse, *, causal=False, sm_scale=None, fwd_workspace=None):
+    """8-bit backward: returns dQ, dK, dV in the input dtype.  fwd_workspace: the workspace the
+    forward of these q, k, v wrote (bwd_workspace); its quantization of Q and K is then reused
+    (sage_attn_bwd_after_fwd) instead of recomputed."""
     q, k, v = _qkv(q, k, v)
     B, H, N, d = q.shape
     check_bwd_inputs(q, o, do, lse)
     p = problem(B, H, N, d, causal=causal, sm_scale=sm_scale, dtype=q.dtype)
     nbytes = ctypes.c_size_t()
     _check(lib().sage_attn_bwd_ws_size(ctypes.byref(p), ctypes.byref(nbytes)))
-    ws = torch.empty(max(nbytes.value, 16), dtype=torch.uint8, device=q.device)
+    if fwd_workspace is not None:
+        if (fwd_workspace.dtype != torch.uint8 or fwd_workspace.device != q.device or
+                fwd_workspace.numel() < nbytes.value or not fwd_workspace.is_contiguous()):
+            raise ValueError("fwd_workspace must be a contiguous uint8 tensor on q's device of at least "
+                             f"{nbytes.value} bytes (bwd_workspace)")
+        ws, fn = fwd_workspace, lib().sage_attn_bwd_after_fwd
+    else:
+        ws, fn = torch.empty(max(nbytes.value, 16), dtype=torch.uint8, device=q.device), lib().sage_attn_bwd
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     o, do, lse = o.contiguous(), do.contiguous(), lse.contiguous()
-    _check(lib().sage_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
-                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()))
+    _check(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()))
     return dq, dk, dv
 
 
@@ -275,13 +296,15 @@ class SageAttnFn(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, causal=False, sm_scale=None):
-        o, lse = sageattn(q, k, v, causal=causal, sm_scale=sm_scale, return_lse=True)
-        ctx.save_for_backward(q, k, v, o, lse)
+        # the forward quantizes into a backward-sized workspace that the backward then reuses
+        ws = bwd_workspace(q, causal=causal, sm_scale=sm_scale)
+        o, lse = sageattn(q, k, v, causal=causal, sm_scale=sm_scale, return_lse=True, workspace=ws)
+        ctx.save_for_backward(q, k, v, o, lse, ws)
         ctx.causal, ctx.sm_scale = causal, sm_scale
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = attn_bwd(q, k, v, o, do, lse, causal=ctx.causal, sm_scale=ctx.sm_scale)
+        q, k, v, o, lse, ws = ctx.saved_tensors
+        dq, dk, dv = attn_bwd(q, k, v, o, do, lse, causal=ctx.causal, sm_scale=ctx.sm_scale, fwd_workspace=ws)
         return dq, dk, dv, None, None

@@ -755,7 +755,7 @@ BwdLayout bwd_layout(const Shape& s) {
 template <int DT, int D>
 hipError_t bwd_run(const Shape& s, const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, void* dq, void* dk, void* dv, uint8_t* ws, size_t qbytes, const QuantPtrs& qp,
-                   hipStream_t st) {
+                   bool requant, hipStream_t st) {
   const int BH = s.B * s.H;
   const BwdLayout L = bwd_layout(s);
   uint8_t* b = ws + qbytes;
@@ -777,12 +777,14 @@ hipError_t bwd_run(const Shape& s, const void* q, const void* k, const void* v, 
   bp.doT_codes = b + L.doT;
   bp.qT_codes = b + L.qT;
   bp.kT_codes = b + L.kT;
-  // forward quantization of Q, K (the codes the forward used; V's are not needed), then the
-  // backward prologue
-  Shape sqk = s;
-  sqk.pv_fmt = PV_NONE;
-  hipError_t e = launch_prologue(q, k, v, sqk, qp, st);
-  if (e != hipSuccess) return e;
+  // forward quantization of Q, K (the codes the forward used; V's are not needed) -- unless the
+  // buffer already holds the forward's own (requant false) -- then the backward prologue
+  if (requant) {
+    Shape sqk = s;
+    sqk.pv_fmt = PV_NONE;
+    const hipError_t e = launch_prologue(q, k, v, sqk, qp, st);
+    if (e != hipSuccess) return e;
+  }
   bwd_stats_kernel<DT, D><<<dim3(kStatChunks, BH), 256, 0, st>>>((const uint16_t*)dout, (const uint16_t*)q,
                                                                 (const uint16_t*)k, qp.mu_k, s.N, bp.amax_part);
   bwd_prep_kernel<DT, D><<<dim3(s.Np / 64, BH), 2 * D, 0, st>>>((const uint16_t*)o, (const uint16_t*)dout,
@@ -810,13 +812,13 @@ size_t attn_bwd_ws_bytes(const Shape& s) { return bwd_layout(s).total; }
 
 hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv, void* ws,
-                           size_t qbytes, const QuantPtrs& qp, hipStream_t stream) {
+                           size_t qbytes, const QuantPtrs& qp, bool requant, hipStream_t stream) {
   uint8_t* w = static_cast<uint8_t*>(ws);
   if (s.d == 64)
-    return s.io_dtype == 0 ? bwd_run<0, 64>(s, q, k, v, o, dout, lse, dq, dk, dv, w, qbytes, qp, stream)
-                           : bwd_run<1, 64>(s, q, k, v, o, dout, lse, dq, dk, dv, w, qbytes, qp, stream);
-  return s.io_dtype == 0 ? bwd_run<0, 128>(s, q, k, v, o, dout, lse, dq, dk, dv, w, qbytes, qp, stream)
-                         : bwd_run<1, 128>(s, q, k, v, o, dout, lse, dq, dk, dv, w, qbytes, qp, stream);
+    return s.io_dtype == 0 ? bwd_run<0, 64>(s, q, k, v, o, dout, lse, dq, dk, dv, w, qbytes, qp, requant, stream)
+                           : bwd_run<1, 64>(s, q, k, v, o, dout, lse, dq, dk, dv, w, qbytes, qp, requant, stream);
+  return s.io_dtype == 0 ? bwd_run<0, 128>(s, q, k, v, o, dout, lse, dq, dk, dv, w, qbytes, qp, requant, stream)
+                         : bwd_run<1, 128>(s, q, k, v, o, dout, lse, dq, dk, dv, w, qbytes, qp, requant, stream);
 }
 
 }  // namespace sage

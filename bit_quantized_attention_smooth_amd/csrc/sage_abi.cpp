@@ -328,6 +328,23 @@ sage_status logged(const char* fn, Describe what, sage_status s) {
   return s;
 }
 
+// The backward behind both entry points; requant false: the quant buffer at the front of ws
+// already holds the forward's quantization of these q and k.
+sage_status bwd_impl(const sage_problem* p, const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                     bool requant, void* stream) {
+  size_t need = 0;
+  sage_status s = sage_attn_bwd_ws_size(p, &need);
+  if (s != SAGE_OK) return s;
+  if ((s = check_tensors({q, k, v, o, dout, lse, dq, dk, dv, ws})) != SAGE_OK) return s;
+  if (ws_bytes < need) return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  sage_quant_layout L;
+  compute_layout(p, &L);
+  hipError_t e = sage::launch_attn_bwd(to_shape(p), q, k, v, o, dout, lse, dq, dk, dv, ws, L.total,
+                                       resolve(ws, p, L), requant, (hipStream_t)stream);
+  return e == hipSuccess ? SAGE_OK : hip_fail(e, "backward launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -491,18 +508,15 @@ sage_status sage_attn_bwd(const sage_problem* p, const void* q, const void* k, c
                           const void* dout, const float* lse, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
                           void* stream) {
   CallScope cs_;
-  const sage_status st_ = [&]() -> sage_status {
-    size_t need = 0;
-    sage_status s = sage_attn_bwd_ws_size(p, &need);
-    if (s != SAGE_OK) return s;
-    if ((s = check_tensors({q, k, v, o, dout, lse, dq, dk, dv, ws})) != SAGE_OK) return s;
-    if (ws_bytes < need) return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
-    sage_quant_layout L;
-    compute_layout(p, &L);
-    hipError_t e = sage::launch_attn_bwd(to_shape(p), q, k, v, o, dout, lse, dq, dk, dv, ws, L.total,
-                                         resolve(ws, p, L), (hipStream_t)stream);
-    return e == hipSuccess ? SAGE_OK : hip_fail(e, "backward launch");
-  }();
+  const sage_status st_ = bwd_impl(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, true, stream);
+  return logged(__func__, [&] { return describe(p); }, st_);
+}
+
+sage_status sage_attn_bwd_after_fwd(const sage_problem* p, const void* q, const void* k, const void* v,
+                                    const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  CallScope cs_;
+  const sage_status st_ = bwd_impl(p, q, k, v, o, dout, lse, dq, dk, dv, ws, ws_bytes, false, stream);
   return logged(__func__, [&] { return describe(p); }, st_);
 }
 

@@ -193,10 +193,11 @@ hipError_t launch_prologue(const void* q, const void* k, const void* v, const Sh
 hipError_t launch_attn_fwd(const Shape& s, const QuantPtrs& qp, void* o, float* lse, hipStream_t stream);
 
 // Backward: the workspace is [forward quant buffer (qbytes) | backward extras];
-// attn_bwd_ws_bytes gives the size of the extras.
+// attn_bwd_ws_bytes gives the size of the extras.  requant false: the quant buffer already holds
+// the forward's quantization of these q, k (the Q/K codes, steps, mu_k and LSE term are reused).
 size_t attn_bwd_ws_bytes(const Shape& s);
 hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv, void* ws,
-                           size_t qbytes, const QuantPtrs& qp, hipStream_t stream);
+                           size_t qbytes, const QuantPtrs& qp, bool requant, hipStream_t stream);
 
 }  // namespace sage

@@ -239,6 +239,20 @@ sage_status sage_attn_bwd(const sage_problem *p, const void *q, const void *k, c
                           void *dq, void *dk, void *dv, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * sage_attn_bwd for a training step that ran the forward through sage_attn_fwd_ex (or
+ * sage_quantize) with this workspace: the first sage_quant_size(p) bytes of ws must still hold
+ * the quantized buffer that call wrote for this problem and these q and k (unchanged since), and
+ * the Q/K quantization -- codes, steps, mu_k, LSE term, the forward's own -- is reused instead
+ * of recomputed (the SageAttention3 abstract's 8-bit forward and backward as one training step).
+ * Arguments, sizes (ws at least sage_attn_bwd_ws_size bytes) and errors as sage_attn_bwd; a
+ * buffer that does not hold that quantization gives unspecified gradients, but every access
+ * stays inside ws and the tensors.
+ */
+sage_status sage_attn_bwd_after_fwd(const sage_problem *p, const void *q, const void *k, const void *v,
+                                    const void *o, const void *dout, const float *lse,
+                                    void *dq, void *dk, void *dv, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Packed variable-length sequences with grouped KV heads: the sageattn_varlen
  * entry named on the SageAttention3 code-link page, in FlashAttention's
  * cu_seqlens convention (the implementation builds on FlashAttention: review

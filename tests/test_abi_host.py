@@ -136,6 +136,14 @@ def test_backward_rejects_unsupported_problems():
                            None) == S.ERR_WORKSPACE
     assert L.sage_attn_bwd(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n.value,
                            None) == S.ERR_INVALID_ARG
+    # the after-forward entry checks the same things
+    fn = L.sage_attn_bwd_after_fwd
+    assert fn(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n.value - 1,
+              None) == S.ERR_WORKSPACE
+    assert fn(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n.value,
+              None) == S.ERR_INVALID_ARG
+    assert fn(ctypes.byref(_p(qk_fmt=3, pv_fmt=2)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+              n.value, None) == S.ERR_UNSUPPORTED
 
 
 def _vp(**kw):

@@ -149,6 +149,24 @@ def test_autograd_function(sage):
     assert torch.equal(q.grad, dq) and torch.equal(k.grad, dk) and torch.equal(v.grad, dv)
 
 
+@pytest.mark.parametrize("d,causal,dtype", [(64, True, "bf16"), (128, False, "f16"), (128, True, "bf16")])
+def test_backward_after_forward_reuses_the_forward_quantization(sage, d, causal, dtype):
+    """sage_attn_bwd_after_fwd on the workspace the forward wrote gives the bits of the
+    standalone backward (which quantizes Q and K again: the same kernels on the same data)."""
+    from bit_quantized_attention_smooth_amd.workloads import make_inputs
+    banner(f"backward after forward d={d} causal={causal} {dtype}")
+    x = make_inputs(2, 3, 333, d, dtype=dtype, seed=79, k_off_std=2.0, with_do=True)
+    g = {n: x[n].to(device()) for n in ("q", "k", "v", "do")}
+    sm = 1 / math.sqrt(d)
+    ws = sage.bwd_workspace(g["q"], causal=causal, sm_scale=sm)
+    o, lse = sage.sageattn(g["q"], g["k"], g["v"], causal=causal, sm_scale=sm, return_lse=True, workspace=ws)
+    a = sage.attn_bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=causal, sm_scale=sm, fwd_workspace=ws)
+    b = sage.attn_bwd(g["q"], g["k"], g["v"], o, g["do"], lse, causal=causal, sm_scale=sm)
+    torch.cuda.synchronize()
+    for ga, gb in zip(a, b):
+        assert torch.isfinite(ga).all() and torch.equal(ga, gb)
+
+
 def test_backward_beyond_2e31_elements_matches_heads_alone(sage):
     """Each tensor holds more than 2^31 elements (B=1, H=128, N=131149 ragged, d=128, causal).
     Heads are independent problems (their own statistics, steps and tiles), so the first and
