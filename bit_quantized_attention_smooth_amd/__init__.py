@@ -154,8 +154,46 @@ def attn_fwd_quantized(buf, p, *, dtype=torch.bfloat16, return_lse=False):
     return (o, lse) if return_lse else o
 
 
-def sageattn(q, k, v, *, causal=False, sm_scale=None, qk_fmt="int8", pv_fmt="fp8", return_lse=False, workspace=None):
-    """Quantized attention forward on [B,H,N,d] bf16/fp16 device tensors."""
+def _via_packed(q, k, v, layout, causal, sm_scale, qk_fmt, pv_fmt, return_lse):
+    """B equal-length sequences through the packed-sequence entry (each sequence and head gets
+    the fixed-length entry's quantization and kernels): grouped KV heads, query and key lengths
+    that differ, or [B,N,H,d] tensors, which are already the packed [B*N,H,d] rows."""
+    if layout == "HND":
+        (B, H, Nq, d), (Hkv, Nk) = q.shape, k.shape[1:3]
+        rows = [t.permute(0, 2, 1, 3).reshape(B * n, h, d) for t, n, h in ((q, Nq, H), (k, Nk, Hkv), (v, Nk, Hkv))]
+    else:
+        (B, Nq, H, d), (Nk, Hkv) = q.shape, k.shape[1:3]
+        rows = [t.reshape(B * n, h, d) for t, n, h in ((q, Nq, H), (k, Nk, Hkv), (v, Nk, Hkv))]
+    cu_q = torch.arange(0, B * Nq + 1, Nq, dtype=torch.int32, device=q.device)
+    cu_k = torch.arange(0, B * Nk + 1, Nk, dtype=torch.int32, device=q.device)
+    o, lse = sageattn_varlen(*rows, cu_q, cu_k, Nq, Nk, causal=causal, sm_scale=sm_scale, qk_fmt=qk_fmt,
+                             pv_fmt=pv_fmt, return_lse=True)
+    o = o.reshape(B, Nq, H, d)
+    if layout == "HND":
+        o = o.permute(0, 2, 1, 3).contiguous()
+    lse = lse.reshape(H, B, Nq).permute(1, 0, 2).contiguous()
+    return (o, lse) if return_lse else o
+
+
+def sageattn(q, k, v, *, causal=False, sm_scale=None, qk_fmt="int8", pv_fmt="fp8", return_lse=False, workspace=None,
+             tensor_layout="HND"):
+    """Quantized attention forward on bf16/fp16 device tensors: q [B,H,N_q,d], k and v
+    [B,H_kv,N_k,d] (tensor_layout "HND"), or q [B,N_q,H,d], k and v [B,N_k,H_kv,d] ("NHD").
+    Query head h reads KV head h / (H / H_kv).  Returns O in q's layout (and LSE [B,H,N_q]).
+    Grouped KV heads, N_q != N_k (causal masking then top-left aligned) and "NHD" run through the
+    packed-sequence entry with B equal-length sequences; workspace applies to the plain case."""
+    if tensor_layout not in ("HND", "NHD"):
+        raise ValueError(f"tensor_layout must be 'HND' or 'NHD', got {tensor_layout!r}")
+    if q.dim() == 4 and k.dim() == 4 and k.shape == v.shape:
+        hq, hk = (1, 1) if tensor_layout == "HND" else (2, 2)
+        nq, nk = (2, 2) if tensor_layout == "HND" else (1, 1)
+        same_bd = q.shape[0] == k.shape[0] and q.shape[3] == k.shape[3]
+        grouped_ok = k.shape[hk] >= 1 and q.shape[hq] % k.shape[hk] == 0
+        if same_bd and grouped_ok and (tensor_layout == "NHD" or q.shape[hq] != k.shape[hk]
+                                       or q.shape[nq] != k.shape[nk]):
+            if not (q.is_cuda and k.is_cuda and v.is_cuda):
+                raise ValueError("q, k, v must be device tensors")
+            return _via_packed(q, k, v, tensor_layout, causal, sm_scale, qk_fmt, pv_fmt, return_lse)
     q, k, v = _qkv(q, k, v)
     B, H, N, d = q.shape
     p = problem(B, H, N, d, causal=causal, sm_scale=sm_scale, dtype=q.dtype, qk_fmt=qk_fmt, pv_fmt=pv_fmt)

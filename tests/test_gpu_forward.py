@@ -533,3 +533,42 @@ def test_named_fp16_pv_entry_is_the_f16_format(sage):
     b = sage.sageattn(g["q"], g["k"], g["v"], causal=True, qk_fmt="int8", pv_fmt="f16", return_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("qk,pv", [("int8", "fp8"), ("mxfp4", "fp8"), ("int8", "f16")])
+def test_sageattn_layouts_grouped_heads_and_cross_lengths(sage, qk, pv):
+    """sageattn with tensor_layout "NHD" gives the "HND" bits (same rows, permuted); grouped KV
+    heads give the bits of the same call with each KV head repeated; N_q != N_k matches the
+    oracle's per-sequence simulation (causal top-left aligned)."""
+    import oracle
+    banner(f"sageattn layouts / GQA / cross lengths {qk}/{pv}")
+    dev = device()
+    gen = torch.Generator(device=dev).manual_seed(81)
+    B, H, Hkv, d = 2, 6, 2, 128
+    q = torch.randn(B, H, 300, d, device=dev, generator=gen).to(torch.bfloat16)
+    k = (torch.randn(B, Hkv, 300, d, device=dev, generator=gen) + 2.0).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, 300, d, device=dev, generator=gen).to(torch.bfloat16)
+    kr, vr = (t.repeat_interleave(H // Hkv, dim=1).contiguous() for t in (k, v))
+    for causal in (False, True):
+        a = sage.sageattn(q, kr, vr, causal=causal, qk_fmt=qk, pv_fmt=pv, return_lse=True)   # plain entry
+        b = sage.sageattn(q, k, v, causal=causal, qk_fmt=qk, pv_fmt=pv, return_lse=True)     # grouped heads
+        nhd = [t.permute(0, 2, 1, 3).contiguous() for t in (q, kr, vr)]
+        c = sage.sageattn(*nhd, causal=causal, qk_fmt=qk, pv_fmt=pv, return_lse=True, tensor_layout="NHD")
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+        assert torch.equal(c[0].permute(0, 2, 1, 3), a[0]) and torch.equal(c[1], a[1])
+    # cross lengths: 300 queries against 450 keys
+    k2 = (torch.randn(B, Hkv, 450, d, device=dev, generator=gen) + 2.0).to(torch.bfloat16)
+    v2 = torch.randn(B, Hkv, 450, d, device=dev, generator=gen).to(torch.bfloat16)
+    sm = 1 / math.sqrt(d)
+    for causal in (False, True):
+        o, lse = sage.sageattn(q, k2, v2, causal=causal, sm_scale=sm, qk_fmt=qk, pv_fmt=pv, return_lse=True)
+        torch.cuda.synchronize()
+        rows = [t.permute(0, 2, 1, 3).reshape(-1, t.shape[1], d).float().cpu().numpy() for t in (q, k2, v2)]
+        cq, ck = np.array([0, 300, 600], np.int32), np.array([0, 450, 900], np.int32)
+        o_sim, lse_sim, _, sl = oracle.attn_varlen(*rows, cq, ck, causal, sm, qk_fmt=qk, pv_fmt=pv, tile=TILE,
+                                                   slack=True)
+        og = to_np64(o.permute(0, 2, 1, 3).reshape(-1, H, d))
+        assert within(og, o_sim, sl), excess(og, o_sim, sl)
+        assert cos(og, o_sim) >= 0.9999
+        assert np.allclose(lse.permute(1, 0, 2).reshape(H, -1).cpu().numpy(), lse_sim, rtol=1e-4, atol=2e-3)
