@@ -541,7 +541,7 @@ def main():
                            "prologue_GB/s": round(e["prologue_gbs"], 1),
                            "prologue_cold_GB/s": round(e["prologue_cold_gbs"], 1)}
             if e["d"] == 128 and e["N"] >= 8192:
-                # the spec points (d = 128, N >= 8192): the kernel against its own roofline; for
+                # the d = 128, N >= 8192 points (and the long causal prefill): the kernel against its own roofline; for
                 # MXFP4 QK both the format-mix peak and the literal MXFP4 peak
                 rb = {"bound": "mfma", "achieved": round(e["kernel_tops"], 2), "peak": round(pk, 1),
                       "unit": "TFLOP/s", "frac": round(e["kernel_tops"] / pk, 4), "traffic": None,
