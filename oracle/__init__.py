@@ -262,7 +262,7 @@ def attn_varlen(q, k, v, cu_q, cu_k, causal, sm, qk_fmt="int8", pv_fmt="fp8", ti
     prologue results (None when exact: the exact fp64 reference); with slack, also the admissible
     P~ slack of every output element ([total_q,H,d], zero for exact).
 
-    Beyond marshalling, this driver does the packed-sequence bookkeeping in numpy: it slices each
+    Beyond marshalling, this function does the packed-sequence bookkeeping in numpy: it slices each
     sequence out of the packed arrays and repeats each KV head for the query heads that share it,
     then runs the per-sequence prologue and simulation above on the slices."""
     q, k, v = _f32(q), _f32(k), _f32(v)
