@@ -199,8 +199,16 @@ def sageattn(q, k, v, *, causal=False, sm_scale=None, qk_fmt="int8", pv_fmt="fp8
     p = problem(B, H, N, d, causal=causal, sm_scale=sm_scale, dtype=q.dtype, qk_fmt=qk_fmt, pv_fmt=pv_fmt)
     nbytes = ctypes.c_size_t()
     _check(lib().sage_attn_fwd_ws_size(ctypes.byref(p), ctypes.byref(nbytes)))
-    ws = workspace if workspace is not None and workspace.numel() >= nbytes.value else \
-        torch.empty(nbytes.value, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        # a caller's workspace is used as given (a training step reads the quantization back from
+        # it), so one that cannot hold it is an error rather than silently replaced
+        if (not torch.is_tensor(workspace) or workspace.dtype != torch.uint8 or workspace.device != q.device
+                or not workspace.is_contiguous() or workspace.numel() < nbytes.value):
+            raise ValueError(f"workspace must be a contiguous uint8 tensor on {q.device} of at least "
+                             f"{nbytes.value} bytes")
+        ws = workspace
+    else:
+        ws = torch.empty(nbytes.value, dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
     _check(lib().sage_attn_fwd_ex(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws),
@@ -254,8 +262,15 @@ def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     return (o, lse) if return_lse else o
 
 
+def _bf16_only(q, k, v):
+    # the one-call C entries take no dtype argument: their inputs and output are bfloat16
+    if not all(torch.is_tensor(t) and t.dtype == torch.bfloat16 for t in (q, k, v)):
+        raise ValueError("this entry takes bfloat16 q, k, v only (use sageattn for float16)")
+
+
 def attn_fwd_oneshot(q, k, v, *, causal=False, sm_scale=None, qk_fmt="int8", pv_fmt="fp8"):
     """The one-call C entry (bf16 only; the library allocates its scratch stream-ordered)."""
+    _bf16_only(q, k, v)
     q, k, v = _qkv(q, k, v)
     B, H, N, d = q.shape
     o = torch.empty_like(q)
@@ -269,6 +284,7 @@ def attn_fwd_noalloc(q, k, v, *, causal=False, sm_scale=None, qk_fmt="int8", pv_
     """The no-allocation C entry (bf16 only): its scratch is a fixed 64 MiB array the library
     holds per GPU, shared by every call on that GPU.  `out` (bf16, q's shape) may be given so the
     call allocates nothing here either."""
+    _bf16_only(q, k, v)
     q, k, v = _qkv(q, k, v)
     B, H, N, d = q.shape
     o = torch.empty_like(q) if out is None else out

@@ -263,6 +263,19 @@ def test_backward_binding_rejects_mismatched_o_do_lse():
             S.check_bwd_inputs(q, **kw)
 
 
+def test_one_call_entries_reject_float16_in_the_binding():
+    """The one-call C entries (sage_attn_fwd, sage_attn_fwd_noalloc) take no dtype argument and
+    read bfloat16: the binding refuses float16 tensors before any pointer reaches them."""
+    import torch
+    import bit_quantized_attention_smooth_amd as S
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.float16)
+    for fn in (S.attn_fwd_oneshot, S.attn_fwd_noalloc):
+        with pytest.raises(ValueError, match="bfloat16"):
+            fn(q, q, q)
+        with pytest.raises(ValueError, match="bfloat16"):
+            fn(q.bfloat16(), q, q.bfloat16())
+
+
 def test_noalloc_entry_rejects_problems_beyond_its_scratch():
     """The no-allocation forward holds a 64 MiB quantized buffer per GPU: a problem that needs more
     (B=1 H=32 N=8192 d=128, INT8 / FP8: about 99 MiB) is refused on the host, before any device

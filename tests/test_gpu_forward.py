@@ -524,6 +524,22 @@ def test_oneshot_entry_matches_ex(sage):
     assert torch.equal(a, b)
 
 
+def test_caller_workspace_is_used_as_given_or_refused(sage):
+    """sageattn(..., workspace=) writes the quantization into the caller's buffer (a training step
+    reads it back); a buffer of the wrong dtype, on the host, or too small raises instead of being
+    replaced by a fresh one, and a large enough one gives the same output as a fresh buffer."""
+    banner("caller workspace")
+    _, g = _inputs(1, 2, 256, 64, "bf16", 12, 3.0)
+    want = sage.sageattn(g["q"], g["k"], g["v"], causal=True)
+    ws = sage.bwd_workspace(g["q"], causal=True)
+    got = sage.sageattn(g["q"], g["k"], g["v"], causal=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    for bad in (ws[:64], ws.view(torch.int32) if ws.numel() % 4 == 0 else ws.float(), ws.cpu()):
+        with pytest.raises(ValueError, match="workspace"):
+            sage.sageattn(g["q"], g["k"], g["v"], causal=True, workspace=bad)
+
+
 def test_named_fp16_pv_entry_is_the_f16_format(sage):
     """sageattn_qk_int8_pv_fp16 (the entry name the code-link page lists) is the INT8 QK / fp16
     P~V pair, bit for bit."""
