@@ -407,8 +407,8 @@ __device__ __forceinline__ int quant_ds(const float* x, float a0, float a1, int 
 // ---- key-stationary kernel: dK and dV ----
 // Workgroup: 128 keys (4 waves x 32), loops over 64-query tiles.  LDS per stage:
 // Q rows, dO rows (token-major), dO^T and Q^T (channel rows), lse2 and D (64 floats each).
-// d = 128 doubles the accumulators (dK^T, dV^T: 128 registers) and the operand tiles, so one
-// workgroup runs per CU there, with the accumulators in the AGPR half of the register file.
+// Launched at d = 64 (two workgroups per CU); head dim 128 runs the two-wave kernels below,
+// since its accumulators (dK^T, dV^T: 128 registers) would leave one wave per SIMD.
 template <int D, bool CAUSAL, int DT>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdPtrs bp, void* dk, void* dv, int N, int Np, int BH, float sm) {
   constexpr int TB = 64 * D;                          // one tile of 64 x D bytes
@@ -577,8 +577,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdPtrs 
 
 // ---- query-stationary kernel: dQ ----
 // Workgroup: 128 queries (4 waves x 32), loops over 64-key tiles.  LDS per stage:
-// K_s rows (INT8), V rows (FP8), K_s^T (channel rows, FP8).  One workgroup per CU at d = 128,
-// as for the dK/dV kernel.
+// K_s rows (INT8), V rows (FP8), K_s^T (channel rows, FP8).  Launched at d = 64, as the dK/dV
+// kernel above.
 template <int D, bool CAUSAL, int DT>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdPtrs bp, void* dq, int N, int Np, int BH, float sm) {
   constexpr int TB = 64 * D;
@@ -726,6 +726,381 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdPtrs bp
   }
 }
 
+// ---- head dim 128: two waves per 32-token group ----
+// At d = 128 the accumulators alone (dK^T and dV^T, or dQ^T and (P K_s)^T) take 128 registers of
+// a wave that owns 32 tokens, which leaves one wave per SIMD; a lone wave issues vector work at
+// half the SIMD's rate and mostly alternates between its matrix and vector phases.  Here two
+// waves share each group of 32 stationary tokens (keys in the dK/dV kernel, queries in the dQ
+// kernel): wave half `hw` (waves [hw*G, hw*G + G)) computes the scores of subtile hw of every
+// 64-token tile (S, dP, P~ and dS~ for 32 x 32 pairs), the two waves swap their halves of the
+// FP8 P~ and dS~ operands through LDS, and each then accumulates all 64 tokens of the tile into
+// its half of the channels.  The accumulators fall to 64 registers, so two waves run per SIMD;
+// the matrix and vector work per tile is the same as in the one-wave kernels, split in two.
+// The dS~ block scales are those of the one-wave kernels (block b is subtile b across both
+// lane halves), so every MFMA sees the same operands: dK and dV are bit-identical to them,
+// only the fp32 order of dQ's row sum of dS differs.
+// NW: waves per workgroup (G = NW / 2 token groups); NW = 4 runs two workgroups per CU.
+
+// One wave's half of a tile's FP8 operands, swapped through LDS: 4 dwords of P~ codes, 4 of dS~
+// codes and the E8M0 byte of its dS~ block, [dword][lane] so a wave's accesses are conflict-free.
+constexpr int kXW = 9;
+// Waves per workgroup of the d = 128 kernels: 4 (two workgroups of 64 tokens per CU).
+constexpr int kSplitWaves = 4;
+
+// p[16], ds[16] of subtile hw -> this lane's full B operands (bytes 0-15: subtile 0, 16-31:
+// subtile 1) and the E8M0 byte it supplies (block hh).  am: this lane's max |ds|.  Writes its
+// own half to xo, reads the partner's from xp between two workgroup barriers (the caller's
+// loop runs the same barriers on every wave).
+template <bool ACTIVE>
+__device__ __forceinline__ void swap_halves(const float* p, const float* ds, float am, int hw, int hh, uint32_t* xo,
+                                            const uint32_t* xp, int lane, v8i& pb, v8i& db, int& sb) {
+  int own_p[4], own_d[4], own_b = 0;
+  if (ACTIVE) {
+    // block hw spans subtile hw of both lane halves
+    const uint32_t bmax = max(__float_as_uint(am), __float_as_uint(other_half(am)));
+    own_b = e4m3_scale_byte(bmax);
+    const float sc = __uint_as_float((uint32_t)own_b << 23);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      own_p[i] = pack_fp8x4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+      typedef short v2s __attribute__((ext_vector_type(2)));
+      v2s w = __builtin_bit_cast(v2s, __float_as_int(ds[4 * i]));
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, ds[4 * i], ds[4 * i + 1], sc, false);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, ds[4 * i + 2], ds[4 * i + 3], sc, true);
+      own_d[i] = __builtin_bit_cast(int, w);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      xo[64 * i + lane] = (uint32_t)own_p[i];
+      xo[64 * (4 + i) + lane] = (uint32_t)own_d[i];
+    }
+    xo[64 * 8 + lane] = (uint32_t)own_b;
+  }
+  __syncthreads();
+  if (ACTIVE) {
+    int par_p[4], par_d[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      par_p[i] = (int)xp[64 * i + lane];
+      par_d[i] = (int)xp[64 * (4 + i) + lane];
+    }
+    const int par_b = (int)xp[64 * 8 + lane];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      pb[i] = hw ? par_p[i] : own_p[i];
+      pb[4 + i] = hw ? own_p[i] : par_p[i];
+      db[i] = hw ? par_d[i] : own_d[i];
+      db[4 + i] = hw ? own_d[i] : par_d[i];
+    }
+    sb = hh == hw ? own_b : par_b;
+  }
+}
+
+template <bool CAUSAL, int DT, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dkdv_split_kernel(BwdPtrs bp, void* dk, void* dv, int N, int Np,
+                                                                         int BH, float sm) {
+  constexpr int D = 128, TB = 64 * D, G = NW / 2, KEYS = 32 * G;
+  constexpr int STAGE = 4 * TB + 2 * 64 * 4 + 16;   // + the tile's Q step and dO step
+  constexpr int HCB = D / 64;                         // channel blocks per wave
+  __shared__ __align__(16) uint8_t lds[2][STAGE];
+  __shared__ uint32_t xch[NW][kXW * 64];
+  const int nkt = Np / KEYS;
+  int bh, kt;
+  work_item(blockIdx.x, BH, nkt, bh, kt);
+  const int kbase = kt * KEYS;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = w % G, hw = w / G, partner = grp + G * (1 - hw);
+  const int n = lane & 31, hh = lane >> 5;
+  const int kw = kbase + 32 * grp, key = kw + n;
+  const int nb = Np / 64;
+  const float smlog2e = sm * kLog2e;
+
+  v4i kf[D / 32];
+  v8i vf[D / 64];
+  {
+    const int8_t* kp = bp.k_codes + ((size_t)bh * Np + key) * D + 16 * hh;
+#pragma unroll
+    for (int c = 0; c < D / 32; c++) kf[c] = *reinterpret_cast<const v4i*>(kp + 32 * c);
+    const uint8_t* vp = bp.v_codes + ((size_t)bh * Np + key) * D + 32 * hh;
+#pragma unroll
+    for (int c = 0; c < D / 64; c++) vf[c] = lds_v8i(vp + 64 * c, vp + 64 * c + 16);
+  }
+  const float kstep = bp.k_step[(size_t)bh * nb + kw / 64];
+  const float vstep = bp.v_step[(size_t)bh * nb + kw / 64];
+
+  v16f dV[HCB], dK[HCB];
+#pragma unroll
+  for (int c = 0; c < HCB; c++) dV[c] = dK[c] = v16f{};
+
+  const int qt0 = CAUSAL ? kbase / 64 : 0;
+  const int nqt = (N + 63) / 64;
+  // the tile loads are issued by four waves (the one-wave kernels' pattern)
+  auto stage = [&](int buf, int qt) {
+    if (w >= 4) return;
+    uint8_t* L = lds[buf];
+    const size_t rb = ((size_t)bh * Np + (size_t)qt * 64) * D;
+    const size_t tb = ((size_t)bh * nb + qt) * TB;
+    stage_rows<D>(L, reinterpret_cast<const uint8_t*>(bp.q_codes) + rb, w, lane);
+    stage_rows<D>(L + TB, bp.do_codes + rb, w, lane);
+    stage_cols<D>(L + 2 * TB, bp.doT_codes + tb, w, lane);
+    stage_cols<D>(L + 3 * TB, bp.qT_codes + tb, w, lane);
+    if (w == 0 && lane < 16) load_lds16_async(bp.lse2 + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 16 * lane);
+    if (w == 1 && lane < 16) load_lds16_async(bp.Dvec + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 256 + 16 * lane);
+    if (w == 2 && lane < 2) load_lds4_async((lane ? bp.do_step : bp.q_step) + (size_t)bh * nb + qt, L + 4 * TB + 512);
+  };
+  // one query tile: S, dP of subtile hw on MFMA, its P~ and dS~ on the vector unit, the swap,
+  // then dV^T, dK^T of this wave's channels over the whole tile
+  auto tile = [&](const uint8_t* L, int qt, auto mode) {
+    constexpr int MODE = decltype(mode)::value;   // -1: nothing visible, 1: masked, 0: open
+    constexpr bool ACTIVE = MODE >= 0;
+    float p[16], ds[16], am = 0.0f;
+    if (ACTIVE) {
+      const int qb = qt * 64;
+      const float qstep = reinterpret_cast<const float*>(L + 4 * TB + 512)[0];
+      const float dostep = reinterpret_cast<const float*>(L + 4 * TB + 512)[1];
+      const int row = tile_perm(n, hw);
+      v16i S = v16i{};
+#pragma unroll
+      for (int c = 0; c < D / 32; c++) S = mfma_i8(*reinterpret_cast<const v4i*>(L + rowoff<D>(row, 2 * c + hh)), kf[c], S);
+      v16f Gp = v16f{};
+#pragma unroll
+      for (int c = 0; c < D / 64; c++)
+        Gp = mfma_f8(lds_v8i(L + TB + rowoff<D>(row, 4 * c + 2 * hh), L + TB + rowoff<D>(row, 4 * c + 2 * hh + 1)), vf[c], Gp);
+      // element r: query qb + 32 hh + 16 hw + r, key = this lane's key
+      const float cS = qstep * kstep * smlog2e, cP = dostep * vstep;
+      const float* l2 = reinterpret_cast<const float*>(L + 4 * TB) + 32 * hh + 16 * hw;
+      const float* Dv = reinterpret_cast<const float*>(L + 4 * TB + 256) + 32 * hh + 16 * hw;
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const v4f lv = *reinterpret_cast<const v4f*>(l2 + r);
+        const v4f dvv = *reinterpret_cast<const v4f*>(Dv + r);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float x = fmaf((float)S[r + i], cS, -lv[i]);
+          if (MODE == 1) x = key <= qb + 32 * hh + 16 * hw + r + i ? x : -INFINITY;
+          const float e = fast_exp2(x);
+          const float d = e * fmaf(Gp[r + i], cP, -dvv[i]);
+          p[r + i] = e;
+          ds[r + i] = d;
+          am = fmaxf(am, fabsf(d));
+        }
+      }
+    }
+    v8i pb, db;
+    int sb = 0;
+    swap_halves<ACTIVE>(p, ds, am, hw, hh, xch[w], xch[partner], lane, pb, db, sb);
+    if (ACTIVE) {
+#pragma unroll
+      for (int c = 0; c < HCB; c++) {
+        const int row = 32 * (HCB * hw + c) + n;
+        dV[c] = mfma_f8(lds_v8i(L + 2 * TB + coloff(row, 2 * hh), L + 2 * TB + coloff(row, 2 * hh + 1)), pb, dV[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < HCB; c++) {
+        const int row = 32 * (HCB * hw + c) + n;
+        dK[c] = mfma_f8_sb(lds_v8i(L + 3 * TB + coloff(row, 2 * hh), L + 3 * TB + coloff(row, 2 * hh + 1)), db, dK[c], sb);
+      }
+    }
+  };
+  // per-wave phases over the query tiles, as in the one-wave kernel; both waves of a key group
+  // share them, and every wave runs the swap's barrier on every tile
+  const int qt_first = kw >= N ? nqt : (CAUSAL ? max(qt0, kw / 64) : qt0);
+  const int qt_open = kw >= N ? nqt : (CAUSAL ? max(qt_first, (kw + 94) / 64) : qt0);
+  auto iter = [&](int qt, auto mode) {
+    const int buf = (qt - qt0) & 1;
+    if (qt + 1 < nqt) stage(buf ^ 1, qt + 1);
+    tile(lds[buf], qt, mode);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  };
+  if (qt0 < nqt) stage(0, qt0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  int qt = qt0;
+  for (; qt < min(qt_first, nqt); qt++) iter(qt, std::integral_constant<int, -1>{});
+  for (; qt < min(qt_open, nqt); qt++) iter(qt, std::integral_constant<int, 1>{});
+  for (; qt < nqt; qt++) iter(qt, std::integral_constant<int, 0>{});
+  // epilogue: this wave's channels 32 cb + 8 g + 4 hh + {0..3}, cb = HCB hw + c, of its key
+  if (key < N) {
+    uint16_t* dkr = reinterpret_cast<uint16_t*>(dk) + ((size_t)bh * N + key) * D;
+    uint16_t* dvr = reinterpret_cast<uint16_t*>(dv) + ((size_t)bh * N + key) * D;
+    const float* cdo = bp.chan_step + (size_t)bh * D + 4 * hh;
+    const float* cq = bp.chan_step + ((size_t)BH + bh) * D + 4 * hh;
+    v4f fk[HCB][4], fv[HCB][4];
+#pragma unroll
+    for (int c = 0; c < HCB; c++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        fk[c][g] = *reinterpret_cast<const v4f*>(cq + 32 * (HCB * hw + c) + 8 * g);
+        fv[c][g] = *reinterpret_cast<const v4f*>(cdo + 32 * (HCB * hw + c) + 8 * g);
+      }
+    const float kf448 = sm * (1.0f / 448.0f);
+#pragma unroll
+    for (int c = 0; c < HCB; c++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        const int ch = 32 * (HCB * hw + c) + 8 * g + 4 * hh;
+        uint32_t k2[2], v2[2];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+          const int i0 = 2 * t, i1 = 2 * t + 1;
+          k2[t] = (uint32_t)to_io<DT>(dK[c][4 * g + i0] * (fk[c][g][i0] * kf448)) |
+                  ((uint32_t)to_io<DT>(dK[c][4 * g + i1] * (fk[c][g][i1] * kf448)) << 16);
+          v2[t] = (uint32_t)to_io<DT>(dV[c][4 * g + i0] * (fv[c][g][i0] * (1.0f / 448.0f))) |
+                  ((uint32_t)to_io<DT>(dV[c][4 * g + i1] * (fv[c][g][i1] * (1.0f / 448.0f))) << 16);
+        }
+        *reinterpret_cast<uint2*>(dkr + ch) = make_uint2(k2[0], k2[1]);
+        *reinterpret_cast<uint2*>(dvr + ch) = make_uint2(v2[0], v2[1]);
+      }
+  }
+}
+
+template <bool CAUSAL, int DT, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_split_kernel(BwdPtrs bp, void* dq, int N, int Np, int BH,
+                                                                       float sm) {
+  constexpr int D = 128, TB = 64 * D, G = NW / 2, QUERIES = 32 * G;
+  constexpr int STAGE = 3 * TB + 16;   // + the tile's K step and V step
+  constexpr int HCB = D / 64;
+  __shared__ __align__(16) uint8_t lds[2][STAGE];
+  __shared__ uint32_t xch[NW][kXW * 64];
+  const int nqt = Np / QUERIES;
+  int bh, t;
+  work_item(blockIdx.x, BH, nqt, bh, t);
+  const int qt = CAUSAL ? nqt - 1 - t : t;   // causal: the longest rows first
+  const int qbase = qt * QUERIES;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = w % G, hw = w / G, partner = grp + G * (1 - hw);
+  const int n = lane & 31, hh = lane >> 5;
+  const int qw = qbase + 32 * grp, q = qw + n;
+  const int nb = Np / 64;
+  const float smlog2e = sm * kLog2e;
+
+  v4i qf[D / 32];
+  v8i df[D / 64];
+  {
+    const int8_t* qp = bp.q_codes + ((size_t)bh * Np + q) * D + 16 * hh;
+#pragma unroll
+    for (int c = 0; c < D / 32; c++) qf[c] = *reinterpret_cast<const v4i*>(qp + 32 * c);
+    const uint8_t* dp = bp.do_codes + ((size_t)bh * Np + q) * D + 32 * hh;
+#pragma unroll
+    for (int c = 0; c < D / 64; c++) df[c] = lds_v8i(dp + 64 * c, dp + 64 * c + 16);
+  }
+  const float qstep = bp.q_step[(size_t)bh * nb + q / 64];
+  const float dostep = bp.do_step[(size_t)bh * nb + q / 64];
+  const float l2 = bp.lse2[(size_t)bh * Np + q];
+  const float Dq = bp.Dvec[(size_t)bh * Np + q];
+
+  v16f dQ[HCB], PK[HCB];
+#pragma unroll
+  for (int c = 0; c < HCB; c++) dQ[c] = PK[c] = v16f{};
+  float rsum = 0.0f;
+
+  int nkt = (N + 63) / 64;
+  if (CAUSAL) nkt = min(nkt, (qbase + QUERIES - 1) / 64 + 1);
+  auto stage = [&](int buf, int kt) {
+    if (w >= 4) return;
+    uint8_t* L = lds[buf];
+    const size_t rb = ((size_t)bh * Np + (size_t)kt * 64) * D;
+    const size_t tb = ((size_t)bh * nb + kt) * TB;
+    stage_rows<D>(L, reinterpret_cast<const uint8_t*>(bp.k_codes) + rb, w, lane);
+    stage_rows<D>(L + TB, bp.v_codes + rb, w, lane);
+    stage_cols<D>(L + 2 * TB, bp.kT_codes + tb, w, lane);
+    if (w == 0 && lane < 2) load_lds4_async((lane ? bp.v_step : bp.k_step) + (size_t)bh * nb + kt, L + 3 * TB);
+  };
+  auto tile = [&](const uint8_t* L, int kt, auto mode) {
+    constexpr int MODE = decltype(mode)::value;
+    constexpr bool ACTIVE = MODE >= 0;
+    float p[16], ds[16], am = 0.0f;
+    if (ACTIVE) {
+      const int kb = kt * 64;
+      const float kstep = reinterpret_cast<const float*>(L + 3 * TB)[0];
+      const float vstep = reinterpret_cast<const float*>(L + 3 * TB)[1];
+      const int row = tile_perm(n, hw);
+      v16i S = v16i{};
+#pragma unroll
+      for (int c = 0; c < D / 32; c++) S = mfma_i8(*reinterpret_cast<const v4i*>(L + rowoff<D>(row, 2 * c + hh)), qf[c], S);
+      v16f Gp = v16f{};
+#pragma unroll
+      for (int c = 0; c < D / 64; c++)
+        Gp = mfma_f8(lds_v8i(L + TB + rowoff<D>(row, 4 * c + 2 * hh), L + TB + rowoff<D>(row, 4 * c + 2 * hh + 1)), df[c], Gp);
+      // element r: key kb + 32 hh + 16 hw + r, query = this lane's query
+      const float cS = qstep * kstep * smlog2e, cP = dostep * vstep;
+      const int lim = min(N, CAUSAL ? q + 1 : N) - (kb + 32 * hh + 16 * hw);   // keys r < lim are visible
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        float x = fmaf((float)S[r], cS, -l2);
+        if (MODE == 1) x = r < lim ? x : -INFINITY;
+        const float e = fast_exp2(x);
+        const float d = e * fmaf(Gp[r], cP, -Dq);
+        p[r] = e;
+        ds[r] = d;
+        rsum += d;
+        am = fmaxf(am, fabsf(d));
+      }
+    }
+    v8i pb, db;
+    int sb = 0;
+    swap_halves<ACTIVE>(p, ds, am, hw, hh, xch[w], xch[partner], lane, pb, db, sb);
+    if (ACTIVE) {
+#pragma unroll
+      for (int c = 0; c < HCB; c++) {
+        const int row = 32 * (HCB * hw + c) + n;
+        const v8i a = lds_v8i(L + 2 * TB + coloff(row, 2 * hh), L + 2 * TB + coloff(row, 2 * hh + 1));
+        dQ[c] = mfma_f8_sb(a, db, dQ[c], sb);
+        PK[c] = mfma_f8(a, pb, PK[c]);   // P K_s for the rowsum correction
+      }
+    }
+  };
+  const int nkt_n = (N + 63) / 64;
+  const int nvis = CAUSAL ? min(nkt_n, (qw + 31) / 64 + 1) : nkt_n;
+  const int nfull = min(N / 64, CAUSAL ? (qw + 1) / 64 : nkt_n);
+  auto iter = [&](int kt, auto mode) {
+    const int buf = kt & 1;
+    if (kt + 1 < nkt) stage(buf ^ 1, kt + 1);
+    tile(lds[buf], kt, mode);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  };
+  stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  int kt = 0;
+  for (; kt < min(nfull, nkt); kt++) iter(kt, std::integral_constant<int, 0>{});
+  for (; kt < min(nvis, nkt); kt++) iter(kt, std::integral_constant<int, 1>{});
+  for (; kt < nkt; kt++) iter(kt, std::integral_constant<int, -1>{});
+  // rowsum(dS) over both halves of the keys, in a fixed order (subtile 0's share first)
+  const float rs_own = half_sum(rsum);
+  xch[w][lane] = __float_as_uint(rs_own);
+  __syncthreads();
+  const float rs_par = __uint_as_float(xch[partner][lane]);
+  const float rs = (hw ? rs_par + rs_own : rs_own + rs_par) * (1.0f / 448.0f);
+  if (q < N) {
+    uint16_t* dqr = reinterpret_cast<uint16_t*>(dq) + ((size_t)bh * N + q) * D;
+    const float* ck = bp.chan_step + ((size_t)2 * BH + bh) * D + 4 * hh;
+    v4f fq[HCB][4];
+#pragma unroll
+    for (int c = 0; c < HCB; c++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) fq[c][g] = *reinterpret_cast<const v4f*>(ck + 32 * (HCB * hw + c) + 8 * g);
+    const float f448 = sm * (1.0f / 448.0f);
+#pragma unroll
+    for (int c = 0; c < HCB; c++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        const int ch = 32 * (HCB * hw + c) + 8 * g + 4 * hh;
+        uint32_t w2[2];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; t2++) {
+          const int i0 = 2 * t2, i1 = 2 * t2 + 1;
+          w2[t2] = (uint32_t)to_io<DT>(fq[c][g][i0] * f448 * fmaf(-rs, PK[c][4 * g + i0], dQ[c][4 * g + i0])) |
+                   ((uint32_t)to_io<DT>(fq[c][g][i1] * f448 * fmaf(-rs, PK[c][4 * g + i1], dQ[c][4 * g + i1])) << 16);
+        }
+        *reinterpret_cast<uint2*>(dqr + ch) = make_uint2(w2[0], w2[1]);
+      }
+    if (hw == 0 && hh == 0) bp.Dvec[(size_t)bh * Np + q] = Dq + rs;
+  }
+}
+
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct BwdLayout {
@@ -790,8 +1165,23 @@ hipError_t bwd_run(const Shape& s, const void* q, const void* k, const void* v, 
   bwd_prep_kernel<DT, D><<<dim3(s.Np / 64, BH), 2 * D, 0, st>>>((const uint16_t*)o, (const uint16_t*)dout,
                                                              (const uint16_t*)v, (const uint16_t*)q,
                                                              (const uint16_t*)k, lse, s.N, s.Np, bp);
-  const int grid = BH * (s.Np / 128);
   // dQ first: it turns D into D^ = D + rowsum(dS), which the dK/dV kernel then uses
+  if constexpr (D == 128) {
+    constexpr int NW = kSplitWaves;
+    const int grid = BH * (s.Np / (16 * NW));
+    if (s.causal) {
+      bwd_dq_split_kernel<true, DT, NW><<<grid, 64 * NW, debug_lds_pad(bwd_dq_split_kernel<true, DT, NW>), st>>>(
+          bp, dq, s.N, s.Np, BH, s.sm_scale);
+      bwd_dkdv_split_kernel<true, DT, NW><<<grid, 64 * NW, debug_lds_pad(bwd_dkdv_split_kernel<true, DT, NW>), st>>>(
+          bp, dk, dv, s.N, s.Np, BH, s.sm_scale);
+    } else {
+      bwd_dq_split_kernel<false, DT, NW><<<grid, 64 * NW, debug_lds_pad(bwd_dq_split_kernel<false, DT, NW>), st>>>(
+          bp, dq, s.N, s.Np, BH, s.sm_scale);
+      bwd_dkdv_split_kernel<false, DT, NW><<<grid, 64 * NW, debug_lds_pad(bwd_dkdv_split_kernel<false, DT, NW>), st>>>(
+          bp, dk, dv, s.N, s.Np, BH, s.sm_scale);
+    }
+  } else {
+  const int grid = BH * (s.Np / 128);
   if (s.causal) {
     bwd_dq_kernel<D, true, DT><<<grid, 256, debug_lds_pad(bwd_dq_kernel<D, true, DT>), st>>>(bp, dq, s.N, s.Np, BH,
                                                                                           s.sm_scale);
@@ -802,6 +1192,7 @@ hipError_t bwd_run(const Shape& s, const void* q, const void* k, const void* v, 
                                                                                           s.sm_scale);
     bwd_dkdv_kernel<D, false, DT><<<grid, 256, debug_lds_pad(bwd_dkdv_kernel<D, false, DT>), st>>>(bp, dk, dv, s.N, s.Np,
                                                                                               BH, s.sm_scale);
+  }
   }
   return hipGetLastError();
 }
