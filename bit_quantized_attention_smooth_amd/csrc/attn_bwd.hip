@@ -330,32 +330,27 @@ __device__ __forceinline__ void work_item(int hw_id, int BH, int nt, int& bh, in
   }
 }
 
-// Direct loads of one 64-row token-major tile (64 x D bytes) into LDS with the row swizzle.
+// Direct loads of the 64-row token-major tiles (64 x D bytes, 16-byte chunks under the row
+// swizzle) and of the transposed tiles (D rows x 64 bytes, the channel-row swizzle) into LDS by
+// four waves: each lane's byte offset for load i of wave w is computed once (rows_voff,
+// cols_voff) and the tile's base is a wave-uniform scalar (load_lds16_async_so), so a tile loop
+// does no per-load vector address arithmetic.
 template <int D>
-__device__ __forceinline__ void stage_rows(uint8_t* lds, const uint8_t* g, int w, int lane) {
-  constexpr int CH = D / 16, CHUNKS = 64 * CH;
-#pragma unroll
-  for (int i = 0; i < (CHUNKS + 255) / 256; i++) {
-    const int pbase = 256 * i + 64 * w;
-    if (pbase < CHUNKS) {
-      const int P = pbase + lane, row = P / CH, col = (P % CH) ^ (D == 64 ? swz_row64(row) : (((row >> 1) & 3) | (((row >> 5) & 1) << 2)));
-      load_lds16_async(g + row * D + col * 16, lds + pbase * 16);
-    }
-  }
+__device__ __forceinline__ uint32_t rows_voff(int i, int w, int lane) {
+  constexpr int CH = D / 16;
+  const int P = 256 * i + 64 * w + lane, row = P / CH,
+            col = (P % CH) ^ (D == 64 ? swz_row64(row) : (((row >> 1) & 3) | (((row >> 5) & 1) << 2)));
+  return (uint32_t)(row * D + col * 16);
 }
-// Direct loads of one transposed tile (D rows x 64 bytes) into LDS with the channel-row swizzle.
 template <int D>
-__device__ __forceinline__ void stage_cols(uint8_t* lds, const uint8_t* g, int w, int lane) {
-  constexpr int CHUNKS = D * 4;
-#pragma unroll
-  for (int i = 0; i < (CHUNKS + 255) / 256; i++) {
-    const int pbase = 256 * i + 64 * w;
-    if (pbase < CHUNKS) {
-      const int P = pbase + lane, row = P >> 2, col = (P & 3) ^ swz_t64(row);
-      load_lds16_async(g + row * 64 + col * 16, lds + pbase * 16);
-    }
-  }
+__device__ __forceinline__ uint32_t cols_voff(int i, int w, int lane) {
+  const int P = 256 * i + 64 * w + lane, row = P >> 2, col = (P & 3) ^ swz_t64(row);
+  return (uint32_t)(row * 64 + col * 16);
 }
+// 16-byte loads per lane of one tile (64 x D bytes) shared by four waves: D / 64.
+template <int D>
+constexpr int kTileLoads = 64 * D / 16 / 256;
+
 template <int D>
 __device__ __forceinline__ int rowoff(int row, int chunk) {
   return row * D + ((chunk ^ (D == 64 ? swz_row64(row) : (((row >> 1) & 3) | (((row >> 5) & 1) << 2)))) << 4);
@@ -445,14 +440,24 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdPtrs 
 
   const int qt0 = CAUSAL ? kbase / 64 : 0;
   const int nqt = (N + 63) / 64;
+  uint32_t ro[kTileLoads<D>], co[kTileLoads<D>];
+#pragma unroll
+  for (int i = 0; i < kTileLoads<D>; i++) {
+    ro[i] = rows_voff<D>(i, w, lane);
+    co[i] = cols_voff<D>(i, w, lane);
+  }
   auto stage = [&](int buf, int qt) {
     uint8_t* L = lds[buf];
     const size_t rb = ((size_t)bh * Np + (size_t)qt * 64) * D;
     const size_t tb = ((size_t)bh * nb + qt) * TB;
-    stage_rows<D>(L, reinterpret_cast<const uint8_t*>(bp.q_codes) + rb, w, lane);
-    stage_rows<D>(L + TB, bp.do_codes + rb, w, lane);
-    stage_cols<D>(L + 2 * TB, bp.doT_codes + tb, w, lane);
-    stage_cols<D>(L + 3 * TB, bp.qT_codes + tb, w, lane);
+#pragma unroll
+    for (int i = 0; i < kTileLoads<D>; i++) {
+      const int o = (256 * i + 64 * w) * 16;
+      load_lds16_async_so(reinterpret_cast<const uint8_t*>(bp.q_codes) + rb, ro[i], L + o);
+      load_lds16_async_so(bp.do_codes + rb, ro[i], L + TB + o);
+      load_lds16_async_so(bp.doT_codes + tb, co[i], L + 2 * TB + o);
+      load_lds16_async_so(bp.qT_codes + tb, co[i], L + 3 * TB + o);
+    }
     if (w == 0 && lane < 16) load_lds16_async(bp.lse2 + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 16 * lane);
     if (w == 1 && lane < 16) load_lds16_async(bp.Dvec + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 256 + 16 * lane);
     if (w == 2 && lane < 2) load_lds4_async((lane ? bp.do_step : bp.q_step) + (size_t)bh * nb + qt, L + 4 * TB + 512);
@@ -619,13 +624,23 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdPtrs bp
 
   int nkt = (N + 63) / 64;
   if (CAUSAL) nkt = min(nkt, (qbase + 127) / 64 + 1);
+  uint32_t ro[kTileLoads<D>], co[kTileLoads<D>];
+#pragma unroll
+  for (int i = 0; i < kTileLoads<D>; i++) {
+    ro[i] = rows_voff<D>(i, w, lane);
+    co[i] = cols_voff<D>(i, w, lane);
+  }
   auto stage = [&](int buf, int kt) {
     uint8_t* L = lds[buf];
     const size_t rb = ((size_t)bh * Np + (size_t)kt * 64) * D;
     const size_t tb = ((size_t)bh * nb + kt) * TB;
-    stage_rows<D>(L, reinterpret_cast<const uint8_t*>(bp.k_codes) + rb, w, lane);
-    stage_rows<D>(L + TB, bp.v_codes + rb, w, lane);
-    stage_cols<D>(L + 2 * TB, bp.kT_codes + tb, w, lane);
+#pragma unroll
+    for (int i = 0; i < kTileLoads<D>; i++) {
+      const int o = (256 * i + 64 * w) * 16;
+      load_lds16_async_so(reinterpret_cast<const uint8_t*>(bp.k_codes) + rb, ro[i], L + o);
+      load_lds16_async_so(bp.v_codes + rb, ro[i], L + TB + o);
+      load_lds16_async_so(bp.kT_codes + tb, co[i], L + 2 * TB + o);
+    }
     if (w == 0 && lane < 2) load_lds4_async((lane ? bp.v_step : bp.k_step) + (size_t)bh * nb + kt, L + 3 * TB);
   };
   auto tile = [&](const uint8_t* L, int kt, auto masked_tag) {
@@ -741,58 +756,49 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdPtrs bp
 // only the fp32 order of dQ's row sum of dS differs.
 // NW: waves per workgroup (G = NW / 2 token groups); NW = 4 runs two workgroups per CU.
 
-// One wave's half of a tile's FP8 operands, swapped through LDS: 4 dwords of P~ codes, 4 of dS~
-// codes and the E8M0 byte of its dS~ block, [dword][lane] so a wave's accesses are conflict-free.
-constexpr int kXW = 9;
 // Waves per workgroup of the d = 128 kernels: 4 (two workgroups of 64 tokens per CU).
 constexpr int kSplitWaves = 4;
 
-// p[16], ds[16] of subtile hw -> this lane's full B operands (bytes 0-15: subtile 0, 16-31:
-// subtile 1) and the E8M0 byte it supplies (block hh).  am: this lane's max |ds|.  Writes its
-// own half to xo, reads the partner's from xp between two workgroup barriers (the caller's
-// loop runs the same barriers on every wave).
+// One token group's swap area: quads 0 / 1 hold the P~ codes of subtiles 0 / 1 (the B operand's
+// bytes 0-15 / 16-31), quads 2 / 3 the dS~ codes, as 16-byte [quad][lane] entries (a wave's
+// access is conflict-free), and the E8M0 bytes of the two dS~ blocks.
+struct SwapArea {
+  uint4 q[4][64];
+  uint32_t sb[2][64];
+};
+
+// Subtile hw's 16 P~ and dS~ values of this lane -> its full B operands and the E8M0 byte it
+// supplies (block hh).  am: this lane's max |ds|.  Both waves write their halves and read back
+// the whole, between two workgroup barriers (the caller's loop runs the same barriers on
+// every wave, active or not).
 template <bool ACTIVE>
-__device__ __forceinline__ void swap_halves(const float* p, const float* ds, float am, int hw, int hh, uint32_t* xo,
-                                            const uint32_t* xp, int lane, v8i& pb, v8i& db, int& sb) {
-  int own_p[4], own_d[4], own_b = 0;
+__device__ __forceinline__ void swap_halves(const float* p, const float* ds, float am, int hw, int hh, SwapArea& x,
+                                            int lane, v8i& pb, v8i& db, int& sb) {
   if (ACTIVE) {
     // block hw spans subtile hw of both lane halves
     const uint32_t bmax = max(__float_as_uint(am), __float_as_uint(other_half(am)));
-    own_b = e4m3_scale_byte(bmax);
-    const float sc = __uint_as_float((uint32_t)own_b << 23);
+    const int byte = e4m3_scale_byte(bmax);
+    const float sc = __uint_as_float((uint32_t)byte << 23);
+    uint32_t P[4], Q[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      own_p[i] = pack_fp8x4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+      P[i] = (uint32_t)pack_fp8x4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
       typedef short v2s __attribute__((ext_vector_type(2)));
       v2s w = __builtin_bit_cast(v2s, __float_as_int(ds[4 * i]));
       w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, ds[4 * i], ds[4 * i + 1], sc, false);
       w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, ds[4 * i + 2], ds[4 * i + 3], sc, true);
-      own_d[i] = __builtin_bit_cast(int, w);
+      Q[i] = __builtin_bit_cast(uint32_t, w);
     }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      xo[64 * i + lane] = (uint32_t)own_p[i];
-      xo[64 * (4 + i) + lane] = (uint32_t)own_d[i];
-    }
-    xo[64 * 8 + lane] = (uint32_t)own_b;
+    x.q[hw][lane] = make_uint4(P[0], P[1], P[2], P[3]);
+    x.q[2 + hw][lane] = make_uint4(Q[0], Q[1], Q[2], Q[3]);
+    x.sb[hw][lane] = (uint32_t)byte;
   }
   __syncthreads();
   if (ACTIVE) {
-    int par_p[4], par_d[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      par_p[i] = (int)xp[64 * i + lane];
-      par_d[i] = (int)xp[64 * (4 + i) + lane];
-    }
-    const int par_b = (int)xp[64 * 8 + lane];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      pb[i] = hw ? par_p[i] : own_p[i];
-      pb[4 + i] = hw ? own_p[i] : par_p[i];
-      db[i] = hw ? par_d[i] : own_d[i];
-      db[4 + i] = hw ? own_d[i] : par_d[i];
-    }
-    sb = hh == hw ? own_b : par_b;
+    const uint4 a = x.q[0][lane], b = x.q[1][lane], c = x.q[2][lane], d = x.q[3][lane];
+    pb = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    db = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, (int)d.x, (int)d.y, (int)d.z, (int)d.w};
+    sb = (int)x.sb[hh][lane];
   }
 }
 
@@ -803,13 +809,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dkdv_split_kernel(BwdPtrs
   constexpr int STAGE = 4 * TB + 2 * 64 * 4 + 16;   // + the tile's Q step and dO step
   constexpr int HCB = D / 64;                         // channel blocks per wave
   __shared__ __align__(16) uint8_t lds[2][STAGE];
-  __shared__ uint32_t xch[NW][kXW * 64];
+  __shared__ SwapArea xch[G];
   const int nkt = Np / KEYS;
   int bh, kt;
   work_item(blockIdx.x, BH, nkt, bh, kt);
   const int kbase = kt * KEYS;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = w % G, hw = w / G, partner = grp + G * (1 - hw);
+  const int grp = w % G, hw = w / G;
   const int n = lane & 31, hh = lane >> 5;
   const int kw = kbase + 32 * grp, key = kw + n;
   const int nb = Np / 64;
@@ -835,15 +841,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dkdv_split_kernel(BwdPtrs
   const int qt0 = CAUSAL ? kbase / 64 : 0;
   const int nqt = (N + 63) / 64;
   // the tile loads are issued by four waves (the one-wave kernels' pattern)
+  uint32_t ro[kTileLoads<D>], co[kTileLoads<D>];
+#pragma unroll
+  for (int i = 0; i < kTileLoads<D>; i++) {
+    ro[i] = rows_voff<D>(i, w & 3, lane);
+    co[i] = cols_voff<D>(i, w & 3, lane);
+  }
   auto stage = [&](int buf, int qt) {
     if (w >= 4) return;
     uint8_t* L = lds[buf];
     const size_t rb = ((size_t)bh * Np + (size_t)qt * 64) * D;
     const size_t tb = ((size_t)bh * nb + qt) * TB;
-    stage_rows<D>(L, reinterpret_cast<const uint8_t*>(bp.q_codes) + rb, w, lane);
-    stage_rows<D>(L + TB, bp.do_codes + rb, w, lane);
-    stage_cols<D>(L + 2 * TB, bp.doT_codes + tb, w, lane);
-    stage_cols<D>(L + 3 * TB, bp.qT_codes + tb, w, lane);
+#pragma unroll
+    for (int i = 0; i < kTileLoads<D>; i++) {
+      const int o = (256 * i + 64 * w) * 16;
+      load_lds16_async_so(reinterpret_cast<const uint8_t*>(bp.q_codes) + rb, ro[i], L + o);
+      load_lds16_async_so(bp.do_codes + rb, ro[i], L + TB + o);
+      load_lds16_async_so(bp.doT_codes + tb, co[i], L + 2 * TB + o);
+      load_lds16_async_so(bp.qT_codes + tb, co[i], L + 3 * TB + o);
+    }
     if (w == 0 && lane < 16) load_lds16_async(bp.lse2 + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 16 * lane);
     if (w == 1 && lane < 16) load_lds16_async(bp.Dvec + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 256 + 16 * lane);
     if (w == 2 && lane < 2) load_lds4_async((lane ? bp.do_step : bp.q_step) + (size_t)bh * nb + qt, L + 4 * TB + 512);
@@ -888,7 +904,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dkdv_split_kernel(BwdPtrs
     }
     v8i pb, db;
     int sb = 0;
-    swap_halves<ACTIVE>(p, ds, am, hw, hh, xch[w], xch[partner], lane, pb, db, sb);
+    swap_halves<ACTIVE>(p, ds, am, hw, hh, xch[grp], lane, pb, db, sb);
     if (ACTIVE) {
 #pragma unroll
       for (int c = 0; c < HCB; c++) {
@@ -962,14 +978,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_split_kernel(BwdPtrs b
   constexpr int STAGE = 3 * TB + 16;   // + the tile's K step and V step
   constexpr int HCB = D / 64;
   __shared__ __align__(16) uint8_t lds[2][STAGE];
-  __shared__ uint32_t xch[NW][kXW * 64];
+  __shared__ SwapArea xch[G];
   const int nqt = Np / QUERIES;
   int bh, t;
   work_item(blockIdx.x, BH, nqt, bh, t);
   const int qt = CAUSAL ? nqt - 1 - t : t;   // causal: the longest rows first
   const int qbase = qt * QUERIES;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = w % G, hw = w / G, partner = grp + G * (1 - hw);
+  const int grp = w % G, hw = w / G;
   const int n = lane & 31, hh = lane >> 5;
   const int qw = qbase + 32 * grp, q = qw + n;
   const int nb = Np / 64;
@@ -997,14 +1013,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_split_kernel(BwdPtrs b
 
   int nkt = (N + 63) / 64;
   if (CAUSAL) nkt = min(nkt, (qbase + QUERIES - 1) / 64 + 1);
+  uint32_t ro[kTileLoads<D>], co[kTileLoads<D>];
+#pragma unroll
+  for (int i = 0; i < kTileLoads<D>; i++) {
+    ro[i] = rows_voff<D>(i, w & 3, lane);
+    co[i] = cols_voff<D>(i, w & 3, lane);
+  }
   auto stage = [&](int buf, int kt) {
     if (w >= 4) return;
     uint8_t* L = lds[buf];
     const size_t rb = ((size_t)bh * Np + (size_t)kt * 64) * D;
     const size_t tb = ((size_t)bh * nb + kt) * TB;
-    stage_rows<D>(L, reinterpret_cast<const uint8_t*>(bp.k_codes) + rb, w, lane);
-    stage_rows<D>(L + TB, bp.v_codes + rb, w, lane);
-    stage_cols<D>(L + 2 * TB, bp.kT_codes + tb, w, lane);
+#pragma unroll
+    for (int i = 0; i < kTileLoads<D>; i++) {
+      const int o = (256 * i + 64 * w) * 16;
+      load_lds16_async_so(reinterpret_cast<const uint8_t*>(bp.k_codes) + rb, ro[i], L + o);
+      load_lds16_async_so(bp.v_codes + rb, ro[i], L + TB + o);
+      load_lds16_async_so(bp.kT_codes + tb, co[i], L + 2 * TB + o);
+    }
     if (w == 0 && lane < 2) load_lds4_async((lane ? bp.v_step : bp.k_step) + (size_t)bh * nb + kt, L + 3 * TB);
   };
   auto tile = [&](const uint8_t* L, int kt, auto mode) {
@@ -1040,7 +1066,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_split_kernel(BwdPtrs b
     }
     v8i pb, db;
     int sb = 0;
-    swap_halves<ACTIVE>(p, ds, am, hw, hh, xch[w], xch[partner], lane, pb, db, sb);
+    swap_halves<ACTIVE>(p, ds, am, hw, hh, xch[grp], lane, pb, db, sb);
     if (ACTIVE) {
 #pragma unroll
       for (int c = 0; c < HCB; c++) {
@@ -1069,11 +1095,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_split_kernel(BwdPtrs b
   for (; kt < min(nvis, nkt); kt++) iter(kt, std::integral_constant<int, 1>{});
   for (; kt < nkt; kt++) iter(kt, std::integral_constant<int, -1>{});
   // rowsum(dS) over both halves of the keys, in a fixed order (subtile 0's share first)
-  const float rs_own = half_sum(rsum);
-  xch[w][lane] = __float_as_uint(rs_own);
+  xch[grp].sb[hw][lane] = __float_as_uint(half_sum(rsum));
   __syncthreads();
-  const float rs_par = __uint_as_float(xch[partner][lane]);
-  const float rs = (hw ? rs_par + rs_own : rs_own + rs_par) * (1.0f / 448.0f);
+  const float rs = (__uint_as_float(xch[grp].sb[0][lane]) + __uint_as_float(xch[grp].sb[1][lane])) * (1.0f / 448.0f);
   if (q < N) {
     uint16_t* dqr = reinterpret_cast<uint16_t*>(dq) + ((size_t)bh * N + q) * D;
     const float* ck = bp.chan_step + ((size_t)2 * BH + bh) * D + 4 * hh;

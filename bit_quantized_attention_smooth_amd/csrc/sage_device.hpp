@@ -98,6 +98,18 @@ __device__ __forceinline__ void load_lds16_async(const void* g, void* lds) {
 #endif
 }
 
+// load_lds16_async with the global address split into a wave-uniform 64-bit base (held in
+// scalar registers) and a per-lane 32-bit byte offset (the "saddr" form of the instruction), so
+// a loop that moves the base keeps each lane's offset in one register and does no 64-bit
+// vector address arithmetic per load.
+__device__ __forceinline__ void load_lds16_async_so(const void* sbase, uint32_t voff, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)lds);
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(base) : "memory");
+#endif
+}
+
 // The 4-byte form of load_lds16_async (lane L's dword lands at lds + 4 L), same contract.
 __device__ __forceinline__ void load_lds4_async(const void* g, void* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
