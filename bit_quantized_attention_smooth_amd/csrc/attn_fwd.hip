@@ -283,11 +283,11 @@ __device__ __forceinline__ void issue_k(uint8_t* lds, const FwdArgs& a, size_t k
 #pragma unroll
   for (int i = 0; i < LO::KL; i++) {
     const int pbase = LO::NTHREADS * i + 64 * w;
-    if (pbase < G::KCHUNKS) load_lds16_async(kg + lo.kld[i], lds + pbase * 16);
+    if (pbase < G::KCHUNKS) load_lds16_async_so(kg, lo.kld[i], lds + pbase * 16);
   }
   if (QK == QK_MXFP4 && w == 0 && lane < G::SBYTES / 16) {
     const uint8_t* sg = reinterpret_cast<const uint8_t*>(a.k_scales) + (kt0 + (size_t)j * kTK) * (D / 32);
-    load_lds16_async(sg + lane * 16, lds + G::KBYTES);
+    load_lds16_async_so(sg, lane * 16, lds + G::KBYTES);
   }
 }
 
@@ -299,12 +299,12 @@ __device__ __forceinline__ void issue_v(uint8_t* lds, const FwdArgs& a, size_t k
 #pragma unroll
   for (int i = 0; i < LaneOffs<D, QK, NT, PV>::VL; i++) {
     const int pbase = NT * i + 64 * w;
-    if (pbase < G::VCHUNKS) load_lds16_async(vg + lo.vld[i], lds + pbase * 16);
+    if (pbase < G::VCHUNKS) load_lds16_async_so(vg, lo.vld[i], lds + pbase * 16);
   }
   if (PV != PV_FP8 && w == NT / 64 - 1 && lane < G::VSB / 16) {
     // E8M0 bytes of the tile's two 32-key groups: [group][channel], contiguous in the buffer
     const uint8_t* sg = reinterpret_cast<const uint8_t*>(a.v_scales) + (kt0 / 32 + 2 * j) * D;
-    load_lds16_async(sg + 16 * lane, lds + G::VBYTES + 16 * lane);
+    load_lds16_async_so(sg, 16 * lane, lds + G::VBYTES + 16 * lane);
   }
 }
 
