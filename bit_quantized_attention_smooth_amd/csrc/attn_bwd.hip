@@ -10,11 +10,12 @@
 //   dP  = dO V^T         FP8, per-64-token-block steps of dO and V (they factor out of
 //                        the channel sum)
 //   dS  = P o (dP - D),  D_i = sum_c dO_ic O_ic
-//   dV  = P~^T dO        FP8: P~ = E4M3(448 P), dO^T with per-channel steps (they factor
-//                        out of the query sum)
-//   dK  = sm dS^T Q      FP8: Q^T with per-channel steps; dS in E4M3 with one power-of-two
-//                        scale per 32-element block (an MX block), applied by the scaled MFMA
-//   dQ  = sm (dS K_s - rowsum(dS) P K_s)  FP8 the same way, K_s^T with per-channel steps.
+//   dV  = P~^T dO        FP8: P~ = E4M3(448 P); dO^T in E4M3 with one power-of-two (E8M0)
+//                        scale per channel and 32-token block (an MX block along the
+//                        query sum), applied by the scaled MFMA
+//   dK  = sm dS^T Q      FP8: Q^T the same way; dS in E4M3 with one E8M0 scale per
+//                        32-element block, also applied by the scaled MFMA
+//   dQ  = sm (dS K_s - rowsum(dS) P K_s)  FP8 the same way, K_s^T with MX scales too.
 //                        With quantized dP the rows of dS no longer sum to 0: rowsum(dS) =
 //                        D^ - D, where D^ = sum_j P dP^ is the value consistent with the
 //                        quantized dP.  Replacing D by D^ turns dS into dS - P rowsum(dS); for
@@ -28,7 +29,8 @@
 // loops over query tiles, accumulates dK^T and dV^T) and a query-stationary kernel (a wave
 // owns 32 queries, loops over key tiles, accumulates dQ^T).  A prologue writes the operand
 // layouts they need: dO and V in FP8 token-major with block steps, dO^T, Q^T and K_s^T in
-// FP8 with channel steps, D and the smoothed-domain LSE in log2 units.
+// FP8 with their MX scales (block-local, so no statistics pass over the tensors is needed), D
+// and the smoothed-domain LSE in log2 units.
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
 
@@ -36,7 +38,7 @@ namespace sage {
 
 namespace {
 
-constexpr int kNT = 3;   // channel-step tensors: dO, Q, K_s
+constexpr int kNT = 3;   // transposed FP8 tensors: dO, Q, K_s
 
 // Row of the 64-row operand tile fed to MFMA A-row m in subtile s, so that output lane
 // half h holds tile positions 32h + 16s + r (r = register index).
@@ -56,8 +58,8 @@ struct BwdPtrs {
   const float* mu_k;
   const float* lse_corr;
   // backward prologue outputs
-  uint32_t* amax_part;    // [3, kStatChunks, BH, d] max |x| per token chunk and channel (bit patterns)
-  float* chan_step;       // [3, BH, d] channel steps of dO^T, Q^T, K_s^T codes
+  uint8_t* tsc;           // [3, BH, Np/64, 2, d] E8M0 scales of the dO^T, Q^T, K_s^T codes per channel and
+                          // 32-token block of a tile (block b: tokens 16 b + [0, 16) and 32 + 16 b + [0, 16))
   float* Dvec;            // [BH, Np]
   float* lse2;            // [BH, Np] (LSE - c) log2 e - log2 448; +inf for padding queries
   uint8_t* do_codes;      // [BH, Np, d] E4M3, token-major
@@ -69,55 +71,12 @@ struct BwdPtrs {
   uint8_t* kT_codes;      // [BH, Np/64, d, 64] E4M3 of (K - mu_k) / channel step
 };
 
-template <int DT>
-__device__ __forceinline__ void load8io(const uint16_t* p, float* x) {
-  uint4 u = *reinterpret_cast<const uint4*>(p);
-  uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    x[2 * i] = DT == 0 ? bf16_to_f32(w[i] & 0xffff) : f16_to_f32(w[i] & 0xffff);
-    x[2 * i + 1] = DT == 0 ? bf16_to_f32(w[i] >> 16) : f16_to_f32(w[i] >> 16);
-  }
-}
-
-// max |dO|, |Q|, |K - mu_k| per channel over one of kStatChunks token chunks of a head;
-// partials, so no buffer needs clearing first.  grid (kStatChunks, BH), 256 threads.
-template <int DT, int D>
-__global__ __launch_bounds__(256) void bwd_stats_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict__ q,
-                                                        const uint16_t* __restrict__ k, const float* __restrict__ mu_k,
-                                                        int N, uint32_t* __restrict__ part) {
-  constexpr int C8 = D / 8, RP = 256 / C8;
-  const int bh = blockIdx.y, ch = blockIdx.x, BH = gridDim.y, tid = threadIdx.x, c0 = (tid % C8) * 8, r0 = tid / C8;
-  const int len = (N + kStatChunks - 1) / kStatChunks, t0 = ch * len, t1 = min(N, t0 + len);
-  float mu[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) mu[i] = mu_k[(size_t)bh * D + c0 + i];
-  uint32_t a[kNT][8] = {};
-  for (int r = t0 + r0; r < t1; r += RP) {
-    const size_t off = ((size_t)bh * N + r) * D + c0;
-    float x[kNT][8];
-    load8io<DT>(dout + off, x[0]);
-    load8io<DT>(q + off, x[1]);
-    load8io<DT>(k + off, x[2]);
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      a[0][i] = max(a[0][i], __float_as_uint(fabsf(x[0][i])));
-      a[1][i] = max(a[1][i], __float_as_uint(fabsf(x[1][i])));
-      a[2][i] = max(a[2][i], __float_as_uint(fabsf(x[2][i] - mu[i])));
-    }
-  }
-  __shared__ uint32_t s_a[kNT][RP][D];
-#pragma unroll
-  for (int t = 0; t < kNT; t++)
-#pragma unroll
-    for (int i = 0; i < 8; i++) s_a[t][r0][c0 + i] = a[t][i];
-  __syncthreads();
-  for (int j = tid; j < kNT * D; j += 256) {
-    const int t = j / D, c = j % D;
-    uint32_t m = 0;
-    for (int r = 0; r < RP; r++) m = max(m, s_a[t][r][c]);
-    part[(((size_t)t * kStatChunks + ch) * BH + bh) * D + c] = m;
-  }
+// E8M0 byte of the smallest power of two s with amax / s <= 448 (the E4M3 maximum), at
+// least 1 so that the scale is a normal float.  amax = 2^(E-127) (1 + f): E - 8 suffices
+// when 1 + f <= 1.75, else E - 7.
+__device__ __forceinline__ int e4m3_scale_byte(uint32_t amax_bits) {
+  const int e = (int)(amax_bits >> 23) - 8 + ((amax_bits & 0x7fffff) > 0x600000 ? 1 : 0);
+  return max(e, 1);
 }
 
 // Unpack 8 16-bit inputs (one 16-byte load) to fp32.
@@ -132,7 +91,7 @@ __device__ __forceinline__ void unpack8io(const uint4 u, float* x) {
 }
 
 // Per 64-token block: D, lse2, dO / V token-major FP8 with block steps, dO^T / Q^T / K_s^T
-// FP8 with channel steps.  grid (Np/64, BH), 2*D threads.  A thread holds channels
+// FP8 with E8M0 scales per channel and 32-token block.  grid (Np/64, BH), 2*D threads.  A thread holds channels
 // 8 cidx .. 8 cidx + 7 of the block's rows 4 rg .. 4 rg + 3, so one channel's four codes are
 // one dword of the transposed [channel][token] layout; a wave covers 8 channel groups x 8
 // row groups (8 rows of 128 contiguous bytes per load).  The transposed dwords pass through
@@ -148,8 +107,7 @@ __global__ __launch_bounds__(2 * D) void bwd_prep_kernel(const uint16_t* __restr
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int cidx = 8 * (w % CG) + (lane & 7), rg = 8 * (w / CG) + (lane >> 3), c0 = 8 * cidx;
   const int nb = Np / 64;
-  __shared__ float s_inv[kNT][D];
-  __shared__ float s_pre[kNT][D];   // power of two applied to x before the step's reciprocal
+  __shared__ uint32_t s_bm[kNT][2][2][D];   // max |x| per (tensor, block, wave row, channel), bits
   __shared__ uint32_t s_red[2][NW];
   __shared__ float s_dsum[CG][64];
   __shared__ uint32_t s_T[kNT][D * RS];
@@ -168,77 +126,93 @@ __global__ __launch_bounds__(2 * D) void bwd_prep_kernel(const uint16_t* __restr
       rk[r] = *reinterpret_cast<const uint4*>(k + off);
     }
   }
-  // channel steps from the chunk partials: code = x * 448 / amax
-  for (int j = tid; j < kNT * D; j += NTH) {
-    const int t = j / D, c = j % D;
-    uint32_t m = 0;
-#pragma unroll
-    for (int ch = 0; ch < kStatChunks; ch++) m = max(m, bp.amax_part[(((size_t)t * kStatChunks + ch) * BH + bh) * D + c]);
-    const float am = __uint_as_float(m);
-    // code = (x pre) * (448 / (amax pre)): pre = 2^64 for maxima below 2^-64, whose 448 / amax
-    // would exceed binary32 (x pre is exact; pre = 1 otherwise)
-    const float pre = am < 0x1p-64f ? 0x1p64f : 1.0f;
-    s_pre[t][c] = pre;
-    s_inv[t][c] = am == 0.0f ? 0.0f : 448.0f / (am * pre);
-    if (blk == 0) bp.chan_step[((size_t)t * BH + bh) * D + c] = am / 448.0f;
-  }
   float mu[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) mu[i] = bp.mu_k[(size_t)bh * D + c0 + i];
-  __syncthreads();
-  // row sums dO.O, max |dO| and |V|, and the channel-step codes, two rows at a time
-  uint32_t tw[kNT][8];
+  // row sums dO.O and the thread's max |dO|, |V| (the token-major codes' block steps)
   uint32_t ad = 0, av = 0;
 #pragma unroll
-  for (int h = 0; h < 2; h++) {
+  for (int r = 0; r < 4; r++) {
+    float xd[8], xo[8], xv[8];
+    unpack8io<DT>(rd[r], xd);
+    unpack8io<DT>(ro[r], xo);
+    unpack8io<DT>(rv[r], xv);
+    float dsum = 0.0f;
 #pragma unroll
-    for (int r2 = 0; r2 < 2; r2++) {
-      const int r = 2 * h + r2;
-      float xd[8], xo[8], xv[8];
-      unpack8io<DT>(rd[r], xd);
-      unpack8io<DT>(ro[r], xo);
-      unpack8io<DT>(rv[r], xv);
-      float dsum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        dsum += xd[i] * xo[i];
-        ad = max(ad, __float_as_uint(fabsf(xd[i])));
-        av = max(av, __float_as_uint(fabsf(xv[i])));
-      }
-      // sum over the 8 lanes of this wave that share the row
-#pragma unroll
-      for (int o2 = 1; o2 < 8; o2 <<= 1) dsum += __shfl_xor(dsum, o2);
-      if ((lane & 7) == 0) s_dsum[w % CG][4 * rg + r] = dsum;
+    for (int i = 0; i < 8; i++) {
+      dsum += xd[i] * xo[i];
+      ad = max(ad, __float_as_uint(fabsf(xd[i])));
+      av = max(av, __float_as_uint(fabsf(xv[i])));
     }
-    const int r0 = 2 * h;
-    float xd[2][8], xq[2][8], xk[2][8];
+    // sum over the 8 lanes of this wave that share the row
 #pragma unroll
-    for (int r2 = 0; r2 < 2; r2++) {
-      unpack8io<DT>(rd[r0 + r2], xd[r2]);
-      unpack8io<DT>(rq[r0 + r2], xq[r2]);
-      unpack8io<DT>(rk[r0 + r2], xk[r2]);
-      const bool in = t0 + 4 * rg + r0 + r2 < N;   // padding rows stay zero (not -mu_k)
+    for (int o2 = 1; o2 < 8; o2 <<= 1) dsum += __shfl_xor(dsum, o2);
+    if ((lane & 7) == 0) s_dsum[w % CG][4 * rg + r] = dsum;
+  }
+  // Transposed codes of dO, Q and K_s = K - mu_k with one E8M0 scale per channel and 32-token
+  // block, the blocks the scaled MFMA applies along its 64-token K dimension: block b holds the
+  // tile's tokens 16 b + [0, 16) and 32 + 16 b + [0, 16), i.e. rows of lane half b of both wave
+  // rows.  The scale is the smallest power of two that keeps the block's max |x| at or below
+  // 448 (no element clips).  Each lane half first reduces its 16 rows per channel (lanes
+  // l ^ 8, l ^ 16), the two wave rows then meet in LDS.
+  const int bsel = lane >> 5, wrow = w / CG;
+  auto tensor_row = [&](int t, int r, float* x) {
+    unpack8io<DT>(t == 0 ? rd[r] : t == 1 ? rq[r] : rk[r], x);
+    if (t == 2) {
+      const bool in = t0 + 4 * rg + r < N;   // padding rows stay zero (not -mu_k)
 #pragma unroll
-      for (int i = 0; i < 8; i++) xk[r2][i] = in ? xk[r2][i] - mu[i] : 0.0f;
+      for (int i = 0; i < 8; i++) x[i] = in ? x[i] - mu[i] : 0.0f;
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < kNT; t++) {
+    uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      float x[8];
+      tensor_row(t, r, x);
+#pragma unroll
+      for (int i = 0; i < 8; i++) m[i] = max(m[i], __float_as_uint(fabsf(x[i])));
     }
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      const float s0 = s_inv[0][c0 + i], s1 = s_inv[1][c0 + i], s2 = s_inv[2][c0 + i];
+      m[i] = max(m[i], (uint32_t)__shfl_xor((int)m[i], 8));
+      m[i] = max(m[i], (uint32_t)__shfl_xor((int)m[i], 16));
+    }
+    if ((lane & 24) == 0) {
 #pragma unroll
-      for (int r2 = 0; r2 < 2; r2++) {
-        xd[r2][i] *= s_pre[0][c0 + i];
-        xq[r2][i] *= s_pre[1][c0 + i];
-        xk[r2][i] *= s_pre[2][c0 + i];
-      }
-      if (h == 0) {   // rows 0, 1 -> bytes 0, 1
-        tw[0][i] = __builtin_amdgcn_cvt_pk_fp8_f32(xd[0][i] * s0, xd[1][i] * s0, 0, false);
-        tw[1][i] = __builtin_amdgcn_cvt_pk_fp8_f32(xq[0][i] * s1, xq[1][i] * s1, 0, false);
-        tw[2][i] = __builtin_amdgcn_cvt_pk_fp8_f32(xk[0][i] * s2, xk[1][i] * s2, 0, false);
-      } else {        // rows 2, 3 -> bytes 2, 3
-        tw[0][i] = __builtin_amdgcn_cvt_pk_fp8_f32(xd[0][i] * s0, xd[1][i] * s0, tw[0][i], true);
-        tw[1][i] = __builtin_amdgcn_cvt_pk_fp8_f32(xq[0][i] * s1, xq[1][i] * s1, tw[1][i], true);
-        tw[2][i] = __builtin_amdgcn_cvt_pk_fp8_f32(xk[0][i] * s2, xk[1][i] * s2, tw[2][i], true);
-      }
+      for (int i = 0; i < 8; i++) s_bm[t][bsel][wrow][c0 + i] = m[i];
+    }
+  }
+  __syncthreads();
+  uint32_t tw[kNT][8];
+#pragma unroll
+  for (int t = 0; t < kNT; t++) {
+    float sc[8];
+    uint8_t byte[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      byte[i] = (uint8_t)e4m3_scale_byte(max(s_bm[t][bsel][0][c0 + i], s_bm[t][bsel][1][c0 + i]));
+      sc[i] = __uint_as_float((uint32_t)byte[i] << 23);
+    }
+    if (wrow == 0 && (lane & 24) == 0) {
+      uint32_t b4[2];
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+        b4[j] = (uint32_t)byte[4 * j] | ((uint32_t)byte[4 * j + 1] << 8) | ((uint32_t)byte[4 * j + 2] << 16) |
+                ((uint32_t)byte[4 * j + 3] << 24);
+      *reinterpret_cast<uint2*>(bp.tsc + ((((size_t)t * BH + bh) * nb + blk) * 2 + bsel) * D + c0) = make_uint2(b4[0], b4[1]);
+    }
+    float x[4][8];
+#pragma unroll
+    for (int r = 0; r < 4; r++) tensor_row(t, r, x[r]);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      typedef short v2s __attribute__((ext_vector_type(2)));
+      v2s c2 = __builtin_bit_cast(v2s, __float_as_int(x[0][i]));
+      c2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c2, x[0][i], x[1][i], sc[i], false);   // rows 0, 1 -> bytes 0, 1
+      c2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c2, x[2][i], x[3][i], sc[i], true);    // rows 2, 3 -> bytes 2, 3
+      tw[t][i] = __builtin_bit_cast(uint32_t, c2);
     }
   }
 #pragma unroll
@@ -362,19 +336,11 @@ __device__ __forceinline__ v8i lds_v8i(const uint8_t* p0, const uint8_t* p1) {
   return v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
 }
 
-// O^T[32 x 32] += A[32 x 64] B[64 x 32] in E4M3, B scaled per 32-element K block by the
-// E8M0 byte `sb` (A unscaled).  The two K blocks of the scaled form are bytes 0-15 and
-// 16-31 of both lane halves; block b takes its scale from the lanes of half b.
-__device__ __forceinline__ v16f mfma_f8_sb(v8i a, v8i b, v16f c, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
-}
-
-// E8M0 byte of the smallest power of two s with amax / s <= 448 (the E4M3 maximum), at
-// least 1 so that the scale is a normal float.  amax = 2^(E-127) (1 + f): E - 8 suffices
-// when 1 + f <= 1.75, else E - 7.
-__device__ __forceinline__ int e4m3_scale_byte(uint32_t amax_bits) {
-  const int e = (int)(amax_bits >> 23) - 8 + ((amax_bits & 0x7fffff) > 0x600000 ? 1 : 0);
-  return max(e, 1);
+// O^T[32 x 32] += A[32 x 64] B[64 x 32] in E4M3 with E8M0 block scales: the two K blocks of
+// the scaled form are bytes 0-15 and 16-31 of both lane halves; A row m's block b takes the
+// byte `sa` of lane m + 32 b, B column m's block b the byte `sb` of the same lane (127: 1).
+__device__ __forceinline__ v16f mfma_f8_ab(v8i a, v8i b, v16f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
 // A lane's 32 dS values (bytes 0-15: subtile 0, bytes 16-31: subtile 1) -> E4M3 B operand
@@ -407,7 +373,8 @@ __device__ __forceinline__ int quant_ds(const float* x, float a0, float a1, int 
 template <int D, bool CAUSAL, int DT>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdPtrs bp, void* dk, void* dv, int N, int Np, int BH, float sm) {
   constexpr int TB = 64 * D;                          // one tile of 64 x D bytes
-  constexpr int STAGE = 4 * TB + 2 * 64 * 4 + 16;   // + the tile's Q step and dO step
+  constexpr int SCO = 4 * TB + 2 * 64 * 4 + 16;     // + lse2, D, the tile's Q step and dO step
+  constexpr int STAGE = SCO + 4 * D;                  // + the E8M0 scales of dO^T and Q^T
   constexpr int NCB = D / 32;
   __shared__ __align__(16) uint8_t lds[2][STAGE];
   const int nkt = Np / 128;
@@ -461,6 +428,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdPtrs 
     if (w == 0 && lane < 16) load_lds16_async(bp.lse2 + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 16 * lane);
     if (w == 1 && lane < 16) load_lds16_async(bp.Dvec + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 256 + 16 * lane);
     if (w == 2 && lane < 2) load_lds4_async((lane ? bp.do_step : bp.q_step) + (size_t)bh * nb + qt, L + 4 * TB + 512);
+    // [dO^T, Q^T][block][channel] scale bytes of this tile
+    if (w == 3 && lane < D / 4)
+      load_lds16_async(bp.tsc + (((size_t)(lane / (D / 8)) * BH + bh) * nb + qt) * 2 * D + 16 * (lane % (D / 8)), L + SCO);
   };
   // one query tile: S, dP on MFMA; P~ and dS on the vector unit; dV^T, dK^T on MFMA
   auto tile = [&](const uint8_t* L, int qt, auto masked_tag) {
@@ -513,7 +483,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdPtrs 
 #pragma unroll
     for (int cb = 0; cb < NCB; cb++) {
       const int row = 32 * cb + n;
-      dV[cb] = mfma_f8(lds_v8i(L + 2 * TB + coloff(row, 2 * hh), L + 2 * TB + coloff(row, 2 * hh + 1)), pb, dV[cb]);
+      dV[cb] = mfma_f8_ab(lds_v8i(L + 2 * TB + coloff(row, 2 * hh), L + 2 * TB + coloff(row, 2 * hh + 1)), pb, dV[cb],
+                          L[SCO + hh * D + row], 127);
     }
     // dK^T += Q^T dS~ (dS in E4M3 with per-block power-of-two scales)
     v8i db;
@@ -521,7 +492,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdPtrs 
 #pragma unroll
     for (int cb = 0; cb < NCB; cb++) {
       const int row = 32 * cb + n;
-      dK[cb] = mfma_f8_sb(lds_v8i(L + 3 * TB + coloff(row, 2 * hh), L + 3 * TB + coloff(row, 2 * hh + 1)), db, dK[cb], sb);
+      dK[cb] = mfma_f8_ab(lds_v8i(L + 3 * TB + coloff(row, 2 * hh), L + 3 * TB + coloff(row, 2 * hh + 1)), db, dK[cb],
+                          L[SCO + 2 * D + hh * D + row], sb);
     }
   };
   // per-wave phases over the query tiles (wave-uniform bounds, so the accumulators never meet
@@ -544,21 +516,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdPtrs 
   for (; qt < min(qt_first, nqt); qt++) iter(qt, std::integral_constant<int, -1>{});
   for (; qt < min(qt_open, nqt); qt++) iter(qt, std::integral_constant<int, 1>{});
   for (; qt < nqt; qt++) iter(qt, std::integral_constant<int, 0>{});
-  // epilogue: dK = sm qT_step dK^T / 448, dV = doT_step dV^T / 448; lane holds channels
-  // 32 cb + 8 g + 4 hh + {0..3} of its key.  All factors are loaded before the first store.
+  // epilogue: dK = sm dK^T / 448, dV = dV^T / 448 (the operand scales were applied by the
+  // MFMA); lane holds channels 32 cb + 8 g + 4 hh + {0..3} of its key
   if (key < N) {
     uint16_t* dkr = reinterpret_cast<uint16_t*>(dk) + ((size_t)bh * N + key) * D;
     uint16_t* dvr = reinterpret_cast<uint16_t*>(dv) + ((size_t)bh * N + key) * D;
-    const float* cdo = bp.chan_step + (size_t)bh * D + 4 * hh;
-    const float* cq = bp.chan_step + ((size_t)BH + bh) * D + 4 * hh;
-    v4f fk[NCB][4], fv[NCB][4];
-#pragma unroll
-    for (int cb = 0; cb < NCB; cb++)
-#pragma unroll
-      for (int g = 0; g < 4; g++) {
-        fk[cb][g] = *reinterpret_cast<const v4f*>(cq + 32 * cb + 8 * g);
-        fv[cb][g] = *reinterpret_cast<const v4f*>(cdo + 32 * cb + 8 * g);
-      }
     const float kf448 = sm * (1.0f / 448.0f);
 #pragma unroll
     for (int cb = 0; cb < NCB; cb++)
@@ -569,10 +531,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdPtrs 
 #pragma unroll
         for (int t = 0; t < 2; t++) {
           const int i0 = 2 * t, i1 = 2 * t + 1;
-          k2[t] = (uint32_t)to_io<DT>(dK[cb][4 * g + i0] * (fk[cb][g][i0] * kf448)) |
-                  ((uint32_t)to_io<DT>(dK[cb][4 * g + i1] * (fk[cb][g][i1] * kf448)) << 16);
-          v2[t] = (uint32_t)to_io<DT>(dV[cb][4 * g + i0] * (fv[cb][g][i0] * (1.0f / 448.0f))) |
-                  ((uint32_t)to_io<DT>(dV[cb][4 * g + i1] * (fv[cb][g][i1] * (1.0f / 448.0f))) << 16);
+          k2[t] = (uint32_t)to_io<DT>(dK[cb][4 * g + i0] * kf448) | ((uint32_t)to_io<DT>(dK[cb][4 * g + i1] * kf448) << 16);
+          v2[t] = (uint32_t)to_io<DT>(dV[cb][4 * g + i0] * (1.0f / 448.0f)) |
+                  ((uint32_t)to_io<DT>(dV[cb][4 * g + i1] * (1.0f / 448.0f)) << 16);
         }
         *reinterpret_cast<uint2*>(dkr + ch) = make_uint2(k2[0], k2[1]);
         *reinterpret_cast<uint2*>(dvr + ch) = make_uint2(v2[0], v2[1]);
@@ -587,7 +548,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdPtrs 
 template <int D, bool CAUSAL, int DT>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdPtrs bp, void* dq, int N, int Np, int BH, float sm) {
   constexpr int TB = 64 * D;
-  constexpr int STAGE = 3 * TB + 16;   // + the tile's K step and V step
+  constexpr int SCO = 3 * TB + 16;     // + the tile's K step and V step
+  constexpr int STAGE = SCO + 2 * D;   // + the E8M0 scales of K_s^T
   constexpr int NCB = D / 32;
   __shared__ __align__(16) uint8_t lds[2][STAGE];
   const int nqt = Np / 128;
@@ -642,6 +604,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdPtrs bp
       load_lds16_async_so(bp.kT_codes + tb, co[i], L + 2 * TB + o);
     }
     if (w == 0 && lane < 2) load_lds4_async((lane ? bp.v_step : bp.k_step) + (size_t)bh * nb + kt, L + 3 * TB);
+    if (w == 1 && lane < D / 8) load_lds16_async(bp.tsc + (((size_t)2 * BH + bh) * nb + kt) * 2 * D + 16 * lane, L + SCO);
   };
   auto tile = [&](const uint8_t* L, int kt, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
@@ -688,8 +651,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdPtrs bp
     for (int cb = 0; cb < NCB; cb++) {
       const int row = 32 * cb + n;
       const v8i a = lds_v8i(L + 2 * TB + coloff(row, 2 * hh), L + 2 * TB + coloff(row, 2 * hh + 1));
-      dQ[cb] = mfma_f8_sb(a, db, dQ[cb], sb);
-      PK[cb] = mfma_f8(a, pb, PK[cb]);   // P K_s for the rowsum correction
+      const int sa = L[SCO + hh * D + row];
+      dQ[cb] = mfma_f8_ab(a, db, dQ[cb], sa, sb);
+      PK[cb] = mfma_f8_ab(a, pb, PK[cb], sa, 127);   // P K_s for the rowsum correction
     }
   };
   // per-wave phases over the key tiles (wave-uniform bounds): fully visible tiles, then the
@@ -711,17 +675,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdPtrs bp
   for (; kt < min(nfull, nkt); kt++) iter(kt, std::integral_constant<int, 0>{});
   for (; kt < min(nvis, nkt); kt++) iter(kt, std::integral_constant<int, 1>{});
   for (; kt < nkt; kt++) iter(kt, std::integral_constant<int, -1>{});
-  // epilogue: dQ = sm kT_step (dQ^T - rs PK^T) / 448 with rs = rowsum(dS); hand D^ = D + rs
+  // epilogue: dQ = sm (dQ^T - rs PK^T) / 448 with rs = rowsum(dS); hand D^ = D + rs
   // to the dK/dV kernel
   const float rs = half_sum(rsum) * (1.0f / 448.0f);
   if (q < N) {
     uint16_t* dqr = reinterpret_cast<uint16_t*>(dq) + ((size_t)bh * N + q) * D;
-    const float* ck = bp.chan_step + ((size_t)2 * BH + bh) * D + 4 * hh;
-    v4f fq[NCB][4];
-#pragma unroll
-    for (int cb = 0; cb < NCB; cb++)
-#pragma unroll
-      for (int g = 0; g < 4; g++) fq[cb][g] = *reinterpret_cast<const v4f*>(ck + 32 * cb + 8 * g);
     const float f448 = sm * (1.0f / 448.0f);
 #pragma unroll
     for (int cb = 0; cb < NCB; cb++)
@@ -732,8 +690,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdPtrs bp
 #pragma unroll
         for (int t2 = 0; t2 < 2; t2++) {
           const int i0 = 2 * t2, i1 = 2 * t2 + 1;
-          w2[t2] = (uint32_t)to_io<DT>(fq[cb][g][i0] * f448 * fmaf(-rs, PK[cb][4 * g + i0], dQ[cb][4 * g + i0])) |
-                   ((uint32_t)to_io<DT>(fq[cb][g][i1] * f448 * fmaf(-rs, PK[cb][4 * g + i1], dQ[cb][4 * g + i1])) << 16);
+          w2[t2] = (uint32_t)to_io<DT>(f448 * fmaf(-rs, PK[cb][4 * g + i0], dQ[cb][4 * g + i0])) |
+                   ((uint32_t)to_io<DT>(f448 * fmaf(-rs, PK[cb][4 * g + i1], dQ[cb][4 * g + i1])) << 16);
         }
         *reinterpret_cast<uint2*>(dqr + ch) = make_uint2(w2[0], w2[1]);
       }
@@ -806,7 +764,8 @@ template <bool CAUSAL, int DT, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dkdv_split_kernel(BwdPtrs bp, void* dk, void* dv, int N, int Np,
                                                                          int BH, float sm) {
   constexpr int D = 128, TB = 64 * D, G = NW / 2, KEYS = 32 * G;
-  constexpr int STAGE = 4 * TB + 2 * 64 * 4 + 16;   // + the tile's Q step and dO step
+  constexpr int SCO = 4 * TB + 2 * 64 * 4 + 16;     // + lse2, D, the tile's Q step and dO step
+  constexpr int STAGE = SCO + 4 * D;                  // + the E8M0 scales of dO^T and Q^T
   constexpr int HCB = D / 64;                         // channel blocks per wave
   __shared__ __align__(16) uint8_t lds[2][STAGE];
   __shared__ SwapArea xch[G];
@@ -863,6 +822,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dkdv_split_kernel(BwdPtrs
     if (w == 0 && lane < 16) load_lds16_async(bp.lse2 + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 16 * lane);
     if (w == 1 && lane < 16) load_lds16_async(bp.Dvec + (size_t)bh * Np + qt * 64 + 4 * lane, L + 4 * TB + 256 + 16 * lane);
     if (w == 2 && lane < 2) load_lds4_async((lane ? bp.do_step : bp.q_step) + (size_t)bh * nb + qt, L + 4 * TB + 512);
+    // [dO^T, Q^T][block][channel] scale bytes of this tile
+    if (w == 3 && lane < D / 4)
+      load_lds16_async(bp.tsc + (((size_t)(lane / (D / 8)) * BH + bh) * nb + qt) * 2 * D + 16 * (lane % (D / 8)), L + SCO);
   };
   // one query tile: S, dP of subtile hw on MFMA, its P~ and dS~ on the vector unit, the swap,
   // then dV^T, dK^T of this wave's channels over the whole tile
@@ -909,12 +871,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dkdv_split_kernel(BwdPtrs
 #pragma unroll
       for (int c = 0; c < HCB; c++) {
         const int row = 32 * (HCB * hw + c) + n;
-        dV[c] = mfma_f8(lds_v8i(L + 2 * TB + coloff(row, 2 * hh), L + 2 * TB + coloff(row, 2 * hh + 1)), pb, dV[c]);
+        dV[c] = mfma_f8_ab(lds_v8i(L + 2 * TB + coloff(row, 2 * hh), L + 2 * TB + coloff(row, 2 * hh + 1)), pb, dV[c],
+                           L[SCO + hh * D + row], 127);
       }
 #pragma unroll
       for (int c = 0; c < HCB; c++) {
         const int row = 32 * (HCB * hw + c) + n;
-        dK[c] = mfma_f8_sb(lds_v8i(L + 3 * TB + coloff(row, 2 * hh), L + 3 * TB + coloff(row, 2 * hh + 1)), db, dK[c], sb);
+        dK[c] = mfma_f8_ab(lds_v8i(L + 3 * TB + coloff(row, 2 * hh), L + 3 * TB + coloff(row, 2 * hh + 1)), db, dK[c],
+                           L[SCO + 2 * D + hh * D + row], sb);
       }
     }
   };
@@ -936,20 +900,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dkdv_split_kernel(BwdPtrs
   for (; qt < min(qt_first, nqt); qt++) iter(qt, std::integral_constant<int, -1>{});
   for (; qt < min(qt_open, nqt); qt++) iter(qt, std::integral_constant<int, 1>{});
   for (; qt < nqt; qt++) iter(qt, std::integral_constant<int, 0>{});
-  // epilogue: this wave's channels 32 cb + 8 g + 4 hh + {0..3}, cb = HCB hw + c, of its key
+  // epilogue: dK = sm dK^T / 448, dV = dV^T / 448 for this wave's channels 32 cb + 8 g + 4 hh +
+  // {0..3}, cb = HCB hw + c, of its key
   if (key < N) {
     uint16_t* dkr = reinterpret_cast<uint16_t*>(dk) + ((size_t)bh * N + key) * D;
     uint16_t* dvr = reinterpret_cast<uint16_t*>(dv) + ((size_t)bh * N + key) * D;
-    const float* cdo = bp.chan_step + (size_t)bh * D + 4 * hh;
-    const float* cq = bp.chan_step + ((size_t)BH + bh) * D + 4 * hh;
-    v4f fk[HCB][4], fv[HCB][4];
-#pragma unroll
-    for (int c = 0; c < HCB; c++)
-#pragma unroll
-      for (int g = 0; g < 4; g++) {
-        fk[c][g] = *reinterpret_cast<const v4f*>(cq + 32 * (HCB * hw + c) + 8 * g);
-        fv[c][g] = *reinterpret_cast<const v4f*>(cdo + 32 * (HCB * hw + c) + 8 * g);
-      }
     const float kf448 = sm * (1.0f / 448.0f);
 #pragma unroll
     for (int c = 0; c < HCB; c++)
@@ -960,10 +915,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dkdv_split_kernel(BwdPtrs
 #pragma unroll
         for (int t = 0; t < 2; t++) {
           const int i0 = 2 * t, i1 = 2 * t + 1;
-          k2[t] = (uint32_t)to_io<DT>(dK[c][4 * g + i0] * (fk[c][g][i0] * kf448)) |
-                  ((uint32_t)to_io<DT>(dK[c][4 * g + i1] * (fk[c][g][i1] * kf448)) << 16);
-          v2[t] = (uint32_t)to_io<DT>(dV[c][4 * g + i0] * (fv[c][g][i0] * (1.0f / 448.0f))) |
-                  ((uint32_t)to_io<DT>(dV[c][4 * g + i1] * (fv[c][g][i1] * (1.0f / 448.0f))) << 16);
+          k2[t] = (uint32_t)to_io<DT>(dK[c][4 * g + i0] * kf448) | ((uint32_t)to_io<DT>(dK[c][4 * g + i1] * kf448) << 16);
+          v2[t] = (uint32_t)to_io<DT>(dV[c][4 * g + i0] * (1.0f / 448.0f)) |
+                  ((uint32_t)to_io<DT>(dV[c][4 * g + i1] * (1.0f / 448.0f)) << 16);
         }
         *reinterpret_cast<uint2*>(dkr + ch) = make_uint2(k2[0], k2[1]);
         *reinterpret_cast<uint2*>(dvr + ch) = make_uint2(v2[0], v2[1]);
@@ -975,7 +929,8 @@ template <bool CAUSAL, int DT, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_split_kernel(BwdPtrs bp, void* dq, int N, int Np, int BH,
                                                                        float sm) {
   constexpr int D = 128, TB = 64 * D, G = NW / 2, QUERIES = 32 * G;
-  constexpr int STAGE = 3 * TB + 16;   // + the tile's K step and V step
+  constexpr int SCO = 3 * TB + 16;     // + the tile's K step and V step
+  constexpr int STAGE = SCO + 2 * D;   // + the E8M0 scales of K_s^T
   constexpr int HCB = D / 64;
   __shared__ __align__(16) uint8_t lds[2][STAGE];
   __shared__ SwapArea xch[G];
@@ -1032,6 +987,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_split_kernel(BwdPtrs b
       load_lds16_async_so(bp.kT_codes + tb, co[i], L + 2 * TB + o);
     }
     if (w == 0 && lane < 2) load_lds4_async((lane ? bp.v_step : bp.k_step) + (size_t)bh * nb + kt, L + 3 * TB);
+    if (w == 1 && lane < D / 8) load_lds16_async(bp.tsc + (((size_t)2 * BH + bh) * nb + kt) * 2 * D + 16 * lane, L + SCO);
   };
   auto tile = [&](const uint8_t* L, int kt, auto mode) {
     constexpr int MODE = decltype(mode)::value;
@@ -1072,8 +1028,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_split_kernel(BwdPtrs b
       for (int c = 0; c < HCB; c++) {
         const int row = 32 * (HCB * hw + c) + n;
         const v8i a = lds_v8i(L + 2 * TB + coloff(row, 2 * hh), L + 2 * TB + coloff(row, 2 * hh + 1));
-        dQ[c] = mfma_f8_sb(a, db, dQ[c], sb);
-        PK[c] = mfma_f8(a, pb, PK[c]);   // P K_s for the rowsum correction
+        const int sa = L[SCO + hh * D + row];
+        dQ[c] = mfma_f8_ab(a, db, dQ[c], sa, sb);
+        PK[c] = mfma_f8_ab(a, pb, PK[c], sa, 127);   // P K_s for the rowsum correction
       }
     }
   };
@@ -1100,12 +1057,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_split_kernel(BwdPtrs b
   const float rs = (__uint_as_float(xch[grp].sb[0][lane]) + __uint_as_float(xch[grp].sb[1][lane])) * (1.0f / 448.0f);
   if (q < N) {
     uint16_t* dqr = reinterpret_cast<uint16_t*>(dq) + ((size_t)bh * N + q) * D;
-    const float* ck = bp.chan_step + ((size_t)2 * BH + bh) * D + 4 * hh;
-    v4f fq[HCB][4];
-#pragma unroll
-    for (int c = 0; c < HCB; c++)
-#pragma unroll
-      for (int g = 0; g < 4; g++) fq[c][g] = *reinterpret_cast<const v4f*>(ck + 32 * (HCB * hw + c) + 8 * g);
     const float f448 = sm * (1.0f / 448.0f);
 #pragma unroll
     for (int c = 0; c < HCB; c++)
@@ -1116,8 +1067,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_split_kernel(BwdPtrs b
 #pragma unroll
         for (int t2 = 0; t2 < 2; t2++) {
           const int i0 = 2 * t2, i1 = 2 * t2 + 1;
-          w2[t2] = (uint32_t)to_io<DT>(fq[c][g][i0] * f448 * fmaf(-rs, PK[c][4 * g + i0], dQ[c][4 * g + i0])) |
-                   ((uint32_t)to_io<DT>(fq[c][g][i1] * f448 * fmaf(-rs, PK[c][4 * g + i1], dQ[c][4 * g + i1])) << 16);
+          w2[t2] = (uint32_t)to_io<DT>(f448 * fmaf(-rs, PK[c][4 * g + i0], dQ[c][4 * g + i0])) |
+                   ((uint32_t)to_io<DT>(f448 * fmaf(-rs, PK[c][4 * g + i1], dQ[c][4 * g + i1])) << 16);
         }
         *reinterpret_cast<uint2*>(dqr + ch) = make_uint2(w2[0], w2[1]);
       }
@@ -1128,7 +1079,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_split_kernel(BwdPtrs b
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct BwdLayout {
-  size_t amax_part, chan_step, Dvec, lse2, do_codes, do_step, v_codes, v_step, doT, qT, kT, total;
+  size_t tsc, Dvec, lse2, do_codes, do_step, v_codes, v_step, doT, qT, kT, total;
 };
 
 BwdLayout bwd_layout(const Shape& s) {
@@ -1136,8 +1087,7 @@ BwdLayout bwd_layout(const Shape& s) {
   BwdLayout L;
   size_t off = 0;
   auto take = [&](size_t b) { size_t o = off; off = round256(off + b); return o; };
-  L.amax_part = take((size_t)kNT * kStatChunks * BH * d * 4);
-  L.chan_step = take((size_t)kNT * BH * d * 4);
+  L.tsc = take((size_t)kNT * BH * (Np / 32) * d);
   L.Dvec = take(BH * Np * 4);
   L.lse2 = take(BH * Np * 4);
   L.do_codes = take(BH * Np * d);
@@ -1165,8 +1115,7 @@ hipError_t bwd_run(const Shape& s, const void* q, const void* k, const void* v, 
   bp.k_step = reinterpret_cast<const float*>(qp.k_scales);
   bp.mu_k = qp.mu_k;
   bp.lse_corr = qp.lse_corr;
-  bp.amax_part = reinterpret_cast<uint32_t*>(b + L.amax_part);
-  bp.chan_step = reinterpret_cast<float*>(b + L.chan_step);
+  bp.tsc = b + L.tsc;
   bp.Dvec = reinterpret_cast<float*>(b + L.Dvec);
   bp.lse2 = reinterpret_cast<float*>(b + L.lse2);
   bp.do_codes = b + L.do_codes;
@@ -1184,8 +1133,6 @@ hipError_t bwd_run(const Shape& s, const void* q, const void* k, const void* v, 
     const hipError_t e = launch_prologue(q, k, v, sqk, qp, st);
     if (e != hipSuccess) return e;
   }
-  bwd_stats_kernel<DT, D><<<dim3(kStatChunks, BH), 256, 0, st>>>((const uint16_t*)dout, (const uint16_t*)q,
-                                                                (const uint16_t*)k, qp.mu_k, s.N, bp.amax_part);
   bwd_prep_kernel<DT, D><<<dim3(s.Np / 64, BH), 2 * D, 0, st>>>((const uint16_t*)o, (const uint16_t*)dout,
                                                              (const uint16_t*)v, (const uint16_t*)q,
                                                              (const uint16_t*)k, lse, s.N, s.Np, bp);

@@ -50,14 +50,23 @@ def test_backward_matches_fp64(sage, causal, N, dtype, d):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_backward_dv_column_sum(sage, d):
-    """Rows of P sum to one, so sum_j dV_j = sum_i dO_i per head and channel."""
+    """Rows of P sum to one, so sum_j dV_j = sum_i dO_i per head and channel, up to the FP8
+    rounding of dO and P~.  Each E4M3 code of dO is off by at most half an ulp, 2^-4 of the value,
+    and round-to-nearest makes these errors independent and uniform: a column's error has a
+    standard deviation of at most 2^-4 sqrt(sum_i dO_i^2 / 3).  Allowed: 6 of those plus 3 % of
+    the column sum (the rows of 448 P quantized to E4M3 sum to 448 within that)."""
     from bit_quantized_attention_smooth_amd.workloads import make_inputs
     banner(f"backward dV column sum d={d}")
     x = make_inputs(1, 2, 512, d, dtype="bf16", seed=77, with_do=True)
     _, _, _, _, dv = _run(sage, x, False, 1 / math.sqrt(d))
-    got = dv.float().sum(dim=2).cpu().numpy()
-    want = x["do"].float().sum(dim=2).numpy()
-    assert np.allclose(got, want, rtol=0.03, atol=0.03 * np.abs(want).max())
+    got = dv.float().sum(dim=2).cpu().numpy().astype(np.float64)
+    dof = x["do"].float().numpy().astype(np.float64)
+    want = dof.sum(axis=2)
+    sigma = 2.0 ** -4 * np.sqrt((dof * dof).sum(axis=2) / 3.0)
+    err = np.abs(got - want)
+    assert (err <= 6.0 * sigma + 0.03 * np.abs(want)).all(), (err.max(), sigma.max())
+    # and the errors look like rounding noise, not a bias: their RMS stays near one sigma
+    assert np.sqrt((err * err).mean()) <= 1.5 * np.sqrt((sigma * sigma).mean()), (np.sqrt((err * err).mean()), sigma.max())
 
 
 def _per_head_cos(got, ref):
