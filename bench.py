@@ -118,11 +118,12 @@ def counter_summary(sq_dir, fetch_dir, write_dir, out_path):
 
     sq_rows(lambda k: "attn_fwd_kernel" in k)
     lines += ["", "## Backward kernels (training workloads B=8 H=16 N=2048, causal; d = 64 and 128)", "",
-              "Template arguments: <head dim, causal, I/O dtype>.  At d = 128 one workgroup runs per CU (one wave",
-              "per SIMD).", "",
+              "Template arguments: d = 64 kernels <head dim, causal, I/O dtype>; d = 128 kernels <causal, I/O",
+              "dtype, waves per workgroup> (two waves per 32-token group, two workgroups per CU).", "",
               "| kernel | workgroups | dispatches | MFMA busy | VALU busy | co-exec | VALU instr. per MFMA | wait share of wave cycles |",
               "|---|---|---|---|---|---|---|---|"]
-    sq_rows(lambda k: "bwd_dq_kernel" in k or "bwd_dkdv_kernel" in k)
+    sq_rows(lambda k: any(x in k for x in ("bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_dq_split_kernel",
+                                           "bwd_dkdv_split_kernel")))
     fe, fdur = dispatch_counters(fetch_dir)
     wr, _ = dispatch_counters(write_dir)
     copy = lambda d, c: max(mean(v[c]) for k, v in d.items() if "sage" not in k[0] and c in v)
