@@ -711,7 +711,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdPtrs bp
 // the matrix and vector work per tile is the same as in the one-wave kernels, split in two.
 // The dS~ block scales are those of the one-wave kernels (block b is subtile b across both
 // lane halves), so every MFMA sees the same operands: dK and dV are bit-identical to them,
-// only the fp32 order of dQ's row sum of dS differs.
+// only the fp32 order of dQ's row sum of dS differs.  The dQ kernel issues a tile's products one
+// iteration late, under the next tile's vector work (one swap barrier per tile fewer); the
+// dK/dV kernel, whose per-query LSE and D terms come from LDS, needed 256 registers and spilled
+// in that form (measured slower), so it swaps and multiplies within the tile.
 // NW: waves per workgroup (G = NW / 2 token groups); NW = 4 runs two workgroups per CU.
 
 // Waves per workgroup of the d = 128 kernels: 4 (two workgroups of 64 tokens per CU).
@@ -725,39 +728,45 @@ struct SwapArea {
   uint32_t sb[2][64];
 };
 
-// Subtile hw's 16 P~ and dS~ values of this lane -> its full B operands and the E8M0 byte it
-// supplies (block hh).  am: this lane's max |ds|.  Both waves write their halves and read back
-// the whole, between two workgroup barriers (the caller's loop runs the same barriers on
-// every wave, active or not).
+// Subtile hw's 16 P~ and dS~ values of this lane -> its half of the pair's swap area (quads hw
+// and 2 + hw) and the E8M0 byte of dS~ block hw.  am: this lane's max |ds|.
+__device__ __forceinline__ void write_half(const float* p, const float* ds, float am, int hw, SwapArea& x, int lane) {
+  // block hw spans subtile hw of both lane halves
+  const uint32_t bmax = max(__float_as_uint(am), __float_as_uint(other_half(am)));
+  const int byte = e4m3_scale_byte(bmax);
+  const float sc = __uint_as_float((uint32_t)byte << 23);
+  uint32_t P[4], Q[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    P[i] = (uint32_t)pack_fp8x4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+    typedef short v2s __attribute__((ext_vector_type(2)));
+    v2s w = __builtin_bit_cast(v2s, __float_as_int(ds[4 * i]));
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, ds[4 * i], ds[4 * i + 1], sc, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, ds[4 * i + 2], ds[4 * i + 3], sc, true);
+    Q[i] = __builtin_bit_cast(uint32_t, w);
+  }
+  x.q[hw][lane] = make_uint4(P[0], P[1], P[2], P[3]);
+  x.q[2 + hw][lane] = make_uint4(Q[0], Q[1], Q[2], Q[3]);
+  x.sb[hw][lane] = (uint32_t)byte;
+}
+
+// The pair's whole B operands (P~, dS~) from the swap area, and the E8M0 byte this lane supplies
+// to the scaled MFMA (dS~ block hh).
+__device__ __forceinline__ void read_operands(const SwapArea& x, int lane, int hh, v8i& pb, v8i& db, int& sb) {
+  const uint4 a = x.q[0][lane], b = x.q[1][lane], c = x.q[2][lane], d = x.q[3][lane];
+  pb = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  db = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, (int)d.x, (int)d.y, (int)d.z, (int)d.w};
+  sb = (int)x.sb[hh][lane];
+}
+
+// Both halves of the pair's operands within one tile: each wave writes its half, a workgroup
+// barrier (every wave runs it, active or not), each reads the whole.
 template <bool ACTIVE>
 __device__ __forceinline__ void swap_halves(const float* p, const float* ds, float am, int hw, int hh, SwapArea& x,
                                             int lane, v8i& pb, v8i& db, int& sb) {
-  if (ACTIVE) {
-    // block hw spans subtile hw of both lane halves
-    const uint32_t bmax = max(__float_as_uint(am), __float_as_uint(other_half(am)));
-    const int byte = e4m3_scale_byte(bmax);
-    const float sc = __uint_as_float((uint32_t)byte << 23);
-    uint32_t P[4], Q[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      P[i] = (uint32_t)pack_fp8x4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
-      typedef short v2s __attribute__((ext_vector_type(2)));
-      v2s w = __builtin_bit_cast(v2s, __float_as_int(ds[4 * i]));
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, ds[4 * i], ds[4 * i + 1], sc, false);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, ds[4 * i + 2], ds[4 * i + 3], sc, true);
-      Q[i] = __builtin_bit_cast(uint32_t, w);
-    }
-    x.q[hw][lane] = make_uint4(P[0], P[1], P[2], P[3]);
-    x.q[2 + hw][lane] = make_uint4(Q[0], Q[1], Q[2], Q[3]);
-    x.sb[hw][lane] = (uint32_t)byte;
-  }
+  if (ACTIVE) write_half(p, ds, am, hw, x, lane);
   __syncthreads();
-  if (ACTIVE) {
-    const uint4 a = x.q[0][lane], b = x.q[1][lane], c = x.q[2][lane], d = x.q[3][lane];
-    pb = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-    db = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, (int)d.x, (int)d.y, (int)d.z, (int)d.w};
-    sb = (int)x.sb[hh][lane];
-  }
+  if (ACTIVE) read_operands(x, lane, hh, pb, db, sb);
 }
 
 template <bool CAUSAL, int DT, int NW>
@@ -989,25 +998,51 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_split_kernel(BwdPtrs b
     if (w == 0 && lane < 2) load_lds4_async((lane ? bp.v_step : bp.k_step) + (size_t)bh * nb + kt, L + 3 * TB);
     if (w == 1 && lane < D / 8) load_lds16_async(bp.tsc + (((size_t)2 * BH + bh) * nb + kt) * 2 * D + 16 * lane, L + SCO);
   };
-  auto tile = [&](const uint8_t* L, int kt, auto mode) {
-    constexpr int MODE = decltype(mode)::value;
-    constexpr bool ACTIVE = MODE >= 0;
-    float p[16], ds[16], am = 0.0f;
-    if (ACTIVE) {
-      const int kb = kt * 64;
-      const float kstep = reinterpret_cast<const float*>(L + 3 * TB)[0];
-      const float vstep = reinterpret_cast<const float*>(L + 3 * TB)[1];
-      const int row = tile_perm(n, hw);
-      v16i S = v16i{};
+  // Tile kt's dQ^T, (P K_s)^T products run one iteration late, as in the dK/dV kernel: S, dP of
+  // tile kt, then the products of tile kt - 1, a barrier that frees the other stage for the
+  // prefetch of tile kt + 1, then the vector work of tile kt.
+  auto products = [&](const uint8_t* L) {
+    v8i pb, db;
+    int sb;
+    read_operands(xch[grp], lane, hh, pb, db, sb);
+#pragma unroll
+    for (int i = 0; i < HCB; i++) {
+      const int row = 32 * (HCB * hw + i) + n;
+      const v8i a = lds_v8i(L + 2 * TB + coloff(row, 2 * hh), L + 2 * TB + coloff(row, 2 * hh + 1));
+      const int sa = L[SCO + hh * D + row];
+      dQ[i] = mfma_f8_ab(a, db, dQ[i], sa, sb);
+      PK[i] = mfma_f8_ab(a, pb, PK[i], sa, 127);   // P K_s for the rowsum correction
+    }
+  };
+  const int nkt_n = (N + 63) / 64;
+  const int nvis = CAUSAL ? min(nkt_n, (qw + 31) / 64 + 1) : nkt_n;
+  const int nfull = min(N / 64, CAUSAL ? (qw + 1) / 64 : nkt_n);
+  bool pend = false;   // tile kt - 1's products are still to be issued
+  auto iter = [&](int kt, auto mode) {
+    constexpr int MODE = decltype(mode)::value;   // 0: open, 1: masked, -1: past this wave's queries
+    const int buf = kt & 1;
+    const uint8_t* L = lds[buf];
+    const int row = tile_perm(n, hw);
+    v16i S = v16i{};
+    v16f Gp = v16f{};
+    if (MODE >= 0) {
 #pragma unroll
       for (int c = 0; c < D / 32; c++) S = mfma_i8(*reinterpret_cast<const v4i*>(L + rowoff<D>(row, 2 * c + hh)), qf[c], S);
-      v16f Gp = v16f{};
 #pragma unroll
       for (int c = 0; c < D / 64; c++)
         Gp = mfma_f8(lds_v8i(L + TB + rowoff<D>(row, 4 * c + 2 * hh), L + TB + rowoff<D>(row, 4 * c + 2 * hh + 1)), df[c], Gp);
+    }
+    if (pend) products(lds[buf ^ 1]);
+    __syncthreads();   // every wave is done with the other stage and the swap area
+    if (kt + 1 < nkt) stage(buf ^ 1, kt + 1);
+    if (MODE >= 0) {
       // element r: key kb + 32 hh + 16 hw + r, query = this lane's query
+      const int kb = kt * 64;
+      const float kstep = reinterpret_cast<const float*>(L + 3 * TB)[0];
+      const float vstep = reinterpret_cast<const float*>(L + 3 * TB)[1];
       const float cS = qstep * kstep * smlog2e, cP = dostep * vstep;
       const int lim = min(N, CAUSAL ? q + 1 : N) - (kb + 32 * hh + 16 * hw);   // keys r < lim are visible
+      float p[16], ds[16], am = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         float x = fmaf((float)S[r], cS, -l2);
@@ -1019,28 +1054,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_split_kernel(BwdPtrs b
         rsum += d;
         am = fmaxf(am, fabsf(d));
       }
+      write_half(p, ds, am, hw, xch[grp], lane);
     }
-    v8i pb, db;
-    int sb = 0;
-    swap_halves<ACTIVE>(p, ds, am, hw, hh, xch[grp], lane, pb, db, sb);
-    if (ACTIVE) {
-#pragma unroll
-      for (int c = 0; c < HCB; c++) {
-        const int row = 32 * (HCB * hw + c) + n;
-        const v8i a = lds_v8i(L + 2 * TB + coloff(row, 2 * hh), L + 2 * TB + coloff(row, 2 * hh + 1));
-        const int sa = L[SCO + hh * D + row];
-        dQ[c] = mfma_f8_ab(a, db, dQ[c], sa, sb);
-        PK[c] = mfma_f8_ab(a, pb, PK[c], sa, 127);   // P K_s for the rowsum correction
-      }
-    }
-  };
-  const int nkt_n = (N + 63) / 64;
-  const int nvis = CAUSAL ? min(nkt_n, (qw + 31) / 64 + 1) : nkt_n;
-  const int nfull = min(N / 64, CAUSAL ? (qw + 1) / 64 : nkt_n);
-  auto iter = [&](int kt, auto mode) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) stage(buf ^ 1, kt + 1);
-    tile(lds[buf], kt, mode);
+    pend = MODE >= 0;
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   };
@@ -1051,10 +1067,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_split_kernel(BwdPtrs b
   for (; kt < min(nfull, nkt); kt++) iter(kt, std::integral_constant<int, 0>{});
   for (; kt < min(nvis, nkt); kt++) iter(kt, std::integral_constant<int, 1>{});
   for (; kt < nkt; kt++) iter(kt, std::integral_constant<int, -1>{});
+  if (pend) products(lds[(nkt - 1) & 1]);
   // rowsum(dS) over both halves of the keys, in a fixed order (subtile 0's share first)
-  xch[grp].sb[hw][lane] = __float_as_uint(half_sum(rsum));
+  __shared__ float rsx[G][2][64];
+  rsx[grp][hw][lane] = half_sum(rsum);
   __syncthreads();
-  const float rs = (__uint_as_float(xch[grp].sb[0][lane]) + __uint_as_float(xch[grp].sb[1][lane])) * (1.0f / 448.0f);
+  const float rs = (rsx[grp][0][lane] + rsx[grp][1][lane]) * (1.0f / 448.0f);
   if (q < N) {
     uint16_t* dqr = reinterpret_cast<uint16_t*>(dq) + ((size_t)bh * N + q) * D;
     const float f448 = sm * (1.0f / 448.0f);
