@@ -710,9 +710,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdPtrs bp
 // its half of the channels.  The accumulators fall to 64 registers, so two waves run per SIMD;
 // the matrix and vector work per tile is the same as in the one-wave kernels, split in two.
 // The dS~ block scales are those of the one-wave form (block b is subtile b across both lane
-// halves), so the split changes no MFMA operand: dK and dV are what one wave per group would
-// compute (measured bit-identical when the split was introduced); only the fp32 order of dQ's
-// row sum of dS differs.  The dQ kernel issues a tile's products one
+// halves), so for the same inputs the split changes no MFMA operand except through D^: dQ's row
+// sum of dS, which D^ adds, is summed in a different fp32 order (each wave's half, then the
+// two halves).  The dQ kernel issues a tile's products one
 // iteration late, under the next tile's vector work (one swap barrier per tile fewer); the
 // dK/dV kernel, whose per-query LSE and D terms come from LDS, needed 256 registers and spilled
 // in that form (measured slower), so it swaps and multiplies within the tile.
